@@ -1,0 +1,449 @@
+/*
+ * CSA2 hot-path ORACLE: a plain, slow CPU statement of what the path computes.
+ *
+ * This file is test infrastructure.  Only the test-suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load it; the product path never does.
+ * It shares no code, header, table or helper with the GPU library.
+ *
+ * Sources (the pages are cited by title and section):
+ *   [R]  "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression"
+ *        (the report), sections 2.3, 2.3.1, 2.3.2, 2.4.4, 4.2.1.
+ *   [N4] reading note "DeepSeek V4.1 Flash: Pushing the Limits of KV Cache
+ *        Compression" (papers.chlience.com), section
+ *        "CSA2：共享存储、刷新选择和逐层计算分别控制" (CSA2: shared storage,
+ *        refreshed selection and per-layer computation), its mode table and
+ *        its decoder search-range / read-range table.
+ *   [C3] course notes "3. 通用基础设施" (3. General infrastructure),
+ *        section 3.2.2 SWA Bounded Replay, window equation.
+ *   OCP  OCP Microscaling Formats (MX) v1.0 -- [R] 2.4.4 names "OCP-standard
+ *        MXFP4" for the FP4 caches.
+ *
+ * Where the pages leave a step open, the plain reading is taken; every such
+ * reading is listed in the design notes of the repository.  The readings that
+ * shape this file:
+ *   - index score  score(t,j) = 2^(ek_j-127) * sum_h w[t,h] * ReLU(d_h * 2^(eq_th-127)),
+ *     d_h = exact dot product of the decoded q and k rows ("lightweight indexer
+ *     that scores the main KV entries using indexer Q and indexer K", [R] 2.3;
+ *     the per-head weights w come with the indexer of DeepSeek-V4's CSA, which
+ *     [R] 2.3.1 says Full mode inherits).  The head sum is evaluated in fp32 as
+ *     acc = +0; for h = 0..H-1: acc = fmaf(w[t,h], r_h, acc)  (one IEEE fused
+ *     multiply-add per head, round to nearest even).  That order is a convention.
+ *   - Top-K: the first min(K, visible) entries under (score descending,
+ *     position ascending); returned in ascending position order, -1 padded.
+ *   - block pool: blocks of 8 aligned at position 0; a block's score is the
+ *     maximum score over its visible positions; the first min(2048, #blocks)
+ *     blocks under (block score descending, block ascending) are kept
+ *     ([R] 2.3.2, [N4] decoder indexer paragraph).
+ *   - attention: one softmax over the union of the selected entries and the
+ *     SWA window, scale 1/sqrt(512), keys = values = the 512-channel latent.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -pthread (the explicit fmaf is the
+ * only fused operation).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Formats (OCP MX v1.0; [R] 2.4.4)                                           */
+/* ------------------------------------------------------------------------ */
+
+/* E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+ * exponent 0 is subnormal: 0.5 * m. */
+double orc_e2m1(uint8_t nibble) {
+    int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* E8M0: 2^(code-127); code 255 is NaN. */
+double orc_e8m0(uint8_t code) {
+    if (code == 255) return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+/* E4M3 "FN": sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0;
+ * S.1111.111 is NaN, there are no infinities. */
+double orc_e4m3(uint8_t code) {
+    int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* bf16: the top 16 bits of an IEEE binary32. */
+float orc_bf16(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Visibility ([R] 2.3: entry j of a ratio-m cache is built from the m tokens  */
+/* jm .. jm+m-1, with no overlap between entries)                             */
+/* ------------------------------------------------------------------------ */
+
+/* Entry j is visible to the query at token position t when every token it
+ * was built from is at or before t:  (j+1)*m - 1 <= t.  Returns how many of
+ * the n_entries are visible (they are always a prefix 0..vis-1). */
+int64_t orc_visible(int64_t n_entries, int64_t t, int m) {
+    if (t < 0) return 0;
+    int64_t v = (t + 1) / m;
+    return v < n_entries ? v : n_entries;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Parallel-for over independent rows (no effect on any value)                */
+/* ------------------------------------------------------------------------ */
+
+typedef void (*row_fn)(void* ctx, int64_t i);
+typedef struct { row_fn fn; void* ctx; int64_t n; int64_t next; pthread_mutex_t mu; } pool_t;
+
+static void* pool_worker(void* p) {
+    pool_t* P = (pool_t*)p;
+    for (;;) {
+        pthread_mutex_lock(&P->mu);
+        int64_t i = P->next++;
+        pthread_mutex_unlock(&P->mu);
+        if (i >= P->n) break;
+        P->fn(P->ctx, i);
+    }
+    return NULL;
+}
+
+static void parallel_for(int64_t n, int nthreads, row_fn fn, void* ctx) {
+    if (nthreads <= 1 || n <= 1) {
+        for (int64_t i = 0; i < n; ++i) fn(ctx, i);
+        return;
+    }
+    if (nthreads > 512) nthreads = 512;
+    pool_t P;
+    P.fn = fn; P.ctx = ctx; P.n = n; P.next = 0;
+    pthread_mutex_init(&P.mu, NULL);
+    pthread_t th[512];
+    for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, pool_worker, &P);
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    pthread_mutex_destroy(&P.mu);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Batch description shared by the calls below.                              */
+/* ------------------------------------------------------------------------ */
+/* row_seq[r]   : sequence of query row r
+ * q_pos[r]     : token position t of query row r
+ * entry_off[b] : first entry of sequence b in the packed caches; entry_off[n_seq] = total
+ * ratio        : compression ratio m                                          */
+
+/* ------------------------------------------------------------------------ */
+/* Index score ([R] 2.3 indexer; [R] 2.3.1 Full/Reindex; [R] 2.3.2 pool)      */
+/* ------------------------------------------------------------------------ */
+
+enum { ORC_Q_FP4 = 0, ORC_Q_FP8 = 1 };
+
+typedef struct {
+    const int32_t *row_seq, *q_pos;
+    const int64_t* entry_off;
+    int ratio, H, q_fmt;
+    const uint8_t *q, *q_sc;
+    const float* w;
+    const uint8_t *k, *k_sc;
+    const int32_t* cand;
+    int64_t cand_stride;
+    float* scores;
+    int64_t score_stride, n_slots;
+    int status;
+} score_ctx;
+
+/* Integer image of an indexer-q element: value * 2^qshift is an integer.
+ * E2M1 values are multiples of 0.5 (qshift 1); E4M3 values are multiples of
+ * 2^-9 (qshift 9). */
+static int64_t q_int(const score_ctx* c, int64_t row, int h, int ch) {
+    if (c->q_fmt == ORC_Q_FP4) {
+        uint8_t byte = c->q[(row * c->H + h) * 64 + ch / 2];
+        uint8_t nib = (ch & 1) ? (byte >> 4) : (byte & 15);
+        return (int64_t)llround(orc_e2m1(nib) * 2.0);
+    } else {
+        uint8_t code = c->q[(row * c->H + h) * 128 + ch];
+        return (int64_t)llround(orc_e4m3(code) * 512.0);
+    }
+}
+
+static int64_t k_int(const score_ctx* c, int64_t e, int ch) {
+    uint8_t byte = c->k[e * 64 + ch / 2];
+    uint8_t nib = (ch & 1) ? (byte >> 4) : (byte & 15);
+    return (int64_t)llround(orc_e2m1(nib) * 2.0);
+}
+
+/* score of one (query row, local entry j), or -inf when j is not visible. */
+static float score_one(const score_ctx* c, int64_t r, int64_t j, const int64_t* qi /* [H][128] */) {
+    int b = c->row_seq[r];
+    int64_t n = c->entry_off[b + 1] - c->entry_off[b];
+    int64_t vis = orc_visible(n, c->q_pos[r], c->ratio);
+    if (j < 0 || j >= vis) return -INFINITY;
+    int64_t e = c->entry_off[b] + j;
+    int64_t kv[128];
+    for (int ch = 0; ch < 128; ++ch) kv[ch] = k_int(c, e, ch);
+    int qshift = (c->q_fmt == ORC_Q_FP4) ? 1 : 9;
+    float acc = 0.0f;
+    for (int h = 0; h < c->H; ++h) {
+        int64_t dot = 0; /* exact: sum of integer products */
+        for (int ch = 0; ch < 128; ++ch) dot += qi[h * 128 + ch] * kv[ch];
+        /* d_h = dot * 2^-(qshift+1): exactly representable in binary32 whenever
+         * |dot| < 2^24, which the value bounds of both query formats ensure. */
+        if (dot >= (1LL << 24) || dot <= -(1LL << 24)) ((score_ctx*)c)->status = 2;
+        float d = (float)ldexp((double)dot, -(qshift + 1));
+        float sq = (float)orc_e8m0(c->q_sc[r * c->H + h]);
+        float rh = fmaxf(d, 0.0f) * sq; /* ReLU, then the query row's power-of-two scale */
+        acc = fmaf(c->w[r * c->H + h], rh, acc);
+    }
+    return acc * (float)orc_e8m0(c->k_sc[e]);
+}
+
+static void score_row(void* p, int64_t r) {
+    const score_ctx* c = (const score_ctx*)p;
+    int64_t* qi = (int64_t*)malloc(sizeof(int64_t) * (size_t)c->H * 128);
+    for (int h = 0; h < c->H; ++h)
+        for (int ch = 0; ch < 128; ++ch) qi[h * 128 + ch] = q_int(c, r, h, ch);
+    float* out = c->scores + r * c->score_stride;
+    int b = c->row_seq[r];
+    int64_t n = c->entry_off[b + 1] - c->entry_off[b];
+    int64_t ns = c->cand ? c->n_slots : n;
+    for (int64_t s = 0; s < ns; ++s) {
+        int64_t j = c->cand ? c->cand[r * c->cand_stride + s] : s;
+        out[s] = score_one(c, r, j, qi);
+    }
+    free(qi);
+}
+
+/* Scores for every query row.  Without a candidate list, slot s of row r is
+ * entry s of the row's sequence (slots 0..N_b-1 are written).  With one, slot
+ * s is entry cand[r][s] (-1 = empty) and n_slots slots are written.  Entries
+ * that are not visible, and empty slots, get -inf.  Returns 0, or 2 when a
+ * dot product fell outside the range where binary32 holds it exactly. */
+int orc_index_score(int64_t total_q, const int32_t* row_seq, const int32_t* q_pos, const int64_t* entry_off,
+                    int ratio, int H, int q_fmt, const uint8_t* q, const uint8_t* q_sc, const float* w,
+                    const uint8_t* k, const uint8_t* k_sc, const int32_t* cand, int64_t cand_stride,
+                    int64_t n_slots, float* scores, int64_t score_stride, int nthreads) {
+    score_ctx c = {row_seq, q_pos, entry_off, ratio, H, q_fmt, q, q_sc, w, k, k_sc,
+                   cand, cand_stride, scores, score_stride, n_slots, 0};
+    parallel_for(total_q, nthreads, score_row, &c);
+    return c.status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Top-K ([R] 2.3: "selects the Top-K entries for each query"; K = 512 in     */
+/* [R] 4.2.1).  Plain definition: sort everything, keep the first K.          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct { float s; int64_t pos; } sp_t;
+
+static int cmp_score_desc_pos_asc(const void* a, const void* b) {
+    const sp_t* x = (const sp_t*)a;
+    const sp_t* y = (const sp_t*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->pos < y->pos) ? -1 : (x->pos > y->pos);
+}
+
+static int cmp_i32_asc(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x < y) ? -1 : (x > y);
+}
+
+typedef struct {
+    const float* scores;
+    int64_t score_stride;
+    const int64_t* n_valid; /* slots 0..n_valid[r]-1 take part */
+    const int32_t* cand;    /* slot -> position, NULL: slot == position */
+    int64_t cand_stride;
+    int K;
+    int32_t* idx;
+} topk_ctx;
+
+static void topk_row(void* p, int64_t r) {
+    const topk_ctx* c = (const topk_ctx*)p;
+    int64_t n = c->n_valid[r];
+    sp_t* a = (sp_t*)malloc(sizeof(sp_t) * (size_t)(n > 0 ? n : 1));
+    for (int64_t s = 0; s < n; ++s) {
+        a[s].s = c->scores[r * c->score_stride + s];
+        a[s].pos = c->cand ? c->cand[r * c->cand_stride + s] : s;
+    }
+    qsort(a, (size_t)n, sizeof(sp_t), cmp_score_desc_pos_asc);
+    int64_t take = n < c->K ? n : c->K;
+    int32_t* out = c->idx + r * c->K;
+    for (int64_t i = 0; i < take; ++i) out[i] = (int32_t)a[i].pos;
+    qsort(out, (size_t)take, sizeof(int32_t), cmp_i32_asc);
+    for (int64_t i = take; i < c->K; ++i) out[i] = -1;
+    free(a);
+}
+
+void orc_topk(int64_t total_q, const float* scores, int64_t score_stride, const int64_t* n_valid,
+              const int32_t* cand, int64_t cand_stride, int K, int32_t* idx, int nthreads) {
+    topk_ctx c = {scores, score_stride, n_valid, cand, cand_stride, K, idx};
+    parallel_for(total_q, nthreads, topk_row, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block pool ([R] 2.3.2 Hierarchical Sparse Indexer; [N4] decoder indexer:   */
+/* both selections come from the same position scores and are independent)  */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float* scores;
+    int64_t score_stride;
+    const int64_t* vis;
+    int block, max_blocks;
+    int32_t *blocks, *pool_pos, *pool_count;
+} pool_ctx;
+
+static void pool_row(void* p, int64_t r) {
+    const pool_ctx* c = (const pool_ctx*)p;
+    int64_t vis = c->vis[r];
+    int64_t nb = (vis + c->block - 1) / c->block; /* blocks with at least one visible position */
+    sp_t* a = (sp_t*)malloc(sizeof(sp_t) * (size_t)(nb > 0 ? nb : 1));
+    for (int64_t b = 0; b < nb; ++b) {
+        float m = -INFINITY;
+        for (int64_t j = b * c->block; j < (b + 1) * c->block && j < vis; ++j) {
+            float s = c->scores[r * c->score_stride + j];
+            if (s > m) m = s;
+        }
+        a[b].s = m;
+        a[b].pos = b;
+    }
+    qsort(a, (size_t)nb, sizeof(sp_t), cmp_score_desc_pos_asc);
+    int64_t take = nb < c->max_blocks ? nb : c->max_blocks;
+    int32_t* ob = c->blocks + r * c->max_blocks;
+    for (int64_t i = 0; i < take; ++i) ob[i] = (int32_t)a[i].pos;
+    qsort(ob, (size_t)take, sizeof(int32_t), cmp_i32_asc);
+    for (int64_t i = take; i < c->max_blocks; ++i) ob[i] = -1;
+    int32_t* op = c->pool_pos + r * (int64_t)c->max_blocks * c->block;
+    int64_t cnt = 0;
+    for (int64_t i = 0; i < take; ++i)
+        for (int64_t j = (int64_t)ob[i] * c->block; j < ((int64_t)ob[i] + 1) * c->block && j < vis; ++j) op[cnt++] = (int32_t)j;
+    for (int64_t i = cnt; i < (int64_t)c->max_blocks * c->block; ++i) op[i] = -1;
+    c->pool_count[r] = (int32_t)cnt;
+    free(a);
+}
+
+void orc_block_pool(int64_t total_q, const float* scores, int64_t score_stride, const int64_t* vis, int block,
+                    int max_blocks, int32_t* blocks, int32_t* pool_pos, int32_t* pool_count, int nthreads) {
+    pool_ctx c = {scores, score_stride, vis, block, max_blocks, blocks, pool_pos, pool_count};
+    parallel_for(total_q, nthreads, pool_row, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gather + dequantise ([R] 2.4.4: cached values are dequantised before       */
+/* attention; [N4] Figure 4 reading: "Selection" reads the selected entries)  */
+/* ------------------------------------------------------------------------ */
+
+/* Main-KV entry e, channel c: E2M1(kv[e][c]) * 2^(sc[e][c/32] - 127). */
+static double kv_value(const uint8_t* kv, const uint8_t* kv_sc, int64_t e, int ch) {
+    uint8_t byte = kv[e * 256 + ch / 2];
+    uint8_t nib = (ch & 1) ? (byte >> 4) : (byte & 15);
+    return orc_e2m1(nib) * orc_e8m0(kv_sc[e * 16 + ch / 32]);
+}
+
+/* out[r][s][c] as bf16 bits; rows for idx == -1 are zero.  The value has at
+ * most two significant bits, so it is exact in bf16: the bits are those of
+ * the binary32 value with the low half dropped (which is zero). */
+void orc_gather_dequant(int64_t total_q, const int32_t* row_seq, const int64_t* entry_off, const uint8_t* kv,
+                        const uint8_t* kv_sc, const int32_t* idx, int K, uint16_t* out) {
+    for (int64_t r = 0; r < total_q; ++r)
+        for (int s = 0; s < K; ++s) {
+            int32_t j = idx[r * K + s];
+            uint16_t* o = out + (r * K + s) * 512;
+            for (int ch = 0; ch < 512; ++ch) {
+                if (j < 0) { o[ch] = 0; continue; }
+                float f = (float)kv_value(kv, kv_sc, entry_off[row_seq[r]] + j, ch);
+                uint32_t u;
+                memcpy(&u, &f, 4);
+                o[ch] = (uint16_t)(u >> 16);
+            }
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sparse latent attention ([R] 2.3: each query attends to the selected       */
+/* entries together with the layer-local SWA KV; [N4] Figure 4 reading: the   */
+/* selected main KV is concatenated with the SWA KV for core attention;      */
+/* [C3] 3.2.2: query i sees SWA keys [max(s, i-W+1), i])                      */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const int32_t *row_seq, *q_pos;
+    const int64_t* entry_off;
+    const uint16_t* q; /* [total_q][Hm][512] bf16 */
+    int Hm;
+    const uint8_t *kv, *kv_sc;
+    const int32_t* idx;
+    int K;
+    const uint16_t* swa; /* [rows][512] bf16 */
+    const int64_t* swa_row_off;
+    const int32_t* swa_pos0;
+    int W;
+    const int32_t* replay_s;
+    double scale;
+    float *out, *lse;
+} attn_ctx;
+
+static void attn_row(void* p, int64_t r) {
+    const attn_ctx* c = (const attn_ctx*)p;
+    int b = c->row_seq[r];
+    int64_t t = c->q_pos[r];
+    int64_t s0 = c->replay_s ? c->replay_s[b] : 0;
+    int64_t u_lo = t - c->W + 1;
+    if (u_lo < s0) u_lo = s0;
+    int64_t n_swa = t - u_lo + 1;
+    if (n_swa < 0) n_swa = 0;
+    int64_t nk = c->K + n_swa;
+    double* keys = (double*)malloc(sizeof(double) * (size_t)nk * 512);
+    int64_t n = 0;
+    for (int s = 0; s < c->K; ++s) {
+        int32_t j = c->idx[r * c->K + s];
+        if (j < 0) continue;
+        for (int ch = 0; ch < 512; ++ch) keys[n * 512 + ch] = kv_value(c->kv, c->kv_sc, c->entry_off[b] + j, ch);
+        ++n;
+    }
+    for (int64_t u = u_lo; u <= t; ++u) {
+        int64_t row = c->swa_row_off[b] + (u - c->swa_pos0[b]);
+        for (int ch = 0; ch < 512; ++ch) keys[n * 512 + ch] = (double)orc_bf16(c->swa[row * 512 + ch]);
+        ++n;
+    }
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    for (int h = 0; h < c->Hm; ++h) {
+        const uint16_t* qh = c->q + (r * c->Hm + h) * 512;
+        double mx = -INFINITY;
+        for (int64_t i = 0; i < n; ++i) {
+            double d = 0.0;
+            for (int ch = 0; ch < 512; ++ch) d += (double)orc_bf16(qh[ch]) * keys[i * 512 + ch];
+            logit[i] = d * c->scale;
+            if (logit[i] > mx) mx = logit[i];
+        }
+        double den = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            logit[i] = exp(logit[i] - mx); /* now the unnormalised weight of key i */
+            den += logit[i];
+        }
+        float* o = c->out + (r * c->Hm + h) * 512;
+        for (int ch = 0; ch < 512; ++ch) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < n; ++i) acc += logit[i] * keys[i * 512 + ch];
+            o[ch] = n > 0 ? (float)(acc / den) : 0.0f;
+        }
+        if (c->lse) c->lse[r * c->Hm + h] = n > 0 ? (float)(mx + log(den)) : -INFINITY;
+    }
+    free(logit);
+    free(keys);
+}
+
+void orc_sparse_attn(int64_t total_q, const int32_t* row_seq, const int32_t* q_pos, const int64_t* entry_off,
+                     const uint16_t* q, int Hm, const uint8_t* kv, const uint8_t* kv_sc, const int32_t* idx, int K,
+                     const uint16_t* swa, const int64_t* swa_row_off, const int32_t* swa_pos0, int W,
+                     const int32_t* replay_s, double scale, float* out, float* lse, int nthreads) {
+    attn_ctx c = {row_seq, q_pos, entry_off, q, Hm, kv, kv_sc, idx, K, swa, swa_row_off, swa_pos0, W, replay_s,
+                  scale, out, lse};
+    parallel_for(total_q, nthreads, attn_row, &c);
+}

@@ -1,0 +1,567 @@
+"""Pins for the CPU oracle: every check compares the oracle with something other
+than itself -- the format tables of the OCP MX v1.0 spec, closed forms, exact
+rational arithmetic, brute force through a different library (numpy / torch),
+and the invariants the pages fix (Top-K inside the block pool, Reindex with the
+Full layer's own query, Reuse = re-gather, sparse = dense when Top-K covers the
+visible range, SWA-only layers, compression ratio 2 visibility).
+
+Pages: the report "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
+Compression" (sections 2.3, 2.3.1, 2.3.2, 2.4.4, 4.2.1), the reading note
+"DeepSeek V4.1 Flash: Pushing the Limits of KV Cache Compression" (mode,
+schedule and search/read tables; the 890-byte ledger) and the course notes
+"3. 通用基础设施" (section 3.2.2, SWA window equation).
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_SWA_ONLY, Q_FP4, Q_FP8, Layer, Workload
+
+# ---------------------------------------------------------------------------
+# helpers (encoders written from the spec; independent of the oracle)
+# ---------------------------------------------------------------------------
+
+# OCP MX v1.0, E2M1 element encodings: magnitude codes 0..7 -> these values.
+E2M1_SPEC = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+E2M1_CODE = {v: i for i, v in enumerate(E2M1_SPEC)}
+
+
+def fp4_code(v):
+    return E2M1_CODE[abs(v)] | (8 if v < 0 else 0)
+
+
+def pack_fp4(vals):
+    """Values on the E2M1 grid -> packed bytes, element 2i in the low nibble."""
+    codes = [fp4_code(v) for v in vals]
+    return np.array([codes[2 * i] | (codes[2 * i + 1] << 4) for i in range(len(codes) // 2)], np.uint8)
+
+
+def rne_f32(x: Fraction) -> float:
+    """Round an exact rational to the nearest binary32 (ties to even)."""
+    if x == 0:
+        return 0.0
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    q = Fraction(2) ** (e - 23)
+    m = a / q
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return float(sign * fl * q)
+
+
+def tiny_workload(n_entries, q_pos, ratio=1, H=1, Hm=1, K=512, W=128, block=8, max_blocks=2048):
+    """A workload skeleton with hand-filled caches (one sequence per n_entries item)."""
+    n_entries = np.asarray(n_entries, np.int64)
+    entry_off = np.zeros(len(n_entries) + 1, np.int64)
+    entry_off[1:] = np.cumsum(n_entries)
+    q_pos_all = np.concatenate([np.asarray(p, np.int64) for p in q_pos]).astype(np.int32)
+    q_off = np.zeros(len(n_entries) + 1, np.int32)
+    q_off[1:] = np.cumsum([len(p) for p in q_pos])
+    row_seq = np.repeat(np.arange(len(n_entries), dtype=np.int32), [len(p) for p in q_pos])
+    swa_pos0 = np.array([max(0, int(min(p)) - W + 1) for p in q_pos], np.int32)
+    swa_len = np.array([int(max(p)) - s + 1 for p, s in zip(q_pos, swa_pos0)], np.int32)
+    swa_row_off = np.zeros(len(n_entries), np.int64)
+    swa_row_off[1:] = np.cumsum(swa_len)[:-1]
+    tot = int(entry_off[-1])
+    wl = Workload("tiny", 0, ratio, H, Hm, K, W, block, max_blocks, n_entries, entry_off, q_off, q_pos_all,
+                  row_seq, swa_row_off, swa_pos0, swa_len)
+    wl.k_idx = np.zeros((tot, 64), np.uint8)
+    wl.k_sc = np.full(tot, 127, np.uint8)
+    wl.kv = np.zeros((tot, 256), np.uint8)
+    wl.kv_sc = np.full((tot, 16), 127, np.uint8)
+    return wl
+
+
+def decode_kv(wl):
+    """Main KV as float64 from the spec table (independent of the oracle)."""
+    lo = wl.kv & 15
+    hi = wl.kv >> 4
+    codes = np.stack([lo, hi], -1).reshape(wl.kv.shape[0], 512)
+    mag = np.array(E2M1_SPEC)[codes & 7]
+    val = np.where(codes & 8, -mag, mag)
+    scale = np.exp2(wl.kv_sc.astype(np.float64) - 127.0)
+    return val * np.repeat(scale, 32, axis=1)
+
+
+def decode_fp4_rows(codes_u8, n):
+    lo = codes_u8 & 15
+    hi = codes_u8 >> 4
+    c = np.stack([lo, hi], -1).reshape(*codes_u8.shape[:-1], n)
+    mag = np.array(E2M1_SPEC)[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# formats
+# ---------------------------------------------------------------------------
+
+def test_e2m1_table_matches_spec():
+    for code in range(16):
+        v = oracle.e2m1(code)
+        mag = E2M1_SPEC[code & 7]
+        assert v == (-mag if code & 8 else mag)
+        assert math.copysign(1.0, v) == (-1.0 if code & 8 else 1.0)
+
+
+def test_e8m0_values():
+    assert oracle.e8m0(127) == 1.0
+    assert oracle.e8m0(0) == 2.0 ** -127
+    assert oracle.e8m0(254) == 2.0 ** 127
+    assert oracle.e8m0(130) == 8.0
+    assert math.isnan(oracle.e8m0(255))
+
+
+def test_e4m3fn_spec_points():
+    # OCP MX v1.0 / OFP8 E4M3: bias 7, max normal 448, min normal 2^-6, min subnormal 2^-9, NaN S.1111.111
+    assert oracle.e4m3(0x00) == 0.0
+    assert oracle.e4m3(0x01) == 2.0 ** -9
+    assert oracle.e4m3(0x07) == 7 * 2.0 ** -9
+    assert oracle.e4m3(0x08) == 2.0 ** -6
+    assert oracle.e4m3(0x38) == 1.0
+    assert oracle.e4m3(0x7E) == 448.0
+    assert oracle.e4m3(0xB8) == -1.0
+    assert math.isnan(oracle.e4m3(0x7F)) and math.isnan(oracle.e4m3(0xFF))
+    vals = [oracle.e4m3(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))  # monotone over the positive codes
+    finite = {oracle.e4m3(c) for c in range(256) if not math.isnan(oracle.e4m3(c))}
+    assert len(finite) == 253  # 254 non-NaN codes, +0 and -0 equal
+
+
+def test_bf16_points():
+    assert oracle.bf16(0x3F80) == 1.0
+    assert oracle.bf16(0xC000) == -2.0
+    assert math.isinf(oracle.bf16(0x7F80))
+    assert oracle.bf16(0x3F00) == 0.5
+
+
+def test_generator_encoders_agree_with_spec():
+    L = synth.lib()
+    for i, v in enumerate(E2M1_SPEC):
+        assert L.csa2synth_encode_e2m1(v) == i
+        if v:
+            assert L.csa2synth_encode_e2m1(-v) == i | 8
+    assert L.csa2synth_encode_e2m1(0.25) == 0  # tie to even (0)
+    assert L.csa2synth_encode_e2m1(0.75) == 2  # tie to even (1.0)
+    assert L.csa2synth_encode_e2m1(2.5) == 4   # tie to even (2.0)
+    assert L.csa2synth_encode_e2m1(5.0) == 6   # tie to even (4.0)
+    assert L.csa2synth_encode_e2m1(100.0) == 7
+    for c in range(0x7F):
+        assert L.csa2synth_encode_e4m3(oracle.e4m3(c)) == c
+
+
+# ---------------------------------------------------------------------------
+# visibility and compression ratio (report 2.3: entry j covers tokens jm..jm+m-1)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m", [1, 2])
+def test_visibility_brute_force(m):
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        n = int(rng.integers(0, 50))
+        t = int(rng.integers(-1, 120))
+        brute = sum(1 for j in range(n) if (j + 1) * m - 1 <= t)
+        assert oracle.visible(n, t, m) == brute
+
+
+def test_prefill_chunk_visibility_closed_form():
+    # 8,192 query tokens at the end of 262,144 tokens, ratio 2 -> 131,072 entries
+    ts = np.arange(253952, 262144)
+    vis = np.array([oracle.visible(131072, int(t), 2) for t in ts])
+    assert vis.min() == 126976 and vis.max() == 131072
+    assert int(vis.sum()) == 1056964608
+    assert all(v == (t + 1) // 2 for v, t in zip(vis[:100], ts[:100]))
+
+
+# ---------------------------------------------------------------------------
+# index score
+# ---------------------------------------------------------------------------
+
+def _score_wl(q_vals_per_head, k_vals, w, q_sc=None, k_sc=127, t=0, n=1):
+    H = len(q_vals_per_head)
+    wl = tiny_workload([n], [[t]], H=H)
+    for j in range(n):
+        wl.k_idx[j] = pack_fp4(k_vals)
+        wl.k_sc[j] = k_sc
+    q = np.stack([pack_fp4(v) for v in q_vals_per_head])[None]
+    qs = np.full((1, H), 127, np.uint8) if q_sc is None else np.asarray(q_sc, np.uint8)[None]
+    return wl, q, qs, np.asarray(w, np.float32)[None]
+
+
+def test_score_hand_values():
+    wl, q, qs, w = _score_wl([[1.0] * 128], [0.5] * 128, [1.0], t=0)
+    s = oracle.index_score(wl, q, qs, w, Q_FP4)
+    assert s[0, 0] == 64.0  # 128 * 1.0 * 0.5
+    wl, q, qs, w = _score_wl([[1.0] * 128], [0.5] * 128, [1.0], q_sc=[128], k_sc=126)
+    assert oracle.index_score(wl, q, qs, w, Q_FP4)[0, 0] == 64.0  # x2 then x0.5
+    wl, q, qs, w = _score_wl([[1.0] * 128], [0.5] * 128, [0.25], q_sc=[129])
+    assert oracle.index_score(wl, q, qs, w, Q_FP4)[0, 0] == 64.0  # 0.25 * 4 * 64
+
+
+def test_score_relu_and_sign():
+    # a negative dot product contributes nothing; a positive one counts once
+    wl, q, qs, w = _score_wl([[1.0] * 128, [-1.0] * 128], [0.5] * 128, [1.0, 1.0])
+    s = oracle.index_score(wl, q, qs, w, Q_FP4)[0, 0]
+    assert s == 64.0 and math.copysign(1, s) == 1
+    wl, q, qs, w = _score_wl([[-1.0] * 128], [0.5] * 128, [1.0])
+    s = oracle.index_score(wl, q, qs, w, Q_FP4)[0, 0]
+    assert s == 0.0 and math.copysign(1, s) == 1.0  # +0, never -0
+
+
+def test_score_invisible_is_neg_inf():
+    # query at t = 2 over 5 entries (ratio 1): entries 3, 4 are not visible
+    wl, q, qs, w = _score_wl([[1.0] * 128], [0.5] * 128, [1.0], t=2, n=5)
+    s = oracle.index_score(wl, q, qs, w, Q_FP4)[0]
+    assert list(s[:3]) == [64.0] * 3 and np.all(np.isneginf(s[3:]))
+
+
+def test_score_head_sum_order_exact_rational():
+    """The canonical fp32 head sum (one fused multiply-add per head, h ascending)
+    against an exact rational evaluation with round-to-nearest-even per step."""
+    rng = np.random.default_rng(7)
+    H = 64
+    for trial in range(6):
+        dots = rng.integers(-40, 60, size=H)
+        qv = []
+        for d in dots:  # q_h = d ones (or minus ones), k = all ones -> dot = d
+            row = [0.0] * 128
+            for i in range(abs(int(d))):
+                row[i] = 1.0 if d > 0 else -1.0
+            qv.append(row)
+        w = rng.random(H, dtype=np.float32)
+        eq = rng.integers(120, 135, size=H)
+        ek = int(rng.integers(120, 135))
+        wl, q, qs, ww = _score_wl(qv, [1.0] * 128, w, q_sc=eq, k_sc=ek)
+        got = oracle.index_score(wl, q, qs, ww, Q_FP4)[0, 0]
+        acc = Fraction(0)
+        for h in range(H):
+            r = Fraction(max(int(dots[h]), 0)) * Fraction(2) ** (int(eq[h]) - 127)
+            acc = Fraction(rne_f32(Fraction(float(w[h])) * r + acc))
+        want = rne_f32(acc * Fraction(2) ** (ek - 127))
+        assert got == want, (trial, got, want)
+
+
+def test_score_exact_against_float64_dot():
+    """Random quantised data, w = 1 for every head: the head sum is then exact,
+    so the score equals the float64 value of the definition."""
+    wl = synth.config("decode_c0", n_entries=[300])
+    L = wl.layers[0]
+    w1 = np.ones_like(L.w)
+    s = oracle.index_score(wl, L.q_idx, L.q_sc, w1, Q_FP4)[0]
+    k = decode_fp4_rows(wl.k_idx, 128)                      # [N][128]
+    q = decode_fp4_rows(L.q_idx[0], 128)                    # [H][128]
+    d = q @ k.T                                             # exact in float64
+    r = np.maximum(d, 0) * np.exp2(L.q_sc[0].astype(np.float64) - 127)[:, None]
+    want = r.sum(0) * np.exp2(wl.k_sc.astype(np.float64) - 127)
+    assert np.array_equal(s[:300].astype(np.float64), want)
+
+
+def test_score_fp8_query_hand_and_random():
+    # E4M3 query code 0x38 = 1.0, 0x30 = 0.5 ; k = 0.5
+    wl = tiny_workload([1], [[1]], ratio=2, H=1)
+    wl.k_idx[0] = pack_fp4([0.5] * 128)
+    q = np.full((1, 1, 128), 0x38, np.uint8)
+    q[0, 0, 64:] = 0x30
+    s = oracle.index_score(wl, q, np.full((1, 1), 127, np.uint8), np.ones((1, 1), np.float32), Q_FP8)
+    assert s[0, 0] == 64 * 0.5 + 64 * 0.25
+    # random FP8 rows from the generator, w = 1: exact float64 comparison
+    wl = synth.config("prefill_c3", tokens=600, T=8, n_layers=1)
+    L = wl.layers[0]
+    w1 = np.ones_like(L.w)
+    s = oracle.index_score(wl, L.q_idx, L.q_sc, w1, Q_FP8)
+    e4 = np.array([oracle.e4m3(c) if (c & 0x7F) != 0x7F else 0.0 for c in range(256)])
+    k = decode_fp4_rows(wl.k_idx, 128)
+    for r in range(8):
+        q = e4[L.q_idx[r]]
+        d = q @ k.T
+        rr = np.maximum(d, 0) * np.exp2(L.q_sc[r].astype(np.float64) - 127)[:, None]
+        want = rr.sum(0) * np.exp2(wl.k_sc.astype(np.float64) - 127)
+        vis = oracle.visible(300, int(wl.q_pos[r]), 2)
+        assert np.array_equal(s[r, :vis].astype(np.float64), want[:vis])
+        assert np.all(np.isneginf(s[r, vis:300]))
+
+
+# ---------------------------------------------------------------------------
+# Top-K (report 2.3; K = 512 in 4.2.1)
+# ---------------------------------------------------------------------------
+
+def test_topk_hand_ties():
+    s = np.array([[3, 5, 5, 1, 5]], np.float32)
+    assert list(oracle.topk(s, [5], 2)[0]) == [1, 2]
+    assert list(oracle.topk(s, [5], 4)[0]) == [0, 1, 2, 4]
+    assert list(oracle.topk(s, [5], 7)[0]) == [0, 1, 2, 3, 4, -1, -1]
+    assert list(oracle.topk(s, [3], 2)[0]) == [1, 2]   # only slots 0..2 take part
+    cand = np.array([[10, 20, 30, -1, -1]], np.int32)
+    s2 = np.array([[1, 2, 2, 0, 0]], np.float32)
+    assert list(oracle.topk(s2, [3], 1, cand=cand)[0]) == [20]
+
+
+@pytest.mark.parametrize("distinct", [3, 50, 100000])
+def test_topk_against_lexsort(distinct):
+    rng = np.random.default_rng(distinct)
+    rows, n, K = 6, 3000, 512
+    s = (rng.integers(0, distinct, size=(rows, n)) * 0.125).astype(np.float32)
+    nv = rng.integers(100, n, size=rows)
+    got = oracle.topk(s, nv, K)
+    for r in range(rows):
+        m = int(nv[r])
+        order = np.lexsort((np.arange(m), -s[r, :m].astype(np.float64)))
+        want = np.sort(order[:K])
+        want = np.concatenate([want, -np.ones(K - len(want), np.int64)])
+        assert np.array_equal(got[r], want)
+
+
+# ---------------------------------------------------------------------------
+# block pool (report 2.3.2; reading note decoder indexer paragraph)
+# ---------------------------------------------------------------------------
+
+def test_block_pool_hand_case():
+    s = np.array([[1, 9, 3, 3, 9, 0, 2, 2, 5]], np.float32)
+    blocks, pool, cnt = oracle.block_pool(s, [9], block=2, max_blocks=2)
+    assert list(blocks[0]) == [0, 2]
+    assert list(pool[0][:4]) == [0, 1, 4, 5] and cnt[0] == 4
+    # partial last block counts its visible positions only; a tie goes to the lower block
+    s = np.array([[1, 1, 0, 0, 1]], np.float32)
+    blocks, pool, cnt = oracle.block_pool(s, [5], block=2, max_blocks=2)
+    assert list(blocks[0]) == [0, 2] and list(pool[0]) == [0, 1, 4, -1] and cnt[0] == 3
+
+
+def test_block_pool_brute_force_and_invariants():
+    rng = np.random.default_rng(3)
+    rows, n = 3, 40000
+    s = (rng.integers(0, 2000, size=(rows, n)) * 0.5).astype(np.float32)
+    vis = np.array([40000, 39999, 17000])
+    blocks, pool, cnt = oracle.block_pool(s, vis, 8, 2048)
+    topk = oracle.topk(s, vis, 512)
+    for r in range(rows):
+        v = int(vis[r])
+        nb = (v + 7) // 8
+        padded = np.full(nb * 8, -np.inf)
+        padded[:v] = s[r, :v]
+        bmax = padded.reshape(nb, 8).max(1)
+        order = np.lexsort((np.arange(nb), -bmax))
+        want = np.sort(order[:2048])
+        assert np.array_equal(blocks[r][: len(want)], want) and np.all(blocks[r][len(want):] == -1)
+        pp = pool[r][: cnt[r]]
+        assert cnt[r] <= 16384 and np.all(np.diff(pp) > 0) and np.all(pool[r][cnt[r]:] == -1)
+        assert set(pp.tolist()) == {j for b in want for j in range(8 * b, min(8 * b + 8, v))}
+        # Top-512 is inside the pool: every block ranked ahead of a selected
+        # position's block holds a distinct position ranked ahead of it.
+        sel = topk[r][topk[r] >= 0]
+        assert set(sel.tolist()) <= set(pp.tolist())
+
+
+def test_block_pool_is_everything_when_small():
+    rng = np.random.default_rng(4)
+    s = rng.random((1, 16384)).astype(np.float32)
+    blocks, pool, cnt = oracle.block_pool(s, [16384], 8, 2048)
+    assert cnt[0] == 16384 and np.array_equal(pool[0], np.arange(16384))
+    blocks, pool, cnt = oracle.block_pool(s, [1001], 8, 2048)
+    assert cnt[0] == 1001 and np.array_equal(pool[0][:1001], np.arange(1001))
+
+
+# ---------------------------------------------------------------------------
+# gather + dequant (report 2.4.4)
+# ---------------------------------------------------------------------------
+
+def test_gather_dequant_against_spec_decode():
+    wl = synth.config("decode_c0", n_entries=[700])
+    rng = np.random.default_rng(5)
+    idx = np.sort(rng.choice(700, 512, replace=False)).astype(np.int32)[None]
+    idx[0, -5:] = -1
+    out = oracle.gather_dequant(wl, idx)
+    ref = decode_kv(wl)
+    got = bf16_to_f64(out[0])
+    for s in range(512):
+        if idx[0, s] < 0:
+            assert np.all(out[0, s] == 0)
+        else:
+            assert np.array_equal(got[s], ref[idx[0, s]])
+
+
+# ---------------------------------------------------------------------------
+# attention (report 2.3; reading note Figure 4: selected main KV concatenated
+# with the SWA KV; course notes 3.2.2: window [max(s, i-W+1), i])
+# ---------------------------------------------------------------------------
+
+def _dense_ref(q, keys, scale):
+    """torch's scaled_dot_product_attention in float64 on the CPU with K = V =
+    keys; the heads are the batch dimension."""
+    qt = torch.from_numpy(np.ascontiguousarray(q))[:, None, :]          # [H, 1, 512]
+    kt = torch.from_numpy(np.ascontiguousarray(keys))[None].expand(q.shape[0], *keys.shape).contiguous()
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=scale)
+    return out[:, 0, :].numpy()
+
+
+def _attn_setup(n, Hm=4, t=None, W=128):
+    wl = synth.config("decode_c0", n_entries=[n], Hm=Hm, W=W)
+    return wl, wl.layers[0]
+
+
+def test_sparse_equals_dense_when_topk_covers_all():
+    wl, L = _attn_setup(300)
+    idx = np.full((1, 512), -1, np.int32)
+    idx[0, :300] = np.arange(300)
+    out, lse = oracle.sparse_attn(wl, L.q_main, idx, L.swa)
+    keys = np.concatenate([decode_kv(wl)[:300], bf16_to_f64(L.swa)])  # window rows 172..299
+    assert L.swa.shape[0] == 128
+    q = bf16_to_f64(L.q_main[0])
+    ref = _dense_ref(q, keys, 1 / math.sqrt(512))
+    np.testing.assert_allclose(out[0], ref, rtol=1e-6, atol=1e-6)
+    logits = (q @ keys.T) / math.sqrt(512)
+    np.testing.assert_allclose(lse[0], np.log(np.exp(logits).sum(1)), rtol=1e-6)
+
+
+def test_swa_only_equals_dense_window():
+    wl, L = _attn_setup(300)
+    idx = np.full((1, 512), -1, np.int32)
+    out, _ = oracle.sparse_attn(wl, L.q_main, idx, L.swa)
+    ref = _dense_ref(bf16_to_f64(L.q_main[0]), bf16_to_f64(L.swa), 1 / math.sqrt(512))
+    np.testing.assert_allclose(out[0], ref, rtol=1e-6, atol=1e-6)
+
+
+def test_short_context_window_and_replay_start():
+    # t = 40 < W - 1: the window is [0, 40]; with a replay start s = 25 it is [25, 40]
+    wl = synth.config("decode_c0", n_entries=[41], Hm=2)
+    L = wl.layers[0]
+    assert L.swa.shape[0] == 41
+    idx = np.full((1, 512), -1, np.int32)
+    out, _ = oracle.sparse_attn(wl, L.q_main, idx, L.swa)
+    q = bf16_to_f64(L.q_main[0])
+    np.testing.assert_allclose(out[0], _dense_ref(q, bf16_to_f64(L.swa), 1 / math.sqrt(512)), rtol=1e-6, atol=1e-6)
+    out, _ = oracle.sparse_attn(wl, L.q_main, idx, L.swa, replay_s=np.array([25], np.int32))
+    np.testing.assert_allclose(out[0], _dense_ref(q, bf16_to_f64(L.swa[25:]), 1 / math.sqrt(512)), rtol=1e-6,
+                               atol=1e-6)
+
+
+def test_identical_keys_closed_form():
+    # every key equal -> softmax is uniform: output = the key, lse = logit + log(n)
+    wl = tiny_workload([600], [[599]], Hm=2)
+    row = pack_fp4(([1.0, -0.5, 2.0, 0.0] * 128)[:512])
+    wl.kv[:] = row
+    wl.kv_sc[:] = 126
+    key = decode_kv(wl)[0]
+    swa = np.tile(((key.astype(np.float32).view(np.uint32)) >> 16).astype(np.uint16), (128, 1))
+    q = np.tile(((np.linspace(-1, 1, 512).astype(np.float32).view(np.uint32)) >> 16).astype(np.uint16), (1, 2, 1))
+    idx = np.arange(512, dtype=np.int32)[None]
+    out, lse = oracle.sparse_attn(wl, q, idx, swa)
+    np.testing.assert_allclose(out[0, 0], key, rtol=1e-12, atol=1e-12)
+    logit = bf16_to_f64(q[0, 0]) @ key / math.sqrt(512)
+    assert abs(lse[0, 0] - (logit + math.log(640))) < 1e-5
+
+
+def test_attention_order_invariant():
+    wl, L = _attn_setup(2000)
+    rng = np.random.default_rng(9)
+    idx = np.sort(rng.choice(2000, 512, replace=False)).astype(np.int32)[None]
+    out1, lse1 = oracle.sparse_attn(wl, L.q_main, idx, L.swa)
+    out2, lse2 = oracle.sparse_attn(wl, L.q_main, idx[:, ::-1].copy(), L.swa)
+    np.testing.assert_allclose(out1, out2, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(lse1, lse2, rtol=1e-7)
+
+
+# ---------------------------------------------------------------------------
+# modes and the layer chain (report 2.3.1; reading note mode + schedule tables)
+# ---------------------------------------------------------------------------
+
+def _small_chain(n=24000, n_seq=2):
+    return synth.config("chain_c2", n_seq=n_seq, n=n, Hm=4)
+
+
+def test_reuse_equals_regather_with_source_indices():
+    wl = _small_chain()
+    res = oracle.layer_chain(wl)
+    by = {r["layer"]: r for r in res}
+    # layers 21..23 reuse 20's indices; 25..27 reuse 24's
+    for reuse, src in [(21, 20), (23, 20), (25, 24), (39, 36)]:
+        assert np.array_equal(by[reuse]["idx"], by[src]["idx"])
+        L = [x for x in wl.layers if x.index == reuse][0]
+        out, _ = oracle.sparse_attn(wl, L.q_main, by[src]["idx"], L.swa)
+        assert np.array_equal(out, by[reuse]["out"])
+
+
+def test_reindex_with_full_layer_query_reproduces_full_topk():
+    wl = _small_chain()
+    full = [x for x in wl.layers if x.index == 20][0]
+    for L in wl.layers:
+        if L.mode == MODE_REINDEX:
+            L.q_idx, L.q_sc, L.w = full.q_idx, full.q_sc, full.w
+    by = {r["layer"]: r for r in oracle.layer_chain(wl, attn=False)}
+    for l in (24, 28, 32, 36):
+        assert np.array_equal(by[l]["idx"], by[20]["idx"])
+
+
+def test_reindex_equals_full_scores_masked_to_pool():
+    """Reading note implementation table: the released reference scores the
+    whole range and then masks to the candidates; the pool-only path must agree."""
+    wl = _small_chain()
+    by = {r["layer"]: r for r in oracle.layer_chain(wl, attn=False)}
+    vis = oracle.row_visible(wl)
+    L = [x for x in wl.layers if x.index == 28][0]
+    full = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, Q_FP4)
+    for r in range(wl.total_q):
+        pp = by[20]["pool_pos"][r][: by[20]["pool_count"][r]]
+        masked = np.full(full.shape[1], -np.inf, np.float32)
+        masked[pp] = full[r, pp]
+        nv = int(vis[r])
+        order = np.lexsort((np.arange(nv), -masked[:nv].astype(np.float64)))
+        want = np.sort(order[:512])
+        assert np.array_equal(by[28]["idx"][r], want)
+    assert not np.array_equal(by[28]["idx"], by[20]["idx"])  # a different selection in general
+
+
+def test_pool_contains_full_topk_and_is_bounded():
+    wl = _small_chain()
+    by = {r["layer"]: r for r in oracle.layer_chain(wl, attn=False)}
+    for r in range(wl.total_q):
+        cnt = by[20]["pool_count"][r]
+        assert cnt == 16384  # 24,000 entries -> 3,000 blocks > 2,048
+        assert set(by[20]["idx"][r].tolist()) <= set(by[20]["pool_pos"][r][:cnt].tolist())
+        for l in (24, 28, 32, 36):
+            assert set(by[l]["idx"][r].tolist()) <= set(by[20]["pool_pos"][r][:cnt].tolist())
+
+
+def test_swa_only_layers_and_encoder_ratio():
+    # layers 0-1 are SWA only; an encoder group at ratio 2 is Full + 5 Reuse
+    wl = synth.make_workload("enc", 11, [500], 3, [(0, MODE_SWA_ONLY, False), (1, MODE_SWA_ONLY, False),
+                                                  (2, MODE_FULL, False), (3, MODE_REUSE, False)],
+                             ratio=2, Hm=2, q_pos=[np.array([900, 950, 999])])
+    res = oracle.layer_chain(wl)
+    assert np.all(res[0]["idx"] == -1) and np.all(res[1]["idx"] == -1)
+    vis = [oracle.visible(500, t, 2) for t in (900, 950, 999)]
+    assert vis == [450, 475, 500]
+    for r in range(3):
+        sel = res[2]["idx"][r]
+        assert np.all(sel[sel >= 0] < vis[r])
+    L0 = wl.layers[0]
+    for r, t in enumerate((900, 950, 999)):
+        lo = t - 127 - int(wl.swa_pos0[0])
+        keys = bf16_to_f64(L0.swa[lo: lo + 128])
+        ref = _dense_ref(bf16_to_f64(L0.q_main[r]), keys, 1 / math.sqrt(512))
+        np.testing.assert_allclose(res[0]["out"][r], ref, rtol=1e-6, atol=1e-6)
+
+
+def test_cache_ledger_matches_pages():
+    # reading note ledger: 256 + 32 + 64 + 4 = 356 B per position;
+    # 3 encoder source layers at half length + 1 decoder source layer -> 890 B/token
+    from compressed_sparse_attention_amd import ledger
+    assert ledger.bytes_per_position("pages") == 356
+    assert ledger.bytes_per_token("pages") == 890
+    assert ledger.bytes_per_position("mxfp4_e8m0") == 337
+    assert ledger.bytes_per_token("mxfp4_e8m0") == 842.5
