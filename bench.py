@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 hot path on one MI355X.
+
+Default workload (decode_c1): 64 sequences x 131,072 global entries (ratio 1),
+one query each at t = N-1, one Full-mode layer: lightning-indexer scan over the
+FP4 indexer K of every visible entry, Top-512, gather + dequant of the MXFP4
+main-KV latents, SWA-128, latent attention with 64 heads of 512.  A step is
+one csa2_layer_chain call over the whole batch, i.e. one decode layer-step.
+
+Prints ONE JSON line with the contract fields plus:
+  roofline      the dominant kernel (the indexer scan), its algorithmic bytes per
+                launch / its mean launch time, timed here with HIP events on the
+                stream it runs on, against the 8 TB/s HBM peak
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  prefill_index the prefill indexer (8,192 E4M3 queries x 131,072 entries at
+                ratio 2, causal) in TFLOP/s of algorithmic FLOPs
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA2 decode layer-steps/s at 128K ctx + achieved HBM GB/s; prefill index TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--n-seq", type=int, default=64)
+    ap.add_argument("--n", type=int, default=131072)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=16)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    from compressed_sparse_attention_amd import csa2 as C
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import DevWorkload, prepare_chain, run_chain
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    C.lib()
+    dev = torch.device("cuda:0")
+
+    t0 = time.time()
+    wl = synth.config("decode_c1", n_seq=args.n_seq, n=args.n)
+    log(f"[bench] generated decode_c1 inputs in {time.time() - t0:.1f}s")
+    dw = DevWorkload(wl, dev)
+    # a second copy of every cache so that consecutive steps do not hit in the 256 MB MALL
+    dw2 = DevWorkload.__new__(DevWorkload)
+    dw2.__dict__.update(dw.__dict__)
+    dw2.k_idx, dw2.k_sc, dw2.kv, dw2.kv_sc = dw.k_idx.clone(), dw.k_sc.clone(), dw.kv.clone(), dw.kv_sc.clone()
+    nq, n_layers = wl.total_q, len(wl.layers)
+    ws = C.workspace(C.csa2_workspace_size(C.CSA2_WS_LAYER_CHAIN, dw.batch, wl.K, wl.max_blocks, n_layers), dev)
+    copies = [dw, dw2]
+    calls = [prepare_chain(d, want_idx=False, want_lse=False, ws=ws, pool=False)[0] for d in copies]
+
+    def step(i):
+        calls[i % 2]()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    log(f"[bench] layer chain: {ms_step * 1000:.1f} us per decode layer-step")
+
+    # algorithmic bytes of one layer-step: scan 65 B per visible entry per sequence,
+    # per query: q/w (64 x (64 + 1 + 4) B), gathered 512 x 272 B, SWA 128 x 1024 B,
+    # main q 64 x 512 x 2 B, output 64 x 512 x 4 B, indices 512 x 4 B
+    vis_total = int(sum(min(int(wl.n_entries[b]), int(t) + 1) for b, t in zip(wl.row_seq, wl.q_pos)))
+    per_q = wl.H * (64 + 1 + 4) + wl.K * 272 + wl.W * 1024 + wl.Hm * 512 * 2 + wl.Hm * 512 * 4 + wl.K * 4
+    step_bytes = vis_total * 65 + nq * per_q
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # dominant kernel: the indexer scan, same kernel the chain launches, timed
+    # with HIP events on the stream it runs on
+    L0 = dw.layers[0]
+    stride = dw.batch.max_entries
+    sc_buf = torch.empty((nq, stride), dtype=torch.float32, device=dev)
+
+    def scan(i):
+        d = copies[i % 2]
+        C.csa2_index_score(d.batch, wl.H, C.CSA2_Q_FP4, L0["q_idx"], L0["q_sc"], L0["w"], d.k_idx, d.k_sc,
+                           scores=sc_buf)
+
+    for i in range(2):
+        scan(i)
+    torch.cuda.synchronize()
+    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s2.record()
+    for i in range(args.steps):
+        scan(i)
+    e2.record()
+    torch.cuda.synchronize()
+    scan_ms = s2.elapsed_time(e2) / args.steps
+    scan_bytes = vis_total * 65 + nq * wl.H * (64 + 1 + 4)
+    scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
+    log(f"[bench] scan kernel: {scan_ms * 1000:.1f} us, {scan_gbs:.0f} GB/s algorithmic")
+
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_step, 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4+bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_c1", "batch": wl.n_seq, "entries_per_seq": int(wl.n_entries[0]),
+                   "ratio": wl.ratio, "layers": 1, "mode": "full", "topk": wl.K, "swa_window": wl.W,
+                   "index_heads": wl.H, "main_heads": wl.Hm, "latent_dim": 512,
+                   "step_algorithmic_bytes": step_bytes, "step_hbm_gbs": round(step_gbs, 1),
+                   "sequence_layer_steps_per_s": round(wl.n_seq * 1000.0 / ms_step, 1)},
+        "roofline": {"kernel": "k_score_decode (indexer scan)", "bound": "hbm", "achieved": round(scan_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "mean_launch_us": round(scan_ms * 1000, 2),
+                     "algorithmic_bytes_per_launch": scan_bytes},
+    }
+    del sc_buf
+
+    if not args.no_prefill:
+        result["prefill_index"] = bench_prefill(args, C, synth, torch, dev)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, wl, dw, C, run_chain)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(args, C, synth, torch, dev):
+    """Prefill indexer: 8,192 E4M3 query rows (t = 253,952..262,143) against
+    131,072 entries (262,144 tokens at ratio 2), causal."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import DevWorkload
+
+    wl = synth.config("prefill_c3", n_layers=1, Hm=16)
+    dw = DevWorkload(wl, dev)
+    L = dw.layers[0]
+    nq = wl.total_q
+    sc = torch.empty((nq, dw.batch.max_entries), dtype=torch.float32, device=dev)
+
+    def run():
+        C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP8, L["q_idx"], L["q_sc"], L["w"], dw.k_idx, dw.k_sc, scores=sc)
+
+    run()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(3, args.steps // 4)
+    s.record()
+    for _ in range(reps):
+        run()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    pairs = int(sum(min(int(wl.n_entries[0]), (int(t) + 1) // 2) for t in wl.q_pos))
+    flops = 2.0 * pairs * wl.H * 128
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] prefill index: {ms:.2f} ms, {tflops:.0f} TFLOP/s")
+    del sc
+    return {"workload": "prefill_c3 index score", "ms": round(ms, 3), "pairs": pairs, "flops": flops,
+            "tflops": round(tflops, 1), "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+            "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "mfma": "bf16 32x32x16 (E4M3 x E2M1 operands converted exactly)"}
+
+
+def cpu_baseline(args, wl, dw, C, run_chain):
+    """The CPU oracle on the first cpu_sample_seqs sequences of the same
+    workload (their full layer chain), scaled to layer-steps/s of the whole
+    batch.  Its indices are also compared with the GPU's for those rows."""
+    import numpy as np
+
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    oracle.NTHREADS = threads
+    rows = np.arange(min(args.cpu_sample_seqs, wl.total_q))
+    t0 = time.time()
+    ref = oracle.layer_chain(wl, rows=rows)
+    dt = time.time() - t0
+    outs, _, _ = run_chain(dw, want_idx=True, want_lse=False, pool=False)
+    got_idx = outs[0]["idx"].cpu().numpy()[rows]
+    got_out = outs[0]["out"].cpu().numpy()[rows]
+    idx_equal = bool(np.array_equal(got_idx, ref[0]["idx"]))
+    err = float(np.abs(got_out.astype(np.float64) - ref[0]["out"]).max())
+    frac = len(rows) / wl.total_q
+    value = 1.0 / (dt / frac)
+    log(f"[bench] oracle: {dt:.1f}s for {len(rows)} sequences on {threads} threads")
+    return {"value": round(value, 5), "unit": "layer-steps/s", "cores": int(min(threads, len(rows))), "kind": "oracle",
+            "sample": f"{len(rows)} of {wl.total_q} sequences of decode_c1 (full 131,072-entry scan, Top-512, "
+                      f"attention), {dt:.1f} s wall, scaled by {wl.total_q}/{len(rows)}",
+            "sample_indices_equal_gpu": idx_equal, "sample_attn_max_abs_err": err}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,388 @@
+// C ABI of libcsa2: argument validation, workspace carving and launch order.
+// Every entry point validates on the host, then enqueues kernels on the
+// caller's stream and returns; nothing here synchronises with the device.
+#include <cmath>
+#include <cstring>
+
+#include "csa2_internal.h"
+
+using namespace csa2;
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+csa2_status hip_fail(hipError_t e) {
+    g_last_hip_error = (int32_t)e;
+    return CSA2_ERR_HIP;
+}
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Validates the batch descriptor and derives the launch geometry.
+csa2_status batch_geometry(const csa2_batch* b, Geometry* g) {
+    if (!b || b->n_seq < 1 || b->total_q < 1 || b->ratio < 1) return CSA2_ERR_INVALID_ARG;
+    if (!b->h_entry_off || !b->h_q_off || !b->h_q_pos || !b->d_entry_off || !b->d_q_off || !b->d_q_pos ||
+        !b->d_row_seq)
+        return CSA2_ERR_INVALID_ARG;
+    if (b->h_entry_off[0] != 0 || b->h_q_off[0] != 0 || b->h_q_off[b->n_seq] != b->total_q) return CSA2_ERR_INVALID_ARG;
+    int64_t max_n = 0;
+    int max_q = 0;
+    for (int s = 0; s < b->n_seq; ++s) {
+        const int64_t n = b->h_entry_off[s + 1] - b->h_entry_off[s];
+        const int nq = b->h_q_off[s + 1] - b->h_q_off[s];
+        if (n < 0 || nq < 0) return CSA2_ERR_INVALID_ARG;
+        if (n > max_n) max_n = n;
+        if (nq > max_q) max_q = nq;
+    }
+    if (max_n >= ((int64_t)1 << 31)) return CSA2_ERR_UNSUPPORTED;
+    for (int r = 0; r < b->total_q; ++r)
+        if (b->h_q_pos[r] < 0) return CSA2_ERR_INVALID_ARG;
+    g->n_seq = b->n_seq;
+    g->total_q = b->total_q;
+    g->ratio = b->ratio;
+    g->max_entries = max_n;
+    g->max_q_per_seq = max_q;
+    return CSA2_OK;
+}
+
+csa2_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return CSA2_OK;
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255)) return CSA2_ERR_WORKSPACE;
+    return CSA2_OK;
+}
+
+csa2_status check_swa(const csa2_batch* b, const csa2_swa_layout* sw) {
+    if (!sw || sw->window < 1 || sw->window > 1024) return sw && sw->window > 1024 ? CSA2_ERR_UNSUPPORTED : CSA2_ERR_INVALID_ARG;
+    if (!sw->h_row_off || !sw->h_pos0 || !sw->h_len || !sw->d_row_off || !sw->d_pos0) return CSA2_ERR_INVALID_ARG;
+    if ((sw->h_replay_s == nullptr) != (sw->d_replay_s == nullptr)) return CSA2_ERR_INVALID_ARG;
+    for (int s = 0; s < b->n_seq; ++s) {
+        if (sw->h_len[s] < 0 || sw->h_pos0[s] < 0 || sw->h_row_off[s] < 0) return CSA2_ERR_INVALID_ARG;
+        const int64_t rep = sw->h_replay_s ? sw->h_replay_s[s] : 0;
+        for (int r = b->h_q_off[s]; r < b->h_q_off[s + 1]; ++r) {
+            const int64_t t = b->h_q_pos[r];
+            int64_t lo = t - sw->window + 1;
+            if (lo < rep) lo = rep;
+            if (lo > t) continue;  // empty window
+            if (lo < sw->h_pos0[s] || t >= (int64_t)sw->h_pos0[s] + sw->h_len[s]) return CSA2_ERR_INVALID_ARG;
+        }
+    }
+    return CSA2_OK;
+}
+
+size_t pool_ws_bytes(const Geometry& g, int block) {
+    const int64_t nb = (g.max_entries + block - 1) / block;
+    return al256((size_t)g.total_q * (size_t)(nb > 0 ? nb : 1) * 4) + topk_ws_bytes(g.total_q);
+}
+
+struct ChainWs {
+    size_t scores, pool_scores, pool_ws, idx_cur, idx_empty, pool_out, total;
+};
+
+ChainWs chain_ws(const Geometry& g, int K, int block, int max_blocks) {
+    ChainWs w{};
+    size_t off = 0;
+    w.scores = off;
+    off += al256((size_t)g.total_q * (size_t)(g.max_entries > 0 ? g.max_entries : 1) * 4);
+    w.pool_scores = off;
+    off += al256((size_t)g.total_q * (size_t)max_blocks * block * 4);
+    w.pool_ws = off;  // block scores + Top-K workspace (the Top-K calls reuse its tail)
+    off += pool_ws_bytes(g, block);
+    w.idx_cur = off;
+    off += al256((size_t)g.total_q * K * 4);
+    w.idx_empty = off;
+    off += al256((size_t)g.total_q * K * 4);
+    w.pool_out = off;
+    off += al256((size_t)g.total_q * max_blocks * 4) + al256((size_t)g.total_q * max_blocks * block * 4) +
+           al256((size_t)g.total_q * 4);
+    w.total = off;
+    return w;
+}
+
+__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+}  // namespace
+
+extern "C" {
+
+CSA2_API int32_t csa2_version(void) { return 1; }
+
+CSA2_API int32_t csa2_last_hip_error(void) { return g_last_hip_error; }
+
+CSA2_API const char* csa2_status_string(csa2_status s) {
+    switch (s) {
+        case CSA2_OK: return "ok";
+        case CSA2_ERR_INVALID_ARG: return "invalid argument";
+        case CSA2_ERR_UNSUPPORTED: return "unsupported size or format";
+        case CSA2_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case CSA2_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+CSA2_API size_t csa2_workspace_size(int32_t which, const csa2_batch* batch, int32_t K, int32_t max_blocks,
+                                    int32_t n_layers) {
+    Geometry g;
+    if (batch_geometry(batch, &g) != CSA2_OK) return 0;
+    switch (which) {
+        case CSA2_WS_TOPK: return topk_ws_bytes(g.total_q);
+        case CSA2_WS_BLOCK_POOL: return pool_ws_bytes(g, 8);
+        case CSA2_WS_SPARSE_ATTN: return 0;
+        case CSA2_WS_LAYER_CHAIN:
+            if (K < 1 || max_blocks < 1 || n_layers < 1) return 0;
+            return chain_ws(g, K, 8, max_blocks).total;
+        default: return 0;
+    }
+}
+
+CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_t q_fmt, const void* q,
+                                      const uint8_t* q_sc, const float* w, const uint8_t* k_fp4,
+                                      const uint8_t* k_sc, const int32_t* cand, int32_t cand_stride,
+                                      float* scores, int64_t score_stride, hipStream_t stream) {
+    Geometry g;
+    csa2_status st = batch_geometry(batch, &g);
+    if (st) return st;
+    if (!q || !q_sc || !w || !k_fp4 || !k_sc || !scores) return CSA2_ERR_INVALID_ARG;
+    if (q_fmt != CSA2_Q_FP4 && q_fmt != CSA2_Q_FP8) return CSA2_ERR_INVALID_ARG;
+    if (H != 32 && H != 64) return CSA2_ERR_UNSUPPORTED;
+    if (cand) {
+        if (q_fmt != CSA2_Q_FP4) return CSA2_ERR_UNSUPPORTED;
+        if (cand_stride < 1 || score_stride < cand_stride) return CSA2_ERR_INVALID_ARG;
+    } else if (score_stride < g.max_entries || score_stride < 1) {
+        return CSA2_ERR_INVALID_ARG;
+    }
+    ScoreLaunch a{batch, g, H, q_fmt, (const uint8_t*)q, q_sc, w, k_fp4, k_sc, cand, cand_stride, scores, score_stride};
+    hipError_t e = launch_index_score(a, stream);
+    return e == hipSuccess ? CSA2_OK : hip_fail(e);
+}
+
+CSA2_API csa2_status csa2_topk(const csa2_batch* batch, const float* scores, int64_t score_stride,
+                               const int32_t* cand, int32_t cand_stride, const int32_t* cand_count, int32_t K,
+                               int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Geometry g;
+    csa2_status st = batch_geometry(batch, &g);
+    if (st) return st;
+    if (!scores || !idx) return CSA2_ERR_INVALID_ARG;
+    if (K < 1 || K > kMaxK) return K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
+    int64_t max_slots = g.max_entries;
+    if (cand) {
+        if (!cand_count || cand_stride < 1 || score_stride < cand_stride) return CSA2_ERR_INVALID_ARG;
+        max_slots = cand_stride;
+    } else if (score_stride < g.max_entries) {
+        return CSA2_ERR_INVALID_ARG;
+    }
+    if ((st = check_ws(ws, ws_bytes, topk_ws_bytes(g.total_q)))) return st;
+    TopkLaunch a{};
+    a.b = batch;
+    a.g = g;
+    a.scores = scores;
+    a.stride = score_stride;
+    a.max_slots = max_slots;
+    a.cand = cand;
+    a.cand_stride = cand_stride;
+    a.cand_count = cand_count;
+    a.block_mode = 0;
+    a.block = 1;
+    a.K = K;
+    a.idx = idx;
+    a.ws = ws;
+    hipError_t e = launch_topk(a, stream);
+    return e == hipSuccess ? CSA2_OK : hip_fail(e);
+}
+
+CSA2_API csa2_status csa2_block_pool(const csa2_batch* batch, const float* scores, int64_t score_stride,
+                                     int32_t block, int32_t max_blocks, int32_t* blocks, int32_t* pool_pos,
+                                     int32_t* pool_count, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Geometry g;
+    csa2_status st = batch_geometry(batch, &g);
+    if (st) return st;
+    if (!scores || !blocks || !pool_pos || !pool_count) return CSA2_ERR_INVALID_ARG;
+    if (block != 8) return block < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
+    if (max_blocks < 1 || max_blocks > kMaxK) return max_blocks < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
+    if (score_stride < g.max_entries) return CSA2_ERR_INVALID_ARG;
+    if ((st = check_ws(ws, ws_bytes, pool_ws_bytes(g, block)))) return st;
+    const int64_t nb = (g.max_entries + block - 1) / block;
+    PoolLaunch a{};
+    a.b = batch;
+    a.g = g;
+    a.scores = scores;
+    a.stride = score_stride;
+    a.block = block;
+    a.max_blocks = max_blocks;
+    a.blocks = blocks;
+    a.pool_pos = pool_pos;
+    a.pool_count = pool_count;
+    a.bscores = (float*)ws;
+    a.bstride = nb > 0 ? nb : 1;
+    a.topk_ws = (char*)ws + al256((size_t)g.total_q * (size_t)a.bstride * 4);
+    hipError_t e = launch_block_pool(a, stream);
+    return e == hipSuccess ? CSA2_OK : hip_fail(e);
+}
+
+CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, const uint8_t* kv_fp4, const uint8_t* kv_sc,
+                                         const int32_t* idx, int32_t K, uint16_t* out_bf16, hipStream_t stream) {
+    Geometry g;
+    csa2_status st = batch_geometry(batch, &g);
+    if (st) return st;
+    if (!kv_fp4 || !kv_sc || !idx || !out_bf16) return CSA2_ERR_INVALID_ARG;
+    if (K < 1 || K > 4096) return K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
+    hipError_t e = launch_gather_dequant(batch, g, kv_fp4, kv_sc, idx, K, out_bf16, stream);
+    return e == hipSuccess ? CSA2_OK : hip_fail(e);
+}
+
+CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16,
+                                      const uint8_t* kv_fp4, const uint8_t* kv_sc, const int32_t* idx, int32_t K,
+                                      const uint16_t* swa_bf16, const csa2_swa_layout* swa, float softmax_scale,
+                                      float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    Geometry g;
+    csa2_status st = batch_geometry(batch, &g);
+    if (st) return st;
+    if (!q_bf16 || !kv_fp4 || !kv_sc || !idx || !swa_bf16 || !out) return CSA2_ERR_INVALID_ARG;
+    if (Hm < 16 || Hm % 16) return Hm < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
+    if (K < 1 || K > kMaxK) return K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return CSA2_ERR_INVALID_ARG;
+    if ((st = check_swa(batch, swa))) return st;
+    AttnLaunch a{batch, g, Hm, q_bf16, kv_fp4, kv_sc, idx, K, swa_bf16, swa, softmax_scale, out, lse};
+    hipError_t e = launch_sparse_attn(a, stream);
+    return e == hipSuccess ? CSA2_OK : hip_fail(e);
+}
+
+CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_params* p, int32_t n_layers,
+                                      const csa2_layer* layers, const csa2_swa_layout* swa, int32_t* pool_blocks,
+                                      int32_t* pool_pos, int32_t* pool_count, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+    Geometry g;
+    csa2_status st = batch_geometry(batch, &g);
+    if (st) return st;
+    if (!p || !layers || n_layers < 1) return CSA2_ERR_INVALID_ARG;
+    if (p->H != 32 && p->H != 64) return CSA2_ERR_UNSUPPORTED;
+    if (p->Hm < 16 || p->Hm % 16) return CSA2_ERR_UNSUPPORTED;
+    if (p->K < 1 || p->K > kMaxK) return p->K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
+    if (p->block != 8) return CSA2_ERR_UNSUPPORTED;
+    if (p->max_blocks < 1 || p->max_blocks > kMaxK) return CSA2_ERR_UNSUPPORTED;
+    if (!(p->softmax_scale > 0.0f) || !std::isfinite(p->softmax_scale)) return CSA2_ERR_INVALID_ARG;
+    if ((st = check_swa(batch, swa))) return st;
+    // static checks of the schedule: every attending layer has main KV, every
+    // REUSE layer has indices, at most one layer builds the pool
+    bool have_kv = false, have_idx = false;
+    int pool_layers = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        const csa2_layer& L = layers[l];
+        if (!L.q_main || !L.swa || !L.out) return CSA2_ERR_INVALID_ARG;
+        switch (L.mode) {
+            case CSA2_MODE_SWA_ONLY: break;
+            case CSA2_MODE_FULL:
+                if (!L.kv_fp4 || !L.kv_sc || !L.k_fp4 || !L.k_sc || !L.q_idx || !L.q_sc || !L.w) return CSA2_ERR_INVALID_ARG;
+                if (L.q_fmt != CSA2_Q_FP4 && L.q_fmt != CSA2_Q_FP8) return CSA2_ERR_INVALID_ARG;
+                have_kv = have_idx = true;
+                if (L.flags & CSA2_LAYER_BUILD_POOL) ++pool_layers;
+                break;
+            case CSA2_MODE_REINDEX:
+                if (!have_kv || !L.q_idx || !L.q_sc || !L.w) return CSA2_ERR_INVALID_ARG;
+                if (L.q_fmt != CSA2_Q_FP4) return CSA2_ERR_UNSUPPORTED;  // pool scoring runs on FP4 queries
+                have_idx = true;
+                break;
+            case CSA2_MODE_REUSE:
+                if (!have_idx) return CSA2_ERR_INVALID_ARG;
+                break;
+            default: return CSA2_ERR_INVALID_ARG;
+        }
+    }
+    if (pool_layers > 1) return CSA2_ERR_INVALID_ARG;
+    const ChainWs cw = chain_ws(g, p->K, p->block, p->max_blocks);
+    if ((st = check_ws(ws, ws_bytes, cw.total))) return st;
+    char* base = (char*)ws;
+    float* scores = (float*)(base + cw.scores);
+    float* pscores = (float*)(base + cw.pool_scores);
+    char* pws = base + cw.pool_ws;
+    int32_t* idx_cur = (int32_t*)(base + cw.idx_cur);
+    int32_t* idx_empty = (int32_t*)(base + cw.idx_empty);
+    char* po = base + cw.pool_out;
+    int32_t* pb = pool_blocks ? pool_blocks : (int32_t*)po;
+    po += al256((size_t)g.total_q * p->max_blocks * 4);
+    int32_t* pp = pool_pos ? pool_pos : (int32_t*)po;
+    po += al256((size_t)g.total_q * p->max_blocks * p->block * 4);
+    int32_t* pc = pool_count ? pool_count : (int32_t*)po;
+    const int64_t nb = (g.max_entries + p->block - 1) / p->block;
+    const size_t bsc_bytes = al256((size_t)g.total_q * (size_t)(nb > 0 ? nb : 1) * 4);
+    void* topk_ws = pws + bsc_bytes;
+    const int pool_stride = p->max_blocks * p->block;
+
+    hipError_t e;
+    const int64_t nidx = (int64_t)g.total_q * p->K;
+    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((nidx + 255) / 256 < 2048 ? (nidx + 255) / 256 : 2048)), dim3(256), 0,
+                       stream, idx_empty, nidx, -1);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e);
+
+    const csa2_layer* src = nullptr;  // latest Full layer (main KV + indexer K)
+    bool pool_built = false;
+    for (int l = 0; l < n_layers; ++l) {
+        const csa2_layer& L = layers[l];
+        const int32_t* use_idx = idx_cur;
+        if (L.mode == CSA2_MODE_FULL || L.mode == CSA2_MODE_REINDEX) {
+            const bool full = L.mode == CSA2_MODE_FULL;
+            if (full) {
+                src = &L;
+                pool_built = false;
+            }
+            const bool on_pool = !full && pool_built;
+            ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, src->k_fp4, src->k_sc,
+                           on_pool ? pp : nullptr, on_pool ? pool_stride : 0, on_pool ? pscores : scores,
+                           on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1)};
+            if ((e = launch_index_score(sa, stream)) != hipSuccess) return hip_fail(e);
+            if (full && (L.flags & CSA2_LAYER_BUILD_POOL)) {
+                PoolLaunch pa{};
+                pa.b = batch;
+                pa.g = g;
+                pa.scores = scores;
+                pa.stride = g.max_entries > 0 ? g.max_entries : 1;
+                pa.block = p->block;
+                pa.max_blocks = p->max_blocks;
+                pa.blocks = pb;
+                pa.pool_pos = pp;
+                pa.pool_count = pc;
+                pa.bscores = (float*)pws;
+                pa.bstride = nb > 0 ? nb : 1;
+                pa.topk_ws = topk_ws;
+                if ((e = launch_block_pool(pa, stream)) != hipSuccess) return hip_fail(e);
+                pool_built = true;
+            }
+            TopkLaunch ta{};
+            ta.b = batch;
+            ta.g = g;
+            ta.scores = on_pool ? pscores : scores;
+            ta.stride = on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1);
+            ta.max_slots = on_pool ? pool_stride : g.max_entries;
+            ta.cand = on_pool ? pp : nullptr;
+            ta.cand_stride = on_pool ? pool_stride : 0;
+            ta.cand_count = on_pool ? pc : nullptr;
+            ta.block_mode = 0;
+            ta.block = 1;
+            ta.K = p->K;
+            ta.idx = idx_cur;
+            ta.ws = topk_ws;
+            if ((e = launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
+        } else if (L.mode == CSA2_MODE_SWA_ONLY) {
+            use_idx = idx_empty;
+        }
+        const uint8_t* kv = src ? src->kv_fp4 : nullptr;
+        const uint8_t* kvs = src ? src->kv_sc : nullptr;
+        if (!kv) {  // SWA-only layers before any Full layer: no entry is read
+            kv = (const uint8_t*)L.swa;
+            kvs = (const uint8_t*)L.swa;
+        }
+        AttnLaunch aa{batch, g, p->Hm, L.q_main, kv, kvs, use_idx, p->K, L.swa, swa, p->softmax_scale, L.out, L.lse};
+        if ((e = launch_sparse_attn(aa, stream)) != hipSuccess) return hip_fail(e);
+        if (L.idx_out) {
+            if ((e = hipMemcpyAsync(L.idx_out, use_idx, (size_t)nidx * 4, hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+                return hip_fail(e);
+        }
+    }
+    return CSA2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,291 @@
+// Gather + dequantise of the selected main-KV latents, and sparse latent
+// attention over [selected entries ++ SWA window].
+//
+// Report "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression":
+// section 2.3 (each query attends to its Top-K entries together with the
+// layer-local sliding-window KV), section 2.4.4 (FP4 main KV is dequantised
+// before attention), section 4.2.1 (64 query heads of dim 512 sharing one
+// latent, window 128).  The reading note "DeepSeek V4.1 Flash: Pushing the
+// Limits of KV Cache Compression" (Figure 4 reading) has the selected main KV
+// concatenated with the SWA KV and handed to core attention as one key set.
+// Course notes "3. 通用基础设施", section 3.2.2: query i sees SWA keys
+// [max(s, i-W+1), i].
+//
+// E2M1 x E8M0 values have at most two significant bits, so the dequantised
+// bf16 latents are exact.  gfx950's v_cvt_scalef32_pk_bf16_fp4 converts two
+// E2M1 nibbles (low nibble -> low half) and multiplies by the block scale.
+#include "csa2_internal.h"
+
+namespace csa2 {
+namespace {
+
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
+
+// 8 E2M1 values (one dword) times `scale` -> 8 bf16 (as 4 dwords).
+__device__ __forceinline__ v4i fp4x8_to_bf16(uint32_t codes, float scale) {
+    auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    return v4i{__builtin_bit_cast(int, a), __builtin_bit_cast(int, b), __builtin_bit_cast(int, c),
+               __builtin_bit_cast(int, d)};
+}
+
+__device__ __forceinline__ float e8m0_f32(uint32_t e) { return __builtin_ldexpf(1.0f, (int)e - 127); }
+
+// ---------------------------------------------------------------------------
+// gather + dequantise: grid (K, total_q), 64 threads, 8 channels per thread
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_gather_dequant(const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
+                                                       const int64_t* __restrict__ entry_off,
+                                                       const int32_t* __restrict__ row_seq,
+                                                       const int32_t* __restrict__ idx, int K,
+                                                       uint16_t* __restrict__ out) {
+    const int s = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
+    const int32_t j = idx[(int64_t)row * K + s];
+    const int b = row_seq[row];
+    v4i v = {0, 0, 0, 0};
+    if (j >= 0 && j < entry_off[b + 1] - entry_off[b]) {  // out-of-range entries read as empty
+        const int64_t e = entry_off[b] + j;
+        const uint32_t codes = *reinterpret_cast<const uint32_t*>(kv + e * 256 + 4 * t);
+        v = fp4x8_to_bf16(codes, e8m0_f32(kv_sc[e * 16 + (8 * t) / 32]));
+    }
+    *reinterpret_cast<v4i*>(out + ((int64_t)row * K + s) * 512 + 8 * t) = v;
+}
+
+// ---------------------------------------------------------------------------
+// sparse attention: one workgroup per (query row, group of 16 heads), 4 waves.
+// Keys come in blocks of 64: first the selected entries (idx order), then the
+// SWA rows of the window.  Per block: dequantise into LDS (row-major bf16),
+// S = Q K^T on v_mfma_f32_16x16x32_bf16 (wave w: keys 16w..16w+15), online
+// softmax in fp32, O += P V (wave w: channels 128w..128w+127) with V read
+// transposed by ds_read_b64_tr_b16.
+// ---------------------------------------------------------------------------
+constexpr int HG = 16;
+constexpr int KB = 64;
+constexpr int LROW = 512 + 8;  // LDS row stride in bf16 (16 B of padding)
+
+__global__ __launch_bounds__(256) void k_sparse_attn(
+    const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
+    const int32_t* __restrict__ idx, int K, const uint16_t* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
+    const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ replay_s, int W,
+    const int64_t* __restrict__ entry_off, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ q_pos,
+    float scale_log2, float* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg) {
+    __shared__ __attribute__((aligned(16))) uint16_t kl[KB * LROW];
+    __shared__ float sl[HG][KB];
+    __shared__ int kvalid[KB];
+    __shared__ int nsel_sh;
+
+    // the n_hg head groups of one row share an XCD (blocks are dealt to XCDs round-robin)
+    const int L = blockIdx.x;
+    const int xcd = L & 7;
+    const int kq = L >> 3;
+    const int hg = kq % n_hg;
+    const int row = (kq / n_hg) * 8 + xcd;
+    if (row >= total_q) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lg = lane >> 4, li = lane & 15;
+
+    const int b = row_seq[row];
+    const int64_t t = q_pos[row];
+    const int64_t e0 = entry_off[b];
+    const int64_t n_ent = entry_off[b + 1] - e0;
+    const int64_t s_rep = replay_s ? (int64_t)replay_s[b] : 0;
+    int64_t u_lo = t - W + 1;
+    u_lo = u_lo > s_rep ? u_lo : s_rep;
+    const int n_swa = t >= u_lo ? (int)(t - u_lo + 1) : 0;
+    const int32_t* irow = idx + (int64_t)row * K;
+
+    if (tid == 0) nsel_sh = 0;
+    __syncthreads();
+    {
+        int last = 0;
+        for (int s = tid; s < K; s += 256)
+            if (irow[s] >= 0) last = s + 1;
+        if (last) atomicMax(&nsel_sh, last);
+    }
+    __syncthreads();
+    const int n_sel = nsel_sh;
+    const int n_keys = n_sel + n_swa;
+    const int n_blocks = (n_keys + KB - 1) / KB;
+
+    // Q operand (16 heads x 512): lane holds head 16hg + li, channels 8lg + 32ks + [0, 8)
+    const int hq = HG * hg + li;
+    v8bf Q[16];
+    {
+        const uint16_t* qr = q + ((int64_t)row * Hm + hq) * 512 + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, ld16(qr + 32 * ks));
+    }
+    v4f O[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) O[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+    // running max and sums for head li (identical in every wave): l_run sums the
+    // bf16 weights the P V product uses (it normalises the output), l_lse the
+    // fp32 weights (it gives the log-sum-exp)
+    float m_run = -INFINITY, l_run = 0.0f, l_lse = 0.0f;
+
+    for (int blk = 0; blk < n_blocks; ++blk) {
+        // 1) stage 64 keys: thread -> key tid/4, channels 128*(tid%4) .. +128
+        {
+            const int key = tid >> 2, part = tid & 3;
+            const int vk = KB * blk + key;
+            uint16_t* dst = kl + key * LROW + 128 * part;
+            int valid = 0;
+            if (vk < n_sel) {
+                const int32_t j = irow[vk];
+                if (j >= 0 && j < n_ent) {
+                    valid = 1;
+                    const int64_t e = e0 + j;
+                    const uint8_t* src = kv + e * 256 + 64 * part;
+                    const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(kv_sc + e * 16 + 4 * part);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {  // 32 channels per scale
+                        const v4i c = ld16(src + 16 * i);
+                        const float sc = e8m0_f32((sc4 >> (8 * i)) & 255u);
+#pragma unroll
+                        for (int d = 0; d < 4; ++d)
+                            *reinterpret_cast<v4i*>(dst + 32 * i + 8 * d) = fp4x8_to_bf16((uint32_t)c[d], sc);
+                    }
+                }
+            } else if (vk < n_keys) {
+                valid = 1;
+                const int64_t u = u_lo + (vk - n_sel);
+                const int64_t r = swa_row_off[b] + (u - swa_pos0[b]);
+                const uint16_t* src = swa + r * 512 + 128 * part;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = ld16(src + 8 * i);
+            }
+            if (!valid) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = v4i{0, 0, 0, 0};
+            }
+            if (part == 0) kvalid[key] = valid;
+        }
+        __syncthreads();
+
+        // 2) S = Q K^T for keys 16*wave .. +16: lane gets S[head 4lg+v][key 16wave + li]
+        {
+            v4f S = {0.f, 0.f, 0.f, 0.f};
+            const uint16_t* kr = kl + (16 * wave + li) * LROW + 8 * lg;
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks) {
+                const v8bf Bk = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kr + 32 * ks));
+                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Q[ks], Bk, S, 0, 0, 0);
+            }
+            const int key = 16 * wave + li;
+            const bool ok = kvalid[key] != 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sl[4 * lg + v][key] = ok ? S[v] * scale_log2 : -INFINITY;
+        }
+        __syncthreads();
+
+        // 3) online softmax (base 2) for head li over keys 8lg + 32ks + i
+        float p[16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                p[8 * ks + i] = sl[li][8 * lg + 32 * ks + i];
+                mx = fmaxf(mx, p[8 * ks + i]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        float alpha;
+        v8bf P[2];
+        float rs = 0.0f, rs32 = 0.0f;
+        if (m_new == -INFINITY) {  // nothing valid yet
+            alpha = 1.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) p[i] = 0.0f;
+        } else {
+            alpha = exp2f(m_run - m_new);  // m_run = -inf -> 0
+#pragma unroll
+            for (int i = 0; i < 16; ++i) p[i] = exp2f(p[i] - m_new);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const __bf16 pb = (__bf16)p[8 * ks + i];
+                P[ks][i] = pb;
+                rs += (float)pb;  // normalise with the weights actually used
+                rs32 += p[8 * ks + i];
+            }
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
+        rs32 += __shfl_xor(rs32, 16);
+        rs32 += __shfl_xor(rs32, 32);
+        l_run = l_run * alpha + rs;
+        l_lse = l_lse * alpha + rs32;
+        m_run = m_new;
+        // O rows are heads 4lg + v: fetch their alpha from lane (4lg + v)
+        float av[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * lg + v);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) O[nt][v] *= av[v];
+
+        // 4) O += P V for channels 128*wave + 16nt + li
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const int n0 = 128 * wave + 16 * nt;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int kb = 8 * lg + 32 * ks;
+                const uint16_t* a0 = kl + (kb + (li >> 2)) * LROW + n0 + 4 * (li & 3);
+                const uint16_t* a1 = kl + (kb + 4 + (li >> 2)) * LROW + n0 + 4 * (li & 3);
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(a0));
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(a1));
+                const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P[ks], __builtin_bit_cast(v8bf, both), O[nt], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+
+    // finalise: O / l for heads 4lg + v
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    float iv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) iv[v] = __shfl(inv, 4 * lg + v);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            out[((int64_t)row * Hm + HG * hg + 4 * lg + v) * 512 + 128 * wave + 16 * nt + li] = O[nt][v] * iv[v];
+    if (lse && wave == 0 && lane < 16)
+        lse[(int64_t)row * Hm + HG * hg + lane] =
+            l_lse > 0.0f ? (m_run + log2f(l_lse)) * 0.69314718055994531f : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_gather_dequant(const csa2_batch* b, Geometry g, const uint8_t* kv, const uint8_t* kv_sc,
+                                 const int32_t* idx, int K, uint16_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_gather_dequant, dim3(K, g.total_q), dim3(64), 0, s, kv, kv_sc, b->d_entry_off, b->d_row_seq,
+                       idx, K, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
+    const int n_hg = a.Hm / HG;
+    const int rows8 = (a.g.total_q + 7) / 8 * 8;
+    const unsigned nblk = (unsigned)rows8 * (unsigned)n_hg;
+    hipLaunchKernelGGL(k_sparse_attn, dim3(nblk), dim3(256), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, a.swa,
+                       a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,
+                       a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q, n_hg);
+    return hipGetLastError();
+}
+
+}  // namespace csa2

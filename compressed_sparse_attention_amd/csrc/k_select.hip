@@ -1,0 +1,476 @@
+// Exact Top-K selection and the hierarchical block pool.
+//
+// Top-K (report "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
+// Compression", section 2.3; K = 512 in section 4.2.1): per query row, the
+// first min(K, n) slots under (score descending, position ascending), returned
+// in ascending position order.  Scores are non-negative binary32 values, so
+// their bit patterns order like the values; the composite
+//     key64 = (score bits << 32) | (0xFFFFFFFF - slot)
+// is then unique per slot and orders exactly like (score desc, slot asc), so
+// the selection is a plain radix select on key64 with no tie cases.
+//
+// Pass structure (every pass spans many workgroups per row):
+//   hist     histogram of score bits 30..19 (4096 bins) per row
+//   thresh   per row, the bin that holds the K-th largest score
+//   collect  every slot in a bin at or above it -> per-row candidate list
+//   final    per row, radix select on key64 among the candidates in LDS,
+//            then a bitonic sort of the K winners by slot
+//   fallback rows whose candidate list overflowed (heavy ties) are selected
+//            straight from the scores with the same radix select and an
+//            in-order compaction
+//
+// Block pool (section 2.3.2; the reading note "DeepSeek V4.1 Flash: Pushing
+// the Limits of KV Cache Compression": block selection uses the same position
+// scores and is independent of the Top-K): block score = max over the block's
+// visible positions; the Top-max_blocks blocks are chosen with the same
+// selection (slots = blocks), then expanded to their visible positions.
+#include "csa2_internal.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kHChunk = 8192;  // slots per workgroup in the histogram / collect passes
+
+struct RowSrc {
+    const int64_t* entry_off;
+    const int32_t* row_seq;
+    const int32_t* q_pos;
+    int ratio;
+    const int32_t* cand_count;  // non-null: n = cand_count[row]
+    int block_mode, block;
+    int64_t max_n;              // slots per row that exist in memory (clamps cand_count)
+};
+
+__device__ __forceinline__ int64_t row_n(const RowSrc& rs, int row) {
+    if (rs.cand_count) {
+        const int64_t c = rs.cand_count[row];
+        return c <= 0 ? 0 : (c < rs.max_n ? c : rs.max_n);
+    }
+    const int b = rs.row_seq[row];
+    const int64_t n = rs.entry_off[b + 1] - rs.entry_off[b];
+    const int64_t vis = visible_count(n, rs.q_pos[row], rs.ratio);
+    return rs.block_mode ? (vis + rs.block - 1) / rs.block : vis;
+}
+
+__device__ __forceinline__ uint32_t score_key(float s) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, s);
+    return (u & 0x80000000u) ? 0u : u;  // contract: scores >= +0; anything negative orders as +0
+}
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t slot) {
+    return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - slot);
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_hist(const float* __restrict__ scores, int64_t stride, RowSrc rs,
+                                              uint32_t* __restrict__ hist) {
+    __shared__ uint32_t h[kHistBins];
+    const int row = blockIdx.y;
+    const int64_t n = row_n(rs, row);
+    const int64_t s0 = (int64_t)blockIdx.x * kHChunk;
+    if (s0 >= n) return;
+    const int64_t s1 = s0 + kHChunk < n ? s0 + kHChunk : n;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
+    __syncthreads();
+    const float* sr = scores + (int64_t)row * stride;
+    for (int64_t s = s0 + threadIdx.x; s < s1; s += 256) atomicAdd(&h[score_key(sr[s]) >> 19], 1u);
+    __syncthreads();
+    uint32_t* gh = hist + (int64_t)row * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256)
+        if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// One workgroup per row: find the bin holding the kk-th largest key.
+__global__ __launch_bounds__(256) void k_thresh(const uint32_t* __restrict__ hist, RowSrc rs, int K,
+                                                RowSel* __restrict__ sel) {
+    __shared__ uint32_t part[256];
+    const int row = blockIdx.x;
+    const int64_t n = row_n(rs, row);
+    const uint32_t kk = (uint32_t)(n < K ? n : K);
+    const uint32_t* h = hist + (int64_t)row * kHistBins;
+    const int t = threadIdx.x;
+    // thread t owns bins [4096 - 16(t+1), 4096 - 16t), i.e. thread 0 the top bins
+    const int hi = kHistBins - 16 * t;
+    uint32_t s = 0;
+    for (int i = 1; i <= 16; ++i) s += h[hi - i];
+    part[t] = s;
+    if (t == 0) {
+        sel[row].n = (uint32_t)n;
+        sel[row].kk = kk;
+        sel[row].cnt = 0;
+        sel[row].bin = kk == 0 ? (uint32_t)kHistBins : 0u;  // overwritten below by the bin that holds the kk-th key
+    }
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
+        const uint32_t v = t >= off ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    if (kk == 0) return;
+    const uint32_t before = t ? part[t - 1] : 0;
+    if (before < kk && kk <= part[t]) {
+        uint32_t c = before;
+        for (int i = 1; i <= 16; ++i) {
+            c += h[hi - i];
+            if (c >= kk) {
+                sel[row].bin = (uint32_t)(hi - i);
+                break;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_collect(const float* __restrict__ scores, int64_t stride, RowSrc rs,
+                                                 RowSel* __restrict__ sel, uint64_t* __restrict__ cand_buf) {
+    const int row = blockIdx.y;
+    const int64_t n = row_n(rs, row);
+    const int64_t s0 = (int64_t)blockIdx.x * kHChunk;
+    if (s0 >= n) return;
+    const uint32_t bin = sel[row].bin;
+    if (bin >= (uint32_t)kHistBins) return;
+    const int64_t s1 = s0 + kHChunk < n ? s0 + kHChunk : n;
+    const float* sr = scores + (int64_t)row * stride;
+    uint64_t* cb = cand_buf + (int64_t)row * kCandCap;
+    const int lane = threadIdx.x & 63;
+    for (int64_t base = s0; base < s1; base += 256) {
+        const int64_t s = base + threadIdx.x;
+        uint32_t key = 0;
+        bool take = false;
+        if (s < s1) {
+            key = score_key(sr[s]);
+            take = (key >> 19) >= bin;
+        }
+        const uint64_t m = __ballot(take);
+        if (m) {
+            uint32_t pos0 = 0;
+            if (lane == 0) pos0 = atomicAdd(&sel[row].cnt, (uint32_t)__popcll(m));
+            pos0 = __shfl(pos0, 0);
+            if (take) {
+                const uint32_t p = pos0 + (uint32_t)__popcll(m & ((1ull << lane) - 1));
+                if (p < (uint32_t)kCandCap) cb[p] = composite(key, (uint32_t)s);
+            }
+        }
+    }
+}
+
+// Radix select helpers over key64 with 8-bit digits from the top.  `count`
+// elements (from LDS or generated) are examined per level; the result is the
+// smallest threshold T such that exactly kk elements have key64 >= T.
+struct RadixState {
+    uint64_t prefix;  // fixed high bits (already shifted down by `shift`)
+    int shift;        // bits below the fixed prefix
+    uint32_t need;    // elements still to take among those matching the prefix
+    int done;
+};
+
+// Block-wide (every thread of the workgroup calls it, no divergence around the
+// barriers): given a 256-bin histogram of the current digit among elements that
+// match the fixed prefix, find the digit d with  above(d) < need <= above(d) +
+// hist[d]  (above(d) = elements with a larger digit), which is unique, and
+// advance the state.
+__device__ void radix_step(const uint32_t* hist256, uint32_t* scan256, RadixState* st, int* found) {
+    const int t = threadIdx.x;
+    if (t < 64) {
+        // lane t owns digits 255-4t .. 252-4t; descending exclusive scan
+        const int d0 = 255 - 4 * t;
+        const uint32_t a = hist256[d0], b = hist256[d0 - 1], c = hist256[d0 - 2], d = hist256[d0 - 3];
+        const uint32_t sum = a + b + c + d;
+        uint32_t incl = sum;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t v = __shfl_up(incl, off);
+            if (t >= off) incl += v;
+        }
+        const uint32_t excl = incl - sum;
+        scan256[d0] = excl;
+        scan256[d0 - 1] = excl + a;
+        scan256[d0 - 2] = excl + a + b;
+        scan256[d0 - 3] = excl + a + b + c;
+    }
+    __syncthreads();
+    if (t < 256) {
+        const uint32_t above = scan256[t], here = hist256[t];
+        if (above < st->need && st->need <= above + here) *found = t;
+    }
+    __syncthreads();
+    if (t == 0) {
+        const int d = *found;
+        const uint32_t above = scan256[d], here = hist256[d];
+        st->need -= above;
+        st->prefix = (st->prefix << 8) | (uint64_t)d;
+        st->shift -= 8;
+        if (here == st->need || st->shift == 0) st->done = 1;
+    }
+    __syncthreads();
+}
+
+// Bitonic sort of `cnt` u32 values in LDS, padded to a power of two with 0xFFFFFFFF.
+__device__ void bitonic_sort_u32(uint32_t* a, int npow2) {
+    for (int k = 2; k <= npow2; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < npow2; i += blockDim.x) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const uint32_t x = a[i], y = a[l];
+                    const bool up = (i & k) == 0;
+                    if ((x > y) == up) {
+                        a[i] = y;
+                        a[l] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+}
+
+__device__ __forceinline__ int32_t map_slot(const int32_t* cand, int cand_stride, int row, uint32_t slot) {
+    return cand ? cand[(int64_t)row * cand_stride + slot] : (int32_t)slot;
+}
+
+__global__ __launch_bounds__(1024) void k_final(RowSel* __restrict__ sel, const uint64_t* __restrict__ cand_buf,
+                                                const int32_t* __restrict__ cand, int cand_stride, int K,
+                                                int32_t* __restrict__ idx) {
+    __shared__ uint64_t c[kCandCap];
+    __shared__ uint32_t winners[kMaxK];
+    __shared__ uint32_t hist256[256], scan256[256];
+    __shared__ RadixState st;
+    __shared__ uint32_t nwin;
+    __shared__ int found;
+    const int row = blockIdx.x;
+    const uint32_t cnt = sel[row].cnt, kk = sel[row].kk;
+    int32_t* out = idx + (int64_t)row * K;
+    if (cnt > (uint32_t)kCandCap) return;  // handled by the fallback
+    for (int i = threadIdx.x + (int)kk; i < K; i += 1024) out[i] = -1;
+    if (kk == 0) return;
+    for (uint32_t i = threadIdx.x; i < cnt; i += 1024) c[i] = cand_buf[(int64_t)row * kCandCap + i];
+    if (threadIdx.x == 0) {
+        st.prefix = 0;
+        st.shift = 64;
+        st.need = kk;
+        st.done = (cnt == kk);  // every candidate wins
+        nwin = 0;
+    }
+    __syncthreads();
+    while (!st.done) {
+        for (int i = threadIdx.x; i < 256; i += 1024) hist256[i] = 0;
+        __syncthreads();
+        const int sh = st.shift;
+        const uint64_t pf = st.prefix;
+        for (uint32_t i = threadIdx.x; i < cnt; i += 1024) {
+            const uint64_t x = c[i];
+            const bool m = sh >= 64 ? true : ((x >> sh) == pf);
+            if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - 8)) & 255u], 1u);
+        }
+        __syncthreads();
+        radix_step(hist256, scan256, &st, &found);
+    }
+    // winners: key64 >= prefix << shift
+    const int sh = st.shift;
+    const uint64_t pf = st.prefix;
+    for (uint32_t i = threadIdx.x; i < cnt; i += 1024) {
+        const uint64_t x = c[i];
+        const bool win = sh >= 64 ? true : ((x >> sh) >= pf);
+        if (win) {
+            const uint32_t p = atomicAdd(&nwin, 1u);
+            if (p < (uint32_t)kMaxK) winners[p] = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu);
+        }
+    }
+    __syncthreads();
+    int np2 = 1;
+    while (np2 < (int)kk) np2 <<= 1;
+    for (int i = threadIdx.x + (int)kk; i < np2; i += 1024) winners[i] = 0xFFFFFFFFu;
+    __syncthreads();
+    bitonic_sort_u32(winners, np2);
+    for (int i = threadIdx.x; i < (int)kk; i += 1024) out[i] = map_slot(cand, cand_stride, row, winners[i]);
+}
+
+// Rows whose candidate list overflowed: radix select over all slots, reading
+// the scores again at each level, then an in-order compaction.
+__global__ __launch_bounds__(1024) void k_fallback(const float* __restrict__ scores, int64_t stride, RowSrc rs,
+                                                   RowSel* __restrict__ sel, const int32_t* __restrict__ cand,
+                                                   int cand_stride, int K, int32_t* __restrict__ idx) {
+    __shared__ uint32_t hist256[256], scan256[256];
+    __shared__ RadixState st;
+    __shared__ int found;
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t base;
+    const int row = blockIdx.x;
+    if (sel[row].cnt <= (uint32_t)kCandCap) return;
+    const uint32_t kk = sel[row].kk;
+    const int64_t n = sel[row].n;
+    const float* sr = scores + (int64_t)row * stride;
+    int32_t* out = idx + (int64_t)row * K;
+    for (int i = threadIdx.x + (int)kk; i < K; i += 1024) out[i] = -1;
+    if (threadIdx.x == 0) {
+        st.prefix = 0;
+        st.shift = 64;
+        st.need = kk;
+        st.done = 0;
+        base = 0;
+    }
+    __syncthreads();
+    while (!st.done) {
+        for (int i = threadIdx.x; i < 256; i += 1024) hist256[i] = 0;
+        __syncthreads();
+        const int sh = st.shift;
+        const uint64_t pf = st.prefix;
+        for (int64_t s = threadIdx.x; s < n; s += 1024) {
+            const uint64_t x = composite(score_key(sr[s]), (uint32_t)s);
+            const bool m = sh >= 64 ? true : ((x >> sh) == pf);
+            if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - 8)) & 255u], 1u);
+        }
+        __syncthreads();
+        radix_step(hist256, scan256, &st, &found);
+    }
+    const int sh = st.shift;
+    const uint64_t pf = st.prefix;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int64_t s0 = 0; s0 < n; s0 += 1024) {
+        const int64_t s = s0 + threadIdx.x;
+        bool win = false;
+        if (s < n) {
+            const uint64_t x = composite(score_key(sr[s]), (uint32_t)s);
+            win = sh >= 64 ? true : ((x >> sh) >= pf);
+        }
+        const uint64_t m = __ballot(win);
+        if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t off = base;
+        for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2];
+        if (win) {
+            const uint32_t p = off + (uint32_t)__popcll(m & ((1ull << lane) - 1));
+            if (p < kk) out[p] = map_slot(cand, cand_stride, row, (uint32_t)s);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t tot = 0;
+            for (int w2 = 0; w2 < 16; ++w2) tot += wsum[w2];
+            base += tot;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// block pool
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_block_max(const float* __restrict__ scores, int64_t stride, RowSrc rs,
+                                                   float* __restrict__ bscores, int64_t bstride) {
+    const int row = blockIdx.y;
+    const int b = rs.row_seq[row];
+    const int64_t n = rs.entry_off[b + 1] - rs.entry_off[b];
+    const int64_t vis = visible_count(n, rs.q_pos[row], rs.ratio);
+    const int64_t nb = (vis + rs.block - 1) / rs.block;
+    const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (blk >= nb) return;
+    const float* sr = scores + (int64_t)row * stride;
+    float m = -INFINITY;
+    for (int64_t j = blk * rs.block; j < (blk + 1) * rs.block && j < vis; ++j) m = fmaxf(m, sr[j]);
+    bscores[(int64_t)row * bstride + blk] = m;
+}
+
+__global__ __launch_bounds__(256) void k_pool_expand(const int32_t* __restrict__ blocks, RowSrc rs, int max_blocks,
+                                                     int32_t* __restrict__ pool_pos, int32_t* __restrict__ pool_count) {
+    __shared__ uint32_t part[256];
+    const int row = blockIdx.x;
+    const int b = rs.row_seq[row];
+    const int64_t n = rs.entry_off[b + 1] - rs.entry_off[b];
+    const int64_t vis = visible_count(n, rs.q_pos[row], rs.ratio);
+    const int32_t* br = blocks + (int64_t)row * max_blocks;
+    int32_t* pr = pool_pos + (int64_t)row * max_blocks * rs.block;
+    const int per = (max_blocks + 255) / 256;  // blocks per thread, in order
+    const int t = threadIdx.x;
+    uint32_t mine = 0;
+    for (int i = t * per; i < (t + 1) * per && i < max_blocks; ++i) {
+        const int32_t bb = br[i];
+        if (bb >= 0) {
+            const int64_t lo = (int64_t)bb * rs.block;
+            const int64_t hi = lo + rs.block < vis ? lo + rs.block : vis;
+            mine += (uint32_t)(hi > lo ? hi - lo : 0);
+        }
+    }
+    part[t] = mine;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const uint32_t v = t >= off ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    uint32_t w = part[t] - mine;
+    for (int i = t * per; i < (t + 1) * per && i < max_blocks; ++i) {
+        const int32_t bb = br[i];
+        if (bb >= 0) {
+            const int64_t lo = (int64_t)bb * rs.block;
+            const int64_t hi = lo + rs.block < vis ? lo + rs.block : vis;
+            for (int64_t j = lo; j < hi; ++j) pr[w++] = (int32_t)j;
+        }
+    }
+    const uint32_t total = part[255];
+    for (int64_t i = total + t; i < (int64_t)max_blocks * rs.block; i += 256) pr[i] = -1;
+    if (t == 0) pool_count[row] = (int32_t)total;
+}
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t topk_ws_bytes(int total_q) {
+    return al256((size_t)total_q * kHistBins * 4) + al256((size_t)total_q * sizeof(RowSel)) +
+           al256((size_t)total_q * kCandCap * 8);
+}
+
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
+    const int nq = a.g.total_q;
+    char* ws = (char*)a.ws;
+    uint32_t* hist = (uint32_t*)ws;
+    ws += al256((size_t)nq * kHistBins * 4);
+    RowSel* sel = (RowSel*)ws;
+    ws += al256((size_t)nq * sizeof(RowSel));
+    uint64_t* cb = (uint64_t*)ws;
+    RowSrc rs{a.b->d_entry_off, a.b->d_row_seq, a.b->d_q_pos, a.b->ratio, a.cand ? a.cand_count : nullptr,
+              a.block_mode, a.block, a.max_slots};
+    const int64_t nfill = (int64_t)nq * kHistBins;
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((nfill + 255) / 256 < 4096 ? (nfill + 255) / 256 : 4096)), dim3(256), 0,
+                       s, hist, nfill, 0u);
+    const unsigned chunks = (unsigned)((a.max_slots + kHChunk - 1) / kHChunk);
+    hipLaunchKernelGGL(k_hist, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, hist);
+    hipLaunchKernelGGL(k_thresh, dim3(nq), dim3(256), 0, s, hist, rs, a.K, sel);
+    hipLaunchKernelGGL(k_collect, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, sel, cb);
+    hipLaunchKernelGGL(k_final, dim3(nq), dim3(1024), 0, s, sel, cb, a.cand, a.cand_stride, a.K, a.idx);
+    hipLaunchKernelGGL(k_fallback, dim3(nq), dim3(1024), 0, s, a.scores, a.stride, rs, sel, a.cand, a.cand_stride,
+                       a.K, a.idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_pool(const PoolLaunch& a, hipStream_t s) {
+    RowSrc rs{a.b->d_entry_off, a.b->d_row_seq, a.b->d_q_pos, a.b->ratio, nullptr, 1, a.block,
+              (a.g.max_entries + a.block - 1) / a.block};
+    const int64_t max_nb = (a.g.max_entries + a.block - 1) / a.block;
+    hipLaunchKernelGGL(k_block_max, dim3((unsigned)((max_nb + 255) / 256), a.g.total_q), dim3(256), 0, s, a.scores,
+                       a.stride, rs, a.bscores, a.bstride);
+    TopkLaunch t{};
+    t.b = a.b;
+    t.g = a.g;
+    t.scores = a.bscores;
+    t.stride = a.bstride;
+    t.max_slots = max_nb;
+    t.cand = nullptr;
+    t.cand_stride = 0;
+    t.cand_count = nullptr;
+    t.block_mode = 1;
+    t.block = a.block;
+    t.K = a.max_blocks;
+    t.idx = a.blocks;
+    t.ws = a.topk_ws;
+    hipError_t e = launch_topk(t, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_pool_expand, dim3(a.g.total_q), dim3(256), 0, s, a.blocks, rs, a.max_blocks, a.pool_pos,
+                       a.pool_count);
+    return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,265 @@
+/*
+ * csa2.h -- C ABI of libcsa2.so: CSA2 sparse attention over a compressed global
+ * KV cache, written for AMD Instinct MI355X (gfx950).
+ *
+ * The method is that of the report "DeepSeek-V4.1-Flash: Pushing the Limits of
+ * KV Cache Compression": a lightweight indexer scores the cached main-KV
+ * entries with indexer Q and indexer K and keeps the Top-K entries per query;
+ * each query then attends to the selected entries together with the layer's
+ * sliding-window KV (section 2.3).  Layers run in one of three modes -- Full,
+ * Reindex, Reuse -- that share main KV, indexer K and Top-K indices across
+ * layers (section 2.3.1); in the decoder the first Full layer also builds a
+ * block pool that bounds where later Reindex layers search (section 2.3.2).
+ *
+ * Conventions for every call
+ *   - Tensor pointers marked (device) are device memory owned by the caller.
+ *     The library never allocates or frees device memory.  Scratch memory is a
+ *     caller workspace of at least csa2_workspace_size() bytes, 256-byte aligned.
+ *   - Pointers marked (host) are read on the host during the call only.
+ *   - Calls are asynchronous on `stream`: they enqueue kernels and return.  The
+ *     library never synchronises the host with the device.
+ *   - Arguments are validated on the host first; a call that returns an error
+ *     has enqueued nothing (CSA2_ERR_HIP excepted: a launch failed part-way).
+ *   - No global mutable state; calls are thread-safe.  Calls that share a
+ *     workspace must be ordered on one stream.
+ *
+ * Data formats (OCP Microscaling Formats v1.0, which the report names as
+ * "OCP-standard MXFP4", section 2.4.4):
+ *   E2M1  4-bit float, values +-{0, .5, 1, 1.5, 2, 3, 4, 6}; two per byte,
+ *         element 2i in the low nibble of byte i.
+ *   E8M0  8-bit power-of-two scale 2^(e-127); 255 (NaN) is not allowed.
+ *   E4M3  OCP 8-bit float (bias 7, max 448, no infinities).
+ *   bf16  the upper 16 bits of an IEEE binary32.
+ * Layouts (entries of all sequences packed back to back; entry_off gives the
+ * first entry of each sequence):
+ *   main KV     kv_fp4 [total_entries][256] u8 (512 E2M1 latent channels)
+ *               kv_sc  [total_entries][16]  u8 (one E8M0 per 32 channels)
+ *   indexer K   k_fp4  [total_entries][64]  u8 (128 E2M1 channels)
+ *               k_sc   [total_entries]      u8 (one E8M0 per row)
+ *   indexer q   CSA2_Q_FP4: [total_q][H][64] u8, CSA2_Q_FP8: [total_q][H][128] u8
+ *               q_sc   [total_q][H] u8 (one E8M0 per head row)
+ *               w      [total_q][H] f32 head weights
+ *   main q      [total_q][Hm][512] bf16
+ *   SWA KV      [rows][512] bf16 per layer, rows of sequence b at row_off[b],
+ *               holding token positions pos0[b] .. pos0[b]+len[b]-1
+ *   indices     [total_q][K] i32 local entry positions, ascending, -1 padded
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(CSA2_BUILDING_LIBRARY)
+#define CSA2_API __attribute__((visibility("default")))
+#else
+#define CSA2_API
+#endif
+
+typedef int32_t csa2_status;
+#define CSA2_OK 0
+#define CSA2_ERR_INVALID_ARG 1   /* null pointer, bad size, stride too small, inconsistent batch */
+#define CSA2_ERR_UNSUPPORTED 2   /* a size this build does not implement (see each call) */
+#define CSA2_ERR_WORKSPACE 3     /* workspace missing, misaligned or too small */
+#define CSA2_ERR_HIP 4           /* a HIP launch failed; csa2_last_hip_error() has the code */
+
+#define CSA2_Q_FP4 0
+#define CSA2_Q_FP8 1
+
+#define CSA2_MODE_SWA_ONLY 0
+#define CSA2_MODE_FULL 1
+#define CSA2_MODE_REINDEX 2
+#define CSA2_MODE_REUSE 3
+
+#define CSA2_LAYER_BUILD_POOL 1  /* this Full layer builds the block pool (first decoder Full layer) */
+
+/* Ragged batch.  Sequence b owns entries entry_off[b] .. entry_off[b+1]-1 of the
+ * packed caches and query rows q_off[b] .. q_off[b+1]-1; query row r sits at
+ * token position q_pos[r].  With compression ratio m (report 2.3: entry j is
+ * built from tokens jm .. jm+m-1, no overlap) entry j is visible to a query at
+ * token t iff (j+1)*m - 1 <= t; the visible entries are 0 .. vis-1 with
+ * vis = min(N_b, floor((t+1)/m)).  The host arrays and the device arrays hold
+ * the same values: the host copies size the launches, the kernels read the
+ * device copies. */
+typedef struct csa2_batch {
+    int32_t n_seq;               /* >= 1 */
+    int32_t total_q;             /* >= 1 */
+    int32_t ratio;               /* compression ratio m >= 1 (1 decoder, 2 encoder) */
+    int32_t reserved;
+    const int64_t* h_entry_off;  /* (host)   [n_seq+1], non-decreasing, h_entry_off[0] = 0 */
+    const int32_t* h_q_off;      /* (host)   [n_seq+1], non-decreasing, h_q_off[n_seq] = total_q */
+    const int32_t* h_q_pos;      /* (host)   [total_q], >= 0 */
+    const int64_t* d_entry_off;  /* (device) [n_seq+1] */
+    const int32_t* d_q_off;      /* (device) [n_seq+1] */
+    const int32_t* d_q_pos;      /* (device) [total_q] */
+    const int32_t* d_row_seq;    /* (device) [total_q] sequence of each query row */
+} csa2_batch;
+
+/* Sliding-window KV layout, shared by every layer of a call (the rows
+ * themselves are per layer).  Query row r of sequence b at token t attends to
+ * SWA rows for tokens u in [max(s_b, t-W+1), t] (course notes "3. 通用基础设施"
+ * section 3.2.2), s_b = replay start (0 when d_replay_s is NULL).  Every such
+ * token must lie in [pos0[b], pos0[b]+len[b]); the host checks this. */
+typedef struct csa2_swa_layout {
+    int32_t window;              /* W >= 1 (128 in the report, section 4.2.1) */
+    int32_t reserved;
+    const int64_t* h_row_off;    /* (host)   [n_seq] first row of sequence b */
+    const int32_t* h_pos0;       /* (host)   [n_seq] token position of that row */
+    const int32_t* h_len;        /* (host)   [n_seq] rows present */
+    const int32_t* h_replay_s;   /* (host)   [n_seq] or NULL */
+    const int64_t* d_row_off;    /* (device) [n_seq] */
+    const int32_t* d_pos0;       /* (device) [n_seq] */
+    const int32_t* d_replay_s;   /* (device) [n_seq] or NULL */
+} csa2_swa_layout;
+
+/* ---- index score ---------------------------------------------------------
+ * Lightning-indexer scores (report 2.3; Full mode 2.3.1 scores every visible
+ * entry, Reindex mode rescores the shared indexer K with its own q):
+ *   score(r, j) = 2^(k_sc[j]-127) * sum_{h=0..H-1} w[r,h] * ReLU(d_h * 2^(q_sc[r,h]-127))
+ *   d_h = sum_c q[r,h,c] * k[j,c]   (exact: FP4 x FP4, and FP8 x FP4 for |q| <= 16)
+ * The head sum is the binary32 chain acc = +0; acc = fmaf(w[r,h], ReLU(..), acc)
+ * for h ascending, so scores are bit-reproducible.
+ * cand == NULL: slot s of row r is entry s of its sequence; slots 0 .. N_b-1
+ *   are written, -inf where the entry is not visible.
+ * cand != NULL: slot s of row r is entry cand[r*cand_stride + s] (-1 = empty);
+ *   slots 0 .. cand_stride-1 are written, -inf for empty or invisible slots.
+ * q: [total_q][H][64] (CSA2_Q_FP4) or [total_q][H][128] (CSA2_Q_FP8) (device).
+ * scores: [total_q][score_stride] f32 (device); score_stride >= max N_b
+ *   (cand == NULL) or >= cand_stride.
+ * Supported: H in {32, 64}.  CSA2_Q_FP8 requires cand == NULL. */
+CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_t q_fmt, const void* q,
+                                      const uint8_t* q_sc, const float* w, const uint8_t* k_fp4,
+                                      const uint8_t* k_sc, const int32_t* cand, int32_t cand_stride,
+                                      float* scores, int64_t score_stride, hipStream_t stream);
+
+/* ---- Top-K ---------------------------------------------------------------
+ * Per query row, the first min(K, n) slots under (score descending, entry
+ * position ascending), written as entry positions in ascending order and -1
+ * padded (report 2.3, "selects the Top-K entries for each query"; K = 512 in
+ * section 4.2.1).  n = vis(row) when cand == NULL (slots are positions), else
+ * n = cand_count[row] and slot s maps to position cand[row*cand_stride + s];
+ * the first n candidate positions must be ascending.  Scores of the n slots
+ * must be finite and >= +0 (as csa2_index_score writes them).
+ * idx: [total_q][K] i32 (device).  Supported: 1 <= K <= 2048.
+ * Workspace: csa2_workspace_size(CSA2_WS_TOPK, ...). */
+CSA2_API csa2_status csa2_topk(const csa2_batch* batch, const float* scores, int64_t score_stride,
+                               const int32_t* cand, int32_t cand_stride, const int32_t* cand_count, int32_t K,
+                               int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- block pool ----------------------------------------------------------
+ * Hierarchical Sparse Indexer candidate pool (report 2.3.2; the reading note
+ * "DeepSeek V4.1 Flash: Pushing the Limits of KV Cache Compression" states that
+ * the pool and the Top-K are two independent selections from the same
+ * position scores).  Blocks b cover positions [b*block, (b+1)*block), aligned
+ * at 0; a block exists when it holds a visible position and its score is the
+ * maximum score over its visible positions.  The first min(max_blocks, #blocks)
+ * blocks under (block score descending, block ascending) are kept.
+ * scores: Full-mode scores as csa2_index_score writes them (cand == NULL).
+ * blocks:     [total_q][max_blocks] i32 ascending, -1 padded (device)
+ * pool_pos:   [total_q][max_blocks*block] i32 visible positions of the kept
+ *             blocks, ascending, -1 padded (device)
+ * pool_count: [total_q] i32 (device)
+ * Supported: block == 8, 1 <= max_blocks <= 2048.
+ * Workspace: csa2_workspace_size(CSA2_WS_BLOCK_POOL, ...). */
+CSA2_API csa2_status csa2_block_pool(const csa2_batch* batch, const float* scores, int64_t score_stride,
+                                     int32_t block, int32_t max_blocks, int32_t* blocks, int32_t* pool_pos,
+                                     int32_t* pool_count, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- gather + dequantise --------------------------------------------------
+ * out[r][s][c] = E2M1(kv_fp4[e][c]) * 2^(kv_sc[e][c/32]-127) as bf16 (exact),
+ * e = entry_off[seq(r)] + idx[r][s]; rows for idx == -1 are zero.  Main KV is
+ * dequantised before attention (report 2.4.4).
+ * out_bf16: [total_q][K][512] (device).  Supported: 1 <= K <= 4096. */
+CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, const uint8_t* kv_fp4, const uint8_t* kv_sc,
+                                         const int32_t* idx, int32_t K, uint16_t* out_bf16, hipStream_t stream);
+
+/* ---- sparse latent attention ---------------------------------------------
+ * For every query row r and head h: keys = the selected main-KV latents
+ * {x_j : j = idx[r][s] >= 0} followed by the row's SWA rows; K = V = the
+ * 512-channel latent (MQA over a latent shared by all heads); one softmax over
+ * all of them (report 2.3: each query attends to the selected entries together
+ * with the SWA KV; the reading note's Figure 4 reading: the selected main KV is
+ * concatenated with the SWA KV for core attention).
+ *   out[r][h] = sum_u softmax_u(scale * q[r][h] . key_u) * key_u   (fp32)
+ *   lse[r][h] = log sum_u exp(scale * q[r][h] . key_u)               (optional)
+ * q_bf16: [total_q][Hm][512]; swa_bf16: [rows][512] laid out by `swa`;
+ * out: [total_q][Hm][512] f32; lse: [total_q][Hm] f32 or NULL (all device).
+ * Supported: Hm a multiple of 16, 1 <= K <= 2048, window <= 1024.
+ * Workspace: none today (ws may be NULL, ws_bytes 0). */
+CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16,
+                                      const uint8_t* kv_fp4, const uint8_t* kv_sc, const int32_t* idx, int32_t K,
+                                      const uint16_t* swa_bf16, const csa2_swa_layout* swa, float softmax_scale,
+                                      float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- layer chain ---------------------------------------------------------
+ * Runs layers in order with the modes of report 2.3.1 (the reading note's mode
+ * table): FULL scores every visible entry of its own caches, takes Top-K and,
+ * when flagged CSA2_LAYER_BUILD_POOL, the block pool from the same scores;
+ * REINDEX scores the pool (every visible entry when no pool exists) against
+ * the latest Full layer's indexer K with its own q and takes Top-K; REUSE
+ * attends with the latest indices; SWA_ONLY attends to its window only.  Every
+ * layer attends with its own q_main and SWA rows over the latest Full layer's
+ * main KV.  Results equal the composition of the calls above bit for bit. */
+typedef struct csa2_layer {
+    int32_t mode;                /* CSA2_MODE_* */
+    int32_t flags;               /* CSA2_LAYER_BUILD_POOL (FULL only) */
+    int32_t q_fmt;               /* CSA2_Q_FP4 / CSA2_Q_FP8 (FULL, REINDEX) */
+    int32_t reserved;
+    const void* q_idx;           /* (device) indexer q (FULL, REINDEX) */
+    const uint8_t* q_sc;         /* (device) [total_q][H] */
+    const float* w;              /* (device) [total_q][H] */
+    const uint8_t* kv_fp4;       /* (device) main KV of this layer (FULL) */
+    const uint8_t* kv_sc;
+    const uint8_t* k_fp4;        /* (device) indexer K of this layer (FULL) */
+    const uint8_t* k_sc;
+    const uint16_t* q_main;      /* (device) [total_q][Hm][512] bf16 */
+    const uint16_t* swa;         /* (device) SWA rows of this layer, laid out by the chain's swa layout */
+    float* out;                  /* (device) [total_q][Hm][512] */
+    float* lse;                  /* (device) [total_q][Hm] or NULL */
+    int32_t* idx_out;            /* (device) [total_q][K] or NULL: the indices this layer attended with */
+} csa2_layer;
+
+typedef struct csa2_chain_params {
+    int32_t H;                   /* indexer heads (32 or 64) */
+    int32_t Hm;                  /* main query heads (multiple of 16) */
+    int32_t K;                   /* Top-K (<= 2048) */
+    int32_t block;               /* pool block size (8) */
+    int32_t max_blocks;          /* pool blocks (<= 2048) */
+    float softmax_scale;         /* 1/sqrt(512) for the report's latent */
+} csa2_chain_params;
+
+/* pool_blocks [total_q][max_blocks], pool_pos [total_q][max_blocks*block],
+ * pool_count [total_q] (device, each may be NULL): the pool, when one is built.
+ * Workspace: csa2_workspace_size(CSA2_WS_LAYER_CHAIN, ...). */
+CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_params* params, int32_t n_layers,
+                                      const csa2_layer* layers, const csa2_swa_layout* swa, int32_t* pool_blocks,
+                                      int32_t* pool_pos, int32_t* pool_count, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
+
+/* ---- workspace, status ----------------------------------------------------- */
+#define CSA2_WS_TOPK 1
+#define CSA2_WS_BLOCK_POOL 2
+#define CSA2_WS_SPARSE_ATTN 3
+#define CSA2_WS_LAYER_CHAIN 4
+
+/* Bytes of workspace the call `which` needs for this batch; K and max_blocks
+ * as the call will be made (ignored where irrelevant); n_layers for the chain.
+ * Returns 0 on invalid arguments. */
+CSA2_API size_t csa2_workspace_size(int32_t which, const csa2_batch* batch, int32_t K, int32_t max_blocks,
+                                    int32_t n_layers);
+
+CSA2_API const char* csa2_status_string(csa2_status s);
+/* The hipError_t of the last CSA2_ERR_HIP returned on this host thread. */
+CSA2_API int32_t csa2_last_hip_error(void);
+CSA2_API int32_t csa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

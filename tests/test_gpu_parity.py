@@ -1,0 +1,256 @@
+"""GPU parity: every call of the C ABI against the CPU oracle on the same seeded
+inputs.  Scores, indices, pools and dequantised rows must match bit for bit;
+attention outputs within |gpu - ref| <= 2e-3 + 1e-2 |ref|.
+
+Sizes are small enough for the oracle to finish in seconds while spanning
+several tiles, ragged tails and the degenerate cases (1-entry sequences, fewer
+visible entries than K, contexts shorter than the SWA window, ties)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from compressed_sparse_attention_amd import csa2 as C
+from gpu_util import SCALE, DevWorkload, assert_close_attn, dev, run_chain
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_rows_equal(got, ref, wl):
+    """Compare score rows over slots 0..N_b-1 of each row's sequence, bitwise."""
+    got = got.cpu().numpy()
+    for r in range(wl.total_q):
+        n = int(wl.n_entries[wl.row_seq[r]])
+        g, o = got[r, :n], ref[r, :n]
+        if not np.array_equal(g.view(np.uint32), o.view(np.uint32)):
+            bad = np.nonzero(g.view(np.uint32) != o.view(np.uint32))[0]
+            raise AssertionError(f"row {r}: {len(bad)} scores differ, first at slot {bad[0]}: {g[bad[0]]!r} vs {o[bad[0]]!r}")
+
+
+DECODE_CASES = {
+    "c0_4096": dict(name="decode_c0"),
+    "ragged_t1": dict(name="decode_c1", lens=[1, 7, 63, 64, 65, 255, 4097, 9000]),
+    "ragged_t4": dict(name="ragged_c4", lens=[5, 64, 300, 5000, 70000], T=4),
+    "h32": dict(name="decode_c1", lens=[100, 3000], H=32),
+}
+
+
+def _decode_wl(case):
+    c = DECODE_CASES[case]
+    if "lens" not in c:
+        return synth.config(c["name"])
+    T = c.get("T", 1)
+    return synth.make_workload(case, 0xC5A2F000 + len(case), c["lens"], T, [(20, synth.MODE_FULL, False)],
+                               H=c.get("H", 64), Hm=16)
+
+
+@pytest.mark.parametrize("case", list(DECODE_CASES))
+def test_index_score_full_bitwise(case):
+    wl = _decode_wl(case)
+    dw = DevWorkload(wl)
+    L, dL = wl.layers[0], dw.layers[0]
+    got = C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP4, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc)
+    torch.cuda.synchronize()
+    ref = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, synth.Q_FP4)
+    _full_rows_equal(got, ref, wl)
+    # deterministic across runs
+    again = C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP4, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc)
+    assert torch.equal(got.view(torch.int32), again.view(torch.int32))
+
+
+def test_index_score_cand_bitwise():
+    wl = synth.config("chain_c2", n_seq=2, n=30000, Hm=16)
+    dw = DevWorkload(wl)
+    full = wl.layers[0]
+    sc = oracle.index_score(wl, full.q_idx, full.q_sc, full.w, synth.Q_FP4)
+    vis = oracle.row_visible(wl)
+    _, pool, cnt = oracle.block_pool(sc, vis)
+    pool[0, 100:140] = -1  # holes are allowed in a candidate list
+    L = [x for x in wl.layers if x.mode == synth.MODE_REINDEX][0]
+    dL = [x for x in dw.layers if x["index"] == L.index][0]
+    got = C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP4, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc,
+                             cand=dev(pool))
+    torch.cuda.synchronize()
+    ref = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, synth.Q_FP4, cand=pool)
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_index_score_prefill_bitwise(fmt):
+    if fmt == "fp8":
+        wl = synth.config("prefill_c3", tokens=6002, T=150, n_layers=1, Hm=16)
+    else:  # FP4 queries, 9 rows per sequence, ratio 2: the many-query kernel
+        wl = synth.make_workload("pf4", 77, [1500, 2100], 9, [(2, synth.MODE_FULL, False)], ratio=2, Hm=16)
+    dw = DevWorkload(wl)
+    L, dL = wl.layers[0], dw.layers[0]
+    got = C.csa2_index_score(dw.batch, wl.H, L.q_fmt, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc)
+    torch.cuda.synchronize()
+    ref = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, L.q_fmt)
+    _full_rows_equal(got, ref, wl)
+
+
+def _topk_batch(lens, T):
+    qp = [np.arange(n - T, n) for n in lens]
+    return C.Batch(lens, qp), qp
+
+
+@pytest.mark.parametrize("distinct", [4, 1000, 0])
+def test_topk_full_bitwise(distinct):
+    rng = np.random.default_rng(11 + distinct)
+    lens = [3, 511, 512, 513, 20000, 70000]
+    b, qp = _topk_batch(lens, 2)
+    nq = b.total_q
+    stride = max(lens)
+    if distinct:
+        s = (rng.integers(0, distinct, size=(nq, stride)) * 0.5).astype(np.float32)
+    else:  # continuous
+        s = rng.random((nq, stride)).astype(np.float32) * 100
+    vis = np.array([min(n, t + 1) for n, p in zip(lens, qp) for t in p], np.int64)
+    for K in (512, 2048, 17):
+        got = C.csa2_topk(b, dev(s), K)
+        torch.cuda.synchronize()
+        ref = oracle.topk(s, vis, K)
+        assert np.array_equal(got.cpu().numpy(), ref), K
+
+
+def test_topk_all_equal_uses_fallback():
+    # every score equal: the candidate list overflows and the fallback picks the lowest positions
+    lens = [50000, 9000]
+    b, qp = _topk_batch(lens, 1)
+    s = np.full((2, 50000), 3.25, np.float32)
+    got = C.csa2_topk(b, dev(s), 512).cpu().numpy()
+    assert np.array_equal(got[0], np.arange(512)) and np.array_equal(got[1], np.arange(512))
+    vis = np.array([50000, 9000])
+    assert np.array_equal(got, oracle.topk(s, vis, 512))
+
+
+def test_topk_cand_bitwise():
+    rng = np.random.default_rng(5)
+    lens = [100000, 40000]
+    b, qp = _topk_batch(lens, 1)
+    stride = 16384
+    cand = np.full((2, stride), -1, np.int32)
+    cnt = np.array([16384, 7001], np.int32)
+    for r in range(2):
+        cand[r, :cnt[r]] = np.sort(rng.choice(lens[r], cnt[r], replace=False))
+    s = (rng.integers(0, 300, size=(2, stride)) * 0.25).astype(np.float32)
+    got = C.csa2_topk(b, dev(s), 512, cand=dev(cand), cand_count=dev(cnt))
+    ref = oracle.topk(s, cnt.astype(np.int64), 512, cand=cand)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_block_pool_bitwise():
+    rng = np.random.default_rng(8)
+    lens = [7, 16384, 16385, 30001, 90000]
+    b, qp = _topk_batch(lens, 1)
+    s = (rng.integers(0, 5000, size=(len(lens), max(lens))) * 0.125).astype(np.float32)
+    vis = np.array(lens, np.int64)
+    blocks, pool, cnt = C.csa2_block_pool(b, dev(s))
+    rb, rp, rc = oracle.block_pool(s, vis)
+    assert np.array_equal(blocks.cpu().numpy(), rb)
+    assert np.array_equal(pool.cpu().numpy(), rp)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+
+
+def test_gather_dequant_bitwise():
+    wl = synth.config("decode_c1", n_seq=3, n=5000, Hm=16)
+    dw = DevWorkload(wl)
+    rng = np.random.default_rng(2)
+    idx = np.stack([np.sort(rng.choice(5000, 512, replace=False)) for _ in range(3)]).astype(np.int32)
+    idx[1, 400:] = -1
+    got = C.csa2_gather_dequant(dw.batch, dw.kv, dw.kv_sc, dev(idx))
+    assert np.array_equal(got.cpu().numpy(), oracle.gather_dequant(wl, idx))
+
+
+ATTN_CASES = ["decode", "short_ctx", "ragged_t4", "swa_only", "replay", "sparse_idx"]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+def test_sparse_attn_tolerance(case):
+    rng = np.random.default_rng(3)
+    replay = None
+    if case == "decode":
+        wl = synth.config("decode_c1", n_seq=3, n=6000, Hm=64)
+    elif case == "short_ctx":
+        wl = synth.make_workload(case, 5, [40, 100, 1], 1, [(20, synth.MODE_FULL, False)], Hm=32)
+    elif case == "ragged_t4":
+        wl = synth.make_workload(case, 6, [130, 900, 3000], 4, [(20, synth.MODE_FULL, False)], Hm=16)
+    elif case == "swa_only":
+        wl = synth.make_workload(case, 7, [2000, 300], 2, [(0, synth.MODE_SWA_ONLY, False)], Hm=16)
+    elif case == "replay":
+        wl = synth.make_workload(case, 8, [2000, 300], 1, [(20, synth.MODE_FULL, False)], Hm=16)
+        replay = np.array([1950, 0], np.int32)
+    else:
+        wl = synth.make_workload(case, 9, [5000], 1, [(20, synth.MODE_FULL, False)], Hm=16)
+    dw = DevWorkload(wl)
+    nq = wl.total_q
+    vis = oracle.row_visible(wl)
+    idx = np.full((nq, 512), -1, np.int32)
+    if case != "swa_only":
+        for r in range(nq):
+            v = int(vis[r])
+            m = min(v, 512)
+            idx[r, :m] = np.sort(rng.choice(v, m, replace=False)) if v > 0 else []
+    if case == "sparse_idx":
+        idx[0, 10:300:3] = -1  # holes inside the list
+    L, dL = wl.layers[0], dw.layers[0]
+    sw = C.SwaLayout.from_workload(wl, replay_s=replay)
+    out, lse = C.csa2_sparse_attn(dw.batch, dL["q_main"], dw.kv, dw.kv_sc, dev(idx), dL["swa"], sw, SCALE)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_attn(wl, L.q_main, idx, L.swa, replay_s=replay)
+    assert_close_attn(out.cpu().numpy(), ro, case)
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=1e-4, atol=1e-4)
+
+
+CHAIN_CASES = {
+    "c2_small": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16),
+    "c4_small": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16),
+    "c3_small": lambda: synth.config("prefill_c3", tokens=4000, T=96, Hm=16),
+    "encoder_group": lambda: synth.make_workload("enc", 12, [700, 2500], 3, [(0, synth.MODE_SWA_ONLY, False),
+                                                                             (2, synth.MODE_FULL, False),
+                                                                             (3, synth.MODE_REUSE, False),
+                                                                             (4, synth.MODE_REINDEX, False)],
+                                                 ratio=2, Hm=16,
+                                                 q_pos=[np.array([1390, 1395, 1399]), np.array([4000, 4990, 4999])]),
+}
+
+
+@pytest.mark.parametrize("case", list(CHAIN_CASES))
+def test_layer_chain_matches_oracle(case):
+    wl = CHAIN_CASES[case]()
+    dw = DevWorkload(wl)
+    outs, (pb, pp, pc), _ = run_chain(dw)
+    torch.cuda.synchronize()
+    ref = oracle.layer_chain(wl)
+    for o, r in zip(outs, ref):
+        assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"layer {r['layer']} indices"
+        assert_close_attn(o["out"].cpu().numpy(), r["out"], f"layer {r['layer']}")
+        np.testing.assert_allclose(o["lse"].cpu().numpy(), r["lse"], rtol=1e-4, atol=1e-4)
+        if "pool_pos" in r:
+            assert np.array_equal(pb.cpu().numpy(), r["blocks"])
+            assert np.array_equal(pp.cpu().numpy(), r["pool_pos"])
+            assert np.array_equal(pc.cpu().numpy(), r["pool_count"])
+
+
+def test_layer_chain_equals_composition():
+    """The chain's indices and outputs equal those of the individual calls."""
+    wl = synth.config("chain_c2", n_seq=2, n=20000, Hm=16,
+                      schedule=[(20, synth.MODE_FULL, True), (21, synth.MODE_REUSE, False),
+                                (24, synth.MODE_REINDEX, False)])
+    dw = DevWorkload(wl)
+    outs, (pb, pp, pc), _ = run_chain(dw)
+    b = dw.batch
+    f, r = dw.layers[0], dw.layers[2]
+    sc = C.csa2_index_score(b, 64, 0, f["q_idx"], f["q_sc"], f["w"], dw.k_idx, dw.k_sc)
+    idx20 = C.csa2_topk(b, sc, 512)
+    blocks, pool, cnt = C.csa2_block_pool(b, sc)
+    psc = C.csa2_index_score(b, 64, 0, r["q_idx"], r["q_sc"], r["w"], dw.k_idx, dw.k_sc, cand=pool)
+    idx24 = C.csa2_topk(b, psc, 512, cand=pool, cand_count=cnt)
+    o20, _ = C.csa2_sparse_attn(b, f["q_main"], dw.kv, dw.kv_sc, idx20, f["swa"], dw.swa, SCALE)
+    o21, _ = C.csa2_sparse_attn(b, dw.layers[1]["q_main"], dw.kv, dw.kv_sc, idx20, dw.layers[1]["swa"], dw.swa, SCALE)
+    o24, _ = C.csa2_sparse_attn(b, r["q_main"], dw.kv, dw.kv_sc, idx24, r["swa"], dw.swa, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0]["idx"], idx20) and torch.equal(outs[2]["idx"], idx24)
+    assert torch.equal(pp, pool) and torch.equal(pc, cnt) and torch.equal(pb, blocks)
+    assert torch.equal(outs[0]["out"], o20) and torch.equal(outs[1]["out"], o21) and torch.equal(outs[2]["out"], o24)
