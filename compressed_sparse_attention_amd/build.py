@@ -22,6 +22,8 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
     # packed FP32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the epilogues read them without v_accvgpr_read copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -72,8 +72,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         i32, i64, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         B, S = ctypes.POINTER(csa2_batch), ctypes.POINTER(csa2_swa_layout)
-        L.csa2_index_score.argtypes = [B, i32, i32, _vp, _vp, _vp, _vp, _vp, _vp, i32, _vp, i64, _vp]
-        L.csa2_topk.argtypes = [B, _vp, i64, _vp, i32, _vp, i32, _vp, _vp, sz, _vp]
+        L.csa2_index_score.argtypes = [B, i32, i32, _vp, _vp, _vp, _vp, _vp, _vp, i32, _vp, i64, _vp, _vp]
+        L.csa2_topk.argtypes = [B, _vp, i64, _vp, i32, _vp, i32, _vp, _vp, _vp, sz, _vp]
         L.csa2_block_pool.argtypes = [B, _vp, i64, i32, i32, _vp, _vp, _vp, _vp, sz, _vp]
         L.csa2_gather_dequant.argtypes = [B, _vp, _vp, _vp, i32, _vp, _vp]
         L.csa2_sparse_attn.argtypes = [B, i32, _vp, _vp, _vp, _vp, i32, _vp, S, f32, _vp, _vp, _vp, sz, _vp]
@@ -166,6 +166,14 @@ class SwaLayout:
         return cls(wl.W, wl.swa_row_off, wl.swa_pos0, wl.swa_len, replay_s, device)
 
 
+HIST_BINS = 4096
+
+
+def hist_buffer(batch, device="cuda"):
+    """A zeroed [total_q][4096] histogram buffer for csa2_index_score / csa2_topk."""
+    return torch.zeros((batch.total_q, HIST_BINS), dtype=torch.int32, device=device)
+
+
 def workspace(nbytes, device="cuda"):
     """A 256-byte aligned workspace tensor (torch's allocator aligns to 512 B)."""
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
@@ -175,7 +183,7 @@ def csa2_workspace_size(which, batch, K=512, max_blocks=2048, n_layers=1):
     return int(lib().csa2_workspace_size(which, ctypes.byref(batch.c), K, max_blocks, n_layers))
 
 
-def csa2_index_score(batch, H, q_fmt, q, q_sc, w, k_fp4, k_sc, cand=None, scores=None, stream=None):
+def csa2_index_score(batch, H, q_fmt, q, q_sc, w, k_fp4, k_sc, cand=None, scores=None, hist=None, stream=None):
     if cand is None:
         stride = batch.max_entries
         cstride = 0
@@ -185,19 +193,20 @@ def csa2_index_score(batch, H, q_fmt, q, q_sc, w, k_fp4, k_sc, cand=None, scores
     if scores is None:
         scores = torch.empty((batch.total_q, max(stride, 1)), dtype=torch.float32, device=q.device)
     st = lib().csa2_index_score(ctypes.byref(batch.c), H, q_fmt, _ptr(q), _ptr(q_sc), _ptr(w), _ptr(k_fp4),
-                                _ptr(k_sc), _ptr(cand), cstride, _ptr(scores), scores.shape[1], _stream(stream))
+                                _ptr(k_sc), _ptr(cand), cstride, _ptr(scores), scores.shape[1], _ptr(hist),
+                                _stream(stream))
     _check(st, "csa2_index_score")
     return scores
 
 
-def csa2_topk(batch, scores, K, cand=None, cand_count=None, idx=None, ws=None, stream=None):
+def csa2_topk(batch, scores, K, cand=None, cand_count=None, hist=None, idx=None, ws=None, stream=None):
     if idx is None:
         idx = torch.empty((batch.total_q, K), dtype=torch.int32, device=scores.device)
     if ws is None:
         ws = workspace(csa2_workspace_size(CSA2_WS_TOPK, batch, K), scores.device)
     st = lib().csa2_topk(ctypes.byref(batch.c), _ptr(scores), scores.shape[1], _ptr(cand),
-                         0 if cand is None else cand.shape[1], _ptr(cand_count), K, _ptr(idx), _ptr(ws), ws.numel(),
-                         _stream(stream))
+                         0 if cand is None else cand.shape[1], _ptr(cand_count), K, _ptr(hist), _ptr(idx), _ptr(ws),
+                         ws.numel(), _stream(stream))
     _check(st, "csa2_topk")
     return idx
 

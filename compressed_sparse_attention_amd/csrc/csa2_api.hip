@@ -140,7 +140,7 @@ CSA2_API size_t csa2_workspace_size(int32_t which, const csa2_batch* batch, int3
 CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_t q_fmt, const void* q,
                                       const uint8_t* q_sc, const float* w, const uint8_t* k_fp4,
                                       const uint8_t* k_sc, const int32_t* cand, int32_t cand_stride,
-                                      float* scores, int64_t score_stride, hipStream_t stream) {
+                                      float* scores, int64_t score_stride, uint32_t* hist, hipStream_t stream) {
     Geometry g;
     csa2_status st = batch_geometry(batch, &g);
     if (st) return st;
@@ -153,14 +153,16 @@ CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_
     } else if (score_stride < g.max_entries || score_stride < 1) {
         return CSA2_ERR_INVALID_ARG;
     }
-    ScoreLaunch a{batch, g, H, q_fmt, (const uint8_t*)q, q_sc, w, k_fp4, k_sc, cand, cand_stride, scores, score_stride};
+    if (hist && (q_fmt != CSA2_Q_FP4 || (!cand && g.max_q_per_seq > 4))) return CSA2_ERR_UNSUPPORTED;
+    ScoreLaunch a{batch, g, H, q_fmt, (const uint8_t*)q, q_sc, w, k_fp4, k_sc, cand, cand_stride, scores, score_stride,
+                  hist};
     hipError_t e = launch_index_score(a, stream);
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
 
 CSA2_API csa2_status csa2_topk(const csa2_batch* batch, const float* scores, int64_t score_stride,
                                const int32_t* cand, int32_t cand_stride, const int32_t* cand_count, int32_t K,
-                               int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+                               const uint32_t* hist, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
     Geometry g;
     csa2_status st = batch_geometry(batch, &g);
     if (st) return st;
@@ -188,6 +190,7 @@ CSA2_API csa2_status csa2_topk(const csa2_batch* batch, const float* scores, int
     a.K = K;
     a.idx = idx;
     a.ws = ws;
+    a.hist = hist;
     hipError_t e = launch_topk(a, stream);
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
@@ -314,9 +317,13 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
 
     hipError_t e;
     const int64_t nidx = (int64_t)g.total_q * p->K;
-    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((nidx + 255) / 256 < 2048 ? (nidx + 255) / 256 : 2048)), dim3(256), 0,
-                       stream, idx_empty, nidx, -1);
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e);
+    bool any_swa_only = false;
+    for (int l = 0; l < n_layers; ++l) any_swa_only |= layers[l].mode == CSA2_MODE_SWA_ONLY;
+    if (any_swa_only) {  // the empty index list SWA-only layers attend with
+        hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((nidx + 255) / 256 < 2048 ? (nidx + 255) / 256 : 2048)),
+                           dim3(256), 0, stream, idx_empty, nidx, -1);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e);
+    }
 
     const csa2_layer* src = nullptr;  // latest Full layer (main KV + indexer K)
     bool pool_built = false;
@@ -330,10 +337,33 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                 pool_built = false;
             }
             const bool on_pool = !full && pool_built;
+            // the score kernel builds the Top-K histogram when it can (FP4 queries,
+            // at most 4 rows per sequence or a candidate list); the Top-K pass then
+            // starts from it.  A pool built from these scores needs its own pass.
+            const bool fused = L.q_fmt == CSA2_Q_FP4 && (on_pool || g.max_q_per_seq <= 4);
+            if (fused && (e = clear_topk_ws(topk_ws, g.total_q, true, stream)) != hipSuccess) return hip_fail(e);
             ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, src->k_fp4, src->k_sc,
                            on_pool ? pp : nullptr, on_pool ? pool_stride : 0, on_pool ? pscores : scores,
-                           on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1)};
+                           on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1),
+                           fused ? topk_ws_hist(topk_ws) : nullptr};
             if ((e = launch_index_score(sa, stream)) != hipSuccess) return hip_fail(e);
+            TopkLaunch ta{};
+            ta.b = batch;
+            ta.g = g;
+            ta.scores = on_pool ? pscores : scores;
+            ta.stride = on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1);
+            ta.max_slots = on_pool ? pool_stride : g.max_entries;
+            ta.cand = on_pool ? pp : nullptr;
+            ta.cand_stride = on_pool ? pool_stride : 0;
+            ta.cand_count = on_pool ? pc : nullptr;
+            ta.block_mode = 0;
+            ta.block = 1;
+            ta.K = p->K;
+            ta.idx = idx_cur;
+            ta.ws = topk_ws;
+            ta.hist = fused ? topk_ws_hist(topk_ws) : nullptr;
+            if ((e = launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
+            // the pool runs its own selection in the same workspace: after the Top-K
             if (full && (L.flags & CSA2_LAYER_BUILD_POOL)) {
                 PoolLaunch pa{};
                 pa.b = batch;
@@ -351,21 +381,6 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                 if ((e = launch_block_pool(pa, stream)) != hipSuccess) return hip_fail(e);
                 pool_built = true;
             }
-            TopkLaunch ta{};
-            ta.b = batch;
-            ta.g = g;
-            ta.scores = on_pool ? pscores : scores;
-            ta.stride = on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1);
-            ta.max_slots = on_pool ? pool_stride : g.max_entries;
-            ta.cand = on_pool ? pp : nullptr;
-            ta.cand_stride = on_pool ? pool_stride : 0;
-            ta.cand_count = on_pool ? pc : nullptr;
-            ta.block_mode = 0;
-            ta.block = 1;
-            ta.K = p->K;
-            ta.idx = idx_cur;
-            ta.ws = topk_ws;
-            if ((e = launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
         } else if (L.mode == CSA2_MODE_SWA_ONLY) {
             use_idx = idx_empty;
         }

@@ -61,6 +61,7 @@ struct ScoreLaunch {
     int cand_stride;
     float* scores;
     int64_t stride;
+    uint32_t* hist;             // nullable: [total_q][kHistBins], zeroed by the caller
 };
 hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s);
 
@@ -78,8 +79,13 @@ struct TopkLaunch {
     int K;
     int32_t* idx;               // [total_q][K]
     void* ws;
+    const uint32_t* hist;       // nullable: histogram of the scores made with them (skips the histogram pass)
 };
 size_t topk_ws_bytes(int total_q);
+// zero the histogram and row state of a Top-K workspace (done by launch_topk
+// itself unless the caller filled the histogram beforehand)
+hipError_t clear_topk_ws(void* ws, int total_q, bool hist_too, hipStream_t s);
+uint32_t* topk_ws_hist(void* ws);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 
 struct PoolLaunch {

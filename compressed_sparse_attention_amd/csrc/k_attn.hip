@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     __shared__ __attribute__((aligned(16))) uint16_t kl[KB * LROW];
     __shared__ float sl[HG][KB];
     __shared__ int kvalid[KB];
+    __shared__ int32_t kidx[kMaxK];
     __shared__ int nsel_sh;
 
     // the n_hg head groups of one row share an XCD (blocks are dealt to XCDs round-robin)
@@ -100,14 +101,18 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     int64_t u_lo = t - W + 1;
     u_lo = u_lo > s_rep ? u_lo : s_rep;
     const int n_swa = t >= u_lo ? (int)(t - u_lo + 1) : 0;
-    const int32_t* irow = idx + (int64_t)row * K;
+    const int32_t* irow = idx + (int64_t)row * K;  // staged into kidx below
 
     if (tid == 0) nsel_sh = 0;
     __syncthreads();
     {
         int last = 0;
-        for (int s = tid; s < K; s += 256)
-            if (irow[s] >= 0) last = s + 1;
+        for (int s = tid; s < K; s += 256) {
+            int32_t j = irow[s];
+            j = (j >= 0 && j < n_ent) ? j : -1;  // out-of-range entries read as empty
+            kidx[s] = j;
+            if (j >= 0) last = s + 1;
+        }
         if (last) atomicMax(&nsel_sh, last);
     }
     __syncthreads();
@@ -122,6 +127,9 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
         const uint16_t* qr = q + ((int64_t)row * Hm + hq) * 512 + 8 * lg;
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, ld16(qr + 32 * ks));
+        // wait for Q here (vmcnt 0, other counters untouched) so that the loop
+        // below never waits on memory except for the block it stages
+        __builtin_amdgcn_s_waitcnt(0x0F70);
     }
     v4f O[8];
 #pragma unroll
@@ -131,27 +139,42 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     // fp32 weights (it gives the log-sum-exp)
     float m_run = -INFINITY, l_run = 0.0f, l_lse = 0.0f;
 
+    // this thread stages key tid/4 of each block, channels 128*(tid%4) .. +128;
+    // the main-KV part of the next block is fetched into registers while the
+    // current block computes
+    const int skey = tid >> 2, part = tid & 3;
+    v4i pc[4];
+    uint32_t psc = 0;
+    auto fetch = [&](int blk) {
+        const int vk = KB * blk + skey;
+        if (vk < n_sel && blk < n_blocks) {
+            const int32_t j = kidx[vk];
+            if (j >= 0) {
+                const int64_t e = e0 + j;
+                const uint8_t* src = kv + e * 256 + 64 * part;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pc[i] = ld16(src + 16 * i);
+                psc = *reinterpret_cast<const uint32_t*>(kv_sc + e * 16 + 4 * part);
+            }
+        }
+    };
+    fetch(0);
+
     for (int blk = 0; blk < n_blocks; ++blk) {
-        // 1) stage 64 keys: thread -> key tid/4, channels 128*(tid%4) .. +128
+        // 1) stage 64 keys
         {
-            const int key = tid >> 2, part = tid & 3;
-            const int vk = KB * blk + key;
-            uint16_t* dst = kl + key * LROW + 128 * part;
+            const int vk = KB * blk + skey;
+            uint16_t* dst = kl + skey * LROW + 128 * part;
             int valid = 0;
             if (vk < n_sel) {
-                const int32_t j = irow[vk];
-                if (j >= 0 && j < n_ent) {
+                if (kidx[vk] >= 0) {
                     valid = 1;
-                    const int64_t e = e0 + j;
-                    const uint8_t* src = kv + e * 256 + 64 * part;
-                    const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(kv_sc + e * 16 + 4 * part);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {  // 32 channels per scale
-                        const v4i c = ld16(src + 16 * i);
-                        const float sc = e8m0_f32((sc4 >> (8 * i)) & 255u);
+                        const float sc = e8m0_f32((psc >> (8 * i)) & 255u);
 #pragma unroll
                         for (int d = 0; d < 4; ++d)
-                            *reinterpret_cast<v4i*>(dst + 32 * i + 8 * d) = fp4x8_to_bf16((uint32_t)c[d], sc);
+                            *reinterpret_cast<v4i*>(dst + 32 * i + 8 * d) = fp4x8_to_bf16((uint32_t)pc[i][d], sc);
                     }
                 }
             } else if (vk < n_keys) {
@@ -159,15 +182,19 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
                 const int64_t u = u_lo + (vk - n_sel);
                 const int64_t r = swa_row_off[b] + (u - swa_pos0[b]);
                 const uint16_t* src = swa + r * 512 + 128 * part;
+                v4i tmp[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = ld16(src + 8 * i);
+                for (int i = 0; i < 16; ++i) tmp[i] = ld16(src + 8 * i);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = tmp[i];
             }
             if (!valid) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = v4i{0, 0, 0, 0};
             }
-            if (part == 0) kvalid[key] = valid;
+            if (part == 0) kvalid[skey] = valid;
         }
+        fetch(blk + 1);
         __syncthreads();
 
         // 2) S = Q K^T for keys 16*wave .. +16: lane gets S[head 4lg+v][key 16wave + li]

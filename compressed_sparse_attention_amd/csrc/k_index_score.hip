@@ -70,6 +70,24 @@ __device__ __forceinline__ float head_sum(v16f (&acc)[NMT][2], const float* __re
     return s;
 }
 
+// Histogram of the written scores over bits 30..19 (the bins the Top-K pass
+// starts from), kept in LDS per query row and flushed with one global atomic
+// per non-empty bin.  Negative scores (only possible with negative head
+// weights) count in bin 0, as the Top-K pass orders them.
+__device__ __forceinline__ uint32_t score_bin(float s) {
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? 0u : (u >> 19);
+}
+
+__device__ __forceinline__ void hist_clear(uint32_t* h, int nbins) {
+    for (int i = threadIdx.x; i < nbins; i += blockDim.x) h[i] = 0;
+}
+
+__device__ __forceinline__ void hist_flush(const uint32_t* h, uint32_t* __restrict__ g) {
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
+        if (h[i]) atomicAdd(&g[i], h[i]);
+}
+
 // ---------------------------------------------------------------------------
 // Decode scan: every sequence has at most TQ query rows (1 for plain decode, 4
 // for the speculative-verify shape); they share one pass over the sequence's
@@ -77,15 +95,17 @@ __device__ __forceinline__ float head_sum(v16f (&acc)[NMT][2], const float* __re
 // FP4 x FP4; channel c of a row sits at (lane half g, k-step ks, nibble e)
 // with c = 64g + 32ks + e for both operands.
 // ---------------------------------------------------------------------------
-template <int H, int TQ>
+template <int H, int TQ, bool HIST>
 __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_sc,
                                                       const float* __restrict__ w, const uint8_t* __restrict__ k,
                                                       const uint8_t* __restrict__ k_sc,
                                                       const int64_t* __restrict__ entry_off,
                                                       const int32_t* __restrict__ q_off,
                                                       const int32_t* __restrict__ q_pos, int ratio,
-                                                      float* __restrict__ scores, int64_t stride, int chunk) {
+                                                      float* __restrict__ scores, int64_t stride, int chunk,
+                                                      uint32_t* __restrict__ hist) {
     constexpr int NMT = H / 32;
+    __shared__ uint32_t hl[HIST ? TQ * kHistBins : 1];
     const int b = blockIdx.y;
     const int64_t e0 = entry_off[b];
     const int64_t n = entry_off[b + 1] - e0;
@@ -97,6 +117,7 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     if (nq <= 0) return;  // a sequence without query rows has no scores
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5, li = lane & 31;
+    if (HIST) hist_clear(hl, TQ * kHistBins);
 
     v8i A[TQ][NMT][2];
     int SA[TQ][NMT];
@@ -113,19 +134,35 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
             SA[t][mt] = q_sc[(int64_t)row * H + 32 * mt + li];
         }
     }
+    if (HIST) __syncthreads();
 
-    for (int64_t p0 = c0 + 64 * wave; p0 < c1; p0 += 256) {
-        v8i B[2][2];
+    // software pipeline: the indexer K of the next tile is in flight while
+    // the current tile computes
+    v4i Bn[2][2];
+    int ekn = 127;
+    auto fetch = [&](int64_t p0) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             int64_t j = p0 + 32 * nt + li;
             j = j < n ? j : n - 1;
             const uint8_t* kr = k + (e0 + j) * 64 + 32 * g;
-            B[nt][0] = widen(ld16(kr));
-            B[nt][1] = widen(ld16(kr + 16));
+            Bn[nt][0] = ld16(kr);
+            Bn[nt][1] = ld16(kr + 16);
         }
         const int64_t jl = p0 + lane;
-        const int ek = jl < n ? (int)k_sc[e0 + jl] : 127;
+        ekn = jl < n ? (int)k_sc[e0 + jl] : 127;
+    };
+    int64_t p0 = c0 + 64 * wave;
+    if (p0 < c1) fetch(p0);
+    for (; p0 < c1; p0 += 256) {
+        v8i B[2][2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) B[nt][ks] = widen(Bn[nt][ks]);
+        const int ek = ekn;
+        if (p0 + 256 < c1) fetch(p0 + 256);
+        const int64_t jl = p0 + lane;
 #pragma unroll
         for (int t = 0; t < TQ; ++t) {
             if (t >= nq) break;
@@ -139,8 +176,17 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
                     for (int ks = 0; ks < 2; ++ks) acc[mt][nt] = mfma_scaled(A[t][mt][ks], B[nt][ks], acc[mt][nt], SA[t][mt], 4);
                 }
             const float s = head_sum<NMT>(acc, w + (int64_t)(r0 + t) * H);
-            if (jl < n) scores[(int64_t)(r0 + t) * stride + jl] = jl < vis[t] ? ldexpf(s, ek - 127) : -INFINITY;
+            if (jl < n) {
+                const bool visible = jl < vis[t];
+                const float sc = visible ? ldexpf(s, ek - 127) : -INFINITY;
+                scores[(int64_t)(r0 + t) * stride + jl] = sc;
+                if (HIST && visible) atomicAdd(&hl[t * kHistBins + score_bin(sc)], 1u);
+            }
         }
+    }
+    if (HIST) {
+        __syncthreads();
+        for (int t = 0; t < TQ && t < nq; ++t) hist_flush(hl + t * kHistBins, hist + (int64_t)(r0 + t) * kHistBins);
     }
 }
 
@@ -148,7 +194,7 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
 // Candidate (Reindex) scoring: slot s of row r scores entry cand[r][s].
 // Grid (slot chunks of 1024, total_q).  Same operand mapping as the decode scan.
 // ---------------------------------------------------------------------------
-template <int H>
+template <int H, bool HIST>
 __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_sc,
                                                     const float* __restrict__ w, const uint8_t* __restrict__ k,
                                                     const uint8_t* __restrict__ k_sc,
@@ -156,9 +202,11 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ 
                                                     const int32_t* __restrict__ row_seq,
                                                     const int32_t* __restrict__ q_pos, int ratio,
                                                     const int32_t* __restrict__ cand, int cand_stride,
-                                                    float* __restrict__ scores, int64_t stride) {
+                                                    float* __restrict__ scores, int64_t stride,
+                                                    uint32_t* __restrict__ hist) {
     constexpr int NMT = H / 32;
     constexpr int CH = 1024;
+    __shared__ uint32_t hl[HIST ? kHistBins : 1];
     const int row = blockIdx.y;
     const int s0 = blockIdx.x * CH;
     if (s0 >= cand_stride) return;
@@ -175,6 +223,7 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ 
         for (int s = s0 + threadIdx.x; s < s1; s += 256) srow[s] = -INFINITY;
         return;
     }
+    if (HIST) hist_clear(hl, kHistBins);
     v8i A[NMT][2];
     int SA[NMT];
 #pragma unroll
@@ -184,6 +233,7 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ 
         A[mt][1] = widen(ld16(qr + 16));
         SA[mt] = q_sc[(int64_t)row * H + 32 * mt + li];
     }
+    if (HIST) __syncthreads();
     for (int p0 = s0 + 64 * wave; p0 < s1; p0 += 256) {
         v8i B[2][2];
 #pragma unroll
@@ -209,7 +259,17 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ 
                 for (int ks = 0; ks < 2; ++ks) acc[mt][nt] = mfma_scaled(A[mt][ks], B[nt][ks], acc[mt][nt], SA[mt], 4);
             }
         const float sc = head_sum<NMT>(acc, w + (int64_t)row * H);
-        if (sl < s1) srow[sl] = ok ? ldexpf(sc, ek - 127) : -INFINITY;
+        if (sl < s1) {
+            const float v = ok ? ldexpf(sc, ek - 127) : -INFINITY;
+            srow[sl] = v;
+            // the Top-K pass over a candidate list takes its first cand_count
+            // slots, which are the non-empty ones of a pool list
+            if (HIST && ok) atomicAdd(&hl[score_bin(v)], 1u);
+        }
+    }
+    if (HIST) {
+        __syncthreads();
+        hist_flush(hl, hist + (int64_t)row * kHistBins);
     }
 }
 
@@ -474,24 +534,31 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
     const csa2_batch* b = a.b;
     if (a.cand) {
         dim3 grid((a.cand_stride + 1023) / 1024, a.g.total_q);
-        if (a.H == 64)
-            hipLaunchKernelGGL((k_score_cand<64>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc, b->d_entry_off,
-                               b->d_row_seq, b->d_q_pos, b->ratio, a.cand, a.cand_stride, a.scores, a.stride);
-        else
-            hipLaunchKernelGGL((k_score_cand<32>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc, b->d_entry_off,
-                               b->d_row_seq, b->d_q_pos, b->ratio, a.cand, a.cand_stride, a.scores, a.stride);
+#define CSA2_CAND(HH, HI)                                                                                        \
+    hipLaunchKernelGGL((k_score_cand<HH, HI>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,            \
+                       b->d_entry_off, b->d_row_seq, b->d_q_pos, b->ratio, a.cand, a.cand_stride, a.scores,      \
+                       a.stride, a.hist)
+        if (a.H == 64) {
+            if (a.hist) CSA2_CAND(64, true); else CSA2_CAND(64, false);
+        } else {
+            if (a.hist) CSA2_CAND(32, true); else CSA2_CAND(32, false);
+        }
+#undef CSA2_CAND
         return hipGetLastError();
     }
     if (a.q_fmt == CSA2_Q_FP4 && a.g.max_q_per_seq <= 4) {
         const int chunk = 4096;
         dim3 grid((unsigned)((a.g.max_entries + chunk - 1) / chunk), a.g.n_seq);
-#define CSA2_DEC(HH, TT)                                                                                         \
-    hipLaunchKernelGGL((k_score_decode<HH, TT>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,          \
-                       b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, chunk)
+#define CSA2_DEC(HH, TT, HI)                                                                                     \
+    hipLaunchKernelGGL((k_score_decode<HH, TT, HI>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,      \
+                       b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, chunk, a.hist)
+        const bool one = a.g.max_q_per_seq <= 1;
         if (a.H == 64) {
-            if (a.g.max_q_per_seq <= 1) CSA2_DEC(64, 1); else CSA2_DEC(64, 4);
+            if (a.hist) { if (one) CSA2_DEC(64, 1, true); else CSA2_DEC(64, 4, true); }
+            else { if (one) CSA2_DEC(64, 1, false); else CSA2_DEC(64, 4, false); }
         } else {
-            if (a.g.max_q_per_seq <= 1) CSA2_DEC(32, 1); else CSA2_DEC(32, 4);
+            if (a.hist) { if (one) CSA2_DEC(32, 1, true); else CSA2_DEC(32, 4, true); }
+            else { if (one) CSA2_DEC(32, 1, false); else CSA2_DEC(32, 4, false); }
         }
 #undef CSA2_DEC
         return hipGetLastError();

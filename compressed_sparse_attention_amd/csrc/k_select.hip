@@ -65,6 +65,8 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// Histogram of score bits 30..19 per row.  Each thread keeps 8 loads in
+// flight before it touches the shared histogram.
 __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ scores, int64_t stride, RowSrc rs,
                                               uint32_t* __restrict__ hist) {
     __shared__ uint32_t h[kHistBins];
@@ -76,85 +78,136 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ scores, 
     for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
     __syncthreads();
     const float* sr = scores + (int64_t)row * stride;
-    for (int64_t s = s0 + threadIdx.x; s < s1; s += 256) atomicAdd(&h[score_key(sr[s]) >> 19], 1u);
+    for (int64_t base = s0; base < s1; base += 256 * 8) {
+        uint32_t key[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t s = base + threadIdx.x + 256 * u;
+            key[u] = s < s1 ? score_key(sr[s]) : 0xFFFFFFFFu;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (key[u] != 0xFFFFFFFFu) atomicAdd(&h[key[u] >> 19], 1u);
+    }
     __syncthreads();
     uint32_t* gh = hist + (int64_t)row * kHistBins;
     for (int i = threadIdx.x; i < kHistBins; i += 256)
         if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// One workgroup per row: find the bin holding the kk-th largest key.
-__global__ __launch_bounds__(256) void k_thresh(const uint32_t* __restrict__ hist, RowSrc rs, int K,
-                                                RowSel* __restrict__ sel) {
-    __shared__ uint32_t part[256];
-    const int row = blockIdx.x;
-    const int64_t n = row_n(rs, row);
-    const uint32_t kk = (uint32_t)(n < K ? n : K);
-    const uint32_t* h = hist + (int64_t)row * kHistBins;
+// Block-wide: the bin that holds the kk-th largest key of the row (every
+// thread returns it); kHistBins when kk == 0.
+// Inclusive scan of one value per thread over a 256-thread workgroup: a
+// shuffle scan inside each wave, then the wave totals through LDS.
+__device__ uint32_t block_scan_256(uint32_t v, uint32_t* wtot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+    }
+    if (lane == 63) wtot[wave] = v;
+    __syncthreads();
+    for (int w2 = 0; w2 < wave; ++w2) v += wtot[w2];
+    return v;
+}
+
+// Block-wide: the bin that holds the kk-th largest key of the row (every
+// thread returns it); kHistBins when kk == 0.
+__device__ uint32_t threshold_bin(const uint32_t* __restrict__ h, uint32_t kk, uint32_t* wtot, uint32_t* found) {
     const int t = threadIdx.x;
     // thread t owns bins [4096 - 16(t+1), 4096 - 16t), i.e. thread 0 the top bins
     const int hi = kHistBins - 16 * t;
+    uint32_t c[16];
     uint32_t s = 0;
-    for (int i = 1; i <= 16; ++i) s += h[hi - i];
-    part[t] = s;
-    if (t == 0) {
-        sel[row].n = (uint32_t)n;
-        sel[row].kk = kk;
-        sel[row].cnt = 0;
-        sel[row].bin = kk == 0 ? (uint32_t)kHistBins : 0u;  // overwritten below by the bin that holds the kk-th key
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        c[i] = h[hi - 1 - i];
+        s += c[i];
     }
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
-        const uint32_t v = t >= off ? part[t - off] : 0;
-        __syncthreads();
-        part[t] += v;
-        __syncthreads();
-    }
-    if (kk == 0) return;
-    const uint32_t before = t ? part[t - 1] : 0;
-    if (before < kk && kk <= part[t]) {
-        uint32_t c = before;
-        for (int i = 1; i <= 16; ++i) {
-            c += h[hi - i];
-            if (c >= kk) {
-                sel[row].bin = (uint32_t)(hi - i);
+    if (t == 0) *found = kk == 0 ? (uint32_t)kHistBins : 0u;
+    const uint32_t incl = block_scan_256(s, wtot);
+    const uint32_t before = incl - s;
+    if (kk > 0 && before < kk && kk <= incl) {
+        uint32_t acc = before;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            acc += c[i];
+            if (acc >= kk) {
+                *found = (uint32_t)(hi - 1 - i);
                 break;
             }
         }
     }
+    __syncthreads();
+    return *found;
 }
 
+// Candidates: every slot whose bin is at or above the threshold bin goes to
+// the row's candidate list.  A workgroup first gathers its candidates in LDS
+// and then reserves room in the row's list with a single atomic (a returning
+// atomic per wave on one counter would serialise).  A workgroup with more
+// candidates than its LDS list holds marks the row as overflowed, which sends
+// the row to the exact fallback of k_final.  Every workgroup derives the
+// threshold bin from the finished histogram itself; the first workgroup of
+// each row records it for the final pass.
+constexpr int kLocalCand = 2048;
+
 __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ scores, int64_t stride, RowSrc rs,
-                                                 RowSel* __restrict__ sel, uint64_t* __restrict__ cand_buf) {
+                                                 const uint32_t* __restrict__ hist, int K, RowSel* __restrict__ sel,
+                                                 uint64_t* __restrict__ cand_buf) {
+    __shared__ uint32_t part[4];
+    __shared__ uint32_t found;
+    __shared__ uint64_t lc[kLocalCand];
+    __shared__ uint32_t lcount, gbase;
     const int row = blockIdx.y;
     const int64_t n = row_n(rs, row);
     const int64_t s0 = (int64_t)blockIdx.x * kHChunk;
-    if (s0 >= n) return;
-    const uint32_t bin = sel[row].bin;
-    if (bin >= (uint32_t)kHistBins) return;
-    const int64_t s1 = s0 + kHChunk < n ? s0 + kHChunk : n;
+    if (s0 >= n && blockIdx.x != 0) return;
     const float* sr = scores + (int64_t)row * stride;
-    uint64_t* cb = cand_buf + (int64_t)row * kCandCap;
+    const int64_t s1 = s0 + kHChunk < n ? s0 + kHChunk : n;
+    // issue this thread's loads before the threshold search
+    uint32_t key[kHChunk / 256];
+#pragma unroll
+    for (int u = 0; u < kHChunk / 256; ++u) {
+        const int64_t s = s0 + threadIdx.x + 256 * u;
+        key[u] = s < s1 ? score_key(sr[s]) : 0u;
+    }
+    if (threadIdx.x == 0) lcount = 0;
+    const uint32_t kk = (uint32_t)(n < K ? n : K);
+    const uint32_t bin = threshold_bin(hist + (int64_t)row * kHistBins, kk, part, &found);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        sel[row].n = (uint32_t)n;
+        sel[row].kk = kk;
+        sel[row].bin = bin;
+    }
+    if (bin >= (uint32_t)kHistBins || s0 >= n) return;
     const int lane = threadIdx.x & 63;
-    for (int64_t base = s0; base < s1; base += 256) {
-        const int64_t s = base + threadIdx.x;
-        uint32_t key = 0;
-        bool take = false;
-        if (s < s1) {
-            key = score_key(sr[s]);
-            take = (key >> 19) >= bin;
-        }
+#pragma unroll
+    for (int u = 0; u < kHChunk / 256; ++u) {
+        const int64_t s = s0 + threadIdx.x + 256 * u;
+        const bool take = s < s1 && (key[u] >> 19) >= bin;
         const uint64_t m = __ballot(take);
         if (m) {
-            uint32_t pos0 = 0;
-            if (lane == 0) pos0 = atomicAdd(&sel[row].cnt, (uint32_t)__popcll(m));
-            pos0 = __shfl(pos0, 0);
+            uint32_t p0 = 0;
+            if (lane == 0) p0 = atomicAdd(&lcount, (uint32_t)__popcll(m));
+            p0 = __shfl(p0, 0);
             if (take) {
-                const uint32_t p = pos0 + (uint32_t)__popcll(m & ((1ull << lane) - 1));
-                if (p < (uint32_t)kCandCap) cb[p] = composite(key, (uint32_t)s);
+                const uint32_t p = p0 + (uint32_t)__popcll(m & ((1ull << lane) - 1));
+                if (p < (uint32_t)kLocalCand) lc[p] = composite(key[u], (uint32_t)s);
             }
         }
     }
+    __syncthreads();
+    const uint32_t cnt = lcount;
+    if (cnt == 0) return;
+    if (threadIdx.x == 0)
+        gbase = atomicAdd(&sel[row].cnt, cnt <= (uint32_t)kLocalCand ? cnt : (uint32_t)kCandCap + 1u);
+    __syncthreads();
+    if (cnt > (uint32_t)kLocalCand) return;  // row overflowed: k_final selects it from the scores
+    uint64_t* cb = cand_buf + (int64_t)row * kCandCap;
+    for (uint32_t i = threadIdx.x; i < cnt; i += 256)
+        if (gbase + i < (uint32_t)kCandCap) cb[gbase + i] = lc[i];
 }
 
 // Radix select helpers over key64 with 8-bit digits from the top.  `count`
@@ -207,118 +260,53 @@ __device__ void radix_step(const uint32_t* hist256, uint32_t* scan256, RadixStat
     __syncthreads();
 }
 
-// Bitonic sort of `cnt` u32 values in LDS, padded to a power of two with 0xFFFFFFFF.
-__device__ void bitonic_sort_u32(uint32_t* a, int npow2) {
-    for (int k = 2; k <= npow2; k <<= 1)
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < npow2; i += blockDim.x) {
-                const int l = i ^ j;
-                if (l > i) {
-                    const uint32_t x = a[i], y = a[l];
-                    const bool up = (i & k) == 0;
-                    if ((x > y) == up) {
-                        a[i] = y;
-                        a[l] = x;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-}
-
 __device__ __forceinline__ int32_t map_slot(const int32_t* cand, int cand_stride, int row, uint32_t slot) {
     return cand ? cand[(int64_t)row * cand_stride + slot] : (int32_t)slot;
 }
 
-__global__ __launch_bounds__(1024) void k_final(RowSel* __restrict__ sel, const uint64_t* __restrict__ cand_buf,
+// One workgroup per row: exact selection of the kk winners by key64 and their
+// output in ascending position order.  Rows whose candidate list fitted are
+// selected from the list in LDS; rows whose list overflowed (heavy ties) are
+// selected from the scores themselves (the same radix select reading the row
+// at every level, then an in-order compaction).
+__global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores, int64_t stride,
+                                                const RowSel* __restrict__ sel, const uint64_t* __restrict__ cand_buf,
                                                 const int32_t* __restrict__ cand, int cand_stride, int K,
                                                 int32_t* __restrict__ idx) {
     __shared__ uint64_t c[kCandCap];
     __shared__ uint32_t winners[kMaxK];
     __shared__ uint32_t hist256[256], scan256[256];
     __shared__ RadixState st;
-    __shared__ uint32_t nwin;
-    __shared__ int found;
-    const int row = blockIdx.x;
-    const uint32_t cnt = sel[row].cnt, kk = sel[row].kk;
-    int32_t* out = idx + (int64_t)row * K;
-    if (cnt > (uint32_t)kCandCap) return;  // handled by the fallback
-    for (int i = threadIdx.x + (int)kk; i < K; i += 1024) out[i] = -1;
-    if (kk == 0) return;
-    for (uint32_t i = threadIdx.x; i < cnt; i += 1024) c[i] = cand_buf[(int64_t)row * kCandCap + i];
-    if (threadIdx.x == 0) {
-        st.prefix = 0;
-        st.shift = 64;
-        st.need = kk;
-        st.done = (cnt == kk);  // every candidate wins
-        nwin = 0;
-    }
-    __syncthreads();
-    while (!st.done) {
-        for (int i = threadIdx.x; i < 256; i += 1024) hist256[i] = 0;
-        __syncthreads();
-        const int sh = st.shift;
-        const uint64_t pf = st.prefix;
-        for (uint32_t i = threadIdx.x; i < cnt; i += 1024) {
-            const uint64_t x = c[i];
-            const bool m = sh >= 64 ? true : ((x >> sh) == pf);
-            if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - 8)) & 255u], 1u);
-        }
-        __syncthreads();
-        radix_step(hist256, scan256, &st, &found);
-    }
-    // winners: key64 >= prefix << shift
-    const int sh = st.shift;
-    const uint64_t pf = st.prefix;
-    for (uint32_t i = threadIdx.x; i < cnt; i += 1024) {
-        const uint64_t x = c[i];
-        const bool win = sh >= 64 ? true : ((x >> sh) >= pf);
-        if (win) {
-            const uint32_t p = atomicAdd(&nwin, 1u);
-            if (p < (uint32_t)kMaxK) winners[p] = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu);
-        }
-    }
-    __syncthreads();
-    int np2 = 1;
-    while (np2 < (int)kk) np2 <<= 1;
-    for (int i = threadIdx.x + (int)kk; i < np2; i += 1024) winners[i] = 0xFFFFFFFFu;
-    __syncthreads();
-    bitonic_sort_u32(winners, np2);
-    for (int i = threadIdx.x; i < (int)kk; i += 1024) out[i] = map_slot(cand, cand_stride, row, winners[i]);
-}
-
-// Rows whose candidate list overflowed: radix select over all slots, reading
-// the scores again at each level, then an in-order compaction.
-__global__ __launch_bounds__(1024) void k_fallback(const float* __restrict__ scores, int64_t stride, RowSrc rs,
-                                                   RowSel* __restrict__ sel, const int32_t* __restrict__ cand,
-                                                   int cand_stride, int K, int32_t* __restrict__ idx) {
-    __shared__ uint32_t hist256[256], scan256[256];
-    __shared__ RadixState st;
+    __shared__ uint32_t nwin, base;
     __shared__ int found;
     __shared__ uint32_t wsum[16];
-    __shared__ uint32_t base;
     const int row = blockIdx.x;
-    if (sel[row].cnt <= (uint32_t)kCandCap) return;
-    const uint32_t kk = sel[row].kk;
+    const uint32_t cnt = sel[row].cnt, kk = sel[row].kk;
     const int64_t n = sel[row].n;
+    const bool from_list = cnt <= (uint32_t)kCandCap;
     const float* sr = scores + (int64_t)row * stride;
     int32_t* out = idx + (int64_t)row * K;
     for (int i = threadIdx.x + (int)kk; i < K; i += 1024) out[i] = -1;
+    if (kk == 0) return;
+    if (from_list)
+        for (uint32_t i = threadIdx.x; i < cnt; i += 1024) c[i] = cand_buf[(int64_t)row * kCandCap + i];
     if (threadIdx.x == 0) {
         st.prefix = 0;
         st.shift = 64;
         st.need = kk;
-        st.done = 0;
+        st.done = from_list && cnt == kk;  // every candidate wins
+        nwin = 0;
         base = 0;
     }
     __syncthreads();
+    const int64_t m_elems = from_list ? (int64_t)cnt : n;
     while (!st.done) {
         for (int i = threadIdx.x; i < 256; i += 1024) hist256[i] = 0;
         __syncthreads();
         const int sh = st.shift;
         const uint64_t pf = st.prefix;
-        for (int64_t s = threadIdx.x; s < n; s += 1024) {
-            const uint64_t x = composite(score_key(sr[s]), (uint32_t)s);
+        for (int64_t i = threadIdx.x; i < m_elems; i += 1024) {
+            const uint64_t x = from_list ? c[i] : composite(score_key(sr[i]), (uint32_t)i);
             const bool m = sh >= 64 ? true : ((x >> sh) == pf);
             if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - 8)) & 255u], 1u);
         }
@@ -327,6 +315,31 @@ __global__ __launch_bounds__(1024) void k_fallback(const float* __restrict__ sco
     }
     const int sh = st.shift;
     const uint64_t pf = st.prefix;
+    if (from_list) {
+        // winners: key64 >= prefix << shift; then sort their slots
+        for (uint32_t i = threadIdx.x; i < cnt; i += 1024) {
+            const uint64_t x = c[i];
+            const bool win = sh >= 64 ? true : ((x >> sh) >= pf);
+            if (win) {
+                const uint32_t p = atomicAdd(&nwin, 1u);
+                if (p < (uint32_t)kMaxK) winners[p] = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu);
+            }
+        }
+        __syncthreads();
+        // ascending output: a winner's rank is the number of winners with a
+        // smaller slot (slots are distinct); every thread reads winners[j] in
+        // lock step, so the reads are LDS broadcasts
+        const int nw = (int)kk;
+        for (int i0 = 0; i0 < nw; i0 += 1024) {
+            const int i = i0 + (int)threadIdx.x;
+            const uint32_t my = i < nw ? winners[i] : 0xFFFFFFFFu;
+            int rank = 0;
+            for (int j = 0; j < nw; ++j) rank += winners[j] < my;
+            if (i < nw) out[rank] = map_slot(cand, cand_stride, row, my);
+        }
+        return;
+    }
+    // overflowed row: in-order compaction over all slots
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int64_t s0 = 0; s0 < n; s0 += 1024) {
         const int64_t s = s0 + threadIdx.x;
@@ -423,6 +436,18 @@ size_t topk_ws_bytes(int total_q) {
            al256((size_t)total_q * kCandCap * 8);
 }
 
+uint32_t* topk_ws_hist(void* ws) { return (uint32_t*)ws; }
+
+hipError_t clear_topk_ws(void* ws, int nq, bool hist_too, hipStream_t s) {
+    // histogram and row state are adjacent: clear both with one fill
+    const size_t hb = al256((size_t)nq * kHistBins * 4);
+    char* base = (char*)ws + (hist_too ? 0 : hb);
+    const int64_t nfill = (int64_t)(((hist_too ? hb : 0) + al256((size_t)nq * sizeof(RowSel))) / 4);
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((nfill + 255) / 256 < 2048 ? (nfill + 255) / 256 : 2048)), dim3(256), 0,
+                       s, (uint32_t*)base, nfill, 0u);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
     const int nq = a.g.total_q;
     char* ws = (char*)a.ws;
@@ -433,16 +458,22 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
     uint64_t* cb = (uint64_t*)ws;
     RowSrc rs{a.b->d_entry_off, a.b->d_row_seq, a.b->d_q_pos, a.b->ratio, a.cand ? a.cand_count : nullptr,
               a.block_mode, a.block, a.max_slots};
-    const int64_t nfill = (int64_t)nq * kHistBins;
-    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((nfill + 255) / 256 < 4096 ? (nfill + 255) / 256 : 4096)), dim3(256), 0,
-                       s, hist, nfill, 0u);
     const unsigned chunks = (unsigned)((a.max_slots + kHChunk - 1) / kHChunk);
-    hipLaunchKernelGGL(k_hist, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, hist);
-    hipLaunchKernelGGL(k_thresh, dim3(nq), dim3(256), 0, s, hist, rs, a.K, sel);
-    hipLaunchKernelGGL(k_collect, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, sel, cb);
-    hipLaunchKernelGGL(k_final, dim3(nq), dim3(1024), 0, s, sel, cb, a.cand, a.cand_stride, a.K, a.idx);
-    hipLaunchKernelGGL(k_fallback, dim3(nq), dim3(1024), 0, s, a.scores, a.stride, rs, sel, a.cand, a.cand_stride,
-                       a.K, a.idx);
+    const uint32_t* h = a.hist;
+    if (h && h != hist) {
+        hipError_t e = clear_topk_ws(a.ws, nq, false, s);
+        if (e != hipSuccess) return e;
+    } else if (!h) {
+        hipError_t e = clear_topk_ws(a.ws, nq, true, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_hist, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, hist);
+        h = hist;
+    }
+    // (h == hist: the caller cleared the workspace and filled its histogram)
+    hipLaunchKernelGGL(k_collect, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, h, a.K,
+                       sel, cb);
+    hipLaunchKernelGGL(k_final, dim3(nq), dim3(1024), 0, s, a.scores, a.stride, sel, cb, a.cand, a.cand_stride, a.K,
+                       a.idx);
     return hipGetLastError();
 }
 
@@ -466,6 +497,7 @@ hipError_t launch_block_pool(const PoolLaunch& a, hipStream_t s) {
     t.K = a.max_blocks;
     t.idx = a.blocks;
     t.ws = a.topk_ws;
+    t.hist = nullptr;
     hipError_t e = launch_topk(t, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_pool_expand, dim3(a.g.total_q), dim3(256), 0, s, a.blocks, rs, a.max_blocks, a.pool_pos,

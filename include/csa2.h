@@ -132,11 +132,17 @@ typedef struct csa2_swa_layout {
  * q: [total_q][H][64] (CSA2_Q_FP4) or [total_q][H][128] (CSA2_Q_FP8) (device).
  * scores: [total_q][score_stride] f32 (device); score_stride >= max N_b
  *   (cand == NULL) or >= cand_stride.
+ * hist: NULL, or [total_q][4096] u32 (device, zeroed by the caller) that
+ *   receives, per row, the count of written finite scores in each bin of bits
+ *   30..19 (visible slots; with cand, the non-empty visible slots).  Passing it
+ *   on to csa2_topk saves the Top-K pass its own histogram pass.  Not
+ *   produced for CSA2_Q_FP8 queries in this build (the call then returns
+ *   CSA2_ERR_UNSUPPORTED).
  * Supported: H in {32, 64}.  CSA2_Q_FP8 requires cand == NULL. */
 CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_t q_fmt, const void* q,
                                       const uint8_t* q_sc, const float* w, const uint8_t* k_fp4,
                                       const uint8_t* k_sc, const int32_t* cand, int32_t cand_stride,
-                                      float* scores, int64_t score_stride, hipStream_t stream);
+                                      float* scores, int64_t score_stride, uint32_t* hist, hipStream_t stream);
 
 /* ---- Top-K ---------------------------------------------------------------
  * Per query row, the first min(K, n) slots under (score descending, entry
@@ -146,11 +152,14 @@ CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_
  * n = cand_count[row] and slot s maps to position cand[row*cand_stride + s];
  * the first n candidate positions must be ascending.  Scores of the n slots
  * must be finite and >= +0 (as csa2_index_score writes them).
+ * hist: NULL, or the histogram csa2_index_score wrote for exactly these scores
+ *   (with cand, valid when the first cand_count slots are all non-empty and
+ *   visible, as in a block pool).
  * idx: [total_q][K] i32 (device).  Supported: 1 <= K <= 2048.
  * Workspace: csa2_workspace_size(CSA2_WS_TOPK, ...). */
 CSA2_API csa2_status csa2_topk(const csa2_batch* batch, const float* scores, int64_t score_stride,
                                const int32_t* cand, int32_t cand_stride, const int32_t* cand_count, int32_t K,
-                               int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+                               const uint32_t* hist, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- block pool ----------------------------------------------------------
  * Hierarchical Sparse Indexer candidate pool (report 2.3.2; the reading note

@@ -58,11 +58,11 @@ class HostBatch:
 
 def _score(b, **kw):
     args = dict(H=64, q_fmt=0, q=FAKE, q_sc=FAKE, w=FAKE, k=FAKE, k_sc=FAKE, cand=None, cstride=0, scores=FAKE,
-                stride=1000, stream=None)
+                stride=1000, hist=None, stream=None)
     args.update(kw)
     return C.lib().csa2_index_score(ctypes.byref(b.c), args["H"], args["q_fmt"], args["q"], args["q_sc"], args["w"],
                                     args["k"], args["k_sc"], args["cand"], args["cstride"], args["scores"],
-                                    args["stride"], args["stream"])
+                                    args["stride"], args["hist"], args["stream"])
 
 
 def test_index_score_validation():
@@ -74,6 +74,9 @@ def test_index_score_validation():
     assert _score(b, cand=FAKE, cstride=0) == C.CSA2_ERR_INVALID_ARG
     assert _score(b, cand=FAKE, cstride=64, stride=32) == C.CSA2_ERR_INVALID_ARG
     assert _score(b, cand=FAKE, cstride=64, stride=64, q_fmt=1) == C.CSA2_ERR_UNSUPPORTED
+    assert _score(b, q_fmt=1, hist=FAKE) == C.CSA2_ERR_UNSUPPORTED   # no fused histogram for E4M3 queries
+    many = HostBatch([1000], [list(range(990, 1000))])
+    assert _score(many, hist=FAKE) == C.CSA2_ERR_UNSUPPORTED         # nor for the many-query scan
 
 
 def test_batch_validation():
@@ -100,7 +103,7 @@ def test_topk_validation():
     need = L.csa2_workspace_size(C.CSA2_WS_TOPK, ctypes.byref(b.c), 512, 2048, 1)
     assert need > 0
     topk = lambda K, ws, n, stride=1000, cand=None, cnt=None, cs=0: L.csa2_topk(
-        ctypes.byref(b.c), FAKE, stride, cand, cs, cnt, K, FAKE, ws, n, None)
+        ctypes.byref(b.c), FAKE, stride, cand, cs, cnt, K, None, FAKE, ws, n, None)
     assert topk(0, FAKE, need) == C.CSA2_ERR_INVALID_ARG
     assert topk(4096, FAKE, need) == C.CSA2_ERR_UNSUPPORTED
     assert topk(512, None, 0) == C.CSA2_ERR_WORKSPACE

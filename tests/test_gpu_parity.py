@@ -54,9 +54,19 @@ def test_index_score_full_bitwise(case):
     torch.cuda.synchronize()
     ref = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, synth.Q_FP4)
     _full_rows_equal(got, ref, wl)
-    # deterministic across runs
-    again = C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP4, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc)
-    assert torch.equal(got.view(torch.int32), again.view(torch.int32))
+    # deterministic across runs; the variant that also builds the Top-K histogram
+    # writes the same scores, and its histogram equals one counted on the host
+    hist = C.hist_buffer(dw.batch)
+    again = C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP4, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc,
+                               hist=hist)
+    _full_rows_equal(again, ref, wl)  # slots past N_b are not written; compare the written ones
+    vis = oracle.row_visible(wl)
+    h = hist.cpu().numpy()
+    for r in range(wl.total_q):
+        bins = ref[r, :vis[r]].view(np.uint32) >> 19
+        assert np.array_equal(h[r], np.bincount(bins, minlength=4096)), r
+    # Top-K from the fused histogram equals Top-K without it
+    assert torch.equal(C.csa2_topk(dw.batch, got, 512, hist=hist), C.csa2_topk(dw.batch, got, 512))
 
 
 def test_index_score_cand_bitwise():
@@ -69,11 +79,16 @@ def test_index_score_cand_bitwise():
     pool[0, 100:140] = -1  # holes are allowed in a candidate list
     L = [x for x in wl.layers if x.mode == synth.MODE_REINDEX][0]
     dL = [x for x in dw.layers if x["index"] == L.index][0]
+    hist = C.hist_buffer(dw.batch)
     got = C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP4, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc,
-                             cand=dev(pool))
+                             cand=dev(pool), hist=hist)
     torch.cuda.synchronize()
     ref = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, synth.Q_FP4, cand=pool)
     assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    h = hist.cpu().numpy()
+    for r in range(wl.total_q):
+        fin = ref[r][np.isfinite(ref[r])]
+        assert np.array_equal(h[r], np.bincount(fin.view(np.uint32) >> 19, minlength=4096)), r
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "fp4"])
