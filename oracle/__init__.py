@@ -166,11 +166,15 @@ def gather_dequant(wl, idx):
     return out
 
 
-def sparse_attn(wl, q_main, idx, swa, replay_s=None, rows=None, scale=None, with_lse=True):
+def sparse_attn(wl, q_main, idx, swa, replay_s=None, rows=None, scale=None, with_lse=True, idx_of_rows=False):
+    """rows: a subset of query rows; idx then holds either every row's indices
+    (selected here) or, with idx_of_rows, only the subset's."""
     row_seq, q_pos = wl.row_seq, wl.q_pos
     if rows is not None:
         rows = np.asarray(rows, np.int64)
-        row_seq, q_pos, q_main, idx = row_seq[rows], q_pos[rows], q_main[rows], idx[rows]
+        row_seq, q_pos, q_main = row_seq[rows], q_pos[rows], q_main[rows]
+        if not idx_of_rows:
+            idx = idx[rows]
     q_main = _c(q_main, np.uint16)
     idx = _c(idx, np.int32)
     nr, Hm, _ = q_main.shape
@@ -233,7 +237,7 @@ def layer_chain(wl, rows=None, attn=True):
             use_idx = idx_cur
         res["idx"] = use_idx
         if attn:
-            res["out"], res["lse"] = sparse_attn(wl, L.q_main, use_idx, L.swa, rows=sel_rows)
+            res["out"], res["lse"] = sparse_attn(wl, L.q_main, use_idx, L.swa, rows=sel_rows, idx_of_rows=True)
         results.append(res)
     return results
 

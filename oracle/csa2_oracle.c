@@ -202,16 +202,25 @@ static float score_one(const score_ctx* c, int64_t r, int64_t j, const int64_t* 
     return acc * (float)orc_e8m0(c->k_sc[e]);
 }
 
-static void score_row(void* p, int64_t r) {
+/* Work item = (row, chunk of 65,536 slots): scores are independent of each
+ * other, so splitting a row changes nothing but the number of busy threads. */
+#define SCORE_CHUNK 65536
+
+static void score_item(void* p, int64_t item) {
     const score_ctx* c = (const score_ctx*)p;
+    int64_t nchunk = (c->n_slots + SCORE_CHUNK - 1) / SCORE_CHUNK;
+    if (nchunk < 1) nchunk = 1;
+    int64_t r = item / nchunk, ch0 = (item % nchunk) * SCORE_CHUNK;
+    int b = c->row_seq[r];
+    int64_t n = c->entry_off[b + 1] - c->entry_off[b];
+    int64_t ns = c->cand ? c->n_slots : n;
+    if (ch0 >= ns) return;
+    int64_t ch1 = ch0 + SCORE_CHUNK < ns ? ch0 + SCORE_CHUNK : ns;
     int64_t* qi = (int64_t*)malloc(sizeof(int64_t) * (size_t)c->H * 128);
     for (int h = 0; h < c->H; ++h)
         for (int ch = 0; ch < 128; ++ch) qi[h * 128 + ch] = q_int(c, r, h, ch);
     float* out = c->scores + r * c->score_stride;
-    int b = c->row_seq[r];
-    int64_t n = c->entry_off[b + 1] - c->entry_off[b];
-    int64_t ns = c->cand ? c->n_slots : n;
-    for (int64_t s = 0; s < ns; ++s) {
+    for (int64_t s = ch0; s < ch1; ++s) {
         int64_t j = c->cand ? c->cand[r * c->cand_stride + s] : s;
         out[s] = score_one(c, r, j, qi);
     }
@@ -227,9 +236,12 @@ int orc_index_score(int64_t total_q, const int32_t* row_seq, const int32_t* q_po
                     int ratio, int H, int q_fmt, const uint8_t* q, const uint8_t* q_sc, const float* w,
                     const uint8_t* k, const uint8_t* k_sc, const int32_t* cand, int64_t cand_stride,
                     int64_t n_slots, float* scores, int64_t score_stride, int nthreads) {
+    /* without a candidate list the caller passes n_slots = the largest N_b */
     score_ctx c = {row_seq, q_pos, entry_off, ratio, H, q_fmt, q, q_sc, w, k, k_sc,
                    cand, cand_stride, scores, score_stride, n_slots, 0};
-    parallel_for(total_q, nthreads, score_row, &c);
+    int64_t nchunk = (n_slots + SCORE_CHUNK - 1) / SCORE_CHUNK;
+    if (nchunk < 1) nchunk = 1;
+    parallel_for(total_q * nchunk, nthreads, score_item, &c);
     return c.status;
 }
 
