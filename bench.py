@@ -41,7 +41,36 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
-    return ap.parse_args()
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="short run for hardware-counter collection: a few steps, a few scan launches and one "
+                         "512 MiB device copy that calibrates the byte counters")
+    a = ap.parse_args()
+    if a.profile_pass:
+        a.steps, a.warmup, a.no_cpu_baseline, a.no_prefill = 3, 1, True, True
+    return a
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic_decode_c1.json")
+SCAN_SOURCES = [os.path.join(ROOT, "compressed_sparse_attention_amd", "csrc", f)
+                for f in ("k_index_score.hip", "csa2_internal.h")]
+
+
+def scan_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per scan launch from the committed counter runs, if they were
+    taken on the kernel source as it is now; otherwise None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    return rec.get("bytes_per_launch") if rec.get("source_sha") == scan_source_hash() else None
 
 
 def log(*a):
@@ -150,10 +179,17 @@ def main():
                    "sequence_layer_steps_per_s": round(wl.n_seq * 1000.0 / ms_step, 1)},
         "roofline": {"kernel": "k_score_decode<64,1,hist> (indexer scan)", "bound": "hbm", "achieved": round(scan_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "mean_launch_us": round(scan_ms * 1000, 2),
+                     "traffic": measured_traffic(), "mean_launch_us": round(scan_ms * 1000, 2),
                      "algorithmic_bytes_per_launch": scan_bytes},
     }
     del sc_buf
+    if args.profile_pass:  # calibration copy for the byte counters
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = 512 << 20
+        result["scan_source_sha"] = scan_source_hash()
 
     if not args.no_prefill:
         result["prefill_index"] = bench_prefill(args, C, synth, torch, dev)
