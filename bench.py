@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
+    ap.add_argument("--workload", default="decode_c1",
+                    choices=["decode_c1", "decode_c0", "chain_c2", "prefill_c3", "ragged_c4"],
+                    help="decode_c1 (default) prints the full line; the others time their layer chain only")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for hardware-counter collection: a few steps, a few scan launches and one "
                          "512 MiB device copy that calibrates the byte counters")
@@ -95,6 +98,8 @@ def main():
     torch.cuda.set_device(0)
     C.lib()
     dev = torch.device("cuda:0")
+    if args.workload != "decode_c1":
+        return chain_only(args, synth, C, torch, dev)
 
     t0 = time.time()
     wl = synth.config("decode_c1", n_seq=args.n_seq, n=args.n)
@@ -198,6 +203,33 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args, wl, dw, C, run_chain)
 
     print(json.dumps(result), flush=True)
+
+
+def chain_only(args, synth, C, torch, dev):
+    """Time the layer chain of another workload (one call = all its layers)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import DevWorkload, prepare_chain
+
+    t0 = time.time()
+    wl = synth.config(args.workload)
+    log(f"[bench] generated {args.workload} in {time.time() - t0:.1f}s")
+    dw = DevWorkload(wl, dev)
+    call = prepare_chain(dw, want_idx=False, want_lse=False)[0]
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        call()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    n_layers = len(wl.layers)
+    res = {"metric": METRIC, "workload": args.workload, "ms_per_chain": round(ms, 4), "layers": n_layers,
+           "value": round(n_layers * 1000.0 / ms, 2), "unit": "layer-steps/s", "rows": wl.total_q,
+           "entries": wl.total_entries}
+    print(json.dumps(res), flush=True)
 
 
 def bench_prefill(args, C, synth, torch, dev):

@@ -234,16 +234,18 @@ def csa2_gather_dequant(batch, kv_fp4, kv_sc, idx, stream=None):
 
 
 def csa2_sparse_attn(batch, q_bf16, kv_fp4, kv_sc, idx, swa_rows, swa_layout, softmax_scale, out=None, lse=None,
-                     want_lse=True, stream=None):
+                     want_lse=True, ws=None, split=True, stream=None):
     Hm = q_bf16.shape[1]
     dev = q_bf16.device
     if out is None:
         out = torch.empty((batch.total_q, Hm, 512), dtype=torch.float32, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((batch.total_q, Hm), dtype=torch.float32, device=dev)
+    if ws is None and split:
+        ws = workspace(csa2_workspace_size(CSA2_WS_SPARSE_ATTN, batch, idx.shape[1]), dev)
     st = lib().csa2_sparse_attn(ctypes.byref(batch.c), Hm, _ptr(q_bf16), _ptr(kv_fp4), _ptr(kv_sc), _ptr(idx),
                                 idx.shape[1], _ptr(swa_rows), ctypes.byref(swa_layout.c), float(softmax_scale),
-                                _ptr(out), _ptr(lse), None, 0, _stream(stream))
+                                _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check(st, "csa2_sparse_attn")
     return out, lse
 

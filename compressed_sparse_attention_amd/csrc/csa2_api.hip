@@ -76,14 +76,16 @@ size_t pool_ws_bytes(const Geometry& g, int block) {
 }
 
 struct ChainWs {
-    size_t scores, pool_scores, pool_ws, idx_cur, idx_empty, pool_out, total;
+    size_t scores, pool_scores, pool_ws, idx_cur, idx_empty, pool_out, attn, attn_bytes, total;
 };
 
 ChainWs chain_ws(const Geometry& g, int K, int block, int max_blocks) {
     ChainWs w{};
     size_t off = 0;
-    w.scores = off;
-    off += al256((size_t)g.total_q * (size_t)(g.max_entries > 0 ? g.max_entries : 1) * 4);
+    w.scores = off;  // score rows, or the scan's per-chunk lists and counts (never both in one layer)
+    const size_t rows_bytes = al256((size_t)g.total_q * (size_t)(g.max_entries > 0 ? g.max_entries : 1) * 4);
+    const size_t lists_bytes = al256(local_lists_bytes(g)) + al256(local_counts_bytes(g));
+    off += rows_bytes > lists_bytes ? rows_bytes : lists_bytes;
     w.pool_scores = off;
     off += al256((size_t)g.total_q * (size_t)max_blocks * block * 4);
     w.pool_ws = off;  // block scores + Top-K workspace (the Top-K calls reuse its tail)
@@ -95,6 +97,9 @@ ChainWs chain_ws(const Geometry& g, int K, int block, int max_blocks) {
     w.pool_out = off;
     off += al256((size_t)g.total_q * max_blocks * 4) + al256((size_t)g.total_q * max_blocks * block * 4) +
            al256((size_t)g.total_q * 4);
+    w.attn = off;  // attention partials for 64 heads and a 128-row window
+    w.attn_bytes = attn_ws_bytes(g, 64, attn_splits(g, 64, K, 128));
+    off += al256(w.attn_bytes);
     w.total = off;
     return w;
 }
@@ -129,7 +134,9 @@ CSA2_API size_t csa2_workspace_size(int32_t which, const csa2_batch* batch, int3
     switch (which) {
         case CSA2_WS_TOPK: return topk_ws_bytes(g.total_q);
         case CSA2_WS_BLOCK_POOL: return pool_ws_bytes(g, 8);
-        case CSA2_WS_SPARSE_ATTN: return 0;
+        case CSA2_WS_SPARSE_ATTN:  // for 64 heads and a 128-row window; a smaller workspace means fewer splits
+            if (K < 1) return 0;
+            return attn_ws_bytes(g, 64, attn_splits(g, 64, K, 128));
         case CSA2_WS_LAYER_CHAIN:
             if (K < 1 || max_blocks < 1 || n_layers < 1) return 0;
             return chain_ws(g, K, 8, max_blocks).total;
@@ -239,8 +246,6 @@ CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const
                                       const uint8_t* kv_fp4, const uint8_t* kv_sc, const int32_t* idx, int32_t K,
                                       const uint16_t* swa_bf16, const csa2_swa_layout* swa, float softmax_scale,
                                       float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
     Geometry g;
     csa2_status st = batch_geometry(batch, &g);
     if (st) return st;
@@ -249,7 +254,9 @@ CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const
     if (K < 1 || K > kMaxK) return K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
     if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return CSA2_ERR_INVALID_ARG;
     if ((st = check_swa(batch, swa))) return st;
-    AttnLaunch a{batch, g, Hm, q_bf16, kv_fp4, kv_sc, idx, K, swa_bf16, swa, softmax_scale, out, lse};
+    if (ws && ((uintptr_t)ws & 255)) return CSA2_ERR_WORKSPACE;
+    AttnLaunch a{batch, g, Hm, q_bf16, kv_fp4, kv_sc, idx, K, swa_bf16, swa, softmax_scale, out, lse, ws,
+                 ws ? ws_bytes : 0};
     hipError_t e = launch_sparse_attn(a, stream);
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
@@ -337,49 +344,87 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                 pool_built = false;
             }
             const bool on_pool = !full && pool_built;
-            // the score kernel builds the Top-K histogram when it can (FP4 queries,
-            // at most 4 rows per sequence or a candidate list); the Top-K pass then
-            // starts from it.  A pool built from these scores needs its own pass.
-            const bool fused = L.q_fmt == CSA2_Q_FP4 && (on_pool || g.max_q_per_seq <= 4);
-            if (fused && (e = clear_topk_ws(topk_ws, g.total_q, true, stream)) != hipSuccess) return hip_fail(e);
-            ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, src->k_fp4, src->k_sc,
-                           on_pool ? pp : nullptr, on_pool ? pool_stride : 0, on_pool ? pscores : scores,
-                           on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1),
-                           fused ? topk_ws_hist(topk_ws) : nullptr};
-            if ((e = launch_index_score(sa, stream)) != hipSuccess) return hip_fail(e);
-            TopkLaunch ta{};
-            ta.b = batch;
-            ta.g = g;
-            ta.scores = on_pool ? pscores : scores;
-            ta.stride = on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1);
-            ta.max_slots = on_pool ? pool_stride : g.max_entries;
-            ta.cand = on_pool ? pp : nullptr;
-            ta.cand_stride = on_pool ? pool_stride : 0;
-            ta.cand_count = on_pool ? pc : nullptr;
-            ta.block_mode = 0;
-            ta.block = 1;
-            ta.K = p->K;
-            ta.idx = idx_cur;
-            ta.ws = topk_ws;
-            ta.hist = fused ? topk_ws_hist(topk_ws) : nullptr;
-            if ((e = launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
-            // the pool runs its own selection in the same workspace: after the Top-K
-            if (full && (L.flags & CSA2_LAYER_BUILD_POOL)) {
-                PoolLaunch pa{};
-                pa.b = batch;
-                pa.g = g;
-                pa.scores = scores;
-                pa.stride = g.max_entries > 0 ? g.max_entries : 1;
-                pa.block = p->block;
-                pa.max_blocks = p->max_blocks;
-                pa.blocks = pb;
-                pa.pool_pos = pp;
-                pa.pool_count = pc;
-                pa.bscores = (float*)pws;
-                pa.bstride = nb > 0 ? nb : 1;
-                pa.topk_ws = topk_ws;
-                if ((e = launch_block_pool(pa, stream)) != hipSuccess) return hip_fail(e);
-                pool_built = true;
+            const bool build_pool = full && (L.flags & CSA2_LAYER_BUILD_POOL);
+            if (full && local_scan_ok(g, L.q_fmt)) {
+                // decode scan: per-chunk candidate lists and the rows' histograms
+                // instead of score rows (plus the block maxima of the pool)
+                const int ch = local_chunk(g);
+                const int64_t mc = (g.max_entries + ch - 1) / ch;
+                LocalOut lo{};
+                lo.lists = (uint64_t*)scores;
+                lo.counts = (uint32_t*)((char*)scores + al256(local_lists_bytes(g)));
+                lo.bscores = build_pool ? (float*)pws : nullptr;
+                lo.bstride = nb > 0 ? nb : 1;
+                lo.max_chunks = (int)(mc > 0 ? mc : 1);
+                lo.chunk = ch;
+                lo.K = p->K;
+                lo.block = p->block;
+                if ((e = clear_topk_ws(topk_ws, g.total_q, true, stream)) != hipSuccess) return hip_fail(e);
+                ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, L.k_fp4, L.k_sc,
+                               nullptr, 0, nullptr, 0, topk_ws_hist(topk_ws), &lo};
+                if ((e = launch_index_score(sa, stream)) != hipSuccess) return hip_fail(e);
+                if ((e = launch_topk_local(batch, g, lo, idx_cur, topk_ws, stream)) != hipSuccess) return hip_fail(e);
+                if (build_pool) {  // after the Top-K: the pool's selection reuses its workspace
+                    PoolLaunch pa{};
+                    pa.b = batch;
+                    pa.g = g;
+                    pa.block = p->block;
+                    pa.max_blocks = p->max_blocks;
+                    pa.blocks = pb;
+                    pa.pool_pos = pp;
+                    pa.pool_count = pc;
+                    pa.bscores = (float*)pws;
+                    pa.bstride = nb > 0 ? nb : 1;
+                    pa.topk_ws = topk_ws;
+                    pa.bscores_ready = true;
+                    if ((e = launch_block_pool(pa, stream)) != hipSuccess) return hip_fail(e);
+                    pool_built = true;
+                }
+            } else {
+                // the score kernel builds the Top-K histogram when it can (FP4 queries,
+                // at most 4 rows per sequence or a candidate list); the Top-K pass then
+                // starts from it.  A pool built from these scores needs its own pass.
+                const bool fused = L.q_fmt == CSA2_Q_FP4 && (on_pool || g.max_q_per_seq <= 4);
+                if (fused && (e = clear_topk_ws(topk_ws, g.total_q, true, stream)) != hipSuccess) return hip_fail(e);
+                ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, src->k_fp4, src->k_sc,
+                               on_pool ? pp : nullptr, on_pool ? pool_stride : 0, on_pool ? pscores : scores,
+                               on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1),
+                               fused ? topk_ws_hist(topk_ws) : nullptr};
+                if ((e = launch_index_score(sa, stream)) != hipSuccess) return hip_fail(e);
+                TopkLaunch ta{};
+                ta.b = batch;
+                ta.g = g;
+                ta.scores = on_pool ? pscores : scores;
+                ta.stride = on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1);
+                ta.max_slots = on_pool ? pool_stride : g.max_entries;
+                ta.cand = on_pool ? pp : nullptr;
+                ta.cand_stride = on_pool ? pool_stride : 0;
+                ta.cand_count = on_pool ? pc : nullptr;
+                ta.block_mode = 0;
+                ta.block = 1;
+                ta.K = p->K;
+                ta.idx = idx_cur;
+                ta.ws = topk_ws;
+                ta.hist = fused ? topk_ws_hist(topk_ws) : nullptr;
+                if ((e = launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
+                // the pool runs its own selection in the same workspace: after the Top-K
+                if (build_pool) {
+                    PoolLaunch pa{};
+                    pa.b = batch;
+                    pa.g = g;
+                    pa.scores = scores;
+                    pa.stride = g.max_entries > 0 ? g.max_entries : 1;
+                    pa.block = p->block;
+                    pa.max_blocks = p->max_blocks;
+                    pa.blocks = pb;
+                    pa.pool_pos = pp;
+                    pa.pool_count = pc;
+                    pa.bscores = (float*)pws;
+                    pa.bstride = nb > 0 ? nb : 1;
+                    pa.topk_ws = topk_ws;
+                    if ((e = launch_block_pool(pa, stream)) != hipSuccess) return hip_fail(e);
+                    pool_built = true;
+                }
             }
         } else if (L.mode == CSA2_MODE_SWA_ONLY) {
             use_idx = idx_empty;
@@ -390,7 +435,8 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
             kv = (const uint8_t*)L.swa;
             kvs = (const uint8_t*)L.swa;
         }
-        AttnLaunch aa{batch, g, p->Hm, L.q_main, kv, kvs, use_idx, p->K, L.swa, swa, p->softmax_scale, L.out, L.lse};
+        AttnLaunch aa{batch, g, p->Hm, L.q_main, kv, kvs, use_idx, p->K, L.swa, swa, p->softmax_scale, L.out, L.lse,
+                      base + cw.attn, cw.attn_bytes};
         if ((e = launch_sparse_attn(aa, stream)) != hipSuccess) return hip_fail(e);
         if (L.idx_out) {
             if ((e = hipMemcpyAsync(L.idx_out, use_idx, (size_t)nidx * 4, hipMemcpyDeviceToDevice, stream)) != hipSuccess)

@@ -45,6 +45,120 @@ __host__ __device__ inline int64_t visible_count(int64_t n, int64_t t, int m) {
 }
 
 // ---------------------------------------------------------------------------
+// Selection order shared by the scan and the Top-K passes.  Scores are
+// non-negative binary32 values (a negative one orders as +0), so their bit
+// patterns order like the values, and
+//     key64 = (score bits << 32) | (0xFFFFFFFF - position)
+// is unique per position and orders exactly like (score desc, position asc).
+// The histogram bin of a score is its bits 30..19, i.e. key64 >> 51.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t score_key(float s) {
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? 0u : u;
+}
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t slot) {
+    return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - slot);
+}
+
+// Inclusive scan of one value per thread over a 256-thread workgroup: a
+// shuffle scan inside each wave, then the wave totals through LDS.  Every
+// thread of the workgroup calls it.
+__device__ inline uint32_t block_scan_256(uint32_t v, uint32_t* wtot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+    }
+    if (lane == 63) wtot[wave] = v;
+    __syncthreads();
+    for (int w2 = 0; w2 < wave; ++w2) v += wtot[w2];
+    return v;
+}
+
+// Bin counts of a histogram in plain 32-bit words, or packed two 16-bit
+// counts per word (bin 2i in the low half of word i).
+struct PlainBins {
+    const uint32_t* h;
+    __device__ uint32_t operator()(int b) const { return h[b]; }
+};
+struct PackedBins {
+    const uint32_t* h;
+    __device__ uint32_t operator()(int b) const { return (h[b >> 1] >> (16 * (b & 1))) & 0xFFFFu; }
+};
+
+// Block-wide (256 threads): the bin that holds the kk-th largest key; every
+// thread returns it; kHistBins when kk == 0.  `found` and `wtot` are LDS
+// scratch; a caller that calls it again must pass a barrier first.
+template <class Bins>
+__device__ inline uint32_t threshold_bin(Bins h, uint32_t kk, uint32_t* wtot, uint32_t* found) {
+    const int t = threadIdx.x;
+    // thread t owns bins [4096 - 16(t+1), 4096 - 16t), i.e. thread 0 the top bins
+    const int hi = kHistBins - 16 * t;
+    uint32_t c[16];
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        c[i] = h(hi - 1 - i);
+        s += c[i];
+    }
+    if (t == 0) *found = kk == 0 ? (uint32_t)kHistBins : 0u;
+    const uint32_t incl = block_scan_256(s, wtot);
+    const uint32_t before = incl - s;
+    if (kk > 0 && before < kk && kk <= incl) {
+        uint32_t acc = before;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            acc += c[i];
+            if (acc >= kk) {
+                *found = (uint32_t)(hi - 1 - i);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    return *found;
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk candidate lists written by the decode scan in place of the full
+// score rows.  A chunk is a run of positions one scan workgroup covers.  For
+// each (row, chunk) the scan keeps every visible position whose bin is at or
+// above the bin of the chunk's min(K, visible)-th largest score; the row's
+// Top-K lies in the union of its chunks' lists, because a position ranked
+// among the row's first K is ranked among its chunk's first K.  Lists hold
+// key64 values in position order.
+// ---------------------------------------------------------------------------
+struct LocalOut {
+    uint64_t* lists;     // [total_q][max_chunks][chunk]
+    uint32_t* counts;    // [total_q][max_chunks]; written for chunks that hold positions
+    float* bscores;      // nullable: block maxima [total_q][bstride] for the block pool
+    int64_t bstride;
+    int max_chunks;
+    int chunk;
+    int K;
+    int block;
+};
+
+// positions per decode-scan workgroup: 4 waves x 16 tiles of 64, halved for
+// the 4-row scan when it keeps its rows' scores on chip (LDS budget)
+constexpr int decode_chunk(int tq, bool local) { return (local && tq > 1) ? 2048 : 4096; }
+// the scan writes local lists for FP4 queries and at most 4 rows per sequence
+inline bool local_scan_ok(const Geometry& g, int q_fmt) { return q_fmt == CSA2_Q_FP4 && g.max_q_per_seq <= 4; }
+inline int local_chunk(const Geometry& g) { return decode_chunk(g.max_q_per_seq <= 1 ? 1 : 4, true); }
+inline size_t local_lists_bytes(const Geometry& g) {
+    const int ch = local_chunk(g);
+    const int64_t mc = (g.max_entries + ch - 1) / ch;
+    return (size_t)g.total_q * (size_t)(mc > 0 ? mc : 1) * ch * 8;
+}
+inline size_t local_counts_bytes(const Geometry& g) {
+    const int ch = local_chunk(g);
+    const int64_t mc = (g.max_entries + ch - 1) / ch;
+    return (size_t)g.total_q * (size_t)(mc > 0 ? mc : 1) * 4;
+}
+
+// ---------------------------------------------------------------------------
 // Kernel launchers (defined in the .hip files).  All return hipError_t of
 // the launch; shapes were validated by the caller.
 // ---------------------------------------------------------------------------
@@ -62,6 +176,7 @@ struct ScoreLaunch {
     float* scores;
     int64_t stride;
     uint32_t* hist;             // nullable: [total_q][kHistBins], zeroed by the caller
+    const LocalOut* local;      // nullable: decode scan writes per-chunk candidate lists, not scores
 };
 hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s);
 
@@ -87,6 +202,10 @@ size_t topk_ws_bytes(int total_q);
 hipError_t clear_topk_ws(void* ws, int total_q, bool hist_too, hipStream_t s);
 uint32_t* topk_ws_hist(void* ws);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
+// Top-K from a scan's per-chunk lists and its histogram (in the workspace,
+// cleared before the scan together with the row state)
+hipError_t launch_topk_local(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, void* ws,
+                             hipStream_t s);
 
 struct PoolLaunch {
     const csa2_batch* b;
@@ -100,6 +219,7 @@ struct PoolLaunch {
     float* bscores;             // workspace [total_q][bstride]
     int64_t bstride;
     void* topk_ws;
+    bool bscores_ready;         // the scan already wrote the block maxima
 };
 hipError_t launch_block_pool(const PoolLaunch& a, hipStream_t s);
 
@@ -117,7 +237,12 @@ struct AttnLaunch {
     float scale;
     float* out;
     float* lse;
+    void* ws;                   // partial results when the key blocks are split (may be NULL)
+    size_t ws_bytes;
 };
+// key-block splits the attention would use, and the workspace they need
+int attn_splits(const Geometry& g, int Hm, int K, int W);
+size_t attn_ws_bytes(const Geometry& g, int Hm, int S);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_gather_dequant(const csa2_batch* b, Geometry g, const uint8_t* kv, const uint8_t* kv_sc,
                                  const int32_t* idx, int K, uint16_t* out, hipStream_t s);

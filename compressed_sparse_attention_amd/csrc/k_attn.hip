@@ -73,19 +73,23 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     const int32_t* __restrict__ idx, int K, const uint16_t* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
     const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ replay_s, int W,
     const int64_t* __restrict__ entry_off, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ q_pos,
-    float scale_log2, float* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg) {
+    float scale_log2, float* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg, int S,
+    float* __restrict__ partial) {
     __shared__ __attribute__((aligned(16))) uint16_t kl[KB * LROW];
     __shared__ float sl[HG][KB];
     __shared__ int kvalid[KB];
     __shared__ int32_t kidx[kMaxK];
     __shared__ int nsel_sh;
 
-    // the n_hg head groups of one row share an XCD (blocks are dealt to XCDs round-robin)
+    // the n_hg x S workgroups of one row share an XCD (workgroups are dealt to
+    // XCDs round-robin), so the row's gathered keys are read from one L2
     const int L = blockIdx.x;
     const int xcd = L & 7;
     const int kq = L >> 3;
-    const int hg = kq % n_hg;
-    const int row = (kq / n_hg) * 8 + xcd;
+    const int units = n_hg * S;
+    const int hg = (kq % units) / S;
+    const int sp = (kq % units) % S;  // which part of the row's key blocks
+    const int row = (kq / units) * 8 + xcd;
     if (row >= total_q) return;
 
     const int tid = threadIdx.x;
@@ -119,6 +123,9 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     const int n_sel = nsel_sh;
     const int n_keys = n_sel + n_swa;
     const int n_blocks = (n_keys + KB - 1) / KB;
+    const int per = (n_blocks + S - 1) / S;
+    const int blk0 = sp * per;
+    const int blk1 = blk0 + per < n_blocks ? blk0 + per : n_blocks;
 
     // Q operand (16 heads x 512): lane holds head 16hg + li, channels 8lg + 32ks + [0, 8)
     const int hq = HG * hg + li;
@@ -147,7 +154,7 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     uint32_t psc = 0;
     auto fetch = [&](int blk) {
         const int vk = KB * blk + skey;
-        if (vk < n_sel && blk < n_blocks) {
+        if (vk < n_sel && blk < blk1) {
             const int32_t j = kidx[vk];
             if (j >= 0) {
                 const int64_t e = e0 + j;
@@ -158,9 +165,9 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
             }
         }
     };
-    fetch(0);
+    fetch(blk0);
 
-    for (int blk = 0; blk < n_blocks; ++blk) {
+    for (int blk = blk0; blk < blk1; ++blk) {
         // 1) stage 64 keys
         {
             const int vk = KB * blk + skey;
@@ -227,7 +234,11 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         float alpha;
-        v8bf P[2];
+        // each weight as the sum of two bf16 values (hi + lo), so that the P V
+        // product carries about 16 significant bits of it; a single bf16 weight
+        // (8 bits) costs up to ~3e-3 of absolute output error when a handful of
+        // keys carry the softmax
+        v8bf P[2], Plo[2];
         float rs = 0.0f, rs32 = 0.0f;
         if (m_new == -INFINITY) {  // nothing valid yet
             alpha = 1.0f;
@@ -243,8 +254,10 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const __bf16 pb = (__bf16)p[8 * ks + i];
+                const __bf16 pl = (__bf16)(p[8 * ks + i] - (float)pb);
                 P[ks][i] = pb;
-                rs += (float)pb;  // normalise with the weights actually used
+                Plo[ks][i] = pl;
+                rs += (float)pb + (float)pl;  // normalise with the weights actually used
                 rs32 += p[8 * ks + i];
             }
         rs += __shfl_xor(rs, 16);
@@ -275,12 +288,29 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
                 const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(a0));
                 const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(a1));
                 const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P[ks], __builtin_bit_cast(v8bf, both), O[nt], 0, 0, 0);
+                const v8bf vb = __builtin_bit_cast(v8bf, both);
+                O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P[ks], vb, O[nt], 0, 0, 0);
+                O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Plo[ks], vb, O[nt], 0, 0, 0);
             }
         }
         __syncthreads();
     }
 
+    if (S > 1) {
+        // partial result of this part of the keys: unnormalised O, its max and
+        // both sums, combined by k_attn_combine
+        float* po = partial + (((int64_t)row * n_hg + hg) * S + sp) * (HG * 516);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) po[(4 * lg + v) * 512 + 128 * wave + 16 * nt + li] = O[nt][v];
+        if (wave == 0 && lane < 16) {
+            po[HG * 512 + 4 * lane + 0] = m_run;
+            po[HG * 512 + 4 * lane + 1] = l_run;
+            po[HG * 512 + 4 * lane + 2] = l_lse;
+        }
+        return;
+    }
     // finalise: O / l for heads 4lg + v
     const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
     float iv[4];
@@ -296,6 +326,52 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
             l_lse > 0.0f ? (m_run + log2f(l_lse)) * 0.69314718055994531f : -INFINITY;
 }
 
+// Merge the S partial results of each (row, head): with M = max_s m_s and
+// a_s = 2^(m_s - M), O = sum_s a_s O_s / sum_s a_s l_s.  One workgroup of 128
+// threads per (row, head); thread t owns channels 4t .. 4t+3, so every load of
+// the merge is issued at once.
+constexpr int kMaxSplit = 8;
+
+__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part, int Hm, int n_hg, int S,
+                                                      float* __restrict__ out, float* __restrict__ lse) {
+    const int row = blockIdx.x / Hm, h = blockIdx.x % Hm;
+    const int hg = h / HG, hh = h % HG;
+    const float* base = part + ((int64_t)row * n_hg + hg) * S * (HG * 516);
+    const int t = threadIdx.x;
+    float m[kMaxSplit], l[kMaxSplit], ll[kMaxSplit];
+    v4f o[kMaxSplit];
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+        if (s < S) {
+            const float* ps = base + s * (HG * 516);
+            m[s] = ps[HG * 512 + 4 * hh];
+            l[s] = ps[HG * 512 + 4 * hh + 1];
+            ll[s] = ps[HG * 512 + 4 * hh + 2];
+            o[s] = *reinterpret_cast<const v4f*>(ps + hh * 512 + 4 * t);
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s)
+        if (s < S) M = fmaxf(M, m[s]);
+    float L = 0.0f, Llse = 0.0f;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s) {
+            if (s < S) {
+                const float a = exp2f(m[s] - M);  // a part with no valid key has m = -inf: weight 0
+                L += a * l[s];
+                Llse += a * ll[s];
+                acc += a * o[s];
+            }
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    *reinterpret_cast<v4f*>(out + ((int64_t)row * Hm + h) * 512 + 4 * t) = acc * inv;
+    if (lse && t == 0) lse[(int64_t)row * Hm + h] = Llse > 0.0f ? (M + log2f(Llse)) * 0.69314718055994531f : -INFINITY;
+}
+
 }  // namespace
 
 hipError_t launch_gather_dequant(const csa2_batch* b, Geometry g, const uint8_t* kv, const uint8_t* kv_sc,
@@ -305,13 +381,34 @@ hipError_t launch_gather_dequant(const csa2_batch* b, Geometry g, const uint8_t*
     return hipGetLastError();
 }
 
+int attn_splits(const Geometry& g, int Hm, int K, int W) {
+    // split the key blocks of a (row, head group) over several workgroups when
+    // the grid would otherwise leave the chip under-filled (< 2 per CU)
+    const int units = g.total_q * (Hm / HG);
+    const int max_blocks = (K + W + KB - 1) / KB;
+    int S = (512 + units - 1) / units;
+    S = S < 1 ? 1 : (S > kMaxSplit ? kMaxSplit : S);
+    return S < max_blocks ? S : max_blocks;
+}
+
+size_t attn_ws_bytes(const Geometry& g, int Hm, int S) {
+    return S <= 1 ? 0 : (size_t)g.total_q * (Hm / HG) * S * (HG * 516) * sizeof(float);
+}
+
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
     const int n_hg = a.Hm / HG;
+    int S = attn_splits(a.g, a.Hm, a.K, a.sw->window);
+    while (S > 1 && attn_ws_bytes(a.g, a.Hm, S) > a.ws_bytes) --S;  // use what the workspace allows
     const int rows8 = (a.g.total_q + 7) / 8 * 8;
-    const unsigned nblk = (unsigned)rows8 * (unsigned)n_hg;
+    const unsigned nblk = (unsigned)rows8 * (unsigned)n_hg * (unsigned)S;
+    float* part = S > 1 ? (float*)a.ws : nullptr;
     hipLaunchKernelGGL(k_sparse_attn, dim3(nblk), dim3(256), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, a.swa,
                        a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,
-                       a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q, n_hg);
+                       a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q, n_hg, S,
+                       part);
+    if (S > 1)
+        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(a.g.total_q * a.Hm)), dim3(128), 0, s, part, a.Hm, n_hg, S,
+                           a.out, a.lse);
     return hipGetLastError();
 }
 

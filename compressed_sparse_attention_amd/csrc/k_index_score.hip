@@ -32,41 +32,50 @@ __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v1
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, 127);
 }
 
-__device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
+// E2M1 operands occupy the low four dwords of the 8-dword operand; the upper
+// four are never read, so they are left undefined (no registers zeroed)
+__device__ __forceinline__ v8i widen(v4i x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1); }
 
 __device__ __forceinline__ v4i ld16(const uint8_t* p) { return *reinterpret_cast<const v4i*>(p); }
 
-// After the MFMAs of one 64-position tile, acc[mt][nt] holds heads 32mt.. of
+// max(x, 0) as one integer max on the bit pattern: negative floats (and -0)
+// are negative integers and map to +0, the rest are unchanged.  fmaxf would
+// add a NaN-quieting max in front of it; the MFMA results are never NaN.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// After the MFMAs of one 64-position tile, acc[nt] holds 32 heads of
 // positions 32nt + l%32.  Swap the upper half of nt = 0 with the lower half of
-// nt = 1 so that every lane holds all H heads of position p0 + lane, then run
-// the canonical head sum.  `w` points at the row's H weights (uniform).
-// Callers run it with all 64 lanes active (the swap reads the partner lane)
-// and predicate only the store.
+// nt = 1 so that every lane holds the 32 heads of position p0 + lane, then
+// continue the canonical head sum over them from s.  `w` points at the 32
+// weights of these heads (uniform).  Callers run it with all 64 lanes active
+// (the swap reads the partner lane) and predicate only the store.
+__device__ __forceinline__ float head_sum_32(v16f (&acc)[2], const float* __restrict__ w, float s) {
+    float x[16], y[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        // element values go through __float_as_uint: a bit cast applied to a
+        // vector element expression would read element 0 of the vector
+        const float e0 = acc[0][v], e1 = acc[1][v];
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(e0), __float_as_uint(e1), false, false);
+        x[v] = __uint_as_float((unsigned)r[0]);  // heads 8*(v/4) + v%4
+        y[v] = __uint_as_float((unsigned)r[1]);  // heads 8*(v/4) + 4 + v%4
+    }
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = __builtin_fmaf(w[8 * gq + i], relu(x[4 * gq + i]), s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = __builtin_fmaf(w[8 * gq + 4 + i], relu(y[4 * gq + i]), s);
+    }
+    return s;
+}
+
+// The whole head sum from +0 over NMT groups of 32 heads, h = 0 .. 32 NMT - 1.
 template <int NMT>
 __device__ __forceinline__ float head_sum(v16f (&acc)[NMT][2], const float* __restrict__ w) {
-    float x[NMT][16], y[NMT][16];
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            // element values go through __float_as_uint: a bit cast applied to a
-            // vector element expression would read element 0 of the vector
-            const float e0 = acc[mt][0][v], e1 = acc[mt][1][v];
-            auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(e0), __float_as_uint(e1), false, false);
-            x[mt][v] = __uint_as_float((unsigned)r[0]);  // rows 8*(v/4) + v%4
-            y[mt][v] = __uint_as_float((unsigned)r[1]);  // rows 8*(v/4) + 4 + v%4
-        }
     float s = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s = __builtin_fmaf(w[32 * mt + 8 * gq + i], fmaxf(x[mt][4 * gq + i], 0.0f), s);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s = __builtin_fmaf(w[32 * mt + 8 * gq + 4 + i], fmaxf(y[mt][4 * gq + i], 0.0f), s);
-        }
+    for (int mt = 0; mt < NMT; ++mt) s = head_sum_32(acc[mt], w + 32 * mt, s);
     return s;
 }
 
@@ -88,24 +97,51 @@ __device__ __forceinline__ void hist_flush(const uint32_t* h, uint32_t* __restri
         if (h[i]) atomicAdd(&g[i], h[i]);
 }
 
+// The decode scan counts at most 4096 positions per row, so its LDS histogram
+// packs two 16-bit counts per word (bin 2i in the low half of word i).
+__device__ __forceinline__ void hist16_add(uint32_t* h, uint32_t bin) { atomicAdd(&h[bin >> 1], 1u << (16 * (bin & 1))); }
+
+// Adds the counts of bins lo .. kHistBins-1 to the global histogram g.
+__device__ __forceinline__ void hist16_flush(const uint32_t* h, uint32_t* __restrict__ g, uint32_t lo = 0) {
+    for (int i = threadIdx.x + (int)(lo >> 1); i < kHistBins / 2; i += blockDim.x) {
+        const uint32_t v = h[i];
+        if ((v & 0xFFFFu) && (uint32_t)(2 * i) >= lo) atomicAdd(&g[2 * i], v & 0xFFFFu);
+        if (v >> 16) atomicAdd(&g[2 * i + 1], v >> 16);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Decode scan: every sequence has at most TQ query rows (1 for plain decode, 4
 // for the speculative-verify shape); they share one pass over the sequence's
 // indexer K.  Grid (chunks, n_seq); 4 waves; each wave takes 64-position tiles.
 // FP4 x FP4; channel c of a row sits at (lane half g, k-step ks, nibble e)
 // with c = 64g + 32ks + e for both operands.
+//
+// Outputs (OUT): kOutScores writes the score rows; kOutHist also builds the
+// rows' bin histograms; kOutLocal keeps the chunk's scores in LDS and writes,
+// besides the histograms, the chunk's candidate list per row (LocalOut) and,
+// when asked, the block maxima of the block pool.
 // ---------------------------------------------------------------------------
-template <int H, int TQ, bool HIST>
+enum : int { kOutScores = 0, kOutHist = 1, kOutLocal = 2 };
+
+template <int H, int TQ, int OUT>
 __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_sc,
                                                       const float* __restrict__ w, const uint8_t* __restrict__ k,
                                                       const uint8_t* __restrict__ k_sc,
                                                       const int64_t* __restrict__ entry_off,
                                                       const int32_t* __restrict__ q_off,
                                                       const int32_t* __restrict__ q_pos, int ratio,
-                                                      float* __restrict__ scores, int64_t stride, int chunk,
-                                                      uint32_t* __restrict__ hist) {
+                                                      float* __restrict__ scores, int64_t stride,
+                                                      uint32_t* __restrict__ hist, LocalOut lo) {
     constexpr int NMT = H / 32;
-    __shared__ uint32_t hl[HIST ? TQ * kHistBins : 1];
+    constexpr bool HIST = OUT != kOutScores;
+    constexpr bool LOCAL = OUT == kOutLocal;
+    constexpr int chunk = decode_chunk(TQ, LOCAL);
+    __shared__ uint32_t hl[HIST ? TQ * kHistBins / 2 : 1];
+    __shared__ __attribute__((aligned(16))) float sl[LOCAL ? TQ : 1][LOCAL ? chunk : 1];  // the chunk's scores per row
+    __shared__ uint8_t ekl[chunk];                           // the chunk's indexer K scales
+    __shared__ uint32_t wtot[4], found;
+    __shared__ uint16_t pos16[LOCAL ? chunk : 1];  // a row's candidate offsets in the chunk
     const int b = blockIdx.y;
     const int64_t e0 = entry_off[b];
     const int64_t n = entry_off[b + 1] - e0;
@@ -117,7 +153,20 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     if (nq <= 0) return;  // a sequence without query rows has no scores
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5, li = lane & 31;
-    if (HIST) hist_clear(hl, TQ * kHistBins);
+    if (HIST) {  // before any load is in flight: the barrier costs nothing here
+        hist_clear(hl, TQ * kHistBins / 2);
+        __syncthreads();
+    }
+    // the scales of this wave's positions (position p_w + 256 j + lane), staged
+    // in LDS below once the query operands and the first two tiles are in
+    // flight as well; only this wave reads them, so no barrier is needed
+    const int64_t p_w = c0 + 64 * wave;
+    uint8_t sb[chunk / 256];
+#pragma unroll
+    for (int j = 0; j < chunk / 256; ++j) {
+        const int64_t p = p_w + 256 * j + lane;
+        sb[j] = p < c1 ? k_sc[e0 + p] : 0;
+    }
 
     v8i A[TQ][NMT][2];
     int SA[TQ][NMT];
@@ -134,59 +183,153 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
             SA[t][mt] = q_sc[(int64_t)row * H + 32 * mt + li];
         }
     }
-    if (HIST) __syncthreads();
 
-    // software pipeline: the indexer K of the next tile is in flight while
-    // the current tile computes
-    v4i Bn[2][2];
-    int ekn = 127;
-    auto fetch = [&](int64_t p0) {
+    // Two-deep software pipeline over this wave's tiles p_w, p_w + 256, ...:
+    // buffers X and Y hold the indexer K of two tiles; a buffer is refilled
+    // with the tile after next right after the MFMAs have read it, so two
+    // tiles are in flight while the head-sum epilogue of a tile runs.  The
+    // refill has no branch: past this wave's last tile it re-reads that tile
+    // (a cache hit), and rows past the end of the sequence are clamped to its
+    // last row, so no wait on a load is forced before its data is used.
+    struct Buf {
+        v4i k[2][2];
+    };
+    const int n_tiles = p_w < c1 ? (int)((c1 - p_w + 255) / 256) : 0;
+    const int64_t p_last = p_w + 256 * (int64_t)(n_tiles - 1);
+    auto fetch = [&](Buf& bf, int64_t p0) {
+        const uint8_t* kt = k + (e0 + p0) * 64;  // uniform
+        const uint32_t last = (uint32_t)(n - 1 - p0 < 63 ? n - 1 - p0 : 63);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            int64_t j = p0 + 32 * nt + li;
-            j = j < n ? j : n - 1;
-            const uint8_t* kr = k + (e0 + j) * 64 + 32 * g;
-            Bn[nt][0] = ld16(kr);
-            Bn[nt][1] = ld16(kr + 16);
+            const uint32_t r = min((uint32_t)(32 * nt + li), last);
+            bf.k[nt][0] = ld16(kt + r * 64 + 32 * g);
+            bf.k[nt][1] = ld16(kt + r * 64 + 32 * g + 16);
         }
-        const int64_t jl = p0 + lane;
-        ekn = jl < n ? (int)k_sc[e0 + jl] : 127;
     };
-    int64_t p0 = c0 + 64 * wave;
-    if (p0 < c1) fetch(p0);
-    for (; p0 < c1; p0 += 256) {
-        v8i B[2][2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) B[nt][ks] = widen(Bn[nt][ks]);
-        const int ek = ekn;
-        if (p0 + 256 < c1) fetch(p0 + 256);
+    // score the tile at p0 from bf, refilling bf with the tile at p_next once
+    // the last query's MFMAs have consumed it
+    auto tile = [&](Buf& bf, int64_t p0, int64_t p_next) {
         const int64_t jl = p0 + lane;
 #pragma unroll
         for (int t = 0; t < TQ; ++t) {
             if (t >= nq) break;
-            v16f acc[NMT][2];
+            // one group of 32 heads at a time: its MFMAs, then its part of the
+            // head sum (32 accumulator registers live instead of 32 NMT)
+            float s = 0.0f;
 #pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
+            for (int mt = 0; mt < NMT; ++mt) {
+                v16f acc[2];
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    acc[mt][nt] = v16f{};
+                    acc[nt] = v16f{};
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) acc[mt][nt] = mfma_scaled(A[t][mt][ks], B[nt][ks], acc[mt][nt], SA[t][mt], 4);
+                    for (int ks = 0; ks < 2; ++ks)
+                        acc[nt] = mfma_scaled(A[t][mt][ks], widen(bf.k[nt][ks]), acc[nt], SA[t][mt], 4);
                 }
-            const float s = head_sum<NMT>(acc, w + (int64_t)(r0 + t) * H);
+                if (mt == NMT - 1 && (t == nq - 1 || t == TQ - 1)) fetch(bf, p_next);
+                s = head_sum_32(acc, w + (int64_t)(r0 + t) * H + 32 * mt, s);
+                // keep the next group's MFMAs after this head sum, so that
+                // only one group's accumulators are live at a time
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if (jl < n) {
                 const bool visible = jl < vis[t];
-                const float sc = visible ? ldexpf(s, ek - 127) : -INFINITY;
-                scores[(int64_t)(r0 + t) * stride + jl] = sc;
-                if (HIST && visible) atomicAdd(&hl[t * kHistBins + score_bin(sc)], 1u);
+                const float sc = visible ? ldexpf(s, (int)ekl[p0 - c0 + lane] - 127) : -INFINITY;
+                if constexpr (LOCAL)
+                    sl[t][p0 - c0 + lane] = sc;
+                else
+                    scores[(int64_t)(r0 + t) * stride + jl] = sc;
+                if (HIST && visible) hist16_add(hl + t * (kHistBins / 2), score_bin(sc));
             }
         }
+    };
+    // X's loads are issued before Y's, here as in the loop, so that the wait
+    // at the top of the loop can leave Y's loads in flight (vmcnt counts in
+    // issue order); a wave without tiles reads the chunk's first tile, so that
+    // every wave reaches the staging below with the same loads in flight
+    Buf X, Y;
+    const int64_t p_first = n_tiles > 0 ? p_w : c0;
+    fetch(X, p_first);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(Y, n_tiles > 1 ? p_w + 256 : p_first);
+    __builtin_amdgcn_sched_barrier(0);
+    // keep the loads above this point (they would otherwise sink to their first
+    // use, behind the staging's wait)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < chunk / 256; ++j) ekl[64 * wave + 256 * j + lane] = sb[j];
+    // pairs of tiles, then an odd last one: the loop body has no exit of its
+    // own, so every path into the loop header has the same loads in flight
+    int i = 0;
+    for (; i + 1 < n_tiles; i += 2) {
+        const int64_t p0 = p_w + 256 * (int64_t)i;
+        tile(X, p0, p0 + 512 <= p_last ? p0 + 512 : p_last);
+        tile(Y, p0 + 256, p0 + 768 <= p_last ? p0 + 768 : p_last);
     }
-    if (HIST) {
-        __syncthreads();
-        for (int t = 0; t < TQ && t < nq; ++t) hist_flush(hl + t * kHistBins, hist + (int64_t)(r0 + t) * kHistBins);
+    if (i < n_tiles) tile(X, p_last, p_last);
+    if (!HIST) return;
+    __syncthreads();
+    if constexpr (LOCAL) {
+        const int tid = threadIdx.x;
+        for (int t = 0; t < TQ && t < nq; ++t) {
+            const int row = r0 + t;
+            const int64_t nv64 = vis[t] - c0;
+            const int nv = nv64 <= 0 ? 0 : (nv64 < c1 - c0 ? (int)nv64 : (int)(c1 - c0));
+            const uint32_t kk = (uint32_t)(nv < lo.K ? nv : lo.K);
+            const uint32_t bstar = threshold_bin(PackedBins{hl + t * (kHistBins / 2)}, kk, wtot, &found);
+            // the chunk's candidates in position order: thread tid owns positions
+            // [PER tid, PER tid + PER) of the chunk; one block-wide scan of the
+            // per-thread counts places every thread's run in the list
+            constexpr int PER = chunk / 256;
+            float v[PER];
+#pragma unroll
+            for (int j = 0; j < PER; j += 4) {
+                const v4f x = *reinterpret_cast<const v4f*>(&sl[t][PER * tid + j]);
+                v[j] = x[0];
+                v[j + 1] = x[1];
+                v[j + 2] = x[2];
+                v[j + 3] = x[3];
+            }
+            uint32_t take = 0;
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+                take |= (uint32_t)(kk > 0 && PER * tid + j < nv && score_bin(v[j]) >= bstar) << j;
+            const uint32_t mine = (uint32_t)__popc(take);
+            uint32_t off = block_scan_256(mine, wtot) - mine;
+            const uint32_t base = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+            // the list through LDS (chunk offsets), then written out coalesced
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+                if ((take >> j) & 1u) pos16[off++] = (uint16_t)(PER * tid + j);
+            __syncthreads();
+            uint64_t* lr = lo.lists + ((int64_t)row * lo.max_chunks + blockIdx.x) * chunk;
+            for (uint32_t i = tid; i < base; i += 256) {
+                const uint32_t pl = pos16[i];
+                lr[i] = composite(score_key(sl[t][pl]), (uint32_t)(c0 + pl));
+            }
+            if (tid == 0) lo.counts[(int64_t)row * lo.max_chunks + blockIdx.x] = base;
+            if (lo.bscores) {  // block maxima over the visible positions of the chunk's blocks
+                const int64_t nb = (vis[t] + lo.block - 1) / lo.block;
+                for (int lb = tid; lb < chunk / lo.block; lb += 256) {
+                    const int64_t blk = c0 / lo.block + lb;
+                    if (blk >= nb) break;
+                    float mx = -INFINITY;
+                    for (int j = lb * lo.block; j < (lb + 1) * lo.block && j < nv; ++j) mx = fmaxf(mx, sl[t][j]);
+                    lo.bscores[(int64_t)row * lo.bstride + blk] = mx;
+                }
+            }
+            // Only the bins from the chunk's threshold up reach the row's
+            // histogram.  The row's threshold bin B is at or above the threshold
+            // of every chunk with at least K visible positions (such a chunk
+            // alone has K positions at or above its threshold), and a chunk with
+            // fewer flushes all its bins, so the row's counts at and above B are
+            // complete, which is all the threshold search reads.
+            hist16_flush(hl + t * (kHistBins / 2), hist + (int64_t)row * kHistBins, kk ? bstar : (uint32_t)kHistBins);
+            __syncthreads();  // threshold_bin's LDS scratch is reused by the next row
+        }
+    } else {
+        for (int t = 0; t < TQ && t < nq; ++t)
+            hist16_flush(hl + t * (kHistBins / 2), hist + (int64_t)(r0 + t) * kHistBins);
     }
 }
 
@@ -547,19 +690,25 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
         return hipGetLastError();
     }
     if (a.q_fmt == CSA2_Q_FP4 && a.g.max_q_per_seq <= 4) {
-        const int chunk = 4096;
-        dim3 grid((unsigned)((a.g.max_entries + chunk - 1) / chunk), a.g.n_seq);
-#define CSA2_DEC(HH, TT, HI)                                                                                     \
-    hipLaunchKernelGGL((k_score_decode<HH, TT, HI>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,      \
-                       b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, chunk, a.hist)
         const bool one = a.g.max_q_per_seq <= 1;
-        if (a.H == 64) {
-            if (a.hist) { if (one) CSA2_DEC(64, 1, true); else CSA2_DEC(64, 4, true); }
-            else { if (one) CSA2_DEC(64, 1, false); else CSA2_DEC(64, 4, false); }
-        } else {
-            if (a.hist) { if (one) CSA2_DEC(32, 1, true); else CSA2_DEC(32, 4, true); }
-            else { if (one) CSA2_DEC(32, 1, false); else CSA2_DEC(32, 4, false); }
-        }
+        const int out = a.local ? kOutLocal : (a.hist ? kOutHist : kOutScores);
+        const int chunk = decode_chunk(one ? 1 : 4, out == kOutLocal);
+        const LocalOut lo = a.local ? *a.local : LocalOut{};
+        dim3 grid((unsigned)((a.g.max_entries + chunk - 1) / chunk), a.g.n_seq);
+#define CSA2_DEC(HH, TT, OO)                                                                                     \
+    hipLaunchKernelGGL((k_score_decode<HH, TT, OO>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,      \
+                       b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, a.hist, lo)
+#define CSA2_DEC_T(HH, OO) \
+    do { if (one) CSA2_DEC(HH, 1, OO); else CSA2_DEC(HH, 4, OO); } while (0)
+#define CSA2_DEC_O(HH)                                                       \
+    do {                                                                     \
+        if (out == kOutLocal) CSA2_DEC_T(HH, kOutLocal);                     \
+        else if (out == kOutHist) CSA2_DEC_T(HH, kOutHist);                  \
+        else CSA2_DEC_T(HH, kOutScores);                                     \
+    } while (0)
+        if (a.H == 64) CSA2_DEC_O(64); else CSA2_DEC_O(32);
+#undef CSA2_DEC_O
+#undef CSA2_DEC_T
 #undef CSA2_DEC
         return hipGetLastError();
     }

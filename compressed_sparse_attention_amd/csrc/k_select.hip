@@ -52,15 +52,6 @@ __device__ __forceinline__ int64_t row_n(const RowSrc& rs, int row) {
     return rs.block_mode ? (vis + rs.block - 1) / rs.block : vis;
 }
 
-__device__ __forceinline__ uint32_t score_key(float s) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, s);
-    return (u & 0x80000000u) ? 0u : u;  // contract: scores >= +0; anything negative orders as +0
-}
-
-__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t slot) {
-    return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - slot);
-}
-
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -95,54 +86,6 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ scores, 
         if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// Block-wide: the bin that holds the kk-th largest key of the row (every
-// thread returns it); kHistBins when kk == 0.
-// Inclusive scan of one value per thread over a 256-thread workgroup: a
-// shuffle scan inside each wave, then the wave totals through LDS.
-__device__ uint32_t block_scan_256(uint32_t v, uint32_t* wtot) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t u = __shfl_up(v, off);
-        if (lane >= off) v += u;
-    }
-    if (lane == 63) wtot[wave] = v;
-    __syncthreads();
-    for (int w2 = 0; w2 < wave; ++w2) v += wtot[w2];
-    return v;
-}
-
-// Block-wide: the bin that holds the kk-th largest key of the row (every
-// thread returns it); kHistBins when kk == 0.
-__device__ uint32_t threshold_bin(const uint32_t* __restrict__ h, uint32_t kk, uint32_t* wtot, uint32_t* found) {
-    const int t = threadIdx.x;
-    // thread t owns bins [4096 - 16(t+1), 4096 - 16t), i.e. thread 0 the top bins
-    const int hi = kHistBins - 16 * t;
-    uint32_t c[16];
-    uint32_t s = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        c[i] = h[hi - 1 - i];
-        s += c[i];
-    }
-    if (t == 0) *found = kk == 0 ? (uint32_t)kHistBins : 0u;
-    const uint32_t incl = block_scan_256(s, wtot);
-    const uint32_t before = incl - s;
-    if (kk > 0 && before < kk && kk <= incl) {
-        uint32_t acc = before;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            acc += c[i];
-            if (acc >= kk) {
-                *found = (uint32_t)(hi - 1 - i);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-    return *found;
-}
-
 // Candidates: every slot whose bin is at or above the threshold bin goes to
 // the row's candidate list.  A workgroup first gathers its candidates in LDS
 // and then reserves room in the row's list with a single atomic (a returning
@@ -175,7 +118,7 @@ __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ score
     }
     if (threadIdx.x == 0) lcount = 0;
     const uint32_t kk = (uint32_t)(n < K ? n : K);
-    const uint32_t bin = threshold_bin(hist + (int64_t)row * kHistBins, kk, part, &found);
+    const uint32_t bin = threshold_bin(PlainBins{hist + (int64_t)row * kHistBins}, kk, part, &found);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         sel[row].n = (uint32_t)n;
         sel[row].kk = kk;
@@ -207,6 +150,67 @@ __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ score
     if (cnt > (uint32_t)kLocalCand) return;  // row overflowed: k_final selects it from the scores
     uint64_t* cb = cand_buf + (int64_t)row * kCandCap;
     for (uint32_t i = threadIdx.x; i < cnt; i += 256)
+        if (gbase + i < (uint32_t)kCandCap) cb[gbase + i] = lc[i];
+}
+
+// The same filter over a decode scan's per-chunk lists (LocalOut): workgroup
+// (c, row) reads chunk c's list of the row, which already holds key64 values.
+__global__ __launch_bounds__(256) void k_collect_local(const uint64_t* __restrict__ lists,
+                                                       const uint32_t* __restrict__ counts, int max_chunks,
+                                                       int chunk, RowSrc rs, const uint32_t* __restrict__ hist,
+                                                       int K, RowSel* __restrict__ sel,
+                                                       uint64_t* __restrict__ cand_buf) {
+    constexpr int U = 4096 / 256;  // chunk <= 4096
+    __shared__ uint32_t part[4];
+    __shared__ uint32_t found;
+    __shared__ uint64_t lc[kLocalCand];
+    __shared__ uint32_t lcount, gbase;
+    const int row = blockIdx.y;
+    const int64_t n = row_n(rs, row);
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+    if (c0 >= n && blockIdx.x != 0) return;
+    const uint32_t cnt = c0 < n ? counts[(int64_t)row * max_chunks + blockIdx.x] : 0u;
+    const uint64_t* lr = lists + ((int64_t)row * max_chunks + blockIdx.x) * chunk;
+    uint64_t key[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t i = threadIdx.x + 256 * u;
+        key[u] = i < cnt ? lr[i] : 0ull;
+    }
+    if (threadIdx.x == 0) lcount = 0;
+    const uint32_t kk = (uint32_t)(n < K ? n : K);
+    const uint32_t bin = threshold_bin(PlainBins{hist + (int64_t)row * kHistBins}, kk, part, &found);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        sel[row].n = (uint32_t)n;
+        sel[row].kk = kk;
+        sel[row].bin = bin;
+    }
+    if (bin >= (uint32_t)kHistBins || cnt == 0) return;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t i = threadIdx.x + 256 * u;
+        const bool take = i < cnt && (uint32_t)(key[u] >> 51) >= bin;
+        const uint64_t m = __ballot(take);
+        if (m) {
+            uint32_t p0 = 0;
+            if (lane == 0) p0 = atomicAdd(&lcount, (uint32_t)__popcll(m));
+            p0 = __shfl(p0, 0);
+            if (take) {
+                const uint32_t p = p0 + (uint32_t)__popcll(m & ((1ull << lane) - 1));
+                if (p < (uint32_t)kLocalCand) lc[p] = key[u];
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t nc = lcount;
+    if (nc == 0) return;
+    if (threadIdx.x == 0)
+        gbase = atomicAdd(&sel[row].cnt, nc <= (uint32_t)kLocalCand ? nc : (uint32_t)kCandCap + 1u);
+    __syncthreads();
+    if (nc > (uint32_t)kLocalCand) return;  // row overflowed: k_final selects it from the lists
+    uint64_t* cb = cand_buf + (int64_t)row * kCandCap;
+    for (uint32_t i = threadIdx.x; i < nc; i += 256)
         if (gbase + i < (uint32_t)kCandCap) cb[gbase + i] = lc[i];
 }
 
@@ -264,15 +268,23 @@ __device__ __forceinline__ int32_t map_slot(const int32_t* cand, int cand_stride
     return cand ? cand[(int64_t)row * cand_stride + slot] : (int32_t)slot;
 }
 
+// Where an overflowed row's elements are read from: the score row, or the
+// scan's per-chunk lists (lists != nullptr), each in position order.
+struct FallbackSrc {
+    const uint64_t* lists;
+    const uint32_t* counts;
+    int max_chunks, chunk;
+};
+
 // One workgroup per row: exact selection of the kk winners by key64 and their
 // output in ascending position order.  Rows whose candidate list fitted are
 // selected from the list in LDS; rows whose list overflowed (heavy ties) are
-// selected from the scores themselves (the same radix select reading the row
-// at every level, then an in-order compaction).
+// selected from all their elements (the same radix select reading them at
+// every level, then an in-order compaction).
 __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores, int64_t stride,
                                                 const RowSel* __restrict__ sel, const uint64_t* __restrict__ cand_buf,
                                                 const int32_t* __restrict__ cand, int cand_stride, int K,
-                                                int32_t* __restrict__ idx) {
+                                                int32_t* __restrict__ idx, FallbackSrc fb) {
     __shared__ uint64_t c[kCandCap];
     __shared__ uint32_t winners[kMaxK];
     __shared__ uint32_t hist256[256], scan256[256];
@@ -299,16 +311,29 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         base = 0;
     }
     __syncthreads();
+    const bool from_lists = !from_list && fb.lists;
+    const int n_chunks = from_lists ? (int)((n + fb.chunk - 1) / fb.chunk) : 1;
     const int64_t m_elems = from_list ? (int64_t)cnt : n;
     while (!st.done) {
         for (int i = threadIdx.x; i < 256; i += 1024) hist256[i] = 0;
         __syncthreads();
         const int sh = st.shift;
         const uint64_t pf = st.prefix;
-        for (int64_t i = threadIdx.x; i < m_elems; i += 1024) {
-            const uint64_t x = from_list ? c[i] : composite(score_key(sr[i]), (uint32_t)i);
-            const bool m = sh >= 64 ? true : ((x >> sh) == pf);
-            if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - 8)) & 255u], 1u);
+        if (from_lists) {
+            for (int ch = 0; ch < n_chunks; ++ch) {
+                const uint32_t cn = fb.counts[(int64_t)row * fb.max_chunks + ch];
+                const uint64_t* lr = fb.lists + ((int64_t)row * fb.max_chunks + ch) * fb.chunk;
+                for (uint32_t i = threadIdx.x; i < cn; i += 1024) {
+                    const uint64_t x = lr[i];
+                    if (sh >= 64 || (x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - 8)) & 255u], 1u);
+                }
+            }
+        } else {
+            for (int64_t i = threadIdx.x; i < m_elems; i += 1024) {
+                const uint64_t x = from_list ? c[i] : composite(score_key(sr[i]), (uint32_t)i);
+                const bool m = sh >= 64 ? true : ((x >> sh) == pf);
+                if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - 8)) & 255u], 1u);
+            }
         }
         __syncthreads();
         radix_step(hist256, scan256, &st, &found);
@@ -339,31 +364,36 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         }
         return;
     }
-    // overflowed row: in-order compaction over all slots
+    // overflowed row: in-order compaction over all elements (position order)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int64_t s0 = 0; s0 < n; s0 += 1024) {
-        const int64_t s = s0 + threadIdx.x;
-        bool win = false;
-        if (s < n) {
-            const uint64_t x = composite(score_key(sr[s]), (uint32_t)s);
-            win = sh >= 64 ? true : ((x >> sh) >= pf);
+    for (int ch = 0; ch < n_chunks; ++ch) {
+        const int64_t cn = from_lists ? (int64_t)fb.counts[(int64_t)row * fb.max_chunks + ch] : n;
+        const uint64_t* lr = from_lists ? fb.lists + ((int64_t)row * fb.max_chunks + ch) * fb.chunk : nullptr;
+        for (int64_t s0 = 0; s0 < cn; s0 += 1024) {
+            const int64_t s = s0 + threadIdx.x;
+            bool win = false;
+            uint64_t x = 0;
+            if (s < cn) {
+                x = from_lists ? lr[s] : composite(score_key(sr[s]), (uint32_t)s);
+                win = sh >= 64 ? true : ((x >> sh) >= pf);
+            }
+            const uint64_t m = __ballot(win);
+            if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
+            __syncthreads();
+            uint32_t off = base;
+            for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2];
+            if (win) {
+                const uint32_t p = off + (uint32_t)__popcll(m & ((1ull << lane) - 1));
+                if (p < kk) out[p] = map_slot(cand, cand_stride, row, 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu));
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                uint32_t tot = 0;
+                for (int w2 = 0; w2 < 16; ++w2) tot += wsum[w2];
+                base += tot;
+            }
+            __syncthreads();
         }
-        const uint64_t m = __ballot(win);
-        if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
-        __syncthreads();
-        uint32_t off = base;
-        for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2];
-        if (win) {
-            const uint32_t p = off + (uint32_t)__popcll(m & ((1ull << lane) - 1));
-            if (p < kk) out[p] = map_slot(cand, cand_stride, row, (uint32_t)s);
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            uint32_t tot = 0;
-            for (int w2 = 0; w2 < 16; ++w2) tot += wsum[w2];
-            base += tot;
-        }
-        __syncthreads();
     }
 }
 
@@ -473,7 +503,24 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL(k_collect, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, h, a.K,
                        sel, cb);
     hipLaunchKernelGGL(k_final, dim3(nq), dim3(1024), 0, s, a.scores, a.stride, sel, cb, a.cand, a.cand_stride, a.K,
-                       a.idx);
+                       a.idx, FallbackSrc{nullptr, nullptr, 0, 1});
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_local(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, void* ws,
+                             hipStream_t s) {
+    const int nq = g.total_q;
+    char* w = (char*)ws;
+    const uint32_t* hist = (const uint32_t*)w;
+    w += al256((size_t)nq * kHistBins * 4);
+    RowSel* sel = (RowSel*)w;
+    w += al256((size_t)nq * sizeof(RowSel));
+    uint64_t* cb = (uint64_t*)w;
+    RowSrc rs{b->d_entry_off, b->d_row_seq, b->d_q_pos, b->ratio, nullptr, 0, 1, g.max_entries};
+    hipLaunchKernelGGL(k_collect_local, dim3((unsigned)lo.max_chunks, nq), dim3(256), 0, s, lo.lists, lo.counts,
+                       lo.max_chunks, lo.chunk, rs, hist, lo.K, sel, cb);
+    hipLaunchKernelGGL(k_final, dim3(nq), dim3(1024), 0, s, (const float*)nullptr, (int64_t)0, sel, cb,
+                       (const int32_t*)nullptr, 0, lo.K, idx, FallbackSrc{lo.lists, lo.counts, lo.max_chunks, lo.chunk});
     return hipGetLastError();
 }
 
@@ -481,8 +528,9 @@ hipError_t launch_block_pool(const PoolLaunch& a, hipStream_t s) {
     RowSrc rs{a.b->d_entry_off, a.b->d_row_seq, a.b->d_q_pos, a.b->ratio, nullptr, 1, a.block,
               (a.g.max_entries + a.block - 1) / a.block};
     const int64_t max_nb = (a.g.max_entries + a.block - 1) / a.block;
-    hipLaunchKernelGGL(k_block_max, dim3((unsigned)((max_nb + 255) / 256), a.g.total_q), dim3(256), 0, s, a.scores,
-                       a.stride, rs, a.bscores, a.bstride);
+    if (!a.bscores_ready)
+        hipLaunchKernelGGL(k_block_max, dim3((unsigned)((max_nb + 255) / 256), a.g.total_q), dim3(256), 0, s, a.scores,
+                           a.stride, rs, a.bscores, a.bstride);
     TopkLaunch t{};
     t.b = a.b;
     t.g = a.g;

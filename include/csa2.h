@@ -200,7 +200,11 @@ CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, const uint8_t*
  * q_bf16: [total_q][Hm][512]; swa_bf16: [rows][512] laid out by `swa`;
  * out: [total_q][Hm][512] f32; lse: [total_q][Hm] f32 or NULL (all device).
  * Supported: Hm a multiple of 16, 1 <= K <= 2048, window <= 1024.
- * Workspace: none today (ws may be NULL, ws_bytes 0). */
+ * Workspace (optional): with csa2_workspace_size(CSA2_WS_SPARSE_ATTN, ...)
+ * bytes the call may split each row's keys over several workgroups when the
+ * batch is small and merge the parts; with less (or NULL) it splits less (or
+ * not at all).  Results agree either way within the tolerance of a softmax
+ * merge, not bit for bit. */
 CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16,
                                       const uint8_t* kv_fp4, const uint8_t* kv_sc, const int32_t* idx, int32_t K,
                                       const uint16_t* swa_bf16, const csa2_swa_layout* swa, float softmax_scale,

@@ -248,6 +248,39 @@ def test_layer_chain_matches_oracle(case):
             assert np.array_equal(pc.cpu().numpy(), r["pool_count"])
 
 
+TIE_CASES = {
+    # every score 0 (all head weights 0): each chunk keeps all its positions,
+    # the rows overflow the candidate list and take the exact fallback
+    "all_equal_t1": dict(lens=[3, 700, 9000, 20000], T=1, heads=0),
+    "all_equal_t4": dict(lens=[5, 3000, 20000], T=4, heads=0),
+    # one head: few distinct scores, long runs of ties at the thresholds
+    "one_head_t1": dict(lens=[3, 700, 9000, 20000], T=1, heads=1),
+    "one_head_t4": dict(lens=[5, 3000, 20000], T=4, heads=1),
+}
+
+
+@pytest.mark.parametrize("case", list(TIE_CASES))
+def test_layer_chain_ties(case):
+    c = TIE_CASES[case]
+    wl = synth.make_workload(case, 0xC5A2E000 + len(case), c["lens"], c["T"],
+                             [(20, synth.MODE_FULL, True), (24, synth.MODE_REINDEX, False), (25, synth.MODE_REUSE, False)],
+                             Hm=16)
+    for L in wl.layers:
+        if L.w is not None:
+            L.w[:, c["heads"]:] = 0.0
+    dw = DevWorkload(wl)
+    outs, (pb, pp, pc), _ = run_chain(dw)
+    torch.cuda.synchronize()
+    ref = oracle.layer_chain(wl)
+    for o, r in zip(outs, ref):
+        assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"layer {r['layer']} indices"
+        assert_close_attn(o["out"].cpu().numpy(), r["out"], f"layer {r['layer']}")
+        if "pool_pos" in r:
+            assert np.array_equal(pb.cpu().numpy(), r["blocks"])
+            assert np.array_equal(pp.cpu().numpy(), r["pool_pos"])
+            assert np.array_equal(pc.cpu().numpy(), r["pool_count"])
+
+
 def test_layer_chain_equals_composition():
     """The chain's indices and outputs equal those of the individual calls."""
     wl = synth.config("chain_c2", n_seq=2, n=20000, Hm=16,
