@@ -49,7 +49,8 @@ class csa2_layer(ctypes.Structure):
 
 class csa2_chain_params(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("Hm", ctypes.c_int32), ("K", ctypes.c_int32), ("block", ctypes.c_int32),
-                ("max_blocks", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("max_blocks", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("scan_begin", ctypes.c_void_p), ("scan_end", ctypes.c_void_p)]
 
 
 class CSA2Error(RuntimeError):

@@ -104,6 +104,17 @@ ChainWs chain_ws(const Geometry& g, int K, int block, int max_blocks) {
     return w;
 }
 
+// The index scan of a Full layer, between the caller's events the first time.
+hipError_t timed_scan(const ScoreLaunch& sa, const csa2_chain_params* p, bool* timed, hipStream_t stream) {
+    const bool rec = !*timed && (p->scan_begin || p->scan_end);
+    hipError_t e;
+    if (rec && p->scan_begin && (e = hipEventRecord(p->scan_begin, stream)) != hipSuccess) return e;
+    if ((e = launch_index_score(sa, stream)) != hipSuccess) return e;
+    if (rec && p->scan_end && (e = hipEventRecord(p->scan_end, stream)) != hipSuccess) return e;
+    *timed = true;
+    return hipSuccess;
+}
+
 __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -334,6 +345,7 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
 
     const csa2_layer* src = nullptr;  // latest Full layer (main KV + indexer K)
     bool pool_built = false;
+    bool scan_timed = false;  // the caller's scan events go round the first Full layer's scan
     for (int l = 0; l < n_layers; ++l) {
         const csa2_layer& L = layers[l];
         const int32_t* use_idx = idx_cur;
@@ -362,7 +374,7 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                 if ((e = clear_topk_ws(topk_ws, g.total_q, true, stream)) != hipSuccess) return hip_fail(e);
                 ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, L.k_fp4, L.k_sc,
                                nullptr, 0, nullptr, 0, topk_ws_hist(topk_ws), &lo};
-                if ((e = launch_index_score(sa, stream)) != hipSuccess) return hip_fail(e);
+                if ((e = timed_scan(sa, p, &scan_timed, stream)) != hipSuccess) return hip_fail(e);
                 if ((e = launch_topk_local(batch, g, lo, idx_cur, topk_ws, stream)) != hipSuccess) return hip_fail(e);
                 if (build_pool) {  // after the Top-K: the pool's selection reuses its workspace
                     PoolLaunch pa{};
@@ -390,7 +402,8 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                                on_pool ? pp : nullptr, on_pool ? pool_stride : 0, on_pool ? pscores : scores,
                                on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1),
                                fused ? topk_ws_hist(topk_ws) : nullptr};
-                if ((e = launch_index_score(sa, stream)) != hipSuccess) return hip_fail(e);
+                if ((e = full ? timed_scan(sa, p, &scan_timed, stream) : launch_index_score(sa, stream)) != hipSuccess)
+                    return hip_fail(e);
                 TopkLaunch ta{};
                 ta.b = batch;
                 ta.g = g;

@@ -29,6 +29,8 @@ struct RowSel {
     uint32_t kk;       // min(K, n)
     uint32_t bin;      // threshold bin (candidates have bin >= this)
     uint32_t cnt;      // candidates collected (may exceed kCandCap -> fallback)
+    uint32_t above;    // keys in the bins above the threshold bin (all of them win)
+    uint32_t pad[3];
 };
 
 struct Geometry {
@@ -89,8 +91,9 @@ struct PackedBins {
 };
 
 // Block-wide (256 threads): the bin that holds the kk-th largest key; every
-// thread returns it; kHistBins when kk == 0.  `found` and `wtot` are LDS
-// scratch; a caller that calls it again must pass a barrier first.
+// thread returns it; kHistBins when kk == 0.  found[0..1] (LDS) end up holding
+// the bin and the count of keys in the bins above it.  `found` and `wtot` are
+// LDS scratch; a caller that calls it again must pass a barrier first.
 template <class Bins>
 __device__ inline uint32_t threshold_bin(Bins h, uint32_t kk, uint32_t* wtot, uint32_t* found) {
     const int t = threadIdx.x;
@@ -103,22 +106,26 @@ __device__ inline uint32_t threshold_bin(Bins h, uint32_t kk, uint32_t* wtot, ui
         c[i] = h(hi - 1 - i);
         s += c[i];
     }
-    if (t == 0) *found = kk == 0 ? (uint32_t)kHistBins : 0u;
+    if (t == 0) {
+        found[0] = kk == 0 ? (uint32_t)kHistBins : 0u;
+        found[1] = 0;
+    }
     const uint32_t incl = block_scan_256(s, wtot);
     const uint32_t before = incl - s;
     if (kk > 0 && before < kk && kk <= incl) {
         uint32_t acc = before;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            acc += c[i];
-            if (acc >= kk) {
-                *found = (uint32_t)(hi - 1 - i);
+            if (acc + c[i] >= kk) {
+                found[0] = (uint32_t)(hi - 1 - i);
+                found[1] = acc;
                 break;
             }
+            acc += c[i];
         }
     }
     __syncthreads();
-    return *found;
+    return found[0];
 }
 
 // ---------------------------------------------------------------------------

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(64) void k_gather_dequant(const uint8_t* __restrict
 // ---------------------------------------------------------------------------
 constexpr int HG = 16;
 constexpr int KB = 64;
-constexpr int LROW = 512 + 8;  // LDS row stride in bf16 (16 B of padding)
+constexpr int LROW = 512 + 8;  // LDS row stride of the staged keys in bf16 (16 B of padding)
+constexpr int SLROW = KB + 4;  // LDS row stride of the logits in floats
 
 __global__ __launch_bounds__(256) void k_sparse_attn(
     const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     float scale_log2, float* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg, int S,
     float* __restrict__ partial) {
     __shared__ __attribute__((aligned(16))) uint16_t kl[KB * LROW];
-    __shared__ float sl[HG][KB];
+    __shared__ float sl[HG][SLROW];
     __shared__ int kvalid[KB];
     __shared__ int32_t kidx[kMaxK];
     __shared__ int nsel_sh;
@@ -146,10 +147,12 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     // fp32 weights (it gives the log-sum-exp)
     float m_run = -INFINITY, l_run = 0.0f, l_lse = 0.0f;
 
-    // this thread stages key tid/4 of each block, channels 128*(tid%4) .. +128;
+    // this thread stages key `skey` of each block, channels 128*part .. +128;
     // the main-KV part of the next block is fetched into registers while the
     // current block computes
-    const int skey = tid >> 2, part = tid & 3;
+    // (16 consecutive lanes take 16 keys of one part, so that their LDS
+    // writes of a row segment fall in distinct banks)
+    const int skey = (tid & 15) + 16 * (tid >> 6), part = (tid >> 4) & 3;
     v4i pc[4];
     uint32_t psc = 0;
     auto fetch = [&](int blk) {
@@ -331,6 +334,7 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
 // threads per (row, head); thread t owns channels 4t .. 4t+3, so every load of
 // the merge is issued at once.
 constexpr int kMaxSplit = 8;
+constexpr int kAttnTargetWgs = 256;  // workgroups the key splits aim for (more splits cost more than they hide)
 
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part, int Hm, int n_hg, int S,
                                                       float* __restrict__ out, float* __restrict__ lse) {
@@ -386,7 +390,7 @@ int attn_splits(const Geometry& g, int Hm, int K, int W) {
     // the grid would otherwise leave the chip under-filled (< 2 per CU)
     const int units = g.total_q * (Hm / HG);
     const int max_blocks = (K + W + KB - 1) / KB;
-    int S = (512 + units - 1) / units;
+    int S = (kAttnTargetWgs + units - 1) / units;
     S = S < 1 ? 1 : (S > kMaxSplit ? kMaxSplit : S);
     return S < max_blocks ? S : max_blocks;
 }

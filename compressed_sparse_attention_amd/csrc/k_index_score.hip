@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     __shared__ uint32_t hl[HIST ? TQ * kHistBins / 2 : 1];
     __shared__ __attribute__((aligned(16))) float sl[LOCAL ? TQ : 1][LOCAL ? chunk : 1];  // the chunk's scores per row
     __shared__ uint8_t ekl[chunk];                           // the chunk's indexer K scales
-    __shared__ uint32_t wtot[4], found;
+    __shared__ uint32_t wtot[4], found[2];
     __shared__ uint16_t pos16[LOCAL ? chunk : 1];  // a row's candidate offsets in the chunk
     const int b = blockIdx.y;
     const int64_t e0 = entry_off[b];
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
             const int64_t nv64 = vis[t] - c0;
             const int nv = nv64 <= 0 ? 0 : (nv64 < c1 - c0 ? (int)nv64 : (int)(c1 - c0));
             const uint32_t kk = (uint32_t)(nv < lo.K ? nv : lo.K);
-            const uint32_t bstar = threshold_bin(PackedBins{hl + t * (kHistBins / 2)}, kk, wtot, &found);
+            const uint32_t bstar = threshold_bin(PackedBins{hl + t * (kHistBins / 2)}, kk, wtot, found);
             // the chunk's candidates in position order: thread tid owns positions
             // [PER tid, PER tid + PER) of the chunk; one block-wide scan of the
             // per-thread counts places every thread's run in the list

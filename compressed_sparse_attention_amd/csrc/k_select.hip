@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ score
                                                  const uint32_t* __restrict__ hist, int K, RowSel* __restrict__ sel,
                                                  uint64_t* __restrict__ cand_buf) {
     __shared__ uint32_t part[4];
-    __shared__ uint32_t found;
+    __shared__ uint32_t found[2];
     __shared__ uint64_t lc[kLocalCand];
     __shared__ uint32_t lcount, gbase;
     const int row = blockIdx.y;
@@ -118,11 +118,12 @@ __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ score
     }
     if (threadIdx.x == 0) lcount = 0;
     const uint32_t kk = (uint32_t)(n < K ? n : K);
-    const uint32_t bin = threshold_bin(PlainBins{hist + (int64_t)row * kHistBins}, kk, part, &found);
+    const uint32_t bin = threshold_bin(PlainBins{hist + (int64_t)row * kHistBins}, kk, part, found);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         sel[row].n = (uint32_t)n;
         sel[row].kk = kk;
         sel[row].bin = bin;
+        sel[row].above = found[1];
     }
     if (bin >= (uint32_t)kHistBins || s0 >= n) return;
     const int lane = threadIdx.x & 63;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256) void k_collect_local(const uint64_t* __restric
                                                        uint64_t* __restrict__ cand_buf) {
     constexpr int U = 4096 / 256;  // chunk <= 4096
     __shared__ uint32_t part[4];
-    __shared__ uint32_t found;
+    __shared__ uint32_t found[2];
     __shared__ uint64_t lc[kLocalCand];
     __shared__ uint32_t lcount, gbase;
     const int row = blockIdx.y;
@@ -172,18 +173,25 @@ __global__ __launch_bounds__(256) void k_collect_local(const uint64_t* __restric
     const uint32_t cnt = c0 < n ? counts[(int64_t)row * max_chunks + blockIdx.x] : 0u;
     const uint64_t* lr = lists + ((int64_t)row * max_chunks + blockIdx.x) * chunk;
     uint64_t key[U];
+    // the first 1024 entries (a list's usual length) are read without waiting
+    // for the count (the list region always holds `chunk` entries; entries
+    // past the count are ignored), the rest once the count is known
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t i = threadIdx.x + 256 * u;
-        key[u] = i < cnt ? lr[i] : 0ull;
+        if (u < 4)
+            key[u] = i < (uint32_t)chunk ? lr[i] : 0ull;
+        else
+            key[u] = i < cnt ? lr[i] : 0ull;
     }
     if (threadIdx.x == 0) lcount = 0;
     const uint32_t kk = (uint32_t)(n < K ? n : K);
-    const uint32_t bin = threshold_bin(PlainBins{hist + (int64_t)row * kHistBins}, kk, part, &found);
+    const uint32_t bin = threshold_bin(PlainBins{hist + (int64_t)row * kHistBins}, kk, part, found);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         sel[row].n = (uint32_t)n;
         sel[row].kk = kk;
         sel[row].bin = bin;
+        sel[row].above = found[1];
     }
     if (bin >= (uint32_t)kHistBins || cnt == 0) return;
     const int lane = threadIdx.x & 63;
@@ -224,6 +232,9 @@ struct RadixState {
     int done;
 };
 
+// digit width at a level: 8 bits, or what realigns `shift` to a multiple of 8
+__device__ __forceinline__ int digit_bits(int shift) { return (shift & 7) ? (shift & 7) : 8; }
+
 // Block-wide (every thread of the workgroup calls it, no divergence around the
 // barriers): given a 256-bin histogram of the current digit among elements that
 // match the fixed prefix, find the digit d with  above(d) < need <= above(d) +
@@ -255,10 +266,11 @@ __device__ void radix_step(const uint32_t* hist256, uint32_t* scan256, RadixStat
     __syncthreads();
     if (t == 0) {
         const int d = *found;
+        const int w = digit_bits(st->shift);
         const uint32_t above = scan256[d], here = hist256[d];
         st->need -= above;
-        st->prefix = (st->prefix << 8) | (uint64_t)d;
-        st->shift -= 8;
+        st->prefix = (st->prefix << w) | (uint64_t)d;
+        st->shift -= w;
         if (here == st->need || st->shift == 0) st->done = 1;
     }
     __syncthreads();
@@ -287,6 +299,7 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
                                                 int32_t* __restrict__ idx, FallbackSrc fb) {
     __shared__ uint64_t c[kCandCap];
     __shared__ uint32_t winners[kMaxK];
+    __shared__ uint32_t part_rank[512];
     __shared__ uint32_t hist256[256], scan256[256];
     __shared__ RadixState st;
     __shared__ uint32_t nwin, base;
@@ -309,6 +322,14 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         st.done = from_list && cnt == kk;  // every candidate wins
         nwin = 0;
         base = 0;
+        if (from_list && !st.done) {
+            // the candidates are the keys of the threshold bin and of the bins
+            // above it (all of which win): select among the threshold bin's keys
+            // only, from bit 51 down
+            st.prefix = sel[row].bin;
+            st.shift = 51;
+            st.need = kk - sel[row].above;
+        }
     }
     __syncthreads();
     const bool from_lists = !from_list && fb.lists;
@@ -318,6 +339,7 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         for (int i = threadIdx.x; i < 256; i += 1024) hist256[i] = 0;
         __syncthreads();
         const int sh = st.shift;
+        const int w = digit_bits(sh);
         const uint64_t pf = st.prefix;
         if (from_lists) {
             for (int ch = 0; ch < n_chunks; ++ch) {
@@ -325,14 +347,14 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
                 const uint64_t* lr = fb.lists + ((int64_t)row * fb.max_chunks + ch) * fb.chunk;
                 for (uint32_t i = threadIdx.x; i < cn; i += 1024) {
                     const uint64_t x = lr[i];
-                    if (sh >= 64 || (x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - 8)) & 255u], 1u);
+                    if (sh >= 64 || (x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
                 }
             }
         } else {
             for (int64_t i = threadIdx.x; i < m_elems; i += 1024) {
                 const uint64_t x = from_list ? c[i] : composite(score_key(sr[i]), (uint32_t)i);
                 const bool m = sh >= 64 ? true : ((x >> sh) == pf);
-                if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - 8)) & 255u], 1u);
+                if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
             }
         }
         __syncthreads();
@@ -352,9 +374,20 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         }
         __syncthreads();
         // ascending output: a winner's rank is the number of winners with a
-        // smaller slot (slots are distinct); every thread reads winners[j] in
-        // lock step, so the reads are LDS broadcasts
+        // smaller slot (slots are distinct); the threads of a wave read
+        // winners[j] in lock step, so the reads are LDS broadcasts
         const int nw = (int)kk;
+        if (nw <= 512) {  // two threads per winner, each counting over half of them
+            const int i = threadIdx.x & 511, half = threadIdx.x >> 9;
+            const uint32_t my = i < nw ? winners[i] : 0xFFFFFFFFu;
+            const int j0 = half ? nw / 2 : 0, j1 = half ? nw : nw / 2;
+            uint32_t r = 0;
+            for (int j = j0; j < j1; ++j) r += winners[j] < my;
+            if (half) part_rank[i] = r;
+            __syncthreads();
+            if (!half && i < nw) out[r + part_rank[i]] = map_slot(cand, cand_stride, row, my);
+            return;
+        }
         for (int i0 = 0; i0 < nw; i0 += 1024) {
             const int i = i0 + (int)threadIdx.x;
             const uint32_t my = i < nw ? winners[i] : 0xFFFFFFFFu;

@@ -245,6 +245,11 @@ typedef struct csa2_chain_params {
     int32_t block;               /* pool block size (8) */
     int32_t max_blocks;          /* pool blocks (<= 2048) */
     float softmax_scale;         /* 1/sqrt(512) for the report's latent */
+    /* Optional (NULL = unused): events recorded on `stream` immediately before
+     * and after the index-scan kernel of the chain's first Full layer, so that
+     * a caller can time that kernel alone. */
+    hipEvent_t scan_begin;
+    hipEvent_t scan_end;
 } csa2_chain_params;
 
 /* pool_blocks [total_q][max_blocks], pool_pos [total_q][max_blocks*block],
