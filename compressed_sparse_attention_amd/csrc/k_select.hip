@@ -154,72 +154,58 @@ __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ score
         if (gbase + i < (uint32_t)kCandCap) cb[gbase + i] = lc[i];
 }
 
-// The same filter over a decode scan's per-chunk lists (LocalOut): workgroup
-// (c, row) reads chunk c's list of the row, which already holds key64 values.
-__global__ __launch_bounds__(256) void k_collect_local(const uint64_t* __restrict__ lists,
-                                                       const uint32_t* __restrict__ counts, int max_chunks,
-                                                       int chunk, RowSrc rs, const uint32_t* __restrict__ hist,
-                                                       int K, RowSel* __restrict__ sel,
-                                                       uint64_t* __restrict__ cand_buf) {
-    constexpr int U = 4096 / 256;  // chunk <= 4096
-    __shared__ uint32_t part[4];
-    __shared__ uint32_t found[2];
-    __shared__ uint64_t lc[kLocalCand];
-    __shared__ uint32_t lcount, gbase;
-    const int row = blockIdx.y;
+// Per row, the threshold bin of its Top-K in the finished histogram (and the
+// count above it), recorded in `sel` for the passes over the scan's lists.
+__global__ __launch_bounds__(256) void k_row_threshold(const uint32_t* __restrict__ hist, RowSrc rs, int K,
+                                                       RowSel* __restrict__ sel) {
+    __shared__ uint32_t wtot[4], found[2];
+    const int row = blockIdx.x;
     const int64_t n = row_n(rs, row);
-    const int64_t c0 = (int64_t)blockIdx.x * chunk;
-    if (c0 >= n && blockIdx.x != 0) return;
-    const uint32_t cnt = c0 < n ? counts[(int64_t)row * max_chunks + blockIdx.x] : 0u;
-    const uint64_t* lr = lists + ((int64_t)row * max_chunks + blockIdx.x) * chunk;
-    uint64_t key[U];
-    // the first 1024 entries (a list's usual length) are read without waiting
-    // for the count (the list region always holds `chunk` entries; entries
-    // past the count are ignored), the rest once the count is known
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t i = threadIdx.x + 256 * u;
-        if (u < 4)
-            key[u] = i < (uint32_t)chunk ? lr[i] : 0ull;
-        else
-            key[u] = i < cnt ? lr[i] : 0ull;
-    }
-    if (threadIdx.x == 0) lcount = 0;
     const uint32_t kk = (uint32_t)(n < K ? n : K);
-    const uint32_t bin = threshold_bin(PlainBins{hist + (int64_t)row * kHistBins}, kk, part, found);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const uint32_t bin = threshold_bin(PlainBins{hist + (int64_t)row * kHistBins}, kk, wtot, found);
+    if (threadIdx.x == 0) {
         sel[row].n = (uint32_t)n;
         sel[row].kk = kk;
         sel[row].bin = bin;
         sel[row].above = found[1];
+        sel[row].cnt = 0;
     }
-    if (bin >= (uint32_t)kHistBins || cnt == 0) return;
-    const int lane = threadIdx.x & 63;
+}
+
+// The same filter over a decode scan's per-chunk lists (LocalOut), with the
+// row's threshold bin from k_row_threshold.
+// Workgroup (c, row) keeps the entries of chunk c's list at or above that bin,
+// compacted in place at the front of the list in position order (the list is
+// read whole into registers first), and records their count in place of the
+// list's.  No atomics: the final pass finds each chunk's run by a prefix sum.
+__global__ __launch_bounds__(256) void k_collect_local(uint64_t* __restrict__ lists, uint32_t* __restrict__ counts,
+                                                       int max_chunks, int chunk,
+                                                       const RowSel* __restrict__ sel) {
+    constexpr int U = 4096 / 256;  // entries per thread; chunk <= 4096
+    __shared__ uint32_t wtot[4];
+    const int row = blockIdx.y;
+    const RowSel rsel = sel[row];
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+    if (c0 >= (int64_t)rsel.n || rsel.kk == 0) return;  // uniform
+    uint32_t* cp = counts + (int64_t)row * max_chunks + blockIdx.x;
+    uint64_t* lr = lists + ((int64_t)row * max_chunks + blockIdx.x) * chunk;
+    const uint32_t cnt = *cp;
+    const uint32_t per = (uint32_t)chunk / 256;  // thread t owns entries [per t, per t + per)
+    const uint32_t i0 = per * threadIdx.x;
+    uint64_t key[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t i = threadIdx.x + 256 * u;
-        const bool take = i < cnt && (uint32_t)(key[u] >> 51) >= bin;
-        const uint64_t m = __ballot(take);
-        if (m) {
-            uint32_t p0 = 0;
-            if (lane == 0) p0 = atomicAdd(&lcount, (uint32_t)__popcll(m));
-            p0 = __shfl(p0, 0);
-            if (take) {
-                const uint32_t p = p0 + (uint32_t)__popcll(m & ((1ull << lane) - 1));
-                if (p < (uint32_t)kLocalCand) lc[p] = key[u];
-            }
-        }
-    }
-    __syncthreads();
-    const uint32_t nc = lcount;
-    if (nc == 0) return;
-    if (threadIdx.x == 0)
-        gbase = atomicAdd(&sel[row].cnt, nc <= (uint32_t)kLocalCand ? nc : (uint32_t)kCandCap + 1u);
-    __syncthreads();
-    if (nc > (uint32_t)kLocalCand) return;  // row overflowed: k_final selects it from the lists
-    uint64_t* cb = cand_buf + (int64_t)row * kCandCap;
-    for (uint32_t i = threadIdx.x; i < nc; i += 256)
-        if (gbase + i < (uint32_t)kCandCap) cb[gbase + i] = lc[i];
+    for (int u = 0; u < U; ++u) key[u] = (uint32_t)u < per && i0 + u < cnt ? lr[i0 + u] : 0ull;
+    uint32_t take = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        take |= (uint32_t)((uint32_t)u < per && i0 + u < cnt && (uint32_t)(key[u] >> 51) >= rsel.bin) << u;
+    const uint32_t mine = (uint32_t)__popc(take);
+    uint32_t off = block_scan_256(mine, wtot) - mine;  // the barrier inside follows every load
+    const uint32_t total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if ((take >> u) & 1u) lr[off++] = key[u];
+    if (threadIdx.x == 0) *cp = total;
 }
 
 // Radix select helpers over key64 with 8-bit digits from the top.  `count`
@@ -280,14 +266,6 @@ __device__ __forceinline__ int32_t map_slot(const int32_t* cand, int cand_stride
     return cand ? cand[(int64_t)row * cand_stride + slot] : (int32_t)slot;
 }
 
-// Where an overflowed row's elements are read from: the score row, or the
-// scan's per-chunk lists (lists != nullptr), each in position order.
-struct FallbackSrc {
-    const uint64_t* lists;
-    const uint32_t* counts;
-    int max_chunks, chunk;
-};
-
 // One workgroup per row: exact selection of the kk winners by key64 and their
 // output in ascending position order.  Rows whose candidate list fitted are
 // selected from the list in LDS; rows whose list overflowed (heavy ties) are
@@ -296,7 +274,7 @@ struct FallbackSrc {
 __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores, int64_t stride,
                                                 const RowSel* __restrict__ sel, const uint64_t* __restrict__ cand_buf,
                                                 const int32_t* __restrict__ cand, int cand_stride, int K,
-                                                int32_t* __restrict__ idx, FallbackSrc fb) {
+                                                int32_t* __restrict__ idx) {
     __shared__ uint64_t c[kCandCap];
     __shared__ uint32_t winners[kMaxK];
     __shared__ uint32_t part_rank[512];
@@ -332,8 +310,6 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         }
     }
     __syncthreads();
-    const bool from_lists = !from_list && fb.lists;
-    const int n_chunks = from_lists ? (int)((n + fb.chunk - 1) / fb.chunk) : 1;
     const int64_t m_elems = from_list ? (int64_t)cnt : n;
     while (!st.done) {
         for (int i = threadIdx.x; i < 256; i += 1024) hist256[i] = 0;
@@ -341,21 +317,10 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         const int sh = st.shift;
         const int w = digit_bits(sh);
         const uint64_t pf = st.prefix;
-        if (from_lists) {
-            for (int ch = 0; ch < n_chunks; ++ch) {
-                const uint32_t cn = fb.counts[(int64_t)row * fb.max_chunks + ch];
-                const uint64_t* lr = fb.lists + ((int64_t)row * fb.max_chunks + ch) * fb.chunk;
-                for (uint32_t i = threadIdx.x; i < cn; i += 1024) {
-                    const uint64_t x = lr[i];
-                    if (sh >= 64 || (x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
-                }
-            }
-        } else {
-            for (int64_t i = threadIdx.x; i < m_elems; i += 1024) {
-                const uint64_t x = from_list ? c[i] : composite(score_key(sr[i]), (uint32_t)i);
-                const bool m = sh >= 64 ? true : ((x >> sh) == pf);
-                if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
-            }
+        for (int64_t i = threadIdx.x; i < m_elems; i += 1024) {
+            const uint64_t x = from_list ? c[i] : composite(score_key(sr[i]), (uint32_t)i);
+            const bool m = sh >= 64 ? true : ((x >> sh) == pf);
+            if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
         }
         __syncthreads();
         radix_step(hist256, scan256, &st, &found);
@@ -397,35 +362,172 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         }
         return;
     }
-    // overflowed row: in-order compaction over all elements (position order)
+    // overflowed row: in-order compaction over all slots
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int ch = 0; ch < n_chunks; ++ch) {
-        const int64_t cn = from_lists ? (int64_t)fb.counts[(int64_t)row * fb.max_chunks + ch] : n;
-        const uint64_t* lr = from_lists ? fb.lists + ((int64_t)row * fb.max_chunks + ch) * fb.chunk : nullptr;
-        for (int64_t s0 = 0; s0 < cn; s0 += 1024) {
-            const int64_t s = s0 + threadIdx.x;
-            bool win = false;
-            uint64_t x = 0;
-            if (s < cn) {
-                x = from_lists ? lr[s] : composite(score_key(sr[s]), (uint32_t)s);
-                win = sh >= 64 ? true : ((x >> sh) >= pf);
+    for (int64_t s0 = 0; s0 < n; s0 += 1024) {
+        const int64_t s = s0 + threadIdx.x;
+        bool win = false;
+        if (s < n) {
+            const uint64_t x = composite(score_key(sr[s]), (uint32_t)s);
+            win = sh >= 64 ? true : ((x >> sh) >= pf);
+        }
+        const uint64_t m = __ballot(win);
+        if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t off = base;
+        for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2];
+        if (win) {
+            const uint32_t p = off + (uint32_t)__popcll(m & ((1ull << lane) - 1));
+            if (p < kk) out[p] = map_slot(cand, cand_stride, row, (uint32_t)s);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t tot = 0;
+            for (int w2 = 0; w2 < 16; ++w2) tot += wsum[w2];
+            base += tot;
+        }
+        __syncthreads();
+    }
+}
+
+// Final selection from the compacted per-chunk lists (k_collect_local): one
+// workgroup per row.  The chunks' runs are concatenated in chunk order into
+// LDS, which puts the candidates in position order; the radix select starts
+// at bit 51 over the threshold bin's keys (the bins above all win), and the
+// winners are written out in that same order by a running compaction, so no
+// sort is needed.  A row with more candidates than LDS holds streams them
+// from the lists at every step instead.
+constexpr int kMaxChunksLds = 4096;  // chunks whose run offsets fit in LDS
+
+__global__ __launch_bounds__(1024) void k_final_local(const uint64_t* __restrict__ lists,
+                                                      const uint32_t* __restrict__ counts, int max_chunks,
+                                                      int chunk, const RowSel* __restrict__ sel, int K,
+                                                      int32_t* __restrict__ idx) {
+    __shared__ uint64_t c[kCandCap];
+    __shared__ uint32_t roff[kMaxChunksLds + 1];
+    __shared__ uint32_t hist256[256], scan256[256];
+    __shared__ RadixState st;
+    __shared__ int found;
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t base;
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const RowSel rsel = sel[row];
+    const uint32_t kk = rsel.kk;
+    int32_t* out = idx + (int64_t)row * K;
+    for (int i = tid + (int)kk; i < K; i += 1024) out[i] = -1;
+    if (kk == 0) return;
+    const int n_ch = (int)(((int64_t)rsel.n + chunk - 1) / chunk);
+    const uint32_t* cr = counts + (int64_t)row * max_chunks;
+    const uint64_t* lrow = lists + (int64_t)row * max_chunks * chunk;
+    const bool in_lds_offsets = n_ch <= kMaxChunksLds;
+    // run offsets: exclusive prefix sum of the runs' lengths
+    if (in_lds_offsets) {
+        if (tid == 0) base = 0;
+        __syncthreads();
+        for (int c0 = 0; c0 < n_ch; c0 += 1024) {
+            const int ch = c0 + tid;
+            const uint32_t v = ch < n_ch ? cr[ch] : 0u;
+            uint32_t incl = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t u = __shfl_up(incl, o);
+                if (lane >= o) incl += u;
             }
-            const uint64_t m = __ballot(win);
-            if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
+            if (lane == 63) wsum[wave] = incl;
             __syncthreads();
-            uint32_t off = base;
-            for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2];
-            if (win) {
-                const uint32_t p = off + (uint32_t)__popcll(m & ((1ull << lane) - 1));
-                if (p < kk) out[p] = map_slot(cand, cand_stride, row, 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu));
-            }
+            uint32_t before = base;
+            for (int w2 = 0; w2 < wave; ++w2) before += wsum[w2];
+            if (ch < n_ch) roff[ch] = before + incl - v;
             __syncthreads();
-            if (threadIdx.x == 0) {
+            if (tid == 0) {
                 uint32_t tot = 0;
                 for (int w2 = 0; w2 < 16; ++w2) tot += wsum[w2];
                 base += tot;
             }
             __syncthreads();
+        }
+        if (tid == 0) roff[n_ch] = base;
+        __syncthreads();
+    }
+    const uint32_t total = in_lds_offsets ? roff[n_ch] : 0xFFFFFFFFu;
+    const bool from_lds = total <= (uint32_t)kCandCap;
+    // element e of the concatenation (e < total): chunk by binary search
+    auto elem = [&](uint32_t e) -> uint64_t {
+        int lo = 0, hi = n_ch;  // roff[lo] <= e < roff[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (roff[mid] <= e) lo = mid; else hi = mid;
+        }
+        return lrow[(int64_t)lo * chunk + (e - roff[lo])];
+    };
+    if (from_lds)
+        for (uint32_t e = tid; e < total; e += 1024) c[e] = elem(e);
+    if (tid == 0) {
+        st.prefix = rsel.bin;
+        st.shift = 51;
+        st.need = kk - rsel.above;
+        st.done = 0;
+        base = 0;
+    }
+    __syncthreads();
+    // visit every candidate: from LDS, or streamed from the runs (chunk order)
+    auto for_each = [&](auto&& fn) {
+        if (from_lds) {
+            for (uint32_t e = tid; e < total; e += 1024) fn(c[e]);
+        } else {
+            for (int ch = 0; ch < n_ch; ++ch) {
+                const uint32_t cn = cr[ch];
+                for (uint32_t j = tid; j < cn; j += 1024) fn(lrow[(int64_t)ch * chunk + j]);
+            }
+        }
+    };
+    while (!st.done) {
+        if (tid < 256) hist256[tid] = 0;
+        __syncthreads();
+        const int sh = st.shift;
+        const int w = digit_bits(sh);
+        const uint64_t pf = st.prefix;
+        for_each([&](uint64_t x) {
+            if ((x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
+        });
+        __syncthreads();
+        radix_step(hist256, scan256, &st, &found);
+    }
+    const int sh = st.shift;
+    const uint64_t pf = st.prefix;
+    // winners (key64 >= prefix << shift) in candidate order = position order
+    auto emit = [&](uint64_t x, bool valid) {
+        const bool win = valid && (x >> sh) >= pf;
+        const uint64_t m = __ballot(win);
+        if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t off = base;
+        for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2];
+        if (win) {
+            const uint32_t p = off + (uint32_t)__popcll(m & ((1ull << lane) - 1));
+            if (p < kk) out[p] = (int32_t)(0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu));
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t tot = 0;
+            for (int w2 = 0; w2 < 16; ++w2) tot += wsum[w2];
+            base += tot;
+        }
+        __syncthreads();
+    };
+    if (from_lds) {
+        for (uint32_t e0 = 0; e0 < total; e0 += 1024) {
+            const uint32_t e = e0 + tid;
+            emit(e < total ? c[e] : 0ull, e < total);
+        }
+    } else {
+        for (int ch = 0; ch < n_ch; ++ch) {
+            const uint32_t cn = cr[ch];
+            for (uint32_t j0 = 0; j0 < cn; j0 += 1024) {
+                const uint32_t j = j0 + tid;
+                emit(j < cn ? lrow[(int64_t)ch * chunk + j] : 0ull, j < cn);
+            }
         }
     }
 }
@@ -536,24 +638,21 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL(k_collect, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, h, a.K,
                        sel, cb);
     hipLaunchKernelGGL(k_final, dim3(nq), dim3(1024), 0, s, a.scores, a.stride, sel, cb, a.cand, a.cand_stride, a.K,
-                       a.idx, FallbackSrc{nullptr, nullptr, 0, 1});
+                       a.idx);
     return hipGetLastError();
 }
 
 hipError_t launch_topk_local(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, void* ws,
                              hipStream_t s) {
     const int nq = g.total_q;
-    char* w = (char*)ws;
-    const uint32_t* hist = (const uint32_t*)w;
-    w += al256((size_t)nq * kHistBins * 4);
-    RowSel* sel = (RowSel*)w;
-    w += al256((size_t)nq * sizeof(RowSel));
-    uint64_t* cb = (uint64_t*)w;
+    const uint32_t* hist = (const uint32_t*)ws;
+    RowSel* sel = (RowSel*)((char*)ws + al256((size_t)nq * kHistBins * 4));
     RowSrc rs{b->d_entry_off, b->d_row_seq, b->d_q_pos, b->ratio, nullptr, 0, 1, g.max_entries};
+    hipLaunchKernelGGL(k_row_threshold, dim3(nq), dim3(256), 0, s, hist, rs, lo.K, sel);
     hipLaunchKernelGGL(k_collect_local, dim3((unsigned)lo.max_chunks, nq), dim3(256), 0, s, lo.lists, lo.counts,
-                       lo.max_chunks, lo.chunk, rs, hist, lo.K, sel, cb);
-    hipLaunchKernelGGL(k_final, dim3(nq), dim3(1024), 0, s, (const float*)nullptr, (int64_t)0, sel, cb,
-                       (const int32_t*)nullptr, 0, lo.K, idx, FallbackSrc{lo.lists, lo.counts, lo.max_chunks, lo.chunk});
+                       lo.max_chunks, lo.chunk, (const RowSel*)sel);
+    hipLaunchKernelGGL(k_final_local, dim3(nq), dim3(1024), 0, s, (const uint64_t*)lo.lists, (const uint32_t*)lo.counts,
+                       lo.max_chunks, lo.chunk, (const RowSel*)sel, lo.K, idx);
     return hipGetLastError();
 }
 
