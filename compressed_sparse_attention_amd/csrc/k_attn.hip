@@ -21,6 +21,7 @@ namespace {
 
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 typedef short v8s __attribute__((ext_vector_type(8)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 
@@ -35,6 +36,25 @@ __device__ __forceinline__ v4i fp4x8_to_bf16(uint32_t codes, float scale) {
 }
 
 __device__ __forceinline__ float e8m0_f32(uint32_t e) { return __builtin_ldexpf(1.0f, (int)e - 127); }
+
+// Reductions over lane pairs l, l ^ D (D = 16 or 32) on the VALU: the swap
+// leaves this lane's value and its partner's in the two results (in some order).
+template <int D>
+__device__ __forceinline__ v2u lane_pair(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if constexpr (D == 16) return __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    else return __builtin_amdgcn_permlane32_swap(u, u, false, false);
+}
+template <int D>
+__device__ __forceinline__ float xor_max(float x) {
+    const v2u r = lane_pair<D>(x);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <int D>
+__device__ __forceinline__ float xor_sum(float x) {
+    const v2u r = lane_pair<D>(x);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // ---------------------------------------------------------------------------
 // gather + dequantise: grid (K, total_q), 64 threads, 8 channels per thread
@@ -147,13 +167,14 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     // fp32 weights (it gives the log-sum-exp)
     float m_run = -INFINITY, l_run = 0.0f, l_lse = 0.0f;
 
-    // this thread stages key `skey` of each block, channels 128*part .. +128;
+    // this thread stages key `skey` of each block, channels CP*part .. +CP;
     // the main-KV part of the next block is fetched into registers while the
-    // current block computes
-    // (16 consecutive lanes take 16 keys of one part, so that their LDS
-    // writes of a row segment fall in distinct banks)
+    // current block computes.  16 consecutive lanes take 16 keys of one part,
+    // so that their LDS writes of a row segment fall in distinct banks.
+    constexpr int CP = 128;         // channels per part (4 parts)
+    constexpr int NB = CP / 32;     // 32-channel scale blocks per part
     const int skey = (tid & 15) + 16 * (tid >> 6), part = (tid >> 4) & 3;
-    v4i pc[4];
+    v4i pc[NB];
     uint32_t psc = 0;
     auto fetch = [&](int blk) {
         const int vk = KB * blk + skey;
@@ -161,9 +182,9 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
             const int32_t j = kidx[vk];
             if (j >= 0) {
                 const int64_t e = e0 + j;
-                const uint8_t* src = kv + e * 256 + 64 * part;
+                const uint8_t* src = kv + e * 256 + (CP / 2) * part;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pc[i] = ld16(src + 16 * i);
+                for (int i = 0; i < NB; ++i) pc[i] = ld16(src + 16 * i);
                 psc = *reinterpret_cast<const uint32_t*>(kv_sc + e * 16 + 4 * part);
             }
         }
@@ -174,13 +195,13 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
         // 1) stage 64 keys
         {
             const int vk = KB * blk + skey;
-            uint16_t* dst = kl + skey * LROW + 128 * part;
+            uint16_t* dst = kl + skey * LROW + CP * part;
             int valid = 0;
             if (vk < n_sel) {
                 if (kidx[vk] >= 0) {
                     valid = 1;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {  // 32 channels per scale
+                    for (int i = 0; i < NB; ++i) {  // 32 channels per scale
                         const float sc = e8m0_f32((psc >> (8 * i)) & 255u);
 #pragma unroll
                         for (int d = 0; d < 4; ++d)
@@ -191,16 +212,16 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
                 valid = 1;
                 const int64_t u = u_lo + (vk - n_sel);
                 const int64_t r = swa_row_off[b] + (u - swa_pos0[b]);
-                const uint16_t* src = swa + r * 512 + 128 * part;
-                v4i tmp[16];
+                const uint16_t* src = swa + r * 512 + CP * part;
+                v4i tmp[CP / 8];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) tmp[i] = ld16(src + 8 * i);
+                for (int i = 0; i < CP / 8; ++i) tmp[i] = ld16(src + 8 * i);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = tmp[i];
+                for (int i = 0; i < CP / 8; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = tmp[i];
             }
             if (!valid) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = v4i{0, 0, 0, 0};
+                for (int i = 0; i < CP / 8; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = v4i{0, 0, 0, 0};
             }
             if (part == 0) kvalid[skey] = valid;
         }
@@ -209,13 +230,15 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
 
         // 2) S = Q K^T for keys 16*wave .. +16: lane gets S[head 4lg+v][key 16wave + li]
         {
-            v4f S = {0.f, 0.f, 0.f, 0.f};
+            // four independent accumulation chains over the 16 k-steps
+            v4f Sp[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             const uint16_t* kr = kl + (16 * wave + li) * LROW + 8 * lg;
 #pragma unroll
             for (int ks = 0; ks < 16; ++ks) {
                 const v8bf Bk = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kr + 32 * ks));
-                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Q[ks], Bk, S, 0, 0, 0);
+                Sp[ks & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Q[ks], Bk, Sp[ks & 3], 0, 0, 0);
             }
+            const v4f S = (Sp[0] + Sp[1]) + (Sp[2] + Sp[3]);
             const int key = 16 * wave + li;
             const bool ok = kvalid[key] != 0;
 #pragma unroll
@@ -233,8 +256,8 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
                 p[8 * ks + i] = sl[li][8 * lg + 32 * ks + i];
                 mx = fmaxf(mx, p[8 * ks + i]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = xor_max<16>(mx);
+        mx = xor_max<32>(mx);
         const float m_new = fmaxf(m_run, mx);
         float alpha;
         // each weight as the sum of two bf16 values (hi + lo), so that the P V
@@ -263,10 +286,10 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
                 rs += (float)pb + (float)pl;  // normalise with the weights actually used
                 rs32 += p[8 * ks + i];
             }
-        rs += __shfl_xor(rs, 16);
-        rs += __shfl_xor(rs, 32);
-        rs32 += __shfl_xor(rs32, 16);
-        rs32 += __shfl_xor(rs32, 32);
+        rs = xor_sum<16>(rs);
+        rs = xor_sum<32>(rs);
+        rs32 = xor_sum<16>(rs32);
+        rs32 = xor_sum<32>(rs32);
         l_run = l_run * alpha + rs;
         l_lse = l_lse * alpha + rs32;
         m_run = m_new;
@@ -333,42 +356,38 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
 // a_s = 2^(m_s - M), O = sum_s a_s O_s / sum_s a_s l_s.  One workgroup of 128
 // threads per (row, head); thread t owns channels 4t .. 4t+3, so every load of
 // the merge is issued at once.
-constexpr int kMaxSplit = 8;
+constexpr int kMaxSplit = 8;  // the combine is instantiated for S = 2 .. kMaxSplit
 constexpr int kAttnTargetWgs = 256;  // workgroups the key splits aim for (more splits cost more than they hide)
 
-__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part, int Hm, int n_hg, int S,
+template <int S>
+__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part, int Hm, int n_hg,
                                                       float* __restrict__ out, float* __restrict__ lse) {
     const int row = blockIdx.x / Hm, h = blockIdx.x % Hm;
     const int hg = h / HG, hh = h % HG;
     const float* base = part + ((int64_t)row * n_hg + hg) * S * (HG * 516);
     const int t = threadIdx.x;
-    float m[kMaxSplit], l[kMaxSplit], ll[kMaxSplit];
-    v4f o[kMaxSplit];
+    float m[S], l[S], ll[S];
+    v4f o[S];
 #pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s) {
-        if (s < S) {
-            const float* ps = base + s * (HG * 516);
-            m[s] = ps[HG * 512 + 4 * hh];
-            l[s] = ps[HG * 512 + 4 * hh + 1];
-            ll[s] = ps[HG * 512 + 4 * hh + 2];
-            o[s] = *reinterpret_cast<const v4f*>(ps + hh * 512 + 4 * t);
-        }
+    for (int s = 0; s < S; ++s) {
+        const float* ps = base + s * (HG * 516);
+        m[s] = ps[HG * 512 + 4 * hh];  // the same address in every lane: one scalar load
+        l[s] = ps[HG * 512 + 4 * hh + 1];
+        ll[s] = ps[HG * 512 + 4 * hh + 2];
+        o[s] = *reinterpret_cast<const v4f*>(ps + hh * 512 + 4 * t);
     }
     float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s)
-        if (s < S) M = fmaxf(M, m[s]);
+    for (int s = 0; s < S; ++s) M = fmaxf(M, m[s]);
     float L = 0.0f, Llse = 0.0f;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
 #pragma unroll
-        for (int s = 0; s < kMaxSplit; ++s) {
-            if (s < S) {
-                const float a = exp2f(m[s] - M);  // a part with no valid key has m = -inf: weight 0
-                L += a * l[s];
-                Llse += a * ll[s];
-                acc += a * o[s];
-            }
+        for (int s = 0; s < S; ++s) {
+            const float a = exp2f(m[s] - M);  // a part with no valid key has m = -inf: weight 0
+            L += a * l[s];
+            Llse += a * ll[s];
+            acc += a * o[s];
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -387,7 +406,7 @@ hipError_t launch_gather_dequant(const csa2_batch* b, Geometry g, const uint8_t*
 
 int attn_splits(const Geometry& g, int Hm, int K, int W) {
     // split the key blocks of a (row, head group) over several workgroups when
-    // the grid would otherwise leave the chip under-filled (< 2 per CU)
+    // the grid would otherwise leave CUs idle
     const int units = g.total_q * (Hm / HG);
     const int max_blocks = (K + W + KB - 1) / KB;
     int S = (kAttnTargetWgs + units - 1) / units;
@@ -410,9 +429,17 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
                        a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,
                        a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q, n_hg, S,
                        part);
-    if (S > 1)
-        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(a.g.total_q * a.Hm)), dim3(128), 0, s, part, a.Hm, n_hg, S,
-                           a.out, a.lse);
+    if (S > 1) {
+        const dim3 cg((unsigned)(a.g.total_q * a.Hm));
+        switch (S) {
+#define CSA2_COMBINE(N) \
+    case N: hipLaunchKernelGGL((k_attn_combine<N>), cg, dim3(128), 0, s, part, a.Hm, n_hg, a.out, a.lse); break;
+            CSA2_COMBINE(2) CSA2_COMBINE(3) CSA2_COMBINE(4) CSA2_COMBINE(5)
+            CSA2_COMBINE(6) CSA2_COMBINE(7) CSA2_COMBINE(8)
+#undef CSA2_COMBINE
+            default: return hipErrorInvalidValue;
+        }
+    }
     return hipGetLastError();
 }
 

@@ -184,12 +184,15 @@ __global__ __launch_bounds__(256) void k_collect_local(uint64_t* __restrict__ li
     constexpr int U = 4096 / 256;  // entries per thread; chunk <= 4096
     __shared__ uint32_t wtot[4];
     const int row = blockIdx.y;
+    uint32_t* cp = counts + (int64_t)row * max_chunks + blockIdx.x;
+    uint64_t* lr = lists + ((int64_t)row * max_chunks + blockIdx.x) * chunk;
+    // the count is read together with the row state (it is in bounds for every
+    // chunk; a chunk past the row's visible range is not used)
+    const uint32_t cnt_raw = *cp;
     const RowSel rsel = sel[row];
     const int64_t c0 = (int64_t)blockIdx.x * chunk;
     if (c0 >= (int64_t)rsel.n || rsel.kk == 0) return;  // uniform
-    uint32_t* cp = counts + (int64_t)row * max_chunks + blockIdx.x;
-    uint64_t* lr = lists + ((int64_t)row * max_chunks + blockIdx.x) * chunk;
-    const uint32_t cnt = *cp;
+    const uint32_t cnt = cnt_raw;
     const uint32_t per = (uint32_t)chunk / 256;  // thread t owns entries [per t, per t + per)
     const uint32_t i0 = per * threadIdx.x;
     uint64_t key[U];
@@ -412,13 +415,15 @@ __global__ __launch_bounds__(1024) void k_final_local(const uint64_t* __restrict
     __shared__ uint32_t base;
     const int row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t* cr = counts + (int64_t)row * max_chunks;
+    // the first 1024 run lengths are read together with the row state
+    const uint32_t len0 = tid < max_chunks ? cr[tid] : 0u;
     const RowSel rsel = sel[row];
     const uint32_t kk = rsel.kk;
     int32_t* out = idx + (int64_t)row * K;
     for (int i = tid + (int)kk; i < K; i += 1024) out[i] = -1;
     if (kk == 0) return;
     const int n_ch = (int)(((int64_t)rsel.n + chunk - 1) / chunk);
-    const uint32_t* cr = counts + (int64_t)row * max_chunks;
     const uint64_t* lrow = lists + (int64_t)row * max_chunks * chunk;
     const bool in_lds_offsets = n_ch <= kMaxChunksLds;
     // run offsets: exclusive prefix sum of the runs' lengths
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(1024) void k_final_local(const uint64_t* __restrict
         __syncthreads();
         for (int c0 = 0; c0 < n_ch; c0 += 1024) {
             const int ch = c0 + tid;
-            const uint32_t v = ch < n_ch ? cr[ch] : 0u;
+            const uint32_t v = ch < n_ch ? (c0 == 0 ? len0 : cr[ch]) : 0u;
             uint32_t incl = v;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {

@@ -178,7 +178,7 @@ def test_gather_dequant_bitwise():
     assert np.array_equal(got.cpu().numpy(), oracle.gather_dequant(wl, idx))
 
 
-ATTN_CASES = ["decode", "short_ctx", "ragged_t4", "swa_only", "replay", "sparse_idx"]
+ATTN_CASES = ["decode", "short_ctx", "ragged_t4", "swa_only", "replay", "sparse_idx", "swa_only_h64", "replay_h64"]
 
 
 @pytest.mark.parametrize("case", ATTN_CASES)
@@ -191,10 +191,12 @@ def test_sparse_attn_tolerance(case):
         wl = synth.make_workload(case, 5, [40, 100, 1], 1, [(20, synth.MODE_FULL, False)], Hm=32)
     elif case == "ragged_t4":
         wl = synth.make_workload(case, 6, [130, 900, 3000], 4, [(20, synth.MODE_FULL, False)], Hm=16)
-    elif case == "swa_only":
-        wl = synth.make_workload(case, 7, [2000, 300], 2, [(0, synth.MODE_SWA_ONLY, False)], Hm=16)
-    elif case == "replay":
-        wl = synth.make_workload(case, 8, [2000, 300], 1, [(20, synth.MODE_FULL, False)], Hm=16)
+    elif case in ("swa_only", "swa_only_h64"):
+        wl = synth.make_workload(case, 7, [2000, 300], 2, [(0, synth.MODE_SWA_ONLY, False)],
+                                 Hm=64 if case.endswith("h64") else 16)
+    elif case in ("replay", "replay_h64"):
+        wl = synth.make_workload(case, 8, [2000, 300], 1, [(20, synth.MODE_FULL, False)],
+                                 Hm=64 if case.endswith("h64") else 16)
         replay = np.array([1950, 0], np.int32)
     else:
         wl = synth.make_workload(case, 9, [5000], 1, [(20, synth.MODE_FULL, False)], Hm=16)
@@ -202,7 +204,7 @@ def test_sparse_attn_tolerance(case):
     nq = wl.total_q
     vis = oracle.row_visible(wl)
     idx = np.full((nq, 512), -1, np.int32)
-    if case != "swa_only":
+    if not case.startswith("swa_only"):
         for r in range(nq):
             v = int(vis[r])
             m = min(v, 512)
@@ -220,6 +222,7 @@ def test_sparse_attn_tolerance(case):
 
 CHAIN_CASES = {
     "c2_small": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16),
+    "c2_small_h64": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=64),
     "c4_small": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16),
     "c3_small": lambda: synth.config("prefill_c3", tokens=4000, T=96, Hm=16),
     "encoder_group": lambda: synth.make_workload("enc", 12, [700, 2500], 3, [(0, synth.MODE_SWA_ONLY, False),
