@@ -547,9 +547,21 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
 // operands are exact in bf16, and v_mfma_f32_32x32x16_bf16 sums them exactly
 // (measured up to a 23-bit window), so this kernel converts both to bf16
 // (the query row's E8M0 scale folded into the conversion, which is exact) and
-// contracts on the bf16 matrix cores.  Channel c of a row sits at k-step
-// ks = c/16, lane half g = (c/8)%2, element c%8.  Grid and staging as in
-// k_score_prefill; two query rows per wave.
+// contracts on the bf16 matrix cores.  Every partial sum of a dot product is
+// a multiple of the smallest product's grid and below the sum of magnitudes,
+// so the channel order inside the contraction does not change the result.
+//
+// A wave holds two query rows.  The 32 rows of its A operand interleave them
+// so that the result's two lane halves belong to different queries: MFMA row
+// m holds query (m/4)%2, head 16 mt + 4 (m/8) + m%4, which lands in lane half
+// (m/4)%2, register 4 (m/8) + m%4.  So a lane receives 16 consecutive heads of
+// its own query for one position, and runs that query's fmaf chain over the
+// heads with no cross-lane exchange; its weights come from LDS (the two lane
+// halves read two broadcast addresses).  Lane half g supplies channels
+// 64 g + 8 ks .. +8 at k-step ks, i.e. bytes 32 g .. 32 g + 31 of an FP4 key
+// row, which are read as two 16-byte pieces; the pieces of row p sit at
+// piece index c ^ ((p / 2) % 4) in LDS, so that the 8 lanes of each LDS read
+// cycle hit distinct banks.  Grid as in k_score_prefill.
 // ---------------------------------------------------------------------------
 template <int H>
 __global__ __launch_bounds__(256) void k_score_prefill_fp8(const uint8_t* __restrict__ q,
@@ -561,11 +573,12 @@ __global__ __launch_bounds__(256) void k_score_prefill_fp8(const uint8_t* __rest
                                                            const int32_t* __restrict__ q_off,
                                                            const int32_t* __restrict__ q_pos, int ratio,
                                                            float* __restrict__ scores, int64_t stride) {
-    constexpr int NMT = H / 32;
+    constexpr int NM = H / 16;  // MFMA row groups: 16 heads of each of the wave's two queries
     constexpr int PT = 1024;
     constexpr int QG = 8;
     __shared__ __attribute__((aligned(16))) uint8_t ks_lds[PT * 64];
     __shared__ uint8_t ksc_lds[PT];
+    __shared__ __attribute__((aligned(16))) float w_lds[QG * H];
     const int b = blockIdx.z;
     const int64_t e0 = entry_off[b];
     const int64_t n = entry_off[b + 1] - e0;
@@ -593,80 +606,103 @@ __global__ __launch_bounds__(256) void k_score_prefill_fp8(const uint8_t* __rest
         const int row = i >> 2, part = i & 3;
         int64_t j = p_base + row;
         j = j < n ? j : n - 1;
-        *reinterpret_cast<v4i*>(ks_lds + row * 64 + part * 16) = ld16(k + (e0 + j) * 64 + part * 16);
+        *reinterpret_cast<v4i*>(ks_lds + row * 64 + 16 * (part ^ ((row >> 1) & 3))) = ld16(k + (e0 + j) * 64 + part * 16);
     }
     for (int i = threadIdx.x; i < PT; i += 256) {
         const int64_t j = p_base + i;
         ksc_lds[i] = j < n ? k_sc[e0 + j] : 127;
     }
+    for (int i = threadIdx.x; i < QG * H; i += 256) {
+        const int qi = i / H;
+        w_lds[i] = w[(int64_t)(qi < nr ? r0 + qi : r0) * H + i % H];
+    }
 
-    v8bf A[2][NMT][8];
-    int64_t vis[2];
-    int rows[2];
+    // A operand: lane li supplies MFMA row li (query (li/4)%2 of the wave)
+    v8bf A[NM][8];
+    {
+        const int qa = 2 * wave + ((li >> 2) & 1);
+        const int64_t row = qa < nr ? r0 + qa : r0;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int qi = 2 * wave + u;
-        rows[u] = qi < nr ? r0 + qi : -1;
-        const int row = qi < nr ? r0 + qi : r0;
-        vis[u] = visible_count(n, q_pos[row], ratio);
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-            const uint8_t* qr = q + ((int64_t)row * H + 32 * mt + li) * 128 + 8 * g;
-            const float sc = __builtin_ldexpf(1.0f, (int)q_sc[(int64_t)row * H + 32 * mt + li] - 127);
+        for (int mt = 0; mt < NM; ++mt) {
+            const int head = 16 * mt + 4 * (li >> 3) + (li & 3);
+            const uint8_t* qr = q + (row * H + head) * 128 + 64 * g;
+            const float sc = __builtin_ldexpf(1.0f, (int)q_sc[row * H + head] - 127);
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
-                const uint2 c = *reinterpret_cast<const uint2*>(qr + 16 * ks);
+                const uint2 c = *reinterpret_cast<const uint2*>(qr + 8 * ks);
                 auto lo0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false);
                 auto lo1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true);
                 auto hi0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false);
                 auto hi1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true);
-                A[u][mt][ks] = v8bf{lo0[0], lo0[1], lo1[0], lo1[1], hi0[0], hi0[1], hi1[0], hi1[1]};
+                A[mt][ks] = v8bf{lo0[0], lo0[1], lo1[0], lo1[1], hi0[0], hi0[1], hi1[0], hi1[1]};
             }
         }
     }
+    // this lane's output query
+    const int qo = 2 * wave + g;
+    const bool live = qo < nr;
+    const int64_t rowo = live ? r0 + qo : r0;
+    const int64_t vis = visible_count(n, q_pos[rowo], ratio);
+    const float* wq = w_lds + qo * H;
     __syncthreads();
 
     for (int tile = 0; tile < PT / 64; ++tile) {
         const int64_t p0 = p_base + 64 * tile;
         if (p0 >= p_end) break;
-        const int64_t jl = p0 + lane;
-        const int ek = ksc_lds[64 * tile + lane];
-        v16f acc[2][NMT][2];
+        // 2 NM groups (nt, mt) in turn: the contraction of group i runs
+        // beside the head sums of group i - 1, and a scheduling barrier
+        // between the steps keeps the compiler from hoisting every group's
+        // contraction ahead of the sums (which would hold all 2 NM results)
+        float s[2] = {0.0f, 0.0f};
+        v8bf B[8];
+        v16f accp;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int i = 0; i <= 2 * NM; ++i) {
+            const int nt = i / NM, mt = i % NM;
+            v16f acc;
+            if (i < 2 * NM) {
+                if (mt == 0) {
+                    const int prow = 64 * tile + 32 * nt + li;
+                    const uint8_t* kr = ks_lds + prow * 64;
+                    const int sw = (prow >> 1) & 3;
+                    const v4i c0 = *reinterpret_cast<const v4i*>(kr + 16 * ((2 * g) ^ sw));
+                    const v4i c1 = *reinterpret_cast<const v4i*>(kr + 16 * ((2 * g + 1) ^ sw));
 #pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
+                    for (int ks = 0; ks < 8; ++ks) {
+                        const uint32_t c = (uint32_t)(ks < 4 ? c0[ks] : c1[ks - 4]);
+                        auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 0);
+                        auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 1);
+                        auto b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 2);
+                        auto b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 3);
+                        B[ks] = v8bf{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+                    }
+                }
+                acc = v16f{};
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) acc[u][mt][nt] = v16f{};
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                // position 64 tile + 32 nt + li, channels 16 ks + 8 g .. +8 = FP4 bytes 8 ks + 4 g .. +4
-                const uint32_t c =
-                    *reinterpret_cast<const uint32_t*>(ks_lds + (64 * tile + 32 * nt + li) * 64 + 8 * ks + 4 * g);
-                auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 0);
-                auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 1);
-                auto b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 2);
-                auto b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 3);
-                const v8bf B = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int mt = 0; mt < NMT; ++mt)
-                        acc[u][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[u][mt][ks], B, acc[u][mt][nt], 0, 0, 0);
+                for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mt][ks], B[ks], acc, 0, 0, 0);
             }
+            if (i > 0) {
+                const int pn = (i - 1) / NM, pm = (i - 1) % NM;
+                const v4f* wv = reinterpret_cast<const v4f*>(wq + 16 * pm);
+                float t = s[pn];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if (rows[u] < 0) break;  // wave-uniform
-            float* dst = scores + (int64_t)rows[u] * stride + jl;
-            if (p0 >= vis[u]) {  // wave-uniform
-                if (jl < n) *dst = -INFINITY;
-                continue;
+                for (int j4 = 0; j4 < 4; ++j4) {
+                    const v4f ww = wv[j4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) t = __builtin_fmaf(ww[e], relu(accp[4 * j4 + e]), t);
+                }
+                // keeps the sums here rather than sunk into the guarded store
+                asm volatile("" ::"v"(t));
+                s[pn] = t;
             }
-            // all 64 lanes must run the head sum: its permlane32_swap reads the partner lane
-            const float s = head_sum<NMT>(acc[u], w + (int64_t)rows[u] * H);
-            if (jl < n) *dst = jl < vis[u] ? ldexpf(s, ek - 127) : -INFINITY;
+            accp = acc;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int64_t j = p0 + 32 * nt + li;
+            const int ek = ksc_lds[64 * tile + 32 * nt + li];
+            if (live && j < n) scores[rowo * stride + j] = j < vis ? ldexpf(s[nt], ek - 127) : -INFINITY;
         }
     }
 }

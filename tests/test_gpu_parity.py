@@ -91,10 +91,13 @@ def test_index_score_cand_bitwise():
         assert np.array_equal(h[r], np.bincount(fin.view(np.uint32) >> 19, minlength=4096)), r
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+@pytest.mark.parametrize("fmt", ["fp8", "fp8_h32", "fp4"])
 def test_index_score_prefill_bitwise(fmt):
     if fmt == "fp8":
         wl = synth.config("prefill_c3", tokens=6002, T=150, n_layers=1, Hm=16)
+    elif fmt == "fp8_h32":  # 32 indexer heads, two sequences, 61 rows each (a ragged row group)
+        wl = synth.make_workload("pf8h32", 91, [2500, 3100], 61, [(2, synth.MODE_FULL, False)], ratio=2, H=32,
+                                 Hm=16, q_fmt=synth.Q_FP8)
     else:  # FP4 queries, 9 rows per sequence, ratio 2: the many-query kernel
         wl = synth.make_workload("pf4", 77, [1500, 2100], 9, [(2, synth.MODE_FULL, False)], ratio=2, Hm=16)
     dw = DevWorkload(wl)
