@@ -563,8 +563,11 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
 // piece index c ^ ((p / 2) % 4) in LDS, so that the 8 lanes of each LDS read
 // cycle hit distinct banks.  Grid as in k_score_prefill.
 // ---------------------------------------------------------------------------
+constexpr int kPrefillChunk = 512;       // positions per LDS buffer
+constexpr int kPrefillSegChunks = 32;    // chunks per workgroup (16,384 positions)
+
 template <int H>
-__global__ __launch_bounds__(256) void k_score_prefill_fp8(const uint8_t* __restrict__ q,
+__global__ __launch_bounds__(256, 2) void k_score_prefill_fp8(const uint8_t* __restrict__ q,
                                                            const uint8_t* __restrict__ q_sc,
                                                            const float* __restrict__ w,
                                                            const uint8_t* __restrict__ k,
@@ -574,10 +577,10 @@ __global__ __launch_bounds__(256) void k_score_prefill_fp8(const uint8_t* __rest
                                                            const int32_t* __restrict__ q_pos, int ratio,
                                                            float* __restrict__ scores, int64_t stride) {
     constexpr int NM = H / 16;  // MFMA row groups: 16 heads of each of the wave's two queries
-    constexpr int PT = 1024;
+    constexpr int PT = kPrefillChunk;
     constexpr int QG = 8;
-    __shared__ __attribute__((aligned(16))) uint8_t ks_lds[PT * 64];
-    __shared__ uint8_t ksc_lds[PT];
+    __shared__ __attribute__((aligned(16))) uint8_t ks_lds[2][PT * 64];
+    __shared__ uint8_t ksc_lds[2][PT];
     __shared__ __attribute__((aligned(16))) float w_lds[QG * H];
     const int b = blockIdx.z;
     const int64_t e0 = entry_off[b];
@@ -591,26 +594,34 @@ __global__ __launch_bounds__(256) void k_score_prefill_fp8(const uint8_t* __rest
         const int64_t v = visible_count(n, q_pos[r0 + i], ratio);
         vmax = v > vmax ? v : vmax;
     }
-    const int64_t p_base = (int64_t)blockIdx.x * PT;
-    if (p_base >= vmax) {
-        for (int i = 0; i < nr; ++i)
-            for (int64_t j = p_base + threadIdx.x; j < p_base + PT && j < n; j += 256)
-                scores[(int64_t)(r0 + i) * stride + j] = -INFINITY;
-        return;
-    }
-    const int64_t p_end = p_base + PT < n ? p_base + PT : n;
+    // this workgroup's segment: chunks [c_lo, c_hi) of PT positions; the
+    // chunks from c_vis on hold no position any of its rows sees
+    const int64_t c_lo = (int64_t)blockIdx.x * kPrefillSegChunks;
+    const int64_t n_chunks = (n + PT - 1) / PT;
+    const int64_t c_hi = c_lo + kPrefillSegChunks < n_chunks ? c_lo + kPrefillSegChunks : n_chunks;
+    const int64_t v_chunks = (vmax + PT - 1) / PT;
+    const int64_t c_vis = c_hi < v_chunks ? c_hi : v_chunks;
+    for (int64_t j = (c_vis > c_lo ? c_vis : c_lo) * PT + threadIdx.x; j < c_hi * PT && j < n; j += 256)
+        for (int i = 0; i < nr; ++i) scores[(int64_t)(r0 + i) * stride + j] = -INFINITY;
+    if (c_lo >= c_vis) return;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5, li = lane & 31;
 
-    for (int i = threadIdx.x; i < PT * 4; i += 256) {
-        const int row = i >> 2, part = i & 3;
-        int64_t j = p_base + row;
+    // 16-byte piece `idx` of a chunk: row idx/4, piece idx%4, stored at piece
+    // index (idx%4) ^ ((row/2)%4) of the row
+    auto piece_src = [&](int64_t c, int idx) {
+        int64_t j = c * PT + (idx >> 2);
         j = j < n ? j : n - 1;
-        *reinterpret_cast<v4i*>(ks_lds + row * 64 + 16 * (part ^ ((row >> 1) & 3))) = ld16(k + (e0 + j) * 64 + part * 16);
-    }
+        return k + (e0 + j) * 64 + (idx & 3) * 16;
+    };
+    auto piece_dst = [&](int buf, int idx) {
+        const int row = idx >> 2;
+        return ks_lds[buf] + row * 64 + 16 * ((idx & 3) ^ ((row >> 1) & 3));
+    };
+    for (int i = threadIdx.x; i < PT * 4; i += 256) *reinterpret_cast<v4i*>(piece_dst(0, i)) = ld16(piece_src(c_lo, i));
     for (int i = threadIdx.x; i < PT; i += 256) {
-        const int64_t j = p_base + i;
-        ksc_lds[i] = j < n ? k_sc[e0 + j] : 127;
+        const int64_t j = c_lo * PT + i;
+        ksc_lds[0][i] = j < n ? k_sc[e0 + j] : 127;
     }
     for (int i = threadIdx.x; i < QG * H; i += 256) {
         const int qi = i / H;
@@ -644,65 +655,87 @@ __global__ __launch_bounds__(256) void k_score_prefill_fp8(const uint8_t* __rest
     const int64_t rowo = live ? r0 + qo : r0;
     const int64_t vis = visible_count(n, q_pos[rowo], ratio);
     const float* wq = w_lds + qo * H;
-    __syncthreads();
 
-    for (int tile = 0; tile < PT / 64; ++tile) {
-        const int64_t p0 = p_base + 64 * tile;
-        if (p0 >= p_end) break;
-        // 2 NM groups (nt, mt) in turn: the contraction of group i runs
-        // beside the head sums of group i - 1, and a scheduling barrier
-        // between the steps keeps the compiler from hoisting every group's
-        // contraction ahead of the sums (which would hold all 2 NM results)
-        float s[2] = {0.0f, 0.0f};
-        v8bf B[8];
-        v16f accp;
+    for (int64_t c = c_lo; c < c_vis; ++c) {
+        // chunk c is in buffer (c - c_lo) % 2, and every wave is done with
+        // the other buffer, which receives chunk c + 1 one tile at a time
+        __syncthreads();
+        const int buf = (int)((c - c_lo) & 1);
+        const bool next = c + 1 < c_vis;
+        const int64_t p_end = (c + 1) * PT < n ? (c + 1) * PT : n;
+        for (int tile = 0; tile < PT / 64; ++tile) {
+            v4i pf = v4i{};
+            uint8_t pfs = 127;
+            const int pidx = 256 * tile + threadIdx.x;
+            if (next) {
+                pf = ld16(piece_src(c + 1, pidx));
+                const int64_t js = (c + 1) * PT + 64 * tile + threadIdx.x;
+                if (threadIdx.x < 64 && js < n) pfs = k_sc[e0 + js];
+            }
+            const int64_t p0 = c * PT + 64 * tile;
+            if (p0 < p_end) {
+                // 2 NM groups (nt, mt) in turn: the contraction of group i
+                // runs beside the head sums of group i - 1, and a scheduling
+                // barrier between the steps keeps the compiler from hoisting
+                // every group's contraction ahead of the sums (which would
+                // hold all 2 NM results)
+                float s[2] = {0.0f, 0.0f};
+                v8bf B[8];
+                v16f accp;
 #pragma unroll
-        for (int i = 0; i <= 2 * NM; ++i) {
-            const int nt = i / NM, mt = i % NM;
-            v16f acc;
-            if (i < 2 * NM) {
-                if (mt == 0) {
-                    const int prow = 64 * tile + 32 * nt + li;
-                    const uint8_t* kr = ks_lds + prow * 64;
-                    const int sw = (prow >> 1) & 3;
-                    const v4i c0 = *reinterpret_cast<const v4i*>(kr + 16 * ((2 * g) ^ sw));
-                    const v4i c1 = *reinterpret_cast<const v4i*>(kr + 16 * ((2 * g + 1) ^ sw));
+                for (int i = 0; i <= 2 * NM; ++i) {
+                    const int nt = i / NM, mt = i % NM;
+                    v16f acc;
+                    if (i < 2 * NM) {
+                        if (mt == 0) {
+                            const int prow = 64 * tile + 32 * nt + li;
+                            const uint8_t* kr = ks_lds[buf] + prow * 64;
+                            const int sw = (prow >> 1) & 3;
+                            const v4i c0 = *reinterpret_cast<const v4i*>(kr + 16 * ((2 * g) ^ sw));
+                            const v4i c1 = *reinterpret_cast<const v4i*>(kr + 16 * ((2 * g + 1) ^ sw));
 #pragma unroll
-                    for (int ks = 0; ks < 8; ++ks) {
-                        const uint32_t c = (uint32_t)(ks < 4 ? c0[ks] : c1[ks - 4]);
-                        auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 0);
-                        auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 1);
-                        auto b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 2);
-                        auto b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 3);
-                        B[ks] = v8bf{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+                            for (int ks = 0; ks < 8; ++ks) {
+                                const uint32_t cw = (uint32_t)(ks < 4 ? c0[ks] : c1[ks - 4]);
+                                auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 0);
+                                auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 1);
+                                auto b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 2);
+                                auto b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 3);
+                                B[ks] = v8bf{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+                            }
+                        }
+                        acc = v16f{};
+#pragma unroll
+                        for (int ks = 0; ks < 8; ++ks)
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mt][ks], B[ks], acc, 0, 0, 0);
                     }
+                    if (i > 0) {
+                        const int pn = (i - 1) / NM, pm = (i - 1) % NM;
+                        const v4f* wv = reinterpret_cast<const v4f*>(wq + 16 * pm);
+                        float t = s[pn];
+#pragma unroll
+                        for (int j4 = 0; j4 < 4; ++j4) {
+                            const v4f ww = wv[j4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) t = __builtin_fmaf(ww[e], relu(accp[4 * j4 + e]), t);
+                        }
+                        // keeps the sums here rather than sunk into the guarded store
+                        asm volatile("" ::"v"(t));
+                        s[pn] = t;
+                    }
+                    accp = acc;
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                acc = v16f{};
 #pragma unroll
-                for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mt][ks], B[ks], acc, 0, 0, 0);
-            }
-            if (i > 0) {
-                const int pn = (i - 1) / NM, pm = (i - 1) % NM;
-                const v4f* wv = reinterpret_cast<const v4f*>(wq + 16 * pm);
-                float t = s[pn];
-#pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const v4f ww = wv[j4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) t = __builtin_fmaf(ww[e], relu(accp[4 * j4 + e]), t);
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int64_t j = p0 + 32 * nt + li;
+                    const int ek = ksc_lds[buf][64 * tile + 32 * nt + li];
+                    if (live && j < p_end) scores[rowo * stride + j] = j < vis ? ldexpf(s[nt], ek - 127) : -INFINITY;
                 }
-                // keeps the sums here rather than sunk into the guarded store
-                asm volatile("" ::"v"(t));
-                s[pn] = t;
             }
-            accp = acc;
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int64_t j = p0 + 32 * nt + li;
-            const int ek = ksc_lds[64 * tile + 32 * nt + li];
-            if (live && j < n) scores[rowo * stride + j] = j < vis ? ldexpf(s[nt], ek - 127) : -INFINITY;
+            if (next) {
+                *reinterpret_cast<v4i*>(piece_dst(buf ^ 1, pidx)) = pf;
+                if (threadIdx.x < 64) ksc_lds[buf ^ 1][64 * tile + threadIdx.x] = pfs;
+            }
         }
     }
 }
@@ -748,20 +781,24 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
 #undef CSA2_DEC
         return hipGetLastError();
     }
-    dim3 grid((unsigned)((a.g.max_entries + 1023) / 1024), (unsigned)((a.g.max_q_per_seq + 7) / 8), a.g.n_seq);
-#define CSA2_PRE(HH, FF)                                                                                          \
-    hipLaunchKernelGGL((k_score_prefill<HH, FF>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,          \
-                       b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride)
     if (a.q_fmt == CSA2_Q_FP8) {
+        // one workgroup per (segment of kPrefillSegChunks chunks, 8 rows);
+        // consecutive segments go to consecutive XCDs
+        constexpr int64_t seg = (int64_t)kPrefillChunk * kPrefillSegChunks;
+        dim3 grid((unsigned)((a.g.max_entries + seg - 1) / seg), (unsigned)((a.g.max_q_per_seq + 7) / 8), a.g.n_seq);
         if (a.H == 64)
             hipLaunchKernelGGL((k_score_prefill_fp8<64>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,
                                b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride);
         else
             hipLaunchKernelGGL((k_score_prefill_fp8<32>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,
                                b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride);
-    } else {
-        if (a.H == 64) CSA2_PRE(64, 4); else CSA2_PRE(32, 4);
+        return hipGetLastError();
     }
+    dim3 grid((unsigned)((a.g.max_entries + 1023) / 1024), (unsigned)((a.g.max_q_per_seq + 7) / 8), a.g.n_seq);
+#define CSA2_PRE(HH, FF)                                                                                          \
+    hipLaunchKernelGGL((k_score_prefill<HH, FF>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,          \
+                       b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride)
+    if (a.H == 64) CSA2_PRE(64, 4); else CSA2_PRE(32, 4);
 #undef CSA2_PRE
     return hipGetLastError();
 }
