@@ -106,11 +106,16 @@ ChainWs chain_ws(const Geometry& g, int K, int block, int max_blocks) {
 
 // The index scan of a Full layer, between the caller's events the first time.
 hipError_t timed_scan(const ScoreLaunch& sa, const csa2_chain_params* p, bool* timed, hipStream_t stream) {
+    // the events are stamped by the kernel's own dispatch (no extra packets
+    // in the queue around it)
     const bool rec = !*timed && (p->scan_begin || p->scan_end);
-    hipError_t e;
-    if (rec && p->scan_begin && (e = hipEventRecord(p->scan_begin, stream)) != hipSuccess) return e;
-    if ((e = launch_index_score(sa, stream)) != hipSuccess) return e;
-    if (rec && p->scan_end && (e = hipEventRecord(p->scan_end, stream)) != hipSuccess) return e;
+    ScoreLaunch a = sa;
+    if (rec) {
+        a.ev_begin = p->scan_begin;
+        a.ev_end = p->scan_end;
+    }
+    const hipError_t e = launch_index_score(a, stream);
+    if (e != hipSuccess) return e;
     *timed = true;
     return hipSuccess;
 }
@@ -371,11 +376,18 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                 lo.chunk = ch;
                 lo.K = p->K;
                 lo.block = p->block;
-                if ((e = clear_topk_ws(topk_ws, g.total_q, true, stream)) != hipSuccess) return hip_fail(e);
+                // rows of few chunks: one kernel selects from the lists alone;
+                // longer rows: the scan also fills the rows' histograms, and
+                // the lists are filtered by many workgroups first
+                const bool fused_topk = (int64_t)lo.max_chunks * lo.chunk <= kFusedTopkEntries;
+                if (!fused_topk && (e = clear_topk_ws(topk_ws, g.total_q, true, stream)) != hipSuccess)
+                    return hip_fail(e);
                 ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, L.k_fp4, L.k_sc,
-                               nullptr, 0, nullptr, 0, topk_ws_hist(topk_ws), &lo};
+                               nullptr, 0, nullptr, 0, fused_topk ? nullptr : topk_ws_hist(topk_ws), &lo};
                 if ((e = timed_scan(sa, p, &scan_timed, stream)) != hipSuccess) return hip_fail(e);
-                if ((e = launch_topk_local(batch, g, lo, idx_cur, topk_ws, stream)) != hipSuccess) return hip_fail(e);
+                if ((e = fused_topk ? launch_topk_fused(batch, g, lo, idx_cur, stream)
+                                    : launch_topk_local(batch, g, lo, idx_cur, topk_ws, stream)) != hipSuccess)
+                    return hip_fail(e);
                 if (build_pool) {  // after the Top-K: the pool's selection reuses its workspace
                     PoolLaunch pa{};
                     pa.b = batch;

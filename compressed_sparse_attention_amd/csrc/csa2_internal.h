@@ -84,10 +84,25 @@ __device__ inline uint32_t block_scan_256(uint32_t v, uint32_t* wtot) {
 struct PlainBins {
     const uint32_t* h;
     __device__ uint32_t operator()(int b) const { return h[b]; }
+    // bins lo .. lo+15 (lo a multiple of 16) in four 16-byte loads
+    __device__ void load16(int lo, uint32_t* c) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = *reinterpret_cast<const uint4*>(h + lo + 4 * i);
+            c[4 * i] = v.x;
+            c[4 * i + 1] = v.y;
+            c[4 * i + 2] = v.z;
+            c[4 * i + 3] = v.w;
+        }
+    }
 };
 struct PackedBins {
     const uint32_t* h;
     __device__ uint32_t operator()(int b) const { return (h[b >> 1] >> (16 * (b & 1))) & 0xFFFFu; }
+    __device__ void load16(int lo, uint32_t* c) const {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[i] = (*this)(lo + i);
+    }
 };
 
 // Block-wide (256 threads): the bin that holds the kk-th largest key; every
@@ -99,11 +114,12 @@ __device__ inline uint32_t threshold_bin(Bins h, uint32_t kk, uint32_t* wtot, ui
     const int t = threadIdx.x;
     // thread t owns bins [4096 - 16(t+1), 4096 - 16t), i.e. thread 0 the top bins
     const int hi = kHistBins - 16 * t;
-    uint32_t c[16];
+    uint32_t up[16], c[16];  // up[i] = bin hi - 16 + i, c[i] = bin hi - 1 - i
+    h.load16(hi - 16, up);
     uint32_t s = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        c[i] = h(hi - 1 - i);
+        c[i] = up[15 - i];
         s += c[i];
     }
     if (t == 0) {
@@ -184,6 +200,7 @@ struct ScoreLaunch {
     int64_t stride;
     uint32_t* hist;             // nullable: [total_q][kHistBins], zeroed by the caller
     const LocalOut* local;      // nullable: decode scan writes per-chunk candidate lists, not scores
+    hipEvent_t ev_begin = nullptr, ev_end = nullptr;  // optional: stamped by the score kernel's dispatch
 };
 hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s);
 
@@ -213,6 +230,12 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 // cleared before the scan together with the row state)
 hipError_t launch_topk_local(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, void* ws,
                              hipStream_t s);
+
+// The whole Top-K from a scan's per-chunk lists in one kernel (one workgroup
+// per row, no histogram from the scan), for rows whose lists hold at most
+// kFusedTopkEntries entries (max_chunks * chunk)
+constexpr int kFusedTopkEntries = 16384;
+hipError_t launch_topk_fused(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, hipStream_t s);
 
 struct PoolLaunch {
     const csa2_batch* b;

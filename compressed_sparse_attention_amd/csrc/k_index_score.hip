@@ -21,6 +21,8 @@
 // of the 32 supplies k = 16g + e (e < 16) and k = 32 + 16g + (e-16) (e >= 16).
 // Result element (row m, column n) lands in lane n + 32*((m/4)%2), register
 // 4*(m/8) + m%4.
+#include <hip/hip_ext.h>
+
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -324,7 +326,8 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
             // alone has K positions at or above its threshold), and a chunk with
             // fewer flushes all its bins, so the row's counts at and above B are
             // complete, which is all the threshold search reads.
-            hist16_flush(hl + t * (kHistBins / 2), hist + (int64_t)row * kHistBins, kk ? bstar : (uint32_t)kHistBins);
+            if (hist)  // the fused Top-K builds the row histogram from the lists instead
+                hist16_flush(hl + t * (kHistBins / 2), hist + (int64_t)row * kHistBins, kk ? bstar : (uint32_t)kHistBins);
             __syncthreads();  // threshold_bin's LDS scratch is reused by the next row
         }
     } else {
@@ -747,7 +750,7 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
     if (a.cand) {
         dim3 grid((a.cand_stride + 1023) / 1024, a.g.total_q);
 #define CSA2_CAND(HH, HI)                                                                                        \
-    hipLaunchKernelGGL((k_score_cand<HH, HI>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,            \
+    hipExtLaunchKernelGGL((k_score_cand<HH, HI>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,            \
                        b->d_entry_off, b->d_row_seq, b->d_q_pos, b->ratio, a.cand, a.cand_stride, a.scores,      \
                        a.stride, a.hist)
         if (a.H == 64) {
@@ -765,7 +768,7 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
         const LocalOut lo = a.local ? *a.local : LocalOut{};
         dim3 grid((unsigned)((a.g.max_entries + chunk - 1) / chunk), a.g.n_seq);
 #define CSA2_DEC(HH, TT, OO)                                                                                     \
-    hipLaunchKernelGGL((k_score_decode<HH, TT, OO>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,      \
+    hipExtLaunchKernelGGL((k_score_decode<HH, TT, OO>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,      \
                        b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, a.hist, lo)
 #define CSA2_DEC_T(HH, OO) \
     do { if (one) CSA2_DEC(HH, 1, OO); else CSA2_DEC(HH, 4, OO); } while (0)
@@ -787,16 +790,16 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
         constexpr int64_t seg = (int64_t)kPrefillChunk * kPrefillSegChunks;
         dim3 grid((unsigned)((a.g.max_entries + seg - 1) / seg), (unsigned)((a.g.max_q_per_seq + 7) / 8), a.g.n_seq);
         if (a.H == 64)
-            hipLaunchKernelGGL((k_score_prefill_fp8<64>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,
+            hipExtLaunchKernelGGL((k_score_prefill_fp8<64>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,
                                b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride);
         else
-            hipLaunchKernelGGL((k_score_prefill_fp8<32>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,
+            hipExtLaunchKernelGGL((k_score_prefill_fp8<32>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,
                                b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((a.g.max_entries + 1023) / 1024), (unsigned)((a.g.max_q_per_seq + 7) / 8), a.g.n_seq);
 #define CSA2_PRE(HH, FF)                                                                                          \
-    hipLaunchKernelGGL((k_score_prefill<HH, FF>), grid, dim3(256), 0, s, a.q, a.q_sc, a.w, a.k, a.k_sc,          \
+    hipExtLaunchKernelGGL((k_score_prefill<HH, FF>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,          \
                        b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride)
     if (a.H == 64) CSA2_PRE(64, 4); else CSA2_PRE(32, 4);
 #undef CSA2_PRE

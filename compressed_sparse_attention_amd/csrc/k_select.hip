@@ -537,6 +537,234 @@ __global__ __launch_bounds__(1024) void k_final_local(const uint64_t* __restrict
     }
 }
 
+// Inclusive scan of one value per thread over a 1024-thread workgroup; `total`
+// receives the workgroup's sum.  Every thread calls it; it ends with a
+// barrier, so `wsum` may be reused right after.
+__device__ inline uint32_t block_scan_1024(uint32_t v, uint32_t* wsum, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) {
+        const uint32_t x = wsum[w2];
+        before += w2 < wave ? x : 0u;
+        tot += x;
+    }
+    *total = tot;
+    __syncthreads();
+    return before + v;
+}
+
+// The whole selection of a row from a decode scan's per-chunk lists, in one
+// workgroup of 1024 threads per row, for rows of a few chunks (the launcher
+// bounds max_chunks * chunk by kFusedEntries).  The histogram of the row's
+// Top-K threshold search is built here from the lists themselves: a chunk's
+// list holds exactly its visible positions at or above the chunk's threshold
+// bin, and the row's threshold bin B lies at or above the threshold of every
+// chunk with K visible positions (a chunk with fewer lists all its
+// positions), so the lists hold every position of the row at or above B, and
+// their histogram has the row's exact counts from B up, which is all the
+// search reads.  Then the entries at or above B are compacted into LDS in
+// concatenation order (chunk order, i.e. position order), the threshold bin's
+// keys are radix-selected from bit 51 down, and the winners are written in
+// that same order.  Each thread holds up to kFusedPer consecutive entries of
+// the concatenation in registers.
+constexpr int kFusedEntries = kFusedTopkEntries;
+constexpr int kFusedPer = kFusedEntries / 1024;
+
+__global__ __launch_bounds__(1024) void k_topk_local(const uint64_t* __restrict__ lists,
+                                                     const uint32_t* __restrict__ counts, int max_chunks, int chunk,
+                                                     RowSrc rs, int K, int32_t* __restrict__ idx) {
+    __shared__ uint64_t c[kFusedEntries];
+    __shared__ uint32_t hcopy[64 * 32];
+    __shared__ uint32_t dcount[64];
+    __shared__ uint32_t roff[kFusedEntries / 64 + 1];
+    __shared__ uint32_t hist256[256], scan256[256];
+    __shared__ RadixState st;
+    __shared__ int found;
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t base, thr[2];
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n = row_n(rs, row);
+    const uint32_t kk = (uint32_t)(n < K ? n : K);
+    int32_t* out = idx + (int64_t)row * K;
+    for (int i = tid + (int)kk; i < K; i += 1024) out[i] = -1;
+    if (kk == 0) return;
+    const int n_ch = (int)((n + chunk - 1) / chunk);  // <= max_chunks <= 1024
+    const uint64_t* lrow = lists + (int64_t)row * max_chunks * chunk;
+    if (tid == 0) {
+        thr[0] = 0;
+        thr[1] = 0;
+    }
+    // run offsets: exclusive prefix sum of the lists' lengths
+    {
+        const uint32_t v = tid < n_ch ? counts[(int64_t)row * max_chunks + tid] : 0u;
+        uint32_t tot;
+        const uint32_t incl = block_scan_1024(v, wsum, &tot);
+        if (tid < n_ch) roff[tid] = incl - v;
+        if (tid == 0) roff[n_ch] = tot;
+        __syncthreads();
+    }
+    const uint32_t total = roff[n_ch];  // <= n_ch * chunk <= kFusedEntries
+    const uint32_t P = (total + 1023) / 1024;
+    const uint32_t e_lo = P * (uint32_t)tid;
+
+    // this thread's entries [e_lo, e_lo + P): first every entry's place in
+    // the lists (no load is in flight while this walks: a loop between the
+    // loads below would make each load wait for the previous ones), then all
+    // the loads at once
+    uint64_t key[kFusedPer];
+    {
+        int ch = 0;
+        if (e_lo < total) {
+            int lo = 0, hi = n_ch;  // roff[lo] <= e_lo < roff[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (roff[mid] <= e_lo) lo = mid; else hi = mid;
+            }
+            ch = lo;
+        }
+        uint32_t bound = roff[ch + 1], start = roff[ch];
+        uint32_t at[kFusedPer];
+#pragma unroll
+        for (int u = 0; u < kFusedPer; ++u) {
+            const uint32_t e = e_lo + (uint32_t)u;
+            at[u] = 0;
+            if ((uint32_t)u < P && e < total) {
+                while (e >= bound) {
+                    ++ch;
+                    start = bound;
+                    bound = roff[ch + 1];
+                }
+                at[u] = (uint32_t)ch * (uint32_t)chunk + (e - start);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kFusedPer; ++u)
+            key[u] = ((uint32_t)u < P && e_lo + (uint32_t)u < total) ? lrow[at[u]] : 0ull;
+    }
+
+    // the threshold bin B, in two 6-bit digits (bin = 64 d1 + d2).  Each level
+    // counts the digits of the entries that match the digits found so far
+    // into 32 copies of a 64-entry histogram (lane l adds to copy l % 32),
+    // because the entries crowd into a few bins and same-address LDS atomics
+    // serialise; then the copies are summed and the digit holding the
+    // need-th largest entry is found from the top.
+    uint32_t B = 0, above = 0;
+    {
+        uint32_t need = kk;
+#pragma unroll
+        for (int level = 0; level < 2; ++level) {
+            for (int i = tid; i < 64 * 32; i += 1024) hcopy[i] = 0;
+            __syncthreads();
+            uint32_t* hc = hcopy + (lane & 31);
+#pragma unroll
+            for (int u = 0; u < kFusedPer; ++u) {
+                const uint32_t bin = (uint32_t)(key[u] >> 51);
+                const bool in = (uint32_t)u < P && e_lo + (uint32_t)u < total && (level == 0 || (bin >> 6) == B);
+                if (in) atomicAdd(&hc[32 * (level == 0 ? bin >> 6 : bin & 63u)], 1u);
+            }
+            __syncthreads();
+            {  // digit d = tid / 16 sums copies 2 (tid % 16), +1; 16 lanes reduce
+                const int d = tid >> 4, part = tid & 15;
+                uint32_t v = hcopy[32 * d + 2 * part] + hcopy[32 * d + 2 * part + 1];
+#pragma unroll
+                for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
+                if (part == 0) dcount[d] = v;
+            }
+            __syncthreads();
+            if (wave == 0) {  // lane l owns digit 63 - l; inclusive scan from the top
+                const uint32_t v = dcount[63 - lane];
+                uint32_t incl = v;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t u2 = __shfl_up(incl, o);
+                    if (lane >= o) incl += u2;
+                }
+                const uint32_t before = incl - v;
+                if (before < need && need <= incl) {
+                    thr[0] = (uint32_t)(63 - lane);
+                    thr[1] = before;
+                }
+            }
+            __syncthreads();
+            B = level == 0 ? thr[0] : (B << 6) | thr[0];
+            above += thr[1];
+            need -= thr[1];
+            __syncthreads();  // thr and hcopy are rewritten by the next level
+        }
+    }
+
+    // the entries at or above B, compacted into LDS in order
+    uint32_t n_cand;
+    {
+        uint32_t take = 0;
+#pragma unroll
+        for (int u = 0; u < kFusedPer; ++u)
+            take |= (uint32_t)((uint32_t)u < P && e_lo + (uint32_t)u < total && (uint32_t)(key[u] >> 51) >= B) << u;
+        const uint32_t mine = (uint32_t)__popc(take);
+        uint32_t off = block_scan_1024(mine, wsum, &n_cand) - mine;
+#pragma unroll
+        for (int u = 0; u < kFusedPer; ++u)
+            if ((take >> u) & 1u) c[off++] = key[u];
+    }
+    if (tid == 0) {
+        st.prefix = B;
+        st.shift = 51;
+        st.need = kk - above;
+        st.done = 0;
+        base = 0;
+    }
+    __syncthreads();
+
+    // radix select among the threshold bin's keys (the bins above all win)
+    while (!st.done) {
+        if (tid < 256) hist256[tid] = 0;
+        __syncthreads();
+        const int sh = st.shift;
+        const int w = digit_bits(sh);
+        const uint64_t pf = st.prefix;
+        for (uint32_t e = tid; e < n_cand; e += 1024) {
+            const uint64_t x = c[e];
+            if ((x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
+        }
+        __syncthreads();
+        radix_step(hist256, scan256, &st, &found);
+    }
+    const int sh = st.shift;
+    const uint64_t pf = st.prefix;
+
+    // winners (key64 >= prefix << shift) in candidate order = position order
+    for (uint32_t e0 = 0; e0 < n_cand; e0 += 1024) {
+        const uint32_t e = e0 + tid;
+        const uint64_t x = e < n_cand ? c[e] : 0ull;
+        const bool win = e < n_cand && (x >> sh) >= pf;
+        const uint64_t m = __ballot(win);
+        if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t o = base;
+        for (int w2 = 0; w2 < wave; ++w2) o += wsum[w2];
+        if (win) {
+            const uint32_t p = o + (uint32_t)__popcll(m & ((1ull << lane) - 1));
+            if (p < kk) out[p] = (int32_t)(0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu));
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t t2 = 0;
+            for (int w2 = 0; w2 < 16; ++w2) t2 += wsum[w2];
+            base += t2;
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // block pool
 // ---------------------------------------------------------------------------
@@ -658,6 +886,14 @@ hipError_t launch_topk_local(const csa2_batch* b, const Geometry& g, const Local
                        lo.max_chunks, lo.chunk, (const RowSel*)sel);
     hipLaunchKernelGGL(k_final_local, dim3(nq), dim3(1024), 0, s, (const uint64_t*)lo.lists, (const uint32_t*)lo.counts,
                        lo.max_chunks, lo.chunk, (const RowSel*)sel, lo.K, idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_fused(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, hipStream_t s) {
+    if ((int64_t)lo.max_chunks * lo.chunk > kFusedEntries) return hipErrorInvalidValue;
+    RowSrc rs{b->d_entry_off, b->d_row_seq, b->d_q_pos, b->ratio, nullptr, 0, 1, g.max_entries};
+    hipLaunchKernelGGL(k_topk_local, dim3(g.total_q), dim3(1024), 0, s, (const uint64_t*)lo.lists,
+                       (const uint32_t*)lo.counts, lo.max_chunks, lo.chunk, rs, lo.K, idx);
     return hipGetLastError();
 }
 

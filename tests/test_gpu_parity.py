@@ -262,6 +262,16 @@ TIE_CASES = {
     # one head: few distinct scores, long runs of ties at the thresholds
     "one_head_t1": dict(lens=[3, 700, 9000, 20000], T=1, heads=1),
     "one_head_t4": dict(lens=[5, 3000, 20000], T=4, heads=1),
+    # rows of at most 16,384 list entries take the one-kernel selection over
+    # the scan's lists: every score tied at its fullest, few distinct scores
+    # with four rows per sequence, and distinct scores
+    "all_equal_fused_t1": dict(lens=[3, 700, 9000, 16384], T=1, heads=0),
+    "one_head_fused_t4": dict(lens=[5, 3000, 8192], T=4, heads=1),
+    "fused_h64": dict(lens=[16384, 1000], T=1, heads=64),
+    # longer rows: the lists are filtered by many workgroups first, from the
+    # scan's histograms (heavy ties, and a row of 74 chunks)
+    "all_equal_long": dict(lens=[40000, 100], T=1, heads=0),
+    "split_topk": dict(lens=[300000, 5000], T=1, heads=64),
 }
 
 
