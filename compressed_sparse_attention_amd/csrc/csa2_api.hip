@@ -84,7 +84,7 @@ ChainWs chain_ws(const Geometry& g, int K, int block, int max_blocks) {
     size_t off = 0;
     w.scores = off;  // score rows, or the scan's per-chunk lists and counts (never both in one layer)
     const size_t rows_bytes = al256((size_t)g.total_q * (size_t)(g.max_entries > 0 ? g.max_entries : 1) * 4);
-    const size_t lists_bytes = al256(local_lists_bytes(g)) + al256(local_counts_bytes(g));
+    const size_t lists_bytes = al256(local_lists_bytes(g)) + 2 * al256(local_counts_bytes(g));  // lists, counts, bounds
     off += rows_bytes > lists_bytes ? rows_bytes : lists_bytes;
     w.pool_scores = off;
     off += al256((size_t)g.total_q * (size_t)max_blocks * block * 4);
@@ -376,10 +376,13 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                 lo.chunk = ch;
                 lo.K = p->K;
                 lo.block = p->block;
-                // rows of few chunks: one kernel selects from the lists alone;
-                // longer rows: the scan also fills the rows' histograms, and
-                // the lists are filtered by many workgroups first
-                const bool fused_topk = (int64_t)lo.max_chunks * lo.chunk <= kFusedTopkEntries;
+                // rows of few chunks: one kernel selects from the lists alone
+                // (with the chunks' bounds); longer rows: the scan also fills
+                // the rows' histograms, and the lists are filtered by many
+                // workgroups first
+                const bool fused_topk =
+                    lo.max_chunks <= kListChunks && (int64_t)lo.max_chunks * lo.chunk <= kFusedTopkEntries;
+                if (fused_topk) lo.lbins = (uint32_t*)((char*)lo.counts + al256(local_counts_bytes(g)));
                 if (!fused_topk && (e = clear_topk_ws(topk_ws, g.total_q, true, stream)) != hipSuccess)
                     return hip_fail(e);
                 ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, L.k_fp4, L.k_sc,

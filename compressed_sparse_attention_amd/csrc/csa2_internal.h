@@ -99,9 +99,18 @@ struct PlainBins {
 struct PackedBins {
     const uint32_t* h;
     __device__ uint32_t operator()(int b) const { return (h[b >> 1] >> (16 * (b & 1))) & 0xFFFFu; }
+    // bins lo .. lo+15 (lo a multiple of 16) in two 16-byte loads
     __device__ void load16(int lo, uint32_t* c) const {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) c[i] = (*this)(lo + i);
+        for (int i = 0; i < 2; ++i) {
+            const uint4 v = *reinterpret_cast<const uint4*>(h + (lo >> 1) + 4 * i);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[8 * i + 2 * j] = w[j] & 0xFFFFu;
+                c[8 * i + 2 * j + 1] = w[j] >> 16;
+            }
+        }
     }
 };
 
@@ -144,6 +153,49 @@ __device__ inline uint32_t threshold_bin(Bins h, uint32_t kk, uint32_t* wtot, ui
     return found[0];
 }
 
+// The same search for two ranks k1 and k2 at once (k2 == 0: not searched):
+// returns the bin of the k1-th largest key and leaves that of the k2-th in
+// *bin2 (kHistBins when the rank is 0).  found[0..3] is LDS scratch.
+template <class Bins>
+__device__ inline uint32_t threshold_bin2(Bins h, uint32_t k1, uint32_t k2, uint32_t* wtot, uint32_t* found,
+                                          uint32_t* bin2) {
+    const int t = threadIdx.x;
+    const int hi = kHistBins - 16 * t;
+    uint32_t up[16], c[16];
+    h.load16(hi - 16, up);
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        c[i] = up[15 - i];
+        s += c[i];
+    }
+    if (t == 0) {
+        found[0] = k1 == 0 ? (uint32_t)kHistBins : 0u;
+        found[2] = k2 == 0 ? (uint32_t)kHistBins : 0u;
+    }
+    const uint32_t incl = block_scan_256(s, wtot);
+    const uint32_t before = incl - s;
+    const uint32_t ks[2] = {k1, k2};
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const uint32_t kk = ks[r];
+        if (kk > 0 && before < kk && kk <= incl) {
+            uint32_t acc = before;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (acc + c[i] >= kk) {
+                    found[2 * r] = (uint32_t)(hi - 1 - i);
+                    break;
+                }
+                acc += c[i];
+            }
+        }
+    }
+    __syncthreads();
+    *bin2 = found[2];
+    return found[0];
+}
+
 // ---------------------------------------------------------------------------
 // Per-chunk candidate lists written by the decode scan in place of the full
 // score rows.  A chunk is a run of positions one scan workgroup covers.  For
@@ -157,6 +209,8 @@ struct LocalOut {
     uint64_t* lists;     // [total_q][max_chunks][chunk]
     uint32_t* counts;    // [total_q][max_chunks]; written for chunks that hold positions
     float* bscores;      // nullable: block maxima [total_q][bstride] for the block pool
+    uint32_t* lbins;     // nullable: [total_q][max_chunks], for each chunk whose positions are all
+                         // visible, the bin of its ceil(K / such chunks)-th largest score
     int64_t bstride;
     int max_chunks;
     int chunk;
@@ -232,9 +286,12 @@ hipError_t launch_topk_local(const csa2_batch* b, const Geometry& g, const Local
                              hipStream_t s);
 
 // The whole Top-K from a scan's per-chunk lists in one kernel (one workgroup
-// per row, no histogram from the scan), for rows whose lists hold at most
-// kFusedTopkEntries entries (max_chunks * chunk)
-constexpr int kFusedTopkEntries = 16384;
+// per row, no histogram from the scan).  Correct for any list length up to
+// kListChunks chunks per row; chosen for rows of at most kFusedTopkEntries
+// entries (max_chunks * chunk), whose lists one workgroup reads in a few
+// passes, while longer rows spread the filtering over many workgroups.
+constexpr int kListChunks = 1024;
+constexpr int64_t kFusedTopkEntries = 262144;
 hipError_t launch_topk_fused(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, hipStream_t s);
 
 struct PoolLaunch {

@@ -77,29 +77,36 @@ __global__ __launch_bounds__(64) void k_gather_dequant(const uint8_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// sparse attention: one workgroup per (query row, group of 16 heads), 4 waves.
-// Keys come in blocks of 64: first the selected entries (idx order), then the
-// SWA rows of the window.  Per block: dequantise into LDS (row-major bf16),
-// S = Q K^T on v_mfma_f32_16x16x32_bf16 (wave w: keys 16w..16w+15), online
-// softmax in fp32, O += P V (wave w: channels 128w..128w+127) with V read
-// transposed by ds_read_b64_tr_b16.
+// sparse attention: one workgroup per (query row, group of 16 heads), two
+// groups of 4 waves ("pipes").  Keys come in blocks of 64: first the SWA rows
+// of the window, then the selected entries (idx order); pipe g takes the
+// blocks blk0 + 2i + g of its part of the row, each pipe with its own LDS key
+// buffer and its own online-softmax state, so that every SIMD has two waves to
+// interleave.  Per block: dequantise into LDS (row-major bf16), S = Q K^T on
+// v_mfma_f32_16x16x32_bf16 (wave w: keys 16w..16w+15), online softmax in
+// fp32, O += P V (wave w: channels 128w..128w+127) with V read transposed by
+// ds_read_b64_tr_b16.  At the end the two pipes' (max, sums, O) are merged.
+// The loads of the first iteration (the SWA rows) are issued together with
+// the query and the index row; later blocks are fetched one iteration ahead.
 // ---------------------------------------------------------------------------
 constexpr int HG = 16;
 constexpr int KB = 64;
+constexpr int NPIPE = 2;
 constexpr int LROW = 512 + 8;  // LDS row stride of the staged keys in bf16 (16 B of padding)
 constexpr int SLROW = KB + 4;  // LDS row stride of the logits in floats
 
-__global__ __launch_bounds__(256) void k_sparse_attn(
+__global__ __launch_bounds__(512) void k_sparse_attn(
     const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
     const int32_t* __restrict__ idx, int K, const uint16_t* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
     const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ replay_s, int W,
     const int64_t* __restrict__ entry_off, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ q_pos,
     float scale_log2, float* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg, int S,
     float* __restrict__ partial) {
-    __shared__ __attribute__((aligned(16))) uint16_t kl[KB * LROW];
-    __shared__ float sl[HG][SLROW];
-    __shared__ int kvalid[KB];
+    __shared__ __attribute__((aligned(16))) uint16_t kl[NPIPE][KB * LROW];
+    __shared__ float sl[NPIPE][HG][SLROW];
+    __shared__ int kvalid[NPIPE][KB];
     __shared__ int32_t kidx[kMaxK];
+    __shared__ float mls[HG][3];
     __shared__ int nsel_sh;
 
     // the n_hg x S workgroups of one row share an XCD (workgroups are dealt to
@@ -114,9 +121,31 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     if (row >= total_q) return;
 
     const int tid = threadIdx.x;
+    const int pipe = __builtin_amdgcn_readfirstlane(tid >> 8);
+    const int pt = tid & 255;  // thread within the pipe
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wave within the pipe
     const int lg = lane >> 4, li = lane & 15;
+
+    // ---- prologue: the query and the index row first (they need only the
+    // row), then the sequence's window and, with it, the first block's SWA rows
+    const int hq = HG * hg + li;
+    v8bf Q[16];
+    {
+        const uint16_t* qr = q + ((int64_t)row * Hm + hq) * 512 + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, ld16(qr + 32 * ks));
+    }
+    const int32_t* irow = idx + (int64_t)row * K;
+    int32_t ir[kMaxK / 512];
+#pragma unroll
+    for (int i = 0; i < kMaxK / 512; ++i) {
+        const int s = tid + 512 * i;
+        ir[i] = s < K ? irow[s] : -1;
+    }
+    // keep the loads above ahead of the scalar loads below (they would
+    // otherwise wait for them)
+    asm volatile("" ::: "memory");
 
     const int b = row_seq[row];
     const int64_t t = q_pos[row];
@@ -126,60 +155,63 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
     int64_t u_lo = t - W + 1;
     u_lo = u_lo > s_rep ? u_lo : s_rep;
     const int n_swa = t >= u_lo ? (int)(t - u_lo + 1) : 0;
-    const int32_t* irow = idx + (int64_t)row * K;  // staged into kidx below
+    const int64_t swa_r0 = swa_row_off[b] + (u_lo - swa_pos0[b]);  // row of key 0 in `swa`
 
+    // the split of the row's blocks over the S workgroups is fixed by the
+    // largest key count (window + K), so it is known before the index row
+    const int max_blocks = (n_swa + K + KB - 1) / KB;
+    const int per = (max_blocks + S - 1) / S;
+    const int blk0 = sp * per;
+    const int blk1 = blk0 + per < max_blocks ? blk0 + per : max_blocks;
+    const int n_it = (blk1 - blk0 + NPIPE - 1) / NPIPE;
+
+    // this thread stages key `skey` of its pipe's blocks, channels CP*part .. +CP
+    constexpr int CP = 128;         // channels per part (4 parts)
+    constexpr int NB = CP / 32;     // 32-channel scale blocks per part
+    const int skey = (pt & 15) + 16 * (pt >> 6), part = (pt >> 4) & 3;
+
+    const int vk_first = KB * (blk0 + pipe) + skey;
+    const bool first_swa = blk0 + pipe < blk1 && vk_first < n_swa;
+    v4i sw[CP / 8];
+    if (first_swa) {
+        const uint16_t* src = swa + (swa_r0 + vk_first) * 512 + CP * part;
+#pragma unroll
+        for (int i = 0; i < CP / 8; ++i) sw[i] = ld16(src + 8 * i);
+    }
     if (tid == 0) nsel_sh = 0;
     __syncthreads();
     {
         int last = 0;
-        for (int s = tid; s < K; s += 256) {
-            int32_t j = irow[s];
-            j = (j >= 0 && j < n_ent) ? j : -1;  // out-of-range entries read as empty
-            kidx[s] = j;
-            if (j >= 0) last = s + 1;
+#pragma unroll
+        for (int i = 0; i < kMaxK / 512; ++i) {
+            const int s = tid + 512 * i;
+            if (s < K) {
+                const int32_t j = (ir[i] >= 0 && ir[i] < n_ent) ? ir[i] : -1;  // out-of-range entries read as empty
+                kidx[s] = j;
+                if (j >= 0) last = s + 1;
+            }
         }
         if (last) atomicMax(&nsel_sh, last);
     }
     __syncthreads();
     const int n_sel = nsel_sh;
-    const int n_keys = n_sel + n_swa;
-    const int n_blocks = (n_keys + KB - 1) / KB;
-    const int per = (n_blocks + S - 1) / S;
-    const int blk0 = sp * per;
-    const int blk1 = blk0 + per < n_blocks ? blk0 + per : n_blocks;
+    const int n_keys = n_swa + n_sel;
 
-    // Q operand (16 heads x 512): lane holds head 16hg + li, channels 8lg + 32ks + [0, 8)
-    const int hq = HG * hg + li;
-    v8bf Q[16];
-    {
-        const uint16_t* qr = q + ((int64_t)row * Hm + hq) * 512 + 8 * lg;
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, ld16(qr + 32 * ks));
-        // wait for Q here (vmcnt 0, other counters untouched) so that the loop
-        // below never waits on memory except for the block it stages
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
     v4f O[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) O[nt] = v4f{0.f, 0.f, 0.f, 0.f};
-    // running max and sums for head li (identical in every wave): l_run sums the
-    // bf16 weights the P V product uses (it normalises the output), l_lse the
-    // fp32 weights (it gives the log-sum-exp)
+    // running max and sums for head li (identical in every wave of a pipe):
+    // l_run sums the bf16 weights the P V product uses (it normalises the
+    // output), l_lse the fp32 weights (it gives the log-sum-exp)
     float m_run = -INFINITY, l_run = 0.0f, l_lse = 0.0f;
 
-    // this thread stages key `skey` of each block, channels CP*part .. +CP;
-    // the main-KV part of the next block is fetched into registers while the
-    // current block computes.  16 consecutive lanes take 16 keys of one part,
-    // so that their LDS writes of a row segment fall in distinct banks.
-    constexpr int CP = 128;         // channels per part (4 parts)
-    constexpr int NB = CP / 32;     // 32-channel scale blocks per part
-    const int skey = (tid & 15) + 16 * (tid >> 6), part = (tid >> 4) & 3;
+    // FP4 rows of a selected key, fetched one iteration ahead
     v4i pc[NB];
     uint32_t psc = 0;
     auto fetch = [&](int blk) {
         const int vk = KB * blk + skey;
-        if (vk < n_sel && blk < blk1) {
-            const int32_t j = kidx[vk];
+        if (blk < blk1 && vk >= n_swa && vk < n_keys) {
+            const int32_t j = kidx[vk - n_swa];
             if (j >= 0) {
                 const int64_t e = e0 + j;
                 const uint8_t* src = kv + e * 256 + (CP / 2) * part;
@@ -189,137 +221,190 @@ __global__ __launch_bounds__(256) void k_sparse_attn(
             }
         }
     };
-    fetch(blk0);
-
-    for (int blk = blk0; blk < blk1; ++blk) {
-        // 1) stage 64 keys
-        {
-            const int vk = KB * blk + skey;
-            uint16_t* dst = kl + skey * LROW + CP * part;
-            int valid = 0;
-            if (vk < n_sel) {
-                if (kidx[vk] >= 0) {
-                    valid = 1;
+    // stage this thread's key of block blk into the pipe's buffer: SWA rows
+    // from `sw` (first iteration) or loaded here (windows longer than the
+    // first iteration's blocks), selected entries from the prefetched FP4 rows
+    uint16_t* klp = kl[pipe];
+    auto stage = [&](int blk, bool swa_in_regs) {
+        const int vk = KB * blk + skey;
+        uint16_t* dst = klp + skey * LROW + CP * part;
+        int valid = 0;
+        if (vk < n_swa) {
+            valid = 1;
+            if (!swa_in_regs) {
+                const uint16_t* src = swa + (swa_r0 + vk) * 512 + CP * part;
 #pragma unroll
-                    for (int i = 0; i < NB; ++i) {  // 32 channels per scale
-                        const float sc = e8m0_f32((psc >> (8 * i)) & 255u);
-#pragma unroll
-                        for (int d = 0; d < 4; ++d)
-                            *reinterpret_cast<v4i*>(dst + 32 * i + 8 * d) = fp4x8_to_bf16((uint32_t)pc[i][d], sc);
-                    }
-                }
-            } else if (vk < n_keys) {
-                valid = 1;
-                const int64_t u = u_lo + (vk - n_sel);
-                const int64_t r = swa_row_off[b] + (u - swa_pos0[b]);
-                const uint16_t* src = swa + r * 512 + CP * part;
-                v4i tmp[CP / 8];
-#pragma unroll
-                for (int i = 0; i < CP / 8; ++i) tmp[i] = ld16(src + 8 * i);
-#pragma unroll
-                for (int i = 0; i < CP / 8; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = tmp[i];
+                for (int i = 0; i < CP / 8; ++i) sw[i] = ld16(src + 8 * i);
             }
-            if (!valid) {
 #pragma unroll
-                for (int i = 0; i < CP / 8; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = v4i{0, 0, 0, 0};
+            for (int i = 0; i < CP / 8; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = sw[i];
+        } else if (vk < n_keys && kidx[vk - n_swa] >= 0) {
+            valid = 1;
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {  // 32 channels per scale
+                const float sc = e8m0_f32((psc >> (8 * i)) & 255u);
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    *reinterpret_cast<v4i*>(dst + 32 * i + 8 * d) = fp4x8_to_bf16((uint32_t)pc[i][d], sc);
             }
-            if (part == 0) kvalid[skey] = valid;
         }
-        fetch(blk + 1);
+        if (!valid) {
+#pragma unroll
+            for (int i = 0; i < CP / 8; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = v4i{0, 0, 0, 0};
+        }
+        if (part == 0) kvalid[pipe][skey] = valid;
+    };
+
+    // first iteration: a selected key in it is loaded now (short windows or a
+    // later part of the row); the next iteration's rows are fetched behind it
+    if (blk0 + pipe < blk1) {
+        fetch(blk0 + pipe);
+        stage(blk0 + pipe, true);
+    }
+    fetch(blk0 + pipe + NPIPE);
+
+    for (int it = 0; it < n_it; ++it) {
+        const int blk = blk0 + NPIPE * it + pipe;
+        const bool active = blk < blk1 && KB * blk < n_keys;  // uniform per pipe
+        if (it > 0) {
+            if (blk < blk1) stage(blk, false);
+            fetch(blk + NPIPE);
+        }
         __syncthreads();
 
         // 2) S = Q K^T for keys 16*wave .. +16: lane gets S[head 4lg+v][key 16wave + li]
-        {
+        if (active) {
             // four independent accumulation chains over the 16 k-steps
             v4f Sp[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            const uint16_t* kr = kl + (16 * wave + li) * LROW + 8 * lg;
+            const uint16_t* kr = klp + (16 * wave + li) * LROW + 8 * lg;
 #pragma unroll
             for (int ks = 0; ks < 16; ++ks) {
                 const v8bf Bk = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kr + 32 * ks));
                 Sp[ks & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Q[ks], Bk, Sp[ks & 3], 0, 0, 0);
             }
-            const v4f S = (Sp[0] + Sp[1]) + (Sp[2] + Sp[3]);
+            const v4f Sv = (Sp[0] + Sp[1]) + (Sp[2] + Sp[3]);
             const int key = 16 * wave + li;
-            const bool ok = kvalid[key] != 0;
+            const bool ok = kvalid[pipe][key] != 0;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sl[4 * lg + v][key] = ok ? S[v] * scale_log2 : -INFINITY;
+            for (int v = 0; v < 4; ++v) sl[pipe][4 * lg + v][key] = ok ? Sv[v] * scale_log2 : -INFINITY;
         }
         __syncthreads();
 
-        // 3) online softmax (base 2) for head li over keys 8lg + 32ks + i
-        float p[16];
-        float mx = -INFINITY;
+        if (active) {
+            // 3) online softmax (base 2) for head li over keys 8lg + 32ks + i
+            float p[16];
+            float mx = -INFINITY;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                p[8 * ks + i] = sl[li][8 * lg + 32 * ks + i];
-                mx = fmaxf(mx, p[8 * ks + i]);
+                for (int i = 0; i < 8; ++i) {
+                    p[8 * ks + i] = sl[pipe][li][8 * lg + 32 * ks + i];
+                    mx = fmaxf(mx, p[8 * ks + i]);
+                }
+            mx = xor_max<16>(mx);
+            mx = xor_max<32>(mx);
+            const float m_new = fmaxf(m_run, mx);
+            float alpha;
+            // each weight as the sum of two bf16 values (hi + lo), so that the P V
+            // product carries about 16 significant bits of it; a single bf16 weight
+            // (8 bits) costs up to ~3e-3 of absolute output error when a handful of
+            // keys carry the softmax
+            v8bf P[2], Plo[2];
+            float rs = 0.0f, rs32 = 0.0f;
+            if (m_new == -INFINITY) {  // nothing valid yet
+                alpha = 1.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) p[i] = 0.0f;
+            } else {
+                // arguments are <= 0 (or -inf): the plain hardware exp2, whose
+                // flush of results below 2^-126 to zero is immaterial here
+                alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // m_run = -inf -> 0
+#pragma unroll
+                for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(p[i] - m_new);
             }
-        mx = xor_max<16>(mx);
-        mx = xor_max<32>(mx);
-        const float m_new = fmaxf(m_run, mx);
-        float alpha;
-        // each weight as the sum of two bf16 values (hi + lo), so that the P V
-        // product carries about 16 significant bits of it; a single bf16 weight
-        // (8 bits) costs up to ~3e-3 of absolute output error when a handful of
-        // keys carry the softmax
-        v8bf P[2], Plo[2];
-        float rs = 0.0f, rs32 = 0.0f;
-        if (m_new == -INFINITY) {  // nothing valid yet
-            alpha = 1.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) p[i] = 0.0f;
-        } else {
-            alpha = exp2f(m_run - m_new);  // m_run = -inf -> 0
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) p[i] = exp2f(p[i] - m_new);
+                for (int i = 0; i < 8; ++i) {
+                    const __bf16 pb = (__bf16)p[8 * ks + i];
+                    const __bf16 pl = (__bf16)(p[8 * ks + i] - (float)pb);
+                    P[ks][i] = pb;
+                    Plo[ks][i] = pl;
+                    rs += (float)pb + (float)pl;  // normalise with the weights actually used
+                    rs32 += p[8 * ks + i];
+                }
+            rs = xor_sum<16>(rs);
+            rs = xor_sum<32>(rs);
+            rs32 = xor_sum<16>(rs32);
+            rs32 = xor_sum<32>(rs32);
+            l_run = l_run * alpha + rs;
+            l_lse = l_lse * alpha + rs32;
+            m_run = m_new;
+            // O rows are heads 4lg + v: fetch their alpha from lane (4lg + v)
+            float av[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * lg + v);
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) O[nt][v] *= av[v];
+
+            // 4) O += P V for channels 128*wave + 16nt + li
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const int n0 = 128 * wave + 16 * nt;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int kb = 8 * lg + 32 * ks;
+                    const uint16_t* a0 = klp + (kb + (li >> 2)) * LROW + n0 + 4 * (li & 3);
+                    const uint16_t* a1 = klp + (kb + 4 + (li >> 2)) * LROW + n0 + 4 * (li & 3);
+                    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(a0));
+                    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(a1));
+                    const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    const v8bf vb = __builtin_bit_cast(v8bf, both);
+                    O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P[ks], vb, O[nt], 0, 0, 0);
+                    O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Plo[ks], vb, O[nt], 0, 0, 0);
+                }
+            }
         }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const __bf16 pb = (__bf16)p[8 * ks + i];
-                const __bf16 pl = (__bf16)(p[8 * ks + i] - (float)pb);
-                P[ks][i] = pb;
-                Plo[ks][i] = pl;
-                rs += (float)pb + (float)pl;  // normalise with the weights actually used
-                rs32 += p[8 * ks + i];
-            }
-        rs = xor_sum<16>(rs);
-        rs = xor_sum<32>(rs);
-        rs32 = xor_sum<16>(rs32);
-        rs32 = xor_sum<32>(rs32);
-        l_run = l_run * alpha + rs;
-        l_lse = l_lse * alpha + rs32;
-        m_run = m_new;
-        // O rows are heads 4lg + v: fetch their alpha from lane (4lg + v)
-        float av[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * lg + v);
+        __syncthreads();
+    }
+
+    // merge the pipes: pipe 1 leaves its state in LDS (its key buffer), pipe 0
+    // combines: with M = max(m0, m1) and a_g = 2^(m_g - M), O = a0 O0 + a1 O1
+    float* ob = reinterpret_cast<float*>(kl[1]);  // 16 x 512 floats
+    if (pipe == 1) {
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) O[nt][v] *= av[v];
-
-        // 4) O += P V for channels 128*wave + 16nt + li
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const int n0 = 128 * wave + 16 * nt;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int kb = 8 * lg + 32 * ks;
-                const uint16_t* a0 = kl + (kb + (li >> 2)) * LROW + n0 + 4 * (li & 3);
-                const uint16_t* a1 = kl + (kb + 4 + (li >> 2)) * LROW + n0 + 4 * (li & 3);
-                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(a0));
-                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(a1));
-                const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                const v8bf vb = __builtin_bit_cast(v8bf, both);
-                O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P[ks], vb, O[nt], 0, 0, 0);
-                O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Plo[ks], vb, O[nt], 0, 0, 0);
-            }
+            for (int v = 0; v < 4; ++v) ob[(4 * lg + v) * 512 + 128 * wave + 16 * nt + li] = O[nt][v];
+        if (wave == 0 && lane < 16) {
+            mls[lane][0] = m_run;
+            mls[lane][1] = l_run;
+            mls[lane][2] = l_lse;
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    if (pipe == 1) return;
+    {
+        const float m1 = mls[li][0];
+        const float M = fmaxf(m_run, m1);
+        const float a0 = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+        const float a1 = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+        l_run = a0 * l_run + a1 * mls[li][1];
+        l_lse = a0 * l_lse + a1 * mls[li][2];
+        m_run = M;
+        float b0[4], b1[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            b0[v] = __shfl(a0, 4 * lg + v);
+            b1[v] = __shfl(a1, 4 * lg + v);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                O[nt][v] = b0[v] * O[nt][v] + b1[v] * ob[(4 * lg + v) * 512 + 128 * wave + 16 * nt + li];
     }
 
     if (S > 1) {
@@ -425,7 +510,7 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
     const int rows8 = (a.g.total_q + 7) / 8 * 8;
     const unsigned nblk = (unsigned)rows8 * (unsigned)n_hg * (unsigned)S;
     float* part = S > 1 ? (float*)a.ws : nullptr;
-    hipLaunchKernelGGL(k_sparse_attn, dim3(nblk), dim3(256), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, a.swa,
+    hipLaunchKernelGGL(k_sparse_attn, dim3(nblk), dim3(512), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, a.swa,
                        a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,
                        a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q, n_hg, S,
                        part);

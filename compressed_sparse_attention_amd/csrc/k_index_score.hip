@@ -142,8 +142,7 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     __shared__ uint32_t hl[HIST ? TQ * kHistBins / 2 : 1];
     __shared__ __attribute__((aligned(16))) float sl[LOCAL ? TQ : 1][LOCAL ? chunk : 1];  // the chunk's scores per row
     __shared__ uint8_t ekl[chunk];                           // the chunk's indexer K scales
-    __shared__ uint32_t wtot[4], found[2];
-    __shared__ uint16_t pos16[LOCAL ? chunk : 1];  // a row's candidate offsets in the chunk
+    __shared__ uint32_t wtot[4], found[4];
     const int b = blockIdx.y;
     const int64_t e0 = entry_off[b];
     const int64_t n = entry_off[b + 1] - e0;
@@ -278,10 +277,23 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
             const int64_t nv64 = vis[t] - c0;
             const int nv = nv64 <= 0 ? 0 : (nv64 < c1 - c0 ? (int)nv64 : (int)(c1 - c0));
             const uint32_t kk = (uint32_t)(nv < lo.K ? nv : lo.K);
-            const uint32_t bstar = threshold_bin(PackedBins{hl + t * (kHistBins / 2)}, kk, wtot, found);
+            // with the chunks' bounds: the row's F chunks whose positions are
+            // all visible each hold m = ceil(K / F) positions at or above the
+            // bin of their m-th largest score, so the smallest of these F bins
+            // is at or below the bin of the row's K-th largest score, and the
+            // Top-K pass only looks at list entries from there up
+            uint32_t m = 0;
+            if (lo.lbins && nv == chunk) {
+                const int64_t n_full = vis[t] / chunk;
+                m = (uint32_t)(((int64_t)lo.K + n_full - 1) / n_full);
+            }
+            uint32_t bm;
+            const uint32_t bstar = threshold_bin2(PackedBins{hl + t * (kHistBins / 2)}, kk, m, wtot, found, &bm);
+            if (m && tid == 0) lo.lbins[(int64_t)row * lo.max_chunks + blockIdx.x] = bm;
             // the chunk's candidates in position order: thread tid owns positions
             // [PER tid, PER tid + PER) of the chunk; one block-wide scan of the
-            // per-thread counts places every thread's run in the list
+            // per-thread counts places every thread's run in the list, which
+            // each thread then writes from its registers
             constexpr int PER = chunk / 256;
             float v[PER];
 #pragma unroll
@@ -299,16 +311,10 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
             const uint32_t mine = (uint32_t)__popc(take);
             uint32_t off = block_scan_256(mine, wtot) - mine;
             const uint32_t base = wtot[0] + wtot[1] + wtot[2] + wtot[3];
-            // the list through LDS (chunk offsets), then written out coalesced
+            uint64_t* lr = lo.lists + ((int64_t)row * lo.max_chunks + blockIdx.x) * chunk;
 #pragma unroll
             for (int j = 0; j < PER; ++j)
-                if ((take >> j) & 1u) pos16[off++] = (uint16_t)(PER * tid + j);
-            __syncthreads();
-            uint64_t* lr = lo.lists + ((int64_t)row * lo.max_chunks + blockIdx.x) * chunk;
-            for (uint32_t i = tid; i < base; i += 256) {
-                const uint32_t pl = pos16[i];
-                lr[i] = composite(score_key(sl[t][pl]), (uint32_t)(c0 + pl));
-            }
+                if ((take >> j) & 1u) lr[off++] = composite(score_key(v[j]), (uint32_t)(c0 + PER * tid + j));
             if (tid == 0) lo.counts[(int64_t)row * lo.max_chunks + blockIdx.x] = base;
             if (lo.bscores) {  // block maxima over the visible positions of the chunk's blocks
                 const int64_t nb = (vis[t] + lo.block - 1) / lo.block;

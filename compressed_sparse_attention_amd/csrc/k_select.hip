@@ -562,101 +562,286 @@ __device__ inline uint32_t block_scan_1024(uint32_t v, uint32_t* wsum, uint32_t*
 }
 
 // The whole selection of a row from a decode scan's per-chunk lists, in one
-// workgroup of 1024 threads per row, for rows of a few chunks (the launcher
-// bounds max_chunks * chunk by kFusedEntries).  The histogram of the row's
-// Top-K threshold search is built here from the lists themselves: a chunk's
-// list holds exactly its visible positions at or above the chunk's threshold
-// bin, and the row's threshold bin B lies at or above the threshold of every
-// chunk with K visible positions (a chunk with fewer lists all its
-// positions), so the lists hold every position of the row at or above B, and
+// workgroup of 1024 threads per row and without a histogram from the scan.
+// The histogram of the row's threshold search is built from the lists: a
+// chunk's list holds exactly its visible positions at or above the chunk's
+// threshold bin, and the row's threshold bin B lies at or above the threshold
+// of every chunk with K visible positions (a chunk with fewer lists all its
+// positions), so the lists hold every position of the row at or above B and
 // their histogram has the row's exact counts from B up, which is all the
-// search reads.  Then the entries at or above B are compacted into LDS in
-// concatenation order (chunk order, i.e. position order), the threshold bin's
-// keys are radix-selected from bit 51 down, and the winners are written in
-// that same order.  Each thread holds up to kFusedPer consecutive entries of
-// the concatenation in registers.
-constexpr int kFusedEntries = kFusedTopkEntries;
-constexpr int kFusedPer = kFusedEntries / 1024;
+// search reads.
+//
+// The lists are read as their concatenation (chunk order = position order).
+// When they hold at most kListWindow entries, thread t keeps entries t,
+// t + 1024, ... in registers and they are read once; otherwise every step
+// streams them from memory again, chunk by chunk.
+//   1. B in two 6-bit digits (bin = 64 d1 + d2), each counted into 32 copies
+//      of a 64-entry LDS histogram (lane l adds to copy l % 32: the entries
+//      crowd into a few bins and same-address LDS atomics serialise);
+//   2. the entries at or above B, compacted into LDS in order (or, past
+//      kCandCap of them, left in the lists and filtered at every later step);
+//   3. radix select of the threshold bin's keys from bit 51 down (the bins
+//      above B all win);
+//   4. the winners, written in order.
+constexpr int kListPer = 28;                    // list entries per thread held in registers
+constexpr int kListWindow = 1024 * kListPer;    // 28,672 entries
+constexpr int kCandPer = kCandCap / 1024;       // LDS candidates per thread in step 4
 
-__global__ __launch_bounds__(1024) void k_topk_local(const uint64_t* __restrict__ lists,
-                                                     const uint32_t* __restrict__ counts, int max_chunks, int chunk,
+__global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict__ lists,
+                                                     const uint32_t* __restrict__ counts,
+                                                     const uint32_t* __restrict__ lbins, int max_chunks, int chunk,
                                                      RowSrc rs, int K, int32_t* __restrict__ idx) {
-    __shared__ uint64_t c[kFusedEntries];
+    __shared__ uint64_t c[kCandCap];
+    __shared__ uint32_t bm[kFusedTopkEntries / 32];  // winners by position
+    __shared__ uint32_t nsurv, lb_sh;
     __shared__ uint32_t hcopy[64 * 32];
     __shared__ uint32_t dcount[64];
-    __shared__ uint32_t roff[kFusedEntries / 64 + 1];
+    __shared__ uint32_t roff[kListChunks + 1];
+    __shared__ uint32_t pcnt[16 * kListPer];
     __shared__ uint32_t hist256[256], scan256[256];
     __shared__ RadixState st;
     __shared__ int found;
     __shared__ uint32_t wsum[16];
-    __shared__ uint32_t base, thr[2];
+    __shared__ uint32_t thr[2];
     const int row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the lists' lengths and bounds are read with the row's size (every
+    // chunk of the row is in bounds; those past the visible range are unused)
+    const uint32_t cnt_raw = tid < max_chunks ? counts[(int64_t)row * max_chunks + tid] : 0u;
+    const uint32_t lb_raw = (lbins && tid < max_chunks) ? lbins[(int64_t)row * max_chunks + tid] : 0xFFFFFFFFu;
     const int64_t n = row_n(rs, row);
     const uint32_t kk = (uint32_t)(n < K ? n : K);
     int32_t* out = idx + (int64_t)row * K;
     for (int i = tid + (int)kk; i < K; i += 1024) out[i] = -1;
     if (kk == 0) return;
-    const int n_ch = (int)((n + chunk - 1) / chunk);  // <= max_chunks <= 1024
+    const int n_ch = (int)((n + chunk - 1) / chunk);  // <= max_chunks <= kListChunks (launcher)
     const uint64_t* lrow = lists + (int64_t)row * max_chunks * chunk;
+    const int n_full = (int)(n / chunk);  // chunks whose positions are all visible
     if (tid == 0) {
         thr[0] = 0;
         thr[1] = 0;
+        nsurv = 0;
+        lb_sh = 0xFFFFFFFFu;
     }
-    // run offsets: exclusive prefix sum of the lists' lengths
+    for (int i = tid; i < kFusedTopkEntries / 32; i += 1024) bm[i] = 0;
+    __syncthreads();  // lb_sh is set before any thread lowers it
+    // run offsets: exclusive prefix sum of the lists' lengths; the lower
+    // bound LB of the row's threshold bin: the smallest of the full chunks'
+    // bounds (0 when there is no full chunk)
     {
-        const uint32_t v = tid < n_ch ? counts[(int64_t)row * max_chunks + tid] : 0u;
+        const uint32_t v = tid < n_ch ? cnt_raw : 0u;
+        if (tid < n_full) atomicMin(&lb_sh, lb_raw);
         uint32_t tot;
         const uint32_t incl = block_scan_1024(v, wsum, &tot);
         if (tid < n_ch) roff[tid] = incl - v;
         if (tid == 0) roff[n_ch] = tot;
         __syncthreads();
     }
-    const uint32_t total = roff[n_ch];  // <= n_ch * chunk <= kFusedEntries
-    const uint32_t P = (total + 1023) / 1024;
-    const uint32_t e_lo = P * (uint32_t)tid;
+    const uint32_t total = roff[n_ch];
+    const uint32_t LB = (lbins && n_full > 0) ? lb_sh : 0u;
+    const bool in_regs = total <= (uint32_t)kListWindow;
 
-    // this thread's entries [e_lo, e_lo + P): first every entry's place in
-    // the lists (no load is in flight while this walks: a loop between the
-    // loads below would make each load wait for the previous ones), then all
-    // the loads at once
-    uint64_t key[kFusedPer];
-    {
+    // in registers: thread t holds entries u * 1024 + t (u < P), so that every
+    // load instruction of a wave reads 512 consecutive bytes of a list
+    uint64_t key[kListPer];
+    const uint32_t P = in_regs ? (total + 1023) / 1024 : 0u;
+    auto valid = [&](int u) { return (uint32_t)u < P && (uint32_t)u * 1024u + (uint32_t)tid < total; };
+    if (in_regs) {
+        // every entry's place in the lists first (no load is in flight while
+        // this walks), as a 32-bit byte offset (a row's lists span at most
+        // kListChunks * 4096 * 8 bytes), then all the loads at once
         int ch = 0;
-        if (e_lo < total) {
-            int lo = 0, hi = n_ch;  // roff[lo] <= e_lo < roff[hi]
+        if ((uint32_t)tid < total) {
+            int lo = 0, hi = n_ch;  // roff[lo] <= tid < roff[hi]
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
-                if (roff[mid] <= e_lo) lo = mid; else hi = mid;
+                if (roff[mid] <= (uint32_t)tid) lo = mid; else hi = mid;
             }
             ch = lo;
         }
         uint32_t bound = roff[ch + 1], start = roff[ch];
-        uint32_t at[kFusedPer];
+        uint32_t at[kListPer];
 #pragma unroll
-        for (int u = 0; u < kFusedPer; ++u) {
-            const uint32_t e = e_lo + (uint32_t)u;
+        for (int u = 0; u < kListPer; ++u) {
+            const uint32_t e = (uint32_t)u * 1024u + (uint32_t)tid;
             at[u] = 0;
-            if ((uint32_t)u < P && e < total) {
+            if (valid(u)) {
                 while (e >= bound) {
                     ++ch;
                     start = bound;
                     bound = roff[ch + 1];
                 }
-                at[u] = (uint32_t)ch * (uint32_t)chunk + (e - start);
+                at[u] = 8u * ((uint32_t)ch * (uint32_t)chunk + (e - start));
             }
         }
+        const char* lb = reinterpret_cast<const char*>(lrow);
 #pragma unroll
-        for (int u = 0; u < kFusedPer; ++u)
-            key[u] = ((uint32_t)u < P && e_lo + (uint32_t)u < total) ? lrow[at[u]] : 0ull;
+        for (int u = 0; u < kListPer; ++u) key[u] = valid(u) ? *reinterpret_cast<const uint64_t*>(lb + at[u]) : 0ull;
+    }
+    // put(rank, u) for the register entries u whose bit is set in `take`,
+    // ranked in list order (u, then wave, then lane): the count of every
+    // (u, wave) pair, one block-wide scan over them, then the rank of each
+    // entry from its pair's offset and the lanes below it.  Returns the total.
+    auto rank_in_regs = [&](uint32_t take, auto&& put) {
+#pragma unroll
+        for (int u = 0; u < kListPer; ++u)
+            if ((uint32_t)u < P) {
+                const uint64_t m = __ballot((take >> u) & 1u);
+                if (lane == 0) pcnt[16 * u + wave] = (uint32_t)__popcll(m);
+            }
+        __syncthreads();
+        const uint32_t v = (uint32_t)tid < 16u * P ? pcnt[tid] : 0u;
+        uint32_t tot;
+        const uint32_t incl = block_scan_1024(v, wsum, &tot);
+        if ((uint32_t)tid < 16u * P) pcnt[tid] = incl - v;
+        __syncthreads();
+        const uint64_t below = (1ull << lane) - 1;
+#pragma unroll
+        for (int u = 0; u < kListPer; ++u)
+            if ((uint32_t)u < P) {
+                const uint64_t m = __ballot((take >> u) & 1u);
+                if ((take >> u) & 1u) put(pcnt[16 * u + wave] + (uint32_t)__popcll(m & below), u);
+            }
+        __syncthreads();  // pcnt is rewritten by the next call
+        return tot;
+    };
+    // fn(key) for every list entry, in no particular order
+    auto for_each_entry = [&](auto&& fn) {
+        if (in_regs) {
+#pragma unroll
+            for (int u = 0; u < kListPer; ++u)
+                if (valid(u)) fn(key[u]);
+        } else {
+            for (int ch = 0; ch < n_ch; ++ch) {
+                const uint32_t cn = roff[ch + 1] - roff[ch];
+                for (uint32_t j = tid; j < cn; j += 1024) fn(lrow[(int64_t)ch * chunk + j]);
+            }
+        }
+    };
+    // put(rank, key) for the entries with pick(key), ranked in list order,
+    // streamed from memory; returns how many there are
+    auto stream_ordered = [&](auto&& pick, auto&& put) {
+        uint32_t base = 0;
+        for (int ch = 0; ch < n_ch; ++ch) {
+            const uint32_t cn = roff[ch + 1] - roff[ch];
+            for (uint32_t j0 = 0; j0 < cn; j0 += 1024) {
+                const uint32_t j = j0 + (uint32_t)tid;
+                const uint64_t x = j < cn ? lrow[(int64_t)ch * chunk + j] : 0ull;
+                const bool hit = j < cn && pick(x);
+                const uint64_t m = __ballot(hit);
+                if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
+                __syncthreads();
+                uint32_t off = base, tot = 0;
+#pragma unroll
+                for (int w2 = 0; w2 < 16; ++w2) {
+                    off += w2 < wave ? wsum[w2] : 0u;
+                    tot += wsum[w2];
+                }
+                if (hit) put(off + (uint32_t)__popcll(m & ((1ull << lane) - 1)), x);
+                base += tot;
+                __syncthreads();  // wsum is rewritten by the next step
+            }
+        }
+        return base;
+    };
+
+    // 0. with the chunks' bound: the list entries at or above LB (a few times
+    // K for distinct scores) go to LDS in any order, the K winners among
+    // them are radix-selected on key64 from the top, marked in a bitmap by
+    // position and written in position order.  More than kCandCap of them
+    // (heavy ties) falls through to the search below.
+    if (lbins) {
+        if (in_regs) {
+            uint32_t mask = 0;
+#pragma unroll
+            for (int u = 0; u < kListPer; ++u) mask |= (uint32_t)(valid(u) && (uint32_t)(key[u] >> 51) >= LB) << u;
+            const uint32_t cnt = (uint32_t)__popc(mask);
+            uint32_t incl = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t u2 = __shfl_up(incl, o);
+                if (lane >= o) incl += u2;
+            }
+            uint32_t base = 0;
+            if (lane == 63 && incl) base = atomicAdd(&nsurv, incl);
+            uint32_t off = __shfl(base, 63) + incl - cnt;
+#pragma unroll
+            for (int u = 0; u < kListPer; ++u)
+                if ((mask >> u) & 1u) {
+                    if (off < (uint32_t)kCandCap) c[off] = key[u];
+                    ++off;
+                }
+        } else {
+            for_each_entry([&](uint64_t x) {
+                if ((uint32_t)(x >> 51) >= LB) {
+                    const uint32_t r = atomicAdd(&nsurv, 1u);
+                    if (r < (uint32_t)kCandCap) c[r] = x;
+                }
+            });
+        }
+        __syncthreads();
+        const uint32_t n_surv = nsurv;
+        if (n_surv <= (uint32_t)kCandCap) {
+            if (tid == 0) {
+                st.prefix = 0;
+                st.shift = 64;
+                st.need = kk;
+                st.done = 0;
+            }
+            __syncthreads();
+            while (!st.done) {
+                if (tid < 256) hist256[tid] = 0;
+                __syncthreads();
+                const int sh = st.shift;
+                const int w = digit_bits(sh);
+                const uint64_t pf = st.prefix;
+                for (uint32_t e = tid; e < n_surv; e += 1024) {
+                    const uint64_t x = c[e];
+                    if (sh >= 64 || (x >> sh) == pf)
+                        atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
+                }
+                __syncthreads();
+                radix_step(hist256, scan256, &st, &found);
+            }
+            const int sh = st.shift;  // < 64: at least one digit was fixed
+            const uint64_t pf = st.prefix;
+            for (uint32_t e = tid; e < n_surv; e += 1024) {
+                const uint64_t x = c[e];
+                if ((x >> sh) >= pf) {
+                    const uint32_t pos = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu);
+                    atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+                }
+            }
+            __syncthreads();
+            // positions in order: thread t owns bitmap words [WPT t, WPT (t + 1))
+            constexpr int kMaxWpt = kFusedTopkEntries / 32 / 1024;
+            const int nwords = (int)((n + 31) / 32);
+            const int WPT = (nwords + 1023) / 1024;
+            uint32_t wd[kMaxWpt];
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int i = 0; i < kMaxWpt; ++i) {
+                const int wi = WPT * tid + i;
+                wd[i] = (i < WPT && wi < nwords) ? bm[wi] : 0u;
+                cnt += (uint32_t)__popc(wd[i]);
+            }
+            uint32_t tot;
+            uint32_t r = block_scan_1024(cnt, wsum, &tot) - cnt;
+#pragma unroll
+            for (int i = 0; i < kMaxWpt; ++i) {
+                uint32_t x = wd[i];
+                while (x) {
+                    const int bit = __ffs(x) - 1;
+                    if (r < kk) out[r] = 32 * (WPT * tid + i) + bit;
+                    ++r;
+                    x &= x - 1;
+                }
+            }
+            return;
+        }
     }
 
-    // the threshold bin B, in two 6-bit digits (bin = 64 d1 + d2).  Each level
-    // counts the digits of the entries that match the digits found so far
-    // into 32 copies of a 64-entry histogram (lane l adds to copy l % 32),
-    // because the entries crowd into a few bins and same-address LDS atomics
-    // serialise; then the copies are summed and the digit holding the
-    // need-th largest entry is found from the top.
+    // 1. the threshold bin B
     uint32_t B = 0, above = 0;
     {
         uint32_t need = kk;
@@ -665,12 +850,10 @@ __global__ __launch_bounds__(1024) void k_topk_local(const uint64_t* __restrict_
             for (int i = tid; i < 64 * 32; i += 1024) hcopy[i] = 0;
             __syncthreads();
             uint32_t* hc = hcopy + (lane & 31);
-#pragma unroll
-            for (int u = 0; u < kFusedPer; ++u) {
-                const uint32_t bin = (uint32_t)(key[u] >> 51);
-                const bool in = (uint32_t)u < P && e_lo + (uint32_t)u < total && (level == 0 || (bin >> 6) == B);
-                if (in) atomicAdd(&hc[32 * (level == 0 ? bin >> 6 : bin & 63u)], 1u);
-            }
+            for_each_entry([&](uint64_t x) {
+                const uint32_t bin = (uint32_t)(x >> 51);
+                if (level == 0 || (bin >> 6) == B) atomicAdd(&hc[32 * (level == 0 ? bin >> 6 : bin & 63u)], 1u);
+            });
             __syncthreads();
             {  // digit d = tid / 16 sums copies 2 (tid % 16), +1; 16 lanes reduce
                 const int d = tid >> 4, part = tid & 15;
@@ -702,38 +885,44 @@ __global__ __launch_bounds__(1024) void k_topk_local(const uint64_t* __restrict_
         }
     }
 
-    // the entries at or above B, compacted into LDS in order
+    // 2. the entries at or above B, in order, into LDS while they fit
     uint32_t n_cand;
-    {
+    if (in_regs) {
         uint32_t take = 0;
 #pragma unroll
-        for (int u = 0; u < kFusedPer; ++u)
-            take |= (uint32_t)((uint32_t)u < P && e_lo + (uint32_t)u < total && (uint32_t)(key[u] >> 51) >= B) << u;
-        const uint32_t mine = (uint32_t)__popc(take);
-        uint32_t off = block_scan_1024(mine, wsum, &n_cand) - mine;
-#pragma unroll
-        for (int u = 0; u < kFusedPer; ++u)
-            if ((take >> u) & 1u) c[off++] = key[u];
+        for (int u = 0; u < kListPer; ++u) take |= (uint32_t)(valid(u) && (uint32_t)(key[u] >> 51) >= B) << u;
+        n_cand = rank_in_regs(take, [&](uint32_t r, int u) {
+            if (r < (uint32_t)kCandCap) c[r] = key[u];
+        });
+    } else {
+        n_cand = stream_ordered([&](uint64_t x) { return (uint32_t)(x >> 51) >= B; },
+                                [&](uint32_t r, uint64_t x) {
+                                    if (r < (uint32_t)kCandCap) c[r] = x;
+                                });
     }
+    const bool in_lds = n_cand <= (uint32_t)kCandCap;
     if (tid == 0) {
         st.prefix = B;
         st.shift = 51;
         st.need = kk - above;
         st.done = 0;
-        base = 0;
     }
     __syncthreads();
 
-    // radix select among the threshold bin's keys (the bins above all win)
+    // 3. radix select among the threshold bin's keys
     while (!st.done) {
         if (tid < 256) hist256[tid] = 0;
         __syncthreads();
         const int sh = st.shift;
         const int w = digit_bits(sh);
         const uint64_t pf = st.prefix;
-        for (uint32_t e = tid; e < n_cand; e += 1024) {
-            const uint64_t x = c[e];
+        auto count = [&](uint64_t x) {
             if ((x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
+        };
+        if (in_lds) {
+            for (uint32_t e = tid; e < n_cand; e += 1024) count(c[e]);
+        } else {
+            for_each_entry(count);  // entries below B never match the prefix
         }
         __syncthreads();
         radix_step(hist256, scan256, &st, &found);
@@ -741,27 +930,39 @@ __global__ __launch_bounds__(1024) void k_topk_local(const uint64_t* __restrict_
     const int sh = st.shift;
     const uint64_t pf = st.prefix;
 
-    // winners (key64 >= prefix << shift) in candidate order = position order
-    for (uint32_t e0 = 0; e0 < n_cand; e0 += 1024) {
-        const uint32_t e = e0 + tid;
-        const uint64_t x = e < n_cand ? c[e] : 0ull;
-        const bool win = e < n_cand && (x >> sh) >= pf;
-        const uint64_t m = __ballot(win);
-        if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
-        __syncthreads();
-        uint32_t o = base;
-        for (int w2 = 0; w2 < wave; ++w2) o += wsum[w2];
-        if (win) {
-            const uint32_t p = o + (uint32_t)__popcll(m & ((1ull << lane) - 1));
-            if (p < kk) out[p] = (int32_t)(0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu));
+    // 4. winners (key64 >= prefix << shift) in position order: per thread its
+    // count, one block-wide scan, and each thread writes its run
+    auto slot_of = [](uint64_t x) { return (int32_t)(0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu)); };
+    if (in_lds) {
+        const uint32_t P2 = (n_cand + 1023) / 1024;  // <= kCandPer
+        const uint32_t c_lo = P2 * (uint32_t)tid;
+        uint32_t win = 0;
+#pragma unroll
+        for (int u = 0; u < kCandPer; ++u) {
+            const uint32_t e = c_lo + (uint32_t)u;
+            win |= (uint32_t)((uint32_t)u < P2 && e < n_cand && (c[e] >> sh) >= pf) << u;
         }
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t t2 = 0;
-            for (int w2 = 0; w2 < 16; ++w2) t2 += wsum[w2];
-            base += t2;
-        }
-        __syncthreads();
+        const uint32_t mine = (uint32_t)__popc(win);
+        uint32_t tot;
+        uint32_t p = block_scan_1024(mine, wsum, &tot) - mine;
+#pragma unroll
+        for (int u = 0; u < kCandPer; ++u)
+            if ((win >> u) & 1u) {
+                if (p < kk) out[p] = slot_of(c[c_lo + u]);
+                ++p;
+            }
+    } else if (in_regs) {
+        uint32_t win = 0;
+#pragma unroll
+        for (int u = 0; u < kListPer; ++u) win |= (uint32_t)(valid(u) && (key[u] >> sh) >= pf) << u;
+        rank_in_regs(win, [&](uint32_t r, int u) {
+            if (r < kk) out[r] = slot_of(key[u]);
+        });
+    } else {
+        stream_ordered([&](uint64_t x) { return (x >> sh) >= pf; },
+                       [&](uint32_t r, uint64_t x) {
+                           if (r < kk) out[r] = slot_of(x);
+                       });
     }
 }
 
@@ -890,10 +1091,11 @@ hipError_t launch_topk_local(const csa2_batch* b, const Geometry& g, const Local
 }
 
 hipError_t launch_topk_fused(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, hipStream_t s) {
-    if ((int64_t)lo.max_chunks * lo.chunk > kFusedEntries) return hipErrorInvalidValue;
+    if (lo.max_chunks > kListChunks || (int64_t)lo.max_chunks * lo.chunk > kFusedTopkEntries)
+        return hipErrorInvalidValue;
     RowSrc rs{b->d_entry_off, b->d_row_seq, b->d_q_pos, b->ratio, nullptr, 0, 1, g.max_entries};
-    hipLaunchKernelGGL(k_topk_local, dim3(g.total_q), dim3(1024), 0, s, (const uint64_t*)lo.lists,
-                       (const uint32_t*)lo.counts, lo.max_chunks, lo.chunk, rs, lo.K, idx);
+    hipLaunchKernelGGL(k_topk_lists, dim3(g.total_q), dim3(1024), 0, s, (const uint64_t*)lo.lists,
+                       (const uint32_t*)lo.counts, (const uint32_t*)lo.lbins, lo.max_chunks, lo.chunk, rs, lo.K, idx);
     return hipGetLastError();
 }
 

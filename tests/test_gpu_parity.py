@@ -262,16 +262,20 @@ TIE_CASES = {
     # one head: few distinct scores, long runs of ties at the thresholds
     "one_head_t1": dict(lens=[3, 700, 9000, 20000], T=1, heads=1),
     "one_head_t4": dict(lens=[5, 3000, 20000], T=4, heads=1),
-    # rows of at most 16,384 list entries take the one-kernel selection over
-    # the scan's lists: every score tied at its fullest, few distinct scores
-    # with four rows per sequence, and distinct scores
+    # rows of at most 262,144 entries take the one-kernel selection over the
+    # scan's lists: lists held in registers (up to 28,672 entries) with every
+    # score tied, few distinct scores with four rows per sequence, distinct
+    # scores; lists streamed from memory (more than 28,672 entries) with their
+    # candidates in LDS, and with every score tied (candidates overflow LDS)
     "all_equal_fused_t1": dict(lens=[3, 700, 9000, 16384], T=1, heads=0),
     "one_head_fused_t4": dict(lens=[5, 3000, 8192], T=4, heads=1),
     "fused_h64": dict(lens=[16384, 1000], T=1, heads=64),
-    # longer rows: the lists are filtered by many workgroups first, from the
-    # scan's histograms (heavy ties, and a row of 74 chunks)
+    "fused_stream": dict(lens=[262144, 3000], T=1, heads=64),
     "all_equal_long": dict(lens=[40000, 100], T=1, heads=0),
+    # longer rows: the lists are filtered by many workgroups first, from the
+    # scan's histograms (a row of 74 chunks, and heavy ties)
     "split_topk": dict(lens=[300000, 5000], T=1, heads=64),
+    "all_equal_split": dict(lens=[270000, 100], T=1, heads=0),
 }
 
 
