@@ -14,6 +14,10 @@ Prints ONE JSON line with the contract fields plus:
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
   prefill_index the prefill indexer (8,192 E4M3 queries x 131,072 entries at
                 ratio 2, causal) in TFLOP/s of algorithmic FLOPs
+  workloads     the layer chain of the other four workloads (decode_c0; the
+                decoder chain of chain_c2 and ragged_c4 with block pool, Reindex
+                and Reuse layers; the prefill_c3 chunk): time per chain and its
+                algorithmic HBM bytes (decode) or FLOPs (prefill)
 """
 import argparse
 import json
@@ -41,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the layer-chain timings of the other four workloads")
     ap.add_argument("--workload", default="decode_c1",
                     choices=["decode_c1", "decode_c0", "chain_c2", "prefill_c3", "ragged_c4"],
                     help="decode_c1 (default) prints the full line; the others time their layer chain only")
@@ -49,7 +55,7 @@ def parse():
                          "512 MiB device copy that calibrates the byte counters")
     a = ap.parse_args()
     if a.profile_pass:
-        a.steps, a.warmup, a.no_cpu_baseline, a.no_prefill = 3, 1, True, True
+        a.steps, a.warmup, a.no_cpu_baseline, a.no_prefill, a.no_workloads = 3, 1, True, True, True
     return a
 
 
@@ -218,6 +224,11 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, wl, dw, C, run_chain)
 
+    if not args.no_workloads:
+        del dw, dw2, copies, calls, ws
+        torch.cuda.empty_cache()
+        result["workloads"] = bench_workloads(synth, C, torch, dev)
+
     print(json.dumps(result), flush=True)
 
 
@@ -246,6 +257,88 @@ def chain_only(args, synth, C, torch, dev):
            "value": round(n_layers * 1000.0 / ms, 2), "unit": "layer-steps/s", "rows": wl.total_q,
            "entries": wl.total_entries}
     print(json.dumps(res), flush=True)
+
+
+def chain_bytes(wl, outs, pool_pos, pool_count):
+    """Algorithmic HBM bytes of one decode step of a layer chain, from the
+    realised selections: the Full layer's scan (65 B per visible entry, read
+    once per sequence) and query/weights; each Reindex layer's gathered
+    indexer-K rows (the union of a sequence's pools, 65 B each); per layer and
+    row the gathered main-KV rows (272 B per selected entry), the SWA rows
+    (1,024 B), the main query, the output and the indices."""
+    import numpy as np
+
+    H, Hm, K, W = wl.H, wl.Hm, wl.K, wl.W
+    vis = np.minimum(wl.n_entries[wl.row_seq], (wl.q_pos.astype(np.int64) + 1) // wl.ratio)
+    seq_vis = np.zeros(wl.n_seq, np.int64)
+    np.maximum.at(seq_vis, wl.row_seq, vis)
+    n_swa = np.minimum(W, wl.q_pos.astype(np.int64) + 1)
+    qw = wl.total_q * H * (64 + 1 + 4)
+    total = 0
+    for L, o in zip(wl.layers, outs):
+        if L.mode == synth_mode("FULL"):
+            total += int(seq_vis.sum()) * 65 + qw
+        elif L.mode == synth_mode("REINDEX"):
+            pp, pc = pool_pos.cpu().numpy(), pool_count.cpu().numpy()
+            for b in range(wl.n_seq):
+                rows = np.nonzero(wl.row_seq == b)[0]
+                u = np.unique(np.concatenate([pp[r, :pc[r]] for r in rows])) if len(rows) else []
+                total += len(u) * 65
+            total += qw
+        n_sel = (o["idx"].cpu().numpy() >= 0).sum(axis=1) if L.mode != synth_mode("SWA_ONLY") else 0
+        total += int(np.sum(n_sel) * 272 + n_swa.sum() * 1024) + wl.total_q * (Hm * 512 * 6 + K * 4)
+    return total
+
+
+def synth_mode(name):
+    import synth
+
+    return getattr(synth, "MODE_" + name)
+
+
+def bench_workloads(synth, C, torch, dev):
+    """The layer chain of the other four workloads: one call = every layer of
+    one decode step (or of the prefill chunk) for the whole batch."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import DevWorkload, prepare_chain
+
+    res = {}
+    for name, reps in (("decode_c0", 20), ("chain_c2", 5), ("ragged_c4", 5), ("prefill_c3", 3)):
+        t0 = time.time()
+        wl = synth.config(name)
+        dw = DevWorkload(wl, dev)
+        call, outs, (pb, pp, pc) = prepare_chain(dw, want_idx=True, want_lse=False)
+        call()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            call()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        n_layers = len(wl.layers)
+        r = {"ms_per_chain": round(ms, 4), "layers": n_layers, "rows": wl.total_q,
+             "entries": wl.total_entries, "layer_steps_per_s": round(n_layers * 1000.0 / ms, 1)}
+        if name == "prefill_c3":
+            vis = np.minimum(wl.n_entries[0], (wl.q_pos.astype(np.int64) + 1) // wl.ratio)
+            idx_flops = 2.0 * float(vis.sum()) * wl.H * 128
+            n_swa = np.minimum(wl.W, wl.q_pos.astype(np.int64) + 1)
+            keys = sum(float((o["idx"].cpu().numpy() >= 0).sum()) + float(n_swa.sum()) for o in outs)
+            attn_flops = keys * wl.Hm * 512 * 4  # Q K^T and P V
+            r.update({"index_flops": idx_flops, "attn_flops": attn_flops,
+                      "tflops": round((idx_flops + attn_flops) / (ms * 1e-3) / 1e12, 1)})
+        else:
+            nb = chain_bytes(wl, outs, pp, pc)
+            gbs = nb / (ms * 1e-3) / 1e9
+            r.update({"algorithmic_bytes": nb, "hbm_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        log(f"[bench] {name}: {ms:.3f} ms per chain of {n_layers} layers ({time.time() - t0:.0f} s incl. inputs)")
+        res[name] = r
+        del dw, outs, call, pb, pp, pc, wl
+        torch.cuda.empty_cache()
+    return res
 
 
 def bench_prefill(args, C, synth, torch, dev):

@@ -409,9 +409,11 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                 }
             } else {
                 // the score kernel builds the Top-K histogram when it can (FP4 queries,
-                // at most 4 rows per sequence or a candidate list); the Top-K pass then
-                // starts from it.  A pool built from these scores needs its own pass.
-                const bool fused = L.q_fmt == CSA2_Q_FP4 && (on_pool || g.max_q_per_seq <= 4);
+                // at most 4 rows per sequence or a candidate list) and the rows are too
+                // long for the one-workgroup selection; the Top-K pass then starts
+                // from it.  A pool built from these scores needs its own pass.
+                const int64_t slots = on_pool ? (int64_t)pool_stride : g.max_entries;
+                const bool fused = L.q_fmt == CSA2_Q_FP4 && (on_pool || g.max_q_per_seq <= 4) && slots > kRowSelMax;
                 if (fused && (e = clear_topk_ws(topk_ws, g.total_q, true, stream)) != hipSuccess) return hip_fail(e);
                 ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, src->k_fp4, src->k_sc,
                                on_pool ? pp : nullptr, on_pool ? pool_stride : 0, on_pool ? pscores : scores,

@@ -274,6 +274,9 @@ struct TopkLaunch {
     void* ws;
     const uint32_t* hist;       // nullable: histogram of the scores made with them (skips the histogram pass)
 };
+// Rows of at most kRowSelMax slots are selected by one workgroup each, from
+// their scores alone (a histogram made with the scores is not used)
+constexpr int kRowSelMax = 16384;
 size_t topk_ws_bytes(int total_q);
 // zero the histogram and row state of a Top-K workspace (done by launch_topk
 // itself unless the caller filled the histogram beforehand)

@@ -77,25 +77,27 @@ __global__ __launch_bounds__(64) void k_gather_dequant(const uint8_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// sparse attention: one workgroup per (query row, group of 16 heads), two
+// sparse attention: one workgroup per (query row, group of 16 heads), NP
 // groups of 4 waves ("pipes").  Keys come in blocks of 64: first the SWA rows
 // of the window, then the selected entries (idx order); pipe g takes the
-// blocks blk0 + 2i + g of its part of the row, each pipe with its own LDS key
-// buffer and its own online-softmax state, so that every SIMD has two waves to
-// interleave.  Per block: dequantise into LDS (row-major bf16), S = Q K^T on
-// v_mfma_f32_16x16x32_bf16 (wave w: keys 16w..16w+15), online softmax in
-// fp32, O += P V (wave w: channels 128w..128w+127) with V read transposed by
-// ds_read_b64_tr_b16.  At the end the two pipes' (max, sums, O) are merged.
-// The loads of the first iteration (the SWA rows) are issued together with
-// the query and the index row; later blocks are fetched one iteration ahead.
+// blocks blk0 + NP i + g of its part of the row, each pipe with its own LDS
+// key buffer and its own online-softmax state.  Per block: dequantise into
+// LDS (row-major bf16), S = Q K^T on v_mfma_f32_16x16x32_bf16 (wave w: keys
+// 16w..16w+15), online softmax in fp32, O += P V (wave w: channels
+// 128w..128w+127) with V read transposed by ds_read_b64_tr_b16.  With two
+// pipes their (max, sums, O) are merged at the end.  The loads of the first
+// iteration (the SWA rows) are issued together with the query and the index
+// row; later blocks are fetched one iteration ahead.  One pipe keeps the LDS
+// of a workgroup at 73 KB, so that two workgroups share a CU; measured, that
+// beats two pipes in one workgroup except on the smallest grids.
 // ---------------------------------------------------------------------------
 constexpr int HG = 16;
 constexpr int KB = 64;
-constexpr int NPIPE = 2;
 constexpr int LROW = 512 + 8;  // LDS row stride of the staged keys in bf16 (16 B of padding)
 constexpr int SLROW = KB + 4;  // LDS row stride of the logits in floats
 
-__global__ __launch_bounds__(512) void k_sparse_attn(
+template <int NPIPE>
+__global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
     const int32_t* __restrict__ idx, int K, const uint16_t* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
     const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ replay_s, int W,
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(512) void k_sparse_attn(
     if (row >= total_q) return;
 
     const int tid = threadIdx.x;
-    const int pipe = __builtin_amdgcn_readfirstlane(tid >> 8);
+    const int pipe = NPIPE == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);
     const int pt = tid & 255;  // thread within the pipe
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wave within the pipe
@@ -137,10 +139,11 @@ __global__ __launch_bounds__(512) void k_sparse_attn(
         for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, ld16(qr + 32 * ks));
     }
     const int32_t* irow = idx + (int64_t)row * K;
-    int32_t ir[kMaxK / 512];
+    constexpr int NT = 256 * NPIPE;
+    int32_t ir[kMaxK / NT];
 #pragma unroll
-    for (int i = 0; i < kMaxK / 512; ++i) {
-        const int s = tid + 512 * i;
+    for (int i = 0; i < kMaxK / NT; ++i) {
+        const int s = tid + NT * i;
         ir[i] = s < K ? irow[s] : -1;
     }
     // keep the loads above ahead of the scalar loads below (they would
@@ -183,8 +186,8 @@ __global__ __launch_bounds__(512) void k_sparse_attn(
     {
         int last = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxK / 512; ++i) {
-            const int s = tid + 512 * i;
+        for (int i = 0; i < kMaxK / NT; ++i) {
+            const int s = tid + NT * i;
             if (s < K) {
                 const int32_t j = (ir[i] >= 0 && ir[i] < n_ent) ? ir[i] : -1;  // out-of-range entries read as empty
                 kidx[s] = j;
@@ -372,40 +375,42 @@ __global__ __launch_bounds__(512) void k_sparse_attn(
 
     // merge the pipes: pipe 1 leaves its state in LDS (its key buffer), pipe 0
     // combines: with M = max(m0, m1) and a_g = 2^(m_g - M), O = a0 O0 + a1 O1
-    float* ob = reinterpret_cast<float*>(kl[1]);  // 16 x 512 floats
-    if (pipe == 1) {
+    if constexpr (NPIPE == 2) {
+        float* ob = reinterpret_cast<float*>(kl[1]);  // 16 x 512 floats
+        if (pipe == 1) {
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+            for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) ob[(4 * lg + v) * 512 + 128 * wave + 16 * nt + li] = O[nt][v];
-        if (wave == 0 && lane < 16) {
-            mls[lane][0] = m_run;
-            mls[lane][1] = l_run;
-            mls[lane][2] = l_lse;
+                for (int v = 0; v < 4; ++v) ob[(4 * lg + v) * 512 + 128 * wave + 16 * nt + li] = O[nt][v];
+            if (wave == 0 && lane < 16) {
+                mls[lane][0] = m_run;
+                mls[lane][1] = l_run;
+                mls[lane][2] = l_lse;
+            }
         }
-    }
-    __syncthreads();
-    if (pipe == 1) return;
-    {
-        const float m1 = mls[li][0];
-        const float M = fmaxf(m_run, m1);
-        const float a0 = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
-        const float a1 = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
-        l_run = a0 * l_run + a1 * mls[li][1];
-        l_lse = a0 * l_lse + a1 * mls[li][2];
-        m_run = M;
-        float b0[4], b1[4];
+        __syncthreads();
+        if (pipe == 1) return;
+        {
+            const float m1 = mls[li][0];
+            const float M = fmaxf(m_run, m1);
+            const float a0 = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+            const float a1 = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+            l_run = a0 * l_run + a1 * mls[li][1];
+            l_lse = a0 * l_lse + a1 * mls[li][2];
+            m_run = M;
+            float b0[4], b1[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            b0[v] = __shfl(a0, 4 * lg + v);
-            b1[v] = __shfl(a1, 4 * lg + v);
+            for (int v = 0; v < 4; ++v) {
+                b0[v] = __shfl(a0, 4 * lg + v);
+                b1[v] = __shfl(a1, 4 * lg + v);
+            }
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    O[nt][v] = b0[v] * O[nt][v] + b1[v] * ob[(4 * lg + v) * 512 + 128 * wave + 16 * nt + li];
         }
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                O[nt][v] = b0[v] * O[nt][v] + b1[v] * ob[(4 * lg + v) * 512 + 128 * wave + 16 * nt + li];
-    }
+        }
 
     if (S > 1) {
         // partial result of this part of the keys: unnormalised O, its max and
@@ -443,6 +448,7 @@ __global__ __launch_bounds__(512) void k_sparse_attn(
 // the merge is issued at once.
 constexpr int kMaxSplit = 8;  // the combine is instantiated for S = 2 .. kMaxSplit
 constexpr int kAttnTargetWgs = 256;  // workgroups the key splits aim for (more splits cost more than they hide)
+constexpr unsigned kAttnTwoPipeWgs = 128;  // grids up to this size run two pipes per workgroup
 
 template <int S>
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part, int Hm, int n_hg,
@@ -510,10 +516,16 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
     const int rows8 = (a.g.total_q + 7) / 8 * 8;
     const unsigned nblk = (unsigned)rows8 * (unsigned)n_hg * (unsigned)S;
     float* part = S > 1 ? (float*)a.ws : nullptr;
-    hipLaunchKernelGGL(k_sparse_attn, dim3(nblk), dim3(512), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, a.swa,
-                       a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,
-                       a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q, n_hg, S,
-                       part);
+    // two pipes per workgroup only where the grid leaves most CUs idle (latency
+    // is all that counts there); otherwise one pipe, two workgroups per CU
+#define CSA2_ATTN(NP)                                                                                             \
+    hipLaunchKernelGGL(k_sparse_attn<NP>, dim3(nblk), dim3(256 * NP), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, \
+                       a.swa, a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,   \
+                       a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q,  \
+                       n_hg, S, part)
+    if (nblk <= kAttnTwoPipeWgs) CSA2_ATTN(2);
+    else CSA2_ATTN(1);
+#undef CSA2_ATTN
     if (S > 1) {
         const dim3 cg((unsigned)(a.g.total_q * a.Hm));
         switch (S) {

@@ -561,6 +561,59 @@ __device__ inline uint32_t block_scan_1024(uint32_t v, uint32_t* wsum, uint32_t*
     return before + v;
 }
 
+// Block-wide (1024 threads, every thread calls it): the bin (bits 30..19 of
+// a score) that holds the kk-th largest of the entries visit() enumerates,
+// and the count of entries in the bins above it.  visit(f) calls f(bin) for
+// each of this thread's entries.  Two 6-bit digits (bin = 64 d1 + d2), each
+// counted into 32 copies of a 64-entry LDS histogram (lane l adds to copy
+// l % 32: the entries crowd into a few bins and same-address LDS atomics
+// serialise); thr[0..1] must be zero on entry.
+template <class Visit>
+__device__ void find_bin(Visit&& visit, uint32_t kk, uint32_t* hcopy, uint32_t* dcount, uint32_t* thr, uint32_t& B,
+                         uint32_t& above) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t need = kk;
+    B = 0;
+    above = 0;
+#pragma unroll
+    for (int level = 0; level < 2; ++level) {
+        for (int i = tid; i < 64 * 32; i += 1024) hcopy[i] = 0;
+        __syncthreads();
+        uint32_t* hc = hcopy + (lane & 31);
+        visit([&](uint32_t bin) {
+            if (level == 0 || (bin >> 6) == B) atomicAdd(&hc[32 * (level == 0 ? bin >> 6 : bin & 63u)], 1u);
+        });
+        __syncthreads();
+        {  // digit d = tid / 16 sums copies 2 (tid % 16), +1; 16 lanes reduce
+            const int d = tid >> 4, part = tid & 15;
+            uint32_t v = hcopy[32 * d + 2 * part] + hcopy[32 * d + 2 * part + 1];
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
+            if (part == 0) dcount[d] = v;
+        }
+        __syncthreads();
+        if (wave == 0) {  // lane l owns digit 63 - l; inclusive scan from the top
+            const uint32_t v = dcount[63 - lane];
+            uint32_t incl = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t u2 = __shfl_up(incl, o);
+                if (lane >= o) incl += u2;
+            }
+            const uint32_t before = incl - v;
+            if (before < need && need <= incl) {
+                thr[0] = (uint32_t)(63 - lane);
+                thr[1] = before;
+            }
+        }
+        __syncthreads();
+        B = level == 0 ? thr[0] : (B << 6) | thr[0];
+        above += thr[1];
+        need -= thr[1];
+        __syncthreads();  // thr and hcopy are rewritten by the next level
+    }
+}
+
 // The whole selection of a row from a decode scan's per-chunk lists, in one
 // workgroup of 1024 threads per row and without a histogram from the scan.
 // The histogram of the row's threshold search is built from the lists: a
@@ -842,48 +895,9 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
     }
 
     // 1. the threshold bin B
-    uint32_t B = 0, above = 0;
-    {
-        uint32_t need = kk;
-#pragma unroll
-        for (int level = 0; level < 2; ++level) {
-            for (int i = tid; i < 64 * 32; i += 1024) hcopy[i] = 0;
-            __syncthreads();
-            uint32_t* hc = hcopy + (lane & 31);
-            for_each_entry([&](uint64_t x) {
-                const uint32_t bin = (uint32_t)(x >> 51);
-                if (level == 0 || (bin >> 6) == B) atomicAdd(&hc[32 * (level == 0 ? bin >> 6 : bin & 63u)], 1u);
-            });
-            __syncthreads();
-            {  // digit d = tid / 16 sums copies 2 (tid % 16), +1; 16 lanes reduce
-                const int d = tid >> 4, part = tid & 15;
-                uint32_t v = hcopy[32 * d + 2 * part] + hcopy[32 * d + 2 * part + 1];
-#pragma unroll
-                for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 16);
-                if (part == 0) dcount[d] = v;
-            }
-            __syncthreads();
-            if (wave == 0) {  // lane l owns digit 63 - l; inclusive scan from the top
-                const uint32_t v = dcount[63 - lane];
-                uint32_t incl = v;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t u2 = __shfl_up(incl, o);
-                    if (lane >= o) incl += u2;
-                }
-                const uint32_t before = incl - v;
-                if (before < need && need <= incl) {
-                    thr[0] = (uint32_t)(63 - lane);
-                    thr[1] = before;
-                }
-            }
-            __syncthreads();
-            B = level == 0 ? thr[0] : (B << 6) | thr[0];
-            above += thr[1];
-            need -= thr[1];
-            __syncthreads();  // thr and hcopy are rewritten by the next level
-        }
-    }
+    uint32_t B, above;
+    find_bin([&](auto&& f) { for_each_entry([&](uint64_t x) { f((uint32_t)(x >> 51)); }); }, kk, hcopy, dcount, thr,
+             B, above);
 
     // 2. the entries at or above B, in order, into LDS while they fit
     uint32_t n_cand;
@@ -963,6 +977,101 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
                        [&](uint32_t r, uint64_t x) {
                            if (r < kk) out[r] = slot_of(x);
                        });
+    }
+}
+
+// The whole selection of a score row of at most kRowSelMax slots (Reindex
+// pools, small block pools) in one workgroup of 1024 threads.  Thread t keeps
+// the keys of slots t + 1024 u in registers; the threshold bin comes from
+// find_bin, the keys of that bin are radix-selected from bit 51 down (the bins
+// above it all win), the winners are marked in an LDS bitmap by slot and
+// written in slot order (slot order is position order: a candidate list holds
+// ascending positions, blocks are numbered by position).
+constexpr int kRowPer = kRowSelMax / 1024;  // slots per thread
+
+__global__ __launch_bounds__(1024) void k_topk_rows(const float* __restrict__ scores, int64_t stride, RowSrc rs,
+                                                    const int32_t* __restrict__ cand, int cand_stride, int K,
+                                                    int32_t* __restrict__ idx) {
+    __shared__ uint32_t hcopy[64 * 32];
+    __shared__ uint32_t dcount[64];
+    __shared__ uint32_t hist256[256], scan256[256];
+    __shared__ uint32_t bm[kRowSelMax / 32];
+    __shared__ RadixState st;
+    __shared__ int found;
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t thr[2];
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float* sr = scores + (int64_t)row * stride;
+    const int64_t n = row_n(rs, row);  // <= kRowSelMax (launcher)
+    const uint32_t kk = (uint32_t)(n < K ? n : K);
+    int32_t* out = idx + (int64_t)row * K;
+    for (int i = tid + (int)kk; i < K; i += 1024) out[i] = -1;
+    if (kk == 0) return;
+    uint32_t key[kRowPer];
+#pragma unroll
+    for (int u = 0; u < kRowPer; ++u) {
+        const int64_t e = tid + 1024 * u;
+        key[u] = e < n ? score_key(sr[e]) : 0u;
+    }
+    auto valid = [&](int u) { return (int64_t)tid + 1024 * u < n; };
+    if (tid == 0) {
+        thr[0] = 0;
+        thr[1] = 0;
+    }
+    if (tid < kRowSelMax / 32) bm[tid] = 0;
+    __syncthreads();
+
+    uint32_t B, above;
+    find_bin(
+        [&](auto&& f) {
+#pragma unroll
+            for (int u = 0; u < kRowPer; ++u)
+                if (valid(u)) f(key[u] >> 19);
+        },
+        kk, hcopy, dcount, thr, B, above);
+
+    if (tid == 0) {
+        st.prefix = B;
+        st.shift = 51;
+        st.need = kk - above;
+        st.done = 0;
+    }
+    __syncthreads();
+    while (!st.done) {
+        if (tid < 256) hist256[tid] = 0;
+        __syncthreads();
+        const int sh = st.shift;
+        const int w = digit_bits(sh);
+        const uint64_t pf = st.prefix;
+#pragma unroll
+        for (int u = 0; u < kRowPer; ++u) {
+            const uint64_t x = composite(key[u], (uint32_t)(tid + 1024 * u));
+            if (valid(u) && (x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
+        }
+        __syncthreads();
+        radix_step(hist256, scan256, &st, &found);
+    }
+    const int sh = st.shift;
+    const uint64_t pf = st.prefix;
+#pragma unroll
+    for (int u = 0; u < kRowPer; ++u) {
+        const uint32_t e = (uint32_t)(tid + 1024 * u);
+        if (valid(u) && (composite(key[u], e) >> sh) >= pf) atomicOr(&bm[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+    // slots in order: thread t owns bitmap word t
+    const int nwords = (int)((n + 31) / 32);
+    uint32_t wd = tid < nwords ? bm[tid] : 0u;
+    const uint32_t cnt = (uint32_t)__popc(wd);
+    uint32_t tot;
+    uint32_t r = block_scan_1024(cnt, wsum, &tot) - cnt;
+    while (wd) {
+        const int bit = __ffs(wd) - 1;
+        const uint32_t slot = 32u * (uint32_t)tid + (uint32_t)bit;
+        if (r < kk) out[r] = map_slot(cand, cand_stride, row, slot);
+        ++r;
+        wd &= wd - 1;
     }
 }
 
@@ -1057,6 +1166,11 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
     uint64_t* cb = (uint64_t*)ws;
     RowSrc rs{a.b->d_entry_off, a.b->d_row_seq, a.b->d_q_pos, a.b->ratio, a.cand ? a.cand_count : nullptr,
               a.block_mode, a.block, a.max_slots};
+    if (a.max_slots <= kRowSelMax) {  // one workgroup per row; any histogram from the caller is not needed
+        hipLaunchKernelGGL(k_topk_rows, dim3(nq), dim3(1024), 0, s, a.scores, a.stride, rs, a.cand, a.cand_stride,
+                           a.K, a.idx);
+        return hipGetLastError();
+    }
     const unsigned chunks = (unsigned)((a.max_slots + kHChunk - 1) / kHChunk);
     const uint32_t* h = a.hist;
     if (h && h != hist) {

@@ -132,6 +132,27 @@ def test_topk_full_bitwise(distinct):
         assert np.array_equal(got.cpu().numpy(), ref), K
 
 
+@pytest.mark.parametrize("distinct", [4, 1000, 0, 1])
+def test_topk_rows_bitwise(distinct):
+    """Rows of at most 16,384 slots: one workgroup per row selects from the
+    scores held in registers (few distinct values, continuous, all equal)."""
+    rng = np.random.default_rng(23 + distinct)
+    lens = [2, 3, 511, 512, 513, 9000, 16384]
+    b, qp = _topk_batch(lens, 2)
+    nq = b.total_q
+    stride = max(lens)
+    if distinct:
+        s = (rng.integers(0, distinct, size=(nq, stride)) * 0.5).astype(np.float32)
+    else:
+        s = rng.random((nq, stride)).astype(np.float32) * 100
+    vis = np.array([min(n, t + 1) for n, p in zip(lens, qp) for t in p], np.int64)
+    for K in (512, 2048, 17):
+        got = C.csa2_topk(b, dev(s), K)
+        torch.cuda.synchronize()
+        ref = oracle.topk(s, vis, K)
+        assert np.array_equal(got.cpu().numpy(), ref), K
+
+
 def test_topk_all_equal_uses_fallback():
     # every score equal: the candidate list overflows and the fallback picks the lowest positions
     lens = [50000, 9000]
