@@ -30,7 +30,9 @@ struct RowSel {
     uint32_t bin;      // threshold bin (candidates have bin >= this)
     uint32_t cnt;      // candidates collected (may exceed kCandCap -> fallback)
     uint32_t above;    // keys in the bins above the threshold bin (all of them win)
-    uint32_t pad[3];
+    uint32_t lb;       // 1: `bin` is only a lower bound of the threshold bin (candidates hold every
+                       //    key from it up; the selection starts from the top key bit)
+    uint32_t pad[2];
 };
 
 struct Geometry {

@@ -30,6 +30,7 @@ namespace csa2 {
 namespace {
 
 constexpr int kHChunk = 8192;  // slots per workgroup in the histogram / collect passes
+constexpr int kFinalBitmapSlots = 262144;  // rows up to this many slots write their winners through a bitmap
 
 struct RowSrc {
     const int64_t* entry_off;
@@ -56,34 +57,35 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-// Histogram of score bits 30..19 per row.  Each thread keeps 8 loads in
-// flight before it touches the shared histogram.
-__global__ __launch_bounds__(256) void k_hist(const float* __restrict__ scores, int64_t stride, RowSrc rs,
-                                              uint32_t* __restrict__ hist) {
+// Chunk bounds (rows with no histogram): workgroup (c, row) counts the bins
+// of slots [c kHChunk, (c+1) kHChunk) in LDS and, when those slots all exist,
+// records the bin of their m-th largest score, m = ceil(K / F), F the row's
+// count of such full chunks.  The F chunks then hold F m >= K slots at or
+// above the smallest recorded bin, so that bin is at or below the row's
+// threshold bin; no global atomics are needed.
+__global__ __launch_bounds__(256) void k_chunk_bound(const float* __restrict__ scores, int64_t stride, RowSrc rs,
+                                                     int K, uint32_t* __restrict__ lb) {
     __shared__ uint32_t h[kHistBins];
+    __shared__ uint32_t wtot[4], found[2];
     const int row = blockIdx.y;
     const int64_t n = row_n(rs, row);
     const int64_t s0 = (int64_t)blockIdx.x * kHChunk;
-    if (s0 >= n) return;
-    const int64_t s1 = s0 + kHChunk < n ? s0 + kHChunk : n;
+    if (s0 + kHChunk > n) return;  // a partial chunk (or none): no bound
+    const int64_t F = n / kHChunk;
+    const uint32_t m = (uint32_t)((K + F - 1) / F);
     for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
     __syncthreads();
-    const float* sr = scores + (int64_t)row * stride;
-    for (int64_t base = s0; base < s1; base += 256 * 8) {
+    const float* sr = scores + (int64_t)row * stride + s0;
+    for (int base = 0; base < kHChunk; base += 256 * 8) {
         uint32_t key[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t s = base + threadIdx.x + 256 * u;
-            key[u] = s < s1 ? score_key(sr[s]) : 0xFFFFFFFFu;
-        }
+        for (int u = 0; u < 8; ++u) key[u] = score_key(sr[base + threadIdx.x + 256 * u]);
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (key[u] != 0xFFFFFFFFu) atomicAdd(&h[key[u] >> 19], 1u);
+        for (int u = 0; u < 8; ++u) atomicAdd(&h[key[u] >> 19], 1u);
     }
     __syncthreads();
-    uint32_t* gh = hist + (int64_t)row * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += 256)
-        if (h[i]) atomicAdd(&gh[i], h[i]);
+    const uint32_t bm = threshold_bin(PlainBins{h}, m, wtot, found);
+    if (threadIdx.x == 0) lb[(int64_t)row * kHistBins + blockIdx.x] = bm;
 }
 
 // Candidates: every slot whose bin is at or above the threshold bin goes to
@@ -96,6 +98,9 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ scores, 
 // each row records it for the final pass.
 constexpr int kLocalCand = 2048;
 
+// LB: `hist` holds the chunk bounds of k_chunk_bound instead of a histogram,
+// and the candidates are the slots at or above the smallest of them.
+template <bool LB>
 __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ scores, int64_t stride, RowSrc rs,
                                                  const uint32_t* __restrict__ hist, int K, RowSel* __restrict__ sel,
                                                  uint64_t* __restrict__ cand_buf) {
@@ -118,12 +123,27 @@ __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ score
     }
     if (threadIdx.x == 0) lcount = 0;
     const uint32_t kk = (uint32_t)(n < K ? n : K);
-    const uint32_t bin = threshold_bin(PlainBins{hist + (int64_t)row * kHistBins}, kk, part, found);
+    uint32_t bin;
+    if constexpr (LB) {
+        // the smallest bound of the row's full chunks (0 without one); a row
+        // with no slot selects nothing
+        const int F = (int)(n / kHChunk);
+        uint32_t v = 0xFFFFFFFFu;
+        for (int c = threadIdx.x; c < F; c += 256) v = min(v, hist[(int64_t)row * kHistBins + c]);
+        for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o));
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+        __syncthreads();
+        v = min(min(part[0], part[1]), min(part[2], part[3]));
+        bin = kk == 0 ? (uint32_t)kHistBins : (F > 0 ? v : 0u);
+    } else {
+        bin = threshold_bin(PlainBins{hist + (int64_t)row * kHistBins}, kk, part, found);
+    }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         sel[row].n = (uint32_t)n;
         sel[row].kk = kk;
         sel[row].bin = bin;
-        sel[row].above = found[1];
+        sel[row].above = LB ? 0u : found[1];
+        sel[row].lb = LB ? 1u : 0u;
     }
     if (bin >= (uint32_t)kHistBins || s0 >= n) return;
     const int lane = threadIdx.x & 63;
@@ -269,6 +289,30 @@ __device__ __forceinline__ int32_t map_slot(const int32_t* cand, int cand_stride
     return cand ? cand[(int64_t)row * cand_stride + slot] : (int32_t)slot;
 }
 
+// Inclusive scan of one value per thread over a 1024-thread workgroup; `total`
+// receives the workgroup's sum.  Every thread calls it; it ends with a
+// barrier, so `wsum` may be reused right after.
+__device__ inline uint32_t block_scan_1024(uint32_t v, uint32_t* wsum, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) {
+        const uint32_t x = wsum[w2];
+        before += w2 < wave ? x : 0u;
+        tot += x;
+    }
+    *total = tot;
+    __syncthreads();
+    return before + v;
+}
+
 // One workgroup per row: exact selection of the kk winners by key64 and their
 // output in ascending position order.  Rows whose candidate list fitted are
 // selected from the list in LDS; rows whose list overflowed (heavy ties) are
@@ -281,6 +325,7 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
     __shared__ uint64_t c[kCandCap];
     __shared__ uint32_t winners[kMaxK];
     __shared__ uint32_t part_rank[512];
+    __shared__ uint32_t bmap[kFinalBitmapSlots / 32];  // winners by slot
     __shared__ uint32_t hist256[256], scan256[256];
     __shared__ RadixState st;
     __shared__ uint32_t nwin, base;
@@ -303,7 +348,7 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         st.done = from_list && cnt == kk;  // every candidate wins
         nwin = 0;
         base = 0;
-        if (from_list && !st.done) {
+        if (from_list && !st.done && !sel[row].lb) {
             // the candidates are the keys of the threshold bin and of the bins
             // above it (all of which win): select among the threshold bin's keys
             // only, from bit 51 down
@@ -330,6 +375,44 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
     }
     const int sh = st.shift;
     const uint64_t pf = st.prefix;
+    if (from_list && n <= kFinalBitmapSlots) {
+        // winners (key64 >= prefix << shift) marked by slot, then written in
+        // slot order: thread t owns bitmap words [WPT t, WPT (t + 1))
+        constexpr int kWpt = kFinalBitmapSlots / 32 / 1024;
+        const int nwords = (int)((n + 31) / 32);
+        for (int i = threadIdx.x; i < nwords; i += 1024) bmap[i] = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < cnt; i += 1024) {
+            const uint64_t x = c[i];
+            if (sh >= 64 || (x >> sh) >= pf) {
+                const uint32_t slot = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu);
+                atomicOr(&bmap[slot >> 5], 1u << (slot & 31));
+            }
+        }
+        __syncthreads();
+        const int wpt = (nwords + 1023) / 1024;
+        uint32_t wd[kWpt];
+        uint32_t wc = 0;
+#pragma unroll
+        for (int i = 0; i < kWpt; ++i) {
+            const int wi = wpt * (int)threadIdx.x + i;
+            wd[i] = (i < wpt && wi < nwords) ? bmap[wi] : 0u;
+            wc += (uint32_t)__popc(wd[i]);
+        }
+        uint32_t tot;
+        uint32_t r = block_scan_1024(wc, wsum, &tot) - wc;
+#pragma unroll
+        for (int i = 0; i < kWpt; ++i) {
+            uint32_t x = wd[i];
+            while (x) {
+                const int bit = __ffs(x) - 1;
+                if (r < kk) out[r] = map_slot(cand, cand_stride, row, 32u * (uint32_t)(wpt * (int)threadIdx.x + i) + (uint32_t)bit);
+                ++r;
+                x &= x - 1;
+            }
+        }
+        return;
+    }
     if (from_list) {
         // winners: key64 >= prefix << shift; then sort their slots
         for (uint32_t i = threadIdx.x; i < cnt; i += 1024) {
@@ -537,29 +620,6 @@ __global__ __launch_bounds__(1024) void k_final_local(const uint64_t* __restrict
     }
 }
 
-// Inclusive scan of one value per thread over a 1024-thread workgroup; `total`
-// receives the workgroup's sum.  Every thread calls it; it ends with a
-// barrier, so `wsum` may be reused right after.
-__device__ inline uint32_t block_scan_1024(uint32_t v, uint32_t* wsum, uint32_t* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t u = __shfl_up(v, o);
-        if (lane >= o) v += u;
-    }
-    if (lane == 63) wsum[wave] = v;
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < 16; ++w2) {
-        const uint32_t x = wsum[w2];
-        before += w2 < wave ? x : 0u;
-        tot += x;
-    }
-    *total = tot;
-    __syncthreads();
-    return before + v;
-}
 
 // Block-wide (1024 threads, every thread calls it): the bin (bits 30..19 of
 // a score) that holds the kk-th largest of the entries visit() enumerates,
@@ -1173,18 +1233,24 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
     }
     const unsigned chunks = (unsigned)((a.max_slots + kHChunk - 1) / kHChunk);
     const uint32_t* h = a.hist;
-    if (h && h != hist) {
+    if (!h) {
+        // no histogram from the caller: the chunk bounds (in the histogram's
+        // place) give a lower bound of each row's threshold bin
         hipError_t e = clear_topk_ws(a.ws, nq, false, s);
         if (e != hipSuccess) return e;
-    } else if (!h) {
-        hipError_t e = clear_topk_ws(a.ws, nq, true, s);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_hist, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, hist);
-        h = hist;
+        hipLaunchKernelGGL(k_chunk_bound, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, a.K,
+                           hist);
+        hipLaunchKernelGGL(k_collect<true>, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs,
+                           hist, a.K, sel, cb);
+    } else {
+        if (h != hist) {
+            hipError_t e = clear_topk_ws(a.ws, nq, false, s);
+            if (e != hipSuccess) return e;
+        }
+        // (h == hist: the caller cleared the workspace and filled its histogram)
+        hipLaunchKernelGGL(k_collect<false>, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, h,
+                           a.K, sel, cb);
     }
-    // (h == hist: the caller cleared the workspace and filled its histogram)
-    hipLaunchKernelGGL(k_collect, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, h, a.K,
-                       sel, cb);
     hipLaunchKernelGGL(k_final, dim3(nq), dim3(1024), 0, s, a.scores, a.stride, sel, cb, a.cand, a.cand_stride, a.K,
                        a.idx);
     return hipGetLastError();
