@@ -214,9 +214,10 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
     q_off = np.zeros(n_seq + 1, np.int32)
     q_off[1:] = np.cumsum([len(p) for p in q_pos])
     row_seq = np.repeat(np.arange(n_seq, dtype=np.int32), [len(p) for p in q_pos])
-    # SWA rows: token positions [min(t) - W + 1, max(t)] clipped at 0, per sequence
-    swa_pos0 = np.array([max(0, int(np.min(p)) - W + 1) for p in q_pos], np.int32)
-    swa_len = np.array([int(np.max(p)) - s + 1 for p, s in zip(q_pos, swa_pos0)], np.int32)
+    # SWA rows: token positions [min(t) - W + 1, max(t)] clipped at 0, per
+    # sequence (none for a sequence without query rows)
+    swa_pos0 = np.array([max(0, int(np.min(p)) - W + 1) if len(p) else 0 for p in q_pos], np.int32)
+    swa_len = np.array([int(np.max(p)) - s + 1 if len(p) else 0 for p, s in zip(q_pos, swa_pos0)], np.int32)
     swa_row_off = np.zeros(n_seq, np.int64)
     swa_row_off[1:] = np.cumsum(swa_len)[:-1]
     wl = Workload(name, seed, ratio, H, Hm, K, W, block, max_blocks, n_entries, entry_off, q_off, q_pos_all,

@@ -249,6 +249,14 @@ CHAIN_CASES = {
     "c2_small_h64": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=64),
     "c4_small": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16),
     "c3_small": lambda: synth.config("prefill_c3", tokens=4000, T=96, Hm=16),
+    # degenerate rows: a sequence with no entries (its row attends to its
+    # window alone), one with entries but no query row, and one with a
+    # single entry; Full with pool, Reindex and Reuse
+    "degenerate": lambda: synth.make_workload("degenerate", 0xC5A2D000, [0, 3000, 5000, 1], 1,
+                                              [(20, synth.MODE_FULL, True), (24, synth.MODE_REINDEX, False),
+                                               (25, synth.MODE_REUSE, False)], Hm=16,
+                                              q_pos=[np.array([5]), np.array([], np.int64),
+                                                     np.array([4990, 4999]), np.array([0])]),
     "encoder_group": lambda: synth.make_workload("enc", 12, [700, 2500], 3, [(0, synth.MODE_SWA_ONLY, False),
                                                                              (2, synth.MODE_FULL, False),
                                                                              (3, synth.MODE_REUSE, False),
