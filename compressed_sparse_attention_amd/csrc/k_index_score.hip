@@ -229,8 +229,10 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
                 }
                 if (mt == NMT - 1 && (t == nq - 1 || t == TQ - 1)) fetch(bf, p_next);
                 s = head_sum_32(acc, w + (int64_t)(r0 + t) * H + 32 * mt, s);
-                // keep the next group's MFMAs after this head sum, so that
-                // only one group's accumulators are live at a time
+                // the partial sum is complete here (not sunk into the guarded
+                // store below), and the next group's MFMAs stay after it, so
+                // that only one group's accumulators are live at a time
+                asm volatile("" : "+v"(s));
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (jl < n) {
