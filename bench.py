@@ -186,6 +186,9 @@ def main():
     scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
     log(f"[bench] scan kernel: {scan_ms * 1000:.1f} us, {scan_gbs:.0f} GB/s algorithmic")
 
+    ceiling = measured_ceiling(torch, dev, scan_bytes)
+    log(f"[bench] plain device copy {ceiling['copy_gbs']:.0f} GB/s (read + write), plain read "
+        f"{ceiling['read_gbs']:.0f} GB/s over {scan_bytes / 1e6:.0f} MB")
     result = {
         "metric": METRIC,
         "value": round(1000.0 / ms_step, 2),
@@ -208,7 +211,8 @@ def main():
                      "bound": "hbm", "achieved": round(scan_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "mean_launch_us": round(scan_ms * 1000, 2),
-                     "algorithmic_bytes_per_launch": scan_bytes},
+                     "algorithmic_bytes_per_launch": scan_bytes,
+                     "measured_ceiling": dict(ceiling, frac_of_read=round(scan_gbs / ceiling["read_gbs"], 4))},
     }
     if args.profile_pass:  # calibration copy for the byte counters
         a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -230,6 +234,39 @@ def main():
         result["workloads"] = bench_workloads(synth, C, torch, dev)
 
     print(json.dumps(result), flush=True)
+
+
+def measured_ceiling(torch, dev, nbytes, reps=10):
+    """Secondary denominators for the scan: what plain torch kernels reach on
+    this device over the same byte count.  A device-to-device copy (bytes read
+    + bytes written per second) and a plain read (an int64 sum of the buffer:
+    bytes read per second).  Buffers are rotated so that the 256 MB MALL does
+    not serve repeats."""
+    n = (nbytes // 8) * 8
+    bufs = [torch.ones(n // 8, dtype=torch.int64, device=dev) for _ in range(2)]
+    dst = torch.empty_like(bufs[0])
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for i in range(3):
+            fn(bufs[i & 1])
+        torch.cuda.synchronize()
+        best = None
+        for i in range(reps):
+            s.record()
+            fn(bufs[i & 1])
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    t_copy = timed(lambda a: dst.copy_(a))
+    t_read = timed(lambda a: a.sum())
+    del bufs, dst
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * n / (t_copy * 1e-3) / 1e9, 1), "read_gbs": round(n / (t_read * 1e-3) / 1e9, 1),
+            "bytes": n, "how": "best of 10: torch copy_ (read + write) and int64 sum (read) of the scan's byte count"}
 
 
 def chain_only(args, synth, C, torch, dev):
