@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the layer-chain timings of the other four workloads")
     ap.add_argument("--workload", default="decode_c1",
-                    choices=["decode_c1", "decode_c0", "chain_c2", "prefill_c3", "ragged_c4"],
+                    choices=["decode_c1", "decode_c0", "chain_c2", "prefill_c3", "ragged_c4", "replay_c5"],
                     help="decode_c1 (default) prints the full line; the others time their layer chain only")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for hardware-counter collection: a few steps, a few scan launches and one "
@@ -334,15 +334,16 @@ def synth_mode(name):
 
 
 def bench_workloads(synth, C, torch, dev):
-    """The layer chain of the other four workloads: one call = every layer of
-    one decode step (or of the prefill chunk) for the whole batch."""
+    """The layer chain of the other workloads: one call = every layer of one
+    decode step (or of the prefill chunk, or of the 128-token decoder replay)
+    for the whole batch."""
     import numpy as np
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gpu_util import DevWorkload, prepare_chain
 
     res = {}
-    for name, reps in (("decode_c0", 20), ("chain_c2", 5), ("ragged_c4", 5), ("prefill_c3", 3)):
+    for name, reps in (("decode_c0", 20), ("chain_c2", 5), ("ragged_c4", 5), ("prefill_c3", 3), ("replay_c5", 3)):
         t0 = time.time()
         wl = synth.config(name)
         dw = DevWorkload(wl, dev)
@@ -359,10 +360,20 @@ def bench_workloads(synth, C, torch, dev):
         n_layers = len(wl.layers)
         r = {"ms_per_chain": round(ms, 4), "layers": n_layers, "rows": wl.total_q,
              "entries": wl.total_entries, "layer_steps_per_s": round(n_layers * 1000.0 / ms, 1)}
-        if name == "prefill_c3":
-            vis = np.minimum(wl.n_entries[0], (wl.q_pos.astype(np.int64) + 1) // wl.ratio)
-            idx_flops = 2.0 * float(vis.sum()) * wl.H * 128
-            n_swa = np.minimum(wl.W, wl.q_pos.astype(np.int64) + 1)
+        if name in ("prefill_c3", "replay_c5"):
+            # many query rows share each scan: FLOP/s.  Full layers score every
+            # visible entry, Reindex layers their pool; attention reads the
+            # selected entries and the (replay-cut) window
+            t = wl.q_pos.astype(np.int64)
+            vis = np.minimum(wl.n_entries[wl.row_seq], (t + 1) // wl.ratio)
+            n_full = sum(1 for L in wl.layers if L.mode == synth.MODE_FULL)
+            n_reindex = sum(1 for L in wl.layers if L.mode == synth.MODE_REINDEX)
+            pooled = float(pc.cpu().numpy().sum()) if n_reindex and pc is not None else 0.0
+            idx_flops = 2.0 * wl.H * 128 * (n_full * float(vis.sum()) + n_reindex * pooled)
+            lo = np.maximum(t - wl.W + 1, 0)
+            if wl.replay_s is not None:
+                lo = np.maximum(lo, wl.replay_s[wl.row_seq].astype(np.int64))
+            n_swa = t - lo + 1
             keys = sum(float((o["idx"].cpu().numpy() >= 0).sum()) + float(n_swa.sum()) for o in outs)
             attn_flops = keys * wl.Hm * 512 * 4  # Q K^T and P V
             r.update({"index_flops": idx_flops, "attn_flops": attn_flops,

@@ -129,15 +129,11 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wave within the pipe
     const int lg = lane >> 4, li = lane & 15;
 
-    // ---- prologue: the query and the index row first (they need only the
-    // row), then the sequence's window and, with it, the first block's SWA rows
-    const int hq = HG * hg + li;
-    v8bf Q[16];
-    {
-        const uint16_t* qr = q + ((int64_t)row * Hm + hq) * 512 + 8 * lg;
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, ld16(qr + 32 * ks));
-    }
+    // ---- prologue: the index row and the query first (they need only the
+    // row), then the sequence's window and, with it, the first block's SWA rows.
+    // The index row goes first: loads complete in issue order, and the index
+    // row is needed first (in LDS, before any selected key is fetched), so its
+    // wait leaves the query's 16 KB in flight.
     const int32_t* irow = idx + (int64_t)row * K;
     constexpr int NT = 256 * NPIPE;
     int32_t ir[kMaxK / NT];
@@ -145,6 +141,14 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     for (int i = 0; i < kMaxK / NT; ++i) {
         const int s = tid + NT * i;
         ir[i] = s < K ? irow[s] : -1;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keeps the index row's loads ahead of the query's
+    const int hq = HG * hg + li;
+    v8bf Q[16];
+    {
+        const uint16_t* qr = q + ((int64_t)row * Hm + hq) * 512 + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, ld16(qr + 32 * ks));
     }
     // keep the loads above ahead of the scalar loads below (they would
     // otherwise wait for them)

@@ -237,7 +237,8 @@ def layer_chain(wl, rows=None, attn=True):
             use_idx = idx_cur
         res["idx"] = use_idx
         if attn:
-            res["out"], res["lse"] = sparse_attn(wl, L.q_main, use_idx, L.swa, rows=sel_rows, idx_of_rows=True)
+            res["out"], res["lse"] = sparse_attn(wl, L.q_main, use_idx, L.swa, replay_s=getattr(wl, "replay_s", None),
+                                                 rows=sel_rows, idx_of_rows=True)
         results.append(res)
     return results
 

@@ -160,6 +160,7 @@ class Workload:
     kv: np.ndarray = None      # [sumN][256] u8
     kv_sc: np.ndarray = None   # [sumN][16] u8
     layers: List[Layer] = field(default_factory=list)
+    replay_s: Optional[np.ndarray] = None  # [n_seq] i32 SWA replay start per sequence (None: 0)
 
     @property
     def n_seq(self):
@@ -198,11 +199,12 @@ def ragged_lengths(seed, n_seq, lo=4096, hi=1048576):
 
 
 def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=64, Hm=64, K=512, W=128,
-                  block=8, max_blocks=2048, q_fmt=Q_FP4, q_pos=None, gen_kv=True, gen_layers=True):
+                  block=8, max_blocks=2048, q_fmt=Q_FP4, q_pos=None, gen_kv=True, gen_layers=True, replay_s=None):
     """Build a workload.  n_entries: per-sequence entry counts.  queries_per_seq:
     T (same for all sequences).  q_pos: explicit token positions per sequence
     (list of arrays) or None for the decode shape t = N*ratio - T + i.
-    schedule: list of (layer index, mode, build_pool)."""
+    schedule: list of (layer index, mode, build_pool).  replay_s: per-sequence
+    SWA replay start s (a query at t sees window rows max(s, t - W + 1) .. t)."""
     n_entries = np.asarray(n_entries, np.int64)
     n_seq = len(n_entries)
     entry_off = np.zeros(n_seq + 1, np.int64)
@@ -222,6 +224,8 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
     swa_row_off[1:] = np.cumsum(swa_len)[:-1]
     wl = Workload(name, seed, ratio, H, Hm, K, W, block, max_blocks, n_entries, entry_off, q_off, q_pos_all,
                   row_seq, swa_row_off, swa_pos0, swa_len)
+    if replay_s is not None:
+        wl.replay_s = np.ascontiguousarray(replay_s, np.int32)
     total = int(entry_off[-1])
     if gen_kv:
         wl.k_idx, ksc = mxfp4_rows(seed, TID_K, total, 128, 128)
@@ -248,7 +252,7 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
     return wl
 
 
-CONFIG_IDS = {"decode_c0": 0, "decode_c1": 1, "chain_c2": 2, "prefill_c3": 3, "ragged_c4": 4}
+CONFIG_IDS = {"decode_c0": 0, "decode_c1": 1, "chain_c2": 2, "prefill_c3": 3, "ragged_c4": 4, "replay_c5": 5}
 
 
 def config(name, **kw):
@@ -273,6 +277,15 @@ def config(name, **kw):
         sched = [(2, MODE_FULL, False)] + [(2 + i, MODE_REUSE, False) for i in range(1, n_layers)]
         qp = [np.arange(tokens - T, tokens, dtype=np.int64)]
         return make_workload(name, seed, [tokens // 2], T, sched, ratio=2, q_fmt=Q_FP8, q_pos=qp, **kw)
+    if name == "replay_c5":
+        # decoder SWA bounded replay: the last T = W prompt tokens of each
+        # sequence run the decoder layers again as T query rows against the
+        # decoder's global cache, every window cut at the first replayed token
+        n_seq = kw.pop("n_seq", 16)
+        n = kw.pop("n", 131072)
+        T = kw.pop("T", 128)
+        sched = kw.pop("schedule", decoder_schedule())
+        return make_workload(name, seed, [n] * n_seq, T, sched, replay_s=[n - T] * n_seq, **kw)
     if name == "ragged_c4":
         n_seq = kw.pop("n_seq", 48)
         lens = kw.pop("lengths", None)

@@ -18,7 +18,7 @@ class DevWorkload:
     def __init__(self, wl, device="cuda"):
         self.wl = wl
         self.batch = C.Batch.from_workload(wl, device)
-        self.swa = C.SwaLayout.from_workload(wl, device=device)
+        self.swa = C.SwaLayout.from_workload(wl, replay_s=getattr(wl, "replay_s", None), device=device)
         self.k_idx = dev(wl.k_idx, device)
         self.k_sc = dev(wl.k_sc, device)
         self.kv = dev(wl.kv, device)

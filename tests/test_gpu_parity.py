@@ -257,6 +257,11 @@ CHAIN_CASES = {
                                                (25, synth.MODE_REUSE, False)], Hm=16,
                                               q_pos=[np.array([5]), np.array([], np.int64),
                                                      np.array([4990, 4999]), np.array([0])]),
+    # decoder SWA bounded replay: the last 128 prompt tokens as FP4 query rows
+    # through Full + pool, Reindex and Reuse, windows cut at the replay start
+    "decoder_replay": lambda: synth.config("replay_c5", n_seq=2, n=6000, T=128, Hm=16,
+                                           schedule=[(20, synth.MODE_FULL, True), (24, synth.MODE_REINDEX, False),
+                                                     (25, synth.MODE_REUSE, False)]),
     "encoder_group": lambda: synth.make_workload("enc", 12, [700, 2500], 3, [(0, synth.MODE_SWA_ONLY, False),
                                                                              (2, synth.MODE_FULL, False),
                                                                              (3, synth.MODE_REUSE, False),

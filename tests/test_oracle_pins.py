@@ -564,3 +564,30 @@ def test_cache_ledger_of_this_layout():
     from compressed_sparse_attention_amd import ledger
     assert ledger.bytes_per_position("mxfp4_e8m0") == 337
     assert ledger.bytes_per_token("mxfp4_e8m0") == 842.5
+
+
+def test_decoder_replay_chain():
+    """Decoder SWA bounded replay (course notes "3. 通用基础设施" §3.2.2: a query
+    at t sees window rows max(s, t - W + 1) .. t): the last T = W prompt tokens
+    rerun the decoder layers with s at the first of them.  A start at 0 changes
+    nothing; the last token's window is not cut, so its row equals the chain
+    without replay; every earlier row loses window keys, so its log-sum-exp is
+    strictly lower (a softmax over a subset of the keys) and its output moves.
+    The selections do not depend on the window."""
+    n, T = 1500, 128
+    sched = [(20, MODE_FULL, True), (24, MODE_REINDEX, False), (25, MODE_REUSE, False)]
+    base = synth.config("replay_c5", n_seq=1, n=n, T=T, Hm=16, schedule=sched)
+    assert list(base.replay_s) == [n - T] and base.q_pos[0] == n - T and base.q_pos[-1] == n - 1
+    plain = synth.config("replay_c5", n_seq=1, n=n, T=T, Hm=16, schedule=sched)
+    plain.replay_s = None
+    zero = synth.config("replay_c5", n_seq=1, n=n, T=T, Hm=16, schedule=sched)
+    zero.replay_s = np.zeros(1, np.int32)
+    rp, rn, rz = oracle.layer_chain(base), oracle.layer_chain(plain), oracle.layer_chain(zero)
+    for a, b, c in zip(rp, rn, rz):
+        assert np.array_equal(a["idx"], b["idx"])
+        np.testing.assert_array_equal(c["out"], b["out"])
+        np.testing.assert_array_equal(c["lse"], b["lse"])
+        np.testing.assert_array_equal(a["out"][-1], b["out"][-1])
+        np.testing.assert_array_equal(a["lse"][-1], b["lse"][-1])
+        assert np.all(a["lse"][:-1] < b["lse"][:-1])
+        assert np.all(np.abs(a["out"][:-1] - b["out"][:-1]).max(axis=(1, 2)) > 0)
