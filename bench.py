@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the layer-chain timings of the other four workloads")
     ap.add_argument("--workload", default="decode_c1",
-                    choices=["decode_c1", "decode_c0", "chain_c2", "prefill_c3", "ragged_c4", "replay_c5"],
+                    choices=["decode_c1", "decode_c0", "chain_c2", "prefill_c3", "ragged_c4", "replay_c5",
+                             "decode_step_40"],
                     help="decode_c1 (default) prints the full line; the others time their layer chain only")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for hardware-counter collection: a few steps, a few scan launches and one "
@@ -125,6 +126,11 @@ def main():
     torch.cuda.set_device(0)
     C.lib()
     dev = torch.device("cuda:0")
+    if args.workload == "decode_step_40":
+        res = {"metric": METRIC, "workload": args.workload}
+        res.update(bench_step_40(synth, torch, dev, reps=args.steps))
+        print(json.dumps(res), flush=True)
+        return
     if args.workload != "decode_c1":
         return chain_only(args, synth, C, torch, dev)
 
@@ -386,7 +392,46 @@ def bench_workloads(synth, C, torch, dev):
         res[name] = r
         del dw, outs, call, pb, pp, pc, wl
         torch.cuda.empty_cache()
+    res["decode_step_40"] = bench_step_40(synth, torch, dev)
     return res
+
+
+def bench_step_40(synth, torch, dev, reps=5):
+    """One decode token of each of 64 sequences at 131,072 tokens through all 40
+    layers: the five chains the layers form (two sliding-window layers, three
+    encoder groups at ratio 2 over 65,536 entries with their own caches, the
+    decoder at ratio 1 over 131,072 entries with the pool), run back to back
+    on one stream and timed together."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import DevWorkload, prepare_chain
+
+    t0 = time.time()
+    wls = synth.decode_step_40()
+    dws = [DevWorkload(wl, dev) for wl in wls]
+    calls = [prepare_chain(dw, want_idx=False, want_lse=False)[0] for dw in dws]
+
+    def step():
+        for c in calls:
+            c()
+
+    step()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    n_layers = sum(len(wl.layers) for wl in wls)
+    n_seq = wls[0].n_seq
+    log(f"[bench] decode_step_40: {ms:.3f} ms per 40-layer step of {n_seq} sequences ({time.time() - t0:.0f} s incl. inputs)")
+    r = {"ms_per_step": round(ms, 4), "layers": n_layers, "sequences": n_seq, "tokens": int(wls[-1].n_entries[0]),
+         "tokens_per_s": round(n_seq * 1000.0 / ms, 1), "layer_steps_per_s": round(n_layers * 1000.0 / ms, 1),
+         "chains": [wl.name for wl in wls]}
+    del calls, dws, wls
+    torch.cuda.empty_cache()
+    return r
 
 
 def bench_prefill(args, C, synth, torch, dev):

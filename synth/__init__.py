@@ -189,6 +189,34 @@ def decoder_schedule(first=20, last=39):
     return out
 
 
+def encoder_schedule():
+    """Encoder layers 0..19 (report 4.2.1): layers 0 and 1 pure sliding window,
+    then three groups of six at ratio 2, each a Full layer and five Reuse."""
+    out = [(0, MODE_SWA_ONLY, False), (1, MODE_SWA_ONLY, False)]
+    for g0 in (2, 8, 14):
+        out.append((g0, MODE_FULL, False))
+        out += [(l, MODE_REUSE, False) for l in range(g0 + 1, g0 + 6)]
+    return out
+
+
+def decode_step_40(n_seq=64, tokens=131072, **kw):
+    """One decode token of every sequence through all 40 layers (report 4.2.1),
+    as the chains the layers form: the two sliding-window layers; each encoder
+    group (Full + 5 Reuse at ratio 2 over tokens / 2 entries, its own source
+    cache); the decoder layers 20..39 at ratio 1 over `tokens` entries with the
+    pool.  Returns the workloads in layer order."""
+    t = [np.array([tokens - 1], np.int64)] * n_seq
+    enc = encoder_schedule()
+    seed = 0xC5A20000 + CONFIG_IDS["decode_step_40"]
+    wls = [make_workload("step40_swa", seed, [tokens // 2] * n_seq, 1, enc[:2], ratio=2, q_pos=t, gen_kv=False, **kw)]
+    for gi, g0 in enumerate((2, 8, 14)):
+        sched = [x for x in enc if g0 <= x[0] < g0 + 6]
+        wls.append(make_workload(f"step40_enc{g0}", seed + 16 * (gi + 1), [tokens // 2] * n_seq, 1, sched, ratio=2,
+                                 q_pos=t, **kw))
+    wls.append(make_workload("step40_dec", seed + 64, [tokens] * n_seq, 1, decoder_schedule(), q_pos=t, **kw))
+    return wls
+
+
 def ragged_lengths(seed, n_seq, lo=4096, hi=1048576):
     """N_b = round(exp(U(ln lo, ln hi))), U from the counter generator."""
     out = np.empty(n_seq, np.int64)
@@ -252,7 +280,8 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
     return wl
 
 
-CONFIG_IDS = {"decode_c0": 0, "decode_c1": 1, "chain_c2": 2, "prefill_c3": 3, "ragged_c4": 4, "replay_c5": 5}
+CONFIG_IDS = {"decode_c0": 0, "decode_c1": 1, "chain_c2": 2, "prefill_c3": 3, "ragged_c4": 4, "replay_c5": 5,
+              "decode_step_40": 6}
 
 
 def config(name, **kw):

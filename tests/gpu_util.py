@@ -11,12 +11,13 @@ SCALE = 1.0 / math.sqrt(512.0)
 
 
 def dev(a, device="cuda"):
-    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
 class DevWorkload:
     def __init__(self, wl, device="cuda"):
         self.wl = wl
+        self.device = torch.device(device)
         self.batch = C.Batch.from_workload(wl, device)
         self.swa = C.SwaLayout.from_workload(wl, replay_s=getattr(wl, "replay_s", None), device=device)
         self.k_idx = dev(wl.k_idx, device)
@@ -37,7 +38,7 @@ def prepare_chain(dw, want_idx=True, want_lse=True, ws=None, pool=True):
     (call, outs, pools) where call() enqueues one csa2_layer_chain."""
     wl = dw.wl
     nq = wl.total_q
-    device = dw.kv.device
+    device = dw.device
     specs, outs = [], []
     for d in dw.layers:
         out = torch.empty((nq, wl.Hm, 512), dtype=torch.float32, device=device)

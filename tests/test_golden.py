@@ -54,6 +54,33 @@ def test_encoder_group_matches_pages():
     assert not any(L.build_pool for L in wl.layers)  # encoder Full layers build no pool
 
 
+def test_forty_layer_step_matches_pages():
+    """The encoder schedule and the 40-layer decode step: layers 0..39 once each,
+    the pure sliding-window layers first, the encoder groups at ratio 2 over
+    half the tokens, the decoder at ratio 1 over all of them."""
+    cfg = golden("pages_config.json")
+    enc = cfg["encoder"]
+    sched = synth.encoder_schedule()
+    assert [l for l, _, _ in sched] == list(range(0, enc["csa2_layers"][1] + 1))
+    assert [l for l, m, _ in sched if m == synth.MODE_SWA_ONLY] == enc["pure_swa_layers"]
+    csa2 = [(l, m) for l, m, _ in sched if m != synth.MODE_SWA_ONLY]
+    for i, (l, m) in enumerate(csa2):
+        assert m == MODES[enc["group"][i % enc["group_size"]]], l
+    assert not any(p for _, _, p in sched)
+    tokens = 1000
+    wls = synth.decode_step_40(n_seq=2, tokens=tokens, Hm=16)
+    layers = [L.index for wl in wls for L in wl.layers]
+    assert layers == list(range(40))
+    for wl in wls:
+        dec = wl.layers[0].index >= cfg["decoder"]["layers"][0]
+        assert wl.ratio == (cfg["decoder"]["ratio"] if dec else enc["ratio"])
+        assert list(wl.n_entries) == [tokens if dec else tokens // 2] * 2
+        assert list(wl.q_pos) == [tokens - 1] * 2
+    # every encoder group reads its own source cache
+    caches = [wl.k_idx.tobytes() for wl in wls[1:4]]
+    assert len(set(caches)) == 3
+
+
 def test_path_sizes_match_pages():
     cfg = golden("pages_config.json")
     wl = synth.config("decode_c0", n_entries=[64])

@@ -288,6 +288,25 @@ def test_layer_chain_matches_oracle(case):
             assert np.array_equal(pc.cpu().numpy(), r["pool_count"])
 
 
+@pytest.mark.gpu
+def test_decode_step_40_matches_oracle():
+    """One decode token through all 40 layers, as the five chains the layers
+    form (sliding-window layers, three encoder groups at ratio 2, the decoder
+    at ratio 1), each against the oracle."""
+    for wl in synth.decode_step_40(n_seq=2, tokens=6000, Hm=16):
+        dw = DevWorkload(wl)
+        outs, (pb, pp, pc), _ = run_chain(dw)
+        torch.cuda.synchronize()
+        ref = oracle.layer_chain(wl)
+        assert [o["layer"] for o in outs] == [r["layer"] for r in ref]
+        for o, r in zip(outs, ref):
+            assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"{wl.name} layer {r['layer']} indices"
+            assert_close_attn(o["out"].cpu().numpy(), r["out"], f"{wl.name} layer {r['layer']}")
+            np.testing.assert_allclose(o["lse"].cpu().numpy(), r["lse"], rtol=1e-4, atol=1e-4)
+            if "pool_pos" in r:
+                assert np.array_equal(pp.cpu().numpy(), r["pool_pos"])
+
+
 TIE_CASES = {
     # every score 0 (all head weights 0): each chunk keeps all its positions,
     # the rows overflow the candidate list and take the exact fallback
