@@ -307,8 +307,9 @@ def chain_bytes(wl, outs, pool_pos, pool_count):
     realised selections: the Full layer's scan (65 B per visible entry, read
     once per sequence) and query/weights; each Reindex layer's gathered
     indexer-K rows (the union of a sequence's pools, 65 B each); per layer and
-    row the gathered main-KV rows (272 B per selected entry), the SWA rows
-    (1,024 B), the main query, the output and the indices."""
+    row the gathered main-KV rows (272 B per selected entry; 288 B with E4M3
+    scales per 16 channels), the SWA rows (1,024 B), the main query, the
+    output and the indices."""
     import numpy as np
 
     H, Hm, K, W = wl.H, wl.Hm, wl.K, wl.W
@@ -329,7 +330,8 @@ def chain_bytes(wl, outs, pool_pos, pool_count):
                 total += len(u) * 65
             total += qw
         n_sel = (o["idx"].cpu().numpy() >= 0).sum(axis=1) if L.mode != synth_mode("SWA_ONLY") else 0
-        total += int(np.sum(n_sel) * 272 + n_swa.sum() * 1024) + wl.total_q * (Hm * 512 * 6 + K * 4)
+        kv_row = 288 if getattr(wl, "kv_fmt", 0) == 1 else 272
+        total += int(np.sum(n_sel) * kv_row + n_swa.sum() * 1024) + wl.total_q * (Hm * 512 * 6 + K * 4)
     return total
 
 
@@ -349,9 +351,11 @@ def bench_workloads(synth, C, torch, dev):
     from gpu_util import DevWorkload, prepare_chain
 
     res = {}
-    for name, reps in (("decode_c0", 20), ("chain_c2", 5), ("ragged_c4", 5), ("prefill_c3", 3), ("replay_c5", 3)):
+    # decode_c1_e4m3kv: decode_c1 with the report's main-KV scales (E4M3 per 16 channels)
+    for name, reps in (("decode_c0", 20), ("decode_c1_e4m3kv", 10), ("chain_c2", 5), ("ragged_c4", 5),
+                       ("prefill_c3", 3), ("replay_c5", 3)):
         t0 = time.time()
-        wl = synth.config(name)
+        wl = synth.config("decode_c1", kv_fmt=1) if name == "decode_c1_e4m3kv" else synth.config(name)
         dw = DevWorkload(wl, dev)
         call, outs, (pb, pp, pc) = prepare_chain(dw, want_idx=True, want_lse=False)
         call()

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, 1, 2, 3, 4
 CSA2_Q_FP4, CSA2_Q_FP8 = 0, 1
+CSA2_KV_MXFP4, CSA2_KV_E4M3_16 = 0, 1
 CSA2_MODE_SWA_ONLY, CSA2_MODE_FULL, CSA2_MODE_REINDEX, CSA2_MODE_REUSE = 0, 1, 2, 3
 CSA2_LAYER_BUILD_POOL = 1
 CSA2_WS_TOPK, CSA2_WS_BLOCK_POOL, CSA2_WS_SPARSE_ATTN, CSA2_WS_LAYER_CHAIN = 1, 2, 3, 4
@@ -42,7 +43,7 @@ class csa2_swa_layout(ctypes.Structure):
 
 class csa2_layer(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("flags", ctypes.c_int32), ("q_fmt", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("q_idx", _vp), ("q_sc", _vp), ("w", _vp), ("kv_fp4", _vp),
+                ("kv_fmt", ctypes.c_int32), ("q_idx", _vp), ("q_sc", _vp), ("w", _vp), ("kv_fp4", _vp),
                 ("kv_sc", _vp), ("k_fp4", _vp), ("k_sc", _vp), ("q_main", _vp), ("swa", _vp), ("out", _vp),
                 ("lse", _vp), ("idx_out", _vp)]
 
@@ -76,8 +77,8 @@ def lib():
         L.csa2_index_score.argtypes = [B, i32, i32, _vp, _vp, _vp, _vp, _vp, _vp, i32, _vp, i64, _vp, _vp]
         L.csa2_topk.argtypes = [B, _vp, i64, _vp, i32, _vp, i32, _vp, _vp, _vp, sz, _vp]
         L.csa2_block_pool.argtypes = [B, _vp, i64, i32, i32, _vp, _vp, _vp, _vp, sz, _vp]
-        L.csa2_gather_dequant.argtypes = [B, _vp, _vp, _vp, i32, _vp, _vp]
-        L.csa2_sparse_attn.argtypes = [B, i32, _vp, _vp, _vp, _vp, i32, _vp, S, f32, _vp, _vp, _vp, sz, _vp]
+        L.csa2_gather_dequant.argtypes = [B, i32, _vp, _vp, _vp, i32, _vp, _vp]
+        L.csa2_sparse_attn.argtypes = [B, i32, _vp, i32, _vp, _vp, _vp, i32, _vp, S, f32, _vp, _vp, _vp, sz, _vp]
         L.csa2_layer_chain.argtypes = [B, ctypes.POINTER(csa2_chain_params), i32, ctypes.POINTER(csa2_layer), S, _vp,
                                        _vp, _vp, _vp, sz, _vp]
         L.csa2_workspace_size.argtypes = [i32, B, i32, i32, i32]
@@ -225,17 +226,17 @@ def csa2_block_pool(batch, scores, block=8, max_blocks=2048, ws=None, stream=Non
     return blocks, pool, cnt
 
 
-def csa2_gather_dequant(batch, kv_fp4, kv_sc, idx, stream=None):
+def csa2_gather_dequant(batch, kv_fp4, kv_sc, idx, stream=None, kv_fmt=CSA2_KV_MXFP4):
     K = idx.shape[1]
     out = torch.empty((batch.total_q, K, 512), dtype=torch.uint16, device=idx.device)
-    st = lib().csa2_gather_dequant(ctypes.byref(batch.c), _ptr(kv_fp4), _ptr(kv_sc), _ptr(idx), K, _ptr(out),
-                                   _stream(stream))
+    st = lib().csa2_gather_dequant(ctypes.byref(batch.c), int(kv_fmt), _ptr(kv_fp4), _ptr(kv_sc), _ptr(idx), K,
+                                   _ptr(out), _stream(stream))
     _check(st, "csa2_gather_dequant")
     return out
 
 
 def csa2_sparse_attn(batch, q_bf16, kv_fp4, kv_sc, idx, swa_rows, swa_layout, softmax_scale, out=None, lse=None,
-                     want_lse=True, ws=None, split=True, stream=None):
+                     want_lse=True, ws=None, split=True, stream=None, kv_fmt=CSA2_KV_MXFP4):
     Hm = q_bf16.shape[1]
     dev = q_bf16.device
     if out is None:
@@ -244,7 +245,7 @@ def csa2_sparse_attn(batch, q_bf16, kv_fp4, kv_sc, idx, swa_rows, swa_layout, so
         lse = torch.empty((batch.total_q, Hm), dtype=torch.float32, device=dev)
     if ws is None and split:
         ws = workspace(csa2_workspace_size(CSA2_WS_SPARSE_ATTN, batch, idx.shape[1]), dev)
-    st = lib().csa2_sparse_attn(ctypes.byref(batch.c), Hm, _ptr(q_bf16), _ptr(kv_fp4), _ptr(kv_sc), _ptr(idx),
+    st = lib().csa2_sparse_attn(ctypes.byref(batch.c), Hm, _ptr(q_bf16), int(kv_fmt), _ptr(kv_fp4), _ptr(kv_sc), _ptr(idx),
                                 idx.shape[1], _ptr(swa_rows), ctypes.byref(swa_layout.c), float(softmax_scale),
                                 _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check(st, "csa2_sparse_attn")
@@ -259,6 +260,7 @@ def make_layers(specs):
         L.mode = sp["mode"]
         L.flags = sp.get("flags", 0)
         L.q_fmt = sp.get("q_fmt", CSA2_Q_FP4)
+        L.kv_fmt = sp.get("kv_fmt", CSA2_KV_MXFP4)
         for f in ("q_idx", "q_sc", "w", "kv_fp4", "kv_sc", "k_fp4", "k_sc", "q_main", "swa", "out", "lse", "idx_out"):
             setattr(L, f, _ptr(sp.get(f)))
     return arr

@@ -247,18 +247,20 @@ CSA2_API csa2_status csa2_block_pool(const csa2_batch* batch, const float* score
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
 
-CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, const uint8_t* kv_fp4, const uint8_t* kv_sc,
-                                         const int32_t* idx, int32_t K, uint16_t* out_bf16, hipStream_t stream) {
+CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, int32_t kv_fmt, const uint8_t* kv_fp4,
+                                         const uint8_t* kv_sc, const int32_t* idx, int32_t K, uint16_t* out_bf16,
+                                         hipStream_t stream) {
     Geometry g;
     csa2_status st = batch_geometry(batch, &g);
     if (st) return st;
+    if (kv_fmt != CSA2_KV_MXFP4 && kv_fmt != CSA2_KV_E4M3_16) return CSA2_ERR_UNSUPPORTED;
     if (!kv_fp4 || !kv_sc || !idx || !out_bf16) return CSA2_ERR_INVALID_ARG;
     if (K < 1 || K > 4096) return K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
-    hipError_t e = launch_gather_dequant(batch, g, kv_fp4, kv_sc, idx, K, out_bf16, stream);
+    hipError_t e = launch_gather_dequant(batch, g, kv_fmt, kv_fp4, kv_sc, idx, K, out_bf16, stream);
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
 
-CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16,
+CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16, int32_t kv_fmt,
                                       const uint8_t* kv_fp4, const uint8_t* kv_sc, const int32_t* idx, int32_t K,
                                       const uint16_t* swa_bf16, const csa2_swa_layout* swa, float softmax_scale,
                                       float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -266,13 +268,14 @@ CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const
     csa2_status st = batch_geometry(batch, &g);
     if (st) return st;
     if (!q_bf16 || !kv_fp4 || !kv_sc || !idx || !swa_bf16 || !out) return CSA2_ERR_INVALID_ARG;
+    if (kv_fmt != CSA2_KV_MXFP4 && kv_fmt != CSA2_KV_E4M3_16) return CSA2_ERR_UNSUPPORTED;
     if (Hm < 16 || Hm % 16) return Hm < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
     if (K < 1 || K > kMaxK) return K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
     if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return CSA2_ERR_INVALID_ARG;
     if ((st = check_swa(batch, swa))) return st;
     if (ws && ((uintptr_t)ws & 255)) return CSA2_ERR_WORKSPACE;
     AttnLaunch a{batch, g, Hm, q_bf16, kv_fp4, kv_sc, idx, K, swa_bf16, swa, softmax_scale, out, lse, ws,
-                 ws ? ws_bytes : 0};
+                 ws ? ws_bytes : 0, kv_fmt};
     hipError_t e = launch_sparse_attn(a, stream);
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
@@ -304,6 +307,7 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
             case CSA2_MODE_FULL:
                 if (!L.kv_fp4 || !L.kv_sc || !L.k_fp4 || !L.k_sc || !L.q_idx || !L.q_sc || !L.w) return CSA2_ERR_INVALID_ARG;
                 if (L.q_fmt != CSA2_Q_FP4 && L.q_fmt != CSA2_Q_FP8) return CSA2_ERR_INVALID_ARG;
+                if (L.kv_fmt != CSA2_KV_MXFP4 && L.kv_fmt != CSA2_KV_E4M3_16) return CSA2_ERR_UNSUPPORTED;
                 have_kv = have_idx = true;
                 if (L.flags & CSA2_LAYER_BUILD_POOL) ++pool_layers;
                 break;
@@ -466,7 +470,7 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
             kvs = (const uint8_t*)L.swa;
         }
         AttnLaunch aa{batch, g, p->Hm, L.q_main, kv, kvs, use_idx, p->K, L.swa, swa, p->softmax_scale, L.out, L.lse,
-                      base + cw.attn, cw.attn_bytes};
+                      base + cw.attn, cw.attn_bytes, src ? src->kv_fmt : CSA2_KV_MXFP4};
         if ((e = launch_sparse_attn(aa, stream)) != hipSuccess) return hip_fail(e);
         if (L.idx_out) {
             if ((e = hipMemcpyAsync(L.idx_out, use_idx, (size_t)nidx * 4, hipMemcpyDeviceToDevice, stream)) != hipSuccess)

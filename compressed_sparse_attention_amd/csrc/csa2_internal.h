@@ -331,12 +331,13 @@ struct AttnLaunch {
     float* lse;
     void* ws;                   // partial results when the key blocks are split (may be NULL)
     size_t ws_bytes;
+    int kv_fmt;                 // CSA2_KV_* of kv_sc
 };
 // key-block splits the attention would use, and the workspace they need
 int attn_splits(const Geometry& g, int Hm, int K, int W);
 size_t attn_ws_bytes(const Geometry& g, int Hm, int S);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
-hipError_t launch_gather_dequant(const csa2_batch* b, Geometry g, const uint8_t* kv, const uint8_t* kv_sc,
+hipError_t launch_gather_dequant(const csa2_batch* b, Geometry g, int kv_fmt, const uint8_t* kv, const uint8_t* kv_sc,
                                  const int32_t* idx, int K, uint16_t* out, hipStream_t s);
 
 }  // namespace csa2

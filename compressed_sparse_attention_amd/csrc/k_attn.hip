@@ -35,7 +35,35 @@ __device__ __forceinline__ v4i fp4x8_to_bf16(uint32_t codes, float scale) {
                __builtin_bit_cast(int, d)};
 }
 
+// The same for a scale that need not be a power of two: the conversions'
+// scale operand applies only its exponent, so the values are converted to f32
+// at unit scale, multiplied by the scale (exact: at most six significant bits)
+// and cut to bf16 (exact for the same reason).
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ int bf16_pair_mul(v2f_t f, float scale) {
+    const uint32_t a = __float_as_uint(f[0] * scale), b = __float_as_uint(f[1] * scale);
+    return (int)((a >> 16) | (b & 0xFFFF0000u));
+}
+__device__ __forceinline__ v4i fp4x8_to_bf16_mul(uint32_t codes, float scale) {
+    return v4i{bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0), scale),
+               bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1), scale),
+               bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2), scale),
+               bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3), scale)};
+}
+
 __device__ __forceinline__ float e8m0_f32(uint32_t e) { return __builtin_ldexpf(1.0f, (int)e - 127); }
+
+// OCP E4M3 ("FN": bias 7, no infinities; the NaN codes are not allowed in a
+// scale) -> f32, exactly: normal codes by their bits, subnormals m * 2^-9.
+__device__ __forceinline__ float e4m3_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (b & 0x80u) ? -v : v;
+}
+
+// Main-KV scale formats: kKvMx one E8M0 per 32 channels (16 bytes a row),
+// kKvE4 one E4M3 per 16 channels (32 bytes a row; the report's section 2.4.4).
+enum : int { kKvMx = 0, kKvE4 = 1 };
 
 // Reductions over lane pairs l, l ^ D (D = 16 or 32) on the VALU: the swap
 // leaves this lane's value and its partner's in the two results (in some order).
@@ -59,6 +87,7 @@ __device__ __forceinline__ float xor_sum(float x) {
 // ---------------------------------------------------------------------------
 // gather + dequantise: grid (K, total_q), 64 threads, 8 channels per thread
 // ---------------------------------------------------------------------------
+template <int KVF>
 __global__ __launch_bounds__(64) void k_gather_dequant(const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
                                                        const int64_t* __restrict__ entry_off,
                                                        const int32_t* __restrict__ row_seq,
@@ -71,7 +100,10 @@ __global__ __launch_bounds__(64) void k_gather_dequant(const uint8_t* __restrict
     if (j >= 0 && j < entry_off[b + 1] - entry_off[b]) {  // out-of-range entries read as empty
         const int64_t e = entry_off[b] + j;
         const uint32_t codes = *reinterpret_cast<const uint32_t*>(kv + e * 256 + 4 * t);
-        v = fp4x8_to_bf16(codes, e8m0_f32(kv_sc[e * 16 + (8 * t) / 32]));
+        if constexpr (KVF == kKvE4)
+            v = fp4x8_to_bf16_mul(codes, e4m3_f32(kv_sc[e * 32 + (8 * t) / 16]));
+        else
+            v = fp4x8_to_bf16(codes, e8m0_f32(kv_sc[e * 16 + (8 * t) / 32]));
     }
     *reinterpret_cast<v4i*>(out + ((int64_t)row * K + s) * 512 + 8 * t) = v;
 }
@@ -96,7 +128,7 @@ constexpr int KB = 64;
 constexpr int LROW = 512 + 8;  // LDS row stride of the staged keys in bf16 (16 B of padding)
 constexpr int SLROW = KB + 4;  // LDS row stride of the logits in floats
 
-template <int NPIPE>
+template <int NPIPE, int KVF>
 __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
     const int32_t* __restrict__ idx, int K, const uint16_t* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
@@ -212,9 +244,10 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     // output), l_lse the fp32 weights (it gives the log-sum-exp)
     float m_run = -INFINITY, l_run = 0.0f, l_lse = 0.0f;
 
-    // FP4 rows of a selected key, fetched one iteration ahead
+    // FP4 rows of a selected key, fetched one iteration ahead, with their
+    // scales: 4 E8M0 (one per 32 channels) or 8 E4M3 (one per 16 channels)
     v4i pc[NB];
-    uint32_t psc = 0;
+    uint32_t psc = 0, psc2 = 0;
     auto fetch = [&](int blk) {
         const int vk = KB * blk + skey;
         if (blk < blk1 && vk >= n_swa && vk < n_keys) {
@@ -224,7 +257,13 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
                 const uint8_t* src = kv + e * 256 + (CP / 2) * part;
 #pragma unroll
                 for (int i = 0; i < NB; ++i) pc[i] = ld16(src + 16 * i);
-                psc = *reinterpret_cast<const uint32_t*>(kv_sc + e * 16 + 4 * part);
+                if constexpr (KVF == kKvE4) {
+                    const uint2 w2 = *reinterpret_cast<const uint2*>(kv_sc + e * 32 + 8 * part);
+                    psc = w2.x;
+                    psc2 = w2.y;
+                } else {
+                    psc = *reinterpret_cast<const uint32_t*>(kv_sc + e * 16 + 4 * part);
+                }
             }
         }
     };
@@ -248,11 +287,21 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
         } else if (vk < n_keys && kidx[vk - n_swa] >= 0) {
             valid = 1;
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {  // 32 channels per scale
-                const float sc = e8m0_f32((psc >> (8 * i)) & 255u);
+            for (int i = 0; i < NB; ++i) {  // 32 channels
+                if constexpr (KVF == kKvE4) {  // a scale per 16 channels: bytes 2i, 2i + 1 of psc:psc2
+                    const uint32_t w = i < 2 ? psc : psc2;
+                    const float s0 = e4m3_f32((w >> (16 * (i & 1))) & 255u);
+                    const float s1 = e4m3_f32((w >> (16 * (i & 1) + 8)) & 255u);
 #pragma unroll
-                for (int d = 0; d < 4; ++d)
-                    *reinterpret_cast<v4i*>(dst + 32 * i + 8 * d) = fp4x8_to_bf16((uint32_t)pc[i][d], sc);
+                    for (int d = 0; d < 4; ++d)
+                        *reinterpret_cast<v4i*>(dst + 32 * i + 8 * d) =
+                            fp4x8_to_bf16_mul((uint32_t)pc[i][d], d < 2 ? s0 : s1);
+                } else {
+                    const float sc = e8m0_f32((psc >> (8 * i)) & 255u);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        *reinterpret_cast<v4i*>(dst + 32 * i + 8 * d) = fp4x8_to_bf16((uint32_t)pc[i][d], sc);
+                }
             }
         }
         if (!valid) {
@@ -492,10 +541,14 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_gather_dequant(const csa2_batch* b, Geometry g, const uint8_t* kv, const uint8_t* kv_sc,
+hipError_t launch_gather_dequant(const csa2_batch* b, Geometry g, int kv_fmt, const uint8_t* kv, const uint8_t* kv_sc,
                                  const int32_t* idx, int K, uint16_t* out, hipStream_t s) {
-    hipLaunchKernelGGL(k_gather_dequant, dim3(K, g.total_q), dim3(64), 0, s, kv, kv_sc, b->d_entry_off, b->d_row_seq,
-                       idx, K, out);
+    if (kv_fmt == kKvE4)
+        hipLaunchKernelGGL(k_gather_dequant<kKvE4>, dim3(K, g.total_q), dim3(64), 0, s, kv, kv_sc, b->d_entry_off,
+                           b->d_row_seq, idx, K, out);
+    else
+        hipLaunchKernelGGL(k_gather_dequant<kKvMx>, dim3(K, g.total_q), dim3(64), 0, s, kv, kv_sc, b->d_entry_off,
+                           b->d_row_seq, idx, K, out);
     return hipGetLastError();
 }
 
@@ -522,13 +575,18 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
     float* part = S > 1 ? (float*)a.ws : nullptr;
     // two pipes per workgroup only where the grid leaves most CUs idle (latency
     // is all that counts there); otherwise one pipe, two workgroups per CU
-#define CSA2_ATTN(NP)                                                                                             \
-    hipLaunchKernelGGL(k_sparse_attn<NP>, dim3(nblk), dim3(256 * NP), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, \
+#define CSA2_ATTN(NP, KF)                                                                                          \
+    hipLaunchKernelGGL((k_sparse_attn<NP, KF>), dim3(nblk), dim3(256 * NP), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, \
                        a.swa, a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,   \
                        a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q,  \
                        n_hg, S, part)
-    if (nblk <= kAttnTwoPipeWgs) CSA2_ATTN(2);
-    else CSA2_ATTN(1);
+    if (a.kv_fmt == kKvE4) {
+        if (nblk <= kAttnTwoPipeWgs) CSA2_ATTN(2, kKvE4);
+        else CSA2_ATTN(1, kKvE4);
+    } else {
+        if (nblk <= kAttnTwoPipeWgs) CSA2_ATTN(2, kKvMx);
+        else CSA2_ATTN(1, kKvMx);
+    }
 #undef CSA2_ATTN
     if (S > 1) {
         const dim3 cg((unsigned)(a.g.total_q * a.Hm));

@@ -33,7 +33,10 @@
  * Layouts (entries of all sequences packed back to back; entry_off gives the
  * first entry of each sequence):
  *   main KV     kv_fp4 [total_entries][256] u8 (512 E2M1 latent channels)
- *               kv_sc  [total_entries][16]  u8 (one E8M0 per 32 channels)
+ *               kv_sc  CSA2_KV_MXFP4:    [total_entries][16] u8 (one E8M0 per 32 channels)
+ *                      CSA2_KV_E4M3_16:  [total_entries][32] u8 (one E4M3 per 16 channels: the
+ *                      report's main-KV format, section 2.4.4, NVFP4's layout without its
+ *                      second-level global scale)
  *   indexer K   k_fp4  [total_entries][64]  u8 (128 E2M1 channels)
  *               k_sc   [total_entries]      u8 (one E8M0 per row)
  *   indexer q   CSA2_Q_FP4: [total_q][H][64] u8, CSA2_Q_FP8: [total_q][H][128] u8
@@ -71,6 +74,9 @@ typedef int32_t csa2_status;
 
 #define CSA2_Q_FP4 0
 #define CSA2_Q_FP8 1
+
+#define CSA2_KV_MXFP4 0    /* main-KV scales: E8M0 per 32 channels */
+#define CSA2_KV_E4M3_16 1  /* main-KV scales: E4M3 per 16 channels */
 
 #define CSA2_MODE_SWA_ONLY 0
 #define CSA2_MODE_FULL 1
@@ -181,12 +187,15 @@ CSA2_API csa2_status csa2_block_pool(const csa2_batch* batch, const float* score
                                      int32_t* pool_count, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- gather + dequantise --------------------------------------------------
- * out[r][s][c] = E2M1(kv_fp4[e][c]) * 2^(kv_sc[e][c/32]-127) as bf16 (exact),
- * e = entry_off[seq(r)] + idx[r][s]; rows for idx == -1 are zero.  Main KV is
- * dequantised before attention (report 2.4.4).
+ * out[r][s][c] = E2M1(kv_fp4[e][c]) * scale(e, c) as bf16 (exact: at most six
+ * significant bits), e = entry_off[seq(r)] + idx[r][s]; rows for idx == -1
+ * are zero.  scale(e, c) = 2^(kv_sc[e][c/32]-127) for CSA2_KV_MXFP4 and
+ * E4M3(kv_sc[e][c/16]) for CSA2_KV_E4M3_16.  Main KV is dequantised before
+ * attention (report 2.4.4).
  * out_bf16: [total_q][K][512] (device).  Supported: 1 <= K <= 4096. */
-CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, const uint8_t* kv_fp4, const uint8_t* kv_sc,
-                                         const int32_t* idx, int32_t K, uint16_t* out_bf16, hipStream_t stream);
+CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, int32_t kv_fmt, const uint8_t* kv_fp4,
+                                         const uint8_t* kv_sc, const int32_t* idx, int32_t K, uint16_t* out_bf16,
+                                         hipStream_t stream);
 
 /* ---- sparse latent attention ---------------------------------------------
  * For every query row r and head h: keys = the selected main-KV latents
@@ -197,6 +206,7 @@ CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, const uint8_t*
  * concatenated with the SWA KV for core attention).
  *   out[r][h] = sum_u softmax_u(scale * q[r][h] . key_u) * key_u   (fp32)
  *   lse[r][h] = log sum_u exp(scale * q[r][h] . key_u)               (optional)
+ * Main-KV values are those of csa2_gather_dequant with the same kv_fmt.
  * q_bf16: [total_q][Hm][512]; swa_bf16: [rows][512] laid out by `swa`;
  * out: [total_q][Hm][512] f32; lse: [total_q][Hm] f32 or NULL (all device).
  * Supported: Hm a multiple of 16, 1 <= K <= 2048, window <= 1024.
@@ -205,7 +215,7 @@ CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, const uint8_t*
  * batch is small and merge the parts; with less (or NULL) it splits less (or
  * not at all).  Results agree either way within the tolerance of a softmax
  * merge, not bit for bit. */
-CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16,
+CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16, int32_t kv_fmt,
                                       const uint8_t* kv_fp4, const uint8_t* kv_sc, const int32_t* idx, int32_t K,
                                       const uint16_t* swa_bf16, const csa2_swa_layout* swa, float softmax_scale,
                                       float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -223,7 +233,7 @@ typedef struct csa2_layer {
     int32_t mode;                /* CSA2_MODE_* */
     int32_t flags;               /* CSA2_LAYER_BUILD_POOL (FULL only) */
     int32_t q_fmt;               /* CSA2_Q_FP4 / CSA2_Q_FP8 (FULL, REINDEX) */
-    int32_t reserved;
+    int32_t kv_fmt;              /* CSA2_KV_* of kv_sc (FULL: the layers up to the next Full layer read it) */
     const void* q_idx;           /* (device) indexer q (FULL, REINDEX) */
     const uint8_t* q_sc;         /* (device) [total_q][H] */
     const float* w;              /* (device) [total_q][H] */

@@ -351,10 +351,15 @@ void orc_block_pool(int64_t total_q, const float* scores, int64_t score_stride, 
 /* attention; [N4] Figure 4 reading: "Selection" reads the selected entries)  */
 /* ------------------------------------------------------------------------ */
 
-/* Main-KV entry e, channel c: E2M1(kv[e][c]) * 2^(sc[e][c/32] - 127). */
-static double kv_value(const uint8_t* kv, const uint8_t* kv_sc, int64_t e, int ch) {
+/* Main-KV entry e, channel c, for the two scale formats:
+ *   fmt 0 (OCP MXFP4):  E2M1(kv[e][c]) * 2^(sc[e][c/32] - 127), 16 scale bytes per row;
+ *   fmt 1 ([R] 2.4.4):  E2M1(kv[e][c]) * E4M3(sc[e][c/16]), 32 scale bytes per row
+ *                       (NVFP4's layout without its second-level global scale).
+ * Either product has at most six significant bits, so it is exact in bf16. */
+static double kv_value(const uint8_t* kv, const uint8_t* kv_sc, int kv_fmt, int64_t e, int ch) {
     uint8_t byte = kv[e * 256 + ch / 2];
     uint8_t nib = (ch & 1) ? (byte >> 4) : (byte & 15);
+    if (kv_fmt == 1) return orc_e2m1(nib) * orc_e4m3(kv_sc[e * 32 + ch / 16]);
     return orc_e2m1(nib) * orc_e8m0(kv_sc[e * 16 + ch / 32]);
 }
 
@@ -362,14 +367,14 @@ static double kv_value(const uint8_t* kv, const uint8_t* kv_sc, int64_t e, int c
  * most two significant bits, so it is exact in bf16: the bits are those of
  * the binary32 value with the low half dropped (which is zero). */
 void orc_gather_dequant(int64_t total_q, const int32_t* row_seq, const int64_t* entry_off, const uint8_t* kv,
-                        const uint8_t* kv_sc, const int32_t* idx, int K, uint16_t* out) {
+                        const uint8_t* kv_sc, int kv_fmt, const int32_t* idx, int K, uint16_t* out) {
     for (int64_t r = 0; r < total_q; ++r)
         for (int s = 0; s < K; ++s) {
             int32_t j = idx[r * K + s];
             uint16_t* o = out + (r * K + s) * 512;
             for (int ch = 0; ch < 512; ++ch) {
                 if (j < 0) { o[ch] = 0; continue; }
-                float f = (float)kv_value(kv, kv_sc, entry_off[row_seq[r]] + j, ch);
+                float f = (float)kv_value(kv, kv_sc, kv_fmt, entry_off[row_seq[r]] + j, ch);
                 uint32_t u;
                 memcpy(&u, &f, 4);
                 o[ch] = (uint16_t)(u >> 16);
@@ -390,6 +395,7 @@ typedef struct {
     const uint16_t* q; /* [total_q][Hm][512] bf16 */
     int Hm;
     const uint8_t *kv, *kv_sc;
+    int kv_fmt;
     const int32_t* idx;
     int K;
     const uint16_t* swa; /* [rows][512] bf16 */
@@ -416,7 +422,8 @@ static void attn_row(void* p, int64_t r) {
     for (int s = 0; s < c->K; ++s) {
         int32_t j = c->idx[r * c->K + s];
         if (j < 0) continue;
-        for (int ch = 0; ch < 512; ++ch) keys[n * 512 + ch] = kv_value(c->kv, c->kv_sc, c->entry_off[b] + j, ch);
+        for (int ch = 0; ch < 512; ++ch)
+            keys[n * 512 + ch] = kv_value(c->kv, c->kv_sc, c->kv_fmt, c->entry_off[b] + j, ch);
         ++n;
     }
     for (int64_t u = u_lo; u <= t; ++u) {
@@ -452,10 +459,11 @@ static void attn_row(void* p, int64_t r) {
 }
 
 void orc_sparse_attn(int64_t total_q, const int32_t* row_seq, const int32_t* q_pos, const int64_t* entry_off,
-                     const uint16_t* q, int Hm, const uint8_t* kv, const uint8_t* kv_sc, const int32_t* idx, int K,
+                     const uint16_t* q, int Hm, const uint8_t* kv, const uint8_t* kv_sc, int kv_fmt, const int32_t* idx,
+                     int K,
                      const uint16_t* swa, const int64_t* swa_row_off, const int32_t* swa_pos0, int W,
                      const int32_t* replay_s, double scale, float* out, float* lse, int nthreads) {
-    attn_ctx c = {row_seq, q_pos, entry_off, q, Hm, kv, kv_sc, idx, K, swa, swa_row_off, swa_pos0, W, replay_s,
+    attn_ctx c = {row_seq, q_pos, entry_off, q, Hm, kv, kv_sc, kv_fmt, idx, K, swa, swa_row_off, swa_pos0, W, replay_s,
                   scale, out, lse};
     parallel_for(total_q, nthreads, attn_row, &c);
 }

@@ -59,9 +59,11 @@ def lib():
         u64, i64, i32, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         L.csa2synth_normal_f32.argtypes = [u64, u64, i64, i64, vp]
         L.csa2synth_uniform_f32.argtypes = [u64, u64, i64, i64, vp]
+        L.csa2synth_normal_f64.argtypes = [u64, u64, i64, i64, vp]
         L.csa2synth_normal_bf16.argtypes = [u64, u64, i64, i64, vp]
         L.csa2synth_mxfp4_rows.argtypes = [u64, u64, i64, i64, i32, i32, vp, vp]
         L.csa2synth_e4m3_rows.argtypes = [u64, u64, i64, i64, i32, vp, vp]
+        L.csa2synth_e2m1_e4m3_rows.argtypes = [u64, u64, i64, i64, i32, vp, vp]
         L.csa2synth_encode_e2m1.argtypes = [ctypes.c_double]
         L.csa2synth_encode_e2m1.restype = ctypes.c_uint8
         L.csa2synth_encode_e4m3.argtypes = [ctypes.c_double]
@@ -84,6 +86,12 @@ def _ptr(a: np.ndarray):
 def normal_f32(seed, tid, n, off=0):
     out = np.empty(n, np.float32)
     lib().csa2synth_normal_f32(seed, tid, off, n, _ptr(out))
+    return out
+
+
+def normal_f64(seed, tid, n, off=0):
+    out = np.empty(n, np.float64)
+    lib().csa2synth_normal_f64(seed, tid, off, n, _ptr(out))
     return out
 
 
@@ -111,6 +119,15 @@ def e4m3_rows(seed, tid, nrows, row_len, row0=0):
     codes = np.empty((nrows, row_len), np.uint8)
     scales = np.empty((nrows,), np.uint8)
     rc = lib().csa2synth_e4m3_rows(seed, tid, row0, nrows, row_len, _ptr(codes), _ptr(scales))
+    assert rc == 0
+    return codes, scales
+
+
+def e2m1_e4m3_rows(seed, tid, nrows, row_len, row0=0):
+    """E2M1 rows with one E4M3 scale per 16 values (the report's main-KV format)."""
+    codes = np.empty((nrows, row_len // 2), np.uint8)
+    scales = np.empty((nrows, row_len // 16), np.uint8)
+    rc = lib().csa2synth_e2m1_e4m3_rows(seed, tid, row0, nrows, row_len, _ptr(codes), _ptr(scales))
     assert rc == 0
     return codes, scales
 
@@ -161,6 +178,7 @@ class Workload:
     kv_sc: np.ndarray = None   # [sumN][16] u8
     layers: List[Layer] = field(default_factory=list)
     replay_s: Optional[np.ndarray] = None  # [n_seq] i32 SWA replay start per sequence (None: 0)
+    kv_fmt: int = 0                        # main-KV scales: 0 E8M0 per 32 channels, 1 E4M3 per 16 channels
 
     @property
     def n_seq(self):
@@ -227,12 +245,15 @@ def ragged_lengths(seed, n_seq, lo=4096, hi=1048576):
 
 
 def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=64, Hm=64, K=512, W=128,
-                  block=8, max_blocks=2048, q_fmt=Q_FP4, q_pos=None, gen_kv=True, gen_layers=True, replay_s=None):
+                  block=8, max_blocks=2048, q_fmt=Q_FP4, q_pos=None, gen_kv=True, gen_layers=True, replay_s=None,
+                  kv_fmt=0):
     """Build a workload.  n_entries: per-sequence entry counts.  queries_per_seq:
     T (same for all sequences).  q_pos: explicit token positions per sequence
     (list of arrays) or None for the decode shape t = N*ratio - T + i.
     schedule: list of (layer index, mode, build_pool).  replay_s: per-sequence
-    SWA replay start s (a query at t sees window rows max(s, t - W + 1) .. t)."""
+    SWA replay start s (a query at t sees window rows max(s, t - W + 1) .. t).
+    kv_fmt: main-KV scales, 0 = OCP MXFP4 (E8M0 per 32 channels), 1 = the
+    report's E4M3 per 16 channels."""
     n_entries = np.asarray(n_entries, np.int64)
     n_seq = len(n_entries)
     entry_off = np.zeros(n_seq + 1, np.int64)
@@ -254,11 +275,15 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
                   row_seq, swa_row_off, swa_pos0, swa_len)
     if replay_s is not None:
         wl.replay_s = np.ascontiguousarray(replay_s, np.int32)
+    wl.kv_fmt = int(kv_fmt)
     total = int(entry_off[-1])
     if gen_kv:
         wl.k_idx, ksc = mxfp4_rows(seed, TID_K, total, 128, 128)
         wl.k_sc = np.ascontiguousarray(ksc.reshape(total))
-        wl.kv, wl.kv_sc = mxfp4_rows(seed, TID_KV, total, 512, 32)
+        if kv_fmt == 1:
+            wl.kv, wl.kv_sc = e2m1_e4m3_rows(seed, TID_KV, total, 512)
+        else:
+            wl.kv, wl.kv_sc = mxfp4_rows(seed, TID_KV, total, 512, 32)
     nq = len(q_pos_all)
     swa_rows = int(swa_len.sum())
     for (li, mode, pool) in schedule:

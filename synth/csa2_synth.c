@@ -98,6 +98,13 @@ static uint8_t e4m3_code(double v) {
     return (uint8_t)(s | (be << 3) | (m - 8));
 }
 
+/* value of an E4M3 code (finite codes only) */
+static double e4m3_value(uint8_t c) {
+    int e = (c >> 3) & 15, m = c & 7;
+    double mag = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return (c & 0x80) ? -mag : mag;
+}
+
 static uint16_t bf16_rne(float f) {
     uint32_t u;
     memcpy(&u, &f, 4);
@@ -115,7 +122,7 @@ static int ilog2_floor(double a) {
 /* ---- threaded row loops -------------------------------------------------- */
 
 typedef struct {
-    int kind; /* 0 normal f32, 1 uniform f32, 2 bf16 normal, 3 mxfp4 rows, 4 e4m3 rows */
+    int kind; /* 0 normal f32, 1 uniform f32, 2 bf16 normal, 3 mxfp4 rows, 4 e4m3 rows, 5 e2m1 + e4m3/16 rows */
     uint64_t seed, tid;
     int64_t row0, nrows;
     int row_len, block;
@@ -185,6 +192,38 @@ static void run_range(const job_t* j, int64_t lo, int64_t hi) {
         free(v);
         break;
     }
+    case 6: {
+        double* o = (double*)j->out;
+        for (int64_t i = lo; i < hi; ++i) o[i] = normal(hash3(j->seed, j->tid, (uint64_t)(j->row0 + i)));
+        break;
+    }
+    case 5: { /* E2M1 rows with one E4M3 scale per 16 values: X = E4M3(amax / 6) (RNE), a block
+               * whose X would be 0 takes the smallest step 2^-9; values E2M1(x / X) (RNE, saturating) */
+        uint8_t* o = (uint8_t*)j->out;
+        int nb = j->row_len / 16;
+        double* v = (double*)malloc(sizeof(double) * (size_t)j->row_len);
+        for (int64_t r = lo; r < hi; ++r) {
+            uint64_t base = (uint64_t)(j->row0 + r) * (uint64_t)j->row_len;
+            for (int c = 0; c < j->row_len; ++c) v[c] = normal(hash3(j->seed, j->tid, base + (uint64_t)c));
+            uint8_t* orow = o + r * (j->row_len / 2);
+            for (int b = 0; b < nb; ++b) {
+                double amax = 0.0;
+                for (int c = 0; c < 16; ++c) amax = fmax(amax, fabs(v[b * 16 + c]));
+                uint8_t sc = e4m3_code(amax / 6.0);
+                if ((sc & 0x7F) == 0) sc = 0x01;
+                j->scales[r * nb + b] = sc;
+                double X = e4m3_value(sc);
+                for (int c = 0; c < 16; c += 2) {
+                    int idx = b * 16 + c;
+                    uint8_t lo4 = e2m1_code(v[idx] / X);
+                    uint8_t hi4 = e2m1_code(v[idx + 1] / X);
+                    orow[idx / 2] = (uint8_t)(lo4 | (hi4 << 4));
+                }
+            }
+        }
+        free(v);
+        break;
+    }
     }
 }
 
@@ -230,6 +269,13 @@ void csa2synth_normal_f32(uint64_t seed, uint64_t tid, int64_t off, int64_t n, f
     run(&j, n);
 }
 
+/* the same N(0,1) draws in double (what the encoders quantise), for tests */
+void csa2synth_normal_f64(uint64_t seed, uint64_t tid, int64_t off, int64_t n, double* out) {
+    job_t j = {0};
+    j.kind = 6; j.seed = seed; j.tid = tid; j.row0 = off; j.out = out;
+    run(&j, n);
+}
+
 void csa2synth_uniform_f32(uint64_t seed, uint64_t tid, int64_t off, int64_t n, float* out) {
     job_t j = {0};
     j.kind = 1; j.seed = seed; j.tid = tid; j.row0 = off; j.out = out;
@@ -261,6 +307,19 @@ int csa2synth_e4m3_rows(uint64_t seed, uint64_t tid, int64_t row0, int64_t nrows
     if (row_len <= 0) return 1;
     job_t j = {0};
     j.kind = 4; j.seed = seed; j.tid = tid; j.row0 = row0; j.row_len = row_len;
+    j.out = codes; j.scales = scales;
+    run(&j, nrows);
+    return 0;
+}
+
+/* nrows rows of row_len N(0,1) values as packed E2M1 codes [nrows][row_len/2]
+ * with one E4M3 scale per 16 values [nrows][row_len/16] (the report's main-KV
+ * cache format, section 2.4.4: NVFP4's layout without its global scale). */
+int csa2synth_e2m1_e4m3_rows(uint64_t seed, uint64_t tid, int64_t row0, int64_t nrows, int row_len, uint8_t* codes,
+                             uint8_t* scales) {
+    if (row_len <= 0 || row_len % 16) return 1;
+    job_t j = {0};
+    j.kind = 5; j.seed = seed; j.tid = tid; j.row0 = row0; j.row_len = row_len;
     j.out = codes; j.scales = scales;
     run(&j, nrows);
     return 0;

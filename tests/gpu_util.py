@@ -48,7 +48,7 @@ def prepare_chain(dw, want_idx=True, want_lse=True, ws=None, pool=True):
               "q_idx": d["q_idx"], "q_sc": d["q_sc"], "w": d["w"], "q_main": d["q_main"], "swa": d["swa"],
               "out": out, "lse": lse, "idx_out": idx}
         if d["mode"] == C.CSA2_MODE_FULL:
-            sp.update(kv_fp4=dw.kv, kv_sc=dw.kv_sc, k_fp4=dw.k_idx, k_sc=dw.k_sc)
+            sp.update(kv_fp4=dw.kv, kv_sc=dw.kv_sc, k_fp4=dw.k_idx, k_sc=dw.k_sc, kv_fmt=getattr(wl, "kv_fmt", 0))
         specs.append(sp)
         outs.append({"layer": d["index"], "out": out, "lse": lse, "idx": idx})
     layers = C.make_layers(specs)

@@ -139,9 +139,11 @@ def _swa(window, row_off, pos0, length, replay=None):
 def test_sparse_attn_validation():
     L = C.lib()
     b = HostBatch([1000], [[999]])
-    attn = lambda Hm=64, K=512, sw=None, scale=0.04: L.csa2_sparse_attn(
-        ctypes.byref(b.c), Hm, FAKE, FAKE, FAKE, FAKE, K, FAKE, ctypes.byref(sw), scale, FAKE, None, None, 0, None)
+    attn = lambda Hm=64, K=512, sw=None, scale=0.04, kv_fmt=0: L.csa2_sparse_attn(
+        ctypes.byref(b.c), Hm, FAKE, kv_fmt, FAKE, FAKE, FAKE, K, FAKE, ctypes.byref(sw), scale, FAKE, None, None, 0,
+        None)
     ok = _swa(128, [0], [872], [128])
+    assert attn(kv_fmt=2, sw=ok) == C.CSA2_ERR_UNSUPPORTED  # main-KV scales: E8M0/32 or E4M3/16 only
     assert attn(Hm=40, sw=ok) == C.CSA2_ERR_UNSUPPORTED
     assert attn(K=0, sw=ok) == C.CSA2_ERR_INVALID_ARG
     assert attn(scale=0.0, sw=ok) == C.CSA2_ERR_INVALID_ARG

@@ -192,17 +192,20 @@ def test_block_pool_bitwise():
     assert np.array_equal(cnt.cpu().numpy(), rc)
 
 
-def test_gather_dequant_bitwise():
-    wl = synth.config("decode_c1", n_seq=3, n=5000, Hm=16)
+@pytest.mark.parametrize("kv_fmt", [0, 1])
+def test_gather_dequant_bitwise(kv_fmt):
+    """kv_fmt 0: E8M0 per 32 channels; 1: the report's E4M3 per 16 channels."""
+    wl = synth.config("decode_c1", n_seq=3, n=5000, Hm=16, kv_fmt=kv_fmt)
     dw = DevWorkload(wl)
     rng = np.random.default_rng(2)
     idx = np.stack([np.sort(rng.choice(5000, 512, replace=False)) for _ in range(3)]).astype(np.int32)
     idx[1, 400:] = -1
-    got = C.csa2_gather_dequant(dw.batch, dw.kv, dw.kv_sc, dev(idx))
+    got = C.csa2_gather_dequant(dw.batch, dw.kv, dw.kv_sc, dev(idx), kv_fmt=kv_fmt)
     assert np.array_equal(got.cpu().numpy(), oracle.gather_dequant(wl, idx))
 
 
-ATTN_CASES = ["decode", "short_ctx", "ragged_t4", "swa_only", "replay", "sparse_idx", "swa_only_h64", "replay_h64"]
+ATTN_CASES = ["decode", "short_ctx", "ragged_t4", "swa_only", "replay", "sparse_idx", "swa_only_h64", "replay_h64",
+              "decode_e4m3kv", "small_e4m3kv"]
 
 
 @pytest.mark.parametrize("case", ATTN_CASES)
@@ -211,6 +214,10 @@ def test_sparse_attn_tolerance(case):
     replay = None
     if case == "decode":
         wl = synth.config("decode_c1", n_seq=3, n=6000, Hm=64)
+    elif case == "decode_e4m3kv":  # the report's main-KV scales (E4M3 per 16 channels), big grid
+        wl = synth.config("decode_c1", n_seq=3, n=6000, Hm=64, kv_fmt=1)
+    elif case == "small_e4m3kv":  # the same with two pipes and split keys (a small grid)
+        wl = synth.make_workload(case, 10, [3000], 1, [(20, synth.MODE_FULL, False)], Hm=16, kv_fmt=1)
     elif case == "short_ctx":
         wl = synth.make_workload(case, 5, [40, 100, 1], 1, [(20, synth.MODE_FULL, False)], Hm=32)
     elif case == "ragged_t4":
@@ -237,7 +244,8 @@ def test_sparse_attn_tolerance(case):
         idx[0, 10:300:3] = -1  # holes inside the list
     L, dL = wl.layers[0], dw.layers[0]
     sw = C.SwaLayout.from_workload(wl, replay_s=replay)
-    out, lse = C.csa2_sparse_attn(dw.batch, dL["q_main"], dw.kv, dw.kv_sc, dev(idx), dL["swa"], sw, SCALE)
+    out, lse = C.csa2_sparse_attn(dw.batch, dL["q_main"], dw.kv, dw.kv_sc, dev(idx), dL["swa"], sw, SCALE,
+                                  kv_fmt=wl.kv_fmt)
     torch.cuda.synchronize()
     ro, rl = oracle.sparse_attn(wl, L.q_main, idx, L.swa, replay_s=replay)
     assert_close_attn(out.cpu().numpy(), ro, case)
@@ -247,6 +255,8 @@ def test_sparse_attn_tolerance(case):
 CHAIN_CASES = {
     "c2_small": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16),
     "c2_small_h64": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=64),
+    # the report's main-KV scales (E4M3 per 16 channels) through Full + pool, Reindex and Reuse
+    "c2_small_e4m3kv": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16, kv_fmt=1),
     "c4_small": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16),
     "c3_small": lambda: synth.config("prefill_c3", tokens=4000, T=96, Hm=16),
     # degenerate rows: a sequence with no entries (its row attends to its

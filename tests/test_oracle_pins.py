@@ -591,3 +591,58 @@ def test_decoder_replay_chain():
         np.testing.assert_array_equal(a["lse"][-1], b["lse"][-1])
         assert np.all(a["lse"][:-1] < b["lse"][:-1])
         assert np.all(np.abs(a["out"][:-1] - b["out"][:-1]).max(axis=(1, 2)) > 0)
+
+
+def test_e2m1_e4m3_block_encoder():
+    """The report's main-KV cache format (section 2.4.4: E2M1 with one E4M3
+    scale per 16 channels, NVFP4 without its second-level global scale) as the
+    generator writes it, checked by brute force over the spec grids: the scale
+    is the E4M3 value nearest to amax / 6 (ties to the even code; a block whose
+    scale would be 0 takes the smallest step), every element the E2M1 value
+    nearest to x / X (ties to the even code, saturating at 6)."""
+    rows, seed, tid = 24, 321, 17
+    codes, scales = synth.e2m1_e4m3_rows(seed, tid, rows, 512)
+    x = synth.normal_f64(seed, tid, rows * 512).reshape(rows, 32, 16)
+    pos = [c for c in range(1, 127)]  # finite positive E4M3 codes (0x7F is NaN)
+    vals = np.array([oracle.e4m3(c) for c in pos])
+    e2 = np.array(E2M1_SPEC)
+    for r in range(rows):
+        for b in range(32):
+            blk = x[r, b]
+            t = np.abs(blk).max() / 6.0
+            d = np.abs(vals - t)
+            best = [pos[i] for i in np.flatnonzero(d == d.min())]
+            want = min(best, key=lambda c: (c & 1, c)) if len(best) > 1 else best[0]
+            assert scales[r, b] == want, (r, b)
+            X = oracle.e4m3(int(scales[r, b]))
+            for c in range(16):
+                a = abs(blk[c]) / X
+                if a >= 6.0:
+                    m = 7
+                else:
+                    dd = np.abs(e2 - a)
+                    cand = np.flatnonzero(dd == dd.min())
+                    m = int(cand[0]) if len(cand) == 1 else int(cand[0] if cand[0] % 2 == 0 else cand[1])
+                byte = codes[r, (16 * b + c) // 2]
+                nib = (byte >> 4) if c & 1 else (byte & 15)
+                assert nib & 7 == m, (r, b, c)
+                assert (nib >> 3) == (1 if blk[c] < 0 and m != 0 else 0)
+
+
+def test_gather_dequant_e4m3_scales_against_spec_decode():
+    """fmt 1 main KV: value = E2M1 * E4M3(scale of its 16-channel block), exact
+    in bf16, decoded here from the spec tables."""
+    wl = synth.config("decode_c0", n_entries=[300], kv_fmt=1)
+    idx = np.array([[0, 5, -1, 299, 17]], np.int32)
+    got = oracle.gather_dequant(wl, idx)
+    for s, j in enumerate(idx[0]):
+        if j < 0:
+            assert not got[0, s].any()
+            continue
+        for ch in range(0, 512, 7):
+            byte = wl.kv[j, ch // 2]
+            nib = (byte >> 4) if ch & 1 else (byte & 15)
+            v = (-1 if nib & 8 else 1) * E2M1_SPEC[nib & 7] * oracle.e4m3(int(wl.kv_sc[j, ch // 16]))
+            f = np.float32(v)
+            assert abs(float(f) - v) == 0.0
+            assert got[0, s, ch] == (f.view(np.uint32) >> 16), (s, ch)
