@@ -308,8 +308,8 @@ def chain_bytes(wl, outs, pool_pos, pool_count):
     once per sequence) and query/weights; each Reindex layer's gathered
     indexer-K rows (the union of a sequence's pools, 65 B each); per layer and
     row the gathered main-KV rows (272 B per selected entry; 288 B with E4M3
-    scales per 16 channels), the SWA rows (1,024 B), the main query, the
-    output and the indices."""
+    scales per 16 channels), the SWA rows (1,024 B; 528 B in MXFP8), the main
+    query, the output and the indices."""
     import numpy as np
 
     H, Hm, K, W = wl.H, wl.Hm, wl.K, wl.W
@@ -331,7 +331,8 @@ def chain_bytes(wl, outs, pool_pos, pool_count):
             total += qw
         n_sel = (o["idx"].cpu().numpy() >= 0).sum(axis=1) if L.mode != synth_mode("SWA_ONLY") else 0
         kv_row = 288 if getattr(wl, "kv_fmt", 0) == 1 else 272
-        total += int(np.sum(n_sel) * kv_row + n_swa.sum() * 1024) + wl.total_q * (Hm * 512 * 6 + K * 4)
+        swa_row = 528 if getattr(wl, "swa_fmt", 0) == 1 else 1024
+        total += int(np.sum(n_sel) * kv_row + n_swa.sum() * swa_row) + wl.total_q * (Hm * 512 * 6 + K * 4)
     return total
 
 
@@ -351,11 +352,15 @@ def bench_workloads(synth, C, torch, dev):
     from gpu_util import DevWorkload, prepare_chain
 
     res = {}
-    # decode_c1_e4m3kv: decode_c1 with the report's main-KV scales (E4M3 per 16 channels)
-    for name, reps in (("decode_c0", 20), ("decode_c1_e4m3kv", 10), ("chain_c2", 5), ("ragged_c4", 5),
+    # decode_c1_pages_fmt: decode_c1 with the report's cache formats, main KV with
+    # E4M3 scales per 16 channels and SWA in FP8 (as OCP MXFP8)
+    for name, reps in (("decode_c0", 20), ("decode_c1_pages_fmt", 10), ("chain_c2", 5), ("ragged_c4", 5),
                        ("prefill_c3", 3), ("replay_c5", 3)):
         t0 = time.time()
-        wl = synth.config("decode_c1", kv_fmt=1) if name == "decode_c1_e4m3kv" else synth.config(name)
+        if name == "decode_c1_pages_fmt":
+            wl = synth.config("decode_c1", kv_fmt=1, swa_fmt=1)
+        else:
+            wl = synth.config(name)
         dw = DevWorkload(wl, dev)
         call, outs, (pb, pp, pc) = prepare_chain(dw, want_idx=True, want_lse=False)
         call()

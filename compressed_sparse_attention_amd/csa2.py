@@ -37,7 +37,7 @@ class csa2_batch(ctypes.Structure):
 
 
 class csa2_swa_layout(ctypes.Structure):
-    _fields_ = [("window", ctypes.c_int32), ("reserved", ctypes.c_int32), ("h_row_off", _vp), ("h_pos0", _vp),
+    _fields_ = [("window", ctypes.c_int32), ("fmt", ctypes.c_int32), ("h_row_off", _vp), ("h_pos0", _vp),
                 ("h_len", _vp), ("h_replay_s", _vp), ("d_row_off", _vp), ("d_pos0", _vp), ("d_replay_s", _vp)]
 
 
@@ -151,7 +151,7 @@ class Batch:
 
 
 class SwaLayout:
-    def __init__(self, window, row_off, pos0, length, replay_s=None, device="cuda"):
+    def __init__(self, window, row_off, pos0, length, replay_s=None, device="cuda", fmt=0):
         dev = torch.device(device)
         self.h_row_off = np.ascontiguousarray(row_off, np.int64)
         self.h_pos0 = np.ascontiguousarray(pos0, np.int32)
@@ -160,12 +160,12 @@ class SwaLayout:
         self.d_row_off = torch.from_numpy(self.h_row_off).to(dev)
         self.d_pos0 = torch.from_numpy(self.h_pos0).to(dev)
         self.d_replay = None if replay_s is None else torch.from_numpy(self.h_replay).to(dev)
-        self.c = csa2_swa_layout(int(window), 0, _ptr(self.h_row_off), _ptr(self.h_pos0), _ptr(self.h_len),
+        self.c = csa2_swa_layout(int(window), int(fmt), _ptr(self.h_row_off), _ptr(self.h_pos0), _ptr(self.h_len),
                                  _ptr(self.h_replay), _ptr(self.d_row_off), _ptr(self.d_pos0), _ptr(self.d_replay))
 
     @classmethod
     def from_workload(cls, wl, replay_s=None, device="cuda"):
-        return cls(wl.W, wl.swa_row_off, wl.swa_pos0, wl.swa_len, replay_s, device)
+        return cls(wl.W, wl.swa_row_off, wl.swa_pos0, wl.swa_len, replay_s, device, getattr(wl, "swa_fmt", 0))
 
 
 HIST_BINS = 4096

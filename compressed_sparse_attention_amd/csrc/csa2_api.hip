@@ -54,6 +54,7 @@ csa2_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 csa2_status check_swa(const csa2_batch* b, const csa2_swa_layout* sw) {
     if (!sw || sw->window < 1 || sw->window > 1024) return sw && sw->window > 1024 ? CSA2_ERR_UNSUPPORTED : CSA2_ERR_INVALID_ARG;
+    if (sw->fmt != CSA2_SWA_BF16 && sw->fmt != CSA2_SWA_MXFP8) return CSA2_ERR_UNSUPPORTED;
     if (!sw->h_row_off || !sw->h_pos0 || !sw->h_len || !sw->d_row_off || !sw->d_pos0) return CSA2_ERR_INVALID_ARG;
     if ((sw->h_replay_s == nullptr) != (sw->d_replay_s == nullptr)) return CSA2_ERR_INVALID_ARG;
     for (int s = 0; s < b->n_seq; ++s) {
@@ -262,19 +263,19 @@ CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, int32_t kv_fmt
 
 CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16, int32_t kv_fmt,
                                       const uint8_t* kv_fp4, const uint8_t* kv_sc, const int32_t* idx, int32_t K,
-                                      const uint16_t* swa_bf16, const csa2_swa_layout* swa, float softmax_scale,
+                                      const void* swa_rows, const csa2_swa_layout* swa, float softmax_scale,
                                       float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
     Geometry g;
     csa2_status st = batch_geometry(batch, &g);
     if (st) return st;
-    if (!q_bf16 || !kv_fp4 || !kv_sc || !idx || !swa_bf16 || !out) return CSA2_ERR_INVALID_ARG;
+    if (!q_bf16 || !kv_fp4 || !kv_sc || !idx || !swa_rows || !out) return CSA2_ERR_INVALID_ARG;
     if (kv_fmt != CSA2_KV_MXFP4 && kv_fmt != CSA2_KV_E4M3_16) return CSA2_ERR_UNSUPPORTED;
     if (Hm < 16 || Hm % 16) return Hm < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
     if (K < 1 || K > kMaxK) return K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
     if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return CSA2_ERR_INVALID_ARG;
     if ((st = check_swa(batch, swa))) return st;
     if (ws && ((uintptr_t)ws & 255)) return CSA2_ERR_WORKSPACE;
-    AttnLaunch a{batch, g, Hm, q_bf16, kv_fp4, kv_sc, idx, K, swa_bf16, swa, softmax_scale, out, lse, ws,
+    AttnLaunch a{batch, g, Hm, q_bf16, kv_fp4, kv_sc, idx, K, swa_rows, swa, softmax_scale, out, lse, ws,
                  ws ? ws_bytes : 0, kv_fmt};
     hipError_t e = launch_sparse_attn(a, stream);
     return e == hipSuccess ? CSA2_OK : hip_fail(e);

@@ -324,7 +324,7 @@ struct AttnLaunch {
     const uint8_t* kv_sc;
     const int32_t* idx;
     int K;
-    const uint16_t* swa;
+    const void* swa;            // SWA rows in the layout's format (bf16 or MXFP8)
     const csa2_swa_layout* sw;
     float scale;
     float* out;

@@ -64,6 +64,9 @@ __device__ __forceinline__ float e4m3_f32(uint32_t b) {
 // Main-KV scale formats: kKvMx one E8M0 per 32 channels (16 bytes a row),
 // kKvE4 one E4M3 per 16 channels (32 bytes a row; the report's section 2.4.4).
 enum : int { kKvMx = 0, kKvE4 = 1 };
+// SWA row formats: bf16 [rows][512], or OCP MXFP8 [rows][528] (512 E4M3 codes,
+// then 16 E8M0 scales, one per 32 channels)
+enum : int { kSwaBf16 = 0, kSwaMx8 = 1 };
 
 // Reductions over lane pairs l, l ^ D (D = 16 or 32) on the VALU: the swap
 // leaves this lane's value and its partner's in the two results (in some order).
@@ -128,10 +131,10 @@ constexpr int KB = 64;
 constexpr int LROW = 512 + 8;  // LDS row stride of the staged keys in bf16 (16 B of padding)
 constexpr int SLROW = KB + 4;  // LDS row stride of the logits in floats
 
-template <int NPIPE, int KVF>
+template <int NPIPE, int KVF, int SWF>
 __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
-    const int32_t* __restrict__ idx, int K, const uint16_t* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
+    const int32_t* __restrict__ idx, int K, const void* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
     const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ replay_s, int W,
     const int64_t* __restrict__ entry_off, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ q_pos,
     float scale_log2, float* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg, int S,
@@ -211,12 +214,23 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
 
     const int vk_first = KB * (blk0 + pipe) + skey;
     const bool first_swa = blk0 + pipe < blk1 && vk_first < n_swa;
+    // this thread's 128 channels of SWA row vk: 16 bf16 loads, or 8 loads of
+    // MXFP8 codes and one of their 4 scales
     v4i sw[CP / 8];
-    if (first_swa) {
-        const uint16_t* src = swa + (swa_r0 + vk_first) * 512 + CP * part;
+    uint32_t swsc = 0;
+    auto load_swa = [&](int vk) {
+        if constexpr (SWF == kSwaMx8) {
+            const uint8_t* rb = reinterpret_cast<const uint8_t*>(swa) + (swa_r0 + vk) * 528;
 #pragma unroll
-        for (int i = 0; i < CP / 8; ++i) sw[i] = ld16(src + 8 * i);
-    }
+            for (int i = 0; i < CP / 16; ++i) sw[i] = ld16(rb + CP * part + 16 * i);
+            swsc = *reinterpret_cast<const uint32_t*>(rb + 512 + 4 * part);
+        } else {
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(swa) + (swa_r0 + vk) * 512 + CP * part;
+#pragma unroll
+            for (int i = 0; i < CP / 8; ++i) sw[i] = ld16(src + 8 * i);
+        }
+    };
+    if (first_swa) load_swa(vk_first);
     if (tid == 0) nsel_sh = 0;
     __syncthreads();
     {
@@ -277,13 +291,28 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
         int valid = 0;
         if (vk < n_swa) {
             valid = 1;
-            if (!swa_in_regs) {
-                const uint16_t* src = swa + (swa_r0 + vk) * 512 + CP * part;
+            if (!swa_in_regs) load_swa(vk);
+            if constexpr (SWF == kSwaMx8) {
+                // E4M3 x E8M0 is exact in bf16 (four significant bits, a power of two)
 #pragma unroll
-                for (int i = 0; i < CP / 8; ++i) sw[i] = ld16(src + 8 * i);
+                for (int i = 0; i < NB; ++i) {  // 32 channels per scale
+                    const float sc = e8m0_f32((swsc >> (8 * i)) & 255u);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {  // 8 channels: two dwords of 4 codes
+                        const uint32_t w0 = (uint32_t)sw[2 * i + d / 2][2 * (d % 2)];
+                        const uint32_t w1 = (uint32_t)sw[2 * i + d / 2][2 * (d % 2) + 1];
+                        auto a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
+                        auto a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
+                        auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
+                        auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
+                        *reinterpret_cast<v8bf*>(dst + 32 * i + 8 * d) =
+                            v8bf{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < CP / 8; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = sw[i];
             }
-#pragma unroll
-            for (int i = 0; i < CP / 8; ++i) *reinterpret_cast<v4i*>(dst + 8 * i) = sw[i];
         } else if (vk < n_keys && kidx[vk - n_swa] >= 0) {
             valid = 1;
 #pragma unroll
@@ -575,18 +604,25 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
     float* part = S > 1 ? (float*)a.ws : nullptr;
     // two pipes per workgroup only where the grid leaves most CUs idle (latency
     // is all that counts there); otherwise one pipe, two workgroups per CU
-#define CSA2_ATTN(NP, KF)                                                                                          \
-    hipLaunchKernelGGL((k_sparse_attn<NP, KF>), dim3(nblk), dim3(256 * NP), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, \
+#define CSA2_ATTN(NP, KF, SF)                                                                                      \
+    hipLaunchKernelGGL((k_sparse_attn<NP, KF, SF>), dim3(nblk), dim3(256 * NP), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, \
                        a.swa, a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,   \
                        a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q,  \
                        n_hg, S, part)
+#define CSA2_ATTN_NP(KF, SF)                  \
+    do {                                      \
+        if (nblk <= kAttnTwoPipeWgs)          \
+            CSA2_ATTN(2, KF, SF);             \
+        else                                  \
+            CSA2_ATTN(1, KF, SF);             \
+    } while (0)
+    const bool swa8 = a.sw->fmt == CSA2_SWA_MXFP8;
     if (a.kv_fmt == kKvE4) {
-        if (nblk <= kAttnTwoPipeWgs) CSA2_ATTN(2, kKvE4);
-        else CSA2_ATTN(1, kKvE4);
+        if (swa8) CSA2_ATTN_NP(kKvE4, kSwaMx8); else CSA2_ATTN_NP(kKvE4, kSwaBf16);
     } else {
-        if (nblk <= kAttnTwoPipeWgs) CSA2_ATTN(2, kKvMx);
-        else CSA2_ATTN(1, kKvMx);
+        if (swa8) CSA2_ATTN_NP(kKvMx, kSwaMx8); else CSA2_ATTN_NP(kKvMx, kSwaBf16);
     }
+#undef CSA2_ATTN_NP
 #undef CSA2_ATTN
     if (S > 1) {
         const dim3 cg((unsigned)(a.g.total_q * a.Hm));

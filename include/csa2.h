@@ -43,8 +43,12 @@
  *               q_sc   [total_q][H] u8 (one E8M0 per head row)
  *               w      [total_q][H] f32 head weights
  *   main q      [total_q][Hm][512] bf16
- *   SWA KV      [rows][512] bf16 per layer, rows of sequence b at row_off[b],
- *               holding token positions pos0[b] .. pos0[b]+len[b]-1
+ *   SWA KV      per layer, rows of sequence b at row_off[b], holding token
+ *               positions pos0[b] .. pos0[b]+len[b]-1; by the layout's fmt:
+ *               CSA2_SWA_BF16  [rows][512] bf16
+ *               CSA2_SWA_MXFP8 [rows][528] u8: 512 E4M3 codes, then 16 E8M0
+ *                              scales (one per 32 channels; OCP MXFP8, the
+ *                              FP8 SWA cache of the report's section 2.4.4)
  *   indices     [total_q][K] i32 local entry positions, ascending, -1 padded
  */
 #ifndef CSA2_H
@@ -77,6 +81,9 @@ typedef int32_t csa2_status;
 
 #define CSA2_KV_MXFP4 0    /* main-KV scales: E8M0 per 32 channels */
 #define CSA2_KV_E4M3_16 1  /* main-KV scales: E4M3 per 16 channels */
+
+#define CSA2_SWA_BF16 0
+#define CSA2_SWA_MXFP8 1
 
 #define CSA2_MODE_SWA_ONLY 0
 #define CSA2_MODE_FULL 1
@@ -114,7 +121,7 @@ typedef struct csa2_batch {
  * token must lie in [pos0[b], pos0[b]+len[b]); the host checks this. */
 typedef struct csa2_swa_layout {
     int32_t window;              /* W >= 1 (128 in the report, section 4.2.1) */
-    int32_t reserved;
+    int32_t fmt;                 /* CSA2_SWA_BF16 or CSA2_SWA_MXFP8: the rows' format */
     const int64_t* h_row_off;    /* (host)   [n_seq] first row of sequence b */
     const int32_t* h_pos0;       /* (host)   [n_seq] token position of that row */
     const int32_t* h_len;        /* (host)   [n_seq] rows present */
@@ -207,7 +214,7 @@ CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, int32_t kv_fmt
  *   out[r][h] = sum_u softmax_u(scale * q[r][h] . key_u) * key_u   (fp32)
  *   lse[r][h] = log sum_u exp(scale * q[r][h] . key_u)               (optional)
  * Main-KV values are those of csa2_gather_dequant with the same kv_fmt.
- * q_bf16: [total_q][Hm][512]; swa_bf16: [rows][512] laid out by `swa`;
+ * q_bf16: [total_q][Hm][512]; swa_rows: the SWA rows in the format and layout of `swa`;
  * out: [total_q][Hm][512] f32; lse: [total_q][Hm] f32 or NULL (all device).
  * Supported: Hm a multiple of 16, 1 <= K <= 2048, window <= 1024.
  * Workspace (optional): with csa2_workspace_size(CSA2_WS_SPARSE_ATTN, ...)
@@ -217,7 +224,7 @@ CSA2_API csa2_status csa2_gather_dequant(const csa2_batch* batch, int32_t kv_fmt
  * merge, not bit for bit. */
 CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16, int32_t kv_fmt,
                                       const uint8_t* kv_fp4, const uint8_t* kv_sc, const int32_t* idx, int32_t K,
-                                      const uint16_t* swa_bf16, const csa2_swa_layout* swa, float softmax_scale,
+                                      const void* swa_rows, const csa2_swa_layout* swa, float softmax_scale,
                                       float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- layer chain ---------------------------------------------------------
@@ -242,7 +249,7 @@ typedef struct csa2_layer {
     const uint8_t* k_fp4;        /* (device) indexer K of this layer (FULL) */
     const uint8_t* k_sc;
     const uint16_t* q_main;      /* (device) [total_q][Hm][512] bf16 */
-    const uint16_t* swa;         /* (device) SWA rows of this layer, laid out by the chain's swa layout */
+    const void* swa;             /* (device) SWA rows of this layer, in the format and layout of the chain's swa layout */
     float* out;                  /* (device) [total_q][Hm][512] */
     float* lse;                  /* (device) [total_q][Hm] or NULL */
     int32_t* idx_out;            /* (device) [total_q][K] or NULL: the indices this layer attended with */

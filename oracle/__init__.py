@@ -61,8 +61,8 @@ def lib():
         L.orc_topk.argtypes = [i64, vp, i64, vp, vp, i64, i32, vp, i32]
         L.orc_block_pool.argtypes = [i64, vp, i64, vp, i32, i32, vp, vp, vp, i32]
         L.orc_gather_dequant.argtypes = [i64, vp, vp, vp, vp, i32, vp, i32, vp]
-        L.orc_sparse_attn.argtypes = [i64, vp, vp, vp, vp, i32, vp, vp, i32, vp, i32, vp, vp, vp, i32, vp, d, vp, vp,
-                                      i32]
+        L.orc_sparse_attn.argtypes = [i64, vp, vp, vp, vp, i32, vp, vp, i32, vp, i32, vp, i32, vp, vp, i32, vp, d, vp,
+                                      vp, i32]
         _lib = L
     return _lib
 
@@ -183,7 +183,8 @@ def sparse_attn(wl, q_main, idx, swa, replay_s=None, rows=None, scale=None, with
     lse = np.empty((nr, Hm), np.float32) if with_lse else None
     sc = 1.0 / math.sqrt(512.0) if scale is None else scale
     lib().orc_sparse_attn(nr, _p(_c(row_seq, np.int32)), _p(_c(q_pos, np.int32)), _p(wl.entry_off), _p(q_main), Hm,
-                          _p(wl.kv), _p(wl.kv_sc), getattr(wl, "kv_fmt", 0), _p(idx), idx.shape[1], _p(_c(swa, np.uint16)),
+                          _p(wl.kv), _p(wl.kv_sc), getattr(wl, "kv_fmt", 0), _p(idx), idx.shape[1],
+                          _p(_c(swa, np.uint8 if getattr(wl, "swa_fmt", 0) == 1 else np.uint16)), getattr(wl, "swa_fmt", 0),
                           _p(_c(wl.swa_row_off, np.int64)), _p(_c(wl.swa_pos0, np.int32)), wl.W,
                           _p(None if replay_s is None else _c(replay_s, np.int32)), sc, _p(out), _p(lse), NTHREADS)
     return out, lse

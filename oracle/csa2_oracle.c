@@ -398,7 +398,8 @@ typedef struct {
     int kv_fmt;
     const int32_t* idx;
     int K;
-    const uint16_t* swa; /* [rows][512] bf16 */
+    const void* swa; /* swa_fmt 0: [rows][512] bf16; 1: [rows][528] MXFP8 (512 E4M3 codes, 16 E8M0 scales) */
+    int swa_fmt;
     const int64_t* swa_row_off;
     const int32_t* swa_pos0;
     int W;
@@ -428,7 +429,14 @@ static void attn_row(void* p, int64_t r) {
     }
     for (int64_t u = u_lo; u <= t; ++u) {
         int64_t row = c->swa_row_off[b] + (u - c->swa_pos0[b]);
-        for (int ch = 0; ch < 512; ++ch) keys[n * 512 + ch] = (double)orc_bf16(c->swa[row * 512 + ch]);
+        for (int ch = 0; ch < 512; ++ch) {
+            if (c->swa_fmt == 1) { /* OCP MXFP8: E4M3 element times the E8M0 scale of its 32 channels */
+                const uint8_t* rb = (const uint8_t*)c->swa + row * 528;
+                keys[n * 512 + ch] = orc_e4m3(rb[ch]) * orc_e8m0(rb[512 + ch / 32]);
+            } else {
+                keys[n * 512 + ch] = (double)orc_bf16(((const uint16_t*)c->swa)[row * 512 + ch]);
+            }
+        }
         ++n;
     }
     double* logit = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
@@ -461,9 +469,9 @@ static void attn_row(void* p, int64_t r) {
 void orc_sparse_attn(int64_t total_q, const int32_t* row_seq, const int32_t* q_pos, const int64_t* entry_off,
                      const uint16_t* q, int Hm, const uint8_t* kv, const uint8_t* kv_sc, int kv_fmt, const int32_t* idx,
                      int K,
-                     const uint16_t* swa, const int64_t* swa_row_off, const int32_t* swa_pos0, int W,
+                     const void* swa, int swa_fmt, const int64_t* swa_row_off, const int32_t* swa_pos0, int W,
                      const int32_t* replay_s, double scale, float* out, float* lse, int nthreads) {
-    attn_ctx c = {row_seq, q_pos, entry_off, q, Hm, kv, kv_sc, kv_fmt, idx, K, swa, swa_row_off, swa_pos0, W, replay_s,
+    attn_ctx c = {row_seq, q_pos, entry_off, q, Hm, kv, kv_sc, kv_fmt, idx, K, swa, swa_fmt, swa_row_off, swa_pos0, W, replay_s,
                   scale, out, lse};
     parallel_for(total_q, nthreads, attn_row, &c);
 }

@@ -64,6 +64,7 @@ def lib():
         L.csa2synth_mxfp4_rows.argtypes = [u64, u64, i64, i64, i32, i32, vp, vp]
         L.csa2synth_e4m3_rows.argtypes = [u64, u64, i64, i64, i32, vp, vp]
         L.csa2synth_e2m1_e4m3_rows.argtypes = [u64, u64, i64, i64, i32, vp, vp]
+        L.csa2synth_mxfp8_rows.argtypes = [u64, u64, i64, i64, i32, vp]
         L.csa2synth_encode_e2m1.argtypes = [ctypes.c_double]
         L.csa2synth_encode_e2m1.restype = ctypes.c_uint8
         L.csa2synth_encode_e4m3.argtypes = [ctypes.c_double]
@@ -132,6 +133,14 @@ def e2m1_e4m3_rows(seed, tid, nrows, row_len, row0=0):
     return codes, scales
 
 
+def mxfp8_rows(seed, tid, nrows, row_len, row0=0):
+    """OCP MXFP8 rows (E4M3 elements, one E8M0 per 32), codes then scales per row."""
+    out = np.empty((nrows, row_len + row_len // 32), np.uint8)
+    rc = lib().csa2synth_mxfp8_rows(seed, tid, row0, nrows, row_len, _ptr(out))
+    assert rc == 0
+    return out
+
+
 def uniform_u64(seed, tid, i):
     return lib().csa2synth_hash(seed, tid, i)
 
@@ -179,6 +188,7 @@ class Workload:
     layers: List[Layer] = field(default_factory=list)
     replay_s: Optional[np.ndarray] = None  # [n_seq] i32 SWA replay start per sequence (None: 0)
     kv_fmt: int = 0                        # main-KV scales: 0 E8M0 per 32 channels, 1 E4M3 per 16 channels
+    swa_fmt: int = 0                       # SWA rows: 0 bf16 [rows][512], 1 MXFP8 [rows][528] (codes, then scales)
 
     @property
     def n_seq(self):
@@ -246,14 +256,15 @@ def ragged_lengths(seed, n_seq, lo=4096, hi=1048576):
 
 def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=64, Hm=64, K=512, W=128,
                   block=8, max_blocks=2048, q_fmt=Q_FP4, q_pos=None, gen_kv=True, gen_layers=True, replay_s=None,
-                  kv_fmt=0):
+                  kv_fmt=0, swa_fmt=0):
     """Build a workload.  n_entries: per-sequence entry counts.  queries_per_seq:
     T (same for all sequences).  q_pos: explicit token positions per sequence
     (list of arrays) or None for the decode shape t = N*ratio - T + i.
     schedule: list of (layer index, mode, build_pool).  replay_s: per-sequence
     SWA replay start s (a query at t sees window rows max(s, t - W + 1) .. t).
     kv_fmt: main-KV scales, 0 = OCP MXFP4 (E8M0 per 32 channels), 1 = the
-    report's E4M3 per 16 channels."""
+    report's E4M3 per 16 channels.  swa_fmt: SWA rows, 0 = bf16, 1 = OCP
+    MXFP8 (E4M3 with one E8M0 per 32 channels, codes then scales per row)."""
     n_entries = np.asarray(n_entries, np.int64)
     n_seq = len(n_entries)
     entry_off = np.zeros(n_seq + 1, np.int64)
@@ -276,6 +287,7 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
     if replay_s is not None:
         wl.replay_s = np.ascontiguousarray(replay_s, np.int32)
     wl.kv_fmt = int(kv_fmt)
+    wl.swa_fmt = int(swa_fmt)
     total = int(entry_off[-1])
     if gen_kv:
         wl.k_idx, ksc = mxfp4_rows(seed, TID_K, total, 128, 128)
@@ -300,7 +312,10 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
                     L.q_sc = s.reshape(nq, H)
                 L.w = uniform_f32(seed, _tid(li, 1), nq * H).reshape(nq, H)
             L.q_main = normal_bf16(seed, _tid(li, 2), nq * Hm * 512).reshape(nq, Hm, 512)
-            L.swa = normal_bf16(seed, _tid(li, 3), swa_rows * 512).reshape(swa_rows, 512)
+            if swa_fmt == 1:
+                L.swa = mxfp8_rows(seed, _tid(li, 3), swa_rows, 512)
+            else:
+                L.swa = normal_bf16(seed, _tid(li, 3), swa_rows * 512).reshape(swa_rows, 512)
         wl.layers.append(L)
     return wl
 

@@ -192,6 +192,28 @@ static void run_range(const job_t* j, int64_t lo, int64_t hi) {
         free(v);
         break;
     }
+    case 7: { /* MXFP8 rows: E4M3 elements with one E8M0 scale per 32, stored inline:
+               * row = row_len code bytes then row_len/32 scale bytes; X = 2^(floor(log2 amax) - 8) */
+        uint8_t* o = (uint8_t*)j->out;
+        int nb = j->row_len / 32, stride = j->row_len + nb;
+        double* v = (double*)malloc(sizeof(double) * (size_t)j->row_len);
+        for (int64_t r = lo; r < hi; ++r) {
+            uint64_t base = (uint64_t)(j->row0 + r) * (uint64_t)j->row_len;
+            for (int c = 0; c < j->row_len; ++c) v[c] = normal(hash3(j->seed, j->tid, base + (uint64_t)c));
+            uint8_t* orow = o + r * stride;
+            for (int b = 0; b < nb; ++b) {
+                double amax = 0.0;
+                for (int c = 0; c < 32; ++c) amax = fmax(amax, fabs(v[b * 32 + c]));
+                int se = amax > 0.0 ? ilog2_floor(amax) - 8 : -127;
+                if (se < -127) se = -127;
+                if (se > 127) se = 127;
+                orow[j->row_len + b] = (uint8_t)(se + 127);
+                for (int c = 0; c < 32; ++c) orow[b * 32 + c] = e4m3_code(ldexp(v[b * 32 + c], -se));
+            }
+        }
+        free(v);
+        break;
+    }
     case 6: {
         double* o = (double*)j->out;
         for (int64_t i = lo; i < hi; ++i) o[i] = normal(hash3(j->seed, j->tid, (uint64_t)(j->row0 + i)));
@@ -321,6 +343,18 @@ int csa2synth_e2m1_e4m3_rows(uint64_t seed, uint64_t tid, int64_t row0, int64_t 
     job_t j = {0};
     j.kind = 5; j.seed = seed; j.tid = tid; j.row0 = row0; j.row_len = row_len;
     j.out = codes; j.scales = scales;
+    run(&j, nrows);
+    return 0;
+}
+
+/* nrows rows of row_len N(0,1) values as OCP MXFP8 (E4M3 elements, one E8M0
+ * scale per 32), each row its row_len code bytes followed by its row_len/32
+ * scale bytes: [nrows][row_len + row_len/32] u8. */
+int csa2synth_mxfp8_rows(uint64_t seed, uint64_t tid, int64_t row0, int64_t nrows, int row_len, uint8_t* rows) {
+    if (row_len <= 0 || row_len % 32) return 1;
+    job_t j = {0};
+    j.kind = 7; j.seed = seed; j.tid = tid; j.row0 = row0; j.row_len = row_len;
+    j.out = rows;
     run(&j, nrows);
     return 0;
 }

@@ -144,6 +144,9 @@ def test_sparse_attn_validation():
         None)
     ok = _swa(128, [0], [872], [128])
     assert attn(kv_fmt=2, sw=ok) == C.CSA2_ERR_UNSUPPORTED  # main-KV scales: E8M0/32 or E4M3/16 only
+    bad_fmt = _swa(128, [0], [872], [128])
+    bad_fmt.fmt = 2
+    assert attn(sw=bad_fmt) == C.CSA2_ERR_UNSUPPORTED  # SWA rows: bf16 or MXFP8 only
     assert attn(Hm=40, sw=ok) == C.CSA2_ERR_UNSUPPORTED
     assert attn(K=0, sw=ok) == C.CSA2_ERR_INVALID_ARG
     assert attn(scale=0.0, sw=ok) == C.CSA2_ERR_INVALID_ARG

@@ -205,7 +205,7 @@ def test_gather_dequant_bitwise(kv_fmt):
 
 
 ATTN_CASES = ["decode", "short_ctx", "ragged_t4", "swa_only", "replay", "sparse_idx", "swa_only_h64", "replay_h64",
-              "decode_e4m3kv", "small_e4m3kv"]
+              "decode_e4m3kv", "small_e4m3kv", "decode_swa8", "small_swa8", "replay_swa8"]
 
 
 @pytest.mark.parametrize("case", ATTN_CASES)
@@ -218,6 +218,13 @@ def test_sparse_attn_tolerance(case):
         wl = synth.config("decode_c1", n_seq=3, n=6000, Hm=64, kv_fmt=1)
     elif case == "small_e4m3kv":  # the same with two pipes and split keys (a small grid)
         wl = synth.make_workload(case, 10, [3000], 1, [(20, synth.MODE_FULL, False)], Hm=16, kv_fmt=1)
+    elif case == "decode_swa8":  # SWA rows in MXFP8 (E4M3, one E8M0 per 32 channels), big grid
+        wl = synth.config("decode_c1", n_seq=3, n=6000, Hm=64, swa_fmt=1)
+    elif case == "small_swa8":  # the same with two pipes and split keys, and the report's main-KV scales
+        wl = synth.make_workload(case, 11, [3000, 90], 1, [(20, synth.MODE_FULL, False)], Hm=16, swa_fmt=1, kv_fmt=1)
+    elif case == "replay_swa8":
+        wl = synth.make_workload(case, 12, [2000, 300], 1, [(20, synth.MODE_FULL, False)], Hm=16, swa_fmt=1)
+        replay = np.array([1950, 0], np.int32)
     elif case == "short_ctx":
         wl = synth.make_workload(case, 5, [40, 100, 1], 1, [(20, synth.MODE_FULL, False)], Hm=32)
     elif case == "ragged_t4":
@@ -244,6 +251,7 @@ def test_sparse_attn_tolerance(case):
         idx[0, 10:300:3] = -1  # holes inside the list
     L, dL = wl.layers[0], dw.layers[0]
     sw = C.SwaLayout.from_workload(wl, replay_s=replay)
+    assert sw.c.fmt == wl.swa_fmt
     out, lse = C.csa2_sparse_attn(dw.batch, dL["q_main"], dw.kv, dw.kv_sc, dev(idx), dL["swa"], sw, SCALE,
                                   kv_fmt=wl.kv_fmt)
     torch.cuda.synchronize()
@@ -257,6 +265,8 @@ CHAIN_CASES = {
     "c2_small_h64": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=64),
     # the report's main-KV scales (E4M3 per 16 channels) through Full + pool, Reindex and Reuse
     "c2_small_e4m3kv": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16, kv_fmt=1),
+    # the pages' cache formats for main KV (E4M3 per 16 channels) and SWA (FP8, as OCP MXFP8)
+    "c2_small_pages_fmt": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16, kv_fmt=1, swa_fmt=1),
     "c4_small": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16),
     "c3_small": lambda: synth.config("prefill_c3", tokens=4000, T=96, Hm=16),
     # degenerate rows: a sequence with no entries (its row attends to its

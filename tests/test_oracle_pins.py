@@ -646,3 +646,36 @@ def test_gather_dequant_e4m3_scales_against_spec_decode():
             f = np.float32(v)
             assert abs(float(f) - v) == 0.0
             assert got[0, s, ch] == (f.view(np.uint32) >> 16), (s, ch)
+
+
+def test_mxfp8_swa_encoder_and_decode():
+    """SWA rows in OCP MXFP8 (the report's section 2.4.4 keeps SWA KV in FP8;
+    the OCP MX family the pages name gives its block form): per 32 channels
+    X = 2^(floor(log2 amax) - 8) (emax of E4M3 is 8), elements the E4M3 values
+    nearest to x / X (ties to the even code), checked by brute force over the
+    spec grid; the oracle's attention reads them as E4M3 * E8M0, which for a
+    lone key in the window (no selected entries) is its output exactly."""
+    rows, seed, tid = 6, 77, 5
+    enc = synth.mxfp8_rows(seed, tid, rows, 512)
+    x = synth.normal_f64(seed, tid, rows * 512).reshape(rows, 16, 32)
+    codes = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    vals = np.array([oracle.e4m3(c) for c in codes])
+    for r in range(rows):
+        for b in range(16):
+            blk = x[r, b]
+            se = math.floor(math.log2(np.abs(blk).max())) - 8
+            assert enc[r, 512 + b] == se + 127
+            for c in range(32):
+                t = blk[c] / 2.0 ** se
+                d = np.abs(vals - t)
+                best = [codes[i] for i in np.flatnonzero(d == d.min())]
+                want = best[0] if len(best) == 1 else min(best, key=lambda k: (k & 1, k))
+                assert oracle.e4m3(int(enc[r, 32 * b + c])) == oracle.e4m3(int(want)), (r, b, c)
+    # one query at t = 0 sees exactly one SWA row and no entry: out = that row
+    wl = synth.make_workload("swa8", 3, [1], 1, [(0, MODE_SWA_ONLY, False)], Hm=16, swa_fmt=1, q_pos=[np.array([0])])
+    L = wl.layers[0]
+    out, lse = oracle.sparse_attn(wl, L.q_main, np.full((1, 512), -1, np.int32), L.swa)
+    row = L.swa[0]
+    want = np.array([oracle.e4m3(int(row[c])) * oracle.e8m0(int(row[512 + c // 32])) for c in range(512)], np.float32)
+    for h in range(16):
+        np.testing.assert_array_equal(out[0, h], want)
