@@ -28,6 +28,11 @@
  *     [R] 2.3.1 says Full mode inherits).  The head sum is evaluated in fp32 as
  *     acc = +0; for h = 0..H-1: acc = fmaf(w[t,h], r_h, acc)  (one IEEE fused
  *     multiply-add per head, round to nearest even).  That order is a convention.
+ *   - index score in the report's indexer format (OCP MXFP4 for indexer q and
+ *     indexer K, [R] 2.4.4: one E8M0 per 32 channels on both sides): the block
+ *     scales enter the dot product, d_h = sum_b 2^(eq_thb + ek_jb - 254) *
+ *     (dot of block b), exact; then r_h = ReLU(d_h), the same fmaf head sum, and
+ *     no per-entry factor after it.
  *   - Top-K: the first min(K, visible) entries under (score descending,
  *     position ascending); returned in ascending position order, -1 padded.
  *   - block pool: blocks of 8 aligned at position 0; a block's score is the
@@ -141,7 +146,7 @@ static void parallel_for(int64_t n, int nthreads, row_fn fn, void* ctx) {
 /* Index score ([R] 2.3 indexer; [R] 2.3.1 Full/Reindex; [R] 2.3.2 pool)      */
 /* ------------------------------------------------------------------------ */
 
-enum { ORC_Q_FP4 = 0, ORC_Q_FP8 = 1 };
+enum { ORC_Q_FP4 = 0, ORC_Q_FP8 = 1, ORC_Q_MXFP4 = 2 };
 
 typedef struct {
     const int32_t *row_seq, *q_pos;
@@ -161,7 +166,7 @@ typedef struct {
  * E2M1 values are multiples of 0.5 (qshift 1); E4M3 values are multiples of
  * 2^-9 (qshift 9). */
 static int64_t q_int(const score_ctx* c, int64_t row, int h, int ch) {
-    if (c->q_fmt == ORC_Q_FP4) {
+    if (c->q_fmt == ORC_Q_FP4 || c->q_fmt == ORC_Q_MXFP4) {
         uint8_t byte = c->q[(row * c->H + h) * 64 + ch / 2];
         uint8_t nib = (ch & 1) ? (byte >> 4) : (byte & 15);
         return (int64_t)llround(orc_e2m1(nib) * 2.0);
@@ -177,6 +182,38 @@ static int64_t k_int(const score_ctx* c, int64_t e, int ch) {
     return (int64_t)llround(orc_e2m1(nib) * 2.0);
 }
 
+/* The report's MXFP4 indexer format: q [T][H][64 B] with q_sc [T][H][4] and
+ * K [N][64 B] with k_sc [N][4], one E8M0 per 32 channels on both sides (OCP
+ * MX v1.0: a block's value is 2^(scale - 127) times its E2M1 elements).  Block
+ * b of head h contributes 2^(eq + ek - 254) times its integer dot product / 4;
+ * the blocks are summed exactly in integers at the smallest block exponent,
+ * so d_h is the exact dot product of the decoded rows. */
+static float score_one_mx(const score_ctx* c, int64_t r, int64_t e, const int64_t* qi, const int64_t* kv) {
+    float acc = 0.0f;
+    for (int h = 0; h < c->H; ++h) {
+        int64_t part[4];
+        int ex[4], emin = 1 << 30;
+        for (int b = 0; b < 4; ++b) {
+            part[b] = 0;
+            for (int ch = 32 * b; ch < 32 * b + 32; ++ch) part[b] += qi[h * 128 + ch] * kv[ch];
+            ex[b] = (int)c->q_sc[(r * c->H + h) * 4 + b] + (int)c->k_sc[e * 4 + b] - 254;
+            if (ex[b] < emin) emin = ex[b];
+        }
+        int64_t dot = 0; /* d_h = dot * 2^(emin - 2) */
+        for (int b = 0; b < 4; ++b) {
+            int sh = ex[b] - emin;
+            if (sh > 30) { ((score_ctx*)c)->status = 2; sh = 30; }
+            dot += part[b] * ((int64_t)1 << sh);
+        }
+        /* exact in binary32 only while |dot| < 2^24: a wider spread of the
+         * block scales needs more bits than binary32 holds */
+        if (dot >= (1LL << 24) || dot <= -(1LL << 24)) ((score_ctx*)c)->status = 2;
+        float d = (float)ldexp((double)dot, emin - 2);
+        acc = fmaf(c->w[r * c->H + h], fmaxf(d, 0.0f), acc);
+    }
+    return acc;
+}
+
 /* score of one (query row, local entry j), or -inf when j is not visible. */
 static float score_one(const score_ctx* c, int64_t r, int64_t j, const int64_t* qi /* [H][128] */) {
     int b = c->row_seq[r];
@@ -186,6 +223,7 @@ static float score_one(const score_ctx* c, int64_t r, int64_t j, const int64_t* 
     int64_t e = c->entry_off[b] + j;
     int64_t kv[128];
     for (int ch = 0; ch < 128; ++ch) kv[ch] = k_int(c, e, ch);
+    if (c->q_fmt == ORC_Q_MXFP4) return score_one_mx(c, r, e, qi, kv);
     int qshift = (c->q_fmt == ORC_Q_FP4) ? 1 : 9;
     float acc = 0.0f;
     for (int h = 0; h < c->H; ++h) {

@@ -32,7 +32,7 @@ _SO = os.path.join(_HERE, "libcsa2_synth.so")
 _SRC = os.path.join(_HERE, "csa2_synth.c")
 
 MODE_SWA_ONLY, MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2, 3
-Q_FP4, Q_FP8 = 0, 1
+Q_FP4, Q_FP8, Q_MXFP4 = 0, 1, 2
 
 TID_K, TID_KV, TID_LEN = 1, 2, 3
 
@@ -155,7 +155,7 @@ class Layer:
     mode: int
     q_fmt: int = Q_FP4
     q_idx: Optional[np.ndarray] = None    # FP4 [T][H][64] or FP8 [T][H][128], u8
-    q_sc: Optional[np.ndarray] = None     # [T][H] u8 (E8M0)
+    q_sc: Optional[np.ndarray] = None     # [T][H] u8 (E8M0), or [T][H][4] for Q_MXFP4
     w: Optional[np.ndarray] = None        # [T][H] f32
     q_main: Optional[np.ndarray] = None   # [T][Hm][512] bf16 bits (u16)
     swa: Optional[np.ndarray] = None      # [rows][512] bf16 bits (u16)
@@ -182,7 +182,7 @@ class Workload:
     swa_pos0: np.ndarray       # [n_seq] i32
     swa_len: np.ndarray        # [n_seq] i32
     k_idx: np.ndarray = None   # [sumN][64] u8
-    k_sc: np.ndarray = None    # [sumN] u8
+    k_sc: np.ndarray = None    # [sumN] u8, or [sumN][4] when the layers use Q_MXFP4
     kv: np.ndarray = None      # [sumN][256] u8
     kv_sc: np.ndarray = None   # [sumN][16] u8
     layers: List[Layer] = field(default_factory=list)
@@ -264,7 +264,10 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
     SWA replay start s (a query at t sees window rows max(s, t - W + 1) .. t).
     kv_fmt: main-KV scales, 0 = OCP MXFP4 (E8M0 per 32 channels), 1 = the
     report's E4M3 per 16 channels.  swa_fmt: SWA rows, 0 = bf16, 1 = OCP
-    MXFP8 (E4M3 with one E8M0 per 32 channels, codes then scales per row)."""
+    MXFP8 (E4M3 with one E8M0 per 32 channels, codes then scales per row).
+    q_fmt: indexer queries, Q_FP4 / Q_FP8 (one E8M0 per head row, indexer K
+    with one E8M0 per row), or Q_MXFP4 (the report's indexer format: queries
+    and indexer K both OCP MXFP4 with one E8M0 per 32 channels)."""
     n_entries = np.asarray(n_entries, np.int64)
     n_seq = len(n_entries)
     entry_off = np.zeros(n_seq + 1, np.int64)
@@ -290,8 +293,11 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
     wl.swa_fmt = int(swa_fmt)
     total = int(entry_off[-1])
     if gen_kv:
-        wl.k_idx, ksc = mxfp4_rows(seed, TID_K, total, 128, 128)
-        wl.k_sc = np.ascontiguousarray(ksc.reshape(total))
+        if q_fmt == Q_MXFP4:  # the report's indexer format: one E8M0 per 32 channels
+            wl.k_idx, wl.k_sc = mxfp4_rows(seed, TID_K, total, 128, 32)
+        else:
+            wl.k_idx, ksc = mxfp4_rows(seed, TID_K, total, 128, 128)
+            wl.k_sc = np.ascontiguousarray(ksc.reshape(total))
         if kv_fmt == 1:
             wl.kv, wl.kv_sc = e2m1_e4m3_rows(seed, TID_KV, total, 512)
         else:
@@ -306,6 +312,10 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
                     c, s = mxfp4_rows(seed, _tid(li, 0), nq * H, 128, 128)
                     L.q_idx = c.reshape(nq, H, 64)
                     L.q_sc = s.reshape(nq, H)
+                elif q_fmt == Q_MXFP4:
+                    c, s = mxfp4_rows(seed, _tid(li, 0), nq * H, 128, 32)
+                    L.q_idx = c.reshape(nq, H, 64)
+                    L.q_sc = s.reshape(nq, H, 4)
                 else:
                     c, s = e4m3_rows(seed, _tid(li, 0), nq * H, 128)
                     L.q_idx = c.reshape(nq, H, 128)

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import synth
-from synth import MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_SWA_ONLY, Q_FP4, Q_FP8, Layer, Workload
+from synth import MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_SWA_ONLY, Q_FP4, Q_FP8, Q_MXFP4, Layer, Workload
 
 # ---------------------------------------------------------------------------
 # helpers (encoders written from the spec; independent of the oracle)
@@ -270,6 +270,47 @@ def test_score_exact_against_float64_dot():
     r = np.maximum(d, 0) * np.exp2(L.q_sc[0].astype(np.float64) - 127)[:, None]
     want = r.sum(0) * np.exp2(wl.k_sc.astype(np.float64) - 127)
     assert np.array_equal(s[:300].astype(np.float64), want)
+
+
+def test_score_mxfp4_block_scales_hand_value():
+    """The report's indexer format (OCP MXFP4 on both sides, one E8M0 per 32
+    channels): every block's scales enter the dot product, and no per-entry
+    factor follows the head sum.  q = k = 1 everywhere, so block b contributes
+    32 * 2^(eq_b + ek_b - 254)."""
+    wl, q, _, w = _score_wl([[1.0] * 128], [1.0] * 128, [1.0])
+    wl.k_sc = np.array([[127, 127, 127, 129]], np.uint8)
+    qs = np.array([[[127, 128, 126, 127]]], np.uint8)
+    assert oracle.index_score(wl, q, qs, w, Q_MXFP4)[0, 0] == 32 * (1 + 2 + 0.5 + 4)
+    # a negative dot product is cut by the ReLU after the block scales apply:
+    # block 0 -> -32 * 2^3, blocks 1..3 -> +32 each: the sum is negative
+    q2 = np.stack([pack_fp4([-1.0] * 32 + [1.0] * 96)])[None]
+    wl.k_sc = np.array([[130, 127, 127, 127]], np.uint8)
+    qs = np.full((1, 1, 4), 127, np.uint8)
+    s = oracle.index_score(wl, q2, qs, w, Q_MXFP4)[0, 0]
+    assert s == 0.0 and math.copysign(1, s) == 1.0
+
+
+def test_score_mxfp4_exact_rational_on_generated_rows():
+    """Generated MXFP4 rows (OCP scale rule per 32-channel block): the block
+    dot products summed in float64 are exact, fit binary32 exactly (the block
+    scales of a q/K pair span a few powers of two), and the head sum with one
+    correctly rounded fused multiply-add per head, evaluated in rationals,
+    equals the oracle's score bit for bit."""
+    wl = synth.config("decode_c0", n_entries=[160], q_fmt=Q_MXFP4)
+    L = wl.layers[0]
+    assert L.q_sc.shape == (1, 64, 4) and wl.k_sc.shape == (160, 4)
+    got = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, Q_MXFP4)[0]
+    q = decode_fp4_rows(L.q_idx[0], 128) * np.repeat(np.exp2(L.q_sc[0].astype(np.float64) - 127), 32, axis=1)
+    k = decode_fp4_rows(wl.k_idx, 128) * np.repeat(np.exp2(wl.k_sc.astype(np.float64) - 127), 32, axis=1)
+    d = q @ k.T                                             # [H][N], exact in float64
+    assert np.array_equal(d.astype(np.float32).astype(np.float64), d)
+    spread = np.ptp(L.q_sc[0][:, None, :].astype(int) + wl.k_sc[None].astype(int), axis=-1)
+    assert spread.max() <= 6
+    for j in range(160):
+        acc = Fraction(0)
+        for h in range(64):
+            acc = Fraction(rne_f32(Fraction(float(L.w[0, h])) * Fraction(max(d[h, j], 0.0)) + acc))
+        assert got[j] == float(acc), (j, got[j], float(acc))
 
 
 def test_score_fp8_query_hand_and_random():
