@@ -305,8 +305,9 @@ def chain_only(args, synth, C, torch, dev):
 def chain_bytes(wl, outs, pool_pos, pool_count):
     """Algorithmic HBM bytes of one decode step of a layer chain, from the
     realised selections: the Full layer's scan (65 B per visible entry, read
-    once per sequence) and query/weights; each Reindex layer's gathered
-    indexer-K rows (the union of a sequence's pools, 65 B each); per layer and
+    once per sequence; 68 B in the MXFP4 indexer format) and query/weights;
+    each Reindex layer's gathered indexer-K rows (the union of a sequence's
+    pools, 65 or 68 B each); per layer and
     row the gathered main-KV rows (272 B per selected entry; 288 B with E4M3
     scales per 16 channels), the SWA rows (1,024 B; 528 B in MXFP8), the main
     query, the output and the indices."""
@@ -317,17 +318,19 @@ def chain_bytes(wl, outs, pool_pos, pool_count):
     seq_vis = np.zeros(wl.n_seq, np.int64)
     np.maximum.at(seq_vis, wl.row_seq, vis)
     n_swa = np.minimum(W, wl.q_pos.astype(np.int64) + 1)
-    qw = wl.total_q * H * (64 + 1 + 4)
+    mx = wl.layers and any(L.q_fmt == synth_mode_q("MXFP4") for L in wl.layers)
+    k_row = 68 if mx else 65
+    qw = wl.total_q * H * (64 + (4 if mx else 1) + 4)
     total = 0
     for L, o in zip(wl.layers, outs):
         if L.mode == synth_mode("FULL"):
-            total += int(seq_vis.sum()) * 65 + qw
+            total += int(seq_vis.sum()) * k_row + qw
         elif L.mode == synth_mode("REINDEX"):
             pp, pc = pool_pos.cpu().numpy(), pool_count.cpu().numpy()
             for b in range(wl.n_seq):
                 rows = np.nonzero(wl.row_seq == b)[0]
                 u = np.unique(np.concatenate([pp[r, :pc[r]] for r in rows])) if len(rows) else []
-                total += len(u) * 65
+                total += len(u) * k_row
             total += qw
         n_sel = (o["idx"].cpu().numpy() >= 0).sum(axis=1) if L.mode != synth_mode("SWA_ONLY") else 0
         kv_row = 288 if getattr(wl, "kv_fmt", 0) == 1 else 272
@@ -342,6 +345,12 @@ def synth_mode(name):
     return getattr(synth, "MODE_" + name)
 
 
+def synth_mode_q(name):
+    import synth
+
+    return getattr(synth, "Q_" + name)
+
+
 def bench_workloads(synth, C, torch, dev):
     """The layer chain of the other workloads: one call = every layer of one
     decode step (or of the prefill chunk, or of the 128-token decoder replay)
@@ -352,13 +361,14 @@ def bench_workloads(synth, C, torch, dev):
     from gpu_util import DevWorkload, prepare_chain
 
     res = {}
-    # decode_c1_pages_fmt: decode_c1 with the report's cache formats, main KV with
-    # E4M3 scales per 16 channels and SWA in FP8 (as OCP MXFP8)
+    # decode_c1_pages_fmt: decode_c1 with the report's cache formats: main KV with
+    # E4M3 scales per 16 channels, indexer q and K in OCP MXFP4 (the 356-byte
+    # position) and SWA in FP8 (as OCP MXFP8)
     for name, reps in (("decode_c0", 20), ("decode_c1_pages_fmt", 10), ("chain_c2", 5), ("ragged_c4", 5),
                        ("prefill_c3", 3), ("replay_c5", 3)):
         t0 = time.time()
         if name == "decode_c1_pages_fmt":
-            wl = synth.config("decode_c1", kv_fmt=1, swa_fmt=1)
+            wl = synth.config("decode_c1", kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4)
         else:
             wl = synth.config(name)
         dw = DevWorkload(wl, dev)
@@ -402,10 +412,13 @@ def bench_workloads(synth, C, torch, dev):
         del dw, outs, call, pb, pp, pc, wl
         torch.cuda.empty_cache()
     res["decode_step_40"] = bench_step_40(synth, torch, dev)
+    # the same step with every cache in the report's formats (E4M3/16 main KV,
+    # MXFP4 indexer, FP8 SWA as MXFP8)
+    res["decode_step_40_pages_fmt"] = bench_step_40(synth, torch, dev, kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4)
     return res
 
 
-def bench_step_40(synth, torch, dev, reps=5):
+def bench_step_40(synth, torch, dev, reps=5, **fmt):
     """One decode token of each of 64 sequences at 131,072 tokens through all 40
     layers: the five chains the layers form (two sliding-window layers, three
     encoder groups at ratio 2 over 65,536 entries with their own caches, the
@@ -415,7 +428,7 @@ def bench_step_40(synth, torch, dev, reps=5):
     from gpu_util import DevWorkload, prepare_chain
 
     t0 = time.time()
-    wls = synth.decode_step_40()
+    wls = synth.decode_step_40(**fmt)
     dws = [DevWorkload(wl, dev) for wl in wls]
     calls = [prepare_chain(dw, want_idx=False, want_lse=False)[0] for dw in dws]
 
@@ -434,7 +447,7 @@ def bench_step_40(synth, torch, dev, reps=5):
     ms = s.elapsed_time(e) / reps
     n_layers = sum(len(wl.layers) for wl in wls)
     n_seq = wls[0].n_seq
-    log(f"[bench] decode_step_40: {ms:.3f} ms per 40-layer step of {n_seq} sequences ({time.time() - t0:.0f} s incl. inputs)")
+    log(f"[bench] decode_step_40{' (pages formats)' if fmt else ''}: {ms:.3f} ms per 40-layer step of {n_seq} sequences ({time.time() - t0:.0f} s incl. inputs)")
     r = {"ms_per_step": round(ms, 4), "layers": n_layers, "sequences": n_seq, "tokens": int(wls[-1].n_entries[0]),
          "tokens_per_s": round(n_seq * 1000.0 / ms, 1), "layer_steps_per_s": round(n_layers * 1000.0 / ms, 1),
          "chains": [wl.name for wl in wls]}

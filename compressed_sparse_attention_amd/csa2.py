@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, 1, 2, 3, 4
-CSA2_Q_FP4, CSA2_Q_FP8 = 0, 1
+CSA2_Q_FP4, CSA2_Q_FP8, CSA2_Q_MXFP4 = 0, 1, 2
 CSA2_KV_MXFP4, CSA2_KV_E4M3_16 = 0, 1
 CSA2_MODE_SWA_ONLY, CSA2_MODE_FULL, CSA2_MODE_REINDEX, CSA2_MODE_REUSE = 0, 1, 2, 3
 CSA2_LAYER_BUILD_POOL = 1

@@ -169,15 +169,15 @@ CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_
     csa2_status st = batch_geometry(batch, &g);
     if (st) return st;
     if (!q || !q_sc || !w || !k_fp4 || !k_sc || !scores) return CSA2_ERR_INVALID_ARG;
-    if (q_fmt != CSA2_Q_FP4 && q_fmt != CSA2_Q_FP8) return CSA2_ERR_INVALID_ARG;
+    if (q_fmt != CSA2_Q_FP4 && q_fmt != CSA2_Q_FP8 && q_fmt != CSA2_Q_MXFP4) return CSA2_ERR_INVALID_ARG;
     if (H != 32 && H != 64) return CSA2_ERR_UNSUPPORTED;
     if (cand) {
-        if (q_fmt != CSA2_Q_FP4) return CSA2_ERR_UNSUPPORTED;
+        if (q_fmt == CSA2_Q_FP8) return CSA2_ERR_UNSUPPORTED;
         if (cand_stride < 1 || score_stride < cand_stride) return CSA2_ERR_INVALID_ARG;
     } else if (score_stride < g.max_entries || score_stride < 1) {
         return CSA2_ERR_INVALID_ARG;
     }
-    if (hist && (q_fmt != CSA2_Q_FP4 || (!cand && g.max_q_per_seq > 4))) return CSA2_ERR_UNSUPPORTED;
+    if (hist && (q_fmt == CSA2_Q_FP8 || (!cand && g.max_q_per_seq > 4))) return CSA2_ERR_UNSUPPORTED;
     ScoreLaunch a{batch, g, H, q_fmt, (const uint8_t*)q, q_sc, w, k_fp4, k_sc, cand, cand_stride, scores, score_stride,
                   hist};
     hipError_t e = launch_index_score(a, stream);
@@ -299,6 +299,7 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
     // static checks of the schedule: every attending layer has main KV, every
     // REUSE layer has indices, at most one layer builds the pool
     bool have_kv = false, have_idx = false;
+    bool src_mx = false;  // the latest Full layer's indexer K carries 32-channel scales
     int pool_layers = 0;
     for (int l = 0; l < n_layers; ++l) {
         const csa2_layer& L = layers[l];
@@ -307,14 +308,17 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
             case CSA2_MODE_SWA_ONLY: break;
             case CSA2_MODE_FULL:
                 if (!L.kv_fp4 || !L.kv_sc || !L.k_fp4 || !L.k_sc || !L.q_idx || !L.q_sc || !L.w) return CSA2_ERR_INVALID_ARG;
-                if (L.q_fmt != CSA2_Q_FP4 && L.q_fmt != CSA2_Q_FP8) return CSA2_ERR_INVALID_ARG;
+                if (L.q_fmt != CSA2_Q_FP4 && L.q_fmt != CSA2_Q_FP8 && L.q_fmt != CSA2_Q_MXFP4) return CSA2_ERR_INVALID_ARG;
+                src_mx = L.q_fmt == CSA2_Q_MXFP4;
                 if (L.kv_fmt != CSA2_KV_MXFP4 && L.kv_fmt != CSA2_KV_E4M3_16) return CSA2_ERR_UNSUPPORTED;
                 have_kv = have_idx = true;
                 if (L.flags & CSA2_LAYER_BUILD_POOL) ++pool_layers;
                 break;
             case CSA2_MODE_REINDEX:
                 if (!have_kv || !L.q_idx || !L.q_sc || !L.w) return CSA2_ERR_INVALID_ARG;
-                if (L.q_fmt != CSA2_Q_FP4) return CSA2_ERR_UNSUPPORTED;  // pool scoring runs on FP4 queries
+                if (L.q_fmt == CSA2_Q_FP8) return CSA2_ERR_UNSUPPORTED;  // pool scoring runs on FP4 queries
+                if (L.q_fmt != CSA2_Q_FP4 && L.q_fmt != CSA2_Q_MXFP4) return CSA2_ERR_INVALID_ARG;
+                if ((L.q_fmt == CSA2_Q_MXFP4) != src_mx) return CSA2_ERR_INVALID_ARG;  // the K's scale layout
                 have_idx = true;
                 break;
             case CSA2_MODE_REUSE:
@@ -418,7 +422,7 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                 // long for the one-workgroup selection; the Top-K pass then starts
                 // from it.  A pool built from these scores needs its own pass.
                 const int64_t slots = on_pool ? (int64_t)pool_stride : g.max_entries;
-                const bool fused = L.q_fmt == CSA2_Q_FP4 && (on_pool || g.max_q_per_seq <= 4) && slots > kRowSelMax;
+                const bool fused = L.q_fmt != CSA2_Q_FP8 && (on_pool || g.max_q_per_seq <= 4) && slots > kRowSelMax;
                 if (fused && (e = clear_topk_ws(topk_ws, g.total_q, true, stream)) != hipSuccess) return hip_fail(e);
                 ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, src->k_fp4, src->k_sc,
                                on_pool ? pp : nullptr, on_pool ? pool_stride : 0, on_pool ? pscores : scores,

@@ -224,7 +224,7 @@ struct LocalOut {
 // the 4-row scan when it keeps its rows' scores on chip (LDS budget)
 constexpr int decode_chunk(int tq, bool local) { return (local && tq > 1) ? 2048 : 4096; }
 // the scan writes local lists for FP4 queries and at most 4 rows per sequence
-inline bool local_scan_ok(const Geometry& g, int q_fmt) { return q_fmt == CSA2_Q_FP4 && g.max_q_per_seq <= 4; }
+inline bool local_scan_ok(const Geometry& g, int q_fmt) { return q_fmt != CSA2_Q_FP8 && g.max_q_per_seq <= 4; }
 inline int local_chunk(const Geometry& g) { return decode_chunk(g.max_q_per_seq <= 1 ? 1 : 4, true); }
 inline size_t local_lists_bytes(const Geometry& g) {
     const int ch = local_chunk(g);

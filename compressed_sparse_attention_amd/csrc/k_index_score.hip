@@ -15,6 +15,14 @@
 // per position in one lane, in the fixed order h = 0..H-1 with one fused
 // multiply-add per head, so the binary32 score is reproducible bit for bit.
 //
+// The report's indexer format (section 2.4.4: FP4 indexer queries and keys in
+// OCP MXFP4) carries one E8M0 per 32 channels on both sides.  With it (MX) the
+// instruction applies the query's block scale (A) and the key's (B) per lane
+// half, so D already holds the scaled dot product and no per-entry factor
+// follows the head sum.  The blocks of a q/K pair then sit on grids up to
+// 2^spread apart; with the spreads of MX-quantised rows (a few powers of two)
+// every partial sum still fits the exact range, which the parity tests check.
+//
 // MFMA layouts (32x32x64, measured on gfx950): lane l supplies A row l%32 and
 // B column l%32; for E2M1 operands lane half g = l/32 supplies k = 32g + e for
 // nibble e = 0..31 of its 16 bytes (low nibble first); for E4M3 operands byte e
@@ -33,6 +41,14 @@ __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v1
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, sa, 0, 127);
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, 127);
 }
+
+// FP4 x FP4 with an E8M0 per lane for each operand (bits 7..0 of sa and sb)
+__device__ __forceinline__ v16f mfma_fp4_mx(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+}
+
+// byte i of a packed word of four E8M0 scales
+__device__ __forceinline__ int scale_byte(uint32_t w, int i) { return (int)((w >> (8 * i)) & 255u); }
 
 // E2M1 operands occupy the low four dwords of the 8-dword operand; the upper
 // four are never read, so they are left undefined (no registers zeroed)
@@ -126,7 +142,7 @@ __device__ __forceinline__ void hist16_flush(const uint32_t* h, uint32_t* __rest
 // ---------------------------------------------------------------------------
 enum : int { kOutScores = 0, kOutHist = 1, kOutLocal = 2 };
 
-template <int H, int TQ, int OUT>
+template <int H, int TQ, int OUT, bool MX>
 __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_sc,
                                                       const float* __restrict__ w, const uint8_t* __restrict__ k,
                                                       const uint8_t* __restrict__ k_sc,
@@ -141,7 +157,7 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     constexpr int chunk = decode_chunk(TQ, LOCAL);
     __shared__ uint32_t hl[HIST ? TQ * kHistBins / 2 : 1];
     __shared__ __attribute__((aligned(16))) float sl[LOCAL ? TQ : 1][LOCAL ? chunk : 1];  // the chunk's scores per row
-    __shared__ uint8_t ekl[chunk];                           // the chunk's indexer K scales
+    __shared__ uint8_t ekl[MX ? 1 : chunk];                  // the chunk's indexer K scales (one per row)
     __shared__ uint32_t wtot[4], found[4];
     const int b = blockIdx.y;
     const int64_t e0 = entry_off[b];
@@ -163,14 +179,18 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     // flight as well; only this wave reads them, so no barrier is needed
     const int64_t p_w = c0 + 64 * wave;
     uint8_t sb[chunk / 256];
+    if constexpr (!MX) {
 #pragma unroll
-    for (int j = 0; j < chunk / 256; ++j) {
-        const int64_t p = p_w + 256 * j + lane;
-        sb[j] = p < c1 ? k_sc[e0 + p] : 0;
+        for (int j = 0; j < chunk / 256; ++j) {
+            const int64_t p = p_w + 256 * j + lane;
+            sb[j] = p < c1 ? k_sc[e0 + p] : 0;
+        }
     }
 
     v8i A[TQ][NMT][2];
-    int SA[TQ][NMT];
+    // the query's scales: one per head row, or with MX the scales of the two
+    // blocks this lane half supplies (blocks 2g + ks at k-step ks)
+    int SA[TQ][NMT][MX ? 2 : 1];
     int64_t vis[TQ];
 #pragma unroll
     for (int t = 0; t < TQ; ++t) {
@@ -181,7 +201,13 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
             const uint8_t* qr = q + ((int64_t)row * H + 32 * mt + li) * 64 + 32 * g;
             A[t][mt][0] = widen(ld16(qr));
             A[t][mt][1] = widen(ld16(qr + 16));
-            SA[t][mt] = q_sc[(int64_t)row * H + 32 * mt + li];
+            if constexpr (MX) {
+                const uint32_t qs = *reinterpret_cast<const uint32_t*>(q_sc + ((int64_t)row * H + 32 * mt + li) * 4);
+                SA[t][mt][0] = scale_byte(qs, 2 * g);
+                SA[t][mt][1] = scale_byte(qs, 2 * g + 1);
+            } else {
+                SA[t][mt][0] = q_sc[(int64_t)row * H + 32 * mt + li];
+            }
         }
     }
 
@@ -194,6 +220,7 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     // last row, so no wait on a load is forced before its data is used.
     struct Buf {
         v4i k[2][2];
+        uint32_t sc[MX ? 2 : 1];  // with MX: the four block scales of column 32nt + li
     };
     const int n_tiles = p_w < c1 ? (int)((c1 - p_w + 255) / 256) : 0;
     const int64_t p_last = p_w + 256 * (int64_t)(n_tiles - 1);
@@ -205,6 +232,7 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
             const uint32_t r = min((uint32_t)(32 * nt + li), last);
             bf.k[nt][0] = ld16(kt + r * 64 + 32 * g);
             bf.k[nt][1] = ld16(kt + r * 64 + 32 * g + 16);
+            if constexpr (MX) bf.sc[nt] = *reinterpret_cast<const uint32_t*>(k_sc + (e0 + p0 + r) * 4);
         }
     };
     // score the tile at p0 from bf, refilling bf with the tile at p_next once
@@ -224,8 +252,13 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
                 for (int nt = 0; nt < 2; ++nt) {
                     acc[nt] = v16f{};
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        acc[nt] = mfma_scaled(A[t][mt][ks], widen(bf.k[nt][ks]), acc[nt], SA[t][mt], 4);
+                    for (int ks = 0; ks < 2; ++ks) {
+                        if constexpr (MX)
+                            acc[nt] = mfma_fp4_mx(A[t][mt][ks], widen(bf.k[nt][ks]), acc[nt], SA[t][mt][ks],
+                                                  scale_byte(bf.sc[nt], 2 * g + ks));
+                        else
+                            acc[nt] = mfma_scaled(A[t][mt][ks], widen(bf.k[nt][ks]), acc[nt], SA[t][mt][0], 4);
+                    }
                 }
                 if (mt == NMT - 1 && (t == nq - 1 || t == TQ - 1)) fetch(bf, p_next);
                 s = head_sum_32(acc, w + (int64_t)(r0 + t) * H + 32 * mt, s);
@@ -237,7 +270,11 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
             }
             if (jl < n) {
                 const bool visible = jl < vis[t];
-                const float sc = visible ? ldexpf(s, (int)ekl[p0 - c0 + lane] - 127) : -INFINITY;
+                float sc = -INFINITY;
+                if (visible) {
+                    if constexpr (MX) sc = s;
+                    else sc = ldexpf(s, (int)ekl[p0 - c0 + lane] - 127);
+                }
                 if constexpr (LOCAL)
                     sl[t][p0 - c0 + lane] = sc;
                 else
@@ -259,8 +296,10 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     // keep the loads above this point (they would otherwise sink to their first
     // use, behind the staging's wait)
     asm volatile("" ::: "memory");
+    if constexpr (!MX) {
 #pragma unroll
-    for (int j = 0; j < chunk / 256; ++j) ekl[64 * wave + 256 * j + lane] = sb[j];
+        for (int j = 0; j < chunk / 256; ++j) ekl[64 * wave + 256 * j + lane] = sb[j];
+    }
     // pairs of tiles, then an odd last one: the loop body has no exit of its
     // own, so every path into the loop header has the same loads in flight
     int i = 0;
@@ -348,7 +387,7 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
 // Candidate (Reindex) scoring: slot s of row r scores entry cand[r][s].
 // Grid (slot chunks of 1024, total_q).  Same operand mapping as the decode scan.
 // ---------------------------------------------------------------------------
-template <int H, bool HIST>
+template <int H, bool HIST, bool MX>
 __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_sc,
                                                     const float* __restrict__ w, const uint8_t* __restrict__ k,
                                                     const uint8_t* __restrict__ k_sc,
@@ -379,17 +418,24 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ 
     }
     if (HIST) hist_clear(hl, kHistBins);
     v8i A[NMT][2];
-    int SA[NMT];
+    int SA[NMT][MX ? 2 : 1];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
         const uint8_t* qr = q + ((int64_t)row * H + 32 * mt + li) * 64 + 32 * g;
         A[mt][0] = widen(ld16(qr));
         A[mt][1] = widen(ld16(qr + 16));
-        SA[mt] = q_sc[(int64_t)row * H + 32 * mt + li];
+        if constexpr (MX) {
+            const uint32_t qs = *reinterpret_cast<const uint32_t*>(q_sc + ((int64_t)row * H + 32 * mt + li) * 4);
+            SA[mt][0] = scale_byte(qs, 2 * g);
+            SA[mt][1] = scale_byte(qs, 2 * g + 1);
+        } else {
+            SA[mt][0] = q_sc[(int64_t)row * H + 32 * mt + li];
+        }
     }
     if (HIST) __syncthreads();
     for (int p0 = s0 + 64 * wave; p0 < s1; p0 += 256) {
         v8i B[2][2];
+        uint32_t bs[2];  // with MX: the four block scales of column 32nt + li
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const int s = p0 + 32 * nt + li;
@@ -398,11 +444,12 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ 
             const uint8_t* kr = k + (e0 + j) * 64 + 32 * g;
             B[nt][0] = widen(ld16(kr));
             B[nt][1] = widen(ld16(kr + 16));
+            if constexpr (MX) bs[nt] = *reinterpret_cast<const uint32_t*>(k_sc + (e0 + j) * 4);
         }
         const int sl = p0 + lane;
         const int64_t jl = sl < s1 ? (int64_t)crow[sl] : -1;
         const bool ok = jl >= 0 && jl < vis;
-        const int ek = ok ? (int)k_sc[e0 + jl] : 127;
+        const int ek = (!MX && ok) ? (int)k_sc[e0 + jl] : 127;
         v16f acc[NMT][2];
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
@@ -410,11 +457,16 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ 
             for (int nt = 0; nt < 2; ++nt) {
                 acc[mt][nt] = v16f{};
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) acc[mt][nt] = mfma_scaled(A[mt][ks], B[nt][ks], acc[mt][nt], SA[mt], 4);
+                for (int ks = 0; ks < 2; ++ks) {
+                    if constexpr (MX)
+                        acc[mt][nt] = mfma_fp4_mx(A[mt][ks], B[nt][ks], acc[mt][nt], SA[mt][ks], scale_byte(bs[nt], 2 * g + ks));
+                    else
+                        acc[mt][nt] = mfma_scaled(A[mt][ks], B[nt][ks], acc[mt][nt], SA[mt][0], 4);
+                }
             }
         const float sc = head_sum<NMT>(acc, w + (int64_t)row * H);
         if (sl < s1) {
-            const float v = ok ? ldexpf(sc, ek - 127) : -INFINITY;
+            const float v = ok ? (MX ? sc : ldexpf(sc, ek - 127)) : -INFINITY;
             srow[sl] = v;
             // the Top-K pass over a candidate list takes its first cand_count
             // slots, which are the non-empty ones of a pool list
@@ -434,7 +486,7 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ 
 // k-step ks = c/64, k = c%64 for both operands (the E4M3 layout fixes it for A;
 // B is loaded to match).
 // ---------------------------------------------------------------------------
-template <int H, int QFMT>
+template <int H, int QFMT, bool MX>
 __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict__ q,
                                                        const uint8_t* __restrict__ q_sc,
                                                        const float* __restrict__ w, const uint8_t* __restrict__ k,
@@ -448,7 +500,8 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
     constexpr int QG = 8;
     constexpr int QROW = QFMT == 0 ? 128 : 64;  // bytes per head row
     __shared__ __attribute__((aligned(16))) uint8_t ks_lds[PT * 64];
-    __shared__ uint8_t ksc_lds[PT];
+    __shared__ uint8_t ksc_lds[MX ? 1 : PT];
+    __shared__ uint32_t ksc4_lds[MX ? PT : 1];  // with MX: the four block scales of each row
     const int b = blockIdx.z;
     const int64_t e0 = entry_off[b];
     const int64_t n = entry_off[b + 1] - e0;
@@ -484,12 +537,17 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
     }
     for (int i = threadIdx.x; i < PT; i += 256) {
         const int64_t j = p_base + i;
-        ksc_lds[i] = j < n ? k_sc[e0 + j] : 127;
+        if constexpr (MX)
+            ksc4_lds[i] = j < n ? *reinterpret_cast<const uint32_t*>(k_sc + (e0 + j) * 4) : 0x7F7F7F7Fu;
+        else
+            ksc_lds[i] = j < n ? k_sc[e0 + j] : 127;
     }
 
     // two query rows per wave, in registers
     v8i A[2][NMT][2];
-    int SA[2][NMT];
+    // the query's scales: one per head row, or with MX the scales of the two
+    // blocks this lane half supplies (block 2ks + g at k-step ks)
+    int SA[2][NMT][MX ? 2 : 1];
     int64_t vis[2];
     int rows[2];
 #pragma unroll
@@ -511,7 +569,13 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
                     A[u][mt][ks] = widen(ld16(qr + 32 * ks + 16 * g));
                 }
             }
-            SA[u][mt] = q_sc[(int64_t)row * H + 32 * mt + li];
+            if constexpr (MX) {
+                const uint32_t qs = *reinterpret_cast<const uint32_t*>(q_sc + ((int64_t)row * H + 32 * mt + li) * 4);
+                SA[u][mt][0] = scale_byte(qs, g);
+                SA[u][mt][1] = scale_byte(qs, 2 + g);
+            } else {
+                SA[u][mt][0] = q_sc[(int64_t)row * H + 32 * mt + li];
+            }
         }
     }
     __syncthreads();
@@ -526,7 +590,12 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
             for (int ks = 0; ks < 2; ++ks)
                 B[nt][ks] = widen(*reinterpret_cast<const v4i*>(ks_lds + (64 * tile + 32 * nt + li) * 64 + 32 * ks + 16 * g));
         const int64_t jl = p0 + lane;
-        const int ek = ksc_lds[64 * tile + lane];
+        const int ek = MX ? 127 : ksc_lds[64 * tile + lane];
+        uint32_t bs[2];
+        if constexpr (MX) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) bs[nt] = ksc4_lds[64 * tile + 32 * nt + li];
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             if (rows[u] < 0) break;
@@ -541,11 +610,16 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
                 for (int nt = 0; nt < 2; ++nt) {
                     acc[mt][nt] = v16f{};
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        acc[mt][nt] = mfma_scaled(A[u][mt][ks], B[nt][ks], acc[mt][nt], SA[u][mt], QFMT == 0 ? 0 : 4);
+                    for (int ks = 0; ks < 2; ++ks) {
+                        if constexpr (MX)
+                            acc[mt][nt] = mfma_fp4_mx(A[u][mt][ks], B[nt][ks], acc[mt][nt], SA[u][mt][ks],
+                                                      scale_byte(bs[nt], 2 * ks + g));
+                        else
+                            acc[mt][nt] = mfma_scaled(A[u][mt][ks], B[nt][ks], acc[mt][nt], SA[u][mt][0], QFMT == 0 ? 0 : 4);
+                    }
                 }
             const float s = head_sum<NMT>(acc, w + (int64_t)rows[u] * H);
-            if (jl < n) scores[(int64_t)rows[u] * stride + jl] = jl < vis[u] ? ldexpf(s, ek - 127) : -INFINITY;
+            if (jl < n) scores[(int64_t)rows[u] * stride + jl] = jl < vis[u] ? (MX ? s : ldexpf(s, ek - 127)) : -INFINITY;
         }
     }
 }
@@ -755,10 +829,13 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill_fp8(const uint8_t* __r
 
 hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
     const csa2_batch* b = a.b;
+    const bool mx = a.q_fmt == CSA2_Q_MXFP4;  // FP4 queries and keys with an E8M0 per 32 channels
     if (a.cand) {
         dim3 grid((a.cand_stride + 1023) / 1024, a.g.total_q);
 #define CSA2_CAND(HH, HI)                                                                                        \
-    hipExtLaunchKernelGGL((k_score_cand<HH, HI>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,            \
+    do { if (mx) CSA2_CAND_M(HH, HI, true); else CSA2_CAND_M(HH, HI, false); } while (0)
+#define CSA2_CAND_M(HH, HI, MM)                                                                                  \
+    hipExtLaunchKernelGGL((k_score_cand<HH, HI, MM>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,            \
                        b->d_entry_off, b->d_row_seq, b->d_q_pos, b->ratio, a.cand, a.cand_stride, a.scores,      \
                        a.stride, a.hist)
         if (a.H == 64) {
@@ -767,16 +844,19 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
             if (a.hist) CSA2_CAND(32, true); else CSA2_CAND(32, false);
         }
 #undef CSA2_CAND
+#undef CSA2_CAND_M
         return hipGetLastError();
     }
-    if (a.q_fmt == CSA2_Q_FP4 && a.g.max_q_per_seq <= 4) {
+    if (a.q_fmt != CSA2_Q_FP8 && a.g.max_q_per_seq <= 4) {
         const bool one = a.g.max_q_per_seq <= 1;
         const int out = a.local ? kOutLocal : (a.hist ? kOutHist : kOutScores);
         const int chunk = decode_chunk(one ? 1 : 4, out == kOutLocal);
         const LocalOut lo = a.local ? *a.local : LocalOut{};
         dim3 grid((unsigned)((a.g.max_entries + chunk - 1) / chunk), a.g.n_seq);
 #define CSA2_DEC(HH, TT, OO)                                                                                     \
-    hipExtLaunchKernelGGL((k_score_decode<HH, TT, OO>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,      \
+    do { if (mx) CSA2_DEC_M(HH, TT, OO, true); else CSA2_DEC_M(HH, TT, OO, false); } while (0)
+#define CSA2_DEC_M(HH, TT, OO, MM)                                                                               \
+    hipExtLaunchKernelGGL((k_score_decode<HH, TT, OO, MM>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,      \
                        b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, a.hist, lo)
 #define CSA2_DEC_T(HH, OO) \
     do { if (one) CSA2_DEC(HH, 1, OO); else CSA2_DEC(HH, 4, OO); } while (0)
@@ -790,6 +870,7 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
 #undef CSA2_DEC_O
 #undef CSA2_DEC_T
 #undef CSA2_DEC
+#undef CSA2_DEC_M
         return hipGetLastError();
     }
     if (a.q_fmt == CSA2_Q_FP8) {
@@ -807,10 +888,13 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
     }
     dim3 grid((unsigned)((a.g.max_entries + 1023) / 1024), (unsigned)((a.g.max_q_per_seq + 7) / 8), a.g.n_seq);
 #define CSA2_PRE(HH, FF)                                                                                          \
-    hipExtLaunchKernelGGL((k_score_prefill<HH, FF>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,          \
+    do { if (mx) CSA2_PRE_M(HH, FF, true); else CSA2_PRE_M(HH, FF, false); } while (0)
+#define CSA2_PRE_M(HH, FF, MM)                                                                                    \
+    hipExtLaunchKernelGGL((k_score_prefill<HH, FF, MM>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,          \
                        b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride)
     if (a.H == 64) CSA2_PRE(64, 4); else CSA2_PRE(32, 4);
 #undef CSA2_PRE
+#undef CSA2_PRE_M
     return hipGetLastError();
 }
 

@@ -38,9 +38,11 @@
  *                      report's main-KV format, section 2.4.4, NVFP4's layout without its
  *                      second-level global scale)
  *   indexer K   k_fp4  [total_entries][64]  u8 (128 E2M1 channels)
- *               k_sc   [total_entries]      u8 (one E8M0 per row)
- *   indexer q   CSA2_Q_FP4: [total_q][H][64] u8, CSA2_Q_FP8: [total_q][H][128] u8
- *               q_sc   [total_q][H] u8 (one E8M0 per head row)
+ *               k_sc   [total_entries]      u8 (one E8M0 per row), or with CSA2_Q_MXFP4
+ *                      [total_entries][4] u8 (one E8M0 per 32 channels)
+ *   indexer q   CSA2_Q_FP4, CSA2_Q_MXFP4: [total_q][H][64] u8, CSA2_Q_FP8: [total_q][H][128] u8
+ *               q_sc   [total_q][H] u8 (one E8M0 per head row), or with CSA2_Q_MXFP4
+ *                      [total_q][H][4] u8 (one E8M0 per 32 channels)
  *               w      [total_q][H] f32 head weights
  *   main q      [total_q][Hm][512] bf16
  *   SWA KV      per layer, rows of sequence b at row_off[b], holding token
@@ -78,6 +80,11 @@ typedef int32_t csa2_status;
 
 #define CSA2_Q_FP4 0
 #define CSA2_Q_FP8 1
+/* The report's indexer format (section 2.4.4: quantisation-aware FP4 indexer
+ * queries and keys in OCP MXFP4): E2M1 queries and indexer K, both with one
+ * E8M0 per 32 channels.  It sets the layout of q_sc and of the indexer K's
+ * k_sc together. */
+#define CSA2_Q_MXFP4 2
 
 #define CSA2_KV_MXFP4 0    /* main-KV scales: E8M0 per 32 channels */
 #define CSA2_KV_E4M3_16 1  /* main-KV scales: E4M3 per 16 channels */
@@ -136,13 +143,22 @@ typedef struct csa2_swa_layout {
  * entry, Reindex mode rescores the shared indexer K with its own q):
  *   score(r, j) = 2^(k_sc[j]-127) * sum_{h=0..H-1} w[r,h] * ReLU(d_h * 2^(q_sc[r,h]-127))
  *   d_h = sum_c q[r,h,c] * k[j,c]   (exact: FP4 x FP4, and FP8 x FP4 for |q| <= 16)
+ * With CSA2_Q_MXFP4 the scales sit inside the dot product and no per-entry
+ * factor follows:
+ *   score(r, j) = sum_h w[r,h] * ReLU(d_h),
+ *   d_h = sum_b 2^(q_sc[r,h,b] + k_sc[j,b] - 254) * sum_{c in block b} q[r,h,c] * k[j,c]
+ * which is exact while the four block exponents of a (head row, entry) pair
+ * span few enough powers of two for d_h to fit binary32 (MX-quantised rows
+ * span a few; rows far outside that may differ from the exact value in the
+ * last bits).
  * The head sum is the binary32 chain acc = +0; acc = fmaf(w[r,h], ReLU(..), acc)
  * for h ascending, so scores are bit-reproducible.
  * cand == NULL: slot s of row r is entry s of its sequence; slots 0 .. N_b-1
  *   are written, -inf where the entry is not visible.
  * cand != NULL: slot s of row r is entry cand[r*cand_stride + s] (-1 = empty);
  *   slots 0 .. cand_stride-1 are written, -inf for empty or invisible slots.
- * q: [total_q][H][64] (CSA2_Q_FP4) or [total_q][H][128] (CSA2_Q_FP8) (device).
+ * q: [total_q][H][64] (CSA2_Q_FP4, CSA2_Q_MXFP4) or [total_q][H][128] (CSA2_Q_FP8)
+ *   (device); q_sc and k_sc as the format sets them (layout table above).
  * scores: [total_q][score_stride] f32 (device); score_stride >= max N_b
  *   (cand == NULL) or >= cand_stride.
  * hist: NULL, or [total_q][4096] u32 (device, zeroed by the caller) that
@@ -151,7 +167,8 @@ typedef struct csa2_swa_layout {
  *   on to csa2_topk saves the Top-K pass its own histogram pass.  Not
  *   produced for CSA2_Q_FP8 queries in this build (the call then returns
  *   CSA2_ERR_UNSUPPORTED).
- * Supported: H in {32, 64}.  CSA2_Q_FP8 requires cand == NULL. */
+ * Supported: H in {32, 64}.  CSA2_Q_FP8 requires cand == NULL.  An unknown
+ * q_fmt is CSA2_ERR_INVALID_ARG. */
 CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_t q_fmt, const void* q,
                                       const uint8_t* q_sc, const float* w, const uint8_t* k_fp4,
                                       const uint8_t* k_sc, const int32_t* cand, int32_t cand_stride,
@@ -239,10 +256,13 @@ CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const
 typedef struct csa2_layer {
     int32_t mode;                /* CSA2_MODE_* */
     int32_t flags;               /* CSA2_LAYER_BUILD_POOL (FULL only) */
-    int32_t q_fmt;               /* CSA2_Q_FP4 / CSA2_Q_FP8 (FULL, REINDEX) */
+    int32_t q_fmt;               /* CSA2_Q_FP4 / CSA2_Q_FP8 / CSA2_Q_MXFP4 (FULL, REINDEX); a
+                                    REINDEX layer uses CSA2_Q_MXFP4 exactly when its
+                                    source Full layer does (the indexer K's scales
+                                    follow the format), else CSA2_ERR_INVALID_ARG */
     int32_t kv_fmt;              /* CSA2_KV_* of kv_sc (FULL: the layers up to the next Full layer read it) */
     const void* q_idx;           /* (device) indexer q (FULL, REINDEX) */
-    const uint8_t* q_sc;         /* (device) [total_q][H] */
+    const uint8_t* q_sc;         /* (device) [total_q][H], or [total_q][H][4] (CSA2_Q_MXFP4) */
     const float* w;              /* (device) [total_q][H] */
     const uint8_t* kv_fp4;       /* (device) main KV of this layer (FULL) */
     const uint8_t* kv_sc;

@@ -75,6 +75,7 @@ def test_index_score_validation():
     assert _score(b, cand=FAKE, cstride=64, stride=32) == C.CSA2_ERR_INVALID_ARG
     assert _score(b, cand=FAKE, cstride=64, stride=64, q_fmt=1) == C.CSA2_ERR_UNSUPPORTED
     assert _score(b, q_fmt=1, hist=FAKE) == C.CSA2_ERR_UNSUPPORTED   # no fused histogram for E4M3 queries
+    assert _score(b, q_fmt=3) == C.CSA2_ERR_INVALID_ARG
     many = HostBatch([1000], [list(range(990, 1000))])
     assert _score(many, hist=FAKE) == C.CSA2_ERR_UNSUPPORTED         # nor for the many-query scan
 
@@ -184,3 +185,11 @@ def test_layer_chain_schedule_validation():
     assert run([full], ws=None, n=0) == C.CSA2_ERR_WORKSPACE
     assert run([dict(full, q_main=None)]) == C.CSA2_ERR_INVALID_ARG
     assert run([full], params=C.csa2_chain_params(64, 64, 512, 16, 2048, 0.044)) == C.CSA2_ERR_UNSUPPORTED
+    # a Reindex layer reads its source's indexer K, whose scale layout follows
+    # the source's format: MXFP4 queries exactly when the source has them
+    rx = dict(mode=C.CSA2_MODE_REINDEX, q_idx=FAKE, q_sc=FAKE, w=FAKE, **base)
+    mx = C.CSA2_Q_MXFP4
+    assert run([dict(full, q_fmt=mx), dict(rx, q_fmt=C.CSA2_Q_FP4)]) == C.CSA2_ERR_INVALID_ARG
+    assert run([full, dict(rx, q_fmt=mx)]) == C.CSA2_ERR_INVALID_ARG
+    assert run([full, dict(rx, q_fmt=C.CSA2_Q_FP8)]) == C.CSA2_ERR_UNSUPPORTED
+    assert run([dict(full, q_fmt=3)]) == C.CSA2_ERR_INVALID_ARG

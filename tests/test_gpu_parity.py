@@ -33,16 +33,22 @@ DECODE_CASES = {
     "ragged_t1": dict(name="decode_c1", lens=[1, 7, 63, 64, 65, 255, 4097, 9000]),
     "ragged_t4": dict(name="ragged_c4", lens=[5, 64, 300, 5000, 70000], T=4),
     "h32": dict(name="decode_c1", lens=[100, 3000], H=32),
+    # the report's indexer format: FP4 queries and keys with an E8M0 per 32
+    # channels (one query row and four rows per sequence, 64 and 32 heads)
+    "c0_mx": dict(name="decode_c0", q_fmt=synth.Q_MXFP4),
+    "ragged_t4_mx": dict(name="ragged_c4", lens=[5, 64, 300, 5000, 70000], T=4, q_fmt=synth.Q_MXFP4),
+    "h32_mx": dict(name="decode_c1", lens=[100, 3000], H=32, q_fmt=synth.Q_MXFP4),
 }
 
 
 def _decode_wl(case):
     c = DECODE_CASES[case]
+    q_fmt = c.get("q_fmt", synth.Q_FP4)
     if "lens" not in c:
-        return synth.config(c["name"])
+        return synth.config(c["name"], q_fmt=q_fmt)
     T = c.get("T", 1)
     return synth.make_workload(case, 0xC5A2F000 + len(case), c["lens"], T, [(20, synth.MODE_FULL, False)],
-                               H=c.get("H", 64), Hm=16)
+                               H=c.get("H", 64), Hm=16, q_fmt=q_fmt)
 
 
 @pytest.mark.parametrize("case", list(DECODE_CASES))
@@ -50,14 +56,14 @@ def test_index_score_full_bitwise(case):
     wl = _decode_wl(case)
     dw = DevWorkload(wl)
     L, dL = wl.layers[0], dw.layers[0]
-    got = C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP4, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc)
+    got = C.csa2_index_score(dw.batch, wl.H, L.q_fmt, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc)
     torch.cuda.synchronize()
-    ref = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, synth.Q_FP4)
+    ref = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, L.q_fmt)
     _full_rows_equal(got, ref, wl)
     # deterministic across runs; the variant that also builds the Top-K histogram
     # writes the same scores, and its histogram equals one counted on the host
     hist = C.hist_buffer(dw.batch)
-    again = C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP4, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc,
+    again = C.csa2_index_score(dw.batch, wl.H, L.q_fmt, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc,
                                hist=hist)
     _full_rows_equal(again, ref, wl)  # slots past N_b are not written; compare the written ones
     vis = oracle.row_visible(wl)
@@ -69,21 +75,22 @@ def test_index_score_full_bitwise(case):
     assert torch.equal(C.csa2_topk(dw.batch, got, 512, hist=hist), C.csa2_topk(dw.batch, got, 512))
 
 
-def test_index_score_cand_bitwise():
-    wl = synth.config("chain_c2", n_seq=2, n=30000, Hm=16)
+@pytest.mark.parametrize("q_fmt", [synth.Q_FP4, synth.Q_MXFP4])
+def test_index_score_cand_bitwise(q_fmt):
+    wl = synth.config("chain_c2", n_seq=2, n=30000, Hm=16, q_fmt=q_fmt)
     dw = DevWorkload(wl)
     full = wl.layers[0]
-    sc = oracle.index_score(wl, full.q_idx, full.q_sc, full.w, synth.Q_FP4)
+    sc = oracle.index_score(wl, full.q_idx, full.q_sc, full.w, q_fmt)
     vis = oracle.row_visible(wl)
     _, pool, cnt = oracle.block_pool(sc, vis)
     pool[0, 100:140] = -1  # holes are allowed in a candidate list
     L = [x for x in wl.layers if x.mode == synth.MODE_REINDEX][0]
     dL = [x for x in dw.layers if x["index"] == L.index][0]
     hist = C.hist_buffer(dw.batch)
-    got = C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP4, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc,
+    got = C.csa2_index_score(dw.batch, wl.H, q_fmt, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc,
                              cand=dev(pool), hist=hist)
     torch.cuda.synchronize()
-    ref = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, synth.Q_FP4, cand=pool)
+    ref = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, q_fmt, cand=pool)
     assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))
     h = hist.cpu().numpy()
     for r in range(wl.total_q):
@@ -91,15 +98,18 @@ def test_index_score_cand_bitwise():
         assert np.array_equal(h[r], np.bincount(fin.view(np.uint32) >> 19, minlength=4096)), r
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "fp8_h32", "fp4"])
+@pytest.mark.parametrize("fmt", ["fp8", "fp8_h32", "fp4", "mxfp4", "mxfp4_h32"])
 def test_index_score_prefill_bitwise(fmt):
     if fmt == "fp8":
         wl = synth.config("prefill_c3", tokens=6002, T=150, n_layers=1, Hm=16)
     elif fmt == "fp8_h32":  # 32 indexer heads, two sequences, 61 rows each (a ragged row group)
         wl = synth.make_workload("pf8h32", 91, [2500, 3100], 61, [(2, synth.MODE_FULL, False)], ratio=2, H=32,
                                  Hm=16, q_fmt=synth.Q_FP8)
-    else:  # FP4 queries, 9 rows per sequence, ratio 2: the many-query kernel
+    elif fmt == "fp4":  # FP4 queries, 9 rows per sequence, ratio 2: the many-query kernel
         wl = synth.make_workload("pf4", 77, [1500, 2100], 9, [(2, synth.MODE_FULL, False)], ratio=2, Hm=16)
+    else:  # the same kernel with the report's MXFP4 indexer format
+        wl = synth.make_workload("pf4mx", 78, [1500, 2100], 9, [(2, synth.MODE_FULL, False)], ratio=2, Hm=16,
+                                 H=32 if fmt.endswith("h32") else 64, q_fmt=synth.Q_MXFP4)
     dw = DevWorkload(wl)
     L, dL = wl.layers[0], dw.layers[0]
     got = C.csa2_index_score(dw.batch, wl.H, L.q_fmt, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc)
@@ -267,7 +277,14 @@ CHAIN_CASES = {
     "c2_small_e4m3kv": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16, kv_fmt=1),
     # the pages' cache formats for main KV (E4M3 per 16 channels) and SWA (FP8, as OCP MXFP8)
     "c2_small_pages_fmt": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16, kv_fmt=1, swa_fmt=1),
+    # the report's indexer format (MXFP4 queries and keys) through Full + pool, Reindex and Reuse
+    "c2_small_mx_idx": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16, q_fmt=synth.Q_MXFP4),
+    # every cache in the pages' format: main KV E2M1 + E4M3/16, indexer MXFP4, SWA FP8 (MXFP8)
+    "c2_small_pages_all": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16, kv_fmt=1, swa_fmt=1,
+                                               q_fmt=synth.Q_MXFP4),
     "c4_small": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16),
+    "c4_small_mx_idx": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16,
+                                            q_fmt=synth.Q_MXFP4),
     "c3_small": lambda: synth.config("prefill_c3", tokens=4000, T=96, Hm=16),
     # degenerate rows: a sequence with no entries (its row attends to its
     # window alone), one with entries but no query row, and one with a
@@ -309,11 +326,14 @@ def test_layer_chain_matches_oracle(case):
 
 
 @pytest.mark.gpu
-def test_decode_step_40_matches_oracle():
+@pytest.mark.parametrize("fmt", ["default", "pages"])
+def test_decode_step_40_matches_oracle(fmt):
     """One decode token through all 40 layers, as the five chains the layers
     form (sliding-window layers, three encoder groups at ratio 2, the decoder
-    at ratio 1), each against the oracle."""
-    for wl in synth.decode_step_40(n_seq=2, tokens=6000, Hm=16):
+    at ratio 1), each against the oracle; in this library's default formats
+    and in the pages' (E4M3/16 main KV, MXFP4 indexer, FP8 SWA)."""
+    kw = dict(kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4) if fmt == "pages" else {}
+    for wl in synth.decode_step_40(n_seq=2, tokens=6000, Hm=16, **kw):
         dw = DevWorkload(wl)
         outs, (pb, pp, pc), _ = run_chain(dw)
         torch.cuda.synchronize()
