@@ -49,7 +49,7 @@ def parse():
                     help="skip the layer-chain timings of the other four workloads")
     ap.add_argument("--workload", default="decode_c1",
                     choices=["decode_c1", "decode_c0", "chain_c2", "prefill_c3", "ragged_c4", "replay_c5",
-                             "decode_step_40"],
+                             "decode_step_40", "decode_step_40_pages_fmt"],
                     help="decode_c1 (default) prints the full line; the others time their layer chain only")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for hardware-counter collection: a few steps, a few scan launches and one "
@@ -126,9 +126,10 @@ def main():
     torch.cuda.set_device(0)
     C.lib()
     dev = torch.device("cuda:0")
-    if args.workload == "decode_step_40":
+    if args.workload.startswith("decode_step_40"):
         res = {"metric": METRIC, "workload": args.workload}
-        res.update(bench_step_40(synth, torch, dev, reps=args.steps))
+        fmt = dict(kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4) if args.workload.endswith("pages_fmt") else {}
+        res.update(bench_step_40(synth, torch, dev, reps=args.steps, **fmt))
         print(json.dumps(res), flush=True)
         return
     if args.workload != "decode_c1":

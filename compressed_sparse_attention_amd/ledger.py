@@ -9,9 +9,11 @@ hold half the sequence each (ratio 2) and one decoder source layer the whole
 sequence, so a token costs (3/2 + 1) * 356 = 890 B (the report, abstract and
 section 4.2.1, quotes 890 B/token).
 
-This library stores main KV as OCP MXFP4 (E2M1 with one E8M0 scale per 32
-channels: 256 + 16 B) and indexer K as E2M1 with one E8M0 scale per row
+By default this library stores main KV as OCP MXFP4 (E2M1 with one E8M0 scale
+per 32 channels: 256 + 16 B) and indexer K as E2M1 with one E8M0 scale per row
 (64 + 1 B): 337 B per position, 842.5 B per token under the same layer count.
+With main KV in E2M1 + E4M3 per 16 channels and the indexer in MXFP4 (one E8M0
+per 32 channels for queries and keys), it stores the layout above ("pages").
 """
 
 LAYOUTS = {
