@@ -58,6 +58,8 @@ def lib():
         L.orc_visible.restype = i64
         L.orc_index_score.argtypes = [i64, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, i64, i32]
         L.orc_index_score.restype = i32
+        L.orc_kv_append.argtypes = [i64, vp, vp, vp, i32, i64, vp, vp]
+        L.orc_kv_append.restype = i32
         L.orc_topk.argtypes = [i64, vp, i64, vp, vp, i64, i32, vp, i32]
         L.orc_block_pool.argtypes = [i64, vp, i64, vp, i32, i32, vp, vp, vp, i32]
         L.orc_gather_dequant.argtypes = [i64, vp, vp, vp, vp, i32, vp, i32, vp]
@@ -106,6 +108,24 @@ def row_visible(wl):
 
 
 # --- steps ------------------------------------------------------------------
+
+def kv_append(x, cs, dst, kv_fmt, rows, kv_fp4=None, kv_sc=None):
+    """Cache append: RoPE on the last 64 latent channels, then quantise all 512
+    (report 2.4.4) into rows dst of a main-KV cache of `rows` rows.  x [n][512]
+    f32, cs [n][32][2] f32 (cos, sin per pair), dst [n] i64.  Returns the
+    cache arrays (fresh zeroed ones unless given)."""
+    x = _c(x, np.float32)
+    cs = _c(cs, np.float32)
+    dst = _c(dst, np.int64)
+    if kv_fp4 is None:
+        kv_fp4 = np.zeros((rows, 256), np.uint8)
+    if kv_sc is None:
+        kv_sc = np.zeros((rows, 32 if kv_fmt == 1 else 16), np.uint8)
+    rc = lib().orc_kv_append(len(dst), _p(x), _p(cs), _p(dst), kv_fmt, rows, _p(kv_fp4), _p(kv_sc))
+    if rc:
+        raise ValueError("kv_append: bad format or destination row")
+    return kv_fp4, kv_sc
+
 
 def index_score(wl, q_idx, q_sc, w, q_fmt, cand=None, n_slots=None, rows=None):
     """Scores [rows][slots] f32.  Full mode (cand None): slots = max N_b;

@@ -513,3 +513,86 @@ void orc_sparse_attn(int64_t total_q, const int32_t* row_seq, const int32_t* q_p
                   scale, out, lse};
     parallel_for(total_q, nthreads, attn_row, &c);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Cache append ([R] 2.4.4: the main KV is quantised after RoPE, all 512     */
+/* channels including the rotated part; [R] 4.2.1: RoPE sub-dimension 64).   */
+/* ------------------------------------------------------------------------ */
+/* Readings: the rotated part is channels 448..511, pairs (448 + 2i, 449 + 2i)
+ * turned by the caller's angle of pair i (cos, sin given per entry), each
+ * output one fp32 product difference or sum with no fused multiply-add.  The
+ * quantiser's decisions are taken in fp32 on correctly rounded quotients:
+ *   E4M3/16 (kv_fmt 1): X = E4M3(fl32(amax / 6)) to nearest even (2^-9 where
+ *     that is 0), codes E2M1(fl32(x / X)) to nearest even, saturating at 6;
+ *   MXFP4/32 (kv_fmt 0, OCP MX v1.0): X = 2^(floor(log2 amax) - 2) (2^0 for an
+ *     all-zero block), codes E2M1(x / X) to nearest even, saturating at 6. */
+
+/* nearest of a finite set of non-negative grid values (ties to the even
+ * code, i.e. the one whose last mantissa bit is 0) -- written as a search
+ * over the grid so that it follows the definition rather than a bit trick */
+static int nearest_code(double a, const double* grid, int n) {
+    int best = 0;
+    for (int i = 1; i < n; ++i) {
+        double db = fabs(a - grid[best]), di = fabs(a - grid[i]);
+        if (di < db || (di == db && (i & 1) == 0 && (best & 1) == 1)) best = i;
+    }
+    return best;
+}
+
+static uint8_t e2m1_rne(float q) {
+    static const double g[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    int c = nearest_code(fabs((double)q), g, 8); /* beyond 6 the nearest is 6: saturation */
+    return (uint8_t)(c | (q < 0.0f ? 8 : 0));
+}
+
+static uint8_t e4m3_rne_pos(float q) { /* q >= 0; codes 0..126 (126 = 448) */
+    static double g[127];
+    static int ready = 0;
+    if (!ready) { for (int i = 0; i < 127; ++i) g[i] = orc_e4m3((uint8_t)i); ready = 1; }
+    return (uint8_t)nearest_code((double)q, g, 127);
+}
+
+static int floor_log2_f(float a) { int e; frexpf(a, &e); return e - 1; }
+
+/* Append n entries: x [n][512] fp32 latents before RoPE, cs [n][32][2] the
+ * cos and sin of each pair's angle, dst [n] the cache row of each entry.
+ * Writes kv_fp4 [rows][256] and kv_sc [rows][16] (kv_fmt 0) or [rows][32]
+ * (kv_fmt 1).  Returns 0, or 1 for a bad format or a row outside [0, rows). */
+int orc_kv_append(int64_t n, const float* x, const float* cs, const int64_t* dst, int kv_fmt, int64_t rows,
+                  uint8_t* kv_fp4, uint8_t* kv_sc) {
+    if (kv_fmt != 0 && kv_fmt != 1) return 1;
+    for (int64_t e = 0; e < n; ++e) {
+        if (dst[e] < 0 || dst[e] >= rows) return 1;
+        float v[512];
+        for (int c = 0; c < 512; ++c) v[c] = x[e * 512 + c];
+        for (int i = 0; i < 32; ++i) {
+            float a = v[448 + 2 * i], b = v[449 + 2 * i];
+            float co = cs[(e * 32 + i) * 2], si = cs[(e * 32 + i) * 2 + 1];
+            float ac = a * co, bs = b * si, as = a * si, bc = b * co;
+            v[448 + 2 * i] = ac - bs;
+            v[449 + 2 * i] = as + bc;
+        }
+        uint8_t* codes = kv_fp4 + dst[e] * 256;
+        int bl = kv_fmt == 1 ? 16 : 32;
+        for (int b0 = 0; b0 < 512; b0 += bl) {
+            float amax = 0.0f;
+            for (int c = b0; c < b0 + bl; ++c) amax = fmaxf(amax, fabsf(v[c]));
+            float X;
+            if (kv_fmt == 1) {
+                uint8_t sc = e4m3_rne_pos(amax / 6.0f);
+                if (sc == 0) sc = 1;
+                kv_sc[dst[e] * 32 + b0 / 16] = sc;
+                X = (float)orc_e4m3(sc);
+            } else {
+                int se = amax > 0.0f ? floor_log2_f(amax) - 2 : 0;
+                kv_sc[dst[e] * 16 + b0 / 32] = (uint8_t)(se + 127);
+                X = ldexpf(1.0f, se);
+            }
+            for (int c = b0; c < b0 + bl; c += 2) {
+                uint8_t lo = e2m1_rne(v[c] / X), hi = e2m1_rne(v[c + 1] / X);
+                codes[c / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+    return 0;
+}

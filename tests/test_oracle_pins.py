@@ -720,3 +720,118 @@ def test_mxfp8_swa_encoder_and_decode():
     want = np.array([oracle.e4m3(int(row[c])) * oracle.e8m0(int(row[512 + c // 32])) for c in range(512)], np.float32)
     for h in range(16):
         np.testing.assert_array_equal(out[0, h], want)
+
+
+# ---------------------------------------------------------------------------
+# cache append: RoPE on the last 64 latent channels, then quantise all 512
+# (report 2.4.4); the encoder below is written from the format definitions
+# ---------------------------------------------------------------------------
+
+def _e4m3_spec(code):
+    """OCP OFP8 E4M3 (FN) value of a non-negative code 0..126, from its fields."""
+    e, m = code >> 3, code & 7
+    return Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+
+
+E4M3_SPEC = [_e4m3_spec(c) for c in range(127)]
+
+
+def _nearest_even(a: Fraction, grid):
+    """Index of the grid value nearest to a >= 0; ties go to the even index."""
+    best = min(range(len(grid)), key=lambda i: (abs(a - grid[i]), i & 1))
+    return best
+
+
+def _spec_append(x, cs, kv_fmt):
+    """One entry: rotation in float32 (products, then difference / sum), then
+    the quantiser with its decisions on float32 quotients."""
+    v = np.asarray(x, np.float32).copy()
+    for i in range(32):
+        a, b = v[448 + 2 * i], v[449 + 2 * i]
+        co, si = np.float32(cs[i, 0]), np.float32(cs[i, 1])
+        v[448 + 2 * i] = np.float32(a * co) - np.float32(b * si)
+        v[449 + 2 * i] = np.float32(a * si) + np.float32(b * co)
+    bl = 16 if kv_fmt == 1 else 32
+    codes, scales = [], []
+    e2m1 = [Fraction(z).limit_denominator(2) for z in E2M1_SPEC]
+    for b0 in range(0, 512, bl):
+        blk = v[b0:b0 + bl]
+        amax = np.float32(np.max(np.abs(blk)))
+        if kv_fmt == 1:
+            sc = _nearest_even(Fraction(float(np.float32(amax / np.float32(6.0)))), E4M3_SPEC) or 1
+            X = np.float32(float(E4M3_SPEC[sc]))
+        else:
+            se = math.frexp(float(amax))[1] - 3 if amax > 0 else 0
+            sc, X = se + 127, np.float32(2.0 ** se)
+        scales.append(sc)
+        for z in blk:
+            q = np.float32(z / X)
+            c = _nearest_even(abs(Fraction(float(q))), e2m1)
+            codes.append(c | (8 if q < 0 else 0))
+    packed = np.array([codes[2 * i] | (codes[2 * i + 1] << 4) for i in range(256)], np.uint8)
+    return packed, np.array(scales, np.uint8)
+
+
+def _angles(rng, n):
+    th = rng.uniform(-np.pi, np.pi, size=(n, 32))
+    return np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
+
+
+@pytest.mark.parametrize("kv_fmt", [0, 1])
+def test_kv_append_matches_spec_encoder(kv_fmt):
+    """Random latents (three magnitudes of block, an all-zero block, a block
+    past the saturation point), random angles, rows written out of order:
+    every row equals the encoder written here from the format definitions,
+    and rows not written stay untouched."""
+    rng = np.random.default_rng(11 + kv_fmt)
+    n = 6
+    x = (rng.standard_normal((n, 512)) * np.array([1, 30, 1e-3, 1, 1, 1])[:, None]).astype(np.float32)
+    x[3, 0:32] = 0.0                       # an all-zero block
+    x[4, 64:96] = 5000.0                   # beyond 6 x 448: the E4M3 scale saturates
+    cs = _angles(rng, n)
+    dst = np.array([7, 2, 0, 5, 3, 9])
+    kv, sc = oracle.kv_append(x, cs, dst, kv_fmt, 10)
+    for e in range(n):
+        want_c, want_s = _spec_append(x[e], cs[e], kv_fmt)
+        assert np.array_equal(kv[dst[e]], want_c), e
+        assert np.array_equal(sc[dst[e]], want_s), e
+    for r in set(range(10)) - set(dst.tolist()):
+        assert not kv[r].any() and not sc[r].any()
+    with pytest.raises(ValueError):
+        oracle.kv_append(x[:1], cs[:1], np.array([10]), kv_fmt, 10)
+
+
+@pytest.mark.parametrize("kv_fmt", [0, 1])
+def test_kv_append_quarter_turn_and_error_bound(kv_fmt):
+    """A quarter turn maps (a, b) to (-b, a) exactly, so appending x with it
+    equals appending the pre-turned x unrotated.  For any angle the decoded
+    row is within the quantiser's half step of the float64 rotation."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 512)).astype(np.float32)
+    quarter = np.zeros((4, 32, 2), np.float32)
+    quarter[..., 1] = 1.0
+    ident = np.zeros((4, 32, 2), np.float32)
+    ident[..., 0] = 1.0
+    xt = x.copy()
+    xt[:, 448::2], xt[:, 449::2] = -x[:, 449::2], x[:, 448::2]
+    dst = np.arange(4)
+    a = oracle.kv_append(x, quarter, dst, kv_fmt, 4)
+    b = oracle.kv_append(xt, ident, dst, kv_fmt, 4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    cs = _angles(rng, 4)
+    kv, sc = oracle.kv_append(x, cs, dst, kv_fmt, 4)
+    rot = x.astype(np.float64).copy()
+    co, si = cs[..., 0].astype(np.float64), cs[..., 1].astype(np.float64)
+    p, q = x[:, 448::2].astype(np.float64), x[:, 449::2].astype(np.float64)
+    rot[:, 448::2], rot[:, 449::2] = p * co - q * si, p * si + q * co
+    if kv_fmt == 1:
+        scale = np.repeat(np.array([[oracle.e4m3(int(c)) for c in r] for r in sc]), 16, axis=1)
+    else:
+        scale = np.repeat(np.exp2(sc.astype(np.float64) - 127), 32, axis=1)
+    deq = decode_fp4_rows(kv, 512) * scale
+    # the E2M1 grid steps by at most 2 below 6, so a half step is at most one
+    # scale unit.  The E4M3 scale follows amax / 6, so nothing saturates by
+    # more than that; the MX scale 2^(floor(log2 amax) - 2) leaves values up to
+    # 8 units that clamp to 6: two units.  1e-6 covers the rotation's rounding.
+    units = 1.0 if kv_fmt == 1 else 2.0
+    assert np.all(np.abs(deq - rot) <= units * scale * (1 + 1e-6))
