@@ -416,7 +416,41 @@ def bench_workloads(synth, C, torch, dev):
     # the same step with every cache in the report's formats (E4M3/16 main KV,
     # MXFP4 indexer, FP8 SWA as MXFP8)
     res["decode_step_40_pages_fmt"] = bench_step_40(synth, torch, dev, kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4)
+    for kv_fmt in (1, 0):
+        res["kv_append_e4m3" if kv_fmt == 1 else "kv_append_mxfp4"] = bench_append(C, torch, dev, kv_fmt)
     return res
+
+
+def bench_append(C, torch, dev, kv_fmt, n=131072, reps=20):
+    """The cache append (RoPE on 64 channels, then FP4 quantisation) of
+    131,072 entries, one source layer's cache of the 262,144-token prefill
+    context at ratio 2.  Algorithmic bytes per entry: the f32 latent (2,048),
+    its angles (256) and row index (8) read; the code row (256) and its scales
+    (32 or 16) written."""
+    g = torch.Generator(device=dev).manual_seed(7)
+    x = torch.randn((n, 512), generator=g, device=dev, dtype=torch.float32)
+    th = torch.rand((n, 32), generator=g, device=dev) * 6.2831853
+    cs = torch.stack([torch.cos(th), torch.sin(th)], -1).contiguous()
+    dst = torch.randperm(n, generator=g, device=dev).to(torch.int64)
+    kv = torch.empty((n, 256), dtype=torch.uint8, device=dev)
+    sc = torch.empty((n, 32 if kv_fmt == 1 else 16), dtype=torch.uint8, device=dev)
+    C.csa2_kv_append(x, cs, dst, kv, sc, kv_fmt=kv_fmt)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        C.csa2_kv_append(x, cs, dst, kv, sc, kv_fmt=kv_fmt)
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1000.0 / reps
+    nb = n * (2048 + 256 + 8 + 256 + sc.shape[1])
+    gbs = nb / (us * 1e-6) / 1e9
+    log(f"[bench] kv_append (kv_fmt {kv_fmt}): {us:.1f} us for {n} entries, {gbs:.0f} GB/s")
+    r = {"us": round(us, 2), "entries": n, "algorithmic_bytes": nb, "hbm_gbs": round(gbs, 1),
+         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del x, th, cs, dst, kv, sc
+    torch.cuda.empty_cache()
+    return r
 
 
 def bench_step_40(synth, torch, dev, reps=5, **fmt):

@@ -184,6 +184,19 @@ CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
 
+CSA2_API csa2_status csa2_kv_append(int64_t n, const float* x, const float* rope_cs, const int64_t* dst_row,
+                                    int64_t n_rows, int32_t kv_fmt, uint8_t* kv_fp4, uint8_t* kv_sc,
+                                    hipStream_t stream) {
+    if (n < 0) return CSA2_ERR_INVALID_ARG;
+    if (kv_fmt != CSA2_KV_MXFP4 && kv_fmt != CSA2_KV_E4M3_16) return CSA2_ERR_UNSUPPORTED;
+    if (n == 0) return CSA2_OK;
+    if (!x || !rope_cs || !dst_row || !kv_fp4 || !kv_sc || n_rows < 1) return CSA2_ERR_INVALID_ARG;
+    if ((n + 3) / 4 > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+    if (((uintptr_t)x | (uintptr_t)rope_cs | (uintptr_t)kv_fp4) & 15) return CSA2_ERR_INVALID_ARG;
+    const hipError_t e = launch_kv_append(n, x, rope_cs, dst_row, n_rows, kv_fmt, kv_fp4, kv_sc, stream);
+    return e == hipSuccess ? CSA2_OK : hip_fail(e);
+}
+
 CSA2_API csa2_status csa2_topk(const csa2_batch* batch, const float* scores, int64_t score_stride,
                                const int32_t* cand, int32_t cand_stride, const int32_t* cand_count, int32_t K,
                                const uint32_t* hist, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -1,0 +1,130 @@
+// Cache append: a new main-KV entry is rotated and quantised into its row.
+//
+// Report "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression",
+// section 2.4.4: the main KV is quantised after RoPE, all 512 channels,
+// rotated part included, in E2M1 with one E4M3 scale per 16 channels (NVFP4's
+// layout without its second-level scale); the OCP MXFP4 form (one E8M0 per 32
+// channels) is this library's other main-KV format.  Section 4.2.1: the RoPE
+// part of the 512-channel latent is 64 dimensions.
+//
+// Readings: the rotated channels are 448..511, pair i = (448 + 2i, 449 + 2i)
+// turned by the caller's (cos, sin) of that pair, each output one rounded
+// product difference or sum (no fused multiply-add).  The quantiser decides
+// in fp32 on correctly rounded quotients: E4M3/16: X = E4M3(amax / 6) to
+// nearest even (2^-9 where that is 0); MXFP4/32: X = 2^(floor(log2 amax) - 2)
+// clamped to the E8M0 range (2^0 for an all-zero block); codes E2M1(x / X) to
+// nearest even, saturating at 6.
+//
+// One wave per entry: lane l holds channels 8l .. 8l + 7, so a 16-channel
+// block is a lane pair and a 32-channel block a lane quad; the 256-byte code
+// row is one dword per lane.
+#include <hip/hip_runtime.h>
+
+#include "csa2_internal.h"
+
+namespace csa2 {
+namespace {
+
+// nearest E2M1 code of q (ties to the even code), saturating at 6
+__device__ __forceinline__ uint32_t e2m1_code_rne(float q) {
+    const float a = fabsf(q);
+    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+    return c | (q < 0.0f ? 8u : 0u);
+}
+
+// nearest E4M3 code of q >= 0 (ties to even), saturating at 448 (code 126)
+__device__ __forceinline__ uint32_t e4m3_code_rne(float q) {
+    if (!(q < 448.0f)) return 126u;
+    if (q < 0.015625f) return (uint32_t)rintf(q * 512.0f);  // subnormal steps of 2^-9 (8 -> 2^-6, code 8)
+    int e;
+    const float m = frexpf(q, &e);                           // q = m 2^e, m in [0.5, 1)
+    const uint32_t m3 = (uint32_t)rintf((m * 2.0f - 1.0f) * 8.0f);  // exact scalings, then one rounding
+    const uint32_t c = ((uint32_t)(e - 1 + 7) << 3) + m3;   // m3 = 8 carries into the exponent
+    return c < 126u ? c : 126u;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t e = c >> 3, m = c & 7u;
+    return e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), (int)e - 10);
+}
+
+template <int KVF>
+__global__ __launch_bounds__(256) void k_kv_append(const float* __restrict__ x, const float* __restrict__ cs,
+                                                   const int64_t* __restrict__ dst, int64_t n, int64_t rows,
+                                                   uint8_t* __restrict__ kv, uint8_t* __restrict__ kv_sc) {
+    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (e >= n) return;
+    const int64_t r = dst[e];
+    if (r < 0 || r >= rows) return;  // rows outside the cache are left alone (the host cannot check them)
+
+    float v[8];
+    {
+        const float4* src = reinterpret_cast<const float4*>(x + e * 512 + 8 * lane);
+        const float4 a = src[0], b = src[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    if (lane >= 56) {  // channels 448 .. 511: pairs 4 (lane - 56) .. + 3
+        // each product rounded on its own: the default contraction would fuse
+        // a cos - b sin into one multiply-add, which rounds differently
+#pragma clang fp contract(off)
+        const float4* cp = reinterpret_cast<const float4*>(cs + (e * 32 + 4 * (lane - 56)) * 2);
+        const float4 c0 = cp[0], c1 = cp[1];
+        const float co[4] = {c0.x, c0.z, c1.x, c1.z}, si[4] = {c0.y, c0.w, c1.y, c1.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float a = v[2 * k], b = v[2 * k + 1];
+            v[2 * k] = a * co[k] - b * si[k];
+            v[2 * k + 1] = a * si[k] + b * co[k];
+        }
+    }
+
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    if constexpr (KVF == 0) am = fmaxf(am, __shfl_xor(am, 2));
+
+    uint32_t sc;
+    float X = 1.0f;
+    int se = 0;
+    if constexpr (KVF == 1) {
+        sc = e4m3_code_rne(__fdiv_rn(am, 6.0f));
+        sc = sc ? sc : 1u;
+        X = e4m3_value(sc);
+    } else {
+        if (am > 0.0f) {
+            int ex;
+            frexpf(am, &ex);  // am = m 2^ex, m in [0.5, 1): floor(log2 am) = ex - 1
+            se = ex - 3 < -127 ? -127 : ex - 3;
+        }
+        sc = (uint32_t)(se + 127);
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float q = KVF == 1 ? __fdiv_rn(v[i], X) : ldexpf(v[i], -se);  // a power of two scales exactly
+        word |= e2m1_code_rne(q) << (4 * i);
+    }
+    *reinterpret_cast<uint32_t*>(kv + r * 256 + 4 * lane) = word;
+    if constexpr (KVF == 1) {
+        if ((lane & 1) == 0) kv_sc[r * 32 + (lane >> 1)] = (uint8_t)sc;
+    } else {
+        if ((lane & 3) == 0) kv_sc[r * 16 + (lane >> 2)] = (uint8_t)sc;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(int64_t n, const float* x, const float* cs, const int64_t* dst, int64_t rows, int kv_fmt,
+                            uint8_t* kv, uint8_t* kv_sc, hipStream_t s) {
+    const dim3 grid((unsigned)((n + 3) / 4));
+    if (kv_fmt == 1)
+        hipLaunchKernelGGL(k_kv_append<1>, grid, dim3(256), 0, s, x, cs, dst, n, rows, kv, kv_sc);
+    else
+        hipLaunchKernelGGL(k_kv_append<0>, grid, dim3(256), 0, s, x, cs, dst, n, rows, kv, kv_sc);
+    return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -174,6 +174,34 @@ CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_
                                       const uint8_t* k_sc, const int32_t* cand, int32_t cand_stride,
                                       float* scores, int64_t score_stride, uint32_t* hist, hipStream_t stream);
 
+/* ---- cache append ---------------------------------------------------------
+ * Writes new main-KV entries into their cache rows the way the report stores
+ * them (section 2.4.4: the cache is quantised after RoPE, all 512 channels
+ * including the rotated part; section 4.2.1: the RoPE part is 64 dimensions).
+ * Entry i (i < n):
+ *   1. rotation of channels 448..511: pair p = (448 + 2p, 449 + 2p), p < 32,
+ *      (a, b) -> (a cos - b sin, a sin + b cos) with (cos, sin) =
+ *      rope_cs[i][p][0..1], each product and the sum or difference rounded
+ *      to fp32 (no fused multiply-add);
+ *   2. quantisation into row dst_row[i] of kv_fp4 / kv_sc, by kv_fmt:
+ *      CSA2_KV_E4M3_16: per 16 channels X = E4M3(fl32(amax / 6)) to nearest
+ *        even (2^-9 where that is 0), kv_sc [rows][32];
+ *      CSA2_KV_MXFP4: per 32 channels X = 2^(floor(log2 amax) - 2), at least
+ *        2^-127 (1 for an all-zero block), kv_sc [rows][16] E8M0;
+ *      codes E2M1(fl32(x / X)) to nearest even, saturating at 6, element 2c in
+ *      the low nibble of byte c of the 256-byte row.
+ * x: [n][512] f32 (device, 16-byte aligned), the entries' latents before RoPE.
+ * rope_cs: [n][32][2] f32 (device, 16-byte aligned).
+ * dst_row: [n] i64 (device); a row outside [0, n_rows) is skipped (the host
+ *   cannot read it to check).  Two entries with one row race.
+ * kv_fp4: [n_rows][256] u8 (device, 16-byte aligned); kv_sc as above.
+ * Errors: n < 0, a NULL pointer or n_rows < 1 with n > 0, misaligned x,
+ * rope_cs or kv_fp4: CSA2_ERR_INVALID_ARG; an unknown kv_fmt:
+ * CSA2_ERR_UNSUPPORTED.  n == 0 does nothing. */
+CSA2_API csa2_status csa2_kv_append(int64_t n, const float* x, const float* rope_cs, const int64_t* dst_row,
+                                    int64_t n_rows, int32_t kv_fmt, uint8_t* kv_fp4, uint8_t* kv_sc,
+                                    hipStream_t stream);
+
 /* ---- Top-K ---------------------------------------------------------------
  * Per query row, the first min(K, n) slots under (score descending, entry
  * position ascending), written as entry positions in ascending order and -1

@@ -524,8 +524,9 @@ void orc_sparse_attn(int64_t total_q, const int32_t* row_seq, const int32_t* q_p
  * quantiser's decisions are taken in fp32 on correctly rounded quotients:
  *   E4M3/16 (kv_fmt 1): X = E4M3(fl32(amax / 6)) to nearest even (2^-9 where
  *     that is 0), codes E2M1(fl32(x / X)) to nearest even, saturating at 6;
- *   MXFP4/32 (kv_fmt 0, OCP MX v1.0): X = 2^(floor(log2 amax) - 2) (2^0 for an
- *     all-zero block), codes E2M1(x / X) to nearest even, saturating at 6. */
+ *   MXFP4/32 (kv_fmt 0, OCP MX v1.0): X = 2^(floor(log2 amax) - 2), at least
+ *     2^-127 (2^0 for an all-zero block), codes E2M1(x / X) to nearest even,
+ *     saturating at 6. */
 
 /* nearest of a finite set of non-negative grid values (ties to the even
  * code, i.e. the one whose last mantissa bit is 0) -- written as a search
@@ -585,6 +586,7 @@ int orc_kv_append(int64_t n, const float* x, const float* cs, const int64_t* dst
                 X = (float)orc_e4m3(sc);
             } else {
                 int se = amax > 0.0f ? floor_log2_f(amax) - 2 : 0;
+                if (se < -127) se = -127; /* the E8M0 range */
                 kv_sc[dst[e] * 16 + b0 / 32] = (uint8_t)(se + 127);
                 X = ldexpf(1.0f, se);
             }

@@ -193,3 +193,18 @@ def test_layer_chain_schedule_validation():
     assert run([full, dict(rx, q_fmt=mx)]) == C.CSA2_ERR_INVALID_ARG
     assert run([full, dict(rx, q_fmt=C.CSA2_Q_FP8)]) == C.CSA2_ERR_UNSUPPORTED
     assert run([dict(full, q_fmt=3)]) == C.CSA2_ERR_INVALID_ARG
+
+
+def test_kv_append_validation():
+    L = C.lib()
+
+    def app(n=4, x=FAKE, cs=FAKE, dst=FAKE, rows=8, fmt=1, kv=FAKE, sc=FAKE):
+        return L.csa2_kv_append(n, x, cs, dst, rows, fmt, kv, sc, None)
+
+    assert app(n=-1) == C.CSA2_ERR_INVALID_ARG
+    assert app(fmt=2) == C.CSA2_ERR_UNSUPPORTED
+    assert app(n=0, x=None) == C.CSA2_OK          # nothing to do, nothing launched
+    assert app(x=None) == C.CSA2_ERR_INVALID_ARG
+    assert app(dst=None) == C.CSA2_ERR_INVALID_ARG
+    assert app(rows=0) == C.CSA2_ERR_INVALID_ARG
+    assert app(x=FAKE + 4) == C.CSA2_ERR_INVALID_ARG   # x must be 16-byte aligned

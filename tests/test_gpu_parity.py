@@ -415,3 +415,45 @@ def test_layer_chain_equals_composition():
     assert torch.equal(outs[0]["idx"], idx20) and torch.equal(outs[2]["idx"], idx24)
     assert torch.equal(pp, pool) and torch.equal(pc, cnt) and torch.equal(pb, blocks)
     assert torch.equal(outs[0]["out"], o20) and torch.equal(outs[1]["out"], o21) and torch.equal(outs[2]["out"], o24)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kv_fmt", [0, 1])
+@pytest.mark.parametrize("n", [1, 5, 3000, 131072])
+def test_kv_append_bitwise(kv_fmt, n):
+    """The cache append (RoPE on the last 64 channels, then quantisation)
+    equals the oracle bit for bit: latents of three magnitudes, an all-zero
+    block and a saturating one, random angles, rows written out of order into
+    a larger cache whose other rows keep their contents.  131,072 entries is
+    one source layer's cache of the prefill context at ratio 2."""
+    rng = np.random.default_rng(1000 + n + kv_fmt)
+    x = (rng.standard_normal((n, 512), dtype=np.float32) * rng.choice([1e-3, 1.0, 40.0], size=(n, 1))).astype(np.float32)
+    if n >= 5:
+        x[2, :64] = 0.0
+        x[3, 100:140] = 7000.0
+    th = rng.uniform(-np.pi, np.pi, size=(n, 32))
+    cs = np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
+    rows = n + 7
+    dst = rng.permutation(rows)[:n].astype(np.int64)
+    ref_kv, ref_sc = oracle.kv_append(x, cs, dst, kv_fmt, rows)
+    nsc = 32 if kv_fmt == 1 else 16
+    kv = torch.full((rows, 256), 0xAB, dtype=torch.uint8, device="cuda")
+    sc = torch.full((rows, nsc), 0xCD, dtype=torch.uint8, device="cuda")
+    C.csa2_kv_append(dev(x), dev(cs), dev(dst), kv, sc, kv_fmt=kv_fmt)
+    torch.cuda.synchronize()
+    got_kv, got_sc = kv.cpu().numpy(), sc.cpu().numpy()
+    assert np.array_equal(got_kv[dst], ref_kv[dst])
+    assert np.array_equal(got_sc[dst], ref_sc[dst])
+    untouched = np.setdiff1d(np.arange(rows), dst)
+    assert np.all(got_kv[untouched] == 0xAB) and np.all(got_sc[untouched] == 0xCD)
+    # a destination outside the cache is skipped; the rest are written as before
+    if n >= 5:
+        bad = dst.copy()
+        bad[1] = rows + 3
+        kv2 = torch.zeros_like(kv)
+        sc2 = torch.zeros_like(sc)
+        C.csa2_kv_append(dev(x), dev(cs), dev(bad), kv2, sc2, kv_fmt=kv_fmt)
+        torch.cuda.synchronize()
+        keep = np.delete(np.arange(n), 1)
+        assert np.array_equal(kv2.cpu().numpy()[dst[keep]], ref_kv[dst[keep]])
+        assert not kv2.cpu().numpy()[dst[1]].any()

@@ -761,7 +761,7 @@ def _spec_append(x, cs, kv_fmt):
             sc = _nearest_even(Fraction(float(np.float32(amax / np.float32(6.0)))), E4M3_SPEC) or 1
             X = np.float32(float(E4M3_SPEC[sc]))
         else:
-            se = math.frexp(float(amax))[1] - 3 if amax > 0 else 0
+            se = max(math.frexp(float(amax))[1] - 3, -127) if amax > 0 else 0
             sc, X = se + 127, np.float32(2.0 ** se)
         scales.append(sc)
         for z in blk:
