@@ -60,6 +60,8 @@ def lib():
         L.orc_index_score.restype = i32
         L.orc_kv_append.argtypes = [i64, vp, vp, vp, i32, i64, vp, vp]
         L.orc_kv_append.restype = i32
+        L.orc_compress.argtypes = [i64, i32, vp, vp, vp]
+        L.orc_compress.restype = i32
         L.orc_topk.argtypes = [i64, vp, i64, vp, vp, i64, i32, vp, i32]
         L.orc_block_pool.argtypes = [i64, vp, i64, vp, i32, i32, vp, vp, vp, i32]
         L.orc_gather_dequant.argtypes = [i64, vp, vp, vp, vp, i32, vp, i32, vp]
@@ -108,6 +110,18 @@ def row_visible(wl):
 
 
 # --- steps ------------------------------------------------------------------
+
+def compress(c_tok, z_tok, m):
+    """Compressor: entry j = per-channel softmax over its m tokens of Z,
+    weighting C (tokens jm .. jm + m - 1).  c_tok, z_tok [n m][512] f32."""
+    c_tok = _c(c_tok, np.float32)
+    z_tok = _c(z_tok, np.float32)
+    n = c_tok.shape[0] // m
+    out = np.empty((n, 512), np.float32)
+    if lib().orc_compress(n, m, _p(c_tok), _p(z_tok), _p(out)):
+        raise ValueError("compress: bad arguments")
+    return out
+
 
 def kv_append(x, cs, dst, kv_fmt, rows, kv_fp4=None, kv_sc=None):
     """Cache append: RoPE on the last 64 latent channels, then quantise all 512

@@ -598,3 +598,29 @@ int orc_kv_append(int64_t n, const float* x, const float* cs, const int64_t* dst
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Compressor (reading note "DeepSeek V4.1 Flash: Pushing the Limits of KV   */
+/* Cache Compression": C_l = H W^KV are the KV entries and Z_l = H W^Z their */
+/* compression weights; CSA2 drops V4's overlapping windows and absolute     */
+/* position embedding).  Reading: entry j combines its m tokens jm..jm+m-1,  */
+/* per channel, with the softmax over those tokens of Z:                     */
+/*   e[j][c] = sum_i exp(Z[jm+i][c]) C[jm+i][c] / sum_i exp(Z[jm+i][c]).     */
+/* In double, rounded to float at the end.                                   */
+/* ------------------------------------------------------------------------ */
+int orc_compress(int64_t n_entries, int m, const float* c_tok, const float* z_tok, float* out) {
+    if (n_entries < 0 || m < 1) return 1;
+    for (int64_t j = 0; j < n_entries; ++j)
+        for (int c = 0; c < 512; ++c) {
+            double mx = -INFINITY;
+            for (int i = 0; i < m; ++i) mx = fmax(mx, (double)z_tok[(j * m + i) * 512 + c]);
+            double num = 0.0, den = 0.0;
+            for (int i = 0; i < m; ++i) {
+                double w = exp((double)z_tok[(j * m + i) * 512 + c] - mx);
+                num += w * (double)c_tok[(j * m + i) * 512 + c];
+                den += w;
+            }
+            out[j * 512 + c] = (float)(num / den);
+        }
+    return 0;
+}

@@ -835,3 +835,39 @@ def test_kv_append_quarter_turn_and_error_bound(kv_fmt):
     # 8 units that clamp to 6: two units.  1e-6 covers the rotation's rounding.
     units = 1.0 if kv_fmt == 1 else 2.0
     assert np.all(np.abs(deq - rot) <= units * scale * (1 + 1e-6))
+
+
+# ---------------------------------------------------------------------------
+# compressor: entry = per-channel softmax over its m tokens of Z, weighting C
+# ---------------------------------------------------------------------------
+
+def test_compress_special_cases():
+    rng = np.random.default_rng(21)
+    c = rng.standard_normal((12, 512)).astype(np.float32)
+    z = (rng.standard_normal((12, 512)) * 3).astype(np.float32)
+    # m = 1: every entry is its token
+    assert np.array_equal(oracle.compress(c, z, 1), c)
+    # equal weights: the mean of the m tokens
+    e = oracle.compress(c, np.zeros_like(z), 3)
+    assert np.allclose(e, c.reshape(4, 3, 512).mean(1), rtol=1e-6, atol=1e-7)
+    # one token's weight far above the others': that token
+    zz = np.zeros_like(z)
+    zz[1::2] = 200.0
+    assert np.array_equal(oracle.compress(c, zz, 2), c[1::2])
+    # a constant added to a channel's Z over an entry's tokens changes nothing
+    # (up to the float32 rounding of Z + shift, about 1e-5 here); a channel
+    # or token mix-up would move the result by order 1
+    shift = np.repeat(rng.standard_normal((6, 512)).astype(np.float32) * 50, 2, axis=0)
+    a, b = oracle.compress(c, z, 2), oracle.compress(c, (z + shift).astype(np.float32), 2)
+    assert np.allclose(a, b, rtol=0, atol=1e-4)
+
+
+def test_compress_two_tokens_closed_form():
+    """m = 2: the softmax of two weights is the logistic function of their
+    difference, so e = C1 + sigma(z0 - z1) (C0 - C1)."""
+    rng = np.random.default_rng(22)
+    c = rng.standard_normal((40, 512)).astype(np.float32)
+    z = rng.standard_normal((40, 512)).astype(np.float32)
+    c0, c1, z0, z1 = (a.astype(np.float64) for a in (c[0::2], c[1::2], z[0::2], z[1::2]))
+    want = c1 + (c0 - c1) / (1.0 + np.exp(z1 - z0))
+    assert np.allclose(oracle.compress(c, z, 2), want, rtol=1e-6, atol=1e-7)
