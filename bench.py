@@ -418,7 +418,35 @@ def bench_workloads(synth, C, torch, dev):
     res["decode_step_40_pages_fmt"] = bench_step_40(synth, torch, dev, kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4)
     for kv_fmt in (1, 0):
         res["kv_append_e4m3" if kv_fmt == 1 else "kv_append_mxfp4"] = bench_append(C, torch, dev, kv_fmt)
+    res["compress"] = bench_compress(C, torch, dev)
     return res
+
+
+def bench_compress(C, torch, dev, n=131072, m=2, reps=20):
+    """The compressor over the 262,144-token prefill context at ratio 2:
+    131,072 entries.  Algorithmic bytes per entry: m rows of C and of Z read
+    (f32), one f32 row written."""
+    g = torch.Generator(device=dev).manual_seed(8)
+    c = torch.randn((n * m, 512), generator=g, device=dev, dtype=torch.float32)
+    z = torch.randn((n * m, 512), generator=g, device=dev, dtype=torch.float32)
+    out = torch.empty((n, 512), dtype=torch.float32, device=dev)
+    C.csa2_compress(c, z, m, out=out)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        C.csa2_compress(c, z, m, out=out)
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1000.0 / reps
+    nb = n * (2 * m + 1) * 2048
+    gbs = nb / (us * 1e-6) / 1e9
+    log(f"[bench] compress (m {m}): {us:.1f} us for {n} entries, {gbs:.0f} GB/s")
+    r = {"us": round(us, 2), "entries": n, "m": m, "algorithmic_bytes": nb, "hbm_gbs": round(gbs, 1),
+         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del c, z, out
+    torch.cuda.empty_cache()
+    return r
 
 
 def bench_append(C, torch, dev, kv_fmt, n=131072, reps=20):

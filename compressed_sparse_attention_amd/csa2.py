@@ -25,7 +25,7 @@ CSA2_LAYER_BUILD_POOL = 1
 CSA2_WS_TOPK, CSA2_WS_BLOCK_POOL, CSA2_WS_SPARSE_ATTN, CSA2_WS_LAYER_CHAIN = 1, 2, 3, 4
 
 EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_block_pool", "csa2_gather_dequant", "csa2_sparse_attn",
-           "csa2_layer_chain", "csa2_kv_append", "csa2_workspace_size", "csa2_status_string", "csa2_last_hip_error",
+           "csa2_layer_chain", "csa2_compress", "csa2_kv_append", "csa2_workspace_size", "csa2_status_string", "csa2_last_hip_error",
            "csa2_version")
 
 _vp = ctypes.c_void_p
@@ -79,6 +79,7 @@ def lib():
         L.csa2_topk.argtypes = [B, _vp, i64, _vp, i32, _vp, i32, _vp, _vp, _vp, sz, _vp]
         L.csa2_block_pool.argtypes = [B, _vp, i64, i32, i32, _vp, _vp, _vp, _vp, sz, _vp]
         L.csa2_gather_dequant.argtypes = [B, i32, _vp, _vp, _vp, i32, _vp, _vp]
+        L.csa2_compress.argtypes = [ctypes.c_int64, i32, _vp, _vp, _vp, _vp]
         L.csa2_kv_append.argtypes = [ctypes.c_int64, _vp, _vp, _vp, ctypes.c_int64, i32, _vp, _vp, _vp]
         L.csa2_sparse_attn.argtypes = [B, i32, _vp, i32, _vp, _vp, _vp, i32, _vp, S, f32, _vp, _vp, _vp, sz, _vp]
         L.csa2_layer_chain.argtypes = [B, ctypes.POINTER(csa2_chain_params), i32, ctypes.POINTER(csa2_layer), S, _vp,
@@ -226,6 +227,17 @@ def csa2_block_pool(batch, scores, block=8, max_blocks=2048, ws=None, stream=Non
                                _ptr(pool), _ptr(cnt), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "csa2_block_pool")
     return blocks, pool, cnt
+
+
+def csa2_compress(c_tok, z_tok, m, out=None, stream=None):
+    """Entries from m tokens each: the per-channel softmax over an entry's
+    tokens of z_tok weights c_tok ([n m][512] f32 each, on the device)."""
+    n = int(c_tok.shape[0]) // int(m)
+    if out is None:
+        out = torch.empty((n, 512), dtype=torch.float32, device=c_tok.device)
+    st = lib().csa2_compress(n, int(m), _ptr(c_tok), _ptr(z_tok), _ptr(out), _stream(stream))
+    _check(st, "csa2_compress")
+    return out
 
 
 def csa2_kv_append(x, rope_cs, dst_row, kv_fp4, kv_sc, kv_fmt=CSA2_KV_MXFP4, stream=None):

@@ -184,6 +184,18 @@ CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
 
+CSA2_API csa2_status csa2_compress(int64_t n_entries, int32_t m, const float* c_tok, const float* z_tok, float* out,
+                                   hipStream_t stream) {
+    if (n_entries < 0) return CSA2_ERR_INVALID_ARG;
+    if (m < 1 || m > 16) return CSA2_ERR_UNSUPPORTED;
+    if (n_entries == 0) return CSA2_OK;
+    if (!c_tok || !z_tok || !out) return CSA2_ERR_INVALID_ARG;
+    if (((uintptr_t)c_tok | (uintptr_t)z_tok | (uintptr_t)out) & 15) return CSA2_ERR_INVALID_ARG;
+    if ((n_entries + 1) / 2 > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+    const hipError_t e = launch_compress(n_entries, m, c_tok, z_tok, out, stream);
+    return e == hipSuccess ? CSA2_OK : hip_fail(e);
+}
+
 CSA2_API csa2_status csa2_kv_append(int64_t n, const float* x, const float* rope_cs, const int64_t* dst_row,
                                     int64_t n_rows, int32_t kv_fmt, uint8_t* kv_fp4, uint8_t* kv_sc,
                                     hipStream_t stream) {

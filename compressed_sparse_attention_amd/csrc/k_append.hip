@@ -115,7 +115,45 @@ __global__ __launch_bounds__(256) void k_kv_append(const float* __restrict__ x, 
     }
 }
 
+// Compressor (reading note "DeepSeek V4.1 Flash: Pushing the Limits of KV
+// Cache Compression": C = H W^KV are the KV rows and Z = H W^Z their
+// compression weights; CSA2 drops V4's overlapping windows and absolute
+// position embedding).  Reading: entry j combines tokens jm .. jm + m - 1 per
+// channel with the softmax over those tokens of Z.  A thread owns 4 channels
+// of one entry (128 threads an entry, 2 entries a workgroup).
+__global__ __launch_bounds__(256) void k_compress(const float* __restrict__ c_tok, const float* __restrict__ z_tok,
+                                                  int64_t n, int m, float* __restrict__ out) {
+    const int64_t j = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+    if (j >= n) return;
+    const int c0 = 4 * (threadIdx.x & 127);
+    const int64_t t0 = j * m;
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int i = 0; i < m; ++i) {
+        const float4 z = *reinterpret_cast<const float4*>(z_tok + (t0 + i) * 512 + c0);
+        mx[0] = fmaxf(mx[0], z.x); mx[1] = fmaxf(mx[1], z.y); mx[2] = fmaxf(mx[2], z.z); mx[3] = fmaxf(mx[3], z.w);
+    }
+    float num[4] = {0.f, 0.f, 0.f, 0.f}, den[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < m; ++i) {
+        const float4 z = *reinterpret_cast<const float4*>(z_tok + (t0 + i) * 512 + c0);
+        const float4 c = *reinterpret_cast<const float4*>(c_tok + (t0 + i) * 512 + c0);
+        const float zz[4] = {z.x, z.y, z.z, z.w}, cc[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float w = expf(zz[k] - mx[k]);  // <= 1: the token with the largest weight gives 1
+            num[k] += w * cc[k];
+            den[k] += w;
+        }
+    }
+    *reinterpret_cast<float4*>(out + j * 512 + c0) =
+        float4{num[0] / den[0], num[1] / den[1], num[2] / den[2], num[3] / den[3]};
+}
+
 }  // namespace
+
+hipError_t launch_compress(int64_t n, int m, const float* c_tok, const float* z_tok, float* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_compress, dim3((unsigned)((n + 1) / 2)), dim3(256), 0, s, c_tok, z_tok, n, m, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_append(int64_t n, const float* x, const float* cs, const int64_t* dst, int64_t rows, int kv_fmt,
                             uint8_t* kv, uint8_t* kv_sc, hipStream_t s) {

@@ -174,6 +174,23 @@ CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_
                                       const uint8_t* k_sc, const int32_t* cand, int32_t cand_stride,
                                       float* scores, int64_t score_stride, uint32_t* hist, hipStream_t stream);
 
+/* ---- compressor -----------------------------------------------------------
+ * The CSA2 compressor: m consecutive tokens become one global entry.  The
+ * reading note "DeepSeek V4.1 Flash: Pushing the Limits of KV Cache
+ * Compression" gives the KV rows C = H W^KV and their compression weights
+ * Z = H W^Z; CSA2 drops V4's overlapping windows and absolute position
+ * embedding, so entry j takes tokens jm .. jm + m - 1.  Reading: per channel,
+ *   out[j][c] = sum_i exp(Z[jm+i][c]) C[jm+i][c] / sum_i exp(Z[jm+i][c])
+ * (the softmax over the entry's tokens), in fp32 with the largest Z of the
+ * channel subtracted first.
+ * c_tok, z_tok: [n_entries * m][512] f32 (device, 16-byte aligned).
+ * out: [n_entries][512] f32 (device, 16-byte aligned): the entries before
+ *   RoPE, as csa2_kv_append takes them.
+ * Errors: n_entries < 0, a NULL or misaligned pointer with n_entries > 0:
+ * CSA2_ERR_INVALID_ARG; m outside 1..16: CSA2_ERR_UNSUPPORTED. */
+CSA2_API csa2_status csa2_compress(int64_t n_entries, int32_t m, const float* c_tok, const float* z_tok, float* out,
+                                   hipStream_t stream);
+
 /* ---- cache append ---------------------------------------------------------
  * Writes new main-KV entries into their cache rows the way the report stores
  * them (section 2.4.4: the cache is quantised after RoPE, all 512 channels

@@ -208,3 +208,17 @@ def test_kv_append_validation():
     assert app(dst=None) == C.CSA2_ERR_INVALID_ARG
     assert app(rows=0) == C.CSA2_ERR_INVALID_ARG
     assert app(x=FAKE + 4) == C.CSA2_ERR_INVALID_ARG   # x must be 16-byte aligned
+
+
+def test_compress_validation():
+    L = C.lib()
+
+    def comp(n=4, m=2, c=FAKE, z=FAKE, out=FAKE):
+        return L.csa2_compress(n, m, c, z, out, None)
+
+    assert comp(n=-1) == C.CSA2_ERR_INVALID_ARG
+    assert comp(m=0) == C.CSA2_ERR_UNSUPPORTED
+    assert comp(m=17) == C.CSA2_ERR_UNSUPPORTED
+    assert comp(n=0, c=None) == C.CSA2_OK
+    assert comp(z=None) == C.CSA2_ERR_INVALID_ARG
+    assert comp(out=FAKE + 8) == C.CSA2_ERR_INVALID_ARG

@@ -457,3 +457,22 @@ def test_kv_append_bitwise(kv_fmt, n):
         keep = np.delete(np.arange(n), 1)
         assert np.array_equal(kv2.cpu().numpy()[dst[keep]], ref_kv[dst[keep]])
         assert not kv2.cpu().numpy()[dst[1]].any()
+
+
+@pytest.mark.parametrize("m,n", [(1, 7), (2, 1), (2, 4099), (4, 300), (2, 131072)])
+def test_compress_tolerance(m, n):
+    """The compressor against the oracle (float64), within a bound derived
+    from its float32 arithmetic: an exp of at most a few units in the last
+    place, m products and sums, one division; 2e-6 of the weighted magnitude.
+    131,072 entries at m = 2 is the 262,144-token prefill context."""
+    rng = np.random.default_rng(3000 + 7 * m + n)
+    c = rng.standard_normal((n * m, 512), dtype=np.float32) * np.float32(3.0)
+    z = rng.standard_normal((n * m, 512), dtype=np.float32) * np.float32(4.0)
+    if n > 2:
+        z[:m, :8] = 80.0  # equal, large weights in one entry's first channels
+    ref = oracle.compress(c, z, m)
+    got = C.csa2_compress(dev(c), dev(z), m).cpu().numpy()
+    zz = z.reshape(n, m, 512).astype(np.float64)
+    w = np.exp(zz - zz.max(1, keepdims=True))
+    mag = (w * np.abs(c.reshape(n, m, 512))).sum(1) / w.sum(1)
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= 2e-6 * mag + 1e-30)
