@@ -624,3 +624,44 @@ int orc_compress(int64_t n_entries, int m, const float* c_tok, const float* z_to
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Indexer-K projection (reading note "DeepSeek V4.1 Flash: Pushing the      */
+/* Limits of KV Cache Compression", configuration section: indexer K is      */
+/* projected directly from the main KV; [R] 2.4.4: indexer keys in MXFP4).   */
+/* Readings: y[o] = sum_k x[k] W[k][o] over the 512 channels of the entry as */
+/* stored before quantisation, evaluated as the fp32 chain acc = +0;         */
+/* acc = fmaf(x[k], W[k][o], acc) for k ascending (a convention, like the    */
+/* head sum); then E2M1 codes with the OCP MX scale 2^(floor(log2 amax) - 2) */
+/* (at least 2^-127; 1 for an all-zero block) per row (k_fmt 0: the default  */
+/* layout, one E8M0 per row) or per 32 channels (k_fmt 1: MXFP4), to nearest */
+/* even, saturating at 6.                                                    */
+/* ------------------------------------------------------------------------ */
+int orc_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst, int k_fmt, int64_t rows,
+                        uint8_t* k_fp4, uint8_t* k_sc, float* y_out /* [n][128] or NULL */) {
+    if (k_fmt != 0 && k_fmt != 1) return 1;
+    for (int64_t e = 0; e < n; ++e) {
+        if (dst[e] < 0 || dst[e] >= rows) return 1;
+        float y[128];
+        for (int o = 0; o < 128; ++o) {
+            float acc = 0.0f;
+            for (int k = 0; k < 512; ++k) acc = fmaf(x[e * 512 + k], W[k * 128 + o], acc);
+            y[o] = acc;
+            if (y_out) y_out[e * 128 + o] = acc;
+        }
+        int bl = k_fmt == 1 ? 32 : 128;
+        for (int b0 = 0; b0 < 128; b0 += bl) {
+            float amax = 0.0f;
+            for (int c = b0; c < b0 + bl; ++c) amax = fmaxf(amax, fabsf(y[c]));
+            int se = amax > 0.0f ? floor_log2_f(amax) - 2 : 0;
+            if (se < -127) se = -127;
+            if (k_fmt == 1) k_sc[dst[e] * 4 + b0 / 32] = (uint8_t)(se + 127);
+            else k_sc[dst[e]] = (uint8_t)(se + 127);
+            for (int c = b0; c < b0 + bl; c += 2) {
+                uint8_t lo = e2m1_rne(ldexpf(y[c], -se)), hi = e2m1_rne(ldexpf(y[c + 1], -se));
+                k_fp4[dst[e] * 64 + c / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+    return 0;
+}

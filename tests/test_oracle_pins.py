@@ -871,3 +871,59 @@ def test_compress_two_tokens_closed_form():
     c0, c1, z0, z1 = (a.astype(np.float64) for a in (c[0::2], c[1::2], z[0::2], z[1::2]))
     want = c1 + (c0 - c1) / (1.0 + np.exp(z1 - z0))
     assert np.allclose(oracle.compress(c, z, 2), want, rtol=1e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------------------
+# indexer-K projection: y = x W (fp32 multiply-add chain), then MXFP4 codes
+# ---------------------------------------------------------------------------
+
+def _spec_mx_codes(y, bl):
+    """E2M1 codes and E8M0 scales of one row y (float32) with blocks of bl,
+    from the OCP MX scale rule and exact nearest-even rounding."""
+    e2m1 = [Fraction(z).limit_denominator(2) for z in E2M1_SPEC]
+    codes, scales = [], []
+    for b0 in range(0, len(y), bl):
+        amax = float(np.max(np.abs(y[b0:b0 + bl])))
+        se = max(math.frexp(amax)[1] - 3, -127) if amax > 0 else 0
+        scales.append(se + 127)
+        for z in y[b0:b0 + bl]:
+            q = Fraction(float(z)) / Fraction(2) ** se
+            codes.append(_nearest_even(abs(q), e2m1) | (8 if q < 0 else 0))
+    return np.array([codes[2 * i] | (codes[2 * i + 1] << 4) for i in range(len(y) // 2)], np.uint8), scales
+
+
+@pytest.mark.parametrize("k_fmt", [0, 1])
+def test_index_k_project_selection_matrix(k_fmt):
+    """W picks and scales single channels (one nonzero per column, a power of
+    two), so every multiply-add chain is exact: y[o] = 2^s x[p(o)].  The codes
+    and scales equal the spec encoder's on that y."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((5, 512)).astype(np.float32) * np.float32(3.0)
+    W = np.zeros((512, 128), np.float32)
+    perm = rng.permutation(512)[:128]
+    sh = rng.integers(-3, 4, size=128)
+    W[perm, np.arange(128)] = np.exp2(sh).astype(np.float32)
+    dst = np.array([4, 0, 2, 6, 1])
+    kf, ks = oracle.index_k_project(x, W, dst, k_fmt, 8)
+    for e in range(5):
+        y = (x[e, perm] * np.exp2(sh)).astype(np.float32)
+        codes, scales = _spec_mx_codes(y, 32 if k_fmt == 1 else 128)
+        assert np.array_equal(kf[dst[e]], codes), e
+        assert list(np.atleast_1d(ks[dst[e]])) == scales, e
+    assert not kf[[3, 5, 7]].any()
+
+
+def test_index_k_project_chain_order():
+    """The projection is the fp32 multiply-add chain in ascending channel
+    order: y equals that chain evaluated in exact rationals with one rounding
+    per step, bit for bit, on values whose products are not exact (a tree or
+    a reversed order would differ in the last bits of most outputs)."""
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((1, 512)).astype(np.float32)
+    W = (rng.standard_normal((512, 128)) * 0.05).astype(np.float32)
+    _, _, y = oracle.index_k_project(x, W, np.array([0]), 0, 1, want_y=True)
+    for o in (0, 77, 127):
+        acc = Fraction(0)
+        for k in range(512):
+            acc = Fraction(rne_f32(Fraction(float(x[0, k])) * Fraction(float(W[k, o])) + acc))
+        assert y[0, o] == float(acc), o
