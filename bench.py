@@ -419,7 +419,36 @@ def bench_workloads(synth, C, torch, dev):
     for kv_fmt in (1, 0):
         res["kv_append_e4m3" if kv_fmt == 1 else "kv_append_mxfp4"] = bench_append(C, torch, dev, kv_fmt)
     res["compress"] = bench_compress(C, torch, dev)
+    res["index_k_project"] = bench_project(C, torch, dev)
     return res
+
+
+def bench_project(C, torch, dev, n=131072, reps=10):
+    """The indexer-K projection of 131,072 entries (one source layer of the
+    prefill context): 2 x 512 x 128 flops an entry as float32 multiply-add
+    chains (against the vector fp32 peak), then MXFP4 codes."""
+    g = torch.Generator(device=dev).manual_seed(9)
+    x = torch.randn((n, 512), generator=g, device=dev, dtype=torch.float32)
+    W = torch.randn((512, 128), generator=g, device=dev, dtype=torch.float32) * 0.05
+    dst = torch.arange(n, device=dev, dtype=torch.int64)
+    kf = torch.empty((n, 64), dtype=torch.uint8, device=dev)
+    ks = torch.empty((n, 4), dtype=torch.uint8, device=dev)
+    C.csa2_index_k_project(x, W, dst, kf, ks, q_fmt=C.CSA2_Q_MXFP4)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        C.csa2_index_k_project(x, W, dst, kf, ks, q_fmt=C.CSA2_Q_MXFP4)
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1000.0 / reps
+    flops = 2.0 * n * 512 * 128
+    tf = flops / (us * 1e-6) / 1e12
+    log(f"[bench] index_k_project: {us:.1f} us for {n} entries, {tf:.1f} TFLOP/s fp32")
+    r = {"us": round(us, 2), "entries": n, "flops": flops, "tflops": round(tf, 2), "frac_fp32_vector_peak": round(tf / 157.3, 4)}
+    del x, W, dst, kf, ks
+    torch.cuda.empty_cache()
+    return r
 
 
 def bench_compress(C, torch, dev, n=131072, m=2, reps=20):

@@ -148,7 +148,91 @@ __global__ __launch_bounds__(256) void k_compress(const float* __restrict__ c_to
         float4{num[0] / den[0], num[1] / den[1], num[2] / den[2], num[3] / den[3]};
 }
 
+// Indexer-K projection (reading note "DeepSeek V4.1 Flash: Pushing the Limits
+// of KV Cache Compression", configuration section: indexer K is projected
+// directly from the main KV; the report, section 2.4.4: indexer keys in
+// MXFP4).  y = x W over the entry's 512 channels, each output the fp32
+// multiply-add chain in ascending channel order (the order the results are
+// defined in), then E2M1 codes with the OCP MX scale 2^(floor(log2 amax) - 2)
+// per row (KF 0) or per 32 channels (KF 1).  16 entries a workgroup, 16
+// threads an entry, 8 outputs a thread; the entries' rows and 64-channel
+// tiles of W are staged in LDS.
+template <int KF>
+__global__ __launch_bounds__(256) void k_index_k_project(const float* __restrict__ x, const float* __restrict__ W,
+                                                         const int64_t* __restrict__ dst, int64_t n, int64_t rows,
+                                                         uint8_t* __restrict__ k_fp4, uint8_t* __restrict__ k_sc) {
+    __shared__ __attribute__((aligned(16))) float xs[16][512];
+    __shared__ __attribute__((aligned(16))) float ws[64][128];
+    const int t = threadIdx.x;
+    const int64_t e0 = (int64_t)blockIdx.x * 16;
+    for (int i = t; i < 16 * 128; i += 256) {  // 16 rows of 128 float4
+        const int el = i >> 7, c4 = i & 127;
+        const float4 v = e0 + el < n ? reinterpret_cast<const float4*>(x + (e0 + el) * 512)[c4]
+                                     : float4{0.f, 0.f, 0.f, 0.f};
+        reinterpret_cast<float4*>(&xs[el][0])[c4] = v;
+    }
+    const int el = t >> 4, og = t & 15;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 8; ++kt) {
+        __syncthreads();  // the previous tile is consumed (and, first, the rows are staged)
+        for (int i = t; i < 64 * 32; i += 256) {  // 64 rows of 32 float4
+            const int kr = i >> 5, c4 = i & 31;
+            reinterpret_cast<float4*>(&ws[kr][0])[c4] = reinterpret_cast<const float4*>(W + (int64_t)(64 * kt + kr) * 128)[c4];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = 0; k < 64; ++k) {
+            const float xk = xs[el][64 * kt + k];
+            const float4 w0 = reinterpret_cast<const float4*>(&ws[k][8 * og])[0];
+            const float4 w1 = reinterpret_cast<const float4*>(&ws[k][8 * og])[1];
+            acc[0] = __builtin_fmaf(xk, w0.x, acc[0]); acc[1] = __builtin_fmaf(xk, w0.y, acc[1]);
+            acc[2] = __builtin_fmaf(xk, w0.z, acc[2]); acc[3] = __builtin_fmaf(xk, w0.w, acc[3]);
+            acc[4] = __builtin_fmaf(xk, w1.x, acc[4]); acc[5] = __builtin_fmaf(xk, w1.y, acc[5]);
+            acc[6] = __builtin_fmaf(xk, w1.z, acc[6]); acc[7] = __builtin_fmaf(xk, w1.w, acc[7]);
+        }
+    }
+    // block maxima over the entry's 16 threads (KF 0) or over 4 (KF 1)
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(acc[i]));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
+    if constexpr (KF == 0) {
+        am = fmaxf(am, __shfl_xor(am, 4));
+        am = fmaxf(am, __shfl_xor(am, 8));
+    }
+    int se = 0;
+    if (am > 0.0f) {
+        int ex;
+        frexpf(am, &ex);
+        se = ex - 3 < -127 ? -127 : ex - 3;
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= e2m1_code_rne(ldexpf(acc[i], -se)) << (4 * i);
+    const int64_t e = e0 + el;
+    if (e >= n) return;
+    const int64_t r = dst[e];
+    if (r < 0 || r >= rows) return;
+    *reinterpret_cast<uint32_t*>(k_fp4 + r * 64 + 4 * og) = word;
+    if constexpr (KF == 1) {
+        if ((og & 3) == 0) k_sc[r * 4 + (og >> 2)] = (uint8_t)(se + 127);
+    } else {
+        if (og == 0) k_sc[r] = (uint8_t)(se + 127);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst, int64_t rows,
+                                  int mx, uint8_t* k_fp4, uint8_t* k_sc, hipStream_t s) {
+    const dim3 grid((unsigned)((n + 15) / 16));
+    if (mx)
+        hipLaunchKernelGGL(k_index_k_project<1>, grid, dim3(256), 0, s, x, W, dst, n, rows, k_fp4, k_sc);
+    else
+        hipLaunchKernelGGL(k_index_k_project<0>, grid, dim3(256), 0, s, x, W, dst, n, rows, k_fp4, k_sc);
+    return hipGetLastError();
+}
 
 hipError_t launch_compress(int64_t n, int m, const float* c_tok, const float* z_tok, float* out, hipStream_t s) {
     hipLaunchKernelGGL(k_compress, dim3((unsigned)((n + 1) / 2)), dim3(256), 0, s, c_tok, z_tok, n, m, out);

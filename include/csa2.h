@@ -174,6 +174,28 @@ CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_
                                       const uint8_t* k_sc, const int32_t* cand, int32_t cand_stride,
                                       float* scores, int64_t score_stride, uint32_t* hist, hipStream_t stream);
 
+/* ---- indexer-K projection --------------------------------------------------
+ * Indexer K of new entries, projected from their main KV (reading note
+ * "DeepSeek V4.1 Flash: Pushing the Limits of KV Cache Compression",
+ * configuration section: indexer K comes directly from the main KV by a
+ * projection; the report, section 2.4.4: FP4 indexer keys in OCP MXFP4):
+ *   y[o] = sum_k x[i][k] W[k][o], o < 128, evaluated as the fp32 chain
+ *          acc = +0; acc = fmaf(x[i][k], W[k][o], acc) for k = 0..511;
+ *   row dst_row[i] of k_fp4 = E2M1(y / X) to nearest even, saturating at 6,
+ *   X = 2^(floor(log2 amax) - 2) (at least 2^-127; 1 when amax = 0) over the
+ *   row (q_fmt CSA2_Q_FP4 or CSA2_Q_FP8: k_sc [rows] u8) or over each 32
+ *   channels (CSA2_Q_MXFP4: k_sc [rows][4] u8).
+ * x: [n][512] f32 (device, 16-byte aligned), the entries' main KV before
+ *   quantisation (after RoPE, as csa2_kv_append rotates it).
+ * W: [512][128] f32 (device, 16-byte aligned).
+ * dst_row: [n] i64 (device); rows outside [0, n_rows) are skipped.
+ * k_fp4: [n_rows][64] u8 (device, 16-byte aligned).
+ * Errors: n < 0, an unknown q_fmt, a NULL or misaligned pointer or
+ * n_rows < 1 with n > 0: CSA2_ERR_INVALID_ARG.  n == 0 does nothing. */
+CSA2_API csa2_status csa2_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst_row,
+                                          int64_t n_rows, int32_t q_fmt, uint8_t* k_fp4, uint8_t* k_sc,
+                                          hipStream_t stream);
+
 /* ---- compressor -----------------------------------------------------------
  * The CSA2 compressor: m consecutive tokens become one global entry.  The
  * reading note "DeepSeek V4.1 Flash: Pushing the Limits of KV Cache

@@ -222,3 +222,17 @@ def test_compress_validation():
     assert comp(n=0, c=None) == C.CSA2_OK
     assert comp(z=None) == C.CSA2_ERR_INVALID_ARG
     assert comp(out=FAKE + 8) == C.CSA2_ERR_INVALID_ARG
+
+
+def test_index_k_project_validation():
+    L = C.lib()
+
+    def proj(n=4, x=FAKE, W=FAKE, dst=FAKE, rows=8, fmt=C.CSA2_Q_MXFP4, kf=FAKE, ks=FAKE):
+        return L.csa2_index_k_project(n, x, W, dst, rows, fmt, kf, ks, None)
+
+    assert proj(n=-1) == C.CSA2_ERR_INVALID_ARG
+    assert proj(fmt=5) == C.CSA2_ERR_INVALID_ARG
+    assert proj(n=0, x=None) == C.CSA2_OK
+    assert proj(W=None) == C.CSA2_ERR_INVALID_ARG
+    assert proj(rows=0) == C.CSA2_ERR_INVALID_ARG
+    assert proj(W=FAKE + 4) == C.CSA2_ERR_INVALID_ARG

@@ -476,3 +476,31 @@ def test_compress_tolerance(m, n):
     w = np.exp(zz - zz.max(1, keepdims=True))
     mag = (w * np.abs(c.reshape(n, m, 512))).sum(1) / w.sum(1)
     assert np.all(np.abs(got.astype(np.float64) - ref) <= 2e-6 * mag + 1e-30)
+
+
+@pytest.mark.parametrize("q_fmt", [synth.Q_FP4, synth.Q_MXFP4])
+@pytest.mark.parametrize("n", [1, 17, 5000, 131072])
+def test_index_k_project_bitwise(q_fmt, n):
+    """The indexer-K projection equals the oracle bit for bit (same float32
+    multiply-add chain, same quantiser), rows written out of order.  At
+    131,072 entries (one source layer of the prefill context) the GPU writes
+    every row and the oracle checks 3,000 sampled ones."""
+    rng = np.random.default_rng(4000 + n + q_fmt)
+    x = rng.standard_normal((n, 512), dtype=np.float32) * np.float32(3.0)
+    if n >= 17:
+        x[5] = 0.0  # an all-zero row: scale 2^0, codes 0
+    W = rng.standard_normal((512, 128), dtype=np.float32) * np.float32(0.05)
+    rows = n + 3
+    dst = rng.permutation(rows)[:n].astype(np.int64)
+    kf = torch.full((rows, 64), 0xAB, dtype=torch.uint8, device="cuda")
+    ks = torch.full((rows, 4) if q_fmt == synth.Q_MXFP4 else (rows,), 0xCD, dtype=torch.uint8, device="cuda")
+    C.csa2_index_k_project(dev(x), dev(W), dev(dst), kf, ks, q_fmt=q_fmt)
+    torch.cuda.synchronize()
+    k_fmt = 1 if q_fmt == synth.Q_MXFP4 else 0
+    sel = np.arange(n) if n <= 5000 else np.sort(rng.choice(n, 3000, replace=False))
+    ref_f, ref_s = oracle.index_k_project(x[sel], W, dst[sel], k_fmt, rows)
+    got_f, got_s = kf.cpu().numpy(), ks.cpu().numpy()
+    assert np.array_equal(got_f[dst[sel]], ref_f[dst[sel]])
+    assert np.array_equal(got_s[dst[sel]], ref_s[dst[sel]])
+    untouched = np.setdiff1d(np.arange(rows), dst)
+    assert np.all(got_f[untouched] == 0xAB)
