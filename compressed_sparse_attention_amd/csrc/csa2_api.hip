@@ -192,7 +192,7 @@ CSA2_API csa2_status csa2_index_k_project(int64_t n, const float* x, const float
     if (n == 0) return CSA2_OK;
     if (!x || !W || !dst_row || !k_fp4 || !k_sc || n_rows < 1) return CSA2_ERR_INVALID_ARG;
     if (((uintptr_t)x | (uintptr_t)W | (uintptr_t)k_fp4) & 15) return CSA2_ERR_INVALID_ARG;
-    if ((n + 15) / 16 > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+    if ((n + 63) / 64 > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
     const hipError_t e =
         launch_index_k_project(n, x, W, dst_row, n_rows, q_fmt == CSA2_Q_MXFP4, k_fp4, k_sc, stream);
     return e == hipSuccess ? CSA2_OK : hip_fail(e);

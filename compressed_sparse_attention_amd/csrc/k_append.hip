@@ -154,71 +154,86 @@ __global__ __launch_bounds__(256) void k_compress(const float* __restrict__ c_to
 // MXFP4).  y = x W over the entry's 512 channels, each output the fp32
 // multiply-add chain in ascending channel order (the order the results are
 // defined in), then E2M1 codes with the OCP MX scale 2^(floor(log2 amax) - 2)
-// per row (KF 0) or per 32 channels (KF 1).  16 entries a workgroup, 16
-// threads an entry, 8 outputs a thread; the entries' rows and 64-channel
-// tiles of W are staged in LDS.
+// per row (KF 0) or per 32 channels (KF 1).  64 entries a workgroup; thread t
+// owns outputs 8 (t % 16) .. + 7 of entries 4 (t / 16) .. + 3, so the 16
+// threads of an entry quad are one 16-lane group.  Per 64-channel step the
+// entries' channels (transposed: one 16-byte read gives a channel of 4
+// entries) and that slice of W are staged in LDS: three 16-byte reads feed 32
+// multiply-adds.
 template <int KF>
 __global__ __launch_bounds__(256) void k_index_k_project(const float* __restrict__ x, const float* __restrict__ W,
                                                          const int64_t* __restrict__ dst, int64_t n, int64_t rows,
                                                          uint8_t* __restrict__ k_fp4, uint8_t* __restrict__ k_sc) {
-    __shared__ __attribute__((aligned(16))) float xs[16][512];
+    __shared__ __attribute__((aligned(16))) float xs[64][64 + 4];  // [channel][entry], padded rows
     __shared__ __attribute__((aligned(16))) float ws[64][128];
     const int t = threadIdx.x;
-    const int64_t e0 = (int64_t)blockIdx.x * 16;
-    for (int i = t; i < 16 * 128; i += 256) {  // 16 rows of 128 float4
-        const int el = i >> 7, c4 = i & 127;
-        const float4 v = e0 + el < n ? reinterpret_cast<const float4*>(x + (e0 + el) * 512)[c4]
-                                     : float4{0.f, 0.f, 0.f, 0.f};
-        reinterpret_cast<float4*>(&xs[el][0])[c4] = v;
-    }
-    const int el = t >> 4, og = t & 15;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int64_t e0 = (int64_t)blockIdx.x * 64;
+    const int eq = t >> 4, og = t & 15;
+    float acc[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
     for (int kt = 0; kt < 8; ++kt) {
-        __syncthreads();  // the previous tile is consumed (and, first, the rows are staged)
-        for (int i = t; i < 64 * 32; i += 256) {  // 64 rows of 32 float4
+        __syncthreads();  // the previous step's tiles are consumed
+        for (int i = t; i < 64 * 16; i += 256) {  // 64 entries x 16 float4 of this step's channels
+            const int el = i >> 4, c4 = i & 15;
+            const float4 v = e0 + el < n ? reinterpret_cast<const float4*>(x + (e0 + el) * 512 + 64 * kt)[c4]
+                                         : float4{0.f, 0.f, 0.f, 0.f};
+            xs[4 * c4 + 0][el] = v.x;
+            xs[4 * c4 + 1][el] = v.y;
+            xs[4 * c4 + 2][el] = v.z;
+            xs[4 * c4 + 3][el] = v.w;
+        }
+        for (int i = t; i < 64 * 32; i += 256) {  // 64 rows of W, 32 float4 each
             const int kr = i >> 5, c4 = i & 31;
             reinterpret_cast<float4*>(&ws[kr][0])[c4] = reinterpret_cast<const float4*>(W + (int64_t)(64 * kt + kr) * 128)[c4];
         }
         __syncthreads();
-#pragma unroll 4
+#pragma unroll 2
         for (int k = 0; k < 64; ++k) {
-            const float xk = xs[el][64 * kt + k];
+            const float4 xv = *reinterpret_cast<const float4*>(&xs[k][4 * eq]);
             const float4 w0 = reinterpret_cast<const float4*>(&ws[k][8 * og])[0];
             const float4 w1 = reinterpret_cast<const float4*>(&ws[k][8 * og])[1];
-            acc[0] = __builtin_fmaf(xk, w0.x, acc[0]); acc[1] = __builtin_fmaf(xk, w0.y, acc[1]);
-            acc[2] = __builtin_fmaf(xk, w0.z, acc[2]); acc[3] = __builtin_fmaf(xk, w0.w, acc[3]);
-            acc[4] = __builtin_fmaf(xk, w1.x, acc[4]); acc[5] = __builtin_fmaf(xk, w1.y, acc[5]);
-            acc[6] = __builtin_fmaf(xk, w1.z, acc[6]); acc[7] = __builtin_fmaf(xk, w1.w, acc[7]);
+            const float xe[4] = {xv.x, xv.y, xv.z, xv.w};
+            const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[j][i] = __builtin_fmaf(xe[j], wv[i], acc[j][i]);
         }
     }
-    // block maxima over the entry's 16 threads (KF 0) or over 4 (KF 1)
-    float am = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(acc[i]));
-    am = fmaxf(am, __shfl_xor(am, 1));
-    am = fmaxf(am, __shfl_xor(am, 2));
-    if constexpr (KF == 0) {
-        am = fmaxf(am, __shfl_xor(am, 4));
-        am = fmaxf(am, __shfl_xor(am, 8));
-    }
-    int se = 0;
-    if (am > 0.0f) {
-        int ex;
-        frexpf(am, &ex);
-        se = ex - 3 < -127 ? -127 : ex - 3;
-    }
-    uint32_t word = 0;
+    for (int j = 0; j < 4; ++j) {
+        // block maxima over the entry's 16 threads (KF 0) or over 4 (KF 1)
+        float am = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= e2m1_code_rne(ldexpf(acc[i], -se)) << (4 * i);
-    const int64_t e = e0 + el;
-    if (e >= n) return;
-    const int64_t r = dst[e];
-    if (r < 0 || r >= rows) return;
-    *reinterpret_cast<uint32_t*>(k_fp4 + r * 64 + 4 * og) = word;
-    if constexpr (KF == 1) {
-        if ((og & 3) == 0) k_sc[r * 4 + (og >> 2)] = (uint8_t)(se + 127);
-    } else {
-        if (og == 0) k_sc[r] = (uint8_t)(se + 127);
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(acc[j][i]));
+        am = fmaxf(am, __shfl_xor(am, 1));
+        am = fmaxf(am, __shfl_xor(am, 2));
+        if constexpr (KF == 0) {
+            am = fmaxf(am, __shfl_xor(am, 4));
+            am = fmaxf(am, __shfl_xor(am, 8));
+        }
+        int se = 0;
+        if (am > 0.0f) {
+            int ex;
+            frexpf(am, &ex);
+            se = ex - 3 < -127 ? -127 : ex - 3;
+        }
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_code_rne(ldexpf(acc[j][i], -se)) << (4 * i);
+        const int64_t e = e0 + 4 * eq + j;
+        if (e >= n) continue;
+        const int64_t r = dst[e];
+        if (r < 0 || r >= rows) continue;
+        *reinterpret_cast<uint32_t*>(k_fp4 + r * 64 + 4 * og) = word;
+        if constexpr (KF == 1) {
+            if ((og & 3) == 0) k_sc[r * 4 + (og >> 2)] = (uint8_t)(se + 127);
+        } else {
+            if (og == 0) k_sc[r] = (uint8_t)(se + 127);
+        }
     }
 }
 
@@ -226,7 +241,7 @@ __global__ __launch_bounds__(256) void k_index_k_project(const float* __restrict
 
 hipError_t launch_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst, int64_t rows,
                                   int mx, uint8_t* k_fp4, uint8_t* k_sc, hipStream_t s) {
-    const dim3 grid((unsigned)((n + 15) / 16));
+    const dim3 grid((unsigned)((n + 63) / 64));
     if (mx)
         hipLaunchKernelGGL(k_index_k_project<1>, grid, dim3(256), 0, s, x, W, dst, n, rows, k_fp4, k_sc);
     else
