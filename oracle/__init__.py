@@ -62,6 +62,8 @@ def lib():
         L.orc_kv_append.restype = i32
         L.orc_compress.argtypes = [i64, i32, vp, vp, vp]
         L.orc_compress.restype = i32
+        L.orc_rope_cast.argtypes = [i64, i32, vp, vp, i32, vp]
+        L.orc_rope_cast.restype = i32
         L.orc_index_k_project.argtypes = [i64, vp, vp, vp, i32, i64, vp, vp, vp]
         L.orc_index_k_project.restype = i32
         L.orc_topk.argtypes = [i64, vp, i64, vp, vp, i64, i32, vp, i32]
@@ -124,6 +126,17 @@ def index_k_project(x, W, dst, k_fmt, rows, want_y=False):
     if lib().orc_index_k_project(len(dst), _p(x), _p(W), _p(dst), k_fmt, rows, _p(k_fp4), _p(k_sc), _p(y)):
         raise ValueError("index_k_project: bad format or destination row")
     return (k_fp4, k_sc, y) if want_y else (k_fp4, k_sc)
+
+
+def rope_cast(x, cs, inverse):
+    """Rotate channels 448..511 of every head row of x [n][heads][512] f32 by
+    the row's angles cs [n][32][2] (negated with `inverse`), then cast all to
+    bf16 (nearest even); returns the bf16 bits [n][heads][512] u16."""
+    x, cs = _c(x, np.float32), _c(cs, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    if lib().orc_rope_cast(x.shape[0], x.shape[1], _p(x), _p(cs), int(inverse), _p(out)):
+        raise ValueError("rope_cast: bad arguments")
+    return out
 
 
 def compress(c_tok, z_tok, m):

@@ -665,3 +665,37 @@ int orc_index_k_project(int64_t n, const float* x, const float* W, const int64_t
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* RoPE and cast around attention (the report's kernel flow names a fused    */
+/* "RoPE-attention-RoPE-cast" kernel: the query is rotated before attention, */
+/* the output's rotated part is turned back after it, and the result is     */
+/* cast).  Reading: the rotated channels and pairs of the append (448..511,  */
+/* pairs (448 + 2i, 449 + 2i), caller-given cos/sin per row and pair; with   */
+/* `inverse` the angle is negated: sin -> -sin), fp32 products without       */
+/* fusion, then every channel to bf16 to nearest even.                      */
+/* ------------------------------------------------------------------------ */
+static uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+int orc_rope_cast(int64_t n_rows, int heads, const float* in, const float* cs, int inverse, uint16_t* out) {
+    if (n_rows < 0 || heads < 1) return 1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int h = 0; h < heads; ++h) {
+            const float* v = in + (r * heads + h) * 512;
+            uint16_t* o = out + (r * heads + h) * 512;
+            for (int c = 0; c < 448; ++c) o[c] = f32_to_bf16_rne(v[c]);
+            for (int i = 0; i < 32; ++i) {
+                float a = v[448 + 2 * i], b = v[449 + 2 * i];
+                float co = cs[(r * 32 + i) * 2], si = cs[(r * 32 + i) * 2 + 1];
+                if (inverse) si = -si;
+                float ac = a * co, bs = b * si, as = a * si, bc = b * co;
+                o[448 + 2 * i] = f32_to_bf16_rne(ac - bs);
+                o[449 + 2 * i] = f32_to_bf16_rne(as + bc);
+            }
+        }
+    return 0;
+}

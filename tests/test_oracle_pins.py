@@ -927,3 +927,64 @@ def test_index_k_project_chain_order():
         for k in range(512):
             acc = Fraction(rne_f32(Fraction(float(x[0, k])) * Fraction(float(W[k, o])) + acc))
         assert y[0, o] == float(acc), o
+
+
+# ---------------------------------------------------------------------------
+# RoPE and cast around attention
+# ---------------------------------------------------------------------------
+
+def _bf16_rne_spec(v):
+    """Nearest bf16 (ties to an even last mantissa bit) of a finite float32,
+    by exact comparison with the two neighbouring bf16 values."""
+    f = Fraction(float(v))
+    u = int(np.float32(v).view(np.uint32))
+    lo = u & 0xFFFF0000
+    hi = lo + 0x10000
+    flo = Fraction(float(np.uint32(lo).view(np.float32)))
+    fhi = Fraction(float(np.uint32(hi).view(np.float32)))
+    dl, dh = abs(f - flo), abs(fhi - f)
+    pick = lo if dl < dh or (dl == dh and ((lo >> 16) & 1) == 0) else hi
+    return pick >> 16
+
+
+def test_rope_cast_zero_angle_is_the_bf16_cast_and_ties_go_even():
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((2, 3, 512)).astype(np.float32)
+    x[0, 0, :4] = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -9], np.float32)  # two ties, one not
+    cs = np.zeros((2, 32, 2), np.float32)
+    cs[..., 0] = 1.0
+    got = oracle.rope_cast(x, cs, False)
+    want = np.vectorize(_bf16_rne_spec, otypes=[np.uint16])(x)
+    assert np.array_equal(got, want)
+    assert list(got[0, 0, :2]) == [0x3F80, 0x3F82]  # 1 + 2^-8 -> 1 (even); 1 + 3 2^-8 -> 1 + 2^-6 (even)
+
+
+def test_rope_cast_quarter_turns_and_inverse():
+    """A quarter turn maps (a, b) to (-b, a) exactly, its inverse (-sin) maps
+    (a, b) to (b, -a); for any angle the inverse undoes the rotation to within
+    the casts' rounding."""
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((3, 2, 512)).astype(np.float32)
+    q = np.zeros((3, 32, 2), np.float32)
+    q[..., 1] = 1.0
+    fwd = oracle.rope_cast(x, q, False)
+    inv = oracle.rope_cast(x, q, True)
+    ident = np.zeros_like(q)
+    ident[..., 0] = 1.0
+    xt = x.copy()
+    xt[..., 448::2], xt[..., 449::2] = -x[..., 449::2], x[..., 448::2]
+    assert np.array_equal(fwd, oracle.rope_cast(xt, ident, False))
+    xi = x.copy()
+    xi[..., 448::2], xi[..., 449::2] = x[..., 449::2], -x[..., 448::2]
+    assert np.array_equal(inv, oracle.rope_cast(xi, ident, False))
+    th = rng.uniform(-np.pi, np.pi, size=(3, 32))
+    cs = np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
+    rot = (oracle.rope_cast(x, cs, False).astype(np.uint32) << 16).view(np.float32)
+    back = (oracle.rope_cast(rot, cs, True).astype(np.uint32) << 16).view(np.float32)
+    # two bf16 casts (2^-9 relative each) around a rotation: the error of a
+    # rotated channel scales with its pair's magnitude, the rest with itself
+    mag = np.abs(x).astype(np.float64)
+    pair = np.maximum(np.abs(x[..., 448::2]), np.abs(x[..., 449::2]))
+    mag[..., 448::2] = pair
+    mag[..., 449::2] = pair
+    assert np.all(np.abs(back.astype(np.float64) - x) <= 2 ** -6 * mag + 1e-30)
