@@ -25,7 +25,7 @@ CSA2_LAYER_BUILD_POOL = 1
 CSA2_WS_TOPK, CSA2_WS_BLOCK_POOL, CSA2_WS_SPARSE_ATTN, CSA2_WS_LAYER_CHAIN = 1, 2, 3, 4
 
 EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_block_pool", "csa2_gather_dequant", "csa2_sparse_attn",
-           "csa2_layer_chain", "csa2_index_k_project", "csa2_compress", "csa2_kv_append", "csa2_workspace_size", "csa2_status_string", "csa2_last_hip_error",
+           "csa2_layer_chain", "csa2_rope_cast", "csa2_index_k_project", "csa2_compress", "csa2_kv_append", "csa2_workspace_size", "csa2_status_string", "csa2_last_hip_error",
            "csa2_version")
 
 _vp = ctypes.c_void_p
@@ -79,6 +79,7 @@ def lib():
         L.csa2_topk.argtypes = [B, _vp, i64, _vp, i32, _vp, i32, _vp, _vp, _vp, sz, _vp]
         L.csa2_block_pool.argtypes = [B, _vp, i64, i32, i32, _vp, _vp, _vp, _vp, sz, _vp]
         L.csa2_gather_dequant.argtypes = [B, i32, _vp, _vp, _vp, i32, _vp, _vp]
+        L.csa2_rope_cast.argtypes = [ctypes.c_int64, i32, _vp, _vp, i32, _vp, _vp]
         L.csa2_index_k_project.argtypes = [ctypes.c_int64, _vp, _vp, _vp, ctypes.c_int64, i32, _vp, _vp, _vp]
         L.csa2_compress.argtypes = [ctypes.c_int64, i32, _vp, _vp, _vp, _vp]
         L.csa2_kv_append.argtypes = [ctypes.c_int64, _vp, _vp, _vp, ctypes.c_int64, i32, _vp, _vp, _vp]
@@ -228,6 +229,17 @@ def csa2_block_pool(batch, scores, block=8, max_blocks=2048, ws=None, stream=Non
                                _ptr(pool), _ptr(cnt), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "csa2_block_pool")
     return blocks, pool, cnt
+
+
+def csa2_rope_cast(x, rope_cs, inverse=False, out=None, stream=None):
+    """Rotate channels 448..511 of every head row of x [n][heads][512] f32 by
+    the row's angles (negated with inverse) and cast to bf16 (u16 bits)."""
+    n, heads = int(x.shape[0]), int(x.shape[1])
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint16, device=x.device)
+    st = lib().csa2_rope_cast(n, heads, _ptr(x), _ptr(rope_cs), int(bool(inverse)), _ptr(out), _stream(stream))
+    _check(st, "csa2_rope_cast")
+    return out
 
 
 def csa2_index_k_project(x, W, dst_row, k_fp4, k_sc, q_fmt=CSA2_Q_FP4, stream=None):

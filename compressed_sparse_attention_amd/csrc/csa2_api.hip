@@ -184,6 +184,17 @@ CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
 
+CSA2_API csa2_status csa2_rope_cast(int64_t n_rows, int32_t heads, const float* in, const float* rope_cs,
+                                    int32_t inverse, uint16_t* out_bf16, hipStream_t stream) {
+    if (n_rows < 0 || heads < 1) return CSA2_ERR_INVALID_ARG;
+    if (n_rows == 0) return CSA2_OK;
+    if (!in || !rope_cs || !out_bf16) return CSA2_ERR_INVALID_ARG;
+    if (((uintptr_t)in | (uintptr_t)rope_cs | (uintptr_t)out_bf16) & 15) return CSA2_ERR_INVALID_ARG;
+    if (n_rows > INT64_MAX / heads || (n_rows * heads + 3) / 4 > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
+    const hipError_t e = launch_rope_cast(n_rows, heads, in, rope_cs, inverse ? 1 : 0, out_bf16, stream);
+    return e == hipSuccess ? CSA2_OK : hip_fail(e);
+}
+
 CSA2_API csa2_status csa2_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst_row,
                                           int64_t n_rows, int32_t q_fmt, uint8_t* k_fp4, uint8_t* k_sc,
                                           hipStream_t stream) {

@@ -337,6 +337,8 @@ struct AttnLaunch {
 int attn_splits(const Geometry& g, int Hm, int K, int W);
 size_t attn_ws_bytes(const Geometry& g, int Hm, int S);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
+hipError_t launch_rope_cast(int64_t n_rows, int heads, const float* in, const float* cs, int inverse, uint16_t* out,
+                            hipStream_t s);
 hipError_t launch_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst, int64_t rows,
                                   int mx, uint8_t* k_fp4, uint8_t* k_sc, hipStream_t s);
 hipError_t launch_compress(int64_t n, int m, const float* c_tok, const float* z_tok, float* out, hipStream_t s);

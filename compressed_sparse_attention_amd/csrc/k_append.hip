@@ -237,7 +237,59 @@ __global__ __launch_bounds__(256) void k_index_k_project(const float* __restrict
     }
 }
 
+// RoPE and cast around attention (the report's kernel flow: a fused
+// "RoPE-attention-RoPE-cast" kernel rotates the query before attention and
+// turns the output's rotated part back after it, then casts).  The pairs and
+// angles are the append's (channels 448..511, caller-given cos/sin per row);
+// `inverse` negates the angle.  64 threads a head row, 8 channels a thread.
+__global__ __launch_bounds__(256) void k_rope_cast(const float* __restrict__ in, const float* __restrict__ cs,
+                                                   int64_t n_rows, int heads, int inverse, uint16_t* __restrict__ out) {
+    const int64_t hr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // head row = row * heads + head
+    if (hr >= n_rows * heads) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t r = hr / heads;
+    float v[8];
+    {
+        const float4* src = reinterpret_cast<const float4*>(in + hr * 512 + 8 * lane);
+        const float4 a = src[0], b = src[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    if (lane >= 56) {
+        // each product rounded on its own, as in the append
+#pragma clang fp contract(off)
+        const float4* cp = reinterpret_cast<const float4*>(cs + (r * 32 + 4 * (lane - 56)) * 2);
+        const float4 c0 = cp[0], c1 = cp[1];
+        const float co[4] = {c0.x, c0.z, c1.x, c1.z};
+        const float sg = inverse ? -1.0f : 1.0f;  // exact negation
+        const float si[4] = {sg * c0.y, sg * c0.w, sg * c1.y, sg * c1.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float a = v[2 * k], b = v[2 * k + 1];
+            v[2 * k] = a * co[k] - b * si[k];
+            v[2 * k + 1] = a * si[k] + b * co[k];
+        }
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
+        lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;  // bf16, nearest even
+        hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+        w[k] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(out + hr * 512 + 8 * lane) = uint4{w[0], w[1], w[2], w[3]};
+}
+
 }  // namespace
+
+hipError_t launch_rope_cast(int64_t n_rows, int heads, const float* in, const float* cs, int inverse, uint16_t* out,
+                            hipStream_t s) {
+    const int64_t hrows = n_rows * heads;
+    hipLaunchKernelGGL(k_rope_cast, dim3((unsigned)((hrows + 3) / 4)), dim3(256), 0, s, in, cs, n_rows, heads, inverse,
+                       out);
+    return hipGetLastError();
+}
 
 hipError_t launch_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst, int64_t rows,
                                   int mx, uint8_t* k_fp4, uint8_t* k_sc, hipStream_t s) {

@@ -174,6 +174,19 @@ CSA2_API csa2_status csa2_index_score(const csa2_batch* batch, int32_t H, int32_
                                       const uint8_t* k_sc, const int32_t* cand, int32_t cand_stride,
                                       float* scores, int64_t score_stride, uint32_t* hist, hipStream_t stream);
 
+/* ---- RoPE and cast around attention ---------------------------------------
+ * The report's kernel flow fuses RoPE, attention, RoPE and a cast: the query
+ * is rotated before attention and the output's rotated part is turned back
+ * after it.  For every head row of in [n_rows][heads][512] f32: channels
+ * 448..511 in pairs (448 + 2p, 449 + 2p) rotated by the row's angle p
+ * (rope_cs [n_rows][32][2] = cos, sin; inverse != 0 negates the angle), each
+ * product and the sum or difference rounded to fp32, then every channel cast
+ * to bf16 to nearest even into out_bf16 [n_rows][heads][512].
+ * All pointers device, 16-byte aligned.  Errors: n_rows < 0, heads < 1, a
+ * NULL or misaligned pointer with n_rows > 0: CSA2_ERR_INVALID_ARG. */
+CSA2_API csa2_status csa2_rope_cast(int64_t n_rows, int32_t heads, const float* in, const float* rope_cs,
+                                    int32_t inverse, uint16_t* out_bf16, hipStream_t stream);
+
 /* ---- indexer-K projection --------------------------------------------------
  * Indexer K of new entries, projected from their main KV (reading note
  * "DeepSeek V4.1 Flash: Pushing the Limits of KV Cache Compression",

@@ -236,3 +236,16 @@ def test_index_k_project_validation():
     assert proj(W=None) == C.CSA2_ERR_INVALID_ARG
     assert proj(rows=0) == C.CSA2_ERR_INVALID_ARG
     assert proj(W=FAKE + 4) == C.CSA2_ERR_INVALID_ARG
+
+
+def test_rope_cast_validation():
+    L = C.lib()
+
+    def rc(n=4, h=64, x=FAKE, cs=FAKE, out=FAKE):
+        return L.csa2_rope_cast(n, h, x, cs, 0, out, None)
+
+    assert rc(n=-1) == C.CSA2_ERR_INVALID_ARG
+    assert rc(h=0) == C.CSA2_ERR_INVALID_ARG
+    assert rc(n=0, x=None) == C.CSA2_OK
+    assert rc(cs=None) == C.CSA2_ERR_INVALID_ARG
+    assert rc(out=FAKE + 2) == C.CSA2_ERR_INVALID_ARG
