@@ -13,6 +13,7 @@ schedule table, decoder search-range / read-range table).
 """
 from __future__ import annotations
 
+import copy
 import ctypes
 import math
 import os
@@ -254,6 +255,18 @@ def sparse_attn(wl, q_main, idx, swa, replay_s=None, rows=None, scale=None, with
 
 # --- layer chain --------------------------------------------------------------
 
+def _with_source(wl, L):
+    """The workload as the layers after Full layer L read it: main KV and
+    indexer K are L's own when it carries them ([R] 2.3.1: a Full layer
+    generates global KV; Reindex and Reuse layers read the preceding Full
+    layer's)."""
+    if L.kv is None:
+        return wl
+    v = copy.copy(wl)
+    v.k_idx, v.k_sc, v.kv, v.kv_sc = L.k_idx, L.k_sc, L.kv, L.kv_sc
+    return v
+
+
 def layer_chain(wl, rows=None, attn=True):
     """Run the layers in index order ([R] 2.3.1 modes; [N4] schedule table).
 
@@ -264,6 +277,8 @@ def layer_chain(wl, rows=None, attn=True):
             exists) against the shared indexer K with its own q, takes Top-K.
     REUSE   attends with the latest indices.
     SWA_ONLY attends to its window only.
+    Main KV and indexer K come from the latest Full layer (its own caches when
+    it carries them, else the workload's).
     Returns per-layer dicts with idx (and pool fields for the pool layer) and
     the attention output."""
     nr_all = wl.total_q
@@ -272,10 +287,13 @@ def layer_chain(wl, rows=None, attn=True):
     idx_cur = None
     pool = None
     results = []
+    src = wl  # the workload as seen through the latest Full layer's caches
     for L in wl.layers:
         res = {"layer": L.index, "mode": L.mode}
         if L.mode == MODE_FULL:
-            sc = index_score(wl, L.q_idx, L.q_sc, L.w, L.q_fmt, rows=sel_rows)
+            src = _with_source(wl, L)
+            pool = None
+            sc = index_score(src, L.q_idx, L.q_sc, L.w, L.q_fmt, rows=sel_rows)
             idx_cur = topk(sc, vis, wl.K)
             if L.build_pool:
                 blocks, pool_pos, cnt = block_pool(sc, vis, wl.block, wl.max_blocks)
@@ -285,10 +303,10 @@ def layer_chain(wl, rows=None, attn=True):
         elif L.mode == MODE_REINDEX:
             if pool is not None:
                 pool_pos, cnt = pool[1], pool[2]
-                sc = _reindex_scores(wl, L, sel_rows, pool_pos)
+                sc = _reindex_scores(src, L, sel_rows, pool_pos)
                 idx_cur = topk(sc, cnt.astype(np.int64), wl.K, cand=pool_pos)
             else:
-                sc = index_score(wl, L.q_idx, L.q_sc, L.w, L.q_fmt, rows=sel_rows)
+                sc = index_score(src, L.q_idx, L.q_sc, L.w, L.q_fmt, rows=sel_rows)
                 idx_cur = topk(sc, vis, wl.K)
             res["scores"] = sc
         elif L.mode == MODE_SWA_ONLY:
@@ -301,7 +319,7 @@ def layer_chain(wl, rows=None, attn=True):
             use_idx = idx_cur
         res["idx"] = use_idx
         if attn:
-            res["out"], res["lse"] = sparse_attn(wl, L.q_main, use_idx, L.swa, replay_s=getattr(wl, "replay_s", None),
+            res["out"], res["lse"] = sparse_attn(src, L.q_main, use_idx, L.swa, replay_s=getattr(wl, "replay_s", None),
                                                  rows=sel_rows, idx_of_rows=True)
         results.append(res)
     return results

@@ -191,23 +191,32 @@ static int64_t k_int(const score_ctx* c, int64_t e, int ch) {
 static float score_one_mx(const score_ctx* c, int64_t r, int64_t e, const int64_t* qi, const int64_t* kv) {
     float acc = 0.0f;
     for (int h = 0; h < c->H; ++h) {
-        int64_t part[4];
+        int64_t part[4], mag[4];
         int ex[4], emin = 1 << 30;
         for (int b = 0; b < 4; ++b) {
             part[b] = 0;
-            for (int ch = 32 * b; ch < 32 * b + 32; ++ch) part[b] += qi[h * 128 + ch] * kv[ch];
+            mag[b] = 0;
+            for (int ch = 32 * b; ch < 32 * b + 32; ++ch) {
+                const int64_t p = qi[h * 128 + ch] * kv[ch];
+                part[b] += p;
+                mag[b] += p < 0 ? -p : p;
+            }
             ex[b] = (int)c->q_sc[(r * c->H + h) * 4 + b] + (int)c->k_sc[e * 4 + b] - 254;
             if (ex[b] < emin) emin = ex[b];
         }
-        int64_t dot = 0; /* d_h = dot * 2^(emin - 2) */
+        int64_t dot = 0, total = 0; /* d_h = dot * 2^(emin - 2) */
         for (int b = 0; b < 4; ++b) {
             int sh = ex[b] - emin;
             if (sh > 30) { ((score_ctx*)c)->status = 2; sh = 30; }
             dot += part[b] * ((int64_t)1 << sh);
+            total += mag[b] * ((int64_t)1 << sh);
         }
-        /* exact in binary32 only while |dot| < 2^24: a wider spread of the
-         * block scales needs more bits than binary32 holds */
-        if (dot >= (1LL << 24) || dot <= -(1LL << 24)) ((score_ctx*)c)->status = 2;
+        /* Every partial sum of the products, in any order, lies within the sum
+         * of their magnitudes; below 2^24 units of the finest block grid each
+         * is exact in binary32, so d_h is the same in every summation order.
+         * Beyond it (block scales spread wide, even when the blocks cancel)
+         * an accumulation in binary32 may round, and the score is not pinned. */
+        if (total >= (1LL << 24)) ((score_ctx*)c)->status = 2;
         float d = (float)ldexp((double)dot, emin - 2);
         acc = fmaf(c->w[r * c->H + h], fmaxf(d, 0.0f), acc);
     }
@@ -227,11 +236,18 @@ static float score_one(const score_ctx* c, int64_t r, int64_t j, const int64_t* 
     int qshift = (c->q_fmt == ORC_Q_FP4) ? 1 : 9;
     float acc = 0.0f;
     for (int h = 0; h < c->H; ++h) {
-        int64_t dot = 0; /* exact: sum of integer products */
-        for (int ch = 0; ch < 128; ++ch) dot += qi[h * 128 + ch] * kv[ch];
-        /* d_h = dot * 2^-(qshift+1): exactly representable in binary32 whenever
-         * |dot| < 2^24, which the value bounds of both query formats ensure. */
-        if (dot >= (1LL << 24) || dot <= -(1LL << 24)) ((score_ctx*)c)->status = 2;
+        int64_t dot = 0, total = 0; /* exact: sum of integer products, and of their magnitudes */
+        for (int ch = 0; ch < 128; ++ch) {
+            const int64_t p = qi[h * 128 + ch] * kv[ch];
+            dot += p;
+            total += p < 0 ? -p : p;
+        }
+        /* d_h = dot * 2^-(qshift+1).  Every partial sum in any order lies
+         * within the sum of magnitudes; below 2^24 units all of them are exact
+         * in binary32, which the value bounds of both query formats ensure
+         * (FP4: at most 128 * 144 units; E4M3 with |q| <= 16: at most
+         * 128 * 8192 * 12 units). */
+        if (total >= (1LL << 24)) ((score_ctx*)c)->status = 2;
         float d = (float)ldexp((double)dot, -(qshift + 1));
         float sq = (float)orc_e8m0(c->q_sc[r * c->H + h]);
         float rh = fmaxf(d, 0.0f) * sq; /* ReLU, then the query row's power-of-two scale */
@@ -675,10 +691,34 @@ int orc_index_k_project(int64_t n, const float* x, const float* W, const int64_t
 /* `inverse` the angle is negated: sin -> -sin), fp32 products without       */
 /* fusion, then every channel to bf16 to nearest even.                      */
 /* ------------------------------------------------------------------------ */
+/* binary32 -> bf16 (binary32's sign and 8-bit exponent, 7 stored fraction
+ * bits) to nearest, ties to even, written from the format: a finite value is
+ * a multiple of its binade's bf16 spacing 2^(e-7) (e = max(floor(log2|x|),
+ * -126), the subnormal spacing below 2^-126); the multiple is rounded to the
+ * nearest integer, ties to the even one, and a result of 2^128 or more is an
+ * infinity.  Infinities stay.  A NaN stays a NaN: sign and leading payload
+ * bits kept, quiet bit set. */
 static uint16_t f32_to_bf16_rne(float f) {
     uint32_t u;
     memcpy(&u, &f, 4);
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040u);
+    if (isinf(f)) return (uint16_t)(sign | 0x7F80u);
+    const double a = fabs((double)f);
+    if (a == 0.0) return sign;
+    int e = ilogb(a);
+    if (e < -126) e = -126;
+    const double unit = ldexp(1.0, e - 7);
+    const double q = a / unit;          /* exact: a has at most 24 significant bits */
+    double r = floor(q);
+    const double frac = q - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) == 1.0)) r += 1.0;
+    const double v = r * unit;
+    if (v >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u);
+    const float vf = (float)v;          /* exact: v has at most 8 significant bits */
+    uint32_t vb;
+    memcpy(&vb, &vf, 4);
+    return (uint16_t)(sign | (vb >> 16));
 }
 
 int orc_rope_cast(int64_t n_rows, int heads, const float* in, const float* cs, int inverse, uint16_t* out) {

@@ -290,6 +290,28 @@ def test_score_mxfp4_block_scales_hand_value():
     assert s == 0.0 and math.copysign(1, s) == 1.0
 
 
+def test_score_mxfp4_flags_wide_block_spread_even_when_blocks_cancel():
+    """The exactness bound of the MXFP4 score is on the sum of the products'
+    magnitudes in units of the finest block grid, not on the final dot
+    product.  q = +6 on block 0 and -6 on block 1, k = 6, and the key's scales
+    of blocks 0 and 1 sit 2^sh above those of blocks 2 and 3: the two big blocks
+    cancel, so d_h is small, while a binary32 accumulation passes through
+    32 * 36 * 2^sh.  In quarter-units the magnitudes sum to 2 * 4,608 * 2^sh
+    plus the small blocks: above 2^24 at sh = 11, which must be refused, and
+    below it at sh = 10, where d_h = 64 * 0.5 * 6 = 192 exactly."""
+    vals = [6.0] * 32 + [-6.0] * 32 + [0.5] * 64
+    wl, q, _, w = _score_wl([vals], [6.0] * 128, [1.0])
+    for sh, flagged in ((11, True), (10, False)):
+        wl.k_sc = np.array([[127 + sh, 127 + sh, 127, 127]], np.uint8)
+        qs = np.full((1, 1, 4), 127, np.uint8)
+        if flagged:
+            with pytest.raises(ValueError):
+                oracle.index_score(wl, q, qs, w, Q_MXFP4)
+        else:
+            # blocks 0, 1 cancel exactly; blocks 2, 3: 64 * 0.5 * 6 = 192
+            assert oracle.index_score(wl, q, qs, w, Q_MXFP4)[0, 0] == 192.0
+
+
 def test_score_mxfp4_exact_rational_on_generated_rows():
     """Generated MXFP4 rows (OCP scale rule per 32-channel block): the block
     dot products summed in float64 are exact, fit binary32 exactly (the block
@@ -596,6 +618,37 @@ def test_swa_only_layers_and_encoder_ratio():
         keys = bf16_to_f64(L0.swa[lo: lo + 128])
         ref = _dense_ref(bf16_to_f64(L0.q_main[r]), keys, 1 / math.sqrt(512))
         np.testing.assert_allclose(res[0]["out"][r], ref, rtol=1e-6, atol=1e-6)
+
+
+def test_encoder_chain_reads_each_full_layers_caches():
+    """Report 2.3.1 (Reindex and Reuse read the global KV of the preceding Full
+    layer) with the reading note's encoder schedule (Full layers 2, 8 and 14,
+    each generating its own KV): layers 0..19 as one chain at ratio 2.  With at
+    most 512 visible entries the Top-K covers them all, so every layer equals
+    dense attention over [all visible entries of its group's Full cache ++ its
+    window], decoded here from the spec table.  A chain that kept the first
+    Full layer's cache would fail from layer 8 on."""
+    n, t = 400, 799  # ratio 2: all 400 entries visible to t = 799
+    wl = synth.make_workload("enc20", 31, [n], 1, synth.encoder_schedule(), ratio=2, Hm=2,
+                             q_pos=[np.array([t])], own_caches=True)
+    fulls = {L.index: L for L in wl.layers if L.mode == MODE_FULL}
+    assert sorted(fulls) == [2, 8, 14]
+    assert not np.array_equal(fulls[2].kv, fulls[8].kv) and not np.array_equal(fulls[8].k_idx, fulls[14].k_idx)
+    res = oracle.layer_chain(wl)
+    for L, r in zip(wl.layers, res):
+        q = bf16_to_f64(L.q_main[0])
+        win = bf16_to_f64(L.swa[t - 127 - int(wl.swa_pos0[0]): t + 1 - int(wl.swa_pos0[0])])
+        if L.mode == MODE_SWA_ONLY:
+            assert np.all(r["idx"] == -1)
+            keys = win
+        else:
+            g = max(i for i in fulls if i <= L.index)
+            assert np.array_equal(r["idx"][0, :n], np.arange(n)) and np.all(r["idx"][0, n:] == -1)
+            view = synth.Workload(**{f: getattr(wl, f) for f in wl.__dataclass_fields__})
+            view.kv, view.kv_sc = fulls[g].kv, fulls[g].kv_sc
+            keys = np.concatenate([decode_kv(view)[:n], win])
+        ref = _dense_ref(q, keys, 1 / math.sqrt(512))
+        np.testing.assert_allclose(r["out"][0], ref, rtol=1e-6, atol=1e-6, err_msg=f"layer {L.index}")
 
 
 def test_cache_ledger_of_this_layout():
@@ -957,6 +1010,35 @@ def test_rope_cast_zero_angle_is_the_bf16_cast_and_ties_go_even():
     want = np.vectorize(_bf16_rne_spec, otypes=[np.uint16])(x)
     assert np.array_equal(got, want)
     assert list(got[0, 0, :2]) == [0x3F80, 0x3F82]  # 1 + 2^-8 -> 1 (even); 1 + 3 2^-8 -> 1 + 2^-6 (even)
+
+
+# float32 bit patterns and their bf16 to nearest even, from the format's
+# definition (sign, 8-bit exponent, 7 stored fraction bits; NaNs stay NaNs
+# with the quiet bit set and the sign and leading payload kept)
+BF16_SPECIAL = [
+    (0x7FC00001, 0x7FC0), (0xFFC00001, 0xFFC0),   # quiet NaNs
+    (0x7F800001, 0x7FC0), (0xFF800001, 0xFFC0),   # signalling NaNs: not infinities
+    (0x7FBFFFFF, 0x7FFF),                          # a full payload does not carry into the sign
+    (0x7F800000, 0x7F80), (0xFF800000, 0xFF80),   # infinities
+    (0x7F7FFFFF, 0x7F80), (0xFF7FFFFF, 0xFF80),   # the largest float32 rounds to infinity
+    (0x7F7F8000, 0x7F80),                          # halfway above the largest bf16 (odd): infinity
+    (0x7F7F7FFF, 0x7F7F),                          # just below halfway: the largest bf16
+    (0x7F7E8000, 0x7F7E),                          # halfway, even below: stays
+    (0x00000001, 0x0000), (0x00008000, 0x0000),   # the smallest subnormal; a tie to the even zero
+    (0x00018000, 0x0002),                          # a subnormal tie to even upwards
+    (0x80000000, 0x8000), (0x00000000, 0x0000),   # signed zeros
+    (0x3F808000, 0x3F80), (0x3F818000, 0x3F82),   # ties in the normal range
+]
+
+
+def test_rope_cast_bf16_specials():
+    x = np.zeros((1, 1, 512), np.float32)
+    bits = np.array([b for b, _ in BF16_SPECIAL], np.uint32)
+    x[0, 0, : len(bits)] = bits.view(np.float32)
+    cs = np.zeros((1, 32, 2), np.float32)
+    cs[..., 0] = 1.0
+    got = oracle.rope_cast(x, cs, False)[0, 0, : len(bits)]
+    assert [int(v) for v in got] == [w for _, w in BF16_SPECIAL]
 
 
 def test_rope_cast_quarter_turns_and_inverse():
