@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CSA2 decode layer-steps/s at 128K ctx + achieved HBM GB/s; prefill index TFLOP/s"
 HBM_PEAK_GBS = 8000.0
+# the pages' exact cache configuration (report 2.4.4 and 4.2.1): 32 indexer
+# heads, E2M1 main KV with an E4M3 scale per 16 channels, MXFP4 indexer q and
+# K, FP8 SWA (as OCP MXFP8); Q_MXFP4 = 2 in the generator
+PAGES_FMT = dict(kv_fmt=1, swa_fmt=1, q_fmt=2, H=32)
 FP8_PEAK_TFLOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -49,7 +53,7 @@ def parse():
                     help="skip the layer-chain timings of the other four workloads")
     ap.add_argument("--workload", default="decode_c1",
                     choices=["decode_c1", "decode_c0", "chain_c2", "prefill_c3", "ragged_c4", "replay_c5",
-                             "decode_step_40", "decode_step_40_pages_fmt"],
+                             "encoder_replay", "decode_step_40", "decode_step_40_pages_fmt"],
                     help="decode_c1 (default) prints the full line; the others time their layer chain only")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for hardware-counter collection: a few steps, a few scan launches and one "
@@ -128,7 +132,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload.startswith("decode_step_40"):
         res = {"metric": METRIC, "workload": args.workload}
-        fmt = dict(kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4) if args.workload.endswith("pages_fmt") else {}
+        fmt = PAGES_FMT if args.workload.endswith("pages_fmt") else {}
         res.update(bench_step_40(synth, torch, dev, reps=args.steps, **fmt))
         print(json.dumps(res), flush=True)
         return
@@ -362,14 +366,14 @@ def bench_workloads(synth, C, torch, dev):
     from gpu_util import DevWorkload, prepare_chain
 
     res = {}
-    # decode_c1_pages_fmt: decode_c1 with the report's cache formats: main KV with
-    # E4M3 scales per 16 channels, indexer q and K in OCP MXFP4 (the 356-byte
-    # position) and SWA in FP8 (as OCP MXFP8)
+    # decode_c1_pages_fmt: decode_c1 in the pages' exact configuration: 32
+    # indexer heads, main KV with E4M3 scales per 16 channels, indexer q and K
+    # in OCP MXFP4 (the 356-byte position) and SWA in FP8 (as OCP MXFP8)
     for name, reps in (("decode_c0", 20), ("decode_c1_pages_fmt", 10), ("chain_c2", 5), ("ragged_c4", 5),
-                       ("prefill_c3", 3), ("replay_c5", 3)):
+                       ("prefill_c3", 3), ("replay_c5", 3), ("encoder_replay", 5)):
         t0 = time.time()
         if name == "decode_c1_pages_fmt":
-            wl = synth.config("decode_c1", kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4)
+            wl = synth.config("decode_c1", **PAGES_FMT)
         else:
             wl = synth.config(name)
         dw = DevWorkload(wl, dev)
@@ -386,7 +390,7 @@ def bench_workloads(synth, C, torch, dev):
         n_layers = len(wl.layers)
         r = {"ms_per_chain": round(ms, 4), "layers": n_layers, "rows": wl.total_q,
              "entries": wl.total_entries, "layer_steps_per_s": round(n_layers * 1000.0 / ms, 1)}
-        if name in ("prefill_c3", "replay_c5"):
+        if name in ("prefill_c3", "replay_c5", "encoder_replay"):
             # many query rows share each scan: FLOP/s.  Full layers score every
             # visible entry, Reindex layers their pool; attention reads the
             # selected entries and the (replay-cut) window
@@ -413,9 +417,9 @@ def bench_workloads(synth, C, torch, dev):
         del dw, outs, call, pb, pp, pc, wl
         torch.cuda.empty_cache()
     res["decode_step_40"] = bench_step_40(synth, torch, dev)
-    # the same step with every cache in the report's formats (E4M3/16 main KV,
-    # MXFP4 indexer, FP8 SWA as MXFP8)
-    res["decode_step_40_pages_fmt"] = bench_step_40(synth, torch, dev, kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4)
+    # the same step in the pages' exact configuration (32 indexer heads,
+    # E4M3/16 main KV, MXFP4 indexer, FP8 SWA as MXFP8)
+    res["decode_step_40_pages_fmt"] = bench_step_40(synth, torch, dev, **PAGES_FMT)
     for kv_fmt in (1, 0):
         res["kv_append_e4m3" if kv_fmt == 1 else "kv_append_mxfp4"] = bench_append(C, torch, dev, kv_fmt)
     res["compress"] = bench_compress(C, torch, dev)
@@ -512,10 +516,10 @@ def bench_append(C, torch, dev, kv_fmt, n=131072, reps=20):
 
 def bench_step_40(synth, torch, dev, reps=5, **fmt):
     """One decode token of each of 64 sequences at 131,072 tokens through all 40
-    layers: the five chains the layers form (two sliding-window layers, three
-    encoder groups at ratio 2 over 65,536 entries with their own caches, the
-    decoder at ratio 1 over 131,072 entries with the pool), run back to back
-    on one stream and timed together."""
+    layers: the two chains the layers form (the encoder layers 0..19 at ratio
+    2 over 65,536 entries, with three Full layers each reading its own caches;
+    the decoder at ratio 1 over 131,072 entries with the pool), run back to
+    back on one stream and timed together."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gpu_util import DevWorkload, prepare_chain
 
@@ -584,15 +588,37 @@ def bench_prefill(args, C, synth, torch, dev):
             "mfma": "bf16 32x32x16 (E4M3 x E2M1 operands converted exactly)"}
 
 
+def host_cpu():
+    """The host's logical CPU count (`nproc`: the ones this process may use),
+    os.cpu_count() and the CPU model name from /proc/cpuinfo."""
+    import subprocess
+
+    try:
+        nproc = int(subprocess.run(["nproc"], capture_output=True, text=True, check=True).stdout.strip())
+    except (OSError, ValueError, subprocess.CalledProcessError):
+        nproc = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": nproc, "os_cpu_count": os.cpu_count(), "model": model}
+
+
 def cpu_baseline(args, wl, dw, C, run_chain):
     """The CPU oracle on the first cpu_sample_seqs sequences of the same
-    workload (their full layer chain), scaled to layer-steps/s of the whole
-    batch.  Its indices are also compared with the GPU's for those rows."""
+    workload (their full layer chain), on every core this process may use,
+    scaled to layer-steps/s of the whole batch.  Its indices are also
+    compared with the GPU's for those rows."""
     import numpy as np
 
     import oracle
 
-    threads = max(1, min(16, os.cpu_count() or 1))
+    host = host_cpu()
+    threads = max(1, host["nproc"])
     oracle.NTHREADS = threads
     rows = np.arange(min(args.cpu_sample_seqs, wl.total_q))
     t0 = time.time()
@@ -605,10 +631,11 @@ def cpu_baseline(args, wl, dw, C, run_chain):
     err = float(np.abs(got_out.astype(np.float64) - ref[0]["out"]).max())
     frac = len(rows) / wl.total_q
     value = 1.0 / (dt / frac)
-    log(f"[bench] oracle: {dt:.1f}s for {len(rows)} sequences on {threads} threads")
-    return {"value": round(value, 5), "unit": "layer-steps/s", "cores": int(min(threads, len(rows))), "kind": "oracle",
+    log(f"[bench] oracle: {dt:.1f}s for {len(rows)} sequences on {threads} threads ({host['model']})")
+    return {"value": round(value, 5), "unit": "layer-steps/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {wl.total_q} sequences of decode_c1 (full 131,072-entry scan, Top-512, "
                       f"attention), {dt:.1f} s wall, scaled by {wl.total_q}/{len(rows)}",
+            "host": host, "work_units": "score rows split into 65,536-slot pieces, attention rows",
             "sample_indices_equal_gpu": idx_equal, "sample_attn_max_abs_err": err}
 
 

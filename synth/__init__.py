@@ -14,6 +14,14 @@ reading note's decoder schedule table):
               8,192 query tokens t = 253,952..262,143, Full + 5 Reuse, FP8 indexer q
   ragged_c4   48 sequences, N_b log-uniform in [4,096, 1,048,576], 4 queries at
               t = N_b-4..N_b-1, decoder layers 20..39
+  replay_c5   decoder SWA bounded replay: 16 x 131,072 entries, the last 128
+              prompt tokens through decoder layers 20..39, windows cut at the
+              replay start
+  encoder_replay  encoder SWA bounded replay: 262,144 tokens at ratio 2, the
+              last 128 tokens of a cached prefix replayed with a 1,024-token
+              uncached suffix (1,152 E4M3 query rows), Full + 5 Reuse
+  decode_step_40  one decode token through all 40 layers (encoder chain 0..19
+              at ratio 2 with three Full caches, decoder chain 20..39)
 Every raw value is N(0,1) before encoding; head weights are U(0,1).
 """
 from __future__ import annotations
@@ -160,6 +168,13 @@ class Layer:
     q_main: Optional[np.ndarray] = None   # [T][Hm][512] bf16 bits (u16)
     swa: Optional[np.ndarray] = None      # [rows][512] bf16 bits (u16)
     build_pool: bool = False
+    # a Full layer's own caches (None: the workload's); the layers up to the
+    # next Full layer read them (report 2.3.1: Reindex and Reuse share the
+    # global KV and indexer K of the preceding Full layer)
+    k_idx: Optional[np.ndarray] = None
+    k_sc: Optional[np.ndarray] = None
+    kv: Optional[np.ndarray] = None
+    kv_sc: Optional[np.ndarray] = None
 
 
 @dataclass
@@ -229,20 +244,17 @@ def encoder_schedule():
 
 def decode_step_40(n_seq=64, tokens=131072, **kw):
     """One decode token of every sequence through all 40 layers (report 4.2.1),
-    as the chains the layers form: the two sliding-window layers; each encoder
-    group (Full + 5 Reuse at ratio 2 over tokens / 2 entries, its own source
-    cache); the decoder layers 20..39 at ratio 1 over `tokens` entries with the
-    pool.  Returns the workloads in layer order."""
+    as the two chains the layers form: the encoder layers 0..19 at ratio 2 over
+    tokens / 2 entries (two sliding-window layers, then three groups of a Full
+    layer and five Reuse layers, each Full layer with its own caches) and the
+    decoder layers 20..39 at ratio 1 over `tokens` entries with the pool.
+    Returns the workloads in layer order."""
     t = [np.array([tokens - 1], np.int64)] * n_seq
-    enc = encoder_schedule()
     seed = 0xC5A20000 + CONFIG_IDS["decode_step_40"]
-    wls = [make_workload("step40_swa", seed, [tokens // 2] * n_seq, 1, enc[:2], ratio=2, q_pos=t, gen_kv=False, **kw)]
-    for gi, g0 in enumerate((2, 8, 14)):
-        sched = [x for x in enc if g0 <= x[0] < g0 + 6]
-        wls.append(make_workload(f"step40_enc{g0}", seed + 16 * (gi + 1), [tokens // 2] * n_seq, 1, sched, ratio=2,
-                                 q_pos=t, **kw))
-    wls.append(make_workload("step40_dec", seed + 64, [tokens] * n_seq, 1, decoder_schedule(), q_pos=t, **kw))
-    return wls
+    enc = make_workload("step40_enc", seed, [tokens // 2] * n_seq, 1, encoder_schedule(), ratio=2, q_pos=t,
+                        own_caches=True, **kw)
+    dec = make_workload("step40_dec", seed + 64, [tokens] * n_seq, 1, decoder_schedule(), q_pos=t, **kw)
+    return [enc, dec]
 
 
 def ragged_lengths(seed, n_seq, lo=4096, hi=1048576):
@@ -256,7 +268,7 @@ def ragged_lengths(seed, n_seq, lo=4096, hi=1048576):
 
 def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=64, Hm=64, K=512, W=128,
                   block=8, max_blocks=2048, q_fmt=Q_FP4, q_pos=None, gen_kv=True, gen_layers=True, replay_s=None,
-                  kv_fmt=0, swa_fmt=0):
+                  kv_fmt=0, swa_fmt=0, own_caches=False):
     """Build a workload.  n_entries: per-sequence entry counts.  queries_per_seq:
     T (same for all sequences).  q_pos: explicit token positions per sequence
     (list of arrays) or None for the decode shape t = N*ratio - T + i.
@@ -267,7 +279,10 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
     MXFP8 (E4M3 with one E8M0 per 32 channels, codes then scales per row).
     q_fmt: indexer queries, Q_FP4 / Q_FP8 (one E8M0 per head row, indexer K
     with one E8M0 per row), or Q_MXFP4 (the report's indexer format: queries
-    and indexer K both OCP MXFP4 with one E8M0 per 32 channels)."""
+    and indexer K both OCP MXFP4 with one E8M0 per 32 channels).
+    own_caches: every Full layer draws its own main KV and indexer K (the
+    first Full layer's are also the workload's), as the encoder's Full layers
+    2, 8 and 14 each generate theirs."""
     n_entries = np.asarray(n_entries, np.int64)
     n_seq = len(n_entries)
     entry_off = np.zeros(n_seq + 1, np.int64)
@@ -292,20 +307,32 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
     wl.kv_fmt = int(kv_fmt)
     wl.swa_fmt = int(swa_fmt)
     total = int(entry_off[-1])
-    if gen_kv:
+
+    def caches(tid_k, tid_kv):
         if q_fmt == Q_MXFP4:  # the report's indexer format: one E8M0 per 32 channels
-            wl.k_idx, wl.k_sc = mxfp4_rows(seed, TID_K, total, 128, 32)
+            k_idx, k_sc = mxfp4_rows(seed, tid_k, total, 128, 32)
         else:
-            wl.k_idx, ksc = mxfp4_rows(seed, TID_K, total, 128, 128)
-            wl.k_sc = np.ascontiguousarray(ksc.reshape(total))
+            k_idx, ksc = mxfp4_rows(seed, tid_k, total, 128, 128)
+            k_sc = np.ascontiguousarray(ksc.reshape(total))
         if kv_fmt == 1:
-            wl.kv, wl.kv_sc = e2m1_e4m3_rows(seed, TID_KV, total, 512)
+            kv, kv_sc = e2m1_e4m3_rows(seed, tid_kv, total, 512)
         else:
-            wl.kv, wl.kv_sc = mxfp4_rows(seed, TID_KV, total, 512, 32)
+            kv, kv_sc = mxfp4_rows(seed, tid_kv, total, 512, 32)
+        return k_idx, k_sc, kv, kv_sc
+
+    if gen_kv:
+        wl.k_idx, wl.k_sc, wl.kv, wl.kv_sc = caches(TID_K, TID_KV)
     nq = len(q_pos_all)
     swa_rows = int(swa_len.sum())
+    first_full = True
     for (li, mode, pool) in schedule:
         L = Layer(index=li, mode=mode, q_fmt=q_fmt, build_pool=pool)
+        if own_caches and gen_kv and mode == MODE_FULL:
+            if first_full:
+                L.k_idx, L.k_sc, L.kv, L.kv_sc = wl.k_idx, wl.k_sc, wl.kv, wl.kv_sc
+            else:
+                L.k_idx, L.k_sc, L.kv, L.kv_sc = caches(_tid(li, 4), _tid(li, 5))
+            first_full = False
         if gen_layers:
             if mode in (MODE_FULL, MODE_REINDEX):
                 if q_fmt == Q_FP4:
@@ -331,7 +358,7 @@ def make_workload(name, seed, n_entries, queries_per_seq, schedule, ratio=1, H=6
 
 
 CONFIG_IDS = {"decode_c0": 0, "decode_c1": 1, "chain_c2": 2, "prefill_c3": 3, "ragged_c4": 4, "replay_c5": 5,
-              "decode_step_40": 6}
+              "decode_step_40": 6, "encoder_replay": 7}
 
 
 def config(name, **kw):
@@ -365,6 +392,22 @@ def config(name, **kw):
         T = kw.pop("T", 128)
         sched = kw.pop("schedule", decoder_schedule())
         return make_workload(name, seed, [n] * n_seq, T, sched, replay_s=[n - T] * n_seq, **kw)
+    if name == "encoder_replay":
+        # encoder SWA bounded replay: a cached prefix of `prefix` tokens whose
+        # encoder SWA KV is missing; its last W tokens are replayed together
+        # with an uncached suffix through one encoder group (Full + 5 Reuse at
+        # ratio 2, E4M3 indexer queries).  The replayed rows reuse the cached
+        # global KV, the suffix's entries are in the cache too (the suffix
+        # writes global KV), and every window is cut at the replay start
+        tokens = kw.pop("tokens", 262144)
+        suffix = kw.pop("suffix", 1024)
+        W = kw.get("W", 128)
+        n_layers = kw.pop("n_layers", 6)
+        s0 = tokens - suffix - W
+        sched = [(2, MODE_FULL, False)] + [(2 + i, MODE_REUSE, False) for i in range(1, n_layers)]
+        qp = [np.arange(s0, tokens, dtype=np.int64)]
+        return make_workload(name, seed, [tokens // 2], len(qp[0]), sched, ratio=2, q_fmt=Q_FP8, q_pos=qp,
+                             replay_s=[s0], **kw)
     if name == "ragged_c4":
         n_seq = kw.pop("n_seq", 48)
         lens = kw.pop("lengths", None)

@@ -30,6 +30,10 @@ class DevWorkload:
             for f in ("q_idx", "q_sc", "w", "q_main", "swa"):
                 a = getattr(L, f)
                 d[f] = None if a is None else dev(a, device)
+            # a Full layer's own caches; the first Full layer's are the workload's
+            for f in ("k_idx", "k_sc", "kv", "kv_sc"):
+                a = getattr(L, f, None)
+                d[f] = None if a is None else (getattr(self, f) if a is getattr(wl, f) else dev(a, device))
             self.layers.append(d)
 
 
@@ -48,7 +52,10 @@ def prepare_chain(dw, want_idx=True, want_lse=True, ws=None, pool=True):
               "q_idx": d["q_idx"], "q_sc": d["q_sc"], "w": d["w"], "q_main": d["q_main"], "swa": d["swa"],
               "out": out, "lse": lse, "idx_out": idx}
         if d["mode"] == C.CSA2_MODE_FULL:
-            sp.update(kv_fp4=dw.kv, kv_sc=dw.kv_sc, k_fp4=dw.k_idx, k_sc=dw.k_sc, kv_fmt=getattr(wl, "kv_fmt", 0))
+            own = d.get("kv") is not None
+            sp.update(kv_fp4=d["kv"] if own else dw.kv, kv_sc=d["kv_sc"] if own else dw.kv_sc,
+                      k_fp4=d["k_idx"] if own else dw.k_idx, k_sc=d["k_sc"] if own else dw.k_sc,
+                      kv_fmt=getattr(wl, "kv_fmt", 0))
         specs.append(sp)
         outs.append({"layer": d["index"], "out": out, "lse": lse, "idx": idx})
     layers = C.make_layers(specs)

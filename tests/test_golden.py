@@ -76,9 +76,12 @@ def test_forty_layer_step_matches_pages():
         assert wl.ratio == (cfg["decoder"]["ratio"] if dec else enc["ratio"])
         assert list(wl.n_entries) == [tokens if dec else tokens // 2] * 2
         assert list(wl.q_pos) == [tokens - 1] * 2
-    # every encoder group reads its own source cache
-    caches = [wl.k_idx.tobytes() for wl in wls[1:4]]
-    assert len(set(caches)) == 3
+    # the encoder layers form one chain in which every group's Full layer
+    # carries its own source cache
+    assert len(wls) == 2
+    fulls = [L for L in wls[0].layers if L.mode == synth.MODE_FULL]
+    assert [L.index for L in fulls] == [2, 8, 14]
+    assert len({L.k_idx.tobytes() for L in fulls}) == 3 and len({L.kv.tobytes() for L in fulls}) == 3
 
 
 def test_path_sizes_match_pages():

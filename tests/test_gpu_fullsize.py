@@ -8,7 +8,13 @@ for bit, their attention outputs within |gpu - ref| <= 2e-3 + 1e-2 |ref|.
               of 4 rows compared over all 131,072 slots)
   chain_c2    16 x 1,048,576 entries, decoder layers 20..39 with pool (2 rows)
   prefill_c3  8,192 E4M3 query rows over 131,072 entries (ratio 2), Full + 5 Reuse
-              (first, last and every 512th row)
+              (first, last and every 512th row); the index scores of every 16th
+              row and the first and last 64 rows, over all 131,072 slots
+  encoder_replay  1,152 E4M3 query rows (the last 128 prefix tokens replayed with
+              a 1,024-token suffix) over 131,072 entries, Full + 5 Reuse
+  decode_step_40  one decode token of 64 sequences through all 40 layers, in the
+              pages' exact configuration (32 indexer heads, E4M3/16 main KV,
+              MXFP4 indexer, FP8 SWA): 4 sequences checked
   ragged_c4   48 sequences of 4K..1M entries, 4 rows each, layers 20..39 with pool
               (the shortest and the longest sequence plus two more: 16 rows)
 """
@@ -76,6 +82,35 @@ def test_fullsize_prefill_c3():
     wl = synth.config("prefill_c3")
     rows = np.unique(np.concatenate([np.arange(0, 8192, 512), [1, 8190, 8191]]))
     _check_chain(wl, rows, "prefill_c3")
+
+
+@pytest.mark.timeout(600)
+def test_fullsize_prefill_c3_scores():
+    """The prefill scorer's scores at full size, bit for bit, on every 16th row
+    plus the first and last 64 (its segments, double buffer and causal cut-offs
+    at the real shape)."""
+    wl = synth.config("prefill_c3", n_layers=1, Hm=16)
+    dw = DevWorkload(wl)
+    L, dL = wl.layers[0], dw.layers[0]
+    rows = np.unique(np.concatenate([np.arange(0, 8192, 16), np.arange(64), np.arange(8192 - 64, 8192)]))
+    got = C.csa2_index_score(dw.batch, wl.H, C.CSA2_Q_FP8, dL["q_idx"], dL["q_sc"], dL["w"], dw.k_idx, dw.k_sc)
+    got = got[torch.from_numpy(rows).to(got.device)].cpu().numpy()
+    _say(f"[prefill_c3 scores] GPU done; oracle on {len(rows)} rows x {wl.total_entries} slots")
+    ref = oracle.index_score(wl, L.q_idx, L.q_sc, L.w, synth.Q_FP8, rows=rows)
+    bad = np.nonzero((got.view(np.uint32) != ref.view(np.uint32)).any(axis=1))[0]
+    assert len(bad) == 0, f"{len(bad)} rows differ, first row {rows[bad[0]]}"
+    _say(f"[prefill_c3 scores] {len(rows)} rows equal bit for bit")
+
+
+def test_fullsize_encoder_replay():
+    wl = synth.config("encoder_replay")
+    rows = np.unique(np.concatenate([np.arange(0, wl.total_q, 64), [1, 127, 128, 129, wl.total_q - 1]]))
+    _check_chain(wl, rows, "encoder_replay")
+
+
+def test_fullsize_decode_step_40_pages():
+    for wl in synth.decode_step_40(kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4, H=32):
+        _check_chain(wl, np.array([0, 21, 42, 63]), wl.name)
 
 
 def test_fullsize_ragged_c4():

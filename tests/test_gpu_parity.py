@@ -98,10 +98,19 @@ def test_index_score_cand_bitwise(q_fmt):
         assert np.array_equal(h[r], np.bincount(fin.view(np.uint32) >> 19, minlength=4096)), r
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "fp8_h32", "fp4", "mxfp4", "mxfp4_h32"])
+# E4M3 query rows over 60,000 entries at ratio 2: four 16,384-position
+# segments of the prefill scorer, rows of one 8-row group with causal cutoffs
+# early, mid-segment, mid-chunk (not a multiple of 512) and at the end
+_PF8_SEG_T = np.array([9999, 32770, 33000, 40033, 65535, 66001, 99999, 100001, 110003, 119999, 20, 1], np.int64)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp8_h32", "fp8_segments", "fp4", "mxfp4", "mxfp4_h32"])
 def test_index_score_prefill_bitwise(fmt):
     if fmt == "fp8":
         wl = synth.config("prefill_c3", tokens=6002, T=150, n_layers=1, Hm=16)
+    elif fmt == "fp8_segments":
+        wl = synth.make_workload("pf8seg", 92, [60000], len(_PF8_SEG_T), [(2, synth.MODE_FULL, False)], ratio=2,
+                                 Hm=16, q_fmt=synth.Q_FP8, q_pos=[_PF8_SEG_T])
     elif fmt == "fp8_h32":  # 32 indexer heads, two sequences, 61 rows each (a ragged row group)
         wl = synth.make_workload("pf8h32", 91, [2500, 3100], 61, [(2, synth.MODE_FULL, False)], ratio=2, H=32,
                                  Hm=16, q_fmt=synth.Q_FP8)
@@ -299,6 +308,31 @@ CHAIN_CASES = {
     "decoder_replay": lambda: synth.config("replay_c5", n_seq=2, n=6000, T=128, Hm=16,
                                            schedule=[(20, synth.MODE_FULL, True), (24, synth.MODE_REINDEX, False),
                                                      (25, synth.MODE_REUSE, False)]),
+    # encoder layers 0..19 as one chain at ratio 2: layers 0-1 sliding window
+    # only, then Full layers 2, 8 and 14, each with its own main KV and indexer
+    # K, read by the Reuse layers after it (report 2.3.1; reading note schedule
+    # table); FP4 query rows (decode) and E4M3 query rows (prefill)
+    "encoder_20": lambda: synth.make_workload("enc20", 13, [3000, 9000], 2, synth.encoder_schedule(), ratio=2, Hm=16,
+                                              q_pos=[np.array([5990, 5999]), np.array([17000, 17999])],
+                                              own_caches=True),
+    "encoder_20_fp8": lambda: synth.make_workload("enc20f8", 14, [4000], 40, synth.encoder_schedule(), ratio=2,
+                                                  Hm=16, q_fmt=synth.Q_FP8, own_caches=True,
+                                                  q_pos=[np.arange(7960, 8000)]),
+    # the report's 32 indexer heads through the chain: the one-row and the
+    # four-row scan with their fused lists, Reindex on the pool
+    "c2_small_h32": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16, H=32),
+    "c4_small_h32": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16, H=32),
+    # the pages' exact configuration: 32 indexer heads, E4M3/16 main KV, MXFP4
+    # indexer q and K, FP8 SWA (as OCP MXFP8)
+    "c2_small_pages_h32": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16, H=32, kv_fmt=1, swa_fmt=1,
+                                               q_fmt=synth.Q_MXFP4),
+    "c4_small_pages_h32": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16, H=32,
+                                               kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4),
+    # encoder SWA bounded replay (course notes "3. 通用基础设施" §3.2.2,
+    # encoder paragraph): the last 128 tokens of the cached prefix replayed
+    # with a 200-token uncached suffix as E4M3 query rows through one encoder
+    # group at ratio 2, every window cut at the replay start
+    "encoder_replay": lambda: synth.config("encoder_replay", tokens=6000, suffix=200, Hm=16),
     "encoder_group": lambda: synth.make_workload("enc", 12, [700, 2500], 3, [(0, synth.MODE_SWA_ONLY, False),
                                                                              (2, synth.MODE_FULL, False),
                                                                              (3, synth.MODE_REUSE, False),
@@ -328,11 +362,12 @@ def test_layer_chain_matches_oracle(case):
 @pytest.mark.gpu
 @pytest.mark.parametrize("fmt", ["default", "pages"])
 def test_decode_step_40_matches_oracle(fmt):
-    """One decode token through all 40 layers, as the five chains the layers
-    form (sliding-window layers, three encoder groups at ratio 2, the decoder
-    at ratio 1), each against the oracle; in this library's default formats
-    and in the pages' (E4M3/16 main KV, MXFP4 indexer, FP8 SWA)."""
-    kw = dict(kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4) if fmt == "pages" else {}
+    """One decode token through all 40 layers, as the two chains the layers
+    form (the encoder layers 0..19 at ratio 2 with three Full caches, the
+    decoder at ratio 1), each against the oracle; in this library's default
+    formats and in the pages' exact configuration (32 indexer heads, E4M3/16
+    main KV, MXFP4 indexer, FP8 SWA; report 4.2.1 and 2.4.4)."""
+    kw = dict(kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4, H=32) if fmt == "pages" else {}
     for wl in synth.decode_step_40(n_seq=2, tokens=6000, Hm=16, **kw):
         dw = DevWorkload(wl)
         outs, (pb, pp, pc), _ = run_chain(dw)
@@ -518,3 +553,18 @@ def test_rope_cast_bitwise(n, heads, inverse):
     cs = np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
     got = C.csa2_rope_cast(dev(x), dev(cs), inverse=inverse).cpu().numpy()
     assert np.array_equal(got, oracle.rope_cast(x, cs, inverse))
+
+
+def test_rope_cast_specials_bitwise():
+    """NaNs (quiet and signalling), infinities, the largest float32 and ties
+    around the largest bf16, in the channels that are only cast: equal to the
+    oracle bit for bit (NaNs stay NaNs, overflow gives infinity)."""
+    from test_oracle_pins import BF16_SPECIAL
+    x = np.random.default_rng(77).standard_normal((3, 4, 512), dtype=np.float32)
+    bits = np.array([b for b, _ in BF16_SPECIAL], np.uint32)
+    x[:, :, : len(bits)] = bits.view(np.float32)
+    th = np.random.default_rng(78).uniform(-np.pi, np.pi, size=(3, 32))
+    cs = np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
+    got = C.csa2_rope_cast(dev(x), dev(cs)).cpu().numpy()
+    assert np.array_equal(got, oracle.rope_cast(x, cs, False))
+    assert [int(v) for v in got[0, 0, : len(bits)]] == [w for _, w in BF16_SPECIAL]
