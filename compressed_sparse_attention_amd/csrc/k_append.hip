@@ -237,6 +237,18 @@ __global__ __launch_bounds__(256) void k_index_k_project(const float* __restrict
     }
 }
 
+// binary32 -> bf16 to nearest even.  Finite values and infinities: adding
+// 0x7FFF plus the kept part's lowest bit carries exactly when the dropped 16
+// bits exceed half a unit, or equal it with an odd kept part; a carry out of
+// the largest finite value gives infinity.  A NaN stays a NaN: its sign and
+// leading payload bits are kept and the quiet bit is set (the addition alone
+// could carry a NaN into an infinity or the other sign).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // RoPE and cast around attention (the report's kernel flow: a fused
 // "RoPE-attention-RoPE-cast" kernel rotates the query before attention and
 // turns the output's rotated part back after it, then casts).  The pairs and
@@ -272,12 +284,7 @@ __global__ __launch_bounds__(256) void k_rope_cast(const float* __restrict__ in,
     }
     uint32_t w[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
-        lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;  // bf16, nearest even
-        hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
-        w[k] = lo | (hi << 16);
-    }
+    for (int k = 0; k < 4; ++k) w[k] = bf16_rne(v[2 * k]) | (bf16_rne(v[2 * k + 1]) << 16);
     *reinterpret_cast<uint4*>(out + hr * 512 + 8 * lane) = uint4{w[0], w[1], w[2], w[3]};
 }
 
