@@ -18,13 +18,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, 1, 2, 3, 4
+CSA2_ERR_SCRATCH = 5
 CSA2_Q_FP4, CSA2_Q_FP8, CSA2_Q_MXFP4 = 0, 1, 2
 CSA2_KV_MXFP4, CSA2_KV_E4M3_16 = 0, 1
 CSA2_MODE_SWA_ONLY, CSA2_MODE_FULL, CSA2_MODE_REINDEX, CSA2_MODE_REUSE = 0, 1, 2, 3
 CSA2_LAYER_BUILD_POOL = 1
 CSA2_WS_TOPK, CSA2_WS_BLOCK_POOL, CSA2_WS_SPARSE_ATTN, CSA2_WS_LAYER_CHAIN = 1, 2, 3, 4
 
-EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_block_pool", "csa2_gather_dequant", "csa2_sparse_attn",
+EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_topk_noalloc", "csa2_block_pool", "csa2_gather_dequant", "csa2_sparse_attn",
            "csa2_layer_chain", "csa2_rope_cast", "csa2_index_k_project", "csa2_compress", "csa2_kv_append", "csa2_workspace_size", "csa2_status_string", "csa2_last_hip_error",
            "csa2_version")
 
@@ -77,6 +78,7 @@ def lib():
         B, S = ctypes.POINTER(csa2_batch), ctypes.POINTER(csa2_swa_layout)
         L.csa2_index_score.argtypes = [B, i32, i32, _vp, _vp, _vp, _vp, _vp, _vp, i32, _vp, i64, _vp, _vp]
         L.csa2_topk.argtypes = [B, _vp, i64, _vp, i32, _vp, i32, _vp, _vp, _vp, sz, _vp]
+        L.csa2_topk_noalloc.argtypes = [B, _vp, i64, _vp, i32, _vp, i32, _vp, _vp, _vp]
         L.csa2_block_pool.argtypes = [B, _vp, i64, i32, i32, _vp, _vp, _vp, _vp, sz, _vp]
         L.csa2_gather_dequant.argtypes = [B, i32, _vp, _vp, _vp, i32, _vp, _vp]
         L.csa2_rope_cast.argtypes = [ctypes.c_int64, i32, _vp, _vp, i32, _vp, _vp]
@@ -92,8 +94,9 @@ def lib():
         L.csa2_status_string.restype = ctypes.c_char_p
         L.csa2_last_hip_error.restype = i32
         L.csa2_version.restype = i32
-        for name in ("csa2_index_score", "csa2_topk", "csa2_block_pool", "csa2_gather_dequant", "csa2_sparse_attn",
-                     "csa2_layer_chain"):
+        for name in ("csa2_index_score", "csa2_topk", "csa2_topk_noalloc", "csa2_block_pool", "csa2_gather_dequant",
+                     "csa2_sparse_attn", "csa2_layer_chain", "csa2_rope_cast", "csa2_index_k_project", "csa2_compress",
+                     "csa2_kv_append"):
             getattr(L, name).restype = i32
         _lib_handle = L
     return _lib_handle
@@ -215,6 +218,16 @@ def csa2_topk(batch, scores, K, cand=None, cand_count=None, hist=None, idx=None,
                          0 if cand is None else cand.shape[1], _ptr(cand_count), K, _ptr(hist), _ptr(idx), _ptr(ws),
                          ws.numel(), _stream(stream))
     _check(st, "csa2_topk")
+    return idx
+
+
+def csa2_topk_noalloc(batch, scores, K, idx, cand=None, cand_count=None, hist=None, stream=None):
+    """csa2_topk with its workspace in the library's static scratch (no
+    allocation by the library; the caller passes the output idx)."""
+    st = lib().csa2_topk_noalloc(ctypes.byref(batch.c), _ptr(scores), scores.shape[1], _ptr(cand),
+                                 0 if cand is None else cand.shape[1], _ptr(cand_count), K, _ptr(hist), _ptr(idx),
+                                 _stream(stream))
+    _check(st, "csa2_topk_noalloc")
     return idx
 
 

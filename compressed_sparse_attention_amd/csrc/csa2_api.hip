@@ -3,6 +3,7 @@
 // caller's stream and returns; nothing here synchronises with the device.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "csa2_internal.h"
 
@@ -125,6 +126,50 @@ __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// Scratch of csa2_topk_noalloc: the Top-K workspace of up to kNoAllocTopkRows
+// query rows, a file-scope device array that each GPU the library runs on
+// holds until the process ends.  Host code never passes `scratch` itself to a
+// kernel (in host code the name is a stand-in, not the device address): the
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+constexpr int kNoAllocTopkRows = 256;
+constexpr size_t kNoAllocScratchBytes =
+    ((size_t)kNoAllocTopkRows * kHistBins * 4 + 255) / 256 * 256 +
+    ((size_t)kNoAllocTopkRows * sizeof(RowSel) + 255) / 256 * 256 +
+    ((size_t)kNoAllocTopkRows * kCandCap * 8 + 255) / 256 * 256;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on `dev` (nullptr on failure; *err holds
+// the HIP error).
+void* scratch_on(int dev, hipError_t* err) {
+    *err = hipSuccess;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+    int cur = 0;
+    if ((*err = hipGetDevice(&cur)) != hipSuccess) return nullptr;
+    if (cur != dev && (*err = hipSetDevice(dev)) != hipSuccess) return nullptr;
+    void* ptr = nullptr;
+    *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (*err == hipSuccess) *err = e2;
+    }
+    if (*err != hipSuccess || !ptr) {
+        if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+        return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+    return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,6 +185,7 @@ CSA2_API const char* csa2_status_string(csa2_status s) {
         case CSA2_ERR_UNSUPPORTED: return "unsupported size or format";
         case CSA2_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case CSA2_ERR_HIP: return "HIP launch error";
+        case CSA2_ERR_SCRATCH: return "the problem exceeds the static scratch of the allocation-free call";
         default: return "unknown status";
     }
 }
@@ -234,21 +280,39 @@ CSA2_API csa2_status csa2_kv_append(int64_t n, const float* x, const float* rope
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Host validation shared by csa2_topk and csa2_topk_noalloc.
+csa2_status topk_args(const csa2_batch* batch, const float* scores, int64_t score_stride, const int32_t* cand,
+                      int32_t cand_stride, const int32_t* cand_count, int32_t K, int32_t* idx, Geometry* g,
+                      int64_t* max_slots) {
+    csa2_status st = batch_geometry(batch, g);
+    if (st) return st;
+    if (!scores || !idx) return CSA2_ERR_INVALID_ARG;
+    if (K < 1 || K > kMaxK) return K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
+    *max_slots = g->max_entries;
+    if (cand) {
+        if (!cand_count || cand_stride < 1 || score_stride < cand_stride) return CSA2_ERR_INVALID_ARG;
+        *max_slots = cand_stride;
+    } else if (score_stride < g->max_entries) {
+        return CSA2_ERR_INVALID_ARG;
+    }
+    return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 CSA2_API csa2_status csa2_topk(const csa2_batch* batch, const float* scores, int64_t score_stride,
                                const int32_t* cand, int32_t cand_stride, const int32_t* cand_count, int32_t K,
                                const uint32_t* hist, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
     Geometry g;
-    csa2_status st = batch_geometry(batch, &g);
+    int64_t max_slots = 0;
+    csa2_status st = topk_args(batch, scores, score_stride, cand, cand_stride, cand_count, K, idx, &g, &max_slots);
     if (st) return st;
-    if (!scores || !idx) return CSA2_ERR_INVALID_ARG;
-    if (K < 1 || K > kMaxK) return K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
-    int64_t max_slots = g.max_entries;
-    if (cand) {
-        if (!cand_count || cand_stride < 1 || score_stride < cand_stride) return CSA2_ERR_INVALID_ARG;
-        max_slots = cand_stride;
-    } else if (score_stride < g.max_entries) {
-        return CSA2_ERR_INVALID_ARG;
-    }
     if ((st = check_ws(ws, ws_bytes, topk_ws_bytes(g.total_q)))) return st;
     TopkLaunch a{};
     a.b = batch;
@@ -267,6 +331,23 @@ CSA2_API csa2_status csa2_topk(const csa2_batch* batch, const float* scores, int
     a.hist = hist;
     hipError_t e = launch_topk(a, stream);
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
+}
+
+CSA2_API csa2_status csa2_topk_noalloc(const csa2_batch* batch, const float* scores, int64_t score_stride,
+                                       const int32_t* cand, int32_t cand_stride, const int32_t* cand_count, int32_t K,
+                                       const uint32_t* hist, int32_t* idx, hipStream_t stream) {
+    Geometry g;
+    int64_t max_slots = 0;
+    csa2_status st = topk_args(batch, scores, score_stride, cand, cand_stride, cand_count, K, idx, &g, &max_slots);
+    if (st) return st;
+    if (topk_ws_bytes(g.total_q) > kNoAllocScratchBytes) return CSA2_ERR_SCRATCH;
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(e);
+    void* ws = scratch_on(dev, &e);
+    if (!ws) return hip_fail(e);
+    return csa2_topk(batch, scores, score_stride, cand, cand_stride, cand_count, K, hist, idx, ws,
+                     kNoAllocScratchBytes, stream);
 }
 
 CSA2_API csa2_status csa2_block_pool(const csa2_batch* batch, const float* scores, int64_t score_stride,

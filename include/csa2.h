@@ -14,14 +14,16 @@
  * Conventions for every call
  *   - Tensor pointers marked (device) are device memory owned by the caller.
  *     The library never allocates or frees device memory.  Scratch memory is a
- *     caller workspace of at least csa2_workspace_size() bytes, 256-byte aligned.
+ *     caller workspace of at least csa2_workspace_size() bytes, 256-byte aligned
+ *     (csa2_topk_noalloc alone uses a static array in the library instead).
  *   - Pointers marked (host) are read on the host during the call only.
  *   - Calls are asynchronous on `stream`: they enqueue kernels and return.  The
  *     library never synchronises the host with the device.
  *   - Arguments are validated on the host first; a call that returns an error
  *     has enqueued nothing (CSA2_ERR_HIP excepted: a launch failed part-way).
- *   - No global mutable state; calls are thread-safe.  Calls that share a
- *     workspace must be ordered on one stream.
+ *   - No global mutable state other than csa2_topk_noalloc's scratch; calls
+ *     are thread-safe.  Calls that share a workspace (or that scratch) must
+ *     be ordered on one stream.
  *
  * Data formats (OCP Microscaling Formats v1.0, which the report names as
  * "OCP-standard MXFP4", section 2.4.4):
@@ -77,6 +79,7 @@ typedef int32_t csa2_status;
 #define CSA2_ERR_UNSUPPORTED 2   /* a size this build does not implement (see each call) */
 #define CSA2_ERR_WORKSPACE 3     /* workspace missing, misaligned or too small */
 #define CSA2_ERR_HIP 4           /* a HIP launch failed; csa2_last_hip_error() has the code */
+#define CSA2_ERR_SCRATCH 5       /* larger than the static scratch of an allocation-free call */
 
 #define CSA2_Q_FP4 0
 #define CSA2_Q_FP8 1
@@ -270,6 +273,24 @@ CSA2_API csa2_status csa2_kv_append(int64_t n, const float* x, const float* rope
 CSA2_API csa2_status csa2_topk(const csa2_batch* batch, const float* scores, int64_t score_stride,
                                const int32_t* cand, int32_t cand_stride, const int32_t* cand_count, int32_t K,
                                const uint32_t* hist, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- Top-K without allocation ----------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): csa2_topk with the same arguments and results, its workspace
+ * taken from a static scratch array in the library's device code instead of
+ * `ws`.  The array holds the workspace of at most 256 query rows (about
+ * 20 MiB, held on every GPU the library runs on until the process ends);
+ * a batch with more rows returns CSA2_ERR_SCRATCH and enqueues nothing.
+ * The call allocates nothing; its first call on a device looks up the
+ * array's device address (hipGetSymbolAddress) on the stream's device.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or different host threads) race and must be
+ * ordered by the caller.  The array keeps the last call's contents; the call
+ * clears what must start at zero itself. */
+CSA2_API csa2_status csa2_topk_noalloc(const csa2_batch* batch, const float* scores, int64_t score_stride,
+                                       const int32_t* cand, int32_t cand_stride, const int32_t* cand_count, int32_t K,
+                                       const uint32_t* hist, int32_t* idx, hipStream_t stream);
 
 /* ---- block pool ----------------------------------------------------------
  * Hierarchical Sparse Indexer candidate pool (report 2.3.2; the reading note

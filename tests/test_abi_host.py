@@ -37,8 +37,8 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     L = C.lib()
     assert L.csa2_version() >= 1
-    for s in range(5):
-        assert L.csa2_status_string(s)
+    for s in range(6):
+        assert L.csa2_status_string(s) != b"unknown status"
     assert L.csa2_status_string(99) == b"unknown status"
 
 
@@ -249,3 +249,24 @@ def test_rope_cast_validation():
     assert rc(n=0, x=None) == C.CSA2_OK
     assert rc(cs=None) == C.CSA2_ERR_INVALID_ARG
     assert rc(out=FAKE + 2) == C.CSA2_ERR_INVALID_ARG
+
+
+def test_topk_noalloc_validation():
+    """The allocation-free Top-K validates like csa2_topk and refuses a batch
+    whose workspace exceeds its static scratch (more than 256 query rows)
+    before any device work."""
+    L = C.lib()
+
+    def call(b, scores=FAKE, stride=1000, K=512, idx=FAKE, cand=None, cstride=0, cnt=None):
+        return L.csa2_topk_noalloc(ctypes.byref(b.c), scores, stride, cand, cstride, cnt, K, None, idx, None)
+
+    b = HostBatch([1000, 500], [[999], [499]])
+    assert call(b, scores=None) == C.CSA2_ERR_INVALID_ARG
+    assert call(b, idx=None) == C.CSA2_ERR_INVALID_ARG
+    assert call(b, K=0) == C.CSA2_ERR_INVALID_ARG
+    assert call(b, K=4096) == C.CSA2_ERR_UNSUPPORTED
+    assert call(b, stride=999) == C.CSA2_ERR_INVALID_ARG
+    assert call(b, cand=FAKE, cstride=64, cnt=None) == C.CSA2_ERR_INVALID_ARG
+    big = HostBatch([100000] * 257, [[99999]] * 257)
+    assert call(big, stride=100000) == C.CSA2_ERR_SCRATCH
+    assert L.csa2_status_string(C.CSA2_ERR_SCRATCH).startswith(b"the problem exceeds")
