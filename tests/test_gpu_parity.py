@@ -224,14 +224,26 @@ def test_gather_dequant_bitwise(kv_fmt):
 
 
 ATTN_CASES = ["decode", "short_ctx", "ragged_t4", "swa_only", "replay", "sparse_idx", "swa_only_h64", "replay_h64",
-              "decode_e4m3kv", "small_e4m3kv", "decode_swa8", "small_swa8", "replay_swa8"]
+              "decode_e4m3kv", "small_e4m3kv", "decode_swa8", "small_swa8", "replay_swa8",
+              # at least 512 (row, 64-head) workgroups: one workgroup per row and 64 heads
+              "rows_h64", "rows_h64_e4m3kv_swa8", "rows_h128_replay", "rows_h64_holes", "rows_h64_swa_only"]
 
 
 @pytest.mark.parametrize("case", ATTN_CASES)
 def test_sparse_attn_tolerance(case):
     rng = np.random.default_rng(3)
     replay = None
-    if case == "decode":
+    if case in ("rows_h64", "rows_h64_holes"):  # 8 sequences x 65 rows, 300 entries each
+        wl = synth.make_workload(case, 21, [300] * 8, 65, [(20, synth.MODE_FULL, False)], Hm=64)
+    elif case == "rows_h64_e4m3kv_swa8":
+        wl = synth.make_workload(case, 22, [300, 2000, 140, 700], 130, [(20, synth.MODE_FULL, False)], Hm=64,
+                                 kv_fmt=1, swa_fmt=1)
+    elif case == "rows_h128_replay":  # two 64-head groups per row; windows cut at the replay start
+        wl = synth.make_workload(case, 23, [1500, 400], 130, [(20, synth.MODE_FULL, False)], Hm=128)
+        replay = np.array([1400, 0], np.int32)
+    elif case == "rows_h64_swa_only":
+        wl = synth.make_workload(case, 24, [200] * 4, 130, [(0, synth.MODE_SWA_ONLY, False)], Hm=64)
+    elif case == "decode":
         wl = synth.config("decode_c1", n_seq=3, n=6000, Hm=64)
     elif case == "decode_e4m3kv":  # the report's main-KV scales (E4M3 per 16 channels), big grid
         wl = synth.config("decode_c1", n_seq=3, n=6000, Hm=64, kv_fmt=1)
@@ -261,13 +273,16 @@ def test_sparse_attn_tolerance(case):
     nq = wl.total_q
     vis = oracle.row_visible(wl)
     idx = np.full((nq, 512), -1, np.int32)
-    if not case.startswith("swa_only"):
+    if "swa_only" not in case:
         for r in range(nq):
             v = int(vis[r])
             m = min(v, 512)
             idx[r, :m] = np.sort(rng.choice(v, m, replace=False)) if v > 0 else []
     if case == "sparse_idx":
         idx[0, 10:300:3] = -1  # holes inside the list
+    if case == "rows_h64_holes":  # holes inside the lists, some rows with no selected entry
+        idx[::3, 5:250:2] = -1
+        idx[1::7, :] = -1
     L, dL = wl.layers[0], dw.layers[0]
     sw = C.SwaLayout.from_workload(wl, replay_s=replay)
     assert sw.c.fmt == wl.swa_fmt
@@ -295,6 +310,8 @@ CHAIN_CASES = {
     "c4_small_mx_idx": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16,
                                             q_fmt=synth.Q_MXFP4),
     "c3_small": lambda: synth.config("prefill_c3", tokens=4000, T=96, Hm=16),
+    # 520 prefill rows of 64 heads: attention with one workgroup per row and 64 heads
+    "c3_rows_h64": lambda: synth.config("prefill_c3", tokens=4000, T=520, Hm=64),
     # degenerate rows: a sequence with no entries (its row attends to its
     # window alone), one with entries but no query row, and one with a
     # single entry; Full with pool, Reindex and Reuse
