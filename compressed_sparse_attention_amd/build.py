@@ -15,16 +15,18 @@ FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
-    "-shared",
     "-fPIC",
     "-fvisibility=hidden",
     "-DCSA2_BUILDING_LIBRARY",
     "-I" + os.path.join(ROOT, "include"),
     # packed FP32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in VGPRs: the epilogues read them without v_accvgpr_read copies
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# MFMA results in VGPRs: the epilogues read them without v_accvgpr_read copies.
+# Not for the many-row attention, whose 128 accumulator registers per lane
+# live in AGPRs (one wave per SIMD, 512 registers).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_SOURCES = set()
 
 
 def up_to_date():
@@ -34,18 +36,45 @@ def up_to_date():
     return all(os.path.getmtime(f) <= t for f in SOURCES + HEADERS + [__file__])
 
 
-def build(force=True, verbose=False):
-    if not force and up_to_date():
-        return SO
-    tmp = SO + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"
     msgs = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l and l.strip()]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs), file=sys.stderr)
+    return r.returncode, msgs
+
+
+def build(force=True, verbose=False):
+    """Compile every .hip source to an object (in parallel), then link them
+    into libcsa2.so."""
+    if not force and up_to_date():
+        return SO
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+
+    def compile_one(src):
+        name = os.path.basename(src)
+        obj = os.path.join(objdir, name + ".o")
+        extra = [] if name in AGPR_SOURCES else VGPR_FORM
+        rc, msgs = _run([HIPCC, *FLAGS, *extra, "-c", src, "-o", obj])
+        return src, obj, rc, msgs
+
+    workers = max(1, min(len(SOURCES), os.cpu_count() or 4, 8))
+    with ThreadPoolExecutor(workers) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    all_msgs = []
+    for src, _, rc, msgs in results:
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n" + "\n".join(msgs))
+        all_msgs += msgs
+    tmp = SO + ".tmp"
+    rc, msgs = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o, _, _ in results], "-o", tmp])
+    if rc != 0:
+        raise RuntimeError("link failed:\n" + "\n".join(msgs))
+    all_msgs += msgs
+    if verbose and all_msgs:
+        print("\n".join(all_msgs), file=sys.stderr)
     os.replace(tmp, SO)
     return SO
 

@@ -1,0 +1,89 @@
+// Device helpers shared by the attention kernels (k_attn.hip,
+// k_attn_rows.hip): main-KV and SWA dequantisation to bf16, lane-pair
+// reductions, and the LDS key-block geometry.
+//
+// E2M1 x E8M0 main-KV values are exact in bf16 (at most two significant
+// bits times a power of two); with an E4M3 scale per 16 channels at most six
+// significant bits, still exact.  gfx950's v_cvt_scalef32_pk_bf16_fp4 converts
+// two E2M1 nibbles (low nibble -> low half) and multiplies by the exponent of
+// its f32 scale operand.
+#pragma once
+
+#include "csa2_internal.h"
+
+namespace csa2 {
+namespace attn {
+
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
+
+// 8 E2M1 values (one dword) times `scale` -> 8 bf16 (as 4 dwords).
+__device__ __forceinline__ v4i fp4x8_to_bf16(uint32_t codes, float scale) {
+    auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    return v4i{__builtin_bit_cast(int, a), __builtin_bit_cast(int, b), __builtin_bit_cast(int, c),
+               __builtin_bit_cast(int, d)};
+}
+
+// The same for a scale that need not be a power of two: the conversions'
+// scale operand applies only its exponent, so the values are converted to f32
+// at unit scale, multiplied by the scale (exact: at most six significant bits)
+// and cut to bf16 (exact for the same reason).
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ int bf16_pair_mul(v2f_t f, float scale) {
+    const uint32_t a = __float_as_uint(f[0] * scale), b = __float_as_uint(f[1] * scale);
+    return (int)((a >> 16) | (b & 0xFFFF0000u));
+}
+__device__ __forceinline__ v4i fp4x8_to_bf16_mul(uint32_t codes, float scale) {
+    return v4i{bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0), scale),
+               bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1), scale),
+               bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2), scale),
+               bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3), scale)};
+}
+
+__device__ __forceinline__ float e8m0_f32(uint32_t e) { return __builtin_ldexpf(1.0f, (int)e - 127); }
+
+// OCP E4M3 ("FN": bias 7, no infinities; the NaN codes are not allowed in a
+// scale) -> f32, exactly: normal codes by their bits, subnormals m * 2^-9.
+__device__ __forceinline__ float e4m3_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (b & 0x80u) ? -v : v;
+}
+
+// Main-KV scale formats: kKvMx one E8M0 per 32 channels (16 bytes a row),
+// kKvE4 one E4M3 per 16 channels (32 bytes a row; the report's section 2.4.4).
+enum : int { kKvMx = 0, kKvE4 = 1 };
+// SWA row formats: bf16 [rows][512], or OCP MXFP8 [rows][528] (512 E4M3 codes,
+// then 16 E8M0 scales, one per 32 channels)
+enum : int { kSwaBf16 = 0, kSwaMx8 = 1 };
+
+// Reductions over lane pairs l, l ^ D (D = 16 or 32) on the VALU: the swap
+// leaves this lane's value and its partner's in the two results (in some order).
+template <int D>
+__device__ __forceinline__ v2u lane_pair(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if constexpr (D == 16) return __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    else return __builtin_amdgcn_permlane32_swap(u, u, false, false);
+}
+template <int D>
+__device__ __forceinline__ float xor_max(float x) {
+    const v2u r = lane_pair<D>(x);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <int D>
+__device__ __forceinline__ float xor_sum(float x) {
+    const v2u r = lane_pair<D>(x);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+constexpr int KB = 64;               // keys per block
+constexpr int LROW = 512 + 8;        // LDS row stride of a staged key in bf16 (16 B of padding)
+
+}  // namespace attn
+}  // namespace csa2

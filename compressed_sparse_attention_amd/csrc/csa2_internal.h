@@ -337,6 +337,13 @@ struct AttnLaunch {
 int attn_splits(const Geometry& g, int Hm, int K, int W);
 size_t attn_ws_bytes(const Geometry& g, int Hm, int S);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
+// Many rows: one workgroup per (row, 64 heads) when the grid has at least
+// kAttnRowsMinWgs of them, two per CU (launch_sparse_attn dispatches to it)
+constexpr int kAttnRowsMinWgs = 512;
+inline bool attn_rows_ok(const Geometry& g, int Hm) {
+    return Hm % 64 == 0 && (int64_t)g.total_q * (Hm / 64) >= kAttnRowsMinWgs;
+}
+hipError_t launch_sparse_attn_rows(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_rope_cast(int64_t n_rows, int heads, const float* in, const float* cs, int inverse, uint16_t* out,
                             hipStream_t s);
 hipError_t launch_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst, int64_t rows,

@@ -11,81 +11,13 @@
 // Course notes "3. 通用基础设施", section 3.2.2: query i sees SWA keys
 // [max(s, i-W+1), i].
 //
-// E2M1 x E8M0 values have at most two significant bits, so the dequantised
-// bf16 latents are exact.  gfx950's v_cvt_scalef32_pk_bf16_fp4 converts two
-// E2M1 nibbles (low nibble -> low half) and multiplies by the block scale.
-#include "csa2_internal.h"
+// The dequantised bf16 latents are exact (attn_common.h).
+#include "attn_common.h"
 
 namespace csa2 {
 namespace {
 
-typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
-typedef short v8s __attribute__((ext_vector_type(8)));
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
-
-// 8 E2M1 values (one dword) times `scale` -> 8 bf16 (as 4 dwords).
-__device__ __forceinline__ v4i fp4x8_to_bf16(uint32_t codes, float scale) {
-    auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
-    auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
-    auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
-    auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
-    return v4i{__builtin_bit_cast(int, a), __builtin_bit_cast(int, b), __builtin_bit_cast(int, c),
-               __builtin_bit_cast(int, d)};
-}
-
-// The same for a scale that need not be a power of two: the conversions'
-// scale operand applies only its exponent, so the values are converted to f32
-// at unit scale, multiplied by the scale (exact: at most six significant bits)
-// and cut to bf16 (exact for the same reason).
-typedef float v2f_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ int bf16_pair_mul(v2f_t f, float scale) {
-    const uint32_t a = __float_as_uint(f[0] * scale), b = __float_as_uint(f[1] * scale);
-    return (int)((a >> 16) | (b & 0xFFFF0000u));
-}
-__device__ __forceinline__ v4i fp4x8_to_bf16_mul(uint32_t codes, float scale) {
-    return v4i{bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0), scale),
-               bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1), scale),
-               bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2), scale),
-               bf16_pair_mul(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3), scale)};
-}
-
-__device__ __forceinline__ float e8m0_f32(uint32_t e) { return __builtin_ldexpf(1.0f, (int)e - 127); }
-
-// OCP E4M3 ("FN": bias 7, no infinities; the NaN codes are not allowed in a
-// scale) -> f32, exactly: normal codes by their bits, subnormals m * 2^-9.
-__device__ __forceinline__ float e4m3_f32(uint32_t b) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-    return (b & 0x80u) ? -v : v;
-}
-
-// Main-KV scale formats: kKvMx one E8M0 per 32 channels (16 bytes a row),
-// kKvE4 one E4M3 per 16 channels (32 bytes a row; the report's section 2.4.4).
-enum : int { kKvMx = 0, kKvE4 = 1 };
-// SWA row formats: bf16 [rows][512], or OCP MXFP8 [rows][528] (512 E4M3 codes,
-// then 16 E8M0 scales, one per 32 channels)
-enum : int { kSwaBf16 = 0, kSwaMx8 = 1 };
-
-// Reductions over lane pairs l, l ^ D (D = 16 or 32) on the VALU: the swap
-// leaves this lane's value and its partner's in the two results (in some order).
-template <int D>
-__device__ __forceinline__ v2u lane_pair(float x) {
-    const uint32_t u = __float_as_uint(x);
-    if constexpr (D == 16) return __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    else return __builtin_amdgcn_permlane32_swap(u, u, false, false);
-}
-template <int D>
-__device__ __forceinline__ float xor_max(float x) {
-    const v2u r = lane_pair<D>(x);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-template <int D>
-__device__ __forceinline__ float xor_sum(float x) {
-    const v2u r = lane_pair<D>(x);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
+using namespace attn;
 
 // ---------------------------------------------------------------------------
 // gather + dequantise: grid (K, total_q), 64 threads, 8 channels per thread
@@ -127,8 +59,6 @@ __global__ __launch_bounds__(64) void k_gather_dequant(const uint8_t* __restrict
 // beats two pipes in one workgroup except on the smallest grids.
 // ---------------------------------------------------------------------------
 constexpr int HG = 16;
-constexpr int KB = 64;
-constexpr int LROW = 512 + 8;  // LDS row stride of the staged keys in bf16 (16 B of padding)
 constexpr int SLROW = KB + 4;  // LDS row stride of the logits in floats
 
 template <int NPIPE, int KVF, int SWF>
@@ -524,288 +454,6 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
             l_lse > 0.0f ? (m_run + log2f(l_lse)) * 0.69314718055994531f : -INFINITY;
 }
 
-// ---------------------------------------------------------------------------
-// sparse attention for many rows: one workgroup per (query row, 64 heads), so
-// a row's key blocks are dequantised once for all of its heads.  4 waves; wave
-// w owns heads 16w .. 16w+15 of the group for the whole row, so the softmax
-// needs no exchange between waves.  Per block of 64 keys (the SWA rows first,
-// then the selected entries):
-//   stage  the block into LDS as bf16 rows (each thread one key, 128 channels);
-//   S^T    = K Q^T on v_mfma_f32_16x16x32_bf16, four 16-key tiles: A = key rows
-//          from LDS, B = the wave's 16 query rows held in registers.  Lane l
-//          receives head l%16 and keys 16t + 4(l/16) + i of tile t, i.e. every
-//          head's scores sit in the four lanes l%16 + 16g;
-//   softmax online per head in fp32 (base 2); the weights of keys
-//          32s + 16(e/4) + 4g + e%4, e = 0..7, form the A operand of P V step
-//          s in the lane that computed them, as a bf16 pair (hi + lo);
-//   P V    on the same MFMA: B = V read transposed from LDS
-//          (ds_read_b64_tr_b16) in the same key order, O = 16 heads x 512
-//          channels in registers.
-// Two workgroups share a CU (75 KB of LDS each), so one stages while the
-// other computes.
-// ---------------------------------------------------------------------------
-template <int KVF, int SWF>
-__global__ __launch_bounds__(256, 2) void k_sparse_attn_rows(
-    const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
-    const int32_t* __restrict__ idx, int K, const void* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
-    const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ replay_s, int W,
-    const int64_t* __restrict__ entry_off, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ q_pos,
-    float scale_log2, float* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg) {
-    __shared__ __attribute__((aligned(16))) uint16_t kl[KB * LROW];
-    __shared__ __attribute__((aligned(16))) int kvalid[KB];  // read as int4
-    __shared__ int32_t kidx[kMaxK];
-    __shared__ int nsel_sh;
-
-    const int row = blockIdx.x / n_hg, hg = blockIdx.x % n_hg;
-    if (row >= total_q) return;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lg = lane >> 4, li = lane & 15;
-
-    // ---- prologue: the index row, then the wave's query rows
-    const int32_t* irow = idx + (int64_t)row * K;
-    int32_t ir[kMaxK / 256];
-#pragma unroll
-    for (int i = 0; i < kMaxK / 256; ++i) {
-        const int s = tid + 256 * i;
-        ir[i] = s < K ? irow[s] : -1;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const int h0 = 64 * hg + 16 * wave;  // the wave's first head
-    v8bf Q[16];
-    {
-        const uint16_t* qr = q + ((int64_t)row * Hm + h0 + li) * 512 + 8 * lg;
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, ld16(qr + 32 * ks));
-    }
-    asm volatile("" ::: "memory");
-
-    const int b = row_seq[row];
-    const int64_t t = q_pos[row];
-    const int64_t e0 = entry_off[b];
-    const int64_t n_ent = entry_off[b + 1] - e0;
-    const int64_t s_rep = replay_s ? (int64_t)replay_s[b] : 0;
-    int64_t u_lo = t - W + 1;
-    u_lo = u_lo > s_rep ? u_lo : s_rep;
-    const int n_swa = t >= u_lo ? (int)(t - u_lo + 1) : 0;
-    const int64_t swa_r0 = swa_row_off[b] + (u_lo - swa_pos0[b]);
-
-    if (tid == 0) nsel_sh = 0;
-    __syncthreads();
-    {
-        int last = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxK / 256; ++i) {
-            const int s = tid + 256 * i;
-            if (s < K) {
-                const int32_t j = (ir[i] >= 0 && ir[i] < n_ent) ? ir[i] : -1;  // out-of-range entries read as empty
-                kidx[s] = j;
-                if (j >= 0) last = s + 1;
-            }
-        }
-        if (last) atomicMax(&nsel_sh, last);
-    }
-    __syncthreads();
-    const int n_keys = n_swa + nsel_sh;
-    const int n_blk = (n_keys + KB - 1) / KB;
-
-    // this thread stages key `skey` of a block, channels 128 part .. +128;
-    // 16 consecutive lanes take 16 keys of one part (distinct LDS banks)
-    constexpr int CP = 128;
-    constexpr int NB = CP / 32;
-    const int skey = (tid & 15) + 16 * (tid >> 6), part = (tid >> 4) & 3;
-    uint16_t* const kdst = kl + skey * LROW + CP * part;
-    auto stage = [&](int blk) {
-        const int vk = KB * blk + skey;
-        int valid = 0;
-        if (vk < n_swa) {
-            valid = 1;
-            if constexpr (SWF == kSwaMx8) {
-                const uint8_t* rb = reinterpret_cast<const uint8_t*>(swa) + (swa_r0 + vk) * 528;
-                v4i sw[CP / 16];
-#pragma unroll
-                for (int i = 0; i < CP / 16; ++i) sw[i] = ld16(rb + CP * part + 16 * i);
-                const uint32_t swsc = *reinterpret_cast<const uint32_t*>(rb + 512 + 4 * part);
-#pragma unroll
-                for (int i = 0; i < NB; ++i) {
-                    const float sc = e8m0_f32((swsc >> (8 * i)) & 255u);
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        const uint32_t w0 = (uint32_t)sw[2 * i + d / 2][2 * (d % 2)];
-                        const uint32_t w1 = (uint32_t)sw[2 * i + d / 2][2 * (d % 2) + 1];
-                        auto a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
-                        auto a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
-                        auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
-                        auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
-                        *reinterpret_cast<v8bf*>(kdst + 32 * i + 8 * d) =
-                            v8bf{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
-                    }
-                }
-            } else {
-                const uint16_t* src = reinterpret_cast<const uint16_t*>(swa) + (swa_r0 + vk) * 512 + CP * part;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {  // two halves of 8 loads (register budget)
-                    v4i sw[CP / 16];
-#pragma unroll
-                    for (int i = 0; i < CP / 16; ++i) sw[i] = ld16(src + 64 * h + 8 * i);
-#pragma unroll
-                    for (int i = 0; i < CP / 16; ++i) *reinterpret_cast<v4i*>(kdst + 64 * h + 8 * i) = sw[i];
-                }
-            }
-        } else if (vk < n_keys) {
-            const int32_t j = kidx[vk - n_swa];
-            if (j >= 0) {
-                valid = 1;
-                const int64_t e = e0 + j;
-                const uint8_t* src = kv + e * 256 + (CP / 2) * part;
-                v4i pc[NB];
-#pragma unroll
-                for (int i = 0; i < NB; ++i) pc[i] = ld16(src + 16 * i);
-                if constexpr (KVF == kKvE4) {
-                    const uint2 w2 = *reinterpret_cast<const uint2*>(kv_sc + e * 32 + 8 * part);
-#pragma unroll
-                    for (int i = 0; i < NB; ++i) {
-                        const uint32_t w = i < 2 ? w2.x : w2.y;
-                        const float s0 = e4m3_f32((w >> (16 * (i & 1))) & 255u);
-                        const float s1 = e4m3_f32((w >> (16 * (i & 1) + 8)) & 255u);
-#pragma unroll
-                        for (int d = 0; d < 4; ++d)
-                            *reinterpret_cast<v4i*>(kdst + 32 * i + 8 * d) =
-                                fp4x8_to_bf16_mul((uint32_t)pc[i][d], d < 2 ? s0 : s1);
-                    }
-                } else {
-                    const uint32_t psc = *reinterpret_cast<const uint32_t*>(kv_sc + e * 16 + 4 * part);
-#pragma unroll
-                    for (int i = 0; i < NB; ++i) {
-                        const float sc = e8m0_f32((psc >> (8 * i)) & 255u);
-#pragma unroll
-                        for (int d = 0; d < 4; ++d)
-                            *reinterpret_cast<v4i*>(kdst + 32 * i + 8 * d) = fp4x8_to_bf16((uint32_t)pc[i][d], sc);
-                    }
-                }
-            }
-        }
-        if (!valid) {
-#pragma unroll
-            for (int i = 0; i < CP / 8; ++i) *reinterpret_cast<v4i*>(kdst + 8 * i) = v4i{0, 0, 0, 0};
-        }
-        if (part == 0) kvalid[skey] = valid;
-    };
-
-    v4f O[32];
-#pragma unroll
-    for (int nt = 0; nt < 32; ++nt) O[nt] = v4f{0.f, 0.f, 0.f, 0.f};
-    // running max and sums of head h0 + li (the same in the four lanes of a head):
-    // l_run sums the bf16 weight pairs P V uses, l_lse the fp32 weights
-    float m_run = -INFINITY, l_run = 0.0f, l_lse = 0.0f;
-
-    for (int blk = 0; blk < n_blk; ++blk) {
-        if (blk > 0) __syncthreads();  // every wave is done with the previous block
-        stage(blk);
-        __syncthreads();
-
-        // S^T = K Q^T: four independent accumulation chains (key tiles)
-        v4f S[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const v8bf Ak = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kl + (16 * tt + li) * LROW + 32 * ks + 8 * lg));
-                S[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ak, Q[ks], S[tt], 0, 0, 0);
-            }
-        }
-        // scaled logits; keys that are not there score -inf
-        float p[16];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int4 ok = *reinterpret_cast<const int4*>(kvalid + 16 * tt + 4 * lg);
-            const int okv[4] = {ok.x, ok.y, ok.z, ok.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[4 * tt + i] = okv[i] ? S[tt][i] * scale_log2 : -INFINITY;
-                mx = fmaxf(mx, p[4 * tt + i]);
-            }
-        }
-        mx = xor_max<16>(mx);
-        mx = xor_max<32>(mx);
-        const float m_new = fmaxf(m_run, mx);
-        float alpha;
-        if (m_new == -INFINITY) {  // nothing valid yet
-            alpha = 1.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) p[i] = 0.0f;
-        } else {
-            // arguments are <= 0 (or -inf): the hardware exp2
-            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(p[i] - m_new);
-        }
-        // P V operands: step s2 takes tiles 2 s2 and 2 s2 + 1, element e = key
-        // 32 s2 + 16 (e / 4) + 4 lg + e % 4; each weight as a bf16 pair (hi + lo)
-        v8bf P[2], Plo[2];
-        float rs = 0.0f, rs32 = 0.0f;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pv = p[4 * (2 * s2 + e / 4) + e % 4];
-                const __bf16 pb = (__bf16)pv;
-                const __bf16 pl = (__bf16)(pv - (float)pb);
-                P[s2][e] = pb;
-                Plo[s2][e] = pl;
-                rs += (float)pb + (float)pl;
-                rs32 += pv;
-            }
-        rs = xor_sum<16>(rs);
-        rs = xor_sum<32>(rs);
-        rs32 = xor_sum<16>(rs32);
-        rs32 = xor_sum<32>(rs32);
-        l_run = l_run * alpha + rs;
-        l_lse = l_lse * alpha + rs32;
-        m_run = m_new;
-        // O rows are heads 4 lg + v: their alpha lives in lane 4 lg + v; the
-        // rescale is skipped when no head's maximum moved
-        if (__any(alpha != 1.0f)) {
-            float av[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * lg + v);
-#pragma unroll
-            for (int nt = 0; nt < 32; ++nt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) O[nt][v] *= av[v];
-        }
-        // O += P V for channels 16 nt + li
-#pragma unroll
-        for (int nt = 0; nt < 32; ++nt) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const uint16_t* a0 = kl + (32 * s2 + 4 * lg + (li >> 2)) * LROW + 16 * nt + 4 * (li & 3);
-                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(a0));
-                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(a0 + 16 * LROW));
-                const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                const v8bf vb = __builtin_bit_cast(v8bf, both);
-                O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P[s2], vb, O[nt], 0, 0, 0);
-                O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Plo[s2], vb, O[nt], 0, 0, 0);
-            }
-        }
-    }
-
-    // finalise: O / l for heads 4 lg + v
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    float iv[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) iv[v] = __shfl(inv, 4 * lg + v);
-#pragma unroll
-    for (int nt = 0; nt < 32; ++nt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            out[((int64_t)row * Hm + h0 + 4 * lg + v) * 512 + 16 * nt + li] = O[nt][v] * iv[v];
-    if (lse && lg == 0)
-        lse[(int64_t)row * Hm + h0 + li] = l_lse > 0.0f ? (m_run + log2f(l_lse)) * 0.69314718055994531f : -INFINITY;
-}
-
 // Merge the S partial results of each (row, head): with M = max_s m_s and
 // a_s = 2^(m_s - M), O = sum_s a_s O_s / sum_s a_s l_s.  One workgroup of 128
 // threads per (row, head); thread t owns channels 4t .. 4t+3, so every load of
@@ -864,6 +512,7 @@ hipError_t launch_gather_dequant(const csa2_batch* b, Geometry g, int kv_fmt, co
 }
 
 int attn_splits(const Geometry& g, int Hm, int K, int W) {
+    if (attn_rows_ok(g, Hm)) return 1;
     // split the key blocks of a (row, head group) over several workgroups when
     // the grid would otherwise leave CUs idle
     const int units = g.total_q * (Hm / HG);
@@ -877,28 +526,9 @@ size_t attn_ws_bytes(const Geometry& g, int Hm, int S) {
     return S <= 1 ? 0 : (size_t)g.total_q * (Hm / HG) * S * (HG * 516) * sizeof(float);
 }
 
-// grids of at least this many (row, 64-head) workgroups run one workgroup per
-// row and 64 heads (two per CU fill the chip); smaller grids run the split
-// kernel above
-constexpr int kAttnRowsMinWgs = 512;
-
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
     const bool swa8 = a.sw->fmt == CSA2_SWA_MXFP8;
-    if (a.Hm % 64 == 0 && (int64_t)a.g.total_q * (a.Hm / 64) >= kAttnRowsMinWgs) {
-        const int n_hg64 = a.Hm / 64;
-        const dim3 grid((unsigned)(a.g.total_q * n_hg64));
-#define CSA2_ROWS(KF, SF)                                                                                          \
-    hipLaunchKernelGGL((k_sparse_attn_rows<KF, SF>), grid, dim3(256), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K,    \
-                       a.swa, a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,     \
-                       a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q, n_hg64)
-        if (a.kv_fmt == kKvE4) {
-            if (swa8) CSA2_ROWS(kKvE4, kSwaMx8); else CSA2_ROWS(kKvE4, kSwaBf16);
-        } else {
-            if (swa8) CSA2_ROWS(kKvMx, kSwaMx8); else CSA2_ROWS(kKvMx, kSwaBf16);
-        }
-#undef CSA2_ROWS
-        return hipGetLastError();
-    }
+    if (attn_rows_ok(a.g, a.Hm)) return launch_sparse_attn_rows(a, s);
     const int n_hg = a.Hm / HG;
     int S = attn_splits(a.g, a.Hm, a.K, a.sw->window);
     while (S > 1 && attn_ws_bytes(a.g, a.Hm, S) > a.ws_bytes) --S;  // use what the workspace allows
