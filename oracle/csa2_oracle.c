@@ -418,8 +418,9 @@ static double kv_value(const uint8_t* kv, const uint8_t* kv_sc, int kv_fmt, int6
 }
 
 /* out[r][s][c] as bf16 bits; rows for idx == -1 are zero.  The value has at
- * most two significant bits, so it is exact in bf16: the bits are those of
- * the binary32 value with the low half dropped (which is zero). */
+ * most two significant bits with an E8M0 scale and at most six with an E4M3
+ * scale, so it is exact in bf16 either way: the bits are those of the
+ * binary32 value with the low half dropped (which is zero). */
 void orc_gather_dequant(int64_t total_q, const int32_t* row_seq, const int64_t* entry_off, const uint8_t* kv,
                         const uint8_t* kv_sc, int kv_fmt, const int32_t* idx, int K, uint16_t* out) {
     for (int64_t r = 0; r < total_q; ++r)

@@ -36,7 +36,9 @@ from typing import List, Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "libcsa2_synth.so")
+# CSA2_SYNTH_SO: a library built elsewhere from the same source (the
+# sanitizer run of the CPU tests loads an instrumented build through it)
+_SO = os.environ.get("CSA2_SYNTH_SO") or os.path.join(_HERE, "libcsa2_synth.so")
 _SRC = os.path.join(_HERE, "csa2_synth.c")
 
 MODE_SWA_ONLY, MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2, 3
@@ -51,6 +53,8 @@ def _tid(layer: int, what: int) -> int:
 
 def build(force: bool = False) -> str:
     """Compile the generator with gcc (host code only)."""
+    if os.environ.get("CSA2_SYNTH_SO"):
+        return _SO
     if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-pthread", "-shared", "-fPIC", _SRC, "-o", _SO, "-lm"])
     return _SO
