@@ -422,9 +422,70 @@ def bench_workloads(synth, C, torch, dev):
     res["decode_step_40_pages_fmt"] = bench_step_40(synth, torch, dev, **PAGES_FMT)
     for kv_fmt in (1, 0):
         res["kv_append_e4m3" if kv_fmt == 1 else "kv_append_mxfp4"] = bench_append(C, torch, dev, kv_fmt)
+    res["attn_rope"] = bench_attn_rope(synth, C, torch, dev)
     res["compress"] = bench_compress(C, torch, dev)
     res["index_k_project"] = bench_project(C, torch, dev)
     return res
+
+
+def bench_attn_rope(synth, C, torch, dev, reps=20):
+    """The RoPE steps around attention (the report's RoPE-attention-RoPE-cast
+    flow) fused into the attention call, against plain attention (bf16 query
+    in, f32 out) and against the three separate calls, at a decode shape (64
+    rows) and a replay shape (2,048 rows), 64 heads, Top-512 of 32,768
+    entries plus a 128-token window."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import SCALE, DevWorkload
+
+    out = {}
+    for name, n_seq, T in (("decode_64_rows", 64, 1), ("replay_2048_rows", 16, 128)):
+        wl = synth.make_workload("attn_rope", 77, [32768] * n_seq, T, [(20, synth.MODE_FULL, False)])
+        dw = DevWorkload(wl, dev)
+        nq, Hm = wl.total_q, wl.Hm
+        g = torch.Generator(device=dev).manual_seed(11)
+        idx = torch.sort(torch.randint(0, 32768 - T, (nq, 512), generator=g, device=dev), dim=1).values.to(torch.int32)
+        q32 = torch.randn((nq, Hm, 512), generator=g, device=dev, dtype=torch.float32)
+        th = torch.rand((nq, 32), generator=g, device=dev) * 6.2831853
+        cs = torch.stack([torch.cos(th), torch.sin(th)], -1).contiguous()
+        L = dw.layers[0]
+        ws = C.workspace(C.csa2_workspace_size(C.CSA2_WS_SPARSE_ATTN, dw.batch, 512), dev)
+        qb = C.csa2_rope_cast(q32, cs)
+        o32 = torch.empty((nq, Hm, 512), dtype=torch.float32, device=dev)
+        o16 = torch.empty((nq, Hm, 512), dtype=torch.uint16, device=dev)
+
+        def plain():
+            C.csa2_sparse_attn(dw.batch, qb, dw.kv, dw.kv_sc, idx, L["swa"], dw.swa, SCALE, out=o32, want_lse=False,
+                               ws=ws)
+
+        def three():
+            C.csa2_rope_cast(q32, cs, out=qb)
+            plain()
+            C.csa2_rope_cast(o32, cs, inverse=True, out=o16)
+
+        def fused():
+            C.csa2_sparse_attn_rope(dw.batch, q32, cs, dw.kv, dw.kv_sc, idx, L["swa"], dw.swa, SCALE, out=o16,
+                                    want_lse=False, ws=ws)
+
+        r = {}
+        for label, fn in (("plain_attention_us", plain), ("three_calls_us", three), ("fused_us", fused)):
+            fn()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            r[label] = round(s.elapsed_time(e) * 1000.0 / reps, 2)
+        log(f"[bench] attention with RoPE, {name}: plain {r['plain_attention_us']} us, three calls "
+            f"{r['three_calls_us']} us, fused {r['fused_us']} us")
+        r["rows"] = nq
+        out[name] = r
+        del dw, q32, qb, o32, o16, ws, idx
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_project(C, torch, dev, n=131072, reps=10):

@@ -25,7 +25,7 @@ CSA2_MODE_SWA_ONLY, CSA2_MODE_FULL, CSA2_MODE_REINDEX, CSA2_MODE_REUSE = 0, 1, 2
 CSA2_LAYER_BUILD_POOL = 1
 CSA2_WS_TOPK, CSA2_WS_BLOCK_POOL, CSA2_WS_SPARSE_ATTN, CSA2_WS_LAYER_CHAIN = 1, 2, 3, 4
 
-EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_topk_noalloc", "csa2_block_pool", "csa2_gather_dequant", "csa2_sparse_attn",
+EXPORTS = ("csa2_index_score", "csa2_topk", "csa2_topk_noalloc", "csa2_block_pool", "csa2_sparse_attn_rope", "csa2_gather_dequant", "csa2_sparse_attn",
            "csa2_layer_chain", "csa2_rope_cast", "csa2_index_k_project", "csa2_compress", "csa2_kv_append", "csa2_workspace_size", "csa2_status_string", "csa2_last_hip_error",
            "csa2_version")
 
@@ -86,6 +86,8 @@ def lib():
         L.csa2_compress.argtypes = [ctypes.c_int64, i32, _vp, _vp, _vp, _vp]
         L.csa2_kv_append.argtypes = [ctypes.c_int64, _vp, _vp, _vp, ctypes.c_int64, i32, _vp, _vp, _vp]
         L.csa2_sparse_attn.argtypes = [B, i32, _vp, i32, _vp, _vp, _vp, i32, _vp, S, f32, _vp, _vp, _vp, sz, _vp]
+        L.csa2_sparse_attn_rope.argtypes = [B, i32, _vp, _vp, i32, _vp, _vp, _vp, i32, _vp, S, f32, _vp, _vp, _vp, sz,
+                                            _vp]
         L.csa2_layer_chain.argtypes = [B, ctypes.POINTER(csa2_chain_params), i32, ctypes.POINTER(csa2_layer), S, _vp,
                                        _vp, _vp, _vp, sz, _vp]
         L.csa2_workspace_size.argtypes = [i32, B, i32, i32, i32]
@@ -95,7 +97,7 @@ def lib():
         L.csa2_last_hip_error.restype = i32
         L.csa2_version.restype = i32
         for name in ("csa2_index_score", "csa2_topk", "csa2_topk_noalloc", "csa2_block_pool", "csa2_gather_dequant",
-                     "csa2_sparse_attn", "csa2_layer_chain", "csa2_rope_cast", "csa2_index_k_project", "csa2_compress",
+                     "csa2_sparse_attn", "csa2_sparse_attn_rope", "csa2_layer_chain", "csa2_rope_cast", "csa2_index_k_project", "csa2_compress",
                      "csa2_kv_append"):
             getattr(L, name).restype = i32
         _lib_handle = L
@@ -308,6 +310,26 @@ def csa2_sparse_attn(batch, q_bf16, kv_fp4, kv_sc, idx, swa_rows, swa_layout, so
                                 idx.shape[1], _ptr(swa_rows), ctypes.byref(swa_layout.c), float(softmax_scale),
                                 _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check(st, "csa2_sparse_attn")
+    return out, lse
+
+
+def csa2_sparse_attn_rope(batch, q_f32, rope_cs, kv_fp4, kv_sc, idx, swa_rows, swa_layout, softmax_scale, out=None,
+                          lse=None, want_lse=True, ws=None, split=True, stream=None, kv_fmt=CSA2_KV_MXFP4):
+    """Sparse attention with the RoPE steps fused: f32 query before RoPE in,
+    bf16 output (u16 bits) with its rotated channels turned back."""
+    Hm = q_f32.shape[1]
+    dev = q_f32.device
+    if out is None:
+        out = torch.empty((batch.total_q, Hm, 512), dtype=torch.uint16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((batch.total_q, Hm), dtype=torch.float32, device=dev)
+    if ws is None and split:
+        ws = workspace(csa2_workspace_size(CSA2_WS_SPARSE_ATTN, batch, idx.shape[1]), dev)
+    st = lib().csa2_sparse_attn_rope(ctypes.byref(batch.c), Hm, _ptr(q_f32), _ptr(rope_cs), int(kv_fmt), _ptr(kv_fp4),
+                                     _ptr(kv_sc), _ptr(idx), idx.shape[1], _ptr(swa_rows), ctypes.byref(swa_layout.c),
+                                     float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "csa2_sparse_attn_rope")
     return out, lse
 
 

@@ -82,6 +82,50 @@ __device__ __forceinline__ float xor_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// 8 query channels c0 .. c0+7 (c0 a multiple of 8) of a head row as the bf16
+// MFMA operand: from bf16 directly, or (ROPE) from f32 before RoPE, the
+// channels from 448 on rotated by the row's angles, then cast to nearest even
+template <int ROPE>
+__device__ __forceinline__ v8bf load_q8(const void* q, int64_t off, int c0, const float* cs) {
+    if constexpr (ROPE) {
+        const float* p = reinterpret_cast<const float*>(q) + off;
+        const v4f x0 = *reinterpret_cast<const v4f*>(p), x1 = *reinterpret_cast<const v4f*>(p + 4);
+        float f[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        if (c0 >= 448) {
+            const float* c = cs + (c0 - 448);  // pairs p0 .. p0 + 3, two floats each
+            const v4f a = *reinterpret_cast<const v4f*>(c), b = *reinterpret_cast<const v4f*>(c + 4);
+            rope_pair(f[0], f[1], a[0], a[1], 1.0f);
+            rope_pair(f[2], f[3], a[2], a[3], 1.0f);
+            rope_pair(f[4], f[5], b[0], b[1], 1.0f);
+            rope_pair(f[6], f[7], b[2], b[3], 1.0f);
+        }
+        v4i w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = (int)(bf16_rne(f[2 * k]) | (bf16_rne(f[2 * k + 1]) << 16));
+        return __builtin_bit_cast(v8bf, w);
+    } else {
+        return __builtin_bit_cast(v8bf, ld16(reinterpret_cast<const uint16_t*>(q) + off));
+    }
+}
+
+// Final store of output channel c of a head row (value x, this lane's; the
+// partner channel c ^ 1 sits in lane l ^ 1).  ROPE: the channels from 448 on
+// are turned back (the angle negated) and every channel is cast to bf16; the
+// even lane of each pair stores both.  Every lane of the wave calls it.
+template <int ROPE>
+__device__ __forceinline__ void store_out(void* out, int64_t off, int c, float x, const float* cs) {
+    if constexpr (ROPE) {
+        const float y = __shfl_xor(x, 1);
+        if ((c & 1) == 0) {
+            float a = x, b = y;
+            if (c >= 448) rope_pair(a, b, cs[c - 448], cs[c - 447], -1.0f);
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + off) = bf16_rne(a) | (bf16_rne(b) << 16);
+        }
+    } else {
+        reinterpret_cast<float*>(out)[off] = x;
+    }
+}
+
 constexpr int KB = 64;               // keys per block
 constexpr int LROW = 512 + 8;        // LDS row stride of a staged key in bf16 (16 B of padding)
 

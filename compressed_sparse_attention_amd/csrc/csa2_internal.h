@@ -198,6 +198,20 @@ __device__ inline uint32_t threshold_bin2(Bins h, uint32_t k1, uint32_t k2, uint
     return found[0];
 }
 
+// binary32 -> bf16 to nearest even.  Finite values and infinities: adding
+// 0x7FFF plus the kept part's lowest bit carries exactly when the dropped 16
+// bits exceed half a unit, or equal it with an odd kept part; a carry out of
+// the largest finite value gives infinity.  A NaN stays a NaN: its sign and
+// leading payload bits are kept and the quiet bit is set (the addition alone
+// could carry a NaN into an infinity or the other sign).
+__host__ __device__ inline uint32_t bf16_rne(float f) {
+    uint32_t u;
+    __builtin_memcpy(&u, &f, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+
 // ---------------------------------------------------------------------------
 // Per-chunk candidate lists written by the decode scan in place of the full
 // score rows.  A chunk is a run of positions one scan workgroup covers.  For
@@ -332,7 +346,24 @@ struct AttnLaunch {
     void* ws;                   // partial results when the key blocks are split (may be NULL)
     size_t ws_bytes;
     int kv_fmt;                 // CSA2_KV_* of kv_sc
+    // fused RoPE and casts (csa2_sparse_attn_rope): the query comes as f32 before
+    // RoPE (q32) and is rotated and cast to bf16 on load; the output's rotated
+    // channels are turned back and every channel cast to bf16 on store (out16)
+    const float* rope_cs = nullptr;  // [total_q][32][2] cos, sin per pair
+    const float* q32 = nullptr;      // [total_q][Hm][512]
+    uint16_t* out16 = nullptr;       // [total_q][Hm][512]
 };
+
+// RoPE pairs (448 + 2p, 449 + 2p), p < 32, of a head row (the append's and
+// csa2_rope_cast's): (a, b) -> (a cos - b sin, a sin + b cos), each product
+// and the sum or difference rounded to fp32; `sg` = -1 negates the angle.
+__device__ __forceinline__ void rope_pair(float& a, float& b, float co, float si, float sg) {
+#pragma clang fp contract(off)
+    const float s = sg * si;  // exact negation
+    const float x = a, y = b;
+    a = x * co - y * s;
+    b = x * s + y * co;
+}
 // key-block splits the attention would use, and the workspace they need
 int attn_splits(const Geometry& g, int Hm, int K, int W);
 size_t attn_ws_bytes(const Geometry& g, int Hm, int S);

@@ -237,18 +237,6 @@ __global__ __launch_bounds__(256) void k_index_k_project(const float* __restrict
     }
 }
 
-// binary32 -> bf16 to nearest even.  Finite values and infinities: adding
-// 0x7FFF plus the kept part's lowest bit carries exactly when the dropped 16
-// bits exceed half a unit, or equal it with an odd kept part; a carry out of
-// the largest finite value gives infinity.  A NaN stays a NaN: its sign and
-// leading payload bits are kept and the quiet bit is set (the addition alone
-// could carry a NaN into an infinity or the other sign).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // RoPE and cast around attention (the report's kernel flow: a fused
 // "RoPE-attention-RoPE-cast" kernel rotates the query before attention and
 // turns the output's rotated part back after it, then casts).  The pairs and

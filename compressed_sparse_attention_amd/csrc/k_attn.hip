@@ -61,14 +61,14 @@ __global__ __launch_bounds__(64) void k_gather_dequant(const uint8_t* __restrict
 constexpr int HG = 16;
 constexpr int SLROW = KB + 4;  // LDS row stride of the logits in floats
 
-template <int NPIPE, int KVF, int SWF>
+template <int NPIPE, int KVF, int SWF, int ROPE>
 __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
-    const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
+    const void* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
     const int32_t* __restrict__ idx, int K, const void* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
     const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ replay_s, int W,
     const int64_t* __restrict__ entry_off, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ q_pos,
-    float scale_log2, float* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg, int S,
-    float* __restrict__ partial) {
+    float scale_log2, void* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg, int S,
+    float* __restrict__ partial, const float* __restrict__ rope_cs) {
     __shared__ __attribute__((aligned(16))) uint16_t kl[NPIPE][KB * LROW];
     __shared__ float sl[NPIPE][HG][SLROW];
     __shared__ int kvalid[NPIPE][KB];
@@ -110,10 +110,11 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     __builtin_amdgcn_sched_barrier(0);  // keeps the index row's loads ahead of the query's
     const int hq = HG * hg + li;
     v8bf Q[16];
+    const float* row_cs = ROPE ? rope_cs + (int64_t)row * 64 : nullptr;
     {
-        const uint16_t* qr = q + ((int64_t)row * Hm + hq) * 512 + 8 * lg;
+        const int64_t qr = ((int64_t)row * Hm + hq) * 512 + 8 * lg;
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, ld16(qr + 32 * ks));
+        for (int ks = 0; ks < 16; ++ks) Q[ks] = load_q8<ROPE>(q, qr + 32 * ks, 32 * ks + 8 * lg, row_cs);
     }
     // keep the loads above ahead of the scalar loads below (they would
     // otherwise wait for them)
@@ -448,7 +449,8 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            out[((int64_t)row * Hm + HG * hg + 4 * lg + v) * 512 + 128 * wave + 16 * nt + li] = O[nt][v] * iv[v];
+            store_out<ROPE>(out, ((int64_t)row * Hm + HG * hg + 4 * lg + v) * 512 + 128 * wave + 16 * nt + li,
+                            128 * wave + 16 * nt + li, O[nt][v] * iv[v], row_cs);
     if (lse && wave == 0 && lane < 16)
         lse[(int64_t)row * Hm + HG * hg + lane] =
             l_lse > 0.0f ? (m_run + log2f(l_lse)) * 0.69314718055994531f : -INFINITY;
@@ -462,9 +464,10 @@ constexpr int kMaxSplit = 8;  // the combine is instantiated for S = 2 .. kMaxSp
 constexpr int kAttnTargetWgs = 256;  // workgroups the key splits aim for (more splits cost more than they hide)
 constexpr unsigned kAttnTwoPipeWgs = 128;  // grids up to this size run two pipes per workgroup
 
-template <int S>
+template <int S, int ROPE>
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part, int Hm, int n_hg,
-                                                      float* __restrict__ out, float* __restrict__ lse) {
+                                                      void* __restrict__ out, float* __restrict__ lse,
+                                                      const float* __restrict__ rope_cs) {
     const int row = blockIdx.x / Hm, h = blockIdx.x % Hm;
     const int hg = h / HG, hh = h % HG;
     const float* base = part + ((int64_t)row * n_hg + hg) * S * (HG * 516);
@@ -494,7 +497,20 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    *reinterpret_cast<v4f*>(out + ((int64_t)row * Hm + h) * 512 + 4 * t) = acc * inv;
+    const int64_t oo = ((int64_t)row * Hm + h) * 512 + 4 * t;
+    if constexpr (ROPE) {
+        // channels 4t .. 4t+3 are two RoPE pairs: turned back from 448 on, then cast
+        float f[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+        if (4 * t >= 448) {
+            const float* c = rope_cs + (int64_t)row * 64 + (4 * t - 448);
+            rope_pair(f[0], f[1], c[0], c[1], -1.0f);
+            rope_pair(f[2], f[3], c[2], c[3], -1.0f);
+        }
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + oo) =
+            uint2{bf16_rne(f[0]) | (bf16_rne(f[1]) << 16), bf16_rne(f[2]) | (bf16_rne(f[3]) << 16)};
+    } else {
+        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + oo) = acc * inv;
+    }
     if (lse && t == 0) lse[(int64_t)row * Hm + h] = Llse > 0.0f ? (M + log2f(Llse)) * 0.69314718055994531f : -INFINITY;
 }
 
@@ -537,17 +553,25 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
     float* part = S > 1 ? (float*)a.ws : nullptr;
     // two pipes per workgroup only where the grid leaves most CUs idle (latency
     // is all that counts there); otherwise one pipe, two workgroups per CU
-#define CSA2_ATTN(NP, KF, SF)                                                                                      \
-    hipLaunchKernelGGL((k_sparse_attn<NP, KF, SF>), dim3(nblk), dim3(256 * NP), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K, \
-                       a.swa, a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,   \
-                       a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q,  \
-                       n_hg, S, part)
+    const bool rope = a.rope_cs != nullptr;
+    const void* qv = rope ? (const void*)a.q32 : (const void*)a.q;
+    void* ov = rope ? (void*)a.out16 : (void*)a.out;
+#define CSA2_ATTN(NP, KF, SF, RP)                                                                                  \
+    hipLaunchKernelGGL((k_sparse_attn<NP, KF, SF, RP>), dim3(nblk), dim3(256 * NP), 0, s, qv, a.Hm, a.kv, a.kv_sc, a.idx, \
+                       a.K, a.swa, a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off, \
+                       a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, ov, a.lse, a.g.total_q,     \
+                       n_hg, S, part, a.rope_cs)
+#define CSA2_ATTN_RP(NP, KF, SF)                        \
+    do {                                                \
+        if (rope) CSA2_ATTN(NP, KF, SF, 1);             \
+        else CSA2_ATTN(NP, KF, SF, 0);                  \
+    } while (0)
 #define CSA2_ATTN_NP(KF, SF)                  \
     do {                                      \
         if (nblk <= kAttnTwoPipeWgs)          \
-            CSA2_ATTN(2, KF, SF);             \
+            CSA2_ATTN_RP(2, KF, SF);          \
         else                                  \
-            CSA2_ATTN(1, KF, SF);             \
+            CSA2_ATTN_RP(1, KF, SF);          \
     } while (0)
     if (a.kv_fmt == kKvE4) {
         if (swa8) CSA2_ATTN_NP(kKvE4, kSwaMx8); else CSA2_ATTN_NP(kKvE4, kSwaBf16);
@@ -555,12 +579,18 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
         if (swa8) CSA2_ATTN_NP(kKvMx, kSwaMx8); else CSA2_ATTN_NP(kKvMx, kSwaBf16);
     }
 #undef CSA2_ATTN_NP
+#undef CSA2_ATTN_RP
 #undef CSA2_ATTN
     if (S > 1) {
         const dim3 cg((unsigned)(a.g.total_q * a.Hm));
         switch (S) {
-#define CSA2_COMBINE(N) \
-    case N: hipLaunchKernelGGL((k_attn_combine<N>), cg, dim3(128), 0, s, part, a.Hm, n_hg, a.out, a.lse); break;
+#define CSA2_COMBINE(N)                                                                                           \
+    case N:                                                                                                       \
+        if (rope)                                                                                                 \
+            hipLaunchKernelGGL((k_attn_combine<N, 1>), cg, dim3(128), 0, s, part, a.Hm, n_hg, ov, a.lse, a.rope_cs); \
+        else                                                                                                      \
+            hipLaunchKernelGGL((k_attn_combine<N, 0>), cg, dim3(128), 0, s, part, a.Hm, n_hg, ov, a.lse, a.rope_cs); \
+        break;
             CSA2_COMBINE(2) CSA2_COMBINE(3) CSA2_COMBINE(4) CSA2_COMBINE(5)
             CSA2_COMBINE(6) CSA2_COMBINE(7) CSA2_COMBINE(8)
 #undef CSA2_COMBINE

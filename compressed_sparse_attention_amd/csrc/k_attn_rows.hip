@@ -40,13 +40,14 @@ namespace {
 
 using namespace attn;
 
-template <int KVF, int SWF>
+template <int KVF, int SWF, int ROPE>
 __global__ __launch_bounds__(256, 2) void k_sparse_attn_rows(
-    const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
+    const void* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
     const int32_t* __restrict__ idx, int K, const void* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
     const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ replay_s, int W,
     const int64_t* __restrict__ entry_off, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ q_pos,
-    float scale_log2, float* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg) {
+    float scale_log2, void* __restrict__ out, float* __restrict__ lse, int total_q, int n_hg,
+    const float* __restrict__ rope_cs) {
     __shared__ __attribute__((aligned(16))) uint16_t kl[KB * LROW];
     __shared__ __attribute__((aligned(16))) int kvalid[KB];  // read as int4
     __shared__ int32_t kidx[kMaxK];
@@ -70,10 +71,11 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_rows(
     __builtin_amdgcn_sched_barrier(0);
     const int h0 = 64 * hg + 16 * wave;  // the wave's first head
     v8bf Q[16];
+    const float* row_cs = ROPE ? rope_cs + (int64_t)row * 64 : nullptr;
     {
-        const uint16_t* qr = q + ((int64_t)row * Hm + h0 + li) * 512 + 8 * lg;
+        const int64_t qr = ((int64_t)row * Hm + h0 + li) * 512 + 8 * lg;
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, ld16(qr + 32 * ks));
+        for (int ks = 0; ks < 16; ++ks) Q[ks] = load_q8<ROPE>(q, qr + 32 * ks, 32 * ks + 8 * lg, row_cs);
     }
     asm volatile("" ::: "memory");
 
@@ -295,7 +297,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_rows(
     for (int nt = 0; nt < 32; ++nt)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            out[((int64_t)row * Hm + h0 + 4 * lg + v) * 512 + 16 * nt + li] = O[nt][v] * iv[v];
+            store_out<ROPE>(out, ((int64_t)row * Hm + h0 + 4 * lg + v) * 512 + 16 * nt + li, 16 * nt + li,
+                            O[nt][v] * iv[v], row_cs);
     if (lse && lg == 0)
         lse[(int64_t)row * Hm + h0 + li] = l_run > 0.0f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
 }
@@ -306,15 +309,25 @@ hipError_t launch_sparse_attn_rows(const AttnLaunch& a, hipStream_t s) {
     const int n_hg64 = a.Hm / 64;
     const dim3 grid((unsigned)(a.g.total_q * n_hg64));
     const bool swa8 = a.sw->fmt == CSA2_SWA_MXFP8;
-#define CSA2_ROWS(KF, SF)                                                                                          \
-    hipLaunchKernelGGL((k_sparse_attn_rows<KF, SF>), grid, dim3(256), 0, s, a.q, a.Hm, a.kv, a.kv_sc, a.idx, a.K,    \
+    const bool rope = a.rope_cs != nullptr;
+    const void* qv = rope ? (const void*)a.q32 : (const void*)a.q;
+    void* ov = rope ? (void*)a.out16 : (void*)a.out;
+#define CSA2_ROWS_RP(KF, SF, RP)                                                                                   \
+    hipLaunchKernelGGL((k_sparse_attn_rows<KF, SF, RP>), grid, dim3(256), 0, s, qv, a.Hm, a.kv, a.kv_sc, a.idx, a.K, \
                        a.swa, a.sw->d_row_off, a.sw->d_pos0, a.sw->d_replay_s, a.sw->window, a.b->d_entry_off,     \
-                       a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, a.out, a.lse, a.g.total_q, n_hg64)
+                       a.b->d_row_seq, a.b->d_q_pos, a.scale * 1.4426950408889634f, ov, a.lse, a.g.total_q, n_hg64, \
+                       a.rope_cs)
+#define CSA2_ROWS(KF, SF)                        \
+    do {                                         \
+        if (rope) CSA2_ROWS_RP(KF, SF, 1);       \
+        else CSA2_ROWS_RP(KF, SF, 0);            \
+    } while (0)
     if (a.kv_fmt == kKvE4) {
         if (swa8) CSA2_ROWS(kKvE4, kSwaMx8); else CSA2_ROWS(kKvE4, kSwaBf16);
     } else {
         if (swa8) CSA2_ROWS(kKvMx, kSwaMx8); else CSA2_ROWS(kKvMx, kSwaBf16);
     }
+#undef CSA2_ROWS_RP
 #undef CSA2_ROWS
     return hipGetLastError();
 }

@@ -270,3 +270,24 @@ def test_topk_noalloc_validation():
     big = HostBatch([100000] * 257, [[99999]] * 257)
     assert call(big, stride=100000) == C.CSA2_ERR_SCRATCH
     assert L.csa2_status_string(C.CSA2_ERR_SCRATCH).startswith(b"the problem exceeds")
+
+
+def test_sparse_attn_rope_validation():
+    b = HostBatch([1000], [[999]])
+    L = C.lib()
+    row_off, pos0, ln = np.zeros(1, np.int64), np.array([872], np.int32), np.array([128], np.int32)
+    sw = C.csa2_swa_layout(128, 0, row_off.ctypes.data, pos0.ctypes.data, ln.ctypes.data, None, FAKE, FAKE, None)
+
+    def call(Hm=64, q=FAKE, cs=FAKE, kv_fmt=0, K=512, out=FAKE, scale=0.044):
+        return L.csa2_sparse_attn_rope(ctypes.byref(b.c), Hm, q, cs, kv_fmt, FAKE, FAKE, FAKE, K, FAKE,
+                                       ctypes.byref(sw), scale, out, None, None, 0, None)
+
+    assert call(q=None) == C.CSA2_ERR_INVALID_ARG
+    assert call(cs=None) == C.CSA2_ERR_INVALID_ARG
+    assert call(out=None) == C.CSA2_ERR_INVALID_ARG
+    assert call(q=FAKE + 4) == C.CSA2_ERR_INVALID_ARG      # f32 query rows must be 16-byte aligned
+    assert call(out=FAKE + 2) == C.CSA2_ERR_INVALID_ARG    # bf16 pairs are stored 4 bytes at a time
+    assert call(kv_fmt=5) == C.CSA2_ERR_UNSUPPORTED
+    assert call(Hm=24) == C.CSA2_ERR_UNSUPPORTED
+    assert call(K=0) == C.CSA2_ERR_INVALID_ARG
+    assert call(scale=0.0) == C.CSA2_ERR_INVALID_ARG

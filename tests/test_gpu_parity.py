@@ -585,3 +585,55 @@ def test_rope_cast_specials_bitwise():
     got = C.csa2_rope_cast(dev(x), dev(cs)).cpu().numpy()
     assert np.array_equal(got, oracle.rope_cast(x, cs, False))
     assert [int(v) for v in got[0, 0, : len(bits)]] == [w for _, w in BF16_SPECIAL]
+
+
+ROPE_CASES = {
+    # 3 rows of 64 heads: the 16-head kernel with its keys split and merged
+    "decode_split": lambda: synth.config("decode_c1", n_seq=3, n=6000, Hm=64),
+    # the same without a workspace: no split, the kernel stores the output itself
+    "decode_nosplit": lambda: synth.config("decode_c1", n_seq=3, n=6000, Hm=64),
+    # one row of 16 heads: two pipes per workgroup
+    "two_pipes_e4m3kv_swa8": lambda: synth.make_workload("rp2", 31, [3000], 1, [(20, synth.MODE_FULL, False)], Hm=16,
+                                                        kv_fmt=1, swa_fmt=1),
+    # 520 rows of 64 heads: one workgroup per row and 64 heads
+    "rows": lambda: synth.make_workload("rprows", 32, [300] * 8, 65, [(20, synth.MODE_FULL, False)], Hm=64),
+    "rows_e4m3kv_swa8": lambda: synth.make_workload("rprows8", 33, [300] * 4, 130, [(20, synth.MODE_FULL, False)],
+                                                    Hm=64, kv_fmt=1, swa_fmt=1),
+}
+
+
+@pytest.mark.parametrize("case", list(ROPE_CASES))
+def test_sparse_attn_rope_equals_composition(case):
+    """csa2_sparse_attn_rope equals csa2_rope_cast -> csa2_sparse_attn ->
+    csa2_rope_cast (inverse) bit for bit (output and log-sum-exp), and the
+    oracle's composition within the attention tolerance plus the bf16 cast."""
+    wl = ROPE_CASES[case]()
+    dw = DevWorkload(wl)
+    nq, Hm = wl.total_q, wl.Hm
+    rng = np.random.default_rng(600 + len(case))
+    vis = oracle.row_visible(wl)
+    idx = np.full((nq, 512), -1, np.int32)
+    for r in range(nq):
+        m = min(int(vis[r]), 512)
+        idx[r, :m] = np.sort(rng.choice(int(vis[r]), m, replace=False))
+    q32 = rng.standard_normal((nq, Hm, 512), dtype=np.float32)
+    th = rng.uniform(-np.pi, np.pi, size=(nq, 32))
+    cs = np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
+    dq, dcs, didx = dev(q32), dev(cs), dev(idx)
+    L, dL = wl.layers[0], dw.layers[0]
+    split = case != "decode_nosplit"
+    qb = C.csa2_rope_cast(dq, dcs)
+    o32, l1 = C.csa2_sparse_attn(dw.batch, qb, dw.kv, dw.kv_sc, didx, dL["swa"], dw.swa, SCALE, kv_fmt=wl.kv_fmt,
+                                 split=split)
+    want = C.csa2_rope_cast(o32, dcs, inverse=True)
+    got, l2 = C.csa2_sparse_attn_rope(dw.batch, dq, dcs, dw.kv, dw.kv_sc, didx, dL["swa"], dw.swa, SCALE,
+                                      kv_fmt=wl.kv_fmt, split=split)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want), f"{case}: {(got != want).sum().item()} output values differ"
+    assert torch.equal(l1, l2)
+    # against the oracle: its query cast, attention and cast back
+    qref = oracle.rope_cast(q32, cs, False)
+    ro, _ = oracle.sparse_attn(wl, qref, idx, L.swa)
+    ref = (oracle.rope_cast(ro, cs, True).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    g = (got.cpu().numpy().astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(g - ref) <= 2e-3 + 1.2e-2 * np.abs(ref)), f"{case}: max abs err {np.abs(g - ref).max():.3e}"
