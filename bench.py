@@ -430,8 +430,10 @@ def bench_workloads(synth, C, torch, dev):
 
 def bench_attn_rope(synth, C, torch, dev, reps=20):
     """The RoPE steps around attention (the report's RoPE-attention-RoPE-cast
-    flow) fused into the attention call, against plain attention (bf16 query
-    in, f32 out) and against the three separate calls, at a decode shape (64
+    flow) fused into the attention call (bf16 query before RoPE in, bf16 out),
+    against plain attention (bf16 query in, f32 out) and against the three
+    separate calls (query rotation and cast, attention, output rotation and
+    cast), at a decode shape (64
     rows) and a replay shape (2,048 rows), 64 heads, Top-512 of 32,768
     entries plus a 128-token window."""
     import numpy as np
@@ -446,7 +448,8 @@ def bench_attn_rope(synth, C, torch, dev, reps=20):
         nq, Hm = wl.total_q, wl.Hm
         g = torch.Generator(device=dev).manual_seed(11)
         idx = torch.sort(torch.randint(0, 32768 - T, (nq, 512), generator=g, device=dev), dim=1).values.to(torch.int32)
-        q32 = torch.randn((nq, Hm, 512), generator=g, device=dev, dtype=torch.float32)
+        q32 = torch.randn((nq, Hm, 512), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16).float()
+        q16 = q32.to(torch.bfloat16).view(torch.uint16)  # the query before RoPE
         th = torch.rand((nq, 32), generator=g, device=dev) * 6.2831853
         cs = torch.stack([torch.cos(th), torch.sin(th)], -1).contiguous()
         L = dw.layers[0]
@@ -465,7 +468,7 @@ def bench_attn_rope(synth, C, torch, dev, reps=20):
             C.csa2_rope_cast(o32, cs, inverse=True, out=o16)
 
         def fused():
-            C.csa2_sparse_attn_rope(dw.batch, q32, cs, dw.kv, dw.kv_sc, idx, L["swa"], dw.swa, SCALE, out=o16,
+            C.csa2_sparse_attn_rope(dw.batch, q16, cs, dw.kv, dw.kv_sc, idx, L["swa"], dw.swa, SCALE, out=o16,
                                     want_lse=False, ws=ws)
 
         r = {}
@@ -483,7 +486,7 @@ def bench_attn_rope(synth, C, torch, dev, reps=20):
             f"{r['three_calls_us']} us, fused {r['fused_us']} us")
         r["rows"] = nq
         out[name] = r
-        del dw, q32, qb, o32, o16, ws, idx
+        del dw, q32, q16, qb, o32, o16, ws, idx
         torch.cuda.empty_cache()
     return out
 

@@ -313,19 +313,19 @@ def csa2_sparse_attn(batch, q_bf16, kv_fp4, kv_sc, idx, swa_rows, swa_layout, so
     return out, lse
 
 
-def csa2_sparse_attn_rope(batch, q_f32, rope_cs, kv_fp4, kv_sc, idx, swa_rows, swa_layout, softmax_scale, out=None,
+def csa2_sparse_attn_rope(batch, q_bf16, rope_cs, kv_fp4, kv_sc, idx, swa_rows, swa_layout, softmax_scale, out=None,
                           lse=None, want_lse=True, ws=None, split=True, stream=None, kv_fmt=CSA2_KV_MXFP4):
-    """Sparse attention with the RoPE steps fused: f32 query before RoPE in,
-    bf16 output (u16 bits) with its rotated channels turned back."""
-    Hm = q_f32.shape[1]
-    dev = q_f32.device
+    """Sparse attention with the RoPE steps fused: bf16 query before RoPE in
+    (u16 bits), bf16 output (u16 bits) with its rotated channels turned back."""
+    Hm = q_bf16.shape[1]
+    dev = q_bf16.device
     if out is None:
         out = torch.empty((batch.total_q, Hm, 512), dtype=torch.uint16, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((batch.total_q, Hm), dtype=torch.float32, device=dev)
     if ws is None and split:
         ws = workspace(csa2_workspace_size(CSA2_WS_SPARSE_ATTN, batch, idx.shape[1]), dev)
-    st = lib().csa2_sparse_attn_rope(ctypes.byref(batch.c), Hm, _ptr(q_f32), _ptr(rope_cs), int(kv_fmt), _ptr(kv_fp4),
+    st = lib().csa2_sparse_attn_rope(ctypes.byref(batch.c), Hm, _ptr(q_bf16), _ptr(rope_cs), int(kv_fmt), _ptr(kv_fp4),
                                      _ptr(kv_sc), _ptr(idx), idx.shape[1], _ptr(swa_rows), ctypes.byref(swa_layout.c),
                                      float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
                                      0 if ws is None else ws.numel(), _stream(stream))

@@ -83,29 +83,41 @@ __device__ __forceinline__ float xor_sum(float x) {
 }
 
 // 8 query channels c0 .. c0+7 (c0 a multiple of 8) of a head row as the bf16
-// MFMA operand: from bf16 directly, or (ROPE) from f32 before RoPE, the
-// channels from 448 on rotated by the row's angles, then cast to nearest even
+// MFMA operand, read from bf16.  ROPE: the query is before RoPE; the channels
+// from 448 on are widened to f32, rotated by the row's angles and cast back to
+// nearest even, and every other channel goes through the same cast (which
+// leaves a bf16 value as it is, except that a NaN gets its quiet bit set).
 template <int ROPE>
-__device__ __forceinline__ v8bf load_q8(const void* q, int64_t off, int c0, const float* cs) {
+__device__ __forceinline__ v8bf load_q8(const uint16_t* q, int64_t off, int c0, const float* cs) {
+    v4i w = ld16(q + off);
     if constexpr (ROPE) {
-        const float* p = reinterpret_cast<const float*>(q) + off;
-        const v4f x0 = *reinterpret_cast<const v4f*>(p), x1 = *reinterpret_cast<const v4f*>(p + 4);
-        float f[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         if (c0 >= 448) {
+            float f[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                f[2 * k] = __uint_as_float((uint32_t)w[k] << 16);
+                f[2 * k + 1] = __uint_as_float((uint32_t)w[k] & 0xFFFF0000u);
+            }
             const float* c = cs + (c0 - 448);  // pairs p0 .. p0 + 3, two floats each
             const v4f a = *reinterpret_cast<const v4f*>(c), b = *reinterpret_cast<const v4f*>(c + 4);
             rope_pair(f[0], f[1], a[0], a[1], 1.0f);
             rope_pair(f[2], f[3], a[2], a[3], 1.0f);
             rope_pair(f[4], f[5], b[0], b[1], 1.0f);
             rope_pair(f[6], f[7], b[2], b[3], 1.0f);
-        }
-        v4i w;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w[k] = (int)(bf16_rne(f[2 * k]) | (bf16_rne(f[2 * k + 1]) << 16));
-        return __builtin_bit_cast(v8bf, w);
-    } else {
-        return __builtin_bit_cast(v8bf, ld16(reinterpret_cast<const uint16_t*>(q) + off));
+            for (int k = 0; k < 4; ++k) w[k] = (int)(bf16_rne(f[2 * k]) | (bf16_rne(f[2 * k + 1]) << 16));
+        } else {
+            // per bf16 half: its magnitude plus 0x7F carries into bit 15 exactly
+            // for a NaN (magnitude above 0x7F80); that bit moved to bit 6 is the
+            // quiet bit (the halves cannot carry into each other)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t d = (uint32_t)w[k];
+                w[k] = (int)(d | ((((d & 0x7FFF7FFFu) + 0x007F007Fu) & 0x80008000u) >> 9));
+            }
+        }
     }
+    return __builtin_bit_cast(v8bf, w);
 }
 
 // Final store of output channel c of a head row (value x, this lane's; the
@@ -115,7 +127,8 @@ __device__ __forceinline__ v8bf load_q8(const void* q, int64_t off, int c0, cons
 template <int ROPE>
 __device__ __forceinline__ void store_out(void* out, int64_t off, int c, float x, const float* cs) {
     if constexpr (ROPE) {
-        const float y = __shfl_xor(x, 1);
+        // the partner lane's value by a DPP swap of adjacent lanes (quad_perm 1, 0, 3, 2)
+        const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
         if ((c & 1) == 0) {
             float a = x, b = y;
             if (c >= 448) rope_pair(a, b, cs[c - 448], cs[c - 447], -1.0f);

@@ -412,7 +412,7 @@ CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
 
-CSA2_API csa2_status csa2_sparse_attn_rope(const csa2_batch* batch, int32_t Hm, const float* q_f32,
+CSA2_API csa2_status csa2_sparse_attn_rope(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16,
                                            const float* rope_cs, int32_t kv_fmt, const uint8_t* kv_fp4,
                                            const uint8_t* kv_sc, const int32_t* idx, int32_t K, const void* swa_rows,
                                            const csa2_swa_layout* swa, float softmax_scale, uint16_t* out_bf16,
@@ -420,18 +420,17 @@ CSA2_API csa2_status csa2_sparse_attn_rope(const csa2_batch* batch, int32_t Hm, 
     Geometry g;
     csa2_status st = batch_geometry(batch, &g);
     if (st) return st;
-    if (!q_f32 || !rope_cs || !kv_fp4 || !kv_sc || !idx || !swa_rows || !out_bf16) return CSA2_ERR_INVALID_ARG;
-    if (((uintptr_t)q_f32 | (uintptr_t)rope_cs) & 15 || ((uintptr_t)out_bf16 & 3)) return CSA2_ERR_INVALID_ARG;
+    if (!q_bf16 || !rope_cs || !kv_fp4 || !kv_sc || !idx || !swa_rows || !out_bf16) return CSA2_ERR_INVALID_ARG;
+    if (((uintptr_t)q_bf16 | (uintptr_t)rope_cs) & 15 || ((uintptr_t)out_bf16 & 3)) return CSA2_ERR_INVALID_ARG;
     if (kv_fmt != CSA2_KV_MXFP4 && kv_fmt != CSA2_KV_E4M3_16) return CSA2_ERR_UNSUPPORTED;
     if (Hm < 16 || Hm % 16) return Hm < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
     if (K < 1 || K > kMaxK) return K < 1 ? CSA2_ERR_INVALID_ARG : CSA2_ERR_UNSUPPORTED;
     if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return CSA2_ERR_INVALID_ARG;
     if ((st = check_swa(batch, swa))) return st;
     if (ws && ((uintptr_t)ws & 255)) return CSA2_ERR_WORKSPACE;
-    AttnLaunch a{batch, g, Hm, nullptr, kv_fp4, kv_sc, idx, K, swa_rows, swa, softmax_scale, nullptr, lse, ws,
+    AttnLaunch a{batch, g, Hm, q_bf16, kv_fp4, kv_sc, idx, K, swa_rows, swa, softmax_scale, nullptr, lse, ws,
                  ws ? ws_bytes : 0, kv_fmt};
     a.rope_cs = rope_cs;
-    a.q32 = q_f32;
     a.out16 = out_bf16;
     hipError_t e = launch_sparse_attn(a, stream);
     return e == hipSuccess ? CSA2_OK : hip_fail(e);

@@ -346,11 +346,10 @@ struct AttnLaunch {
     void* ws;                   // partial results when the key blocks are split (may be NULL)
     size_t ws_bytes;
     int kv_fmt;                 // CSA2_KV_* of kv_sc
-    // fused RoPE and casts (csa2_sparse_attn_rope): the query comes as f32 before
-    // RoPE (q32) and is rotated and cast to bf16 on load; the output's rotated
-    // channels are turned back and every channel cast to bf16 on store (out16)
+    // fused RoPE and casts (csa2_sparse_attn_rope): q holds the query before
+    // RoPE, rotated and cast on load; the output's rotated channels are turned
+    // back and every channel cast to bf16 on store (out16)
     const float* rope_cs = nullptr;  // [total_q][32][2] cos, sin per pair
-    const float* q32 = nullptr;      // [total_q][Hm][512]
     uint16_t* out16 = nullptr;       // [total_q][Hm][512]
 };
 

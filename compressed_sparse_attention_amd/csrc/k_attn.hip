@@ -63,7 +63,7 @@ constexpr int SLROW = KB + 4;  // LDS row stride of the logits in floats
 
 template <int NPIPE, int KVF, int SWF, int ROPE>
 __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
-    const void* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
+    const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
     const int32_t* __restrict__ idx, int K, const void* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
     const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ replay_s, int W,
     const int64_t* __restrict__ entry_off, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ q_pos,
@@ -554,7 +554,7 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s) {
     // two pipes per workgroup only where the grid leaves most CUs idle (latency
     // is all that counts there); otherwise one pipe, two workgroups per CU
     const bool rope = a.rope_cs != nullptr;
-    const void* qv = rope ? (const void*)a.q32 : (const void*)a.q;
+    const uint16_t* qv = a.q;
     void* ov = rope ? (void*)a.out16 : (void*)a.out;
 #define CSA2_ATTN(NP, KF, SF, RP)                                                                                  \
     hipLaunchKernelGGL((k_sparse_attn<NP, KF, SF, RP>), dim3(nblk), dim3(256 * NP), 0, s, qv, a.Hm, a.kv, a.kv_sc, a.idx, \

@@ -42,7 +42,7 @@ using namespace attn;
 
 template <int KVF, int SWF, int ROPE>
 __global__ __launch_bounds__(256, 2) void k_sparse_attn_rows(
-    const void* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
+    const uint16_t* __restrict__ q, int Hm, const uint8_t* __restrict__ kv, const uint8_t* __restrict__ kv_sc,
     const int32_t* __restrict__ idx, int K, const void* __restrict__ swa, const int64_t* __restrict__ swa_row_off,
     const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ replay_s, int W,
     const int64_t* __restrict__ entry_off, const int32_t* __restrict__ row_seq, const int32_t* __restrict__ q_pos,
@@ -310,7 +310,7 @@ hipError_t launch_sparse_attn_rows(const AttnLaunch& a, hipStream_t s) {
     const dim3 grid((unsigned)(a.g.total_q * n_hg64));
     const bool swa8 = a.sw->fmt == CSA2_SWA_MXFP8;
     const bool rope = a.rope_cs != nullptr;
-    const void* qv = rope ? (const void*)a.q32 : (const void*)a.q;
+    const uint16_t* qv = a.q;
     void* ov = rope ? (void*)a.out16 : (void*)a.out;
 #define CSA2_ROWS_RP(KF, SF, RP)                                                                                   \
     hipLaunchKernelGGL((k_sparse_attn_rows<KF, SF, RP>), grid, dim3(256), 0, s, qv, a.Hm, a.kv, a.kv_sc, a.idx, a.K, \

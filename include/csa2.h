@@ -347,19 +347,21 @@ CSA2_API csa2_status csa2_sparse_attn(const csa2_batch* batch, int32_t Hm, const
 
 /* ---- sparse attention with the RoPE steps fused ---------------------------
  * The report's kernel flow fuses RoPE, attention, RoPE and a cast into one
- * kernel (section 3.2, FlashMLA's RoPE-attention-RoPE-cast).  Equal bit for bit
- * to csa2_rope_cast(q_f32, inverse 0) -> csa2_sparse_attn -> csa2_rope_cast(
- * out, inverse 1), run in one pass: the query is rotated (channels 448..511 in
- * pairs (448 + 2p, 449 + 2p) by the row's angles rope_cs[row][p] = cos, sin)
- * and cast to bf16 as it is loaded; the output's rotated channels are turned
- * back (the angle negated) and every channel is cast to bf16 to nearest even
- * as it is stored.  The log-sum-exp is that of csa2_sparse_attn.
- * q_f32:    [total_q][Hm][512] f32 (device, 16-byte aligned), before RoPE.
+ * kernel (section 3.2, FlashMLA's RoPE-attention-RoPE-cast).  With q_bf16 the
+ * query before RoPE, this equals bit for bit
+ *   csa2_rope_cast(f32(q_bf16), rope_cs, 0) -> csa2_sparse_attn ->
+ *   csa2_rope_cast(out, rope_cs, 1)
+ * in one pass: the query is rotated (channels 448..511 in pairs
+ * (448 + 2p, 449 + 2p) by the row's angles rope_cs[row][p] = cos, sin) and cast
+ * back to bf16 as it is loaded; the output's rotated channels are turned back
+ * (the angle negated) and every channel is cast to bf16 to nearest even as it
+ * is stored.  The log-sum-exp is that of csa2_sparse_attn.
+ * q_bf16:   [total_q][Hm][512] bf16 before RoPE (device, 16-byte aligned).
  * rope_cs:  [total_q][32][2] f32 (device, 16-byte aligned).
  * out_bf16: [total_q][Hm][512] bf16 (device, 4-byte aligned).
  * The other arguments, the workspace and the supported sizes are those of
  * csa2_sparse_attn. */
-CSA2_API csa2_status csa2_sparse_attn_rope(const csa2_batch* batch, int32_t Hm, const float* q_f32,
+CSA2_API csa2_status csa2_sparse_attn_rope(const csa2_batch* batch, int32_t Hm, const uint16_t* q_bf16,
                                            const float* rope_cs, int32_t kv_fmt, const uint8_t* kv_fp4,
                                            const uint8_t* kv_sc, const int32_t* idx, int32_t K, const void* swa_rows,
                                            const csa2_swa_layout* swa, float softmax_scale, uint16_t* out_bf16,

@@ -285,7 +285,7 @@ def test_sparse_attn_rope_validation():
     assert call(q=None) == C.CSA2_ERR_INVALID_ARG
     assert call(cs=None) == C.CSA2_ERR_INVALID_ARG
     assert call(out=None) == C.CSA2_ERR_INVALID_ARG
-    assert call(q=FAKE + 4) == C.CSA2_ERR_INVALID_ARG      # f32 query rows must be 16-byte aligned
+    assert call(q=FAKE + 4) == C.CSA2_ERR_INVALID_ARG      # query rows are read 16 bytes at a time
     assert call(out=FAKE + 2) == C.CSA2_ERR_INVALID_ARG    # bf16 pairs are stored 4 bytes at a time
     assert call(kv_fmt=5) == C.CSA2_ERR_UNSUPPORTED
     assert call(Hm=24) == C.CSA2_ERR_UNSUPPORTED

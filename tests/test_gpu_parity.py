@@ -604,9 +604,10 @@ ROPE_CASES = {
 
 @pytest.mark.parametrize("case", list(ROPE_CASES))
 def test_sparse_attn_rope_equals_composition(case):
-    """csa2_sparse_attn_rope equals csa2_rope_cast -> csa2_sparse_attn ->
-    csa2_rope_cast (inverse) bit for bit (output and log-sum-exp), and the
-    oracle's composition within the attention tolerance plus the bf16 cast."""
+    """csa2_sparse_attn_rope on a bf16 query before RoPE equals csa2_rope_cast
+    (of the query widened to f32) -> csa2_sparse_attn -> csa2_rope_cast
+    (inverse) bit for bit (output and log-sum-exp), and the oracle's
+    composition within the attention tolerance plus the bf16 cast."""
     wl = ROPE_CASES[case]()
     dw = DevWorkload(wl)
     nq, Hm = wl.total_q, wl.Hm
@@ -616,13 +617,15 @@ def test_sparse_attn_rope_equals_composition(case):
     for r in range(nq):
         m = min(int(vis[r]), 512)
         idx[r, :m] = np.sort(rng.choice(int(vis[r]), m, replace=False))
-    q32 = rng.standard_normal((nq, Hm, 512), dtype=np.float32)
+    # the query before RoPE in bf16
+    q16 = (rng.standard_normal((nq, Hm, 512), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q32 = (q16.astype(np.uint32) << 16).view(np.float32)
     th = rng.uniform(-np.pi, np.pi, size=(nq, 32))
     cs = np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
-    dq, dcs, didx = dev(q32), dev(cs), dev(idx)
+    dq, dq32, dcs, didx = dev(q16), dev(q32), dev(cs), dev(idx)
     L, dL = wl.layers[0], dw.layers[0]
     split = case != "decode_nosplit"
-    qb = C.csa2_rope_cast(dq, dcs)
+    qb = C.csa2_rope_cast(dq32, dcs)
     o32, l1 = C.csa2_sparse_attn(dw.batch, qb, dw.kv, dw.kv_sc, didx, dL["swa"], dw.swa, SCALE, kv_fmt=wl.kv_fmt,
                                  split=split)
     want = C.csa2_rope_cast(o32, dcs, inverse=True)
