@@ -19,7 +19,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kHistBins = 4096;        // top 12 value bits of a non-negative binary32 score (bits 30..19)
+constexpr int kHistBins = 4096;        // bits 30..19 of a non-negative binary32 score; negatives in bin 0
 constexpr int kCandCap = 8192;         // per-row candidate capacity of the fast Top-K path
 constexpr int kMaxK = 2048;
 
@@ -49,17 +49,24 @@ __host__ __device__ inline int64_t visible_count(int64_t n, int64_t t, int m) {
 }
 
 // ---------------------------------------------------------------------------
-// Selection order shared by the scan and the Top-K passes.  Scores are
-// non-negative binary32 values (a negative one orders as +0), so their bit
-// patterns order like the values, and
-//     key64 = (score bits << 32) | (0xFFFFFFFF - position)
+// Selection order shared by the scan and the Top-K passes.  A score's bit
+// pattern maps to an unsigned key that orders like the value for every
+// binary32 but NaN (non-negative: set the sign bit; negative: invert all
+// bits; -0 first becomes +0), so -inf < negatives < 0 < positives, and
+//     key64 = (key << 32) | (0xFFFFFFFF - position)
 // is unique per position and orders exactly like (score desc, position asc).
-// The histogram bin of a score is its bits 30..19, i.e. key64 >> 51.
+// The histograms have 4096 bins: a non-negative score's bits 30..19, with
+// every negative score (and -inf) in bin 0.  Keys of a bin b >= 1 share their
+// top 13 bits, b + 4096, so a selection inside such a bin starts at bit 51;
+// bin 0 mixes signs, and a selection that starts there runs from the top bit.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t score_key(float s) {
-    const uint32_t u = __float_as_uint(s);
-    return (u & 0x80000000u) ? 0u : u;
+    uint32_t u = __float_as_uint(s);
+    u = u == 0x80000000u ? 0u : u;  // -0 equals +0: the same key, ties by position
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+__device__ __forceinline__ uint32_t key_bin(uint32_t key) { return key >= 0x80000000u ? (key - 0x80000000u) >> 19 : 0u; }
+__device__ __forceinline__ uint32_t key64_bin(uint64_t x) { return key_bin((uint32_t)(x >> 32)); }
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t slot) {
     return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - slot);

@@ -100,7 +100,8 @@ __device__ __forceinline__ float head_sum(v16f (&acc)[NMT][2], const float* __re
 // Histogram of the written scores over bits 30..19 (the bins the Top-K pass
 // starts from), kept in LDS per query row and flushed with one global atomic
 // per non-empty bin.  Negative scores (only possible with negative head
-// weights) count in bin 0, as the Top-K pass orders them.
+// weights) count in bin 0, where the Top-K pass selects among them by value:
+// the same bin as key_bin(score_key(s)), in two operations.
 __device__ __forceinline__ uint32_t score_bin(float s) {
     const uint32_t u = __float_as_uint(s);
     return (u & 0x80000000u) ? 0u : (u >> 19);

@@ -3,14 +3,14 @@
 // Top-K (report "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
 // Compression", section 2.3; K = 512 in section 4.2.1): per query row, the
 // first min(K, n) slots under (score descending, position ascending), returned
-// in ascending position order.  Scores are non-negative binary32 values, so
-// their bit patterns order like the values; the composite
-//     key64 = (score bits << 32) | (0xFFFFFFFF - slot)
-// is then unique per slot and orders exactly like (score desc, slot asc), so
-// the selection is a plain radix select on key64 with no tie cases.
+// in ascending position order.  A score maps to an order-preserving unsigned
+// key (csa2_internal.h), and the composite
+//     key64 = (key << 32) | (0xFFFFFFFF - slot)
+// is unique per slot and orders exactly like (score desc, slot asc), so the
+// selection is a plain radix select on key64 with no tie cases.
 //
 // Pass structure (every pass spans many workgroups per row):
-//   hist     histogram of score bits 30..19 (4096 bins) per row
+//   hist     histogram of score bits 30..19 (4096 bins; negatives in bin 0) per row
 //   thresh   per row, the bin that holds the K-th largest score
 //   collect  every slot in a bin at or above it -> per-row candidate list
 //   final    per row, radix select on key64 among the candidates in LDS,
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void k_chunk_bound(const float* __restrict__ s
 #pragma unroll
         for (int u = 0; u < 8; ++u) key[u] = score_key(sr[base + threadIdx.x + 256 * u]);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) atomicAdd(&h[key[u] >> 19], 1u);
+        for (int u = 0; u < 8; ++u) atomicAdd(&h[key_bin(key[u])], 1u);
     }
     __syncthreads();
     const uint32_t bm = threshold_bin(PlainBins{h}, m, wtot, found);
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ score
 #pragma unroll
     for (int u = 0; u < kHChunk / 256; ++u) {
         const int64_t s = s0 + threadIdx.x + 256 * u;
-        const bool take = s < s1 && (key[u] >> 19) >= bin;
+        const bool take = s < s1 && key_bin(key[u]) >= bin;
         const uint64_t m = __ballot(take);
         if (m) {
             uint32_t p0 = 0;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void k_collect_local(uint64_t* __restrict__ li
     uint32_t take = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        take |= (uint32_t)((uint32_t)u < per && i0 + u < cnt && (uint32_t)(key[u] >> 51) >= rsel.bin) << u;
+        take |= (uint32_t)((uint32_t)u < per && i0 + u < cnt && key64_bin(key[u]) >= rsel.bin) << u;
     const uint32_t mine = (uint32_t)__popc(take);
     uint32_t off = block_scan_256(mine, wtot) - mine;  // the barrier inside follows every load
     const uint32_t total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
@@ -240,6 +240,29 @@ struct RadixState {
     uint32_t need;    // elements still to take among those matching the prefix
     int done;
 };
+
+// The select state for a candidate set of every key in threshold bin B and
+// the bins above it, `above` of them in the bins above (they all win): in a
+// bin B >= 1 the keys share their top 13 bits (B + 4096) and the select takes
+// kk - above of them from bit 51 down; bin 0 also holds every negative score,
+// so the select runs over all candidates from the top bit.
+__device__ __forceinline__ void start_in_bin(RadixState* st, uint32_t B, uint32_t kk, uint32_t above) {
+    if (B >= 1) {
+        st->prefix = (uint64_t)B + 4096u;
+        st->shift = 51;
+        st->need = kk - above;
+    } else {
+        st->prefix = 0;
+        st->shift = 64;
+        st->need = kk;
+    }
+}
+
+// key64 x against the select state's fixed bits: whether x's bits above
+// `sh` equal the prefix (a shift of 64 leaves no fixed bit: every key
+// matches), or reach it
+__device__ __forceinline__ bool prefix_eq(uint64_t x, int sh, uint64_t pf) { return sh >= 64 || (x >> sh) == pf; }
+__device__ __forceinline__ bool prefix_ge(uint64_t x, int sh, uint64_t pf) { return sh >= 64 || (x >> sh) >= pf; }
 
 // digit width at a level: 8 bits, or what realigns `shift` to a multiple of 8
 __device__ __forceinline__ int digit_bits(int shift) { return (shift & 7) ? (shift & 7) : 8; }
@@ -348,14 +371,7 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         st.done = from_list && cnt == kk;  // every candidate wins
         nwin = 0;
         base = 0;
-        if (from_list && !st.done && !sel[row].lb) {
-            // the candidates are the keys of the threshold bin and of the bins
-            // above it (all of which win): select among the threshold bin's keys
-            // only, from bit 51 down
-            st.prefix = sel[row].bin;
-            st.shift = 51;
-            st.need = kk - sel[row].above;
-        }
+        if (from_list && !st.done && !sel[row].lb) start_in_bin(&st, sel[row].bin, kk, sel[row].above);
     }
     __syncthreads();
     const int64_t m_elems = from_list ? (int64_t)cnt : n;
@@ -367,7 +383,7 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         const uint64_t pf = st.prefix;
         for (int64_t i = threadIdx.x; i < m_elems; i += 1024) {
             const uint64_t x = from_list ? c[i] : composite(score_key(sr[i]), (uint32_t)i);
-            const bool m = sh >= 64 ? true : ((x >> sh) == pf);
+            const bool m = prefix_eq(x, sh, pf);
             if (m) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
         }
         __syncthreads();
@@ -384,7 +400,7 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         __syncthreads();
         for (uint32_t i = threadIdx.x; i < cnt; i += 1024) {
             const uint64_t x = c[i];
-            if (sh >= 64 || (x >> sh) >= pf) {
+            if (prefix_ge(x, sh, pf)) {
                 const uint32_t slot = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu);
                 atomicOr(&bmap[slot >> 5], 1u << (slot & 31));
             }
@@ -417,7 +433,7 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         // winners: key64 >= prefix << shift; then sort their slots
         for (uint32_t i = threadIdx.x; i < cnt; i += 1024) {
             const uint64_t x = c[i];
-            const bool win = sh >= 64 ? true : ((x >> sh) >= pf);
+            const bool win = prefix_ge(x, sh, pf);
             if (win) {
                 const uint32_t p = atomicAdd(&nwin, 1u);
                 if (p < (uint32_t)kMaxK) winners[p] = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu);
@@ -455,7 +471,7 @@ __global__ __launch_bounds__(1024) void k_final(const float* __restrict__ scores
         bool win = false;
         if (s < n) {
             const uint64_t x = composite(score_key(sr[s]), (uint32_t)s);
-            win = sh >= 64 ? true : ((x >> sh) >= pf);
+            win = prefix_ge(x, sh, pf);
         }
         const uint64_t m = __ballot(win);
         if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
@@ -552,9 +568,7 @@ __global__ __launch_bounds__(1024) void k_final_local(const uint64_t* __restrict
     if (from_lds)
         for (uint32_t e = tid; e < total; e += 1024) c[e] = elem(e);
     if (tid == 0) {
-        st.prefix = rsel.bin;
-        st.shift = 51;
-        st.need = kk - rsel.above;
+        start_in_bin(&st, rsel.bin, kk, rsel.above);
         st.done = 0;
         base = 0;
     }
@@ -577,7 +591,7 @@ __global__ __launch_bounds__(1024) void k_final_local(const uint64_t* __restrict
         const int w = digit_bits(sh);
         const uint64_t pf = st.prefix;
         for_each([&](uint64_t x) {
-            if ((x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
+            if (prefix_eq(x, sh, pf)) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
         });
         __syncthreads();
         radix_step(hist256, scan256, &st, &found);
@@ -586,7 +600,7 @@ __global__ __launch_bounds__(1024) void k_final_local(const uint64_t* __restrict
     const uint64_t pf = st.prefix;
     // winners (key64 >= prefix << shift) in candidate order = position order
     auto emit = [&](uint64_t x, bool valid) {
-        const bool win = valid && (x >> sh) >= pf;
+        const bool win = valid && prefix_ge(x, sh, pf);
         const uint64_t m = __ballot(win);
         if (lane == 0) wsum[wave] = (uint32_t)__popcll(m);
         __syncthreads();
@@ -867,7 +881,7 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
         if (in_regs) {
             uint32_t mask = 0;
 #pragma unroll
-            for (int u = 0; u < kListPer; ++u) mask |= (uint32_t)(valid(u) && (uint32_t)(key[u] >> 51) >= LB) << u;
+            for (int u = 0; u < kListPer; ++u) mask |= (uint32_t)(valid(u) && key64_bin(key[u]) >= LB) << u;
             const uint32_t cnt = (uint32_t)__popc(mask);
             uint32_t incl = cnt;
 #pragma unroll
@@ -886,7 +900,7 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
                 }
         } else {
             for_each_entry([&](uint64_t x) {
-                if ((uint32_t)(x >> 51) >= LB) {
+                if (key64_bin(x) >= LB) {
                     const uint32_t r = atomicAdd(&nsurv, 1u);
                     if (r < (uint32_t)kCandCap) c[r] = x;
                 }
@@ -910,7 +924,7 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
                 const uint64_t pf = st.prefix;
                 for (uint32_t e = tid; e < n_surv; e += 1024) {
                     const uint64_t x = c[e];
-                    if (sh >= 64 || (x >> sh) == pf)
+                    if (prefix_eq(x, sh, pf))
                         atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
                 }
                 __syncthreads();
@@ -920,7 +934,7 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
             const uint64_t pf = st.prefix;
             for (uint32_t e = tid; e < n_surv; e += 1024) {
                 const uint64_t x = c[e];
-                if ((x >> sh) >= pf) {
+                if (prefix_ge(x, sh, pf)) {
                     const uint32_t pos = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu);
                     atomicOr(&bm[pos >> 5], 1u << (pos & 31));
                 }
@@ -956,7 +970,7 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
 
     // 1. the threshold bin B
     uint32_t B, above;
-    find_bin([&](auto&& f) { for_each_entry([&](uint64_t x) { f((uint32_t)(x >> 51)); }); }, kk, hcopy, dcount, thr,
+    find_bin([&](auto&& f) { for_each_entry([&](uint64_t x) { f(key64_bin(x)); }); }, kk, hcopy, dcount, thr,
              B, above);
 
     // 2. the entries at or above B, in order, into LDS while they fit
@@ -964,21 +978,19 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
     if (in_regs) {
         uint32_t take = 0;
 #pragma unroll
-        for (int u = 0; u < kListPer; ++u) take |= (uint32_t)(valid(u) && (uint32_t)(key[u] >> 51) >= B) << u;
+        for (int u = 0; u < kListPer; ++u) take |= (uint32_t)(valid(u) && key64_bin(key[u]) >= B) << u;
         n_cand = rank_in_regs(take, [&](uint32_t r, int u) {
             if (r < (uint32_t)kCandCap) c[r] = key[u];
         });
     } else {
-        n_cand = stream_ordered([&](uint64_t x) { return (uint32_t)(x >> 51) >= B; },
+        n_cand = stream_ordered([&](uint64_t x) { return key64_bin(x) >= B; },
                                 [&](uint32_t r, uint64_t x) {
                                     if (r < (uint32_t)kCandCap) c[r] = x;
                                 });
     }
     const bool in_lds = n_cand <= (uint32_t)kCandCap;
     if (tid == 0) {
-        st.prefix = B;
-        st.shift = 51;
-        st.need = kk - above;
+        start_in_bin(&st, B, kk, above);
         st.done = 0;
     }
     __syncthreads();
@@ -991,7 +1003,7 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
         const int w = digit_bits(sh);
         const uint64_t pf = st.prefix;
         auto count = [&](uint64_t x) {
-            if ((x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
+            if (prefix_eq(x, sh, pf)) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
         };
         if (in_lds) {
             for (uint32_t e = tid; e < n_cand; e += 1024) count(c[e]);
@@ -1014,7 +1026,7 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
 #pragma unroll
         for (int u = 0; u < kCandPer; ++u) {
             const uint32_t e = c_lo + (uint32_t)u;
-            win |= (uint32_t)((uint32_t)u < P2 && e < n_cand && (c[e] >> sh) >= pf) << u;
+            win |= (uint32_t)((uint32_t)u < P2 && e < n_cand && prefix_ge(c[e], sh, pf)) << u;
         }
         const uint32_t mine = (uint32_t)__popc(win);
         uint32_t tot;
@@ -1028,12 +1040,12 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
     } else if (in_regs) {
         uint32_t win = 0;
 #pragma unroll
-        for (int u = 0; u < kListPer; ++u) win |= (uint32_t)(valid(u) && (key[u] >> sh) >= pf) << u;
+        for (int u = 0; u < kListPer; ++u) win |= (uint32_t)(valid(u) && prefix_ge(key[u], sh, pf)) << u;
         rank_in_regs(win, [&](uint32_t r, int u) {
             if (r < kk) out[r] = slot_of(key[u]);
         });
     } else {
-        stream_ordered([&](uint64_t x) { return (x >> sh) >= pf; },
+        stream_ordered([&](uint64_t x) { return prefix_ge(x, sh, pf); },
                        [&](uint32_t r, uint64_t x) {
                            if (r < kk) out[r] = slot_of(x);
                        });
@@ -1087,14 +1099,12 @@ __global__ __launch_bounds__(1024) void k_topk_rows(const float* __restrict__ sc
         [&](auto&& f) {
 #pragma unroll
             for (int u = 0; u < kRowPer; ++u)
-                if (valid(u)) f(key[u] >> 19);
+                if (valid(u)) f(key_bin(key[u]));
         },
         kk, hcopy, dcount, thr, B, above);
 
     if (tid == 0) {
-        st.prefix = B;
-        st.shift = 51;
-        st.need = kk - above;
+        start_in_bin(&st, B, kk, above);
         st.done = 0;
     }
     __syncthreads();
@@ -1107,7 +1117,7 @@ __global__ __launch_bounds__(1024) void k_topk_rows(const float* __restrict__ sc
 #pragma unroll
         for (int u = 0; u < kRowPer; ++u) {
             const uint64_t x = composite(key[u], (uint32_t)(tid + 1024 * u));
-            if (valid(u) && (x >> sh) == pf) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
+            if (valid(u) && prefix_eq(x, sh, pf)) atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
         }
         __syncthreads();
         radix_step(hist256, scan256, &st, &found);
@@ -1117,7 +1127,7 @@ __global__ __launch_bounds__(1024) void k_topk_rows(const float* __restrict__ sc
 #pragma unroll
     for (int u = 0; u < kRowPer; ++u) {
         const uint32_t e = (uint32_t)(tid + 1024 * u);
-        if (valid(u) && (composite(key[u], e) >> sh) >= pf) atomicOr(&bm[e >> 5], 1u << (e & 31));
+        if (valid(u) && prefix_ge(composite(key[u], e), sh, pf)) atomicOr(&bm[e >> 5], 1u << (e & 31));
     }
     __syncthreads();
     // slots in order: thread t owns bitmap word t

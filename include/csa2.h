@@ -264,7 +264,8 @@ CSA2_API csa2_status csa2_kv_append(int64_t n, const float* x, const float* rope
  * section 4.2.1).  n = vis(row) when cand == NULL (slots are positions), else
  * n = cand_count[row] and slot s maps to position cand[row*cand_stride + s];
  * the first n candidate positions must be ascending.  Scores of the n slots
- * must be finite and >= +0 (as csa2_index_score writes them).
+ * are ordered by value, negative ones and -inf included (-inf last); they
+ * must not be NaN.
  * hist: NULL, or the histogram csa2_index_score wrote for exactly these scores
  *   (with cand, valid when the first cand_count slots are all non-empty and
  *   visible, as in a block pool).

@@ -132,17 +132,31 @@ def _topk_batch(lens, T):
     return C.Batch(lens, qp), qp
 
 
-@pytest.mark.parametrize("distinct", [4, 1000, 0])
+def _signed_scores(rng, nq, stride):
+    """Scores of both signs: normal values, some rows all negative, exact
+    zeros of both signs, ties and -inf slots."""
+    s = rng.standard_normal((nq, stride)).astype(np.float32)
+    s[::3] = -np.abs(s[::3])                        # rows with no non-negative score
+    s[:, 5::97] = 0.0
+    s[:, 7::89] = -0.0
+    s[:, 11::53] = np.round(s[:, 11::53] * 4) / 4   # ties
+    s[1::2, 13::61] = -np.inf
+    return s
+
+
+@pytest.mark.parametrize("distinct", [4, 1000, 0, -1])
 def test_topk_full_bitwise(distinct):
     rng = np.random.default_rng(11 + distinct)
     lens = [3, 511, 512, 513, 20000, 70000]
     b, qp = _topk_batch(lens, 2)
     nq = b.total_q
     stride = max(lens)
-    if distinct:
+    if distinct > 0:
         s = (rng.integers(0, distinct, size=(nq, stride)) * 0.5).astype(np.float32)
-    else:  # continuous
+    elif distinct == 0:  # continuous
         s = rng.random((nq, stride)).astype(np.float32) * 100
+    else:  # both signs, -inf slots
+        s = _signed_scores(rng, nq, stride)
     vis = np.array([min(n, t + 1) for n, p in zip(lens, qp) for t in p], np.int64)
     for K in (512, 2048, 17):
         got = C.csa2_topk(b, dev(s), K)
@@ -151,19 +165,22 @@ def test_topk_full_bitwise(distinct):
         assert np.array_equal(got.cpu().numpy(), ref), K
 
 
-@pytest.mark.parametrize("distinct", [4, 1000, 0, 1])
+@pytest.mark.parametrize("distinct", [4, 1000, 0, 1, -1])
 def test_topk_rows_bitwise(distinct):
     """Rows of at most 16,384 slots: one workgroup per row selects from the
-    scores held in registers (few distinct values, continuous, all equal)."""
+    scores held in registers (few distinct values, continuous, all equal,
+    both signs with -inf slots)."""
     rng = np.random.default_rng(23 + distinct)
     lens = [2, 3, 511, 512, 513, 9000, 16384]
     b, qp = _topk_batch(lens, 2)
     nq = b.total_q
     stride = max(lens)
-    if distinct:
+    if distinct > 0:
         s = (rng.integers(0, distinct, size=(nq, stride)) * 0.5).astype(np.float32)
-    else:
+    elif distinct == 0:
         s = rng.random((nq, stride)).astype(np.float32) * 100
+    else:
+        s = _signed_scores(rng, nq, stride)
     vis = np.array([min(n, t + 1) for n, p in zip(lens, qp) for t in p], np.int64)
     for K in (512, 2048, 17):
         got = C.csa2_topk(b, dev(s), K)
@@ -437,6 +454,42 @@ def test_layer_chain_ties(case):
     outs, (pb, pp, pc), _ = run_chain(dw)
     torch.cuda.synchronize()
     ref = oracle.layer_chain(wl)
+    for o, r in zip(outs, ref):
+        assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"layer {r['layer']} indices"
+        assert_close_attn(o["out"].cpu().numpy(), r["out"], f"layer {r['layer']}")
+        if "pool_pos" in r:
+            assert np.array_equal(pb.cpu().numpy(), r["blocks"])
+            assert np.array_equal(pp.cpu().numpy(), r["pool_pos"])
+            assert np.array_equal(pc.cpu().numpy(), r["pool_count"])
+
+
+NEGW_CASES = {
+    # head weights of both signs (U(-1, 1)); every third row all negative, so
+    # all of its scores are <= 0 and its threshold lies in bin 0
+    "fused_t1": dict(lens=[3, 700, 9000, 20000, 70000], T=1),
+    "t4": dict(lens=[5, 3000, 20000, 40000], T=4),
+    "split": dict(lens=[300000, 5000], T=1),
+}
+
+
+@pytest.mark.parametrize("case", list(NEGW_CASES))
+def test_layer_chain_negative_weights(case):
+    """Negative head weights give negative scores; the Top-K, the block pool
+    and Reindex order them by value (scan lists, the one-kernel and the split
+    selection from lists, pool and Reindex rows)."""
+    c = NEGW_CASES[case]
+    wl = synth.make_workload("negw_" + case, 0xC5A2B000 + len(case), c["lens"], c["T"],
+                             [(20, synth.MODE_FULL, True), (24, synth.MODE_REINDEX, False), (25, synth.MODE_REUSE, False)],
+                             Hm=16)
+    for L in wl.layers:
+        if L.w is not None:
+            L.w[:] = L.w * 2.0 - 1.0
+            L.w[::3] = -np.abs(L.w[::3])
+    dw = DevWorkload(wl)
+    outs, (pb, pp, pc), _ = run_chain(dw)
+    torch.cuda.synchronize()
+    ref = oracle.layer_chain(wl)
+    assert (ref[0]["scores"][np.isfinite(ref[0]["scores"])] < 0).any()
     for o, r in zip(outs, ref):
         assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"layer {r['layer']} indices"
         assert_close_attn(o["out"].cpu().numpy(), r["out"], f"layer {r['layer']}")
