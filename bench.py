@@ -425,6 +425,7 @@ def bench_workloads(synth, C, torch, dev):
     res["attn_rope"] = bench_attn_rope(synth, C, torch, dev)
     res["compress"] = bench_compress(C, torch, dev)
     res["index_k_project"] = bench_project(C, torch, dev)
+    res["index_k_project_rope"] = bench_project(C, torch, dev, rope=True)
     return res
 
 
@@ -491,30 +492,34 @@ def bench_attn_rope(synth, C, torch, dev, reps=20):
     return out
 
 
-def bench_project(C, torch, dev, n=131072, reps=10):
+def bench_project(C, torch, dev, n=131072, reps=10, rope=False):
     """The indexer-K projection of 131,072 entries (one source layer of the
     prefill context): 2 x 512 x 128 flops an entry as float32 multiply-add
-    chains (against the vector fp32 peak), then MXFP4 codes."""
+    chains (against the vector fp32 peak), then MXFP4 codes.  With `rope` the
+    entries come before RoPE with their angles (the rotation is not counted)."""
     g = torch.Generator(device=dev).manual_seed(9)
     x = torch.randn((n, 512), generator=g, device=dev, dtype=torch.float32)
     W = torch.randn((512, 128), generator=g, device=dev, dtype=torch.float32) * 0.05
+    th = torch.rand((n, 32), generator=g, device=dev, dtype=torch.float32) * 6.283
+    cs = torch.stack([th.cos(), th.sin()], -1).contiguous() if rope else None
     dst = torch.arange(n, device=dev, dtype=torch.int64)
     kf = torch.empty((n, 64), dtype=torch.uint8, device=dev)
     ks = torch.empty((n, 4), dtype=torch.uint8, device=dev)
-    C.csa2_index_k_project(x, W, dst, kf, ks, q_fmt=C.CSA2_Q_MXFP4)
+    C.csa2_index_k_project(x, W, dst, kf, ks, q_fmt=C.CSA2_Q_MXFP4, rope_cs=cs)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(reps):
-        C.csa2_index_k_project(x, W, dst, kf, ks, q_fmt=C.CSA2_Q_MXFP4)
+        C.csa2_index_k_project(x, W, dst, kf, ks, q_fmt=C.CSA2_Q_MXFP4, rope_cs=cs)
     e.record()
     torch.cuda.synchronize()
     us = s.elapsed_time(e) * 1000.0 / reps
     flops = 2.0 * n * 512 * 128
     tf = flops / (us * 1e-6) / 1e12
-    log(f"[bench] index_k_project: {us:.1f} us for {n} entries, {tf:.1f} TFLOP/s fp32")
+    log(f"[bench] index_k_project{' from entries before RoPE' if rope else ''}: {us:.1f} us for {n} entries, "
+        f"{tf:.1f} TFLOP/s fp32")
     r = {"us": round(us, 2), "entries": n, "flops": flops, "tflops": round(tf, 2), "frac_fp32_vector_peak": round(tf / 157.3, 4)}
-    del x, W, dst, kf, ks
+    del x, W, th, cs, dst, kf, ks
     torch.cuda.empty_cache()
     return r
 

@@ -82,7 +82,7 @@ def lib():
         L.csa2_block_pool.argtypes = [B, _vp, i64, i32, i32, _vp, _vp, _vp, _vp, sz, _vp]
         L.csa2_gather_dequant.argtypes = [B, i32, _vp, _vp, _vp, i32, _vp, _vp]
         L.csa2_rope_cast.argtypes = [ctypes.c_int64, i32, _vp, _vp, i32, _vp, _vp]
-        L.csa2_index_k_project.argtypes = [ctypes.c_int64, _vp, _vp, _vp, ctypes.c_int64, i32, _vp, _vp, _vp]
+        L.csa2_index_k_project.argtypes = [ctypes.c_int64, _vp, _vp, _vp, _vp, ctypes.c_int64, i32, _vp, _vp, _vp]
         L.csa2_compress.argtypes = [ctypes.c_int64, i32, _vp, _vp, _vp, _vp]
         L.csa2_kv_append.argtypes = [ctypes.c_int64, _vp, _vp, _vp, ctypes.c_int64, i32, _vp, _vp, _vp]
         L.csa2_sparse_attn.argtypes = [B, i32, _vp, i32, _vp, _vp, _vp, i32, _vp, S, f32, _vp, _vp, _vp, sz, _vp]
@@ -257,12 +257,13 @@ def csa2_rope_cast(x, rope_cs, inverse=False, out=None, stream=None):
     return out
 
 
-def csa2_index_k_project(x, W, dst_row, k_fp4, k_sc, q_fmt=CSA2_Q_FP4, stream=None):
+def csa2_index_k_project(x, W, dst_row, k_fp4, k_sc, q_fmt=CSA2_Q_FP4, rope_cs=None, stream=None):
     """Indexer K of n entries: y = x W (fp32 chain), E2M1 with one E8M0 per row
-    or per 32 channels (CSA2_Q_MXFP4), into rows dst_row of k_fp4 [rows][64]."""
+    or per 32 channels (CSA2_Q_MXFP4), into rows dst_row of k_fp4 [rows][64].
+    x is after RoPE, or before it when its angles rope_cs [n][32][2] are given."""
     n = int(dst_row.shape[0])
-    st = lib().csa2_index_k_project(n, _ptr(x), _ptr(W), _ptr(dst_row), int(k_fp4.shape[0]), int(q_fmt), _ptr(k_fp4),
-                                    _ptr(k_sc), _stream(stream))
+    st = lib().csa2_index_k_project(n, _ptr(x), _ptr(rope_cs), _ptr(W), _ptr(dst_row), int(k_fp4.shape[0]),
+                                    int(q_fmt), _ptr(k_fp4), _ptr(k_sc), _stream(stream))
     _check(st, "csa2_index_k_project")
 
 

@@ -241,17 +241,17 @@ CSA2_API csa2_status csa2_rope_cast(int64_t n_rows, int32_t heads, const float* 
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
 
-CSA2_API csa2_status csa2_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst_row,
-                                          int64_t n_rows, int32_t q_fmt, uint8_t* k_fp4, uint8_t* k_sc,
-                                          hipStream_t stream) {
+CSA2_API csa2_status csa2_index_k_project(int64_t n, const float* x, const float* rope_cs, const float* W,
+                                          const int64_t* dst_row, int64_t n_rows, int32_t q_fmt, uint8_t* k_fp4,
+                                          uint8_t* k_sc, hipStream_t stream) {
     if (n < 0) return CSA2_ERR_INVALID_ARG;
     if (q_fmt != CSA2_Q_FP4 && q_fmt != CSA2_Q_FP8 && q_fmt != CSA2_Q_MXFP4) return CSA2_ERR_INVALID_ARG;
     if (n == 0) return CSA2_OK;
     if (!x || !W || !dst_row || !k_fp4 || !k_sc || n_rows < 1) return CSA2_ERR_INVALID_ARG;
-    if (((uintptr_t)x | (uintptr_t)W | (uintptr_t)k_fp4) & 15) return CSA2_ERR_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)rope_cs | (uintptr_t)W | (uintptr_t)k_fp4) & 15) return CSA2_ERR_INVALID_ARG;
     if ((n + 63) / 64 > 0x7FFFFFFF) return CSA2_ERR_UNSUPPORTED;
     const hipError_t e =
-        launch_index_k_project(n, x, W, dst_row, n_rows, q_fmt == CSA2_Q_MXFP4, k_fp4, k_sc, stream);
+        launch_index_k_project(n, x, rope_cs, W, dst_row, n_rows, q_fmt == CSA2_Q_MXFP4, k_fp4, k_sc, stream);
     return e == hipSuccess ? CSA2_OK : hip_fail(e);
 }
 

@@ -383,8 +383,8 @@ inline bool attn_rows_ok(const Geometry& g, int Hm) {
 hipError_t launch_sparse_attn_rows(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_rope_cast(int64_t n_rows, int heads, const float* in, const float* cs, int inverse, uint16_t* out,
                             hipStream_t s);
-hipError_t launch_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst, int64_t rows,
-                                  int mx, uint8_t* k_fp4, uint8_t* k_sc, hipStream_t s);
+hipError_t launch_index_k_project(int64_t n, const float* x, const float* cs, const float* W, const int64_t* dst,
+                                  int64_t rows, int mx, uint8_t* k_fp4, uint8_t* k_sc, hipStream_t s);
 hipError_t launch_compress(int64_t n, int m, const float* c_tok, const float* z_tok, float* out, hipStream_t s);
 hipError_t launch_kv_append(int64_t n, const float* x, const float* cs, const int64_t* dst, int64_t rows, int kv_fmt,
                             uint8_t* kv, uint8_t* kv_sc, hipStream_t s);

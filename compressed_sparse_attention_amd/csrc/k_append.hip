@@ -151,7 +151,9 @@ __global__ __launch_bounds__(256) void k_compress(const float* __restrict__ c_to
 // Indexer-K projection (reading note "DeepSeek V4.1 Flash: Pushing the Limits
 // of KV Cache Compression", configuration section: indexer K is projected
 // directly from the main KV; the report, section 2.4.4: indexer keys in
-// MXFP4).  y = x W over the entry's 512 channels, each output the fp32
+// MXFP4).  y = x W over the entry's 512 channels (after RoPE: with the
+// entry's angles cs, x is the entry before RoPE and its channels 448..511 are
+// turned on the way into LDS exactly as the append turns them), each output the fp32
 // multiply-add chain in ascending channel order (the order the results are
 // defined in), then E2M1 codes with the OCP MX scale 2^(floor(log2 amax) - 2)
 // per row (KF 0) or per 32 channels (KF 1).  64 entries a workgroup; thread t
@@ -161,9 +163,10 @@ __global__ __launch_bounds__(256) void k_compress(const float* __restrict__ c_to
 // entries) and that slice of W are staged in LDS: three 16-byte reads feed 32
 // multiply-adds.
 template <int KF>
-__global__ __launch_bounds__(256) void k_index_k_project(const float* __restrict__ x, const float* __restrict__ W,
-                                                         const int64_t* __restrict__ dst, int64_t n, int64_t rows,
-                                                         uint8_t* __restrict__ k_fp4, uint8_t* __restrict__ k_sc) {
+__global__ __launch_bounds__(256) void k_index_k_project(const float* __restrict__ x, const float* __restrict__ cs,
+                                                         const float* __restrict__ W, const int64_t* __restrict__ dst,
+                                                         int64_t n, int64_t rows, uint8_t* __restrict__ k_fp4,
+                                                         uint8_t* __restrict__ k_sc) {
     __shared__ __attribute__((aligned(16))) float xs[64][64 + 4];  // [channel][entry], padded rows
     __shared__ __attribute__((aligned(16))) float ws[64][128];
     const int t = threadIdx.x;
@@ -178,8 +181,16 @@ __global__ __launch_bounds__(256) void k_index_k_project(const float* __restrict
         __syncthreads();  // the previous step's tiles are consumed
         for (int i = t; i < 64 * 16; i += 256) {  // 64 entries x 16 float4 of this step's channels
             const int el = i >> 4, c4 = i & 15;
-            const float4 v = e0 + el < n ? reinterpret_cast<const float4*>(x + (e0 + el) * 512 + 64 * kt)[c4]
-                                         : float4{0.f, 0.f, 0.f, 0.f};
+            float4 v = e0 + el < n ? reinterpret_cast<const float4*>(x + (e0 + el) * 512 + 64 * kt)[c4]
+                                   : float4{0.f, 0.f, 0.f, 0.f};
+            if (kt == 7 && cs != nullptr && e0 + el < n) {
+                // channels 448 + 4 c4 .. + 3 are pairs 2 c4 and 2 c4 + 1, turned
+                // as the append turns them: rounded products, then one rounded
+                // difference or sum (no fused multiply-add)
+#pragma clang fp contract(off)
+                const float4 a = reinterpret_cast<const float4*>(cs + (e0 + el) * 64)[c4];  // cos, sin, cos, sin
+                v = float4{v.x * a.x - v.y * a.y, v.x * a.y + v.y * a.x, v.z * a.z - v.w * a.w, v.z * a.w + v.w * a.z};
+            }
             xs[4 * c4 + 0][el] = v.x;
             xs[4 * c4 + 1][el] = v.y;
             xs[4 * c4 + 2][el] = v.z;
@@ -286,13 +297,13 @@ hipError_t launch_rope_cast(int64_t n_rows, int heads, const float* in, const fl
     return hipGetLastError();
 }
 
-hipError_t launch_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst, int64_t rows,
-                                  int mx, uint8_t* k_fp4, uint8_t* k_sc, hipStream_t s) {
+hipError_t launch_index_k_project(int64_t n, const float* x, const float* cs, const float* W, const int64_t* dst,
+                                  int64_t rows, int mx, uint8_t* k_fp4, uint8_t* k_sc, hipStream_t s) {
     const dim3 grid((unsigned)((n + 63) / 64));
     if (mx)
-        hipLaunchKernelGGL(k_index_k_project<1>, grid, dim3(256), 0, s, x, W, dst, n, rows, k_fp4, k_sc);
+        hipLaunchKernelGGL(k_index_k_project<1>, grid, dim3(256), 0, s, x, cs, W, dst, n, rows, k_fp4, k_sc);
     else
-        hipLaunchKernelGGL(k_index_k_project<0>, grid, dim3(256), 0, s, x, W, dst, n, rows, k_fp4, k_sc);
+        hipLaunchKernelGGL(k_index_k_project<0>, grid, dim3(256), 0, s, x, cs, W, dst, n, rows, k_fp4, k_sc);
     return hipGetLastError();
 }
 

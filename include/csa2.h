@@ -202,15 +202,21 @@ CSA2_API csa2_status csa2_rope_cast(int64_t n_rows, int32_t heads, const float* 
  *   row (q_fmt CSA2_Q_FP4 or CSA2_Q_FP8: k_sc [rows] u8) or over each 32
  *   channels (CSA2_Q_MXFP4: k_sc [rows][4] u8).
  * x: [n][512] f32 (device, 16-byte aligned), the entries' main KV before
- *   quantisation (after RoPE, as csa2_kv_append rotates it).
+ *   quantisation: after RoPE when rope_cs is NULL; before RoPE (the rows
+ *   csa2_compress writes and csa2_kv_append takes) when rope_cs is given.
+ * rope_cs: NULL, or [n][32][2] f32 (device, 16-byte aligned), the angles
+ *   csa2_kv_append takes for the same entries; channels 448..511 of x are
+ *   then turned first exactly as csa2_kv_append turns them (pair p =
+ *   (448 + 2p, 449 + 2p), rounded products, no fused multiply-add).
  * W: [512][128] f32 (device, 16-byte aligned).
  * dst_row: [n] i64 (device); rows outside [0, n_rows) are skipped.
  * k_fp4: [n_rows][64] u8 (device, 16-byte aligned).
- * Errors: n < 0, an unknown q_fmt, a NULL or misaligned pointer or
- * n_rows < 1 with n > 0: CSA2_ERR_INVALID_ARG.  n == 0 does nothing. */
-CSA2_API csa2_status csa2_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst_row,
-                                          int64_t n_rows, int32_t q_fmt, uint8_t* k_fp4, uint8_t* k_sc,
-                                          hipStream_t stream);
+ * Errors: n < 0, an unknown q_fmt, a NULL pointer (rope_cs aside), a
+ * misaligned pointer or n_rows < 1 with n > 0: CSA2_ERR_INVALID_ARG.  n == 0
+ * does nothing. */
+CSA2_API csa2_status csa2_index_k_project(int64_t n, const float* x, const float* rope_cs, const float* W,
+                                          const int64_t* dst_row, int64_t n_rows, int32_t q_fmt, uint8_t* k_fp4,
+                                          uint8_t* k_sc, hipStream_t stream);
 
 /* ---- compressor -----------------------------------------------------------
  * The CSA2 compressor: m consecutive tokens become one global entry.  The

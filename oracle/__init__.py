@@ -69,7 +69,7 @@ def lib():
         L.orc_compress.restype = i32
         L.orc_rope_cast.argtypes = [i64, i32, vp, vp, i32, vp]
         L.orc_rope_cast.restype = i32
-        L.orc_index_k_project.argtypes = [i64, vp, vp, vp, i32, i64, vp, vp, vp]
+        L.orc_index_k_project.argtypes = [i64, vp, vp, vp, vp, i32, i64, vp, vp, vp]
         L.orc_index_k_project.restype = i32
         L.orc_topk.argtypes = [i64, vp, i64, vp, vp, i64, i32, vp, i32]
         L.orc_block_pool.argtypes = [i64, vp, i64, vp, i32, i32, vp, vp, vp, i32]
@@ -120,15 +120,18 @@ def row_visible(wl):
 
 # --- steps ------------------------------------------------------------------
 
-def index_k_project(x, W, dst, k_fmt, rows, want_y=False):
+def index_k_project(x, W, dst, k_fmt, rows, want_y=False, cs=None):
     """Indexer K from main-KV entries: y = x W (fp32 multiply-add chain over
     the 512 channels, ascending), then E2M1 with one E8M0 per row (k_fmt 0)
-    or per 32 channels (k_fmt 1), into rows dst of a [rows][64] cache."""
+    or per 32 channels (k_fmt 1), into rows dst of a [rows][64] cache.  x is
+    the entry after RoPE, or before it when its angles cs [n][32][2] are
+    given (then turned first, as kv_append turns it)."""
     x, W, dst = _c(x, np.float32), _c(W, np.float32), _c(dst, np.int64)
+    cs = None if cs is None else _c(cs, np.float32)
     k_fp4 = np.zeros((rows, 64), np.uint8)
     k_sc = np.zeros((rows, 4) if k_fmt == 1 else (rows,), np.uint8)
     y = np.zeros((len(dst), 128), np.float32) if want_y else None
-    if lib().orc_index_k_project(len(dst), _p(x), _p(W), _p(dst), k_fmt, rows, _p(k_fp4), _p(k_sc), _p(y)):
+    if lib().orc_index_k_project(len(dst), _p(x), _p(cs), _p(W), _p(dst), k_fmt, rows, _p(k_fp4), _p(k_sc), _p(y)):
         raise ValueError("index_k_project: bad format or destination row")
     return (k_fp4, k_sc, y) if want_y else (k_fp4, k_sc)
 

@@ -572,6 +572,19 @@ static uint8_t e4m3_rne_pos(float q) { /* q >= 0; codes 0..126 (126 = 448) */
 
 static int floor_log2_f(float a) { int e; frexpf(a, &e); return e - 1; }
 
+/* RoPE on one latent v[512] in place: pair i = (448 + 2i, 449 + 2i) turned by
+ * cs_e[2i] = cos, cs_e[2i + 1] = sin of its angle, each product rounded to
+ * fp32 on its own, then one rounded difference or sum. */
+static void rope_latent(float* v, const float* cs_e) {
+    for (int i = 0; i < 32; ++i) {
+        float a = v[448 + 2 * i], b = v[449 + 2 * i];
+        float co = cs_e[2 * i], si = cs_e[2 * i + 1];
+        float ac = a * co, bs = b * si, as = a * si, bc = b * co;
+        v[448 + 2 * i] = ac - bs;
+        v[449 + 2 * i] = as + bc;
+    }
+}
+
 /* Append n entries: x [n][512] fp32 latents before RoPE, cs [n][32][2] the
  * cos and sin of each pair's angle, dst [n] the cache row of each entry.
  * Writes kv_fp4 [rows][256] and kv_sc [rows][16] (kv_fmt 0) or [rows][32]
@@ -583,13 +596,7 @@ int orc_kv_append(int64_t n, const float* x, const float* cs, const int64_t* dst
         if (dst[e] < 0 || dst[e] >= rows) return 1;
         float v[512];
         for (int c = 0; c < 512; ++c) v[c] = x[e * 512 + c];
-        for (int i = 0; i < 32; ++i) {
-            float a = v[448 + 2 * i], b = v[449 + 2 * i];
-            float co = cs[(e * 32 + i) * 2], si = cs[(e * 32 + i) * 2 + 1];
-            float ac = a * co, bs = b * si, as = a * si, bc = b * co;
-            v[448 + 2 * i] = ac - bs;
-            v[449 + 2 * i] = as + bc;
-        }
+        rope_latent(v, cs + e * 64);
         uint8_t* codes = kv_fp4 + dst[e] * 256;
         int bl = kv_fmt == 1 ? 16 : 32;
         for (int b0 = 0; b0 < 512; b0 += bl) {
@@ -647,22 +654,28 @@ int orc_compress(int64_t n_entries, int m, const float* c_tok, const float* z_to
 /* Limits of KV Cache Compression", configuration section: indexer K is      */
 /* projected directly from the main KV; [R] 2.4.4: indexer keys in MXFP4).   */
 /* Readings: y[o] = sum_k x[k] W[k][o] over the 512 channels of the entry as */
-/* stored before quantisation, evaluated as the fp32 chain acc = +0;         */
+/* stored before quantisation (after RoPE: when cs is given, x is the entry  */
+/* before RoPE and is first turned as the append turns it), evaluated as the */
+/* fp32 chain acc = +0;                                                      */
 /* acc = fmaf(x[k], W[k][o], acc) for k ascending (a convention, like the    */
 /* head sum); then E2M1 codes with the OCP MX scale 2^(floor(log2 amax) - 2) */
 /* (at least 2^-127; 1 for an all-zero block) per row (k_fmt 0: the default  */
 /* layout, one E8M0 per row) or per 32 channels (k_fmt 1: MXFP4), to nearest */
 /* even, saturating at 6.                                                    */
 /* ------------------------------------------------------------------------ */
-int orc_index_k_project(int64_t n, const float* x, const float* W, const int64_t* dst, int k_fmt, int64_t rows,
-                        uint8_t* k_fp4, uint8_t* k_sc, float* y_out /* [n][128] or NULL */) {
+int orc_index_k_project(int64_t n, const float* x, const float* cs /* [n][32][2] or NULL */, const float* W,
+                        const int64_t* dst, int k_fmt, int64_t rows, uint8_t* k_fp4, uint8_t* k_sc,
+                        float* y_out /* [n][128] or NULL */) {
     if (k_fmt != 0 && k_fmt != 1) return 1;
     for (int64_t e = 0; e < n; ++e) {
         if (dst[e] < 0 || dst[e] >= rows) return 1;
+        float v[512];
+        for (int c = 0; c < 512; ++c) v[c] = x[e * 512 + c];
+        if (cs) rope_latent(v, cs + e * 64);
         float y[128];
         for (int o = 0; o < 128; ++o) {
             float acc = 0.0f;
-            for (int k = 0; k < 512; ++k) acc = fmaf(x[e * 512 + k], W[k * 128 + o], acc);
+            for (int k = 0; k < 512; ++k) acc = fmaf(v[k], W[k * 128 + o], acc);
             y[o] = acc;
             if (y_out) y_out[e * 128 + o] = acc;
         }

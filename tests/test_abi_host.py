@@ -227,8 +227,8 @@ def test_compress_validation():
 def test_index_k_project_validation():
     L = C.lib()
 
-    def proj(n=4, x=FAKE, W=FAKE, dst=FAKE, rows=8, fmt=C.CSA2_Q_MXFP4, kf=FAKE, ks=FAKE):
-        return L.csa2_index_k_project(n, x, W, dst, rows, fmt, kf, ks, None)
+    def proj(n=4, x=FAKE, cs=None, W=FAKE, dst=FAKE, rows=8, fmt=C.CSA2_Q_MXFP4, kf=FAKE, ks=FAKE):
+        return L.csa2_index_k_project(n, x, cs, W, dst, rows, fmt, kf, ks, None)
 
     assert proj(n=-1) == C.CSA2_ERR_INVALID_ARG
     assert proj(fmt=5) == C.CSA2_ERR_INVALID_ARG
@@ -236,6 +236,7 @@ def test_index_k_project_validation():
     assert proj(W=None) == C.CSA2_ERR_INVALID_ARG
     assert proj(rows=0) == C.CSA2_ERR_INVALID_ARG
     assert proj(W=FAKE + 4) == C.CSA2_ERR_INVALID_ARG
+    assert proj(cs=FAKE + 8) == C.CSA2_ERR_INVALID_ARG
 
 
 def test_rope_cast_validation():

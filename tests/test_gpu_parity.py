@@ -564,6 +564,74 @@ def test_kv_append_bitwise(kv_fmt, n):
         assert not kv2.cpu().numpy()[dst[1]].any()
 
 
+COMPOSE_CASES = {
+    "default": dict(),
+    # the report's formats: E4M3/16 main KV, MXFP4 indexer K and queries, 32 heads
+    "pages": dict(kv_fmt=1, q_fmt=synth.Q_MXFP4, H=32),
+}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", list(COMPOSE_CASES))
+def test_write_path_feeds_the_chain(case):
+    """The write path composed and read back: tokens -> csa2_compress (m = 2)
+    -> csa2_kv_append and csa2_index_k_project, both from the entries before
+    RoPE with the same angles -> the caches one encoder group (Full, Reuse,
+    Reindex) scores, selects and attends over.  Each channel's compression
+    weights are equal over its two tokens or leave one token's weight below
+    float32's range, so the compressor is exact on both sides; the caches then
+    equal the oracle's bit for bit, and the chain run on the GPU-written caches
+    equals the oracle's chain on its own (indices exact, attention within the
+    attention tolerance)."""
+    kw = COMPOSE_CASES[case]
+    wl = synth.make_workload("compose", 13, [700, 2500], 3, [(2, synth.MODE_FULL, False),
+                                                             (3, synth.MODE_REUSE, False),
+                                                             (4, synth.MODE_REINDEX, False)],
+                             ratio=2, Hm=16, q_pos=[np.array([1390, 1395, 1399]), np.array([4000, 4990, 4999])],
+                             **kw)
+    n, m = int(wl.entry_off[-1]), 2
+    rng = np.random.default_rng(77 + len(case))
+    c_tok = (rng.standard_normal((n * m, 512)) * rng.choice([0.05, 1.0, 8.0], size=(n * m, 1))).astype(np.float32)
+    z_tok = np.zeros((n, m, 512), np.float32)
+    pick = rng.integers(0, 3, size=(n, 512))  # 0: equal weights, 1 or 2: that token alone
+    z_tok[:, 0][pick == 1] = 200.0
+    z_tok[:, 1][pick == 2] = 200.0
+    z_tok = z_tok.reshape(n * m, 512)
+    th = rng.uniform(-np.pi, np.pi, size=(n, 32))
+    cs = np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
+    W = (rng.standard_normal((512, 128)) * 0.05).astype(np.float32)
+    dst = np.arange(n, dtype=np.int64)
+    kv_fmt = getattr(wl, "kv_fmt", 0)
+    k_fmt = 1 if kw.get("q_fmt") == synth.Q_MXFP4 else 0
+
+    x = C.csa2_compress(dev(c_tok), dev(z_tok), m)
+    kv = torch.zeros(wl.kv.shape, dtype=torch.uint8, device="cuda")
+    kv_sc = torch.zeros(wl.kv_sc.shape, dtype=torch.uint8, device="cuda")
+    k_idx = torch.zeros(wl.k_idx.shape, dtype=torch.uint8, device="cuda")
+    k_sc = torch.zeros(wl.k_sc.shape, dtype=torch.uint8, device="cuda")
+    C.csa2_kv_append(x, dev(cs), dev(dst), kv, kv_sc, kv_fmt=kv_fmt)
+    C.csa2_index_k_project(x, dev(W), dev(dst), k_idx, k_sc, q_fmt=kw.get("q_fmt", synth.Q_FP4), rope_cs=dev(cs))
+
+    xr = oracle.compress(c_tok, z_tok, m)
+    assert np.array_equal(x.cpu().numpy(), xr)
+    ref_kv, ref_kv_sc = oracle.kv_append(xr, cs, dst, kv_fmt, n)
+    ref_k, ref_k_sc = oracle.index_k_project(xr, W, dst, k_fmt, n, cs=cs)
+    for got, want, what in ((kv, ref_kv, "kv"), (kv_sc, ref_kv_sc, "kv_sc"), (k_idx, ref_k, "k_idx"),
+                            (k_sc, ref_k_sc, "k_sc")):
+        assert np.array_equal(got.cpu().numpy(), want.reshape(got.shape)), what
+
+    wl.kv, wl.kv_sc, wl.k_idx, wl.k_sc = ref_kv, ref_kv_sc, ref_k, ref_k_sc.reshape(wl.k_sc.shape)
+    dw = DevWorkload(wl)
+    dw.kv, dw.kv_sc, dw.k_idx, dw.k_sc = kv, kv_sc, k_idx, k_sc  # the chain reads what the GPU wrote
+    outs, _, _ = run_chain(dw)
+    torch.cuda.synchronize()
+    ref = oracle.layer_chain(wl)
+    for o, r in zip(outs, ref):
+        assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"layer {r['layer']} indices"
+        assert_close_attn(o["out"].cpu().numpy(), r["out"], f"layer {r['layer']}")
+        np.testing.assert_allclose(o["lse"].cpu().numpy(), r["lse"], rtol=1e-4, atol=1e-4)
+
+
 @pytest.mark.parametrize("m,n", [(1, 7), (2, 1), (2, 4099), (4, 300), (2, 131072)])
 def test_compress_tolerance(m, n):
     """The compressor against the oracle (float64), within a bound derived
@@ -583,14 +651,16 @@ def test_compress_tolerance(m, n):
     assert np.all(np.abs(got.astype(np.float64) - ref) <= 2e-6 * mag + 1e-30)
 
 
+@pytest.mark.parametrize("rope", [False, True])
 @pytest.mark.parametrize("q_fmt", [synth.Q_FP4, synth.Q_MXFP4])
 @pytest.mark.parametrize("n", [1, 17, 5000, 131072])
-def test_index_k_project_bitwise(q_fmt, n):
+def test_index_k_project_bitwise(q_fmt, n, rope):
     """The indexer-K projection equals the oracle bit for bit (same float32
-    multiply-add chain, same quantiser), rows written out of order.  At
-    131,072 entries (one source layer of the prefill context) the GPU writes
-    every row and the oracle checks 3,000 sampled ones."""
-    rng = np.random.default_rng(4000 + n + q_fmt)
+    multiply-add chain, same quantiser), rows written out of order, from the
+    entry after RoPE or, given its angles, before it.  At 131,072 entries (one
+    source layer of the prefill context) the GPU writes every row and the
+    oracle checks 3,000 sampled ones."""
+    rng = np.random.default_rng(4000 + n + q_fmt + 7 * rope)
     x = rng.standard_normal((n, 512), dtype=np.float32) * np.float32(3.0)
     if n >= 17:
         x[5] = 0.0  # an all-zero row: scale 2^0, codes 0
@@ -599,11 +669,15 @@ def test_index_k_project_bitwise(q_fmt, n):
     dst = rng.permutation(rows)[:n].astype(np.int64)
     kf = torch.full((rows, 64), 0xAB, dtype=torch.uint8, device="cuda")
     ks = torch.full((rows, 4) if q_fmt == synth.Q_MXFP4 else (rows,), 0xCD, dtype=torch.uint8, device="cuda")
-    C.csa2_index_k_project(dev(x), dev(W), dev(dst), kf, ks, q_fmt=q_fmt)
+    cs = None
+    if rope:
+        th = rng.uniform(-np.pi, np.pi, size=(n, 32))
+        cs = np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
+    C.csa2_index_k_project(dev(x), dev(W), dev(dst), kf, ks, q_fmt=q_fmt, rope_cs=dev(cs))
     torch.cuda.synchronize()
     k_fmt = 1 if q_fmt == synth.Q_MXFP4 else 0
     sel = np.arange(n) if n <= 5000 else np.sort(rng.choice(n, 3000, replace=False))
-    ref_f, ref_s = oracle.index_k_project(x[sel], W, dst[sel], k_fmt, rows)
+    ref_f, ref_s = oracle.index_k_project(x[sel], W, dst[sel], k_fmt, rows, cs=None if cs is None else cs[sel])
     got_f, got_s = kf.cpu().numpy(), ks.cpu().numpy()
     assert np.array_equal(got_f[dst[sel]], ref_f[dst[sel]])
     assert np.array_equal(got_s[dst[sel]], ref_s[dst[sel]])

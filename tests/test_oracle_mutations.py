@@ -39,6 +39,8 @@ MUTATIONS = [
      "rope"),
     ("mx_flag_dropped", "        if (total >= (1LL << 24)) ((score_ctx*)c)->status = 2;\n        float d = (float)ldexp((double)dot, emin - 2);",
      "        float d = (float)ldexp((double)dot, emin - 2);", "cancel"),
+    ("rope_sin_sign", "v[448 + 2 * i] = ac - bs;", "v[448 + 2 * i] = ac + bs;", "kv_append"),
+    ("projection_rope_dropped", "if (cs) rope_latent(v, cs + e * 64);", "", "index_k_project"),
 ]
 
 

@@ -982,6 +982,54 @@ def test_index_k_project_chain_order():
         assert y[0, o] == float(acc), o
 
 
+@pytest.mark.parametrize("k_fmt", [0, 1])
+def test_index_k_project_rotates_like_the_append(k_fmt):
+    """With the entry's angles the projection takes the entry before RoPE.
+    The identity angle changes nothing; a quarter turn maps (a, b) to (-b, a)
+    exactly, so it equals the projection of the pre-turned x; for any angle,
+    a selection matrix that reads rotated channels gives 2^s times each
+    rotated value, within the rounding of two products and a sum of the
+    float64 rotation (a swapped cos and sin, a wrong sign or a wrong pair
+    would miss by order 1)."""
+    rng = np.random.default_rng(33)
+    n = 6
+    x = rng.standard_normal((n, 512)).astype(np.float32)
+    W = (rng.standard_normal((512, 128)) * 0.05).astype(np.float32)
+    dst = np.array([3, 0, 5, 1, 4, 2])
+    ident = np.zeros((n, 32, 2), np.float32)
+    ident[..., 0] = 1.0
+    quarter = np.zeros((n, 32, 2), np.float32)
+    quarter[..., 1] = 1.0
+    xt = x.copy()
+    xt[:, 448::2], xt[:, 449::2] = -x[:, 449::2], x[:, 448::2]
+    plain = oracle.index_k_project(x, W, dst, k_fmt, n, want_y=True)
+    for got, want in zip(oracle.index_k_project(x, W, dst, k_fmt, n, want_y=True, cs=ident), plain):
+        assert np.array_equal(got, want)
+    turned = oracle.index_k_project(xt, W, dst, k_fmt, n, want_y=True)
+    for got, want in zip(oracle.index_k_project(x, W, dst, k_fmt, n, want_y=True, cs=quarter), turned):
+        assert np.array_equal(got, want)
+    assert not np.array_equal(turned[2], plain[2])
+    cs = _angles(rng, n)
+    Ws = np.zeros((512, 128), np.float32)
+    pick = 448 + rng.permutation(64)
+    sh = rng.integers(-2, 3, size=64)
+    Ws[pick, np.arange(64)] = np.exp2(sh).astype(np.float32)
+    Ws[np.arange(64), 64 + np.arange(64)] = 1.0  # unrotated channels pass through
+    _, _, y = oracle.index_k_project(x, Ws, dst, k_fmt, n, want_y=True, cs=cs)
+    rot = x.astype(np.float64).copy()
+    co, si = cs[..., 0].astype(np.float64), cs[..., 1].astype(np.float64)
+    p, q = x[:, 448::2].astype(np.float64), x[:, 449::2].astype(np.float64)
+    rot[:, 448::2], rot[:, 449::2] = p * co - q * si, p * si + q * co
+    mag = np.empty_like(rot)
+    mag[:, 448::2], mag[:, 449::2] = np.abs(p * co) + np.abs(q * si), np.abs(p * si) + np.abs(q * co)
+    want = rot[:, pick] * np.exp2(sh)
+    # two rounded products and their rounded sum: at most 2^-24 of each
+    # product's magnitude plus half an ulp of the result, here doubled
+    bound = (mag[:, pick] * 2.0 ** -23 + np.abs(rot[:, pick]) * 2.0 ** -23) * np.exp2(sh)
+    assert np.all(np.abs(y[:, :64] - want) <= bound)
+    assert np.array_equal(y[:, 64:], x[:, :64])
+
+
 # ---------------------------------------------------------------------------
 # RoPE and cast around attention
 # ---------------------------------------------------------------------------
