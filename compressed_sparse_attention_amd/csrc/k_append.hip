@@ -179,25 +179,43 @@ __global__ __launch_bounds__(256) void k_index_k_project(const float* __restrict
         for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
     for (int kt = 0; kt < 8; ++kt) {
         __syncthreads();  // the previous step's tiles are consumed
-        for (int i = t; i < 64 * 16; i += 256) {  // 64 entries x 16 float4 of this step's channels
-            const int el = i >> 4, c4 = i & 15;
-            float4 v = e0 + el < n ? reinterpret_cast<const float4*>(x + (e0 + el) * 512 + 64 * kt)[c4]
-                                   : float4{0.f, 0.f, 0.f, 0.f};
-            if (kt == 7 && cs != nullptr && e0 + el < n) {
-                // channels 448 + 4 c4 .. + 3 are pairs 2 c4 and 2 c4 + 1, turned
-                // as the append turns them: rounded products, then one rounded
-                // difference or sum (no fused multiply-add)
-#pragma clang fp contract(off)
-                const float4 a = reinterpret_cast<const float4*>(cs + (e0 + el) * 64)[c4];  // cos, sin, cos, sin
-                v = float4{v.x * a.x - v.y * a.y, v.x * a.y + v.y * a.x, v.z * a.z - v.w * a.w, v.z * a.w + v.w * a.z};
-            }
-            xs[4 * c4 + 0][el] = v.x;
-            xs[4 * c4 + 1][el] = v.y;
-            xs[4 * c4 + 2][el] = v.z;
-            xs[4 * c4 + 3][el] = v.w;
+        // 64 entries x 16 float4 of this step's channels: thread t takes float4
+        // c4 = t % 16 of entries t / 16 + 16 u.  Entries past n re-read entry
+        // n - 1 (their outputs are not stored), so that every load is
+        // unconditional and all are issued before the first is used.
+        const int c4 = t & 15;
+        float4 v[4];
+        int64_t e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t eu = e0 + (t >> 4) + 16 * u;
+            e[u] = eu < n ? eu : n - 1;
+            v[u] = reinterpret_cast<const float4*>(x + e[u] * 512 + 64 * kt)[c4];
         }
-        for (int i = t; i < 64 * 32; i += 256) {  // 64 rows of W, 32 float4 each
-            const int kr = i >> 5, c4 = i & 31;
+        if (kt == 7 && cs != nullptr) {
+            // channels 448 + 4 c4 .. + 3 are pairs 2 c4 and 2 c4 + 1, turned as
+            // the append turns them: rounded products, then one rounded
+            // difference or sum (no fused multiply-add)
+#pragma clang fp contract(off)
+            float4 a[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a[u] = reinterpret_cast<const float4*>(cs + e[u] * 64)[c4];  // cos, sin, cos, sin
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = float4{v[u].x * a[u].x - v[u].y * a[u].y, v[u].x * a[u].y + v[u].y * a[u].x,
+                              v[u].z * a[u].z - v[u].w * a[u].w, v[u].z * a[u].w + v[u].w * a[u].z};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int el = (t >> 4) + 16 * u;
+            xs[4 * c4 + 0][el] = v[u].x;
+            xs[4 * c4 + 1][el] = v[u].y;
+            xs[4 * c4 + 2][el] = v[u].z;
+            xs[4 * c4 + 3][el] = v[u].w;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {  // 64 rows of W, 32 float4 each
+            const int i = t + 256 * u, kr = i >> 5, c4 = i & 31;
             reinterpret_cast<float4*>(&ws[kr][0])[c4] = reinterpret_cast<const float4*>(W + (int64_t)(64 * kt + kr) * 128)[c4];
         }
         __syncthreads();

@@ -439,8 +439,11 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ 
         uint32_t bs[2];  // with MX: the four block scales of column 32nt + li
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
+            // the list reads are unconditional (clamped to the chunk) so that
+            // they are issued together instead of one branch at a time
             const int s = p0 + 32 * nt + li;
-            int64_t j = s < s1 ? (int64_t)crow[s] : -1;
+            const int32_t cj = crow[s < s1 ? s : s1 - 1];
+            int64_t j = s < s1 ? (int64_t)cj : -1;
             j = (j >= 0 && j < vis) ? j : 0;
             const uint8_t* kr = k + (e0 + j) * 64 + 32 * g;
             B[nt][0] = widen(ld16(kr));
@@ -448,9 +451,14 @@ __global__ __launch_bounds__(256) void k_score_cand(const uint8_t* __restrict__ 
             if constexpr (MX) bs[nt] = *reinterpret_cast<const uint32_t*>(k_sc + (e0 + j) * 4);
         }
         const int sl = p0 + lane;
-        const int64_t jl = sl < s1 ? (int64_t)crow[sl] : -1;
+        const int32_t cl = crow[sl < s1 ? sl : s1 - 1];
+        const int64_t jl = sl < s1 ? (int64_t)cl : -1;
         const bool ok = jl >= 0 && jl < vis;
-        const int ek = (!MX && ok) ? (int)k_sc[e0 + jl] : 127;
+        int ek = 127;
+        if constexpr (!MX) {
+            const int e = (int)k_sc[e0 + (ok ? jl : 0)];  // vis > 0: entry 0 exists
+            ek = ok ? e : 127;
+        }
         v16f acc[NMT][2];
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)

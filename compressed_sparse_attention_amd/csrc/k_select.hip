@@ -114,12 +114,20 @@ __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ score
     if (s0 >= n && blockIdx.x != 0) return;
     const float* sr = scores + (int64_t)row * stride;
     const int64_t s1 = s0 + kHChunk < n ? s0 + kHChunk : n;
-    // issue this thread's loads before the threshold search
+    // issue this thread's loads before the threshold search, all of them
+    // unconditionally (a slot past the chunk re-reads its last slot, and every
+    // use below checks s < s1): a load whose value is used under a per-lane
+    // condition is moved into a branch by the compiler and waited for alone
     uint32_t key[kHChunk / 256];
+    if (s1 > s0) {
 #pragma unroll
-    for (int u = 0; u < kHChunk / 256; ++u) {
-        const int64_t s = s0 + threadIdx.x + 256 * u;
-        key[u] = s < s1 ? score_key(sr[s]) : 0u;
+        for (int u = 0; u < kHChunk / 256; ++u) {
+            const int64_t s = s0 + threadIdx.x + 256 * u;
+            key[u] = score_key(sr[s < s1 ? s : s1 - 1]);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kHChunk / 256; ++u) key[u] = 0u;
     }
     if (threadIdx.x == 0) lcount = 0;
     const uint32_t kk = (uint32_t)(n < K ? n : K);
@@ -1083,8 +1091,10 @@ __global__ __launch_bounds__(1024) void k_topk_rows(const float* __restrict__ sc
     uint32_t key[kRowPer];
 #pragma unroll
     for (int u = 0; u < kRowPer; ++u) {
+        // unconditional loads (n >= 1 here; a slot past n re-reads slot n - 1
+        // and every use checks valid(u)), so that they are issued together
         const int64_t e = tid + 1024 * u;
-        key[u] = e < n ? score_key(sr[e]) : 0u;
+        key[u] = score_key(sr[e < n ? e : n - 1]);
     }
     auto valid = [&](int u) { return (int64_t)tid + 1024 * u < n; };
     if (tid == 0) {
