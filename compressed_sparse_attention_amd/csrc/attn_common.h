@@ -82,61 +82,85 @@ __device__ __forceinline__ float xor_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// 8 query channels c0 .. c0+7 (c0 a multiple of 8) of a head row as the bf16
-// MFMA operand, read from bf16.  ROPE: the query is before RoPE; the channels
-// from 448 on are widened to f32, rotated by the row's angles and cast back to
-// nearest even, and every other channel goes through the same cast (which
-// leaves a bf16 value as it is, except that a NaN gets its quiet bit set).
+// A lane's 16 query slices of a head row as bf16 MFMA operands: slice ks holds
+// channels c0 = 32 ks + 8 lg .. c0 + 7 (lg = 0..3, the lane's group), read from
+// bf16 at q + qr + 32 ks.  ROPE: the query is before RoPE; the channels from
+// 448 on (slices 14 and 15, whatever lg) are widened to f32, rotated by the
+// row's angles cs and cast back to nearest even, and every other channel goes
+// through the same cast (which leaves a bf16 value as it is, except that a NaN
+// gets its quiet bit set).  All loads are issued before the first is used.
 template <int ROPE>
-__device__ __forceinline__ v8bf load_q8(const uint16_t* q, int64_t off, int c0, const float* cs) {
-    v4i w = ld16(q + off);
+__device__ __forceinline__ void load_q16(v8bf (&Q)[16], const uint16_t* q, int64_t qr, int lg, const float* cs) {
+    v4i w[16];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) w[ks] = ld16(q + qr + 32 * ks);
     if constexpr (ROPE) {
-        if (c0 >= 448) {
-            float f[8];
+        v4f c[2][2];  // slices 14 and 15: pairs 4 lg .. 4 lg + 3 and 16 + 4 lg .. + 3
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                f[2 * k] = __uint_as_float((uint32_t)w[k] << 16);
-                f[2 * k + 1] = __uint_as_float((uint32_t)w[k] & 0xFFFF0000u);
-            }
-            const float* c = cs + (c0 - 448);  // pairs p0 .. p0 + 3, two floats each
-            const v4f a = *reinterpret_cast<const v4f*>(c), b = *reinterpret_cast<const v4f*>(c + 4);
-            rope_pair(f[0], f[1], a[0], a[1], 1.0f);
-            rope_pair(f[2], f[3], a[2], a[3], 1.0f);
-            rope_pair(f[4], f[5], b[0], b[1], 1.0f);
-            rope_pair(f[6], f[7], b[2], b[3], 1.0f);
+        for (int j = 0; j < 2; ++j) {
+            const float* p = cs + 32 * j + 8 * lg;
+            c[j][0] = *reinterpret_cast<const v4f*>(p);
+            c[j][1] = *reinterpret_cast<const v4f*>(p + 4);
+        }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) w[k] = (int)(bf16_rne(f[2 * k]) | (bf16_rne(f[2 * k + 1]) << 16));
-        } else {
-            // per bf16 half: its magnitude plus 0x7F carries into bit 15 exactly
-            // for a NaN (magnitude above 0x7F80); that bit moved to bit 6 is the
-            // quiet bit (the halves cannot carry into each other)
+        for (int ks = 0; ks < 16; ++ks) {
+            if (ks >= 14) {
+                float f[8];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t d = (uint32_t)w[k];
-                w[k] = (int)(d | ((((d & 0x7FFF7FFFu) + 0x007F007Fu) & 0x80008000u) >> 9));
+                for (int k = 0; k < 4; ++k) {
+                    f[2 * k] = __uint_as_float((uint32_t)w[ks][k] << 16);
+                    f[2 * k + 1] = __uint_as_float((uint32_t)w[ks][k] & 0xFFFF0000u);
+                }
+                const v4f a = c[ks - 14][0], b = c[ks - 14][1];
+                rope_pair(f[0], f[1], a[0], a[1], 1.0f);
+                rope_pair(f[2], f[3], a[2], a[3], 1.0f);
+                rope_pair(f[4], f[5], b[0], b[1], 1.0f);
+                rope_pair(f[6], f[7], b[2], b[3], 1.0f);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w[ks][k] = (int)(bf16_rne(f[2 * k]) | (bf16_rne(f[2 * k + 1]) << 16));
+            } else {
+                // per bf16 half: its magnitude plus 0x7F carries into bit 15
+                // exactly for a NaN (magnitude above 0x7F80); that bit moved to
+                // bit 6 is the quiet bit (the halves cannot carry into each other)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t d = (uint32_t)w[ks][k];
+                    w[ks][k] = (int)(d | ((((d & 0x7FFF7FFFu) + 0x007F007Fu) & 0x80008000u) >> 9));
+                }
             }
         }
     }
-    return __builtin_bit_cast(v8bf, w);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) Q[ks] = __builtin_bit_cast(v8bf, w[ks]);
 }
 
 // Final store of output channel c of a head row (value x, this lane's; the
 // partner channel c ^ 1 sits in lane l ^ 1).  ROPE: the channels from 448 on
-// are turned back (the angle negated) and every channel is cast to bf16; the
-// even lane of each pair stores both.  Every lane of the wave calls it.
+// (rot) are turned back by their pair's angle (co, si), negated, and every
+// channel is cast to bf16; the even lane of each pair stores both.  Every lane
+// of the wave calls it.  The angles come in as values, loaded by the caller
+// ahead of the stores, so that no store waits for a load of its own.
 template <int ROPE>
-__device__ __forceinline__ void store_out(void* out, int64_t off, int c, float x, const float* cs) {
+__device__ __forceinline__ void store_out(void* out, int64_t off, int c, float x, bool rot, float2 cs) {
     if constexpr (ROPE) {
         // the partner lane's value by a DPP swap of adjacent lanes (quad_perm 1, 0, 3, 2)
         const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
         if ((c & 1) == 0) {
             float a = x, b = y;
-            if (c >= 448) rope_pair(a, b, cs[c - 448], cs[c - 447], -1.0f);
+            if (rot) rope_pair(a, b, cs.x, cs.y, -1.0f);
             *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + off) = bf16_rne(a) | (bf16_rne(b) << 16);
         }
     } else {
         reinterpret_cast<float*>(out)[off] = x;
     }
+}
+
+// The (cos, sin) of the pairs a lane's output channels 448 + 16 j + li
+// (j < 4, li = lane % 16) belong to: pair (16 j + li) / 2 of the row's angles
+// cs, read at the even channel of the pair.
+__device__ __forceinline__ void load_out_angles(float2 (&a)[4], const float* cs, int li) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const float2*>(cs + 16 * j + (li & ~1));
 }
 
 constexpr int KB = 64;               // keys per block

@@ -113,8 +113,7 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     const float* row_cs = ROPE ? rope_cs + (int64_t)row * 64 : nullptr;
     {
         const int64_t qr = ((int64_t)row * Hm + hq) * 512 + 8 * lg;
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) Q[ks] = load_q8<ROPE>(q, qr + 32 * ks, 32 * ks + 8 * lg, row_cs);
+        load_q16<ROPE>(Q, q, qr, lg, row_cs);
     }
     // keep the loads above ahead of the scalar loads below (they would
     // otherwise wait for them)
@@ -445,12 +444,17 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     float iv[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) iv[v] = __shfl(inv, 4 * lg + v);
+    // channel 128 wave + 16 nt + li is in the rotated part in wave 3 from nt = 4 on
+    float2 ang[4] = {};
+    if constexpr (ROPE)
+        if (wave == 3) load_out_angles(ang, row_cs, li);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             store_out<ROPE>(out, ((int64_t)row * Hm + HG * hg + 4 * lg + v) * 512 + 128 * wave + 16 * nt + li,
-                            128 * wave + 16 * nt + li, O[nt][v] * iv[v], row_cs);
+                            128 * wave + 16 * nt + li, O[nt][v] * iv[v], wave == 3 && nt >= 4,
+                            ang[nt >= 4 ? nt - 4 : 0]);
     if (lse && wave == 0 && lane < 16)
         lse[(int64_t)row * Hm + HG * hg + lane] =
             l_lse > 0.0f ? (m_run + log2f(l_lse)) * 0.69314718055994531f : -INFINITY;

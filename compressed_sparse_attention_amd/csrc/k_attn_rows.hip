@@ -74,8 +74,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_rows(
     const float* row_cs = ROPE ? rope_cs + (int64_t)row * 64 : nullptr;
     {
         const int64_t qr = ((int64_t)row * Hm + h0 + li) * 512 + 8 * lg;
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) Q[ks] = load_q8<ROPE>(q, qr + 32 * ks, 32 * ks + 8 * lg, row_cs);
+        load_q16<ROPE>(Q, q, qr, lg, row_cs);
     }
     asm volatile("" ::: "memory");
 
@@ -293,12 +292,15 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_rows(
     float iv[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) iv[v] = __shfl(inv, 4 * lg + v);
+    // channel 16 nt + li is in the rotated part from nt = 28 on
+    float2 ang[4] = {};
+    if constexpr (ROPE) load_out_angles(ang, row_cs, li);
 #pragma unroll
     for (int nt = 0; nt < 32; ++nt)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             store_out<ROPE>(out, ((int64_t)row * Hm + h0 + 4 * lg + v) * 512 + 16 * nt + li, 16 * nt + li,
-                            O[nt][v] * iv[v], row_cs);
+                            O[nt][v] * iv[v], nt >= 28, ang[nt >= 28 ? nt - 28 : 0]);
     if (lse && lg == 0)
         lse[(int64_t)row * Hm + h0 + li] = l_run > 0.0f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
 }
