@@ -68,6 +68,17 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 __device__ __forceinline__ uint32_t key_bin(uint32_t key) { return key >= 0x80000000u ? (key - 0x80000000u) >> 19 : 0u; }
 __device__ __forceinline__ uint32_t key64_bin(uint64_t x) { return key_bin((uint32_t)(x >> 32)); }
 
+// A workgroup barrier that orders LDS only: the fences cover the local address
+// space, so the barrier waits for this wave's LDS operations but leaves its
+// global loads in flight (a plain __syncthreads() waits for those as well,
+// which defeats a prefetch issued ahead of it).  For kernels whose waves share
+// data through LDS only.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t slot) {
     return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - slot);
 }

@@ -54,8 +54,10 @@ __global__ __launch_bounds__(64) void k_gather_dequant(const uint8_t* __restrict
 // 128w..128w+127) with V read transposed by ds_read_b64_tr_b16.  With two
 // pipes their (max, sums, O) are merged at the end.  The loads of the first
 // iteration (the SWA rows) are issued together with the query and the index
-// row; later blocks are fetched one iteration ahead.  One pipe keeps the LDS
-// of a workgroup at 73 KB, so that two workgroups share a CU; measured, that
+// row; later blocks are fetched one iteration ahead.  The waves share data
+// through LDS only, so their barriers order LDS only and leave the prefetch
+// in flight.  One pipe keeps the LDS of a workgroup at 73 KB, so that two
+// workgroups share a CU; measured, that
 // beats two pipes in one workgroup except on the smallest grids.
 // ---------------------------------------------------------------------------
 constexpr int HG = 16;
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
     };
     if (first_swa) load_swa(vk_first);
     if (tid == 0) nsel_sh = 0;
-    __syncthreads();
+    lds_barrier();
     {
         int last = 0;
 #pragma unroll
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
         }
         if (last) atomicMax(&nsel_sh, last);
     }
-    __syncthreads();
+    lds_barrier();
     const int n_sel = nsel_sh;
     const int n_keys = n_swa + n_sel;
 
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
             if (blk < blk1) stage(blk, false);
             fetch(blk + NPIPE);
         }
-        __syncthreads();
+        lds_barrier();
 
         // 2) S = Q K^T for keys 16*wave .. +16: lane gets S[head 4lg+v][key 16wave + li]
         if (active) {
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
 #pragma unroll
             for (int v = 0; v < 4; ++v) sl[pipe][4 * lg + v][key] = ok ? Sv[v] * scale_log2 : -INFINITY;
         }
-        __syncthreads();
+        lds_barrier();
 
         if (active) {
             // 3) online softmax (base 2) for head li over keys 8lg + 32ks + i
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // merge the pipes: pipe 1 leaves its state in LDS (its key buffer), pipe 0
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(256 * NPIPE) void k_sparse_attn(
                 mls[lane][2] = l_lse;
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (pipe == 1) return;
         {
             const float m1 = mls[li][0];

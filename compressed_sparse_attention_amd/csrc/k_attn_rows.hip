@@ -24,6 +24,7 @@
 //   P V    on the same MFMA: B = V read transposed from LDS
 //          (ds_read_b64_tr_b16) in the same key order, O = 16 heads x 512
 //          channels in registers.
+// The waves share data through LDS only, so their barriers order LDS only.
 // Two workgroups share a CU (75 KB of LDS each), so one stages while the
 // other computes.  Used only where the grid fills the chip without splitting
 // a row's keys: with splits every part writes a 64-head partial (128 KB), and
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_rows(
     const int64_t swa_r0 = swa_row_off[b] + (u_lo - swa_pos0[b]);
 
     if (tid == 0) nsel_sh = 0;
-    __syncthreads();
+    lds_barrier();
     {
         int last = 0;
 #pragma unroll
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_rows(
         }
         if (last) atomicMax(&nsel_sh, last);
     }
-    __syncthreads();
+    lds_barrier();
     const int n_keys = n_swa + nsel_sh;
     const int n_blk = (n_keys + KB - 1) / KB;
 
@@ -198,9 +199,9 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn_rows(
     float m_run = -INFINITY, l_run = 0.0f;
 
     for (int blk = 0; blk < n_blk; ++blk) {
-        if (blk > 0) __syncthreads();  // every wave is done with the previous block
+        if (blk > 0) lds_barrier();  // every wave is done with the previous block
         stage(blk);
-        __syncthreads();
+        lds_barrier();
 
         // S^T = K Q^T: four independent accumulation chains (key tiles)
         v4f S[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
