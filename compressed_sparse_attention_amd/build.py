@@ -23,8 +23,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 # MFMA results in VGPRs: the epilogues read them without v_accvgpr_read copies.
-# Not for the many-row attention, whose 128 accumulator registers per lane
-# live in AGPRs (one wave per SIMD, 512 registers).
+# A source listed in AGPR_SOURCES is compiled without it (none is at present).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 AGPR_SOURCES = set()
 
