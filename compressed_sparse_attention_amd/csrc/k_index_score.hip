@@ -159,6 +159,7 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     __shared__ uint32_t hl[HIST ? TQ * kHistBins / 2 : 1];
     __shared__ __attribute__((aligned(16))) float sl[LOCAL ? TQ : 1][LOCAL ? chunk : 1];  // the chunk's scores per row
     __shared__ uint8_t ekl[MX ? 1 : chunk];                  // the chunk's indexer K scales (one per row)
+    __shared__ float wl[TQ == 4 ? 4 * H : 1];               // the rows' head weights (four-row scan)
     __shared__ uint32_t wtot[4], found[4];
     const int b = blockIdx.y;
     const int64_t e0 = entry_off[b];
@@ -174,6 +175,20 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     if (HIST) {  // before any load is in flight: the barrier costs nothing here
         hist_clear(hl, TQ * kHistBins / 2);
         __syncthreads();
+    }
+    // four rows: thread i < 4H holds weight i % H of row i / H until it is
+    // staged in LDS with the scales below; vis_pr[pr] is the visible count of
+    // this lane's row of pair pr (row 2 pr + lane half)
+    float w_own = 0.0f;
+    int64_t vis_pr[2] = {0, 0};
+    if constexpr (TQ == 4) {
+        const int i = threadIdx.x;
+        if (i < 4 * H && i / H < nq) w_own = w[(int64_t)(r0 + i / H) * H + i % H];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const int qq = 2 * pr + g;
+            vis_pr[pr] = visible_count(n, q_pos[r0 + (qq < nq ? qq : 0)], ratio);
+        }
     }
     // the scales of this wave's positions (position p_w + 256 j + lane), staged
     // in LDS below once the query operands and the first two tiles are in
@@ -199,15 +214,26 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
         vis[t] = visible_count(n, q_pos[row], ratio);
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
-            const uint8_t* qr = q + ((int64_t)row * H + 32 * mt + li) * 64 + 32 * g;
+            // the A row li of slot (t, mt): head 32 mt + li of row t, or with four
+            // rows M-tile m = NMT (t % 2) + mt of the row pair t / 2, whose row li
+            // holds head 16 m + 4 (li / 8) + li % 4 of row 2 (t / 2) + (li / 4) % 2:
+            // the 32x32 product then leaves each lane half the 16 heads of one row
+            // of the pair in the order the head sum takes them
+            int arow = row, ahead = 32 * mt + li;
+            if constexpr (TQ == 4) {
+                const int qq = 2 * (t >> 1) + ((li >> 2) & 1);
+                arow = r0 + (qq < nq ? qq : 0);
+                ahead = 16 * (NMT * (t & 1) + mt) + 4 * (li >> 3) + (li & 3);
+            }
+            const uint8_t* qr = q + ((int64_t)arow * H + ahead) * 64 + 32 * g;
             A[t][mt][0] = widen(ld16(qr));
             A[t][mt][1] = widen(ld16(qr + 16));
             if constexpr (MX) {
-                const uint32_t qs = *reinterpret_cast<const uint32_t*>(q_sc + ((int64_t)row * H + 32 * mt + li) * 4);
+                const uint32_t qs = *reinterpret_cast<const uint32_t*>(q_sc + ((int64_t)arow * H + ahead) * 4);
                 SA[t][mt][0] = scale_byte(qs, 2 * g);
                 SA[t][mt][1] = scale_byte(qs, 2 * g + 1);
             } else {
-                SA[t][mt][0] = q_sc[(int64_t)row * H + 32 * mt + li];
+                SA[t][mt][0] = q_sc[(int64_t)arow * H + ahead];
             }
         }
     }
@@ -239,6 +265,71 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     // score the tile at p0 from bf, refilling bf with the tile at p_next once
     // the last query's MFMAs have consumed it
     auto tile = [&](Buf& bf, int64_t p0, int64_t p_next) {
+        if constexpr (TQ == 4) {
+            // row pairs: lane half g of a pair's 32x32 products holds 16 heads of
+            // row 2 pr + g (A row mapping above) for positions p0 + li (nt 0) and
+            // p0 + 32 + li (nt 1), so the head sums need no exchange between the
+            // lane halves; the weights of the lane's row come from LDS
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                if (2 * pr >= nq) break;
+                const int qq = 2 * pr + g;
+                float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+                for (int m = 0; m < 2 * NMT; ++m) {
+                    const int t = 2 * pr + m / NMT, mt = m % NMT;
+                    v16f acc[2];
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        acc[nt] = v16f{};
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            if constexpr (MX)
+                                acc[nt] = mfma_fp4_mx(A[t][mt][ks], widen(bf.k[nt][ks]), acc[nt], SA[t][mt][ks],
+                                                      scale_byte(bf.sc[nt], 2 * g + ks));
+                            else
+                                acc[nt] = mfma_scaled(A[t][mt][ks], widen(bf.k[nt][ks]), acc[nt], SA[t][mt][0], 4);
+                        }
+                    }
+                    if (m == 2 * NMT - 1 && (2 * pr + 2 >= nq || pr == 1)) fetch(bf, p_next);
+                    // heads 16 m .. 16 m + 15 of row qq, in order
+                    const v4f* wq = reinterpret_cast<const v4f*>(wl + qq * H + 16 * m);
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const v4f wv = wq[q4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            s0 = __builtin_fmaf(wv[i], relu(acc[0][4 * q4 + i]), s0);
+                            s1 = __builtin_fmaf(wv[i], relu(acc[1][4 * q4 + i]), s1);
+                        }
+                    }
+                    // as below: the partial sums stay where they are computed
+                    asm volatile("" : "+v"(s0), "+v"(s1));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (qq < nq) {
+                    const int64_t vq = vis_pr[pr];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int64_t j = p0 + 32 * h2 + li;
+                        if (j < n) {
+                            const bool visible = j < vq;
+                            float sc = -INFINITY;
+                            if (visible) {
+                                if constexpr (MX) sc = h2 ? s1 : s0;
+                                else sc = ldexpf(h2 ? s1 : s0, (int)ekl[p0 - c0 + 32 * h2 + li] - 127);
+                            }
+                            if constexpr (LOCAL)
+                                sl[qq][p0 - c0 + 32 * h2 + li] = sc;
+                            else
+                                scores[(int64_t)(r0 + qq) * stride + j] = sc;
+                            if (HIST && visible) hist16_add(hl + qq * (kHistBins / 2), score_bin(sc));
+                        }
+                    }
+                }
+            }
+            return;
+        }
         const int64_t jl = p0 + lane;
 #pragma unroll
         for (int t = 0; t < TQ; ++t) {
@@ -300,6 +391,10 @@ __global__ __launch_bounds__(256) void k_score_decode(const uint8_t* __restrict_
     if constexpr (!MX) {
 #pragma unroll
         for (int j = 0; j < chunk / 256; ++j) ekl[64 * wave + 256 * j + lane] = sb[j];
+    }
+    if constexpr (TQ == 4) {  // the weights are read by every wave
+        if (threadIdx.x < 4 * H) wl[threadIdx.x] = w_own;
+        lds_barrier();
     }
     // pairs of tiles, then an odd last one: the loop body has no exit of its
     // own, so every path into the loop header has the same loads in flight
