@@ -1,6 +1,9 @@
 """Helpers for the GPU tests: upload a synthetic workload and run the layer
 chain through the C ABI.  (Not a test module.)"""
+import contextlib
 import math
+import os
+import re
 
 import numpy as np
 import torch
@@ -88,3 +91,18 @@ def assert_close_attn(got, ref, what=""):
     bad = err > 2e-3 + 1e-2 * np.abs(ref)
     assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance; max abs {err.max():.3e}"
     return float(err.max())
+
+
+@contextlib.contextmanager
+def saved_on_failure(wl, tag):
+    """With CSA2_SAVE_FAILED set to a directory, a failure inside the block
+    writes wl's inputs there (synth.replay format, one folder per tag) before
+    the failure propagates; tests/replay_case.py runs them again."""
+    try:
+        yield
+    except BaseException:
+        root = os.environ.get("CSA2_SAVE_FAILED")
+        if root:
+            from synth.replay import save_workload
+            save_workload(wl, os.path.join(root, re.sub(r"[^A-Za-z0-9_.-]+", "_", tag)), note=f"failed: {tag}")
+        raise

@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 from compressed_sparse_attention_amd import csa2 as C
-from gpu_util import SCALE, DevWorkload, assert_close_attn, dev, run_chain
+from gpu_util import SCALE, DevWorkload, assert_close_attn, dev, run_chain, saved_on_failure
 
 pytestmark = pytest.mark.gpu
 
@@ -379,18 +379,48 @@ CHAIN_CASES = {
 @pytest.mark.parametrize("case", list(CHAIN_CASES))
 def test_layer_chain_matches_oracle(case):
     wl = CHAIN_CASES[case]()
+    with saved_on_failure(wl, f"chain_{case}"):
+        dw = DevWorkload(wl)
+        outs, (pb, pp, pc), _ = run_chain(dw)
+        torch.cuda.synchronize()
+        ref = oracle.layer_chain(wl)
+        for o, r in zip(outs, ref):
+            assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"layer {r['layer']} indices"
+            assert_close_attn(o["out"].cpu().numpy(), r["out"], f"layer {r['layer']}")
+            np.testing.assert_allclose(o["lse"].cpu().numpy(), r["lse"], rtol=1e-4, atol=1e-4)
+            if "pool_pos" in r:
+                assert np.array_equal(pb.cpu().numpy(), r["blocks"])
+                assert np.array_equal(pp.cpu().numpy(), r["pool_pos"])
+                assert np.array_equal(pc.cpu().numpy(), r["pool_count"])
+
+
+@pytest.mark.parametrize("case", ["c2_small", "c4_small_pages_h32", "c3_small", "encoder_20"])
+def test_reruns_are_bitwise_identical(case):
+    """Two runs on the same inputs agree bit for bit: the Full layer's scores,
+    every layer's indices, attention outputs and log-sum-exps, and the pool
+    (no floating-point sum depends on the order in which workgroups finish)."""
+    wl = CHAIN_CASES[case]()
     dw = DevWorkload(wl)
-    outs, (pb, pp, pc), _ = run_chain(dw)
+    full = next(i for i, L in enumerate(wl.layers) if L.mode == synth.MODE_FULL)
+    L, dL = wl.layers[full], dw.layers[full]
+    k_idx = dw.k_idx if dL["k_idx"] is None else dL["k_idx"]
+    k_sc = dw.k_sc if dL["k_sc"] is None else dL["k_sc"]
+    s1 = C.csa2_index_score(dw.batch, wl.H, L.q_fmt, dL["q_idx"], dL["q_sc"], dL["w"], k_idx, k_sc)
+    s2 = C.csa2_index_score(dw.batch, wl.H, L.q_fmt, dL["q_idx"], dL["q_sc"], dL["w"], k_idx, k_sc)
+    a, pa, _ = run_chain(dw)
+    b, pb, _ = run_chain(dw)
     torch.cuda.synchronize()
-    ref = oracle.layer_chain(wl)
-    for o, r in zip(outs, ref):
-        assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"layer {r['layer']} indices"
-        assert_close_attn(o["out"].cpu().numpy(), r["out"], f"layer {r['layer']}")
-        np.testing.assert_allclose(o["lse"].cpu().numpy(), r["lse"], rtol=1e-4, atol=1e-4)
-        if "pool_pos" in r:
-            assert np.array_equal(pb.cpu().numpy(), r["blocks"])
-            assert np.array_equal(pp.cpu().numpy(), r["pool_pos"])
-            assert np.array_equal(pc.cpu().numpy(), r["pool_count"])
+    g1, g2 = s1.cpu().numpy().view(np.uint32), s2.cpu().numpy().view(np.uint32)
+    for r in range(wl.total_q):  # the slots of the row's sequence (the rest of a row is not written)
+        n = int(wl.n_entries[wl.row_seq[r]])
+        assert np.array_equal(g1[r, :n], g2[r, :n]), f"row {r} scores"
+    for x, y in zip(a, b):
+        assert torch.equal(x["idx"], y["idx"]), f"layer {x['layer']} indices"
+        assert torch.equal(x["out"].view(torch.int32), y["out"].view(torch.int32)), f"layer {x['layer']} output"
+        assert torch.equal(x["lse"].view(torch.int32), y["lse"].view(torch.int32)), f"layer {x['layer']} lse"
+    if any(L.build_pool for L in wl.layers):  # otherwise the pool outputs are never written
+        for u, v in zip(pa, pb):
+            assert torch.equal(u, v), "pool"
 
 
 @pytest.mark.gpu
@@ -403,17 +433,18 @@ def test_decode_step_40_matches_oracle(fmt):
     main KV, MXFP4 indexer, FP8 SWA; report 4.2.1 and 2.4.4)."""
     kw = dict(kv_fmt=1, swa_fmt=1, q_fmt=synth.Q_MXFP4, H=32) if fmt == "pages" else {}
     for wl in synth.decode_step_40(n_seq=2, tokens=6000, Hm=16, **kw):
-        dw = DevWorkload(wl)
-        outs, (pb, pp, pc), _ = run_chain(dw)
-        torch.cuda.synchronize()
-        ref = oracle.layer_chain(wl)
-        assert [o["layer"] for o in outs] == [r["layer"] for r in ref]
-        for o, r in zip(outs, ref):
-            assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"{wl.name} layer {r['layer']} indices"
-            assert_close_attn(o["out"].cpu().numpy(), r["out"], f"{wl.name} layer {r['layer']}")
-            np.testing.assert_allclose(o["lse"].cpu().numpy(), r["lse"], rtol=1e-4, atol=1e-4)
-            if "pool_pos" in r:
-                assert np.array_equal(pp.cpu().numpy(), r["pool_pos"])
+        with saved_on_failure(wl, f"step40_{fmt}_{wl.name}"):
+            dw = DevWorkload(wl)
+            outs, (pb, pp, pc), _ = run_chain(dw)
+            torch.cuda.synchronize()
+            ref = oracle.layer_chain(wl)
+            assert [o["layer"] for o in outs] == [r["layer"] for r in ref]
+            for o, r in zip(outs, ref):
+                assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"{wl.name} layer {r['layer']} indices"
+                assert_close_attn(o["out"].cpu().numpy(), r["out"], f"{wl.name} layer {r['layer']}")
+                np.testing.assert_allclose(o["lse"].cpu().numpy(), r["lse"], rtol=1e-4, atol=1e-4)
+                if "pool_pos" in r:
+                    assert np.array_equal(pp.cpu().numpy(), r["pool_pos"])
 
 
 TIE_CASES = {
