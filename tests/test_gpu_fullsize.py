@@ -17,6 +17,11 @@ for bit, their attention outputs within |gpu - ref| <= 2e-3 + 1e-2 |ref|.
               MXFP4 indexer, FP8 SWA): 4 sequences checked
   ragged_c4   48 sequences of 4K..1M entries, 4 rows each, layers 20..39 with pool
               (the shortest and the longest sequence plus two more: 16 rows)
+  replay_c5   decoder SWA bounded replay: 16 x 131,072 entries, the last 128
+              prompt tokens of each sequence as FP4 query rows through layers
+              20..39 with pool, windows cut at the replay start (the first,
+              two middle and the last row of 4 sequences: 16 rows)
+  decode_step_40 in the library's default formats as well (4 sequences)
 """
 import sys
 
@@ -120,3 +125,14 @@ def test_fullsize_ragged_c4():
     rows = np.concatenate([np.arange(wl.q_off[b], wl.q_off[b + 1]) for b in seqs])
     _say(f"[ragged_c4] sum N = {int(n.sum())}, min {int(n.min())}, max {int(n.max())}; sampled sequences {seqs.tolist()}")
     _check_chain(wl, rows, "ragged_c4")
+
+
+def test_fullsize_replay_c5():
+    wl = synth.config("replay_c5")
+    rows = np.concatenate([wl.q_off[b] + np.array([0, 63, 64, 127]) for b in (0, 5, 10, 15)])
+    _check_chain(wl, rows, "replay_c5")
+
+
+def test_fullsize_decode_step_40_default():
+    for wl in synth.decode_step_40():
+        _check_chain(wl, np.array([0, 21, 42, 63]), wl.name)
