@@ -367,6 +367,13 @@ CHAIN_CASES = {
     # with a 200-token uncached suffix as E4M3 query rows through one encoder
     # group at ratio 2, every window cut at the replay start
     "encoder_replay": lambda: synth.config("encoder_replay", tokens=6000, suffix=200, Hm=16),
+    # Top-K at the library's largest K (2048 entries plus the window: 34 key
+    # blocks) and at small odd K, through the one-row scan with its fused
+    # selection, the pool and Reindex, and the four-row scan
+    "c1_k2048": lambda: synth.config("decode_c1", n_seq=3, n=40000, Hm=16, K=2048),
+    "c2_k2048": lambda: synth.config("chain_c2", n_seq=2, n=24000, Hm=16, K=2048),
+    "c4_k100": lambda: synth.config("ragged_c4", lengths=[4096, 5000, 17000, 33001], Hm=16, K=100),
+    "c1_k17": lambda: synth.config("decode_c1", n_seq=3, n=9000, Hm=16, K=17),
     "encoder_group": lambda: synth.make_workload("enc", 12, [700, 2500], 3, [(0, synth.MODE_SWA_ONLY, False),
                                                                              (2, synth.MODE_FULL, False),
                                                                              (3, synth.MODE_REUSE, False),
