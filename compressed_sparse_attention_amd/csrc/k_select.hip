@@ -57,21 +57,26 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-// Chunk bounds (rows with no histogram): workgroup (c, row) counts the bins
-// of slots [c kHChunk, (c+1) kHChunk) in LDS and, when those slots all exist,
-// records the bin of their m-th largest score, m = ceil(K / F), F the row's
-// count of such full chunks.  The F chunks then hold F m >= K slots at or
-// above the smallest recorded bin, so that bin is at or below the row's
-// threshold bin; no global atomics are needed.
+// Chunk bounds (rows with no histogram), from every cs-th chunk: workgroup
+// (i, row) counts the bins of the slots of chunk c = cs i, [c kHChunk,
+// (c+1) kHChunk), in LDS and, when those slots all exist, records the bin of
+// their m-th largest score, m = ceil(K / F), F the row's count of such sampled
+// full chunks.  The F chunks then hold F m >= K slots at or above the smallest
+// recorded bin, so that bin is at or below the row's threshold bin; no global
+// atomics are needed.  Sampling reads 1/cs of the scores for a looser bound:
+// about cs K slots pass it instead of about K, which the collect pass and the
+// final radix select absorb while cs K stays well inside their capacity.
+inline int bound_stride(int K) { return K <= 512 ? 4 : (K <= 1024 ? 2 : 1); }
 __global__ __launch_bounds__(256) void k_chunk_bound(const float* __restrict__ scores, int64_t stride, RowSrc rs,
-                                                     int K, uint32_t* __restrict__ lb) {
+                                                     int K, int cs, uint32_t* __restrict__ lb) {
     __shared__ uint32_t h[kHistBins];
     __shared__ uint32_t wtot[4], found[2];
     const int row = blockIdx.y;
     const int64_t n = row_n(rs, row);
-    const int64_t s0 = (int64_t)blockIdx.x * kHChunk;
+    const int64_t c = (int64_t)blockIdx.x * cs;
+    const int64_t s0 = c * kHChunk;
     if (s0 + kHChunk > n) return;  // a partial chunk (or none): no bound
-    const int64_t F = n / kHChunk;
+    const int64_t F = (n / kHChunk + cs - 1) / cs;
     const uint32_t m = (uint32_t)((K + F - 1) / F);
     for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
     __syncthreads();
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(256) void k_chunk_bound(const float* __restrict__ s
     }
     __syncthreads();
     const uint32_t bm = threshold_bin(PlainBins{h}, m, wtot, found);
-    if (threadIdx.x == 0) lb[(int64_t)row * kHistBins + blockIdx.x] = bm;
+    if (threadIdx.x == 0) lb[(int64_t)row * kHistBins + c] = bm;
 }
 
 // Candidates: every slot whose bin is at or above the threshold bin goes to
@@ -102,8 +107,8 @@ constexpr int kLocalCand = 2048;
 // and the candidates are the slots at or above the smallest of them.
 template <bool LB>
 __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ scores, int64_t stride, RowSrc rs,
-                                                 const uint32_t* __restrict__ hist, int K, RowSel* __restrict__ sel,
-                                                 uint64_t* __restrict__ cand_buf) {
+                                                 const uint32_t* __restrict__ hist, int K, int cs,
+                                                 RowSel* __restrict__ sel, uint64_t* __restrict__ cand_buf) {
     __shared__ uint32_t part[4];
     __shared__ uint32_t found[2];
     __shared__ uint64_t lc[kLocalCand];
@@ -133,11 +138,11 @@ __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ score
     const uint32_t kk = (uint32_t)(n < K ? n : K);
     uint32_t bin;
     if constexpr (LB) {
-        // the smallest bound of the row's full chunks (0 without one); a row
-        // with no slot selects nothing
+        // the smallest bound of the row's sampled full chunks (0 without one);
+        // a row with no slot selects nothing
         const int F = (int)(n / kHChunk);
         uint32_t v = 0xFFFFFFFFu;
-        for (int c = threadIdx.x; c < F; c += 256) v = min(v, hist[(int64_t)row * kHistBins + c]);
+        for (int c = cs * threadIdx.x; c < F; c += cs * 256) v = min(v, hist[(int64_t)row * kHistBins + c]);
         for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o));
         if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
         __syncthreads();
@@ -1258,10 +1263,12 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
         // place) give a lower bound of each row's threshold bin
         hipError_t e = clear_topk_ws(a.ws, nq, false, s);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_chunk_bound, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, a.K,
-                           hist);
+        const int cs = bound_stride(a.K);
+        const unsigned sampled = (chunks + cs - 1) / cs;
+        hipLaunchKernelGGL(k_chunk_bound, dim3(sampled ? sampled : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, a.K,
+                           cs, hist);
         hipLaunchKernelGGL(k_collect<true>, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs,
-                           hist, a.K, sel, cb);
+                           hist, a.K, cs, sel, cb);
     } else {
         if (h != hist) {
             hipError_t e = clear_topk_ws(a.ws, nq, false, s);
@@ -1269,7 +1276,7 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
         }
         // (h == hist: the caller cleared the workspace and filled its histogram)
         hipLaunchKernelGGL(k_collect<false>, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, h,
-                           a.K, sel, cb);
+                           a.K, 1, sel, cb);
     }
     hipLaunchKernelGGL(k_final, dim3(nq), dim3(1024), 0, s, a.scores, a.stride, sel, cb, a.cand, a.cand_stride, a.K,
                        a.idx);
