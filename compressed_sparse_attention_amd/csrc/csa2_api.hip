@@ -552,7 +552,7 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                 ScoreLaunch sa{batch, g, p->H, L.q_fmt, (const uint8_t*)L.q_idx, L.q_sc, L.w, L.k_fp4, L.k_sc,
                                nullptr, 0, nullptr, 0, fused_topk ? nullptr : topk_ws_hist(topk_ws), &lo};
                 if ((e = timed_scan(sa, p, &scan_timed, stream)) != hipSuccess) return hip_fail(e);
-                if ((e = fused_topk ? launch_topk_fused(batch, g, lo, idx_cur, stream)
+                if ((e = fused_topk ? launch_topk_fused(batch, g, lo, idx_cur, topk_ws, stream)
                                     : launch_topk_local(batch, g, lo, idx_cur, topk_ws, stream)) != hipSuccess)
                     return hip_fail(e);
                 if (build_pool) {  // after the Top-K: the pool's selection reuses its workspace

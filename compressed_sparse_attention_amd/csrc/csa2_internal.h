@@ -322,14 +322,17 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 hipError_t launch_topk_local(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, void* ws,
                              hipStream_t s);
 
-// The whole Top-K from a scan's per-chunk lists in one kernel (one workgroup
-// per row, no histogram from the scan).  Correct for any list length up to
-// kListChunks chunks per row; chosen for rows of at most kFusedTopkEntries
-// entries (max_chunks * chunk), whose lists one workgroup reads in a few
-// passes, while longer rows spread the filtering over many workgroups.
+// The Top-K from a scan's per-chunk lists and the chunks' bounds, without a
+// histogram from the scan: many workgroups keep the list entries at or above
+// the row's bound (in ws, a Top-K workspace), then one workgroup per row
+// selects among them (or, when they do not fit, from the lists).  Correct for
+// any list length up to kListChunks chunks per row; chosen for rows of at
+// most kFusedTopkEntries entries (max_chunks * chunk), while longer rows take
+// the scan's histogram (launch_topk_local).
 constexpr int kListChunks = 1024;
 constexpr int64_t kFusedTopkEntries = 262144;
-hipError_t launch_topk_fused(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, hipStream_t s);
+hipError_t launch_topk_fused(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, void* ws,
+                             hipStream_t s);
 
 struct PoolLaunch {
     const csa2_batch* b;

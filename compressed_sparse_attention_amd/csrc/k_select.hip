@@ -711,10 +711,16 @@ __device__ void find_bin(Visit&& visit, uint32_t kk, uint32_t* hcopy, uint32_t* 
 // their histogram has the row's exact counts from B up, which is all the
 // search reads.
 //
+// With the filter's parts (below) the row's entries at or above its bound
+// come from them straight into LDS and are selected there; only when a part
+// overflowed, or they do not fit, are the lists read, as follows.
+//
 // The lists are read as their concatenation (chunk order = position order).
 // When they hold at most kListWindow entries, thread t keeps entries t,
 // t + 1024, ... in registers and they are read once; otherwise every step
 // streams them from memory again, chunk by chunk.
+//   0. with the chunks' bounds, the entries at or above LB into LDS and the
+//      select there, while they fit; else
 //   1. B in two 6-bit digits (bin = 64 d1 + d2), each counted into 32 copies
 //      of a 64-entry LDS histogram (lane l adds to copy l % 32: the entries
 //      crowd into a few bins and same-address LDS atomics serialise);
@@ -723,14 +729,137 @@ __device__ void find_bin(Visit&& visit, uint32_t kk, uint32_t* hcopy, uint32_t* 
 //   3. radix select of the threshold bin's keys from bit 51 down (the bins
 //      above B all win);
 //   4. the winners, written in order.
-constexpr int kListPer = 28;                    // list entries per thread held in registers
-constexpr int kListWindow = 1024 * kListPer;    // 28,672 entries
+constexpr int kListPer = 22;                    // list entries per thread held in registers
+constexpr int kListWindow = 1024 * kListPer;    // 22,528 entries
 constexpr int kCandPer = kCandCap / 1024;       // LDS candidates per thread in step 4
+constexpr int kSpecParts = 4;                   // filter parts per wave loaded with their counts
+
+// With the chunks' bounds, the entries that survive the bound are gathered by
+// many workgroups first (k_lists_filter), so that no single compute unit has
+// to pull a whole row's lists: workgroup (g, row) reads the lists of the row's
+// chunks [kPartChunks g, kPartChunks (g + 1)), keeps the entries whose bin is
+// at or above the row's bound LB (the smallest bound of its full chunks, 0
+// without one) and writes them, in any order, to part g of the row's
+// candidate buffer (cap entries from g cap), and their count to
+// part_cnt[row][g].  A count above cap means the part overflowed (only its
+// first cap entries were written): k_topk_lists then selects from the lists.
+// Workgroup (0, row) also writes the row's size to part_n[row], so that the
+// selection reads it with the counts.
+constexpr int kPartChunks = 2;   // list chunks per filter workgroup
+constexpr int kPartPer = 8;      // entries per thread per pass past the first
+constexpr int kSpecPer = 3;      // entries per thread of each list loaded with the lengths (768 of a list)
+constexpr int kMaxParts = 64;    // parts per row (one wave scans their counts)
+
+__global__ __launch_bounds__(256) void k_lists_filter(const uint64_t* __restrict__ lists,
+                                                      const uint32_t* __restrict__ counts,
+                                                      const uint32_t* __restrict__ lbins, int max_chunks, int chunk,
+                                                      RowSrc rs, int cap, uint32_t* __restrict__ part_cnt,
+                                                      uint32_t* __restrict__ part_n, uint64_t* __restrict__ part_keys) {
+    __shared__ uint32_t wmin[4];
+    __shared__ uint32_t nsurv;
+    const int row = blockIdx.y, g = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int c0 = g * kPartChunks;
+    // loaded before the row's size is known, all at once (every address is in
+    // the row's lists; what lies past the visible chunks is not used): the
+    // lengths of this part's lists, the first 256 kSpecPer slots of each (a
+    // list has room for `chunk` >= 256 kSpecPer entries; slots past its
+    // length are unused) and the chunks' bounds (max_chunks <= 256)
+    const uint64_t* lp = lists + ((int64_t)row * max_chunks + c0) * chunk;
+    uint32_t cn[kPartChunks];
+    uint64_t xs[kPartChunks][kSpecPer];
+#pragma unroll
+    for (int i = 0; i < kPartChunks; ++i) {
+        const bool in = c0 + i < max_chunks;
+        cn[i] = in ? counts[(int64_t)row * max_chunks + c0 + i] : 0u;
+#pragma unroll
+        for (int u = 0; u < kSpecPer; ++u) xs[i][u] = in ? lp[(int64_t)i * chunk + tid + 256 * u] : 0ull;
+    }
+    const uint32_t lbv = tid < max_chunks ? lbins[(int64_t)row * max_chunks + tid] : 0xFFFFFFFFu;
+    const int64_t n = row_n(rs, row);
+    const int n_ch = (int)((n + chunk - 1) / chunk);
+    const int n_full = (int)(n / chunk);
+    if (g == 0 && tid == 0) part_n[row] = (uint32_t)n;
+    uint32_t* cnt_out = part_cnt + (int64_t)row * gridDim.x + g;
+    if (c0 >= n_ch) {  // past the row's chunks (or an empty row): an empty part
+        if (tid == 0) *cnt_out = 0u;
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < kPartChunks; ++i) cn[i] = c0 + i < n_ch ? cn[i] : 0u;
+    uint32_t v = tid < n_full ? lbv : 0xFFFFFFFFu;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o));
+    if (lane == 0) wmin[tid >> 6] = v;
+    if (tid == 0) nsurv = 0u;
+    __syncthreads();
+    const uint32_t LB = n_full > 0 ? min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3])) : 0u;
+    uint64_t* dst = part_keys + (int64_t)row * kCandCap + (int64_t)g * cap;
+    // the loaded slots: every keep first, then one reservation per wave
+    {
+        uint32_t keep = 0;
+#pragma unroll
+        for (int i = 0; i < kPartChunks; ++i)
+#pragma unroll
+            for (int u = 0; u < kSpecPer; ++u)
+                keep |= (uint32_t)((uint32_t)(tid + 256 * u) < cn[i] && key64_bin(xs[i][u]) >= LB)
+                        << (i * kSpecPer + u);
+        const uint32_t mine = (uint32_t)__popc(keep);
+        uint32_t incl = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t w = __shfl_up(incl, o);
+            if (lane >= o) incl += w;
+        }
+        uint32_t base = 0;
+        if (lane == 63 && incl) base = atomicAdd(&nsurv, incl);
+        uint32_t p = __shfl(base, 63) + incl - mine;
+#pragma unroll
+        for (int i = 0; i < kPartChunks; ++i)
+#pragma unroll
+            for (int u = 0; u < kSpecPer; ++u)
+                if ((keep >> (i * kSpecPer + u)) & 1u) {
+                    if (p < (uint32_t)cap) dst[p] = xs[i][u];
+                    ++p;
+                }
+    }
+    // the rest of each list, a pass of kPartPer loads per thread at a time (a
+    // slot past the list re-reads its last entry; each use checks j < cn)
+    auto emit = [&](bool take, uint64_t x) {
+        const uint64_t m = __ballot(take);
+        if (m) {
+            uint32_t p0 = 0;
+            if (lane == 0) p0 = atomicAdd(&nsurv, (uint32_t)__popcll(m));
+            p0 = __shfl(p0, 0);
+            const uint32_t p = p0 + (uint32_t)__popcll(m & ((1ull << lane) - 1));
+            if (take && p < (uint32_t)cap) dst[p] = x;
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < kPartChunks; ++i) {
+        for (uint32_t j0 = 256u * kSpecPer; j0 < cn[i]; j0 += 256u * kPartPer) {
+            uint64_t x[kPartPer];
+#pragma unroll
+            for (int u = 0; u < kPartPer; ++u) {
+                const uint32_t j = j0 + (uint32_t)tid + 256u * u;
+                x[u] = lp[(int64_t)i * chunk + (j < cn[i] ? j : cn[i] - 1u)];
+            }
+#pragma unroll
+            for (int u = 0; u < kPartPer; ++u)
+                emit(j0 + (uint32_t)tid + 256u * u < cn[i] && key64_bin(x[u]) >= LB, x[u]);
+        }
+    }
+    __syncthreads();
+    if (tid == 0) *cnt_out = nsurv;
+}
 
 __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict__ lists,
                                                      const uint32_t* __restrict__ counts,
                                                      const uint32_t* __restrict__ lbins, int max_chunks, int chunk,
-                                                     RowSrc rs, int K, int32_t* __restrict__ idx) {
+                                                     RowSrc rs, int K, const uint32_t* __restrict__ part_cnt,
+                                                     const uint32_t* __restrict__ part_n,
+                                                     const uint64_t* __restrict__ part_keys, int parts, int cap,
+                                                     int32_t* __restrict__ idx) {
     __shared__ uint64_t c[kCandCap];
     __shared__ uint32_t bm[kFusedTopkEntries / 32];  // winners by position
     __shared__ uint32_t nsurv, lb_sh;
@@ -742,14 +871,35 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
     __shared__ RadixState st;
     __shared__ int found;
     __shared__ uint32_t wsum[16];
-    __shared__ uint32_t thr[2];
+    __shared__ uint32_t thr[3];
+    __shared__ uint32_t h4k[2 * kHistBins];
+    __shared__ uint32_t pover;
     const int row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // the lists' lengths and bounds are read with the row's size (every
-    // chunk of the row is in bounds; those past the visible range are unused)
-    const uint32_t cnt_raw = tid < max_chunks ? counts[(int64_t)row * max_chunks + tid] : 0u;
-    const uint32_t lb_raw = (lbins && tid < max_chunks) ? lbins[(int64_t)row * max_chunks + tid] : 0xFFFFFFFFu;
-    const int64_t n = row_n(rs, row);
+    // loaded at once: with parts, their counts (parts <= kMaxParts), the
+    // row's size and the first slots of each wave's parts; without, the
+    // row's size with the lists' lengths and bounds (every chunk of the row
+    // is in bounds; those past the visible range are unused)
+    uint32_t pc = 0u;
+    uint64_t ys[kSpecParts][2];
+    uint32_t cnt_raw = 0u, lb_raw = 0xFFFFFFFFu;
+    int64_t n;
+    if (part_cnt) {
+        pc = tid < parts ? part_cnt[(int64_t)row * parts + tid] : 0u;
+#pragma unroll
+        for (int r = 0; r < kSpecParts; ++r) {
+            const int q = wave + 16 * r;  // the same for the whole wave
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+                ys[r][v] = q < parts ? part_keys[(int64_t)row * kCandCap + (int64_t)q * cap + min(lane + 64 * v, cap - 1)]
+                                     : 0ull;
+        }
+        n = (int64_t)part_n[row];
+    } else {
+        cnt_raw = tid < max_chunks ? counts[(int64_t)row * max_chunks + tid] : 0u;
+        lb_raw = (lbins && tid < max_chunks) ? lbins[(int64_t)row * max_chunks + tid] : 0xFFFFFFFFu;
+        n = row_n(rs, row);
+    }
     const uint32_t kk = (uint32_t)(n < K ? n : K);
     int32_t* out = idx + (int64_t)row * K;
     for (int i = tid + (int)kk; i < K; i += 1024) out[i] = -1;
@@ -764,7 +914,178 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
         lb_sh = 0xFFFFFFFFu;
     }
     for (int i = tid; i < kFusedTopkEntries / 32; i += 1024) bm[i] = 0;
+    for (int i = tid; i < 2 * kHistBins; i += 1024) h4k[i] = 0;
+    if (part_cnt && wave == 0) {  // the parts' offsets, and whether one overflowed
+        uint32_t incl = pc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t w = __shfl_up(incl, o);
+            if (lane >= o) incl += w;
+        }
+        if (lane < parts) roff[lane] = incl - pc;
+        if (lane == 63) roff[parts] = incl;  // lanes at or past `parts` hold 0
+        const uint64_t ov = __ballot(lane < parts && pc > (uint32_t)cap);
+        if (lane == 0) pover = ov ? 1u : 0u;
+    }
     __syncthreads();  // lb_sh is set before any thread lowers it
+
+    // The K winners among the n_surv keys in c (every key at or above the
+    // row's bound, in any order): a radix select on key64 from the top with
+    // 12-bit digits, each digit's histogram in 4096 LDS bins (two of them,
+    // cleared at the start, one cleared while the other counts), read from
+    // the top by a block-wide scan; it stops once every key left with the
+    // chosen prefix wins (two digits for distinct scores).  When no key is
+    // negative (nonneg) the top bit is fixed and the first digit is the
+    // score's bin; `counted`: the caller has counted that first histogram
+    // (bins of every key) into h4k and passed a barrier.  The winners are marked in a bitmap by position and
+    // written in position order.
+    auto mark = [&](uint64_t x) {
+        const uint32_t pos = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu);
+        atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+    };
+    auto select_in_lds = [&](uint32_t n_surv, bool nonneg, bool counted) {
+        uint64_t pf = nonneg ? 1u : 0u;  // every key's top bit is set: the first digit is its bin
+        int sh = nonneg ? 63 : 64;
+        uint32_t need = kk;
+        for (int pass = 0;; ++pass) {
+            uint32_t* h = h4k + (pass & 1) * kHistBins;
+            const int w = sh < 12 ? sh : 12;
+            if (pass > 0 || !counted) {
+                for (uint32_t e = tid; e < n_surv; e += 1024) {
+                    const uint64_t x = c[e];
+                    if (prefix_eq(x, sh, pf)) atomicAdd(&h[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
+                }
+                __syncthreads();
+            }
+            {
+                // thread t owns digits top .. top - 3 (t = 0 the highest)
+                const int top = kHistBins - 1 - 4 * tid;
+                uint32_t hb[4], sum = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    hb[i] = h[top - i];
+                    sum += hb[i];
+                }
+                uint32_t tot;
+                const uint32_t incl = block_scan_1024(sum, wsum, &tot);
+                uint32_t acc = incl - sum;
+                if (acc < need && need <= incl) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (acc < need && need <= acc + hb[i]) {
+                            thr[0] = (uint32_t)(top - i);
+                            thr[1] = acc;
+                            thr[2] = hb[i];
+                        }
+                        acc += hb[i];
+                    }
+                }
+            }
+            __syncthreads();
+            const uint32_t d = thr[0], above = thr[1], here = thr[2];
+            for (int i = tid; i < kHistBins; i += 1024) h[i] = 0;  // counted into again two passes on
+            need -= above;
+            pf = (pf << w) | d;
+            sh -= w;
+            if (here == need || sh == 0) break;
+        }
+        for (uint32_t e = tid; e < n_surv; e += 1024) {
+            const uint64_t x = c[e];
+            if (prefix_ge(x, sh, pf)) mark(x);
+        }
+        __syncthreads();
+        // positions in order: thread t owns bitmap words [WPT t, WPT (t + 1))
+        constexpr int kMaxWpt = kFusedTopkEntries / 32 / 1024;
+        const int nwords = (int)((n + 31) / 32);
+        const int WPT = (nwords + 1023) / 1024;
+        uint32_t wd[kMaxWpt];
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxWpt; ++i) {
+            const int wi = WPT * tid + i;
+            wd[i] = (i < WPT && wi < nwords) ? bm[wi] : 0u;
+            cnt += (uint32_t)__popc(wd[i]);
+        }
+        uint32_t tot;
+        uint32_t r = block_scan_1024(cnt, wsum, &tot) - cnt;
+#pragma unroll
+        for (int i = 0; i < kMaxWpt; ++i) {
+            uint32_t x = wd[i];
+            while (x) {
+                const int bit = __ffs(x) - 1;
+                if (r < kk) out[r] = 32 * (WPT * tid + i) + bit;
+                ++r;
+                x &= x - 1;
+            }
+        }
+    };
+
+    // the filter's parts: their entries to LDS when no part overflowed and
+    // they fit, then the select; else the lists are read below.  The first
+    // kSpecParts parts of each wave (w, w + 16, ...) had their first 128
+    // slots loaded with the counts (slots past a part's count are unused)
+    if (part_cnt) {
+        const uint32_t tot = roff[parts];
+        if (!pover && tot <= (uint32_t)kCandCap) {
+            // wave w copies parts w, w + 16, ...: the loaded slots first, then
+            // the rest four loads per lane at a time (a slot past the part
+            // re-reads its last entry)
+            bool neg = false;  // a key whose top bit is clear (a negative score)
+            auto copy_rest = [&](int q, uint32_t from) {
+                const uint32_t b0 = roff[q], cq = roff[q + 1] - b0;
+                const uint64_t* src = part_keys + (int64_t)row * kCandCap + (int64_t)q * cap;
+                for (uint32_t j0 = from; j0 < cq; j0 += 256) {
+                    uint64_t x[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t j = j0 + (uint32_t)lane + 64u * u;
+                        x[u] = src[j < cq ? j : cq - 1u];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t j = j0 + (uint32_t)lane + 64u * u;
+                        if (j < cq) {
+                            c[b0 + j] = x[u];
+                            neg |= (x[u] >> 63) == 0;
+                            atomicAdd(&h4k[(uint32_t)(x[u] >> 51) & 0xFFFu], 1u);
+                        }
+                    }
+                }
+            };
+#pragma unroll
+            for (int r = 0; r < kSpecParts; ++r) {
+                const int q = wave + 16 * r;
+                if (q < parts) {
+                    const uint32_t b0 = roff[q], cq = roff[q + 1] - b0;
+                    const uint32_t have = min(128u, (uint32_t)cap);
+#pragma unroll
+                    for (int v = 0; v < 2; ++v) {
+                        const uint32_t j = (uint32_t)(lane + 64 * v);
+                        if (j < cq && j < have) {
+                            c[b0 + j] = ys[r][v];
+                            neg |= (ys[r][v] >> 63) == 0;
+                            atomicAdd(&h4k[(uint32_t)(ys[r][v] >> 51) & 0xFFFu], 1u);
+                        }
+                    }
+                    copy_rest(q, have);
+                }
+            }
+            for (int q = wave + 16 * kSpecParts; q < parts; q += 16) copy_rest(q, 0u);
+            // the first histogram (bits 62..51: the bin when no key is
+            // negative) was counted with the copy; with a negative key the
+            // select starts from the top bit and counts it again
+            const bool any_neg = __syncthreads_or(neg) != 0;
+            if (any_neg) {
+                for (int i = tid; i < kHistBins; i += 1024) h4k[i] = 0;
+                __syncthreads();
+            }
+            select_in_lds(tot, !any_neg, !any_neg);
+            return;
+        }
+        // roff is rewritten below, after the barrier in the scan
+        cnt_raw = tid < max_chunks ? counts[(int64_t)row * max_chunks + tid] : 0u;
+        lb_raw = (lbins && tid < max_chunks) ? lbins[(int64_t)row * max_chunks + tid] : 0xFFFFFFFFu;
+    }
     // run offsets: exclusive prefix sum of the lists' lengths; the lower
     // bound LB of the row's threshold bin: the smallest of the full chunks'
     // bounds (0 when there is no full chunk)
@@ -922,61 +1243,7 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
         __syncthreads();
         const uint32_t n_surv = nsurv;
         if (n_surv <= (uint32_t)kCandCap) {
-            if (tid == 0) {
-                st.prefix = 0;
-                st.shift = 64;
-                st.need = kk;
-                st.done = 0;
-            }
-            __syncthreads();
-            while (!st.done) {
-                if (tid < 256) hist256[tid] = 0;
-                __syncthreads();
-                const int sh = st.shift;
-                const int w = digit_bits(sh);
-                const uint64_t pf = st.prefix;
-                for (uint32_t e = tid; e < n_surv; e += 1024) {
-                    const uint64_t x = c[e];
-                    if (prefix_eq(x, sh, pf))
-                        atomicAdd(&hist256[(uint32_t)(x >> (sh - w)) & ((1u << w) - 1u)], 1u);
-                }
-                __syncthreads();
-                radix_step(hist256, scan256, &st, &found);
-            }
-            const int sh = st.shift;  // < 64: at least one digit was fixed
-            const uint64_t pf = st.prefix;
-            for (uint32_t e = tid; e < n_surv; e += 1024) {
-                const uint64_t x = c[e];
-                if (prefix_ge(x, sh, pf)) {
-                    const uint32_t pos = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFu);
-                    atomicOr(&bm[pos >> 5], 1u << (pos & 31));
-                }
-            }
-            __syncthreads();
-            // positions in order: thread t owns bitmap words [WPT t, WPT (t + 1))
-            constexpr int kMaxWpt = kFusedTopkEntries / 32 / 1024;
-            const int nwords = (int)((n + 31) / 32);
-            const int WPT = (nwords + 1023) / 1024;
-            uint32_t wd[kMaxWpt];
-            uint32_t cnt = 0;
-#pragma unroll
-            for (int i = 0; i < kMaxWpt; ++i) {
-                const int wi = WPT * tid + i;
-                wd[i] = (i < WPT && wi < nwords) ? bm[wi] : 0u;
-                cnt += (uint32_t)__popc(wd[i]);
-            }
-            uint32_t tot;
-            uint32_t r = block_scan_1024(cnt, wsum, &tot) - cnt;
-#pragma unroll
-            for (int i = 0; i < kMaxWpt; ++i) {
-                uint32_t x = wd[i];
-                while (x) {
-                    const int bit = __ffs(x) - 1;
-                    if (r < kk) out[r] = 32 * (WPT * tid + i) + bit;
-                    ++r;
-                    x &= x - 1;
-                }
-            }
+            select_in_lds(n_surv, false, false);
             return;
         }
     }
@@ -1297,12 +1564,32 @@ hipError_t launch_topk_local(const csa2_batch* b, const Geometry& g, const Local
     return hipGetLastError();
 }
 
-hipError_t launch_topk_fused(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, hipStream_t s) {
-    if (lo.max_chunks > kListChunks || (int64_t)lo.max_chunks * lo.chunk > kFusedTopkEntries)
+hipError_t launch_topk_fused(const csa2_batch* b, const Geometry& g, const LocalOut& lo, int32_t* idx, void* ws,
+                             hipStream_t s) {
+    if (lo.max_chunks > kListChunks || (int64_t)lo.max_chunks * lo.chunk > kFusedTopkEntries ||
+        lo.chunk < 256 * kSpecPer || lo.max_chunks > kPartChunks * kMaxParts)
         return hipErrorInvalidValue;
     RowSrc rs{b->d_entry_off, b->d_row_seq, b->d_q_pos, b->ratio, nullptr, 0, 1, g.max_entries};
-    hipLaunchKernelGGL(k_topk_lists, dim3(g.total_q), dim3(1024), 0, s, (const uint64_t*)lo.lists,
-                       (const uint32_t*)lo.counts, (const uint32_t*)lo.lbins, lo.max_chunks, lo.chunk, rs, lo.K, idx);
+    const int nq = g.total_q;
+    // with the chunks' bounds: the parts' counts in the workspace's histogram
+    // area, their entries in its candidate area (kCandCap per row)
+    uint32_t* part_cnt = nullptr;
+    uint32_t* part_n = nullptr;
+    uint64_t* part_keys = nullptr;
+    int parts = 0, cap = 0;
+    if (lo.lbins && ws) {
+        parts = (lo.max_chunks + kPartChunks - 1) / kPartChunks;  // <= kMaxParts (checked above)
+        cap = kCandCap / parts;
+        part_cnt = (uint32_t*)ws;  // [nq][parts], then [nq] sizes: within the histogram area
+        part_n = part_cnt + (size_t)nq * parts;
+        part_keys = (uint64_t*)((char*)ws + al256((size_t)nq * kHistBins * 4) + al256((size_t)nq * sizeof(RowSel)));
+        hipLaunchKernelGGL(k_lists_filter, dim3(parts, nq), dim3(256), 0, s, (const uint64_t*)lo.lists,
+                           (const uint32_t*)lo.counts, (const uint32_t*)lo.lbins, lo.max_chunks, lo.chunk, rs, cap,
+                           part_cnt, part_n, part_keys);
+    }
+    hipLaunchKernelGGL(k_topk_lists, dim3(nq), dim3(1024), 0, s, (const uint64_t*)lo.lists, (const uint32_t*)lo.counts,
+                       (const uint32_t*)lo.lbins, lo.max_chunks, lo.chunk, rs, lo.K, (const uint32_t*)part_cnt,
+                       (const uint32_t*)part_n, (const uint64_t*)part_keys, parts, cap, idx);
     return hipGetLastError();
 }
 

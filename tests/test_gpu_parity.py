@@ -463,9 +463,9 @@ TIE_CASES = {
     "one_head_t1": dict(lens=[3, 700, 9000, 20000], T=1, heads=1),
     "one_head_t4": dict(lens=[5, 3000, 20000], T=4, heads=1),
     # rows of at most 262,144 entries take the one-kernel selection over the
-    # scan's lists: lists held in registers (up to 28,672 entries) with every
+    # scan's lists: lists held in registers (up to 22,528 entries) with every
     # score tied, few distinct scores with four rows per sequence, distinct
-    # scores; lists streamed from memory (more than 28,672 entries) with their
+    # scores; lists streamed from memory (more than 22,528 entries) with their
     # candidates in LDS, and with every score tied (candidates overflow LDS)
     "all_equal_fused_t1": dict(lens=[3, 700, 9000, 16384], T=1, heads=0),
     "one_head_fused_t4": dict(lens=[5, 3000, 8192], T=4, heads=1),
@@ -528,6 +528,36 @@ def test_layer_chain_negative_weights(case):
     torch.cuda.synchronize()
     ref = oracle.layer_chain(wl)
     assert (ref[0]["scores"][np.isfinite(ref[0]["scores"])] < 0).any()
+    for o, r in zip(outs, ref):
+        assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"layer {r['layer']} indices"
+        assert_close_attn(o["out"].cpu().numpy(), r["out"], f"layer {r['layer']}")
+        if "pool_pos" in r:
+            assert np.array_equal(pb.cpu().numpy(), r["blocks"])
+            assert np.array_equal(pp.cpu().numpy(), r["pool_pos"])
+            assert np.array_equal(pc.cpu().numpy(), r["pool_count"])
+
+
+def test_layer_chain_hot_region():
+    """A row whose Top-K lies in two adjacent chunks: the keys of positions
+    [40960, 49152) of the first sequence get their E8M0 scale raised by 2 (their
+    scores times 4), so each of those chunks' lists holds at least K entries
+    above every other chunk's bound, more than the gathered candidates of one
+    filter workgroup may hold: that row is selected from the lists, the other
+    sequence's rows from the gathered candidates, in the same launch."""
+    wl = synth.make_workload("hot_region", 0xC5A2D001, [131072, 131072], 1,
+                             [(20, synth.MODE_FULL, True), (24, synth.MODE_REINDEX, False), (25, synth.MODE_REUSE, False)],
+                             Hm=16)
+    seen = set()
+    for ks in [wl.k_sc] + [L.k_sc for L in wl.layers]:
+        if ks is not None and id(ks) not in seen:
+            seen.add(id(ks))
+            ks[40960:49152] += 2
+    dw = DevWorkload(wl)
+    outs, (pb, pp, pc), _ = run_chain(dw)
+    torch.cuda.synchronize()
+    ref = oracle.layer_chain(wl)
+    hot = ref[0]["idx"][0]
+    assert ((hot >= 40960) & (hot < 49152)).all(), "the first row's Top-K lies in the raised region"
     for o, r in zip(outs, ref):
         assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"layer {r['layer']} indices"
         assert_close_attn(o["out"].cpu().numpy(), r["out"], f"layer {r['layer']}")
