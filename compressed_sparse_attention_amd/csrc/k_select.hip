@@ -927,7 +927,7 @@ __global__ __launch_bounds__(1024) void k_topk_lists(const uint64_t* __restrict_
         const uint64_t ov = __ballot(lane < parts && pc > (uint32_t)cap);
         if (lane == 0) pover = ov ? 1u : 0u;
     }
-    __syncthreads();  // lb_sh is set before any thread lowers it
+    __syncthreads();  // the cleared LDS, the parts' offsets and lb_sh (before any thread lowers it)
 
     // The K winners among the n_surv keys in c (every key at or above the
     // row's bound, in any order): a radix select on key64 from the top with
