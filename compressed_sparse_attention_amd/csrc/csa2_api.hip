@@ -78,7 +78,8 @@ size_t pool_ws_bytes(const Geometry& g, int block) {
 }
 
 struct ChainWs {
-    size_t scores, pool_scores, pool_ws, idx_cur, idx_empty, pool_out, attn, attn_bytes, total;
+    size_t scores, pool_scores, pool_ws, idx_cur, idx_empty, pool_out, tiles, attn, attn_bytes, total;
+    int64_t tstride;  // tile maxima per row
 };
 
 ChainWs chain_ws(const Geometry& g, int K, int block, int max_blocks) {
@@ -99,6 +100,10 @@ ChainWs chain_ws(const Geometry& g, int K, int block, int max_blocks) {
     w.pool_out = off;
     off += al256((size_t)g.total_q * max_blocks * 4) + al256((size_t)g.total_q * max_blocks * block * 4) +
            al256((size_t)g.total_q * 4);
+    w.tiles = off;  // the prefill scorer's tile maxima [total_q][tstride], then one tile bound per row
+    w.tstride = (g.max_entries + kTile - 1) / kTile;
+    if (w.tstride < 1) w.tstride = 1;
+    off += al256((size_t)g.total_q * (size_t)w.tstride * 4) + al256((size_t)g.total_q * 4);
     w.attn = off;  // attention partials for 64 heads and a 128-row window
     w.attn_bytes = attn_ws_bytes(g, 64, attn_splits(g, 64, K, 128));
     off += al256(w.attn_bytes);
@@ -491,6 +496,8 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
     char* pws = base + cw.pool_ws;
     int32_t* idx_cur = (int32_t*)(base + cw.idx_cur);
     int32_t* idx_empty = (int32_t*)(base + cw.idx_empty);
+    uint32_t* tmax = (uint32_t*)(base + cw.tiles);
+    uint32_t* tbound = (uint32_t*)(base + cw.tiles + al256((size_t)g.total_q * (size_t)cw.tstride * 4));
     char* po = base + cw.pool_out;
     int32_t* pb = pool_blocks ? pool_blocks : (int32_t*)po;
     po += al256((size_t)g.total_q * p->max_blocks * 4);
@@ -583,6 +590,12 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                                on_pool ? pp : nullptr, on_pool ? pool_stride : 0, on_pool ? pscores : scores,
                                on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1),
                                fused ? topk_ws_hist(topk_ws) : nullptr};
+                // a prefill scorer also records its tiles' maxima, which bound the Top-K
+                const bool tiles = !on_pool && prefill_scorer(g, L.q_fmt);
+                if (tiles) {
+                    sa.tmax = tmax;
+                    sa.tstride = cw.tstride;
+                }
                 if ((e = full ? timed_scan(sa, p, &scan_timed, stream) : launch_index_score(sa, stream)) != hipSuccess)
                     return hip_fail(e);
                 TopkLaunch ta{};
@@ -600,6 +613,11 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                 ta.idx = idx_cur;
                 ta.ws = topk_ws;
                 ta.hist = fused ? topk_ws_hist(topk_ws) : nullptr;
+                if (tiles) {
+                    ta.tmax = tmax;
+                    ta.tstride = cw.tstride;
+                    ta.tb = tbound;
+                }
                 if ((e = launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
                 // the pool runs its own selection in the same workspace: after the Top-K
                 if (build_pool) {

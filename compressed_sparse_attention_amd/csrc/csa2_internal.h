@@ -289,7 +289,17 @@ struct ScoreLaunch {
     uint32_t* hist;             // nullable: [total_q][kHistBins], zeroed by the caller
     const LocalOut* local;      // nullable: decode scan writes per-chunk candidate lists, not scores
     hipEvent_t ev_begin = nullptr, ev_end = nullptr;  // optional: stamped by the score kernel's dispatch
+    // nullable, prefill scorers only (prefill_scorer): the key (score_key) of
+    // the largest score of each row's kTile-slot tile, [total_q][tstride],
+    // written for the tiles that hold a slot the row sees
+    uint32_t* tmax = nullptr;
+    int64_t tstride = 0;
 };
+// slots per tile of the prefill scorers' tile maxima
+constexpr int kTile = 64;
+// score rows come from a prefill scorer (many query rows, or E4M3 queries)
+// rather than from the decode scan
+inline bool prefill_scorer(const Geometry& g, int q_fmt) { return q_fmt == CSA2_Q_FP8 || g.max_q_per_seq > 4; }
 hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s);
 
 struct TopkLaunch {
@@ -307,6 +317,12 @@ struct TopkLaunch {
     int32_t* idx;               // [total_q][K]
     void* ws;
     const uint32_t* hist;       // nullable: histogram of the scores made with them (skips the histogram pass)
+    // nullable: the scores' tile maxima (ScoreLaunch::tmax) and room for one
+    // bound per row: rows of at least K tiles are then bounded by their K-th
+    // largest tile maximum and only the tiles that reach it are read
+    const uint32_t* tmax = nullptr;
+    int64_t tstride = 0;
+    uint32_t* tb = nullptr;
 };
 // Rows of at most kRowSelMax slots are selected by one workgroup each, from
 // their scores alone (a histogram made with the scores is not used)

@@ -61,6 +61,25 @@ __device__ __forceinline__ v4i ld16(const uint8_t* p) { return *reinterpret_cast
 // add a NaN-quieting max in front of it; the MFMA results are never NaN.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// Maxima across lanes with DPP moves (VALU operands, no LDS round trip):
+// max32 leaves the maximum of each 32-lane half in its lane 31 (and 63),
+// max64 the maximum of the wave in lane 63; other lanes hold partial maxima.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_max(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF,
+                                                               false)));
+}
+__device__ __forceinline__ float max32(float v) {
+    v = dpp_max<0xB1>(v);        // quad_perm 1,0,3,2: lanes xor 1
+    v = dpp_max<0x4E>(v);        // quad_perm 2,3,0,1: lanes xor 2
+    v = dpp_max<0x141>(v);       // row_half_mirror: the two quads of each 8 lanes
+    v = dpp_max<0x140>(v);       // row_mirror: the two 8-lane halves of each 16-lane row
+    return dpp_max<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3: lane 15 of the row below
+}
+__device__ __forceinline__ float max64(float v) {
+    return dpp_max<0x143, 0xC>(max32(v));  // row_bcast:31 into rows 2 and 3: lane 31
+}
+
 // After the MFMAs of one 64-position tile, acc[nt] holds 32 heads of
 // positions 32nt + l%32.  Swap the upper half of nt = 0 with the lower half of
 // nt = 1 so that every lane holds the 32 heads of position p0 + lane, then
@@ -598,7 +617,8 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
                                                        const int64_t* __restrict__ entry_off,
                                                        const int32_t* __restrict__ q_off,
                                                        const int32_t* __restrict__ q_pos, int ratio,
-                                                       float* __restrict__ scores, int64_t stride) {
+                                                       float* __restrict__ scores, int64_t stride,
+                                                       uint32_t* __restrict__ tmax, int64_t tstride) {
     constexpr int NMT = H / 32;
     constexpr int PT = 1024;
     constexpr int QG = 8;
@@ -723,7 +743,12 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
                     }
                 }
             const float s = head_sum<NMT>(acc, w + (int64_t)rows[u] * H);
-            if (jl < n) scores[(int64_t)rows[u] * stride + jl] = jl < vis[u] ? (MX ? s : ldexpf(s, ek - 127)) : -INFINITY;
+            const float sv = jl < vis[u] ? (MX ? s : ldexpf(s, ek - 127)) : -INFINITY;
+            if (jl < n) scores[(int64_t)rows[u] * stride + jl] = sv;
+            if (tmax) {  // the tile's largest stored score (lanes past n take no part)
+                const float mv = max64(jl < n ? sv : -INFINITY);
+                if (lane == 63) tmax[(int64_t)rows[u] * tstride + p0 / kTile] = score_key(mv);
+            }
         }
     }
 }
@@ -764,7 +789,8 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill_fp8(const uint8_t* __r
                                                            const int64_t* __restrict__ entry_off,
                                                            const int32_t* __restrict__ q_off,
                                                            const int32_t* __restrict__ q_pos, int ratio,
-                                                           float* __restrict__ scores, int64_t stride) {
+                                                           float* __restrict__ scores, int64_t stride,
+                                                           uint32_t* __restrict__ tmax, int64_t tstride) {
     constexpr int NM = H / 16;  // MFMA row groups: 16 heads of each of the wave's two queries
     constexpr int PT = kPrefillChunk;
     constexpr int QG = 8;
@@ -914,11 +940,18 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill_fp8(const uint8_t* __r
                     accp = acc;
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                float mv = -INFINITY;  // the tile's largest stored score for this lane half's query
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const int64_t j = p0 + 32 * nt + li;
                     const int ek = ksc_lds[buf][64 * tile + 32 * nt + li];
-                    if (live && j < p_end) scores[rowo * stride + j] = j < vis ? ldexpf(s[nt], ek - 127) : -INFINITY;
+                    const float sv = j < vis ? ldexpf(s[nt], ek - 127) : -INFINITY;
+                    if (live && j < p_end) scores[rowo * stride + j] = sv;
+                    mv = j < p_end ? fmaxf(mv, sv) : mv;
+                }
+                if (tmax) {
+                    mv = max32(mv);
+                    if (live && li == 31) tmax[rowo * tstride + p0 / kTile] = score_key(mv);
                 }
             }
             if (next) {
@@ -984,10 +1017,10 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
         dim3 grid((unsigned)((a.g.max_entries + seg - 1) / seg), (unsigned)((a.g.max_q_per_seq + 7) / 8), a.g.n_seq);
         if (a.H == 64)
             hipExtLaunchKernelGGL((k_score_prefill_fp8<64>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,
-                               b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride);
+                               b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, a.tmax, a.tstride);
         else
             hipExtLaunchKernelGGL((k_score_prefill_fp8<32>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,
-                               b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride);
+                               b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, a.tmax, a.tstride);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((a.g.max_entries + 1023) / 1024), (unsigned)((a.g.max_q_per_seq + 7) / 8), a.g.n_seq);
@@ -995,7 +1028,7 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
     do { if (mx) CSA2_PRE_M(HH, FF, true); else CSA2_PRE_M(HH, FF, false); } while (0)
 #define CSA2_PRE_M(HH, FF, MM)                                                                                    \
     hipExtLaunchKernelGGL((k_score_prefill<HH, FF, MM>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,          \
-                       b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride)
+                       b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, a.tmax, a.tstride)
     if (a.H == 64) CSA2_PRE(64, 4); else CSA2_PRE(32, 4);
 #undef CSA2_PRE
 #undef CSA2_PRE_M

@@ -67,11 +67,14 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
 // about cs K slots pass it instead of about K, which the collect pass and the
 // final radix select absorb while cs K stays well inside their capacity.
 inline int bound_stride(int K) { return K <= 512 ? 4 : (K <= 1024 ? 2 : 1); }
+// A row with a tile bound (tb[row] != 0, k_tile_bound) needs no chunk bound.
 __global__ __launch_bounds__(256) void k_chunk_bound(const float* __restrict__ scores, int64_t stride, RowSrc rs,
-                                                     int K, int cs, uint32_t* __restrict__ lb) {
+                                                     int K, int cs, const uint32_t* __restrict__ tb,
+                                                     uint32_t* __restrict__ lb) {
     __shared__ uint32_t h[kHistBins];
     __shared__ uint32_t wtot[4], found[2];
     const int row = blockIdx.y;
+    if (tb && tb[row]) return;
     const int64_t n = row_n(rs, row);
     const int64_t c = (int64_t)blockIdx.x * cs;
     const int64_t s0 = c * kHChunk;
@@ -93,6 +96,67 @@ __global__ __launch_bounds__(256) void k_chunk_bound(const float* __restrict__ s
     if (threadIdx.x == 0) lb[(int64_t)row * kHistBins + c] = bm;
 }
 
+// The tile bound of a row from the prefill scorer's tile maxima (the key of
+// the largest score of each kTile-slot tile): a key T at most the kk-th
+// largest of the row's tile maxima.  Those kk tiles each hold a slot that
+// reaches T, so the row's kk-th largest key is at least T, and only the tiles
+// whose maximum reaches T hold candidates.  T is the smallest key of the
+// 128-key sub-bin (bits 31..7) holding that kk-th largest maximum: its bin
+// first, then bits 18..7 within the bin.  tb[row] = 0 (no tile bound) for a
+// row of fewer than kk tiles, or when that maximum lies in bin 0 (where keys
+// of both signs mix).
+constexpr int kTileBatch = 16;  // tile maxima per thread in flight
+
+__global__ __launch_bounds__(256) void k_tile_bound(const uint32_t* __restrict__ tmax, int64_t tstride, RowSrc rs,
+                                                    int K, uint32_t* __restrict__ tb) {
+    __shared__ uint32_t h[kHistBins];
+    __shared__ uint32_t wtot[4], found[2];
+    const int row = blockIdx.x;
+    const int64_t n = row_n(rs, row);
+    const uint32_t kk = (uint32_t)(n < K ? n : K);
+    const int64_t nt = (n + kTile - 1) / kTile;
+    if (kk == 0 || nt < (int64_t)kk) {
+        if (threadIdx.x == 0) tb[row] = 0u;
+        return;
+    }
+    const uint32_t* tr = tmax + (int64_t)row * tstride;
+    // count(f): f(key) for each of the row's nt tile maxima, kTileBatch loads
+    // per thread issued together (a slot past nt re-reads the last one and
+    // is not counted)
+    auto count = [&](auto&& f) {
+        for (int64_t t0 = 0; t0 < nt; t0 += 256 * kTileBatch) {
+            uint32_t k[kTileBatch];
+#pragma unroll
+            for (int u = 0; u < kTileBatch; ++u) {
+                const int64_t t = t0 + threadIdx.x + 256 * u;
+                k[u] = tr[t < nt ? t : nt - 1];
+            }
+#pragma unroll
+            for (int u = 0; u < kTileBatch; ++u)
+                if (t0 + threadIdx.x + 256 * u < nt) f(k[u]);
+        }
+    };
+    for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
+    __syncthreads();
+    count([&](uint32_t k) { atomicAdd(&h[key_bin(k)], 1u); });
+    __syncthreads();
+    const uint32_t B = threshold_bin(PlainBins{h}, kk, wtot, found);
+    const uint32_t above = found[1];
+    if (B == 0) {  // the same for every thread
+        if (threadIdx.x == 0) tb[row] = 0u;
+        return;
+    }
+    for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0;
+    __syncthreads();
+    const uint32_t top = B + 4096u;  // bits 31..19 of every key in bin B
+    count([&](uint32_t k) {
+        if ((k >> 19) == top) atomicAdd(&h[(k >> 7) & 0xFFFu], 1u);
+    });
+    __syncthreads();
+    const uint32_t subbin = threshold_bin(PlainBins{h}, kk - above, wtot, found);
+    if (threadIdx.x == 0) tb[row] = (top << 19) | (subbin << 7);
+}
+
 // Candidates: every slot whose bin is at or above the threshold bin goes to
 // the row's candidate list.  A workgroup first gathers its candidates in LDS
 // and then reserves room in the row's list with a single atomic (a returning
@@ -104,21 +168,106 @@ __global__ __launch_bounds__(256) void k_chunk_bound(const float* __restrict__ s
 constexpr int kLocalCand = 2048;
 
 // LB: `hist` holds the chunk bounds of k_chunk_bound instead of a histogram,
-// and the candidates are the slots at or above the smallest of them.
+// and the candidates are the slots at or above the smallest of them; or, for
+// a row with a tile bound T (tb[row] != 0), the slots whose key reaches T,
+// read only from the tiles whose maximum (tmax) reaches it.
 template <bool LB>
 __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ scores, int64_t stride, RowSrc rs,
                                                  const uint32_t* __restrict__ hist, int K, int cs,
-                                                 RowSel* __restrict__ sel, uint64_t* __restrict__ cand_buf) {
+                                                 const uint32_t* __restrict__ tmax, int64_t tstride,
+                                                 const uint32_t* __restrict__ tb, RowSel* __restrict__ sel,
+                                                 uint64_t* __restrict__ cand_buf) {
     __shared__ uint32_t part[4];
     __shared__ uint32_t found[2];
     __shared__ uint64_t lc[kLocalCand];
     __shared__ uint32_t lcount, gbase;
+    __shared__ uint8_t tl[kHChunk / kTile];
+    __shared__ uint32_t ntl;
     const int row = blockIdx.y;
     const int64_t n = row_n(rs, row);
     const int64_t s0 = (int64_t)blockIdx.x * kHChunk;
     if (s0 >= n && blockIdx.x != 0) return;
     const float* sr = scores + (int64_t)row * stride;
     const int64_t s1 = s0 + kHChunk < n ? s0 + kHChunk : n;
+    const int lane = threadIdx.x & 63;
+    // this workgroup's candidates (lcount of them in lc) to the row's list
+    auto append = [&]() {
+        __syncthreads();
+        const uint32_t cnt = lcount;
+        if (cnt == 0) return;
+        if (threadIdx.x == 0)
+            gbase = atomicAdd(&sel[row].cnt, cnt <= (uint32_t)kLocalCand ? cnt : (uint32_t)kCandCap + 1u);
+        __syncthreads();
+        if (cnt > (uint32_t)kLocalCand) return;  // row overflowed: k_final selects it from the scores
+        uint64_t* cb = cand_buf + (int64_t)row * kCandCap;
+        for (uint32_t i = threadIdx.x; i < cnt; i += 256)
+            if (gbase + i < (uint32_t)kCandCap) cb[gbase + i] = lc[i];
+    };
+    // put(take, key, slot) for the slots of one pass, the candidates gathered
+    // in LDS by one reservation per wave
+    auto put = [&](bool take, uint32_t key, int64_t s) {
+        const uint64_t m = __ballot(take);
+        if (m) {
+            uint32_t p0 = 0;
+            if (lane == 0) p0 = atomicAdd(&lcount, (uint32_t)__popcll(m));
+            p0 = __shfl(p0, 0);
+            if (take) {
+                const uint32_t p = p0 + (uint32_t)__popcll(m & ((1ull << lane) - 1));
+                if (p < (uint32_t)kLocalCand) lc[p] = composite(key, (uint32_t)s);
+            }
+        }
+    };
+    if constexpr (LB) {
+        const uint32_t T = tb ? tb[row] : 0u;
+        if (T) {
+            const uint32_t kk = (uint32_t)(n < K ? n : K);
+            if (blockIdx.x == 0 && threadIdx.x == 0) {
+                sel[row].n = (uint32_t)n;
+                sel[row].kk = kk;
+                sel[row].bin = key_bin(T);
+                sel[row].above = 0u;
+                sel[row].lb = 1u;
+            }
+            if (s0 >= n) return;
+            // the chunk's tiles whose maximum reaches T, listed in LDS
+            const int64_t t0 = s0 / kTile, nt = (n + kTile - 1) / kTile;
+            if (threadIdx.x == 0) {
+                lcount = 0;
+                ntl = 0;
+            }
+            __syncthreads();
+            if (threadIdx.x < kHChunk / kTile) {
+                const int64_t t = t0 + threadIdx.x;
+                const bool reach = t < nt && tmax[(int64_t)row * tstride + (t < nt ? t : nt - 1)] >= T;
+                const uint64_t m = __ballot(reach);
+                uint32_t p0 = 0;
+                if (lane == 0 && m) p0 = atomicAdd(&ntl, (uint32_t)__popcll(m));
+                p0 = __shfl(p0, 0);
+                if (reach) tl[p0 + (uint32_t)__popcll(m & ((1ull << lane) - 1))] = (uint8_t)threadIdx.x;
+            }
+            __syncthreads();
+            // wave w reads listed tiles w, w + 4, ..., kTileBatch / 2 of them a
+            // pass, lane l the tile's slot l (a list index past the end
+            // re-reads the last tile and is not kept)
+            const uint32_t mt = ntl;
+            const int wave = threadIdx.x >> 6;
+            constexpr int TP = kTileBatch / 2;
+            for (uint32_t i0 = (uint32_t)wave; i0 < mt; i0 += 4u * TP) {
+                uint32_t key[TP];
+                int64_t sl[TP];
+#pragma unroll
+                for (int u = 0; u < TP; ++u) {
+                    const uint32_t i = i0 + 4u * u;
+                    sl[u] = s0 + (int64_t)kTile * tl[i < mt ? i : mt - 1] + lane;
+                    key[u] = score_key(sr[sl[u] < s1 ? sl[u] : s1 - 1]);
+                }
+#pragma unroll
+                for (int u = 0; u < TP; ++u) put(i0 + 4u * u < mt && sl[u] < s1 && key[u] >= T, key[u], sl[u]);
+            }
+            append();
+            return;
+        }
+    }
     // issue this thread's loads before the threshold search, all of them
     // unconditionally (a slot past the chunk re-reads its last slot, and every
     // use below checks s < s1): a load whose value is used under a per-lane
@@ -159,32 +308,12 @@ __global__ __launch_bounds__(256) void k_collect(const float* __restrict__ score
         sel[row].lb = LB ? 1u : 0u;
     }
     if (bin >= (uint32_t)kHistBins || s0 >= n) return;
-    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int u = 0; u < kHChunk / 256; ++u) {
         const int64_t s = s0 + threadIdx.x + 256 * u;
-        const bool take = s < s1 && key_bin(key[u]) >= bin;
-        const uint64_t m = __ballot(take);
-        if (m) {
-            uint32_t p0 = 0;
-            if (lane == 0) p0 = atomicAdd(&lcount, (uint32_t)__popcll(m));
-            p0 = __shfl(p0, 0);
-            if (take) {
-                const uint32_t p = p0 + (uint32_t)__popcll(m & ((1ull << lane) - 1));
-                if (p < (uint32_t)kLocalCand) lc[p] = composite(key[u], (uint32_t)s);
-            }
-        }
+        put(s < s1 && key_bin(key[u]) >= bin, key[u], s);
     }
-    __syncthreads();
-    const uint32_t cnt = lcount;
-    if (cnt == 0) return;
-    if (threadIdx.x == 0)
-        gbase = atomicAdd(&sel[row].cnt, cnt <= (uint32_t)kLocalCand ? cnt : (uint32_t)kCandCap + 1u);
-    __syncthreads();
-    if (cnt > (uint32_t)kLocalCand) return;  // row overflowed: k_final selects it from the scores
-    uint64_t* cb = cand_buf + (int64_t)row * kCandCap;
-    for (uint32_t i = threadIdx.x; i < cnt; i += 256)
-        if (gbase + i < (uint32_t)kCandCap) cb[gbase + i] = lc[i];
+    append();
 }
 
 // Per row, the threshold bin of its Top-K in the finished histogram (and the
@@ -1530,12 +1659,19 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
         // place) give a lower bound of each row's threshold bin
         hipError_t e = clear_topk_ws(a.ws, nq, false, s);
         if (e != hipSuccess) return e;
+        // with the scorer's tile maxima, rows of at least K tiles take the
+        // tile bound and skip the chunk bounds
+        const uint32_t* tb = nullptr;
+        if (a.tmax && a.tb) {
+            hipLaunchKernelGGL(k_tile_bound, dim3(nq), dim3(256), 0, s, a.tmax, a.tstride, rs, a.K, a.tb);
+            tb = a.tb;
+        }
         const int cs = bound_stride(a.K);
         const unsigned sampled = (chunks + cs - 1) / cs;
         hipLaunchKernelGGL(k_chunk_bound, dim3(sampled ? sampled : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, a.K,
-                           cs, hist);
+                           cs, tb, hist);
         hipLaunchKernelGGL(k_collect<true>, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs,
-                           hist, a.K, cs, sel, cb);
+                           hist, a.K, cs, a.tmax, a.tstride, tb, sel, cb);
     } else {
         if (h != hist) {
             hipError_t e = clear_topk_ws(a.ws, nq, false, s);
@@ -1543,7 +1679,7 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
         }
         // (h == hist: the caller cleared the workspace and filled its histogram)
         hipLaunchKernelGGL(k_collect<false>, dim3(chunks ? chunks : 1, nq), dim3(256), 0, s, a.scores, a.stride, rs, h,
-                           a.K, 1, sel, cb);
+                           a.K, 1, (const uint32_t*)nullptr, (int64_t)0, (const uint32_t*)nullptr, sel, cb);
     }
     hipLaunchKernelGGL(k_final, dim3(nq), dim3(1024), 0, s, a.scores, a.stride, sel, cb, a.cand, a.cand_stride, a.K,
                        a.idx);
