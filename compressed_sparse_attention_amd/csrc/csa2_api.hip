@@ -590,11 +590,16 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                                on_pool ? pp : nullptr, on_pool ? pool_stride : 0, on_pool ? pscores : scores,
                                on_pool ? (int64_t)pool_stride : (g.max_entries > 0 ? g.max_entries : 1),
                                fused ? topk_ws_hist(topk_ws) : nullptr};
-                // a prefill scorer also records its tiles' maxima, which bound the Top-K
+                // a prefill scorer also records its tiles' maxima, which bound the
+                // Top-K, and the block maxima a pool built here selects from
                 const bool tiles = !on_pool && prefill_scorer(g, L.q_fmt);
                 if (tiles) {
                     sa.tmax = tmax;
                     sa.tstride = cw.tstride;
+                    if (build_pool && p->block == kPoolBlock && L.q_fmt != CSA2_Q_FP8) {
+                        sa.bmax = (float*)pws;
+                        sa.bstride = nb > 0 ? nb : 1;
+                    }
                 }
                 if ((e = full ? timed_scan(sa, p, &scan_timed, stream) : launch_index_score(sa, stream)) != hipSuccess)
                     return hip_fail(e);
@@ -634,6 +639,7 @@ CSA2_API csa2_status csa2_layer_chain(const csa2_batch* batch, const csa2_chain_
                     pa.bscores = (float*)pws;
                     pa.bstride = nb > 0 ? nb : 1;
                     pa.topk_ws = topk_ws;
+                    pa.bscores_ready = sa.bmax != nullptr;  // the scorer wrote the block maxima
                     if ((e = launch_block_pool(pa, stream)) != hipSuccess) return hip_fail(e);
                     pool_built = true;
                 }

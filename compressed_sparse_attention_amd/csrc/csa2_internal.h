@@ -294,7 +294,15 @@ struct ScoreLaunch {
     // written for the tiles that hold a slot the row sees
     uint32_t* tmax = nullptr;
     int64_t tstride = 0;
+    // nullable, the FP4 prefill scorer only (E4M3 queries: an error): the
+    // largest score of each kPoolBlock-slot block of a row, [total_q][bstride]
+    // (what k_block_max computes), written for the blocks that hold a slot
+    // the row sees
+    float* bmax = nullptr;
+    int64_t bstride = 0;
 };
+// slots per block of the block pool the prefill scorers' maxima serve
+constexpr int kPoolBlock = 8;
 // slots per tile of the prefill scorers' tile maxima
 constexpr int kTile = 64;
 // score rows come from a prefill scorer (many query rows, or E4M3 queries)

@@ -62,22 +62,26 @@ __device__ __forceinline__ v4i ld16(const uint8_t* p) { return *reinterpret_cast
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Maxima across lanes with DPP moves (VALU operands, no LDS round trip):
-// max32 leaves the maximum of each 32-lane half in its lane 31 (and 63),
-// max64 the maximum of the wave in lane 63; other lanes hold partial maxima.
+// max8 leaves the maximum of each group of 8 lanes in all 8 of them; from
+// there, max32_8 leaves the maximum of each 32-lane half in its lane 31 (and
+// 63) and max64_8 the maximum of the wave in lane 63 (other lanes hold
+// partial maxima).
 template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ float dpp_max(float v) {
     return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF,
                                                                false)));
 }
-__device__ __forceinline__ float max32(float v) {
-    v = dpp_max<0xB1>(v);        // quad_perm 1,0,3,2: lanes xor 1
-    v = dpp_max<0x4E>(v);        // quad_perm 2,3,0,1: lanes xor 2
-    v = dpp_max<0x141>(v);       // row_half_mirror: the two quads of each 8 lanes
-    v = dpp_max<0x140>(v);       // row_mirror: the two 8-lane halves of each 16-lane row
+__device__ __forceinline__ float max8(float v) {
+    v = dpp_max<0xB1>(v);          // quad_perm 1,0,3,2: lanes xor 1
+    v = dpp_max<0x4E>(v);          // quad_perm 2,3,0,1: lanes xor 2
+    return dpp_max<0x141>(v);      // row_half_mirror: the two quads of each 8 lanes
+}
+__device__ __forceinline__ float max32_8(float v) {
+    v = dpp_max<0x140>(v);          // row_mirror: the two 8-lane halves of each 16-lane row
     return dpp_max<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3: lane 15 of the row below
 }
-__device__ __forceinline__ float max64(float v) {
-    return dpp_max<0x143, 0xC>(max32(v));  // row_bcast:31 into rows 2 and 3: lane 31
+__device__ __forceinline__ float max64_8(float v) {
+    return dpp_max<0x143, 0xC>(max32_8(v));  // row_bcast:31 into rows 2 and 3: lane 31
 }
 
 // After the MFMAs of one 64-position tile, acc[nt] holds 32 heads of
@@ -618,7 +622,8 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
                                                        const int32_t* __restrict__ q_off,
                                                        const int32_t* __restrict__ q_pos, int ratio,
                                                        float* __restrict__ scores, int64_t stride,
-                                                       uint32_t* __restrict__ tmax, int64_t tstride) {
+                                                       uint32_t* __restrict__ tmax, int64_t tstride,
+                                                       float* __restrict__ bmax, int64_t bstride) {
     constexpr int NMT = H / 32;
     constexpr int PT = 1024;
     constexpr int QG = 8;
@@ -745,9 +750,13 @@ __global__ __launch_bounds__(256) void k_score_prefill(const uint8_t* __restrict
             const float s = head_sum<NMT>(acc, w + (int64_t)rows[u] * H);
             const float sv = jl < vis[u] ? (MX ? s : ldexpf(s, ek - 127)) : -INFINITY;
             if (jl < n) scores[(int64_t)rows[u] * stride + jl] = sv;
-            if (tmax) {  // the tile's largest stored score (lanes past n take no part)
-                const float mv = max64(jl < n ? sv : -INFINITY);
-                if (lane == 63) tmax[(int64_t)rows[u] * tstride + p0 / kTile] = score_key(mv);
+            if (tmax || bmax) {  // the blocks' and the tile's largest stored scores (lanes past n take no part)
+                const float bv = max8(jl < n ? sv : -INFINITY);
+                if (bmax && (lane & (kPoolBlock - 1)) == 0) bmax[(int64_t)rows[u] * bstride + jl / kPoolBlock] = bv;
+                if (tmax) {
+                    const float mv = max64_8(bv);
+                    if (lane == 63) tmax[(int64_t)rows[u] * tstride + p0 / kTile] = score_key(mv);
+                }
             }
         }
     }
@@ -950,7 +959,7 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill_fp8(const uint8_t* __r
                     mv = j < p_end ? fmaxf(mv, sv) : mv;
                 }
                 if (tmax) {
-                    mv = max32(mv);
+                    mv = max32_8(max8(mv));
                     if (live && li == 31) tmax[rowo * tstride + p0 / kTile] = score_key(mv);
                 }
             }
@@ -1011,6 +1020,7 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
         return hipGetLastError();
     }
     if (a.q_fmt == CSA2_Q_FP8) {
+        if (a.bmax) return hipErrorInvalidValue;  // block maxima come from the FP4 scorer only
         // one workgroup per (segment of kPrefillSegChunks chunks, 8 rows);
         // consecutive segments go to consecutive XCDs
         constexpr int64_t seg = (int64_t)kPrefillChunk * kPrefillSegChunks;
@@ -1028,7 +1038,8 @@ hipError_t launch_index_score(const ScoreLaunch& a, hipStream_t s) {
     do { if (mx) CSA2_PRE_M(HH, FF, true); else CSA2_PRE_M(HH, FF, false); } while (0)
 #define CSA2_PRE_M(HH, FF, MM)                                                                                    \
     hipExtLaunchKernelGGL((k_score_prefill<HH, FF, MM>), grid, dim3(256), 0, s, a.ev_begin, a.ev_end, 0, a.q, a.q_sc, a.w, a.k, a.k_sc,          \
-                       b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, a.tmax, a.tstride)
+                       b->d_entry_off, b->d_q_off, b->d_q_pos, b->ratio, a.scores, a.stride, a.tmax, a.tstride, a.bmax, \
+                       a.bstride)
     if (a.H == 64) CSA2_PRE(64, 4); else CSA2_PRE(32, 4);
 #undef CSA2_PRE
 #undef CSA2_PRE_M

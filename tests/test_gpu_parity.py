@@ -346,12 +346,14 @@ CHAIN_CASES = {
     # K = 512 tiles of 64 slots take the bound from their tiles' maxima, the
     # others the chunk bounds; E4M3 queries at ratio 2 with visible counts
     # from 1 to 60,000 (32,768 is exactly 512 tiles), and FP4 replay rows over
-    # 40,000 entries
+    # 40,000 entries, whose pool selects from the 8-slot block maxima the
+    # scorer writes
     "prefill_tiles_fp8": lambda: synth.make_workload("pf8tiles", 0xC5A2D002, [60000], len(_PF8_SEG_T),
                                                      [(2, synth.MODE_FULL, False), (3, synth.MODE_REUSE, False)],
                                                      ratio=2, Hm=16, q_fmt=synth.Q_FP8, q_pos=[_PF8_SEG_T]),
     "replay_tiles_fp4": lambda: synth.config("replay_c5", n_seq=1, n=40000, T=64, Hm=16,
-                                             schedule=[(20, synth.MODE_FULL, False), (21, synth.MODE_REUSE, False)]),
+                                             schedule=[(20, synth.MODE_FULL, True), (24, synth.MODE_REINDEX, False),
+                                                       (25, synth.MODE_REUSE, False)]),
     # encoder layers 0..19 as one chain at ratio 2: layers 0-1 sliding window
     # only, then Full layers 2, 8 and 14, each with its own main KV and indexer
     # K, read by the Reuse layers after it (report 2.3.1; reading note schedule
