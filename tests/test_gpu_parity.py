@@ -513,6 +513,45 @@ def test_layer_chain_ties(case):
             assert np.array_equal(pc.cpu().numpy(), r["pool_count"])
 
 
+PREFILL_TIE_CASES = {
+    # the prefill scorers' tile bound under ties: one head (few distinct
+    # scores, long runs of ties at the bound) and none (every score 0: the
+    # bound falls in bin 0 and is not used), E4M3 rows at ratio 2 on both
+    # sides of the K-tile boundary and FP4 replay rows over 40,000 entries
+    "fp8_one_head": dict(fp8=True, heads=1),
+    "fp8_all_equal": dict(fp8=True, heads=0),
+    "fp4_one_head": dict(fp8=False, heads=1),
+}
+
+
+@pytest.mark.parametrize("case", list(PREFILL_TIE_CASES))
+def test_layer_chain_prefill_tile_ties(case):
+    c = PREFILL_TIE_CASES[case]
+    if c["fp8"]:
+        wl = synth.make_workload("pf8ties_" + case, 0xC5A2D010 + c["heads"], [60000], len(_PF8_SEG_T),
+                                 [(2, synth.MODE_FULL, False), (3, synth.MODE_REUSE, False)], ratio=2, Hm=16,
+                                 q_fmt=synth.Q_FP8, q_pos=[_PF8_SEG_T])
+    else:
+        wl = synth.config("replay_c5", n_seq=1, n=40000, T=64, Hm=16, seed=0xC5A2D020,
+                          schedule=[(20, synth.MODE_FULL, True), (24, synth.MODE_REINDEX, False),
+                                    (25, synth.MODE_REUSE, False)])
+    for L in wl.layers:
+        if L.w is not None:
+            L.w[:, c["heads"]:] = 0.0
+    with saved_on_failure(wl, "prefill_ties_" + case):
+        dw = DevWorkload(wl)
+        outs, (pb, pp, pc), _ = run_chain(dw)
+        torch.cuda.synchronize()
+        ref = oracle.layer_chain(wl)
+        for o, r in zip(outs, ref):
+            assert np.array_equal(o["idx"].cpu().numpy(), r["idx"]), f"layer {r['layer']} indices"
+            assert_close_attn(o["out"].cpu().numpy(), r["out"], f"layer {r['layer']}")
+            if "pool_pos" in r:
+                assert np.array_equal(pb.cpu().numpy(), r["blocks"])
+                assert np.array_equal(pp.cpu().numpy(), r["pool_pos"])
+                assert np.array_equal(pc.cpu().numpy(), r["pool_count"])
+
+
 NEGW_CASES = {
     # head weights of both signs (U(-1, 1)); every third row all negative, so
     # all of its scores are <= 0 and its threshold lies in bin 0
