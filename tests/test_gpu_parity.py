@@ -521,6 +521,11 @@ PREFILL_TIE_CASES = {
     "fp8_one_head": dict(fp8=True, heads=1),
     "fp8_all_equal": dict(fp8=True, heads=0),
     "fp4_one_head": dict(fp8=False, heads=1),
+    # head weights of both signs, every third row all negative (its tile
+    # maxima lie in bin 0, so its bound is the chunk bounds'), and K = 1,024
+    # (a row needs 1,024 tiles, 65,536 slots, for the tile bound)
+    "fp8_negative_weights": dict(fp8=True, heads=64, negw=True),
+    "fp8_k1024": dict(fp8=True, heads=64, K=1024, n=80000),
 }
 
 
@@ -528,9 +533,11 @@ PREFILL_TIE_CASES = {
 def test_layer_chain_prefill_tile_ties(case):
     c = PREFILL_TIE_CASES[case]
     if c["fp8"]:
-        wl = synth.make_workload("pf8ties_" + case, 0xC5A2D010 + c["heads"], [60000], len(_PF8_SEG_T),
+        n = c.get("n", 60000)  # visible counts (t + 1) / 2 up to 60,000 of the n entries
+        wl = synth.make_workload("pf8ties_" + case, 0xC5A2D010 + len(case), [n], len(_PF8_SEG_T),
                                  [(2, synth.MODE_FULL, False), (3, synth.MODE_REUSE, False)], ratio=2, Hm=16,
-                                 q_fmt=synth.Q_FP8, q_pos=[_PF8_SEG_T])
+                                 K=c.get("K", 512), q_fmt=synth.Q_FP8,
+                                 q_pos=[_PF8_SEG_T + 2 * (n - 60000)])
     else:
         wl = synth.config("replay_c5", n_seq=1, n=40000, T=64, Hm=16, seed=0xC5A2D020,
                           schedule=[(20, synth.MODE_FULL, True), (24, synth.MODE_REINDEX, False),
@@ -538,6 +545,9 @@ def test_layer_chain_prefill_tile_ties(case):
     for L in wl.layers:
         if L.w is not None:
             L.w[:, c["heads"]:] = 0.0
+            if c.get("negw"):
+                L.w[:] = L.w * 2.0 - 1.0
+                L.w[::3] = -np.abs(L.w[::3])
     with saved_on_failure(wl, "prefill_ties_" + case):
         dw = DevWorkload(wl)
         outs, (pb, pp, pc), _ = run_chain(dw)
